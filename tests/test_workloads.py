@@ -1,0 +1,50 @@
+"""The seeded generators: shapes, determinism and the stated input structure."""
+import numpy as np
+import pytest
+
+import workloads as WL
+
+
+def test_tiny_structure():
+    inp = WL.make_inputs("tiny")
+    X = inp["X"]
+    assert X.shape == (16, 256) and X.dtype == np.float16
+    assert inp["P1"].shape == (16, 16) and inp["P1"].dtype == np.float32
+    assert inp["W"].shape == (256, 256) and inp["W"].dtype == np.float32
+    assert list(inp["outlier_channels"]) == [7, 100]
+    # token 0 (x100) and outlier channels (x50) dominate
+    a = np.abs(X.astype(np.float64))
+    assert a[0].mean() > 30 * a[1:].mean()
+    assert a[1:, [7, 100]].mean() > 20 * np.delete(a[1:], [7, 100], axis=1).mean()
+
+
+def test_deterministic():
+    a = WL.make_inputs("tiny")
+    b = WL.make_inputs("tiny")
+    for k in ("X", "P1", "P2", "W"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_factors_invertible_not_orthogonal():
+    inp = WL.make_inputs("tiny", with_weights=False)
+    P1 = inp["P1"].astype(np.float64)
+    sv = np.linalg.svd(P1, compute_uv=False)
+    assert 0.45 < sv.min() and sv.max() < 2.05
+    assert not np.allclose(P1.T @ P1, np.eye(16), atol=1e-2)
+
+
+@pytest.mark.parametrize("name", ["qkv8b", "down8b"])
+def test_activation_shapes_medium(name):
+    wl = WL.get(name)
+    rng = np.random.default_rng(wl.seed)
+    X, ch = WL.make_activations(wl, rng, M=8)
+    assert X.shape == (8, wl.K) and np.isfinite(X.astype(np.float32)).all()
+    if name == "qkv8b":
+        assert ch.size == round(0.005 * wl.K) == 20
+    else:
+        assert ch.size == 0
+
+
+def test_all_workloads_consistent():
+    for wl in WL.WORKLOADS.values():
+        assert wl.n1 * wl.n2 == wl.K and wl.K % wl.group_size == 0
