@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A4 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qkv8b]
+
+A step is one pass of the whole hot path over one batch: w4a4_linear =
+fused activation transform + per-token INT4 quantization + packing, then the
+INT4 x INT4 GEMM with int32 accumulation and the fp16 dequant epilogue.
+Inputs are seeded synthetic LLaMA-shaped tensors (workloads/), resident in
+HBM before the timed region; weights are merged (P^-1 folded in), quantized
+and packed on the GPU beforehand, as a deployment would do offline.
+
+Prints ONE JSON line.  `value` is TOPS of the whole layer (2*M*N*K integer
+ops per step / step time).  `roofline` reports the dominant kernel (the GEMM)
+against the INT8 MFMA peak (prefill) or HBM bandwidth (decode), its duration
+measured with HIP events on the launch stream.  `cpu_baseline` times the CPU
+oracle on the same workload (host cores, float64 numpy).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 linear TOPS + µs/layer; % of INT8 MFMA peak (prefill) / HBM BW (decode)"
+PEAK_INT8_TOPS = 5000.0          # MI355X dense INT8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+MALL_BYTES = 256 << 20           # Infinity Cache: rotate weight copies past it
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qkv8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def gemm_bytes(wl, M):
+    G = wl.K // wl.group_size
+    b = M * wl.K // 2 + 4 * M + wl.N * wl.K // 2 + 2 * wl.N * G + 2 * M * wl.N
+    if wl.asymmetric:
+        b += 2 * wl.N * G
+    return b
+
+
+def traffic_from_profiles(kernel_tag, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "w4a4_post_quantized_amd", "csrc", rec.get("source", "gemm.hip"))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("source_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The CPU oracle on the same workload: whole passes until `budget_s`."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    # weights are prepared offline on both sides (not timed)
+    Wt = O.merge_weights(inp["W"], inp["P1"], inp["P2"], inp["c"])
+    wq = O.quantize_weights(Wt, wl.group_size, wl.asymmetric)
+    del Wt
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        O.linear(inp["X"], inp["P1"], inp["P2"], wq, c=inp["c"])
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end:
+            break
+    t = float(np.median(times))
+    ops = 2.0 * wl.M * wl.N * wl.K
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole {wl.name} layer ({wl.M}x{wl.K}->{wl.N}), {len(times)} passes, "
+                      f"median {t * 1e3:.1f} ms/pass, weights prepared untimed",
+            "us_per_layer": t * 1e6}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the data-parallel W4A4 linear needs no exchange "
+              "between GPUs, so N > 1 is not run here (each GPU would run the same kernel "
+              "on its share of tokens).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as WL
+    import w4a4_post_quantized_amd as L
+
+    wl = WL.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = WL.make_inputs(wl)
+    M, K, N = wl.M, wl.K, wl.N
+
+    X = torch.from_numpy(inp["X"]).to(dev)
+    P1 = torch.from_numpy(inp["P1"]).to(dev)
+    P2 = torch.from_numpy(inp["P2"]).to(dev)
+
+    # offline: merge P^-1 into the weights and quantize, on the GPU
+    wbytes = N * K // 2
+    decode = M <= 64
+    copies = 1
+    if decode:
+        copies = max(3, -(-MALL_BYTES // wbytes) + 1)
+    Wraw = torch.from_numpy(inp["W"]).to(dev)
+    Wt = L.merge_weights(Wraw, P1, P2)
+    del Wraw
+    packs = []
+    for i in range(copies):
+        packs.append(L.pack_weights(Wt if i == 0 else Wt * (1.0 + 1e-3 * i), wl.group_size,
+                                    wl.asymmetric))
+    del Wt
+    desc = packs[0][0]
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ws = torch.empty(max(1, L.linear_workspace_bytes(M, wl.n1, wl.n2, desc)), dtype=torch.uint8,
+                     device=dev)
+    Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    tq_ws = torch.empty(max(1, L.transform_quant_workspace_bytes(M, wl.n1, wl.n2)),
+                        dtype=torch.uint8, device=dev)
+    g_ws = torch.empty(max(1, L.gemm_workspace_bytes(M, desc)), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        _, Wq, sw, zw = packs[i % copies]
+        L.linear(X, P1, P2, desc, Wq, sw, zw, out=Y, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+
+    # per-kernel durations: the same two launches with HIP events between them
+    # on the launch stream (torch's current stream, which the binding uses)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        _, Wq, sw, zw = packs[i % copies]
+        L.transform_quant(X, P1, P2, out=(Xq, sx), ws=tq_ws)
+        L.gemm(Xq, sx, desc, Wq, sw, zw, out=Y, ws=g_ws)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        _, Wq, sw, zw = packs[i % copies]
+        e0, e1, e2 = evs[i]
+        e0.record()
+        L.transform_quant(X, P1, P2, out=(Xq, sx), ws=tq_ws)
+        e1.record()
+        L.gemm(Xq, sx, desc, Wq, sw, zw, out=Y, ws=g_ws)
+        e2.record()
+    torch.cuda.synchronize()
+    tq_us = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e3
+    gemm_us = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) * 1e3
+
+    ops = 2.0 * M * N * K
+    value = ops / t_step / 1e12
+    if decode:
+        gb = gemm_bytes(wl, M)
+        achieved = gb / (gemm_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = ops / (gemm_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
+    roof["kernel"] = "k_gemm_w4a4"
+    roof["kernel_us"] = round(gemm_us, 2)
+    roof["traffic"] = traffic_from_profiles("gemm", wl.name)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 MFMA/int32 acc (int4 codes), fp32 transform",
+        "data": "synthetic (seeded; LLaMA-shaped, outlier channels and pivot token)",
+        "config": {"workload": wl.description, "name": wl.name, "M": M, "K": K, "N": N,
+                   "n1": wl.n1, "n2": wl.n2, "group_size": wl.group_size,
+                   "asymmetric_weights": wl.asymmetric, "weight_copies_rotated": copies},
+        "us_per_layer": round(t_step * 1e6, 2),
+        "transform_quant_us": round(tq_us, 2),
+        "gemm_us": round(gemm_us, 2),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * w4a4.h — C ABI of libw4a4.so, a W4A4 quantized linear layer for AMD MI355X
+ * (gfx950).
+ *
+ * The layer is the one the FlatQuant page ("FlatQuant: Flatness Matters for
+ * LLM Quantization", section 核心思想) writes as Y ≈ Q(X P) · Q(P^-1 W^T),
+ * with P = P1 ⊗ P2 (section Kronecker 分解), an optional per-channel scale
+ * diag(c) and clipping thresholds (section 额外可学习组件), and the
+ * activation transform fused with quantization per token tile (section
+ * 高效 Kernel 设计).  The quantizer is the uniform one of the FRM-PTQ page
+ * ("FRM-PTQ: Feature Relationship Matching Enhanced Low-Bit Post-Training
+ * Quantization for Large Language Models", section 初步介绍), with 4-bit
+ * codes; weights may use per-group scales (the same page's multi-granularity
+ * group quantization).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Buffers are caller-allocated DEVICE memory unless stated otherwise; the
+ *    library keeps no pointer after the call returns and never allocates on
+ *    the compute path (scratch memory comes in through `ws`).
+ *  - fp16 values are passed as uint16_t bit patterns (IEEE binary16).
+ *  - Layouts are row-major.  A matrix of 4-bit codes [R, K] is stored as
+ *    uint8 [R, K/2]; byte j of a row holds code 2j in its low nibble and code
+ *    2j+1 in its high nibble.  Signed codes (-8..7) are two's-complement
+ *    nibbles; unsigned codes (0..15) are stored as is.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; nothing synchronizes.  Device faults surface at the
+ *    caller's next synchronization.
+ *  - Return value: W4A4_OK (0) or a negative W4A4_ERR_* code.  On an error
+ *    no kernel has been launched and no output has been written;
+ *    w4a4_last_error() returns a message (per host thread).  Nothing aborts
+ *    and no C++ exception crosses this interface.
+ *  - Device pointers must be 16-byte aligned (W4A4_ERR_ALIGNMENT otherwise).
+ *  - Non-finite inputs are outside the contract (codes are then undefined).
+ *  - Calls are re-entrant; concurrent calls must not share output or
+ *    workspace buffers.
+ */
+#ifndef W4A4_H_
+#define W4A4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A4_OK 0
+#define W4A4_ERR_INVALID_ARG (-1) /* null pointer, negative or inconsistent size */
+#define W4A4_ERR_UNSUPPORTED (-2) /* valid but not supported shape (see limits) */
+#define W4A4_ERR_ALIGNMENT (-3)   /* a device pointer is not 16-byte aligned */
+#define W4A4_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required */
+#define W4A4_ERR_HIP (-5)         /* a HIP runtime call or launch failed */
+
+/* Limits: 1 <= K <= 65536, K = n1*n2, K % 128 == 0 for the GEMM, K % 16 == 0
+ * for the activation path; 1 <= n1, n2 <= 256; M >= 0; N >= 1. */
+#define W4A4_MAX_K 65536
+#define W4A4_MAX_FACTOR 256
+
+/* Description of a quantized weight matrix W̃ [N, K].
+ *   group_size: number of consecutive input channels sharing one scale (and
+ *               zero point): K for one scale per output channel, otherwise a
+ *               multiple of 128 that divides K.  G = K / group_size.
+ *   asymmetric: 0 -> signed codes q in [-8, 7], zero point 0;
+ *               1 -> unsigned codes u in [0, 15] with a per-group zero point
+ *                    z (an integer 0..15 stored as fp16). */
+typedef struct w4a4_weight_desc {
+    int32_t N;
+    int32_t K;
+    int32_t group_size;
+    int32_t asymmetric;
+} w4a4_weight_desc;
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int w4a4_version(void);
+
+/* Static string for a status code. */
+const char* w4a4_status_str(int status);
+
+/* Message of the last failing call made by this host thread ("" if none). */
+const char* w4a4_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Offline weight preparation                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace w4a4_merge_weights needs for factors (n1, n2). */
+size_t w4a4_merge_workspace_bytes(int32_t n1, int32_t n2, int32_t K);
+
+/* Merge the inverse transform into the weights (offline):
+ *   W̃ = W · diag(1/c) · (P1 ⊗ P2)^-T,  row n: P1^-1 · W̄_n · P2^-T,
+ * FlatQuant page, section Kronecker 分解 (weight-side factor
+ * P1^-1 ×1 W̃ ×2 (P2^-1)^T) and section 额外可学习组件 (diag(c) is undone
+ * on the weights).  P1 and P2 are inverted on the device (Gauss-Jordan with
+ * partial pivoting, float64); the merge runs in float64 and is rounded once
+ * to float32.
+ *   W  [N, K] fp32 (device), P1 [n1, n1] fp32, P2 [n2, n2] fp32 (device),
+ *   c  [K] fp32 or NULL (no channel scaling), Wt [N, K] fp32 output.
+ *   ws: device workspace of w4a4_merge_workspace_bytes(n1, n2, K) bytes.
+ * Offline and not on the hot path: the call synchronizes `stream` once to
+ * read back the pivots and returns W4A4_ERR_INVALID_ARG if P1 or P2 is
+ * numerically singular (a pivot below 1e-300 in magnitude). */
+int w4a4_merge_weights(const float* W, int32_t N, int32_t K, int32_t n1, int32_t n2,
+                       const float* P1, const float* P2, const float* c, float* Wt,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Quantize and pack merged weights W̃ [N, K] fp32 (offline).
+ * FRM-PTQ page, section 初步介绍: Q(W) = clamp(round(W/s) + z, 0, 2^b - 1),
+ * b = 4, round half to even; FlatQuant page, section 额外可学习组件: alpha_w
+ * in (0, 1] scales the range.  Per group of desc->group_size channels:
+ *   symmetric : s = fp16(alpha_w*max|v|/7), q = clamp(round(v/s), -8, 7)
+ *   asymmetric: lo = alpha_w*min(min v, 0), hi = alpha_w*max(max v, 0),
+ *               s = fp16((hi-lo)/15), z = clamp(round(-lo/s), 0, 15),
+ *               u = clamp(round(v/s) + z, 0, 15)
+ * The scale arithmetic runs in float64 and s is rounded directly to fp16;
+ * codes are computed with the stored fp16 s.  A zero scale gives zero codes
+ * (and z = 0).
+ *   Wq  [N, K/2] uint8 packed codes,  s_w [N, G] fp16 scales,
+ *   z_w [N, G] fp16 zero points (required iff asymmetric, else may be NULL). */
+int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha_w,
+                      uint8_t* Wq, uint16_t* s_w, uint16_t* z_w, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Online activation path                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace w4a4_transform_quant needs (0 is possible). */
+size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2);
+
+/* Fused activation transform + per-token INT4 quantization + packing.
+ * FlatQuant page, section Kronecker 分解 (activation factor P1^T ×1 X̃ ×2 P2)
+ * and section 高效 Kernel 设计 (the token tile is transformed and quantized
+ * on chip); section 额外可学习组件 (diag(c), alpha_a).  For each token m:
+ *   Z_m  = P1^T · reshape(x_m ⊙ c, n1, n2) · P2     (row-major reshape,
+ *          k = i*n2 + j; equals x_m · (P1 ⊗ P2)), computed in fp32 or better
+ *   s_x[m] = alpha_a * max_k |Z_m[k]| / 7           (fp32)
+ *   q    = clamp(round_half_even(Z_m / s_x[m]), -8, 7), 0 if s_x[m] == 0
+ *   Xq[m, :] = packed q.
+ *   X [M, K] fp16, P1 [n1, n1] fp32 (P in P = P1 ⊗ P2, NOT its transpose),
+ *   P2 [n2, n2] fp32, c [K] fp32 or NULL, Xq [M, K/2] uint8, s_x [M] fp32.
+ *   ws: device workspace, w4a4_transform_quant_workspace_bytes(M, n1, n2). */
+int w4a4_transform_quant(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                         const float* P1, const float* P2, const float* c, float alpha_a,
+                         uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes, void* stream);
+
+/* Debug / parity form of the transform: writes Z [M, K] fp32 (the value that
+ * w4a4_transform_quant quantizes, same kernels, same arithmetic). */
+int w4a4_transform(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                   const float* P1, const float* P2, const float* c, float* Z,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* INT4 x INT4 GEMM                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace w4a4_gemm needs for M tokens (0 is possible). */
+size_t w4a4_gemm_workspace_bytes(int32_t M, const w4a4_weight_desc* desc);
+
+/* Y = dequant(Xq · Wq^T) — FlatQuant page, section 核心思想, the product
+ * Q(XP) · Q(P^-1 W^T); FPTQuant page ("FPTQuant: Function-Preserving
+ * Transforms for LLM Quantization", section 3. 伪动态残差缩放): a per-token
+ * scale commutes with a bias-free linear, so it is applied after the integer
+ * product.  With D[m,n,g] = Σ_{k in group g} q_x[m,k]·(u[n,k] - z[n,g])
+ * accumulated exactly in int32:
+ *   Y[m, n] = fp16( s_x[m] · Σ_g s_w[n,g] · D[m,n,g] )    (fp32 epilogue)
+ *   Xq [M, K/2] uint8 (signed codes), s_x [M] fp32, Wq [N, K/2] uint8,
+ *   s_w [N, G] fp16, z_w [N, G] fp16 (asymmetric only), Y [M, N] fp16.
+ *   ws: device workspace, w4a4_gemm_workspace_bytes(M, desc). */
+int w4a4_gemm(const uint8_t* Xq, const float* s_x, int32_t M, const w4a4_weight_desc* desc,
+              const uint8_t* Wq, const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Debug / parity form: the exact int32 accumulators D [M, N, G] (row-major,
+ * g fastest) of the same product, before any scaling. */
+int w4a4_gemm_i32(const uint8_t* Xq, int32_t M, const w4a4_weight_desc* desc,
+                  const uint8_t* Wq, const uint16_t* z_w, int32_t* D, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Whole layer                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace w4a4_linear needs. */
+size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2,
+                                   const w4a4_weight_desc* desc);
+
+/* w4a4_transform_quant followed by w4a4_gemm on the same stream, with the
+ * packed activations and their scales kept in `ws`:
+ *   Y [M, N] fp16 = W4A4 linear of X [M, K] fp16 (K = n1*n2 = desc->K). */
+int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                const float* P1, const float* P2, const float* c, float alpha_a,
+                const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H_ */

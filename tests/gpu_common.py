@@ -1,0 +1,108 @@
+"""Shared helpers of the GPU parity tests (inputs, comparisons, tolerances).
+
+Inputs come from the seeded generators in workloads/ and, for the merged
+weights, from the oracle (an oracle result used as a shared input, never the
+other way round).  Nothing here reads a HIP result back into the oracle.
+"""
+import functools
+import sys
+
+import numpy as np
+
+import oracle as O
+import workloads as WL
+
+WINDOW = 1e-4          # tie window for activation codes, in code units
+REL_L2 = 1e-3          # end-to-end fp16 output bound (relative L2)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device")
+    return torch, torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    torch, dev = torch_dev()
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev)
+
+
+def custom_workload(M, n1, n2, N, group_size=None, asym=False, x_kind="normal",
+                    outliers=(), pivot=0.0, seed=0):
+    K = n1 * n2
+    return WL.Workload(name=f"custom_{M}_{n1}x{n2}_{N}", M=M, K=K, N=N, n1=n1, n2=n2,
+                       group_size=group_size or K, asymmetric=asym, x_kind=x_kind,
+                       outlier_channels=tuple(outliers) if outliers else None,
+                       pivot_token_scale=pivot, seed=seed)
+
+
+@functools.lru_cache(maxsize=4)
+def prepared(name_or_wl, M=None):
+    """Inputs and the oracle's merged fp32 weights for a workload (cached)."""
+    inp = WL.make_inputs(name_or_wl, M=M)
+    inp["Wt"] = O.merge_weights(inp["W"], inp["P1"], inp["P2"], inp["c"])
+    return inp
+
+
+def assert_codes_match(gpu_codes, or_codes, t, window=WINDOW, what="codes"):
+    """Bit-exact except where the oracle's t is within `window` of a tie
+    between the two (adjacent) codes.  Returns the number of excused cells."""
+    g = np.asarray(gpu_codes).astype(np.int16)
+    o = np.asarray(or_codes).astype(np.int16)
+    diff = g != o
+    if not diff.any():
+        return 0
+    lo = np.minimum(g, o)
+    excused = (np.abs(g - o) == 1) & (np.abs(t - (lo + 0.5)) < window)
+    bad = diff & ~excused
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        det = [(tuple(i), int(g[tuple(i)]), int(o[tuple(i)]), float(t[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} mismatches outside the tie window, "
+                             f"first (index, gpu, oracle, t): {det}")
+    return int(diff.sum())
+
+
+def ulp16(y):
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def assert_y_close(Y_gpu, Y64, A=None, rel_term=4e-6, what="Y"):
+    """Per element: |Y - Y64| <= ulp16(Y64)/2 + rel_term*A (A = magnitude of
+    the summed terms, defaults to |Y64|); and relative L2 <= REL_L2."""
+    Yg = np.asarray(Y_gpu, dtype=np.float64)
+    A = np.abs(Y64) if A is None else A
+    err = np.abs(Yg - Y64)
+    tol = 0.5 * ulp16(Y64) * (1 + 1e-9) + rel_term * A
+    bad = err > tol
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound, first {i}: "
+                             f"gpu {Yg[i]} oracle {Y64[i]} tol {tol[i]}")
+    rel = np.linalg.norm(Yg - Y64) / max(np.linalg.norm(Y64), 1e-300)
+    assert rel <= REL_L2, f"{what}: relative L2 {rel}"
+    return rel
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def sample_rows(M, k=13, seed=0):
+    rng = np.random.default_rng(seed + 1000)
+    base = {0, 1, M - 1} if M > 2 else set(range(M))
+    extra = set(rng.choice(M, min(k, M), replace=False).tolist()) if M > 0 else set()
+    return np.array(sorted(base | extra), dtype=np.int64)

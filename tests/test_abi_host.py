@@ -1,0 +1,134 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid calls before touching the GPU (no compute
+call is made here; pointers are fake, non-null, and never dereferenced because
+validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a4_post_quantized_amd as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "w4a4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert names == sorted(W.EXPORTED_SYMBOLS)
+    L = ctypes.CDLL(W.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert W.version() == 0x000100
+    L = W.lib()
+    assert L.w4a4_status_str(0) == b"W4A4_OK"
+    assert L.w4a4_status_str(-3) == b"W4A4_ERR_ALIGNMENT"
+    assert L.w4a4_status_str(42) == b"W4A4_ERR_UNKNOWN"
+
+
+def desc(N=256, K=256, g=256, asym=0):
+    return ctypes.byref(W.WeightDesc(N, K, g, asym))
+
+
+def last():
+    return W.lib().w4a4_last_error().decode()
+
+
+def test_gemm_validation():
+    L = W.lib()
+    args = lambda **kw: dict(dict(Xq=FAKE, sx=FAKE, M=16, d=desc(), Wq=FAKE, sw=FAKE, zw=None,
+                                  Y=FAKE, ws=None, wsb=0), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.w4a4_gemm(a["Xq"], a["sx"], a["M"], a["d"], a["Wq"], a["sw"], a["zw"], a["Y"],
+                           a["ws"], a["wsb"], None)
+
+    assert call(Xq=None) == -1 and "Xq" in last()
+    assert call(Y=None) == -1
+    assert call(M=-1) == -1
+    assert call(Xq=MISALIGNED) == -3
+    assert call(d=desc(K=200, g=200)) == -2          # K % 128
+    assert call(d=desc(K=512, g=64)) == -2           # group not multiple of 128
+    assert call(d=desc(K=512, g=384)) == -2          # group does not divide K
+    assert call(d=desc(N=0)) == -1
+    assert call(d=desc(asym=1)) == -1 and "z_w" in last()   # asym needs z_w
+    assert call(d=desc(asym=2)) == -1
+    assert call(d=None) == -1
+    assert call(d=desc(K=131072, g=131072)) == -2
+    assert call(M=0) == 0                             # empty: nothing to do, no launch
+
+
+def test_gemm_i32_validation():
+    L = W.lib()
+    assert L.w4a4_gemm_i32(FAKE, 4, desc(), FAKE, None, None, None) == -1
+    assert L.w4a4_gemm_i32(FAKE, 4, desc(), FAKE, None, MISALIGNED, None) == -3
+
+
+def test_transform_quant_validation():
+    L = W.lib()
+
+    def call(X=FAKE, M=4, n1=16, n2=16, P1=FAKE, P2=FAKE, c=None, a=1.0, Xq=FAKE, sx=FAKE,
+             ws=FAKE, wsb=1 << 30):
+        return L.w4a4_transform_quant(X, M, n1, n2, P1, P2, c, a, Xq, sx, ws, wsb, None)
+
+    assert call(X=None) == -1
+    assert call(P1=None) == -1
+    assert call(n1=0) == -1
+    assert call(n1=300) == -2
+    assert call(n1=3, n2=5) == -2                     # K % 16
+    assert call(a=0.0) == -1 and call(a=1.5) == -1
+    assert call(c=MISALIGNED) == -3
+    need = L.w4a4_transform_quant_workspace_bytes(4, 16, 16)
+    if need:
+        assert call(wsb=need - 1) == -4
+        assert call(ws=None) == -4
+    assert call(M=0, X=None) == 0
+
+
+def test_pack_and_merge_validation():
+    L = W.lib()
+    assert L.w4a4_pack_weights(desc(), None, 1.0, FAKE, FAKE, None, None) == -1
+    assert L.w4a4_pack_weights(desc(asym=1), FAKE, 1.0, FAKE, FAKE, None, None) == -1
+    assert L.w4a4_pack_weights(desc(), FAKE, 0.0, FAKE, FAKE, None, None) == -1
+    assert L.w4a4_pack_weights(desc(K=256, g=3), FAKE, 1.0, FAKE, FAKE, None, None) == -2
+    nb = L.w4a4_merge_workspace_bytes(16, 16, 256)
+    assert nb > 0 and L.w4a4_merge_workspace_bytes(16, 16, 255) == 0
+    assert L.w4a4_merge_weights(FAKE, 8, 256, 16, 16, FAKE, FAKE, None, FAKE, FAKE, nb - 1, None) == -4
+    assert L.w4a4_merge_weights(FAKE, 8, 250, 16, 16, FAKE, FAKE, None, FAKE, FAKE, nb, None) == -1
+    assert L.w4a4_merge_weights(FAKE, 8, 256, 16, 16, FAKE, None, None, FAKE, FAKE, nb, None) == -1
+
+
+def test_linear_validation():
+    L = W.lib()
+    d = desc(N=256, K=256, g=256)
+    nb = L.w4a4_linear_workspace_bytes(16, 16, 16, d)
+    assert nb >= 16 * 128 + 16 * 4
+
+    def call(n1=16, n2=16, ws=FAKE, wsb=nb, d=d, zw=None):
+        return L.w4a4_linear(FAKE, 16, n1, n2, FAKE, FAKE, None, 1.0, d, FAKE, FAKE, zw, FAKE,
+                             ws, wsb, None)
+
+    assert call(n1=8, n2=16) == -1                    # desc K != n1*n2
+    assert call(wsb=nb - 1) == -4
+    assert call(ws=None) == -1
+    assert call(d=desc(N=256, K=256, g=128, asym=1)) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(W, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(W, "_lib", None)
+    with pytest.raises(ImportError):
+        W.lib()

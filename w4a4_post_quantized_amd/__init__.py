@@ -1,0 +1,270 @@
+"""Python binding of libw4a4 — the W4A4 quantized linear layer on MI355X.
+
+Argument marshalling only: every function forwards torch tensors' device
+pointers, sizes and the current HIP stream to the C entry point of the same
+name (include/w4a4.h) and raises W4A4Error on a non-zero status.  PyTorch is
+used for device memory and streams; all arithmetic runs in the HIP kernels of
+libw4a4.so.  There is no fallback: importing the package fails loudly when the
+library has not been built (``python -m w4a4_post_quantized_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "W4A4Error", "WeightDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "merge_weights", "pack_weights", "transform_quant", "transform", "gemm",
+    "gemm_i32", "linear", "merge_workspace_bytes", "transform_quant_workspace_bytes",
+    "gemm_workspace_bytes", "linear_workspace_bytes", "version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so")
+
+# every function include/w4a4.h declares
+EXPORTED_SYMBOLS = [
+    "w4a4_version", "w4a4_status_str", "w4a4_last_error",
+    "w4a4_merge_workspace_bytes", "w4a4_merge_weights", "w4a4_pack_weights",
+    "w4a4_transform_quant_workspace_bytes", "w4a4_transform_quant", "w4a4_transform",
+    "w4a4_gemm_workspace_bytes", "w4a4_gemm", "w4a4_gemm_i32",
+    "w4a4_linear_workspace_bytes", "w4a4_linear",
+]
+
+
+class W4A4Error(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func} failed with {status}: {msg}")
+        self.status = status
+
+
+class WeightDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("asymmetric", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"WeightDesc(N={self.N}, K={self.K}, group_size={self.group_size}, "
+                f"asymmetric={self.asymmetric})")
+
+    @property
+    def groups(self) -> int:
+        return self.K // self.group_size
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libw4a4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m w4a4_post_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        dp = ctypes.POINTER(WeightDesc)
+        sig = {
+            "w4a4_version": (ctypes.c_int, []),
+            "w4a4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+            "w4a4_last_error": (ctypes.c_char_p, []),
+            "w4a4_merge_workspace_bytes": (sz, [i32, i32, i32]),
+            "w4a4_merge_weights": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "w4a4_pack_weights": (ctypes.c_int, [dp, vp, f32, vp, vp, vp, vp]),
+            "w4a4_transform_quant_workspace_bytes": (sz, [i32, i32, i32]),
+            "w4a4_transform_quant": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, sz, vp]),
+            "w4a4_transform": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "w4a4_gemm_workspace_bytes": (sz, [i32, dp]),
+            "w4a4_gemm": (ctypes.c_int, [vp, vp, i32, dp, vp, vp, vp, vp, vp, sz, vp]),
+            "w4a4_gemm_i32": (ctypes.c_int, [vp, i32, dp, vp, vp, vp, vp]),
+            "w4a4_linear_workspace_bytes": (sz, [i32, i32, i32, dp]),
+            "w4a4_linear": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, dp, vp, vp, vp, vp, vp, sz, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().w4a4_version()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _p(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return getattr(stream, "cuda_stream", stream)
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        msg = lib().w4a4_last_error().decode(errors="replace")
+        raise W4A4Error(status, func, msg)
+
+
+def _need(t, dtype, shape, name):
+    torch = _torch()
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous() or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a contiguous CUDA (HIP) tensor")
+    return torch
+
+
+def _ws(nbytes: int, device, ws=None):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _desc(N, K, group_size, asymmetric) -> WeightDesc:
+    return WeightDesc(int(N), int(K), int(group_size), int(bool(asymmetric)))
+
+
+# ---------------------------------------------------------------------------
+# workspace sizes
+# ---------------------------------------------------------------------------
+def merge_workspace_bytes(n1: int, n2: int) -> int:
+    return lib().w4a4_merge_workspace_bytes(n1, n2, n1 * n2)
+
+
+def transform_quant_workspace_bytes(M: int, n1: int, n2: int) -> int:
+    return lib().w4a4_transform_quant_workspace_bytes(M, n1, n2)
+
+
+def gemm_workspace_bytes(M: int, desc: WeightDesc) -> int:
+    return lib().w4a4_gemm_workspace_bytes(M, ctypes.byref(desc))
+
+
+def linear_workspace_bytes(M: int, n1: int, n2: int, desc: WeightDesc) -> int:
+    return lib().w4a4_linear_workspace_bytes(M, n1, n2, ctypes.byref(desc))
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def merge_weights(W, P1, P2, c=None, out=None, stream=None):
+    """W̃ = W · diag(1/c) · (P1 ⊗ P2)^-T on the device (fp32 [N, K])."""
+    torch = _torch()
+    N, K = W.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    _need(W, torch.float32, (N, K), "W")
+    _need(P1, torch.float32, (n1, n1), "P1")
+    _need(P2, torch.float32, (n2, n2), "P2")
+    if c is not None:
+        _need(c, torch.float32, (K,), "c")
+    Wt = out if out is not None else torch.empty_like(W)
+    nb = merge_workspace_bytes(n1, n2)
+    ws = _ws(nb, W.device)
+    _check(lib().w4a4_merge_weights(_p(W), N, K, n1, n2, _p(P1), _p(P2), _p(c), _p(Wt),
+                                    _p(ws), nb, _stream(stream)), "w4a4_merge_weights")
+    return Wt
+
+
+def pack_weights(Wt, group_size: int, asymmetric: bool, alpha_w: float = 1.0, stream=None):
+    """Quantize merged weights: returns (desc, Wq uint8 [N,K/2], s_w fp16 [N,G],
+    z_w fp16 [N,G] or None)."""
+    torch = _torch()
+    N, K = Wt.shape
+    _need(Wt, torch.float32, (N, K), "Wt")
+    desc = _desc(N, K, group_size, asymmetric)
+    G = K // group_size if group_size > 0 else 0
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=Wt.device)
+    s_w = torch.empty((N, max(G, 1)), dtype=torch.float16, device=Wt.device)
+    z_w = torch.empty((N, max(G, 1)), dtype=torch.float16, device=Wt.device) if asymmetric else None
+    _check(lib().w4a4_pack_weights(ctypes.byref(desc), _p(Wt), float(alpha_w), _p(Wq), _p(s_w),
+                                   _p(z_w), _stream(stream)), "w4a4_pack_weights")
+    return desc, Wq, s_w, z_w
+
+
+def transform_quant(X, P1, P2, c=None, alpha_a: float = 1.0, out=None, ws=None, stream=None):
+    """Fused transform + per-token INT4 quantization: returns (Xq [M,K/2], s_x [M])."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    _need(X, torch.float16, (M, K), "X")
+    _need(P1, torch.float32, (n1, n1), "P1")
+    _need(P2, torch.float32, (n2, n2), "P2")
+    if c is not None:
+        _need(c, torch.float32, (K,), "c")
+    if out is None:
+        Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+        s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
+    else:
+        Xq, s_x = out
+    nb = transform_quant_workspace_bytes(M, n1, n2)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_transform_quant(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
+                                      _p(Xq), _p(s_x), _p(ws), nb if ws is None else ws.numel(),
+                                      _stream(stream)), "w4a4_transform_quant")
+    return Xq, s_x
+
+
+def transform(X, P1, P2, c=None, stream=None):
+    """Debug form: the fp32 transformed activations Z [M, K]."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    _need(X, torch.float16, (M, K), "X")
+    Z = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    nb = transform_quant_workspace_bytes(M, n1, n2)
+    ws = _ws(nb, X.device)
+    _check(lib().w4a4_transform(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), _p(Z), _p(ws), nb,
+                                _stream(stream)), "w4a4_transform")
+    return Z
+
+
+def gemm(Xq, s_x, desc: WeightDesc, Wq, s_w, z_w=None, out=None, ws=None, stream=None):
+    """Y [M, N] fp16 = dequant(Xq · Wq^T)."""
+    torch = _torch()
+    M = Xq.shape[0]
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=Xq.device)
+    nb = gemm_workspace_bytes(M, desc)
+    ws = _ws(nb, Xq.device, ws)
+    _check(lib().w4a4_gemm(_p(Xq), _p(s_x), M, ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y),
+                           _p(ws), nb if ws is None else ws.numel(), _stream(stream)), "w4a4_gemm")
+    return Y
+
+
+def gemm_i32(Xq, desc: WeightDesc, Wq, z_w=None, stream=None):
+    """Exact int32 accumulators D [M, N, G]."""
+    torch = _torch()
+    M = Xq.shape[0]
+    D = torch.empty((M, desc.N, desc.groups), dtype=torch.int32, device=Xq.device)
+    _check(lib().w4a4_gemm_i32(_p(Xq), M, ctypes.byref(desc), _p(Wq), _p(z_w), _p(D),
+                               _stream(stream)), "w4a4_gemm_i32")
+    return D
+
+
+def linear(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, c=None, alpha_a: float = 1.0,
+           out=None, ws=None, stream=None):
+    """Whole W4A4 layer: Y [M, N] fp16."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=X.device)
+    nb = linear_workspace_bytes(M, n1, n2, desc)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_linear(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
+                             ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y), _p(ws),
+                             nb if ws is None else ws.numel(), _stream(stream)), "w4a4_linear")
+    return Y

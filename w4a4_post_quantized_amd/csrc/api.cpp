@@ -1,0 +1,334 @@
+// C ABI of libw4a4: argument validation, status codes, workspace sizing and
+// dispatch to the kernel launchers.  Validation happens entirely on the host
+// before any HIP call, so an invalid call launches nothing and writes no
+// output.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+#include "w4a4.h"
+
+namespace {
+
+thread_local char g_last_error[512] = {0};
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return W4A4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(W4A4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, status, ...)                   \
+    do {                                             \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr, W4A4_ERR_INVALID_ARG, "%s is NULL", #p)
+#define REQUIRE_ALIGNED(p) \
+    REQUIRE(aligned16(p), W4A4_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p)
+
+int check_factors(int32_t M, int32_t n1, int32_t n2) {
+    REQUIRE(M >= 0, W4A4_ERR_INVALID_ARG, "M = %d is negative", M);
+    REQUIRE(n1 >= 1 && n2 >= 1, W4A4_ERR_INVALID_ARG, "n1 = %d, n2 = %d must be >= 1", n1, n2);
+    REQUIRE(n1 <= W4A4_MAX_FACTOR && n2 <= W4A4_MAX_FACTOR, W4A4_ERR_UNSUPPORTED,
+            "n1 = %d, n2 = %d exceed %d", n1, n2, W4A4_MAX_FACTOR);
+    const int64_t K = static_cast<int64_t>(n1) * n2;
+    REQUIRE(K <= W4A4_MAX_K, W4A4_ERR_UNSUPPORTED, "K = n1*n2 = %lld exceeds %d",
+            static_cast<long long>(K), W4A4_MAX_K);
+    REQUIRE(K % 16 == 0, W4A4_ERR_UNSUPPORTED, "K = n1*n2 = %lld is not a multiple of 16",
+            static_cast<long long>(K));
+    return W4A4_OK;
+}
+
+int check_desc(const w4a4_weight_desc* d, bool for_gemm) {
+    REQUIRE(d != nullptr, W4A4_ERR_INVALID_ARG, "desc is NULL");
+    REQUIRE(d->N >= 1, W4A4_ERR_INVALID_ARG, "N = %d must be >= 1", d->N);
+    REQUIRE(d->K >= 1, W4A4_ERR_INVALID_ARG, "K = %d must be >= 1", d->K);
+    REQUIRE(d->K <= W4A4_MAX_K, W4A4_ERR_UNSUPPORTED, "K = %d exceeds %d", d->K, W4A4_MAX_K);
+    REQUIRE(d->K % 2 == 0, W4A4_ERR_UNSUPPORTED, "K = %d is odd", d->K);
+    REQUIRE(d->asymmetric == 0 || d->asymmetric == 1, W4A4_ERR_INVALID_ARG,
+            "asymmetric = %d must be 0 or 1", d->asymmetric);
+    REQUIRE(d->group_size >= 1 && d->K % d->group_size == 0, W4A4_ERR_UNSUPPORTED,
+            "group_size = %d does not divide K = %d", d->group_size, d->K);
+    if (for_gemm) {
+        REQUIRE(d->K % 128 == 0, W4A4_ERR_UNSUPPORTED, "GEMM needs K %% 128 == 0 (K = %d)", d->K);
+        REQUIRE(d->group_size == d->K || d->group_size % 128 == 0, W4A4_ERR_UNSUPPORTED,
+                "GEMM needs group_size == K or a multiple of 128 (group_size = %d)",
+                d->group_size);
+    } else {
+        REQUIRE(d->group_size % 2 == 0, W4A4_ERR_UNSUPPORTED, "group_size = %d is odd",
+                d->group_size);
+    }
+    return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a4_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* w4a4_status_str(int status) {
+    switch (status) {
+        case W4A4_OK: return "W4A4_OK";
+        case W4A4_ERR_INVALID_ARG: return "W4A4_ERR_INVALID_ARG";
+        case W4A4_ERR_UNSUPPORTED: return "W4A4_ERR_UNSUPPORTED";
+        case W4A4_ERR_ALIGNMENT: return "W4A4_ERR_ALIGNMENT";
+        case W4A4_ERR_WORKSPACE: return "W4A4_ERR_WORKSPACE";
+        case W4A4_ERR_HIP: return "W4A4_ERR_HIP";
+        default: return "W4A4_ERR_UNKNOWN";
+    }
+}
+
+const char* w4a4_last_error(void) { return g_last_error; }
+
+// ---------------------------------------------------------------------------
+size_t w4a4_merge_workspace_bytes(int32_t n1, int32_t n2, int32_t K) {
+    if (n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR || n2 > W4A4_MAX_FACTOR) return 0;
+    if (K != n1 * n2) return 0;
+    return w4a4::merge_workspace_bytes(n1, n2, K);
+}
+
+int w4a4_merge_weights(const float* W, int32_t N, int32_t K, int32_t n1, int32_t n2,
+                       const float* P1, const float* P2, const float* c, float* Wt, void* ws,
+                       size_t ws_bytes, void* stream) {
+    REQUIRE(N >= 1, W4A4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
+    if (int s = check_factors(0, n1, n2)) return s;
+    REQUIRE(K == n1 * n2, W4A4_ERR_INVALID_ARG, "K = %d != n1*n2 = %d", K, n1 * n2);
+    REQUIRE_PTR(W);
+    REQUIRE_PTR(P1);
+    REQUIRE_PTR(P2);
+    REQUIRE_PTR(Wt);
+    REQUIRE_PTR(ws);
+    REQUIRE_ALIGNED(W);
+    REQUIRE_ALIGNED(P1);
+    REQUIRE_ALIGNED(P2);
+    REQUIRE_ALIGNED(Wt);
+    REQUIRE_ALIGNED(ws);
+    if (c) REQUIRE_ALIGNED(c);
+    const size_t need = w4a4::merge_workspace_bytes(n1, n2, K);
+    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    bool singular = false;
+    hipError_t e = w4a4::merge_launch(W, N, K, n1, n2, P1, P2, c, Wt, ws,
+                                      static_cast<hipStream_t>(stream), &singular);
+    if (e != hipSuccess) return hip_status(e, "w4a4_merge_weights");
+    REQUIRE(!singular, W4A4_ERR_INVALID_ARG, "P1 or P2 is singular");
+    return ok();
+}
+
+int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha_w,
+                      uint8_t* Wq, uint16_t* s_w, uint16_t* z_w, void* stream) {
+    if (int s = check_desc(desc, false)) return s;
+    REQUIRE(alpha_w > 0.0f && alpha_w <= 1.0f, W4A4_ERR_INVALID_ARG,
+            "alpha_w = %g must lie in (0, 1]", static_cast<double>(alpha_w));
+    REQUIRE_PTR(Wt);
+    REQUIRE_PTR(Wq);
+    REQUIRE_PTR(s_w);
+    if (desc->asymmetric) REQUIRE_PTR(z_w);
+    REQUIRE_ALIGNED(Wt);
+    REQUIRE_ALIGNED(Wq);
+    REQUIRE_ALIGNED(s_w);
+    if (desc->asymmetric) REQUIRE_ALIGNED(z_w);
+    hipError_t e = w4a4::pack_weights_launch(Wt, desc->N, desc->K, desc->group_size,
+                                             desc->asymmetric != 0, alpha_w, Wq, s_w, z_w,
+                                             static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_pack_weights");
+}
+
+// ---------------------------------------------------------------------------
+size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2) {
+    if (M < 0 || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR || n2 > W4A4_MAX_FACTOR) return 0;
+    return w4a4::tq_workspace_bytes(M, n1, n2);
+}
+
+static int tq_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                     const float* P2, const float* c, float alpha_a, bool quantize,
+                     uint8_t* Xq, float* s_x, float* Z, void* ws, size_t ws_bytes,
+                     void* stream, const char* name) {
+    if (int s = check_factors(M, n1, n2)) return s;
+    REQUIRE(alpha_a > 0.0f && alpha_a <= 1.0f, W4A4_ERR_INVALID_ARG,
+            "alpha_a = %g must lie in (0, 1]", static_cast<double>(alpha_a));
+    if (M == 0) return ok();
+    REQUIRE_PTR(X);
+    REQUIRE_PTR(P1);
+    REQUIRE_PTR(P2);
+    REQUIRE_ALIGNED(X);
+    REQUIRE_ALIGNED(P1);
+    REQUIRE_ALIGNED(P2);
+    if (c) REQUIRE_ALIGNED(c);
+    if (quantize) {
+        REQUIRE_PTR(Xq);
+        REQUIRE_PTR(s_x);
+        REQUIRE_ALIGNED(Xq);
+        REQUIRE_ALIGNED(s_x);
+    } else {
+        REQUIRE_PTR(Z);
+        REQUIRE_ALIGNED(Z);
+    }
+    const size_t need = w4a4::tq_workspace_bytes(M, n1, n2);
+    if (need) {
+        REQUIRE(ws != nullptr && ws_bytes >= need, W4A4_ERR_WORKSPACE,
+                "workspace %zu < %zu bytes", ws ? ws_bytes : 0, need);
+        REQUIRE_ALIGNED(ws);
+    }
+    hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, alpha_a, quantize, Xq, s_x, Z, ws,
+                                   ws_bytes, static_cast<hipStream_t>(stream));
+    return hip_status(e, name);
+}
+
+int w4a4_transform_quant(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                         const float* P1, const float* P2, const float* c, float alpha_a,
+                         uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes, void* stream) {
+    return tq_common(X, M, n1, n2, P1, P2, c, alpha_a, true, Xq, s_x, nullptr, ws, ws_bytes,
+                     stream, "w4a4_transform_quant");
+}
+
+int w4a4_transform(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                   const float* P2, const float* c, float* Z, void* ws, size_t ws_bytes,
+                   void* stream) {
+    return tq_common(X, M, n1, n2, P1, P2, c, 1.0f, false, nullptr, nullptr, Z, ws, ws_bytes,
+                     stream, "w4a4_transform");
+}
+
+// ---------------------------------------------------------------------------
+size_t w4a4_gemm_workspace_bytes(int32_t M, const w4a4_weight_desc* desc) {
+    if (M < 0 || desc == nullptr || desc->K < 1 || desc->group_size < 1) return 0;
+    return w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size);
+}
+
+static int gemm_common(const uint8_t* Xq, const float* s_x, int32_t M,
+                       const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                       const uint16_t* z_w, uint16_t* Y, int32_t* D, void* ws,
+                       size_t ws_bytes, void* stream, const char* name) {
+    if (int s = check_desc(desc, true)) return s;
+    REQUIRE(M >= 0, W4A4_ERR_INVALID_ARG, "M = %d is negative", M);
+    if (M == 0) return ok();
+    const bool i32 = (D != nullptr);
+    REQUIRE_PTR(Xq);
+    REQUIRE_PTR(Wq);
+    REQUIRE_ALIGNED(Xq);
+    REQUIRE_ALIGNED(Wq);
+    if (desc->asymmetric) {
+        REQUIRE_PTR(z_w);
+        REQUIRE_ALIGNED(z_w);
+    }
+    if (!i32) {
+        REQUIRE_PTR(s_x);
+        REQUIRE_PTR(s_w);
+        REQUIRE_PTR(Y);
+        REQUIRE_ALIGNED(s_x);
+        REQUIRE_ALIGNED(s_w);
+        REQUIRE_ALIGNED(Y);
+        const size_t need =
+            w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size);
+        if (need) {
+            REQUIRE(ws != nullptr && ws_bytes >= need, W4A4_ERR_WORKSPACE,
+                    "workspace %zu < %zu bytes", ws ? ws_bytes : 0, need);
+            REQUIRE_ALIGNED(ws);
+        }
+    } else {
+        REQUIRE_ALIGNED(D);
+    }
+    w4a4::GemmArgs a{Xq, s_x, Wq, s_w, z_w, Y, D, M, desc->N, desc->K, desc->group_size,
+                     desc->asymmetric != 0};
+    hipError_t e = w4a4::gemm_launch(a, i32, ws, ws_bytes, static_cast<hipStream_t>(stream));
+    return hip_status(e, name);
+}
+
+int w4a4_gemm(const uint8_t* Xq, const float* s_x, int32_t M, const w4a4_weight_desc* desc,
+              const uint8_t* Wq, const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y,
+              void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE_PTR(Y);
+    return gemm_common(Xq, s_x, M, desc, Wq, s_w, z_w, Y, nullptr, ws, ws_bytes, stream,
+                       "w4a4_gemm");
+}
+
+int w4a4_gemm_i32(const uint8_t* Xq, int32_t M, const w4a4_weight_desc* desc,
+                  const uint8_t* Wq, const uint16_t* z_w, int32_t* D, void* stream) {
+    REQUIRE_PTR(D);
+    return gemm_common(Xq, nullptr, M, desc, Wq, nullptr, z_w, nullptr, D, nullptr, 0, stream,
+                       "w4a4_gemm_i32");
+}
+
+// ---------------------------------------------------------------------------
+static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2,
+                                   const w4a4_weight_desc* desc) {
+    if (M < 0 || desc == nullptr || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR ||
+        n2 > W4A4_MAX_FACTOR || desc->K < 1 || desc->group_size < 1)
+        return 0;
+    const size_t K = static_cast<size_t>(n1) * n2;
+    const size_t tq = w4a4::tq_workspace_bytes(M, n1, n2);
+    const size_t gm = w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size);
+    return align256(K / 2 * M) + align256(sizeof(float) * M) + (tq > gm ? tq : gm);
+}
+
+int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                const float* P2, const float* c, float alpha_a, const w4a4_weight_desc* desc,
+                const uint8_t* Wq, const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y,
+                void* ws, size_t ws_bytes, void* stream) {
+    if (int s = check_desc(desc, true)) return s;
+    if (int s = check_factors(M, n1, n2)) return s;
+    REQUIRE(desc->K == n1 * n2, W4A4_ERR_INVALID_ARG, "desc->K = %d != n1*n2 = %d", desc->K,
+            n1 * n2);
+    REQUIRE(alpha_a > 0.0f && alpha_a <= 1.0f, W4A4_ERR_INVALID_ARG,
+            "alpha_a = %g must lie in (0, 1]", static_cast<double>(alpha_a));
+    if (M == 0) return ok();
+    REQUIRE_PTR(X);
+    REQUIRE_PTR(P1);
+    REQUIRE_PTR(P2);
+    REQUIRE_PTR(Wq);
+    REQUIRE_PTR(s_w);
+    REQUIRE_PTR(Y);
+    if (desc->asymmetric) REQUIRE_PTR(z_w);
+    REQUIRE_PTR(ws);
+    REQUIRE_ALIGNED(X);
+    REQUIRE_ALIGNED(P1);
+    REQUIRE_ALIGNED(P2);
+    if (c) REQUIRE_ALIGNED(c);
+    REQUIRE_ALIGNED(Wq);
+    REQUIRE_ALIGNED(s_w);
+    if (desc->asymmetric) REQUIRE_ALIGNED(z_w);
+    REQUIRE_ALIGNED(Y);
+    REQUIRE_ALIGNED(ws);
+    const size_t need = w4a4_linear_workspace_bytes(M, n1, n2, desc);
+    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+
+    const size_t K = static_cast<size_t>(n1) * n2;
+    char* p = static_cast<char*>(ws);
+    uint8_t* Xq = reinterpret_cast<uint8_t*>(p);
+    p += align256(K / 2 * M);
+    float* s_x = reinterpret_cast<float*>(p);
+    p += align256(sizeof(float) * M);
+    void* sub = p;
+    const size_t sub_bytes = ws_bytes - static_cast<size_t>(p - static_cast<char*>(ws));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, alpha_a, true, Xq, s_x, nullptr,
+                                   sub, sub_bytes, st);
+    if (e != hipSuccess) return hip_status(e, "w4a4_linear (transform_quant)");
+    w4a4::GemmArgs a{Xq, s_x, Wq, s_w, z_w, Y, nullptr, M, desc->N, desc->K, desc->group_size,
+                     desc->asymmetric != 0};
+    e = w4a4::gemm_launch(a, false, sub, sub_bytes, st);
+    return hip_status(e, "w4a4_linear (gemm)");
+}
+
+}  // extern "C"
