@@ -229,7 +229,9 @@ def quantize_weights(Wt, group_size: int, asymmetric: bool, alpha_w: float = 1.0
         s16 = fp16_rne((hi - lo) / 15.0)
         s = s16.astype(np.float64)
         safe = np.where(s > 0, s, 1.0)
-        z = np.clip(np.rint(-lo / safe), 0, UMAX)
+        # z is an integer in [0, 15]; adding +0.0 turns the -0.0 that
+        # rint(-0/s) gives for an all-positive group into the integer 0
+        z = np.clip(np.rint(-lo / safe), 0, UMAX) + 0.0
         z = np.where(s > 0, z, 0.0)
         q = np.clip(np.rint(Vg / safe[:, :, None]) + z[:, :, None], 0, UMAX)
         q = np.where((s > 0)[:, :, None], q, 0)

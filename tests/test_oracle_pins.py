@@ -278,6 +278,7 @@ def test_asym_all_positive_group_has_zero_point_zero():
     W = np.linspace(0.01, 0.3, 8, dtype=np.float32)[None, :]
     wq = O.quantize_weights(W, 8, True)
     assert float(wq["z"][0, 0]) == 0.0 and wq["codes"][0, -1] == 15
+    assert wq["z"].view(np.uint16)[0, 0] == 0          # the integer 0, not -0.0
 
 
 # ---------------------------------------------------------------------------
