@@ -95,6 +95,25 @@ def assert_y_close(Y_gpu, Y64, A=None, rel_term=4e-6, what="Y"):
     return rel
 
 
+def assert_linear_close(Y_gpu, Y64, A, flips, what="linear", per_flip=0.02):
+    """Whole-layer check on a [rows, cols] sample.
+
+    Rows whose activation codes equal the oracle's get the tight per-element
+    bound of assert_y_close.  A row with f codes flipped at a rounding tie
+    (allowed by the 1e-4 window) differs by f changed codes times that row's
+    weights; it must stay within relative L2 per_flip * f."""
+    flips = np.asarray(flips)
+    exact = flips == 0
+    if exact.any():
+        assert_y_close(Y_gpu[exact], Y64[exact], A[exact], what=what + " (rows with equal codes)")
+    worst = 0.0
+    for r in np.nonzero(~exact)[0]:
+        e = rel_l2(Y_gpu[r], Y64[r])
+        worst = max(worst, e / flips[r])
+        assert e <= per_flip * flips[r], f"{what}: row {r} with {flips[r]} tie flips, rel L2 {e}"
+    return int((~exact).sum()), worst
+
+
 def rel_l2(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

@@ -9,15 +9,17 @@ test_gpu_parity.py); every other input is the workload's own.  Per workload:
   * int32 accumulators of sampled tokens, all channels and groups: bit-exact
     (sampled channels compared with the oracle);
   * fp16 GEMM output given the oracle's codes: per-element bound on samples;
-  * whole layer: relative L2 <= 1e-3 on sampled tokens x channels.
+  * whole layer on sampled tokens x channels: tokens whose codes equal the
+    oracle's within the per-element bound, tokens with tie flips within a
+    per-flip relative L2 bound.
 """
 import numpy as np
 import pytest
 
 import oracle as O
 import workloads as WL
-from gpu_common import (assert_codes_match, assert_y_close, log, rel_l2, sample_rows, to_dev,
-                        torch_dev)
+from gpu_common import (assert_codes_match, assert_linear_close, assert_y_close, log, rel_l2,
+                        sample_rows, to_dev, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,8 +85,14 @@ def test_full_size(name):
     A = O.epilogue(np.abs(D_or), sx32[rows], wq_s["s"])
     assert_y_close(Yg, Y64, A, what=f"{name} gemm")
 
-    # whole layer end to end (oracle codes vs library codes may differ at ties)
+    # whole layer end to end: library codes may differ from the oracle's at
+    # rounding ties (level 1 window); rows without such flips are held to the
+    # tight per-element bound, the others to a per-flip bound
+    gq = O.unpack_nibbles(take(Xq, rows), True)
+    flips = (gq != act["q"][rows]).sum(axis=1)
     ref = O.epilogue(D_or, act["s_x"][rows], wq_s["s"])
-    rel = rel_l2(take(Y, rows, cols), ref)
-    log(f"[{name}] linear relative L2 on samples {rel:.2e}")
-    assert rel <= 1e-3
+    A_ref = O.epilogue(np.abs(D_or), act["s_x"][rows], wq_s["s"])
+    Ys = take(Y, rows, cols)
+    nflip, worst = assert_linear_close(Ys, ref, A_ref, flips, what=f"{name} linear")
+    log(f"[{name}] linear relative L2 on samples {rel_l2(Ys, ref):.2e}; "
+        f"rows with tie flips {nflip}/{len(rows)} (worst {worst:.2e} per flip)")

@@ -4,8 +4,10 @@ Levels (for every step of the layer):
   1. packed activation codes bit-exact except within 1e-4 of a rounding tie;
      weight codes, scales and zero points bit-exact;
   2. given the oracle's codes, the int32 accumulators bit-exact;
-  3. fp16 output within half an fp16 ulp plus fp32 epilogue rounding per
-     element, and relative L2 <= 1e-3 end to end.
+  3. given the same codes, fp16 output within half an fp16 ulp plus fp32
+     epilogue rounding per element and relative L2 <= 1e-3; end to end the
+     same bound on tokens whose codes equal the oracle's, and a per-flip
+     bound on tokens with a code flipped at a rounding tie.
 Shapes span several tiles with ragged tails, the edge cases (empty, one
 token, all-zero token, all-zero weight row, clipping, diag(c), every group
 mode) and every (n1, n2) pair of the LLaMA-shaped workloads.
@@ -15,8 +17,8 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from gpu_common import (assert_codes_match, assert_y_close, custom_workload, log, prepared,
-                        rel_l2, to_dev, torch_dev)
+from gpu_common import (assert_codes_match, assert_linear_close, assert_y_close, custom_workload,
+                        log, prepared, rel_l2, to_dev, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -259,11 +261,15 @@ def _layer_parity(inp, c=None, alpha=1.0):
     ref = O.linear(inp["X"], inp["P1"], inp["P2"], wq, c=c, alpha_a=alpha)
     desc, Wq, sw, zw = W().pack_weights(to_dev(inp["Wt"]), wl.group_size, wl.asymmetric)
     assert np.array_equal(Wq.cpu().numpy(), wq["packed"])
+    cd = None if c is None else to_dev(c)
     Y = W().linear(to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"]), desc, Wq, sw, zw,
-                   c=None if c is None else to_dev(c), alpha_a=alpha).cpu().numpy()
+                   c=cd, alpha_a=alpha).cpu().numpy()
+    Xq, _ = W().transform_quant(to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"]), cd, alpha)
+    flips = (O.unpack_nibbles(Xq.cpu().numpy(), True) != ref["act"]["q"]).sum(axis=1)
+    A = O.epilogue(np.abs(ref["D"]), ref["act"]["s_x"], wq["s"])
+    assert_linear_close(Y.astype(np.float64), ref["Y64"], A, flips)
     rel = rel_l2(Y, ref["Y64"])
-    log(f"  linear relative L2 {rel:.2e}")
-    assert rel <= 1e-3
+    log(f"  linear relative L2 {rel:.2e}, rows with tie flips {int((flips > 0).sum())}")
     return Y, ref
 
 
