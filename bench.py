@@ -140,7 +140,7 @@ def main():
                      device=dev)
     Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     sx = torch.empty((M,), dtype=torch.float32, device=dev)
-    tq_ws = torch.empty(max(1, L.transform_quant_workspace_bytes(M, wl.n1, wl.n2)),
+    tq_ws = torch.empty(max(1, L.transform_quant_workspace_bytes(M, wl.n1, wl.n2, False)),
                         dtype=torch.uint8, device=dev)
     g_ws = torch.empty(max(1, L.gemm_workspace_bytes(M, desc)), dtype=torch.uint8, device=dev)
 

@@ -124,8 +124,11 @@ int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha
 /* Online activation path                                                    */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace w4a4_transform_quant needs (0 is possible). */
-size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2);
+/* Bytes of workspace w4a4_transform_quant needs (0 is possible); has_c != 0
+ * when the call passes a channel scale c.  Without c the common factor
+ * shapes (n1 <= 128 and n2 in {16, 32, 64, 128}, both multiples of 16) run
+ * one fused kernel and need no workspace. */
+size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t has_c);
 
 /* Fused activation transform + per-token INT4 quantization + packing.
  * FlatQuant page, section Kronecker 分解 (activation factor P1^T ×1 X̃ ×2 P2)
@@ -138,7 +141,8 @@ size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2);
  *   Xq[m, :] = packed q.
  *   X [M, K] fp16, P1 [n1, n1] fp32 (P in P = P1 ⊗ P2, NOT its transpose),
  *   P2 [n2, n2] fp32, c [K] fp32 or NULL, Xq [M, K/2] uint8, s_x [M] fp32.
- *   ws: device workspace, w4a4_transform_quant_workspace_bytes(M, n1, n2). */
+ *   ws: device workspace, w4a4_transform_quant_workspace_bytes(M, n1, n2,
+ *       c != NULL) bytes (may be NULL when that is 0). */
 int w4a4_transform_quant(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                          const float* P1, const float* P2, const float* c, float alpha_a,
                          uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes, void* stream);
@@ -179,8 +183,8 @@ int w4a4_gemm_i32(const uint8_t* Xq, int32_t M, const w4a4_weight_desc* desc,
 /* Whole layer                                                               */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace w4a4_linear needs. */
-size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2,
+/* Bytes of workspace w4a4_linear needs (has_c as for transform_quant). */
+size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t has_c,
                                    const w4a4_weight_desc* desc);
 
 /* w4a4_transform_quant followed by w4a4_gemm on the same stream, with the

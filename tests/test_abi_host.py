@@ -90,10 +90,12 @@ def test_transform_quant_validation():
     assert call(n1=3, n2=5) == -2                     # K % 16
     assert call(a=0.0) == -1 and call(a=1.5) == -1
     assert call(c=MISALIGNED) == -3
-    need = L.w4a4_transform_quant_workspace_bytes(4, 16, 16)
-    if need:
-        assert call(wsb=need - 1) == -4
-        assert call(ws=None) == -4
+    need = L.w4a4_transform_quant_workspace_bytes(4, 16, 16, 1)
+    assert need > 0
+    assert call(c=FAKE, wsb=need - 1) == -4
+    assert call(c=FAKE, ws=None) == -4
+    # without c the (16, 16) shape runs fused and needs no workspace
+    assert L.w4a4_transform_quant_workspace_bytes(4, 16, 16, 0) == 0
     assert call(M=0, X=None) == 0
 
 
@@ -113,7 +115,7 @@ def test_pack_and_merge_validation():
 def test_linear_validation():
     L = W.lib()
     d = desc(N=256, K=256, g=256)
-    nb = L.w4a4_linear_workspace_bytes(16, 16, 16, d)
+    nb = L.w4a4_linear_workspace_bytes(16, 16, 16, 0, d)
     assert nb >= 16 * 128 + 16 * 4
 
     def call(n1=16, n2=16, ws=FAKE, wsb=nb, d=d, zw=None):

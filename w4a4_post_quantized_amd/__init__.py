@@ -71,13 +71,13 @@ def lib() -> ctypes.CDLL:
             "w4a4_merge_workspace_bytes": (sz, [i32, i32, i32]),
             "w4a4_merge_weights": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "w4a4_pack_weights": (ctypes.c_int, [dp, vp, f32, vp, vp, vp, vp]),
-            "w4a4_transform_quant_workspace_bytes": (sz, [i32, i32, i32]),
+            "w4a4_transform_quant_workspace_bytes": (sz, [i32, i32, i32, i32]),
             "w4a4_transform_quant": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, sz, vp]),
             "w4a4_transform": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "w4a4_gemm_workspace_bytes": (sz, [i32, dp]),
             "w4a4_gemm": (ctypes.c_int, [vp, vp, i32, dp, vp, vp, vp, vp, vp, sz, vp]),
             "w4a4_gemm_i32": (ctypes.c_int, [vp, i32, dp, vp, vp, vp, vp]),
-            "w4a4_linear_workspace_bytes": (sz, [i32, i32, i32, dp]),
+            "w4a4_linear_workspace_bytes": (sz, [i32, i32, i32, i32, dp]),
             "w4a4_linear": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, dp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
@@ -147,16 +147,16 @@ def merge_workspace_bytes(n1: int, n2: int) -> int:
     return lib().w4a4_merge_workspace_bytes(n1, n2, n1 * n2)
 
 
-def transform_quant_workspace_bytes(M: int, n1: int, n2: int) -> int:
-    return lib().w4a4_transform_quant_workspace_bytes(M, n1, n2)
+def transform_quant_workspace_bytes(M: int, n1: int, n2: int, has_c: bool = False) -> int:
+    return lib().w4a4_transform_quant_workspace_bytes(M, n1, n2, int(bool(has_c)))
 
 
 def gemm_workspace_bytes(M: int, desc: WeightDesc) -> int:
     return lib().w4a4_gemm_workspace_bytes(M, ctypes.byref(desc))
 
 
-def linear_workspace_bytes(M: int, n1: int, n2: int, desc: WeightDesc) -> int:
-    return lib().w4a4_linear_workspace_bytes(M, n1, n2, ctypes.byref(desc))
+def linear_workspace_bytes(M: int, n1: int, n2: int, desc: WeightDesc, has_c: bool = False) -> int:
+    return lib().w4a4_linear_workspace_bytes(M, n1, n2, int(bool(has_c)), ctypes.byref(desc))
 
 
 # ---------------------------------------------------------------------------
@@ -211,7 +211,7 @@ def transform_quant(X, P1, P2, c=None, alpha_a: float = 1.0, out=None, ws=None, 
         s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
     else:
         Xq, s_x = out
-    nb = transform_quant_workspace_bytes(M, n1, n2)
+    nb = transform_quant_workspace_bytes(M, n1, n2, c is not None)
     ws = _ws(nb, X.device, ws)
     _check(lib().w4a4_transform_quant(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
                                       _p(Xq), _p(s_x), _p(ws), nb if ws is None else ws.numel(),
@@ -226,7 +226,7 @@ def transform(X, P1, P2, c=None, stream=None):
     n1, n2 = P1.shape[0], P2.shape[0]
     _need(X, torch.float16, (M, K), "X")
     Z = torch.empty((M, K), dtype=torch.float32, device=X.device)
-    nb = transform_quant_workspace_bytes(M, n1, n2)
+    nb = transform_quant_workspace_bytes(M, n1, n2, c is not None)
     ws = _ws(nb, X.device)
     _check(lib().w4a4_transform(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), _p(Z), _p(ws), nb,
                                 _stream(stream)), "w4a4_transform")
@@ -262,7 +262,7 @@ def linear(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, c=None, alpha_a: floa
     M, K = X.shape
     n1, n2 = P1.shape[0], P2.shape[0]
     Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=X.device)
-    nb = linear_workspace_bytes(M, n1, n2, desc)
+    nb = linear_workspace_bytes(M, n1, n2, desc, c is not None)
     ws = _ws(nb, X.device, ws)
     _check(lib().w4a4_linear(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
                              ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y), _p(ws),

@@ -153,9 +153,9 @@ int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha
 }
 
 // ---------------------------------------------------------------------------
-size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2) {
+size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t has_c) {
     if (M < 0 || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR || n2 > W4A4_MAX_FACTOR) return 0;
-    return w4a4::tq_workspace_bytes(M, n1, n2);
+    return w4a4::tq_workspace_bytes(M, n1, n2, has_c != 0);
 }
 
 static int tq_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
@@ -182,7 +182,7 @@ static int tq_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const
         REQUIRE_PTR(Z);
         REQUIRE_ALIGNED(Z);
     }
-    const size_t need = w4a4::tq_workspace_bytes(M, n1, n2);
+    const size_t need = w4a4::tq_workspace_bytes(M, n1, n2, c != nullptr);
     if (need) {
         REQUIRE(ws != nullptr && ws_bytes >= need, W4A4_ERR_WORKSPACE,
                 "workspace %zu < %zu bytes", ws ? ws_bytes : 0, need);
@@ -270,13 +270,13 @@ int w4a4_gemm_i32(const uint8_t* Xq, int32_t M, const w4a4_weight_desc* desc,
 // ---------------------------------------------------------------------------
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2,
+size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t has_c,
                                    const w4a4_weight_desc* desc) {
     if (M < 0 || desc == nullptr || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR ||
         n2 > W4A4_MAX_FACTOR || desc->K < 1 || desc->group_size < 1)
         return 0;
     const size_t K = static_cast<size_t>(n1) * n2;
-    const size_t tq = w4a4::tq_workspace_bytes(M, n1, n2);
+    const size_t tq = w4a4::tq_workspace_bytes(M, n1, n2, has_c != 0);
     const size_t gm = w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size);
     return align256(K / 2 * M) + align256(sizeof(float) * M) + (tq > gm ? tq : gm);
 }
@@ -309,7 +309,7 @@ int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const floa
     if (desc->asymmetric) REQUIRE_ALIGNED(z_w);
     REQUIRE_ALIGNED(Y);
     REQUIRE_ALIGNED(ws);
-    const size_t need = w4a4_linear_workspace_bytes(M, n1, n2, desc);
+    const size_t need = w4a4_linear_workspace_bytes(M, n1, n2, c != nullptr, desc);
     REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
 
     const size_t K = static_cast<size_t>(n1) * n2;

@@ -67,29 +67,87 @@ __host__ __device__ inline double f16_bits_to_f64(uint16_t h) {
 }
 
 // ---------------------------------------------------------------------------
-// reductions
+// wave-level data movement and reductions (DPP, no LDS round trip)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// DPP controls (GFX9 encoding): quad_perm [1,0,3,2] swaps neighbours, quad_perm
+// [2,3,0,1] swaps pairs, row_half_mirror reverses each 8 lanes, row_mirror
+// reverses each 16 lanes.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+// value of lane (l ^ 1)
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+    return static_cast<uint32_t>(dpp_i<kDppXor1>(static_cast<int>(v)));
+}
+
+// max over the 16 lanes of each row, in every lane of the row
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppMirror>(v));
     return v;
+}
+__device__ __forceinline__ float row16_min(float v) {
+    v = fminf(v, dpp_f<kDppXor1>(v));
+    v = fminf(v, dpp_f<kDppXor2>(v));
+    v = fminf(v, dpp_f<kDppHalfMirror>(v));
+    v = fminf(v, dpp_f<kDppMirror>(v));
+    return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// max over the wave (64 lanes), wave-uniform result
+__device__ __forceinline__ float wave_max(float v) {
+    v = row16_max(v);
+    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+                 fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = row16_min(v);
+    return fminf(fminf(readlane_f(v, 0), readlane_f(v, 16)),
+                 fminf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
-// round half to even, clamp to the signed 4-bit range, as a nibble
-__device__ __forceinline__ uint32_t quant_nibble(float z, float inv_or_s, bool zero) {
-    float t = z / inv_or_s;
-    float r = __builtin_rintf(t);
+// t = z * inv_s (inv_s = 1/s of the token), round half to even, clamp to the
+// signed 4-bit range, as a nibble; zero scale gives code 0
+__device__ __forceinline__ uint32_t quant_nibble(float z, float inv_s, bool zero) {
+    float r = __builtin_rintf(z * inv_s);
     r = fminf(fmaxf(r, -8.0f), 7.0f);
     int q = zero ? 0 : static_cast<int>(r);
     return static_cast<uint32_t>(q) & 0xFu;
 }
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (cached per device ordinal).
+inline int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 }  // namespace w4a4

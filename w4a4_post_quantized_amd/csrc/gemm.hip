@@ -33,6 +33,8 @@
 //  * MFMA: v_mfma_i32_16x16x64_i8.  Lane l supplies 16 bytes of row (l & 15)
 //    from k-slice (l >> 4) for A and for B; the result lane l holds rows
 //    4*(l >> 4) + r, column l & 15.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -44,7 +46,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 128;          // codes per K tile
 constexpr int ROWB = BK;         // int8 bytes per LDS row
-constexpr int kThreads = 256;
 
 // kModeChan: fp16 output, one weight scale per row (G == 1), scaled once at
 // the end; kModeGroup: fp16 output, per-group fp32 rescale inside the K loop;
@@ -81,18 +82,18 @@ __device__ __forceinline__ void unpack_asym(const uint4& w, uint32_t bias, uint4
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool ASYM, int MODE>
-__global__ __launch_bounds__(kThreads) void k_gemm_w4a4(
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
     const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int32_t* __restrict__ D,
     int M, int N, int K, int group_size) {
-    static_assert(WAVES_M * WAVES_N == kThreads / 64, "4 waves");
+    constexpr int kThreads = WAVES_M * WAVES_N * 64;
     constexpr int WM = BM / WAVES_M;
     constexpr int WN = BN / WAVES_N;
     constexpr int FM = WM / 16;
     constexpr int FN = WN / 16;
-    constexpr int ALD = BM * 4 / kThreads;   // 16-byte packed chunks per thread
-    constexpr int BLD = BN * 4 / kThreads;
+    constexpr int ALD = (BM * 4 + kThreads - 1) / kThreads;   // 16-byte packed chunks per thread
+    constexpr int BLD = (BN * 4 + kThreads - 1) / kThreads;
     static_assert(ALD >= 1 && BLD >= 1, "tile too small for the loader");
     constexpr int TILE_BYTES = (BM + BN) * ROWB;
 
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4(
             const int q = tid + i * kThreads;
             const int row = q >> 2, pc = q & 3;
             const int gm = m0 + row;
-            if (gm < M)
+            if (q < BM * 4 && gm < M)
                 ra[i] = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(gm) * KB + kt * 64 + pc * 16);
             else
                 ra[i] = make_uint4(0, 0, 0, 0);
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4(
             const int q = tid + i * kThreads;
             const int row = q >> 2, pc = q & 3;
             const int gn = n0 + row;
-            if (gn < N) {
+            if (q < BN * 4 && gn < N) {
                 rb[i] = *reinterpret_cast<const uint4*>(Wq + static_cast<size_t>(gn) * KB + kt * 64 + pc * 16);
                 if constexpr (ASYM) {
                     const int g = (kt * BK) / group_size;
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4(
 #pragma unroll
         for (int i = 0; i < ALD; ++i) {
             const int q = tid + i * kThreads;
+            if (q >= BM * 4) break;
             const int row = q >> 2, pc = q & 3;
             uint4 ev, od;
             unpack_signed16(ra[i], ev, od);
@@ -159,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4(
 #pragma unroll
         for (int i = 0; i < BLD; ++i) {
             const int q = tid + i * kThreads;
+            if (q >= BN * 4) break;
             const int row = q >> 2, pc = q & 3;
             uint4 ev, od;
             if constexpr (ASYM)
@@ -201,26 +204,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4(
 
         const uint8_t* As = smem + buf * TILE_BYTES;
         const uint8_t* Bs = As + BM * ROWB;
+        // two MFMA k-steps of 64 codes; the fragments of step 1 are read
+        // from LDS before the MFMAs of step 0 are issued
+        v4i af[2][FM], bf[2][FN];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int ch = 4 * s + fks;
-            v4i af[FM], bf[FN];
 #pragma unroll
             for (int a = 0; a < FM; ++a) {
                 const int row = wm0 + a * 16 + frow;
-                af[a] = *reinterpret_cast<const v4i*>(As + row * ROWB + swz(row, ch) * 16);
+                af[s][a] = *reinterpret_cast<const v4i*>(As + row * ROWB + swz(row, ch) * 16);
             }
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
                 const int row = wn0 + b * 16 + frow;
-                bf[b] = *reinterpret_cast<const v4i*>(Bs + row * ROWB + swz(row, ch) * 16);
+                bf[s][b] = *reinterpret_cast<const v4i*>(Bs + row * ROWB + swz(row, ch) * 16);
             }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int a = 0; a < FM; ++a)
 #pragma unroll
                 for (int b = 0; b < FN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
-        }
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[s][a], bf[s][b], acc[a][b],
+                                                                     0, 0, 0);
 
         // ---- end of a weight group: fold (or emit) the exact int32 sums ----
         const bool group_end = ((kt + 1) % TPG) == 0;
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4(
 template <int BM, int BN, int WM_, int WN_, int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t stream) {
     dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM));
-    dim3 block(kThreads);
+    dim3 block(WM_ * WN_ * 64);
     if (a.asym)
         k_gemm_w4a4<BM, BN, WM_, WN_, true, MODE><<<grid, block, 0, stream>>>(
             a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.D, a.M, a.N, a.K, a.group_size);
@@ -297,6 +305,49 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t stream) {
         k_gemm_w4a4<BM, BN, WM_, WN_, false, MODE><<<grid, block, 0, stream>>>(
             a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.D, a.M, a.N, a.K, a.group_size);
     return hipGetLastError();
+}
+
+using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
+
+// Tile configurations (BM x BN, waves along M x N) for the fp16-output
+// modes; index 0 is the default of each mode.
+struct TileCfg {
+    int bm, bn;
+    LaunchFn chan, group;
+};
+
+#define W4A4_TILE(BM, BN, WM_, WN_)                                                     \
+    TileCfg {                                                                          \
+        BM, BN, &launch_mode<BM, BN, WM_, WN_, kModeChan>,                              \
+            &launch_mode<BM, BN, WM_, WN_, kModeGroup>                                  \
+    }
+// tiles whose per-group fp32 accumulators do not fit the register file
+#define W4A4_TILE_CHAN(BM, BN, WM_, WN_) \
+    TileCfg { BM, BN, &launch_mode<BM, BN, WM_, WN_, kModeChan>, nullptr }
+
+const TileCfg kTiles[] = {
+    W4A4_TILE_CHAN(256, 256, 2, 4),
+    W4A4_TILE_CHAN(256, 256, 2, 2),
+    W4A4_TILE_CHAN(256, 192, 2, 4),
+    W4A4_TILE(256, 128, 2, 4),
+    W4A4_TILE(256, 128, 4, 2),
+    W4A4_TILE(128, 256, 2, 4),
+    W4A4_TILE(128, 128, 2, 2),
+    W4A4_TILE(128, 128, 2, 4),
+};
+#undef W4A4_TILE
+#undef W4A4_TILE_CHAN
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+// Developer override for tile sweeps: W4A4_GEMM_TILE=<index into kTiles>.
+int tile_override() {
+    static int v = -2;
+    if (v == -2) {
+        const char* e = getenv("W4A4_GEMM_TILE");
+        v = e ? atoi(e) : -1;
+        if (v >= kNumTiles) v = -1;
+    }
+    return v;
 }
 
 }  // namespace
@@ -320,8 +371,21 @@ hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_byte
         if (grouped) return launch_mode<64, 64, 2, 2, kModeGroup>(a, stream);
         return launch_mode<64, 64, 2, 2, kModeChan>(a, stream);
     }
-    if (grouped) return launch_mode<128, 128, 2, 2, kModeGroup>(a, stream);
-    return launch_mode<256, 256, 2, 2, kModeChan>(a, stream);
+    int t = tile_override();
+    if (t < 0 || (grouped && kTiles[t].group == nullptr)) {
+        // measured on MI355X: 256x256 tiles when the grid covers the CUs
+        // several times over, 256x192 (8 waves) for about one wave of tiles,
+        // 128x128 with 8 waves for the per-group mode
+        const int cus = device_cu_count();
+        const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
+        if (grouped)
+            t = 7;
+        else if (tiles256 >= 2L * cus)
+            t = 0;
+        else
+            t = (a.N % 192 == 0) ? 2 : 7;
+    }
+    return grouped ? kTiles[t].group(a, stream) : kTiles[t].chan(a, stream);
 }
 
 }  // namespace w4a4

@@ -12,8 +12,8 @@ namespace w4a4 {
 // ---- activation path (transform_quant.hip) --------------------------------
 enum class TqPath { Fused, Split };
 
-TqPath tq_select_path(int M, int n1, int n2);
-size_t tq_workspace_bytes(int M, int n1, int n2);
+TqPath tq_select_path(int M, int n1, int n2, bool has_c);
+size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c);
 
 // quantize=true: Xq/s_x outputs; quantize=false: Z (fp32 [M,K]) output.
 hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,

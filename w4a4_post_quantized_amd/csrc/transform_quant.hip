@@ -7,8 +7,29 @@
 // section 高效 Kernel 设计 (transform and quantize one token tile on chip).
 // FRM-PTQ page, section 初步介绍 (uniform quantizer, here symmetric 4-bit).
 //
-// Split path (any n1, n2): three stream-ordered kernels with fp32 FMA and a
-// workspace holding T = X̄·P2 and Z = P1^T·T:
+// Fused path (n1, n2 multiples of 16, n1 <= 128, n2 in {16, 32, 64, 128},
+// no diag(c)): one kernel, persistent workgroups of max(4, n2/16) waves, one
+// token (or 2-4 tokens when n2 <= 32) per workgroup iteration, each wave
+// owning one 16-column block of its token, everything on chip:
+//   stage 1  T = X̄ · P2 on v_mfma_f32_16x16x32_f16.  X̄ is fp16 and exact as
+//            an operand; P2 is split into fp16 hi + lo (two MFMAs), after a
+//            power-of-two prescale putting max|P2| in [1, 2).  The wave's P2
+//            fragments stay in VGPRs for the life of the workgroup.
+//   stage 2  Z = P1^T · T.  T never leaves the accumulators: its fp32 values,
+//            prescaled per wave by a power of two so max|T| is in
+//            [2^14, 2^15), are split into fp16 hi + lo and used directly as
+//            the B operand (the k order of the MFMA is chosen to match the
+//            accumulator layout).  P1 hi/lo fragments live in LDS, in the
+//            same k order.  Three MFMAs: hi*hi + hi*lo + lo*hi, i.e. about 22
+//            significant bits per product and fp32 accumulation.
+//   quant    per-token absmax by DPP wave reductions + LDS, t = z * (1/s),
+//            round half to even,
+//            nibble pairs formed across neighbouring lanes, packed bytes
+//            staged in LDS and written with coalesced 16-byte stores.
+// Power-of-two scalings are exact and undone before quantization.
+//
+// Split path (any n1, n2 up to 256, and diag(c)): three stream-ordered fp32
+// FMA kernels with a workspace holding T = X̄·P2 and Z = P1^T·T:
 //   stage1  one block per (token m, row r of X̄): T[m, r, :]
 //   stage2  one thread per element of Z, block absmax -> atomicMax per token
 //   quant   8 codes per thread -> one packed 32-bit store
@@ -87,27 +108,352 @@ __global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, i
     const int e0 = idx * 8;
     if (e0 >= K) return;
     const bool zero = !(s > 0.0f);
+    const float inv = zero ? 0.0f : 1.0f / s;
     const float* z = Z + static_cast<size_t>(m) * K + e0;
     uint32_t word = 0;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) word |= quant_nibble(z[t], s, zero) << (4 * t);
+    for (int t = 0; t < 8; ++t) word |= quant_nibble(z[t], inv, zero) << (4 * t);
     reinterpret_cast<uint32_t*>(Xq + static_cast<size_t>(m) * (K / 2))[idx] = word;
+}
+
+
+// ===========================================================================
+// Fused MFMA path
+// ===========================================================================
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// floor(log2(x)) for a positive normal float
+__device__ __forceinline__ int ilog2f(float x) {
+    return static_cast<int>((__float_as_uint(x) >> 23) & 0xFFu) - 127;
+}
+
+template <int N1, int N2>
+struct FusedCfg {
+    static_assert(N1 % 16 == 0 && N2 % 16 == 0, "factors must be multiples of 16");
+    static constexpr int K = N1 * N2;
+    static constexpr int RB = N1 / 16;           // 16-row blocks of X̄, T and Z
+    static constexpr int CB = N2 / 16;           // 16-column blocks, one wave each
+    static constexpr int KS1 = (N2 + 31) / 32;   // stage-1 MFMA k-steps
+    static constexpr int KS2 = (N1 + 31) / 32;   // stage-2 MFMA k-steps
+    static constexpr int NW = CB < 4 ? 4 : CB;   // waves per workgroup
+    static constexpr int NT = NW * 64;           // threads per workgroup
+    static constexpr int TPI = NW / CB;          // tokens per workgroup iteration
+    static_assert(NW % CB == 0 && NW <= 8, "unsupported n2");
+    static constexpr int P1F = RB * KS2 * 64 * 8;  // fp16 elements of one P1 fragment set
+    // X̄ staging: token rows padded by 16 bytes so the 16 rows one MFMA
+    // operand read touches fall in distinct LDS banks
+    static constexpr int XROW = N2 * 2 + 16;       // bytes per staged row
+    static constexpr int XSLOT = N1 * XROW;        // bytes per staged token
+    static constexpr int XCH = K / 8;              // 16-byte chunks per token in HBM
+    static constexpr int XLD = (TPI * XCH + NT - 1) / NT;  // chunks per thread per tile
+};
+
+template <int N1, int N2>
+__global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint16_t* __restrict__ X, int M,
+                                                  const float* __restrict__ P1,
+                                                  const float* __restrict__ P2, float alpha,
+                                                  uint8_t* __restrict__ Xq,
+                                                  float* __restrict__ s_x,
+                                                  float* __restrict__ Zout) {
+    using C = FusedCfg<N1, N2>;
+    constexpr int K = C::K;
+    __shared__ __align__(16) _Float16 p1hi[C::P1F];
+    __shared__ __align__(16) _Float16 p1lo[C::P1F];
+    __shared__ __align__(16) uint8_t qbuf[C::TPI * K / 2];
+    __shared__ __align__(16) uint8_t xs[2][C::TPI * C::XSLOT];
+    constexpr int NT = C::NT;
+    __shared__ float red[2 * C::NW];
+    __shared__ float tok_s[C::TPI];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+    const int li = lane & 15;
+
+    // ---- power-of-two prescale of the factors ------------------------------
+    float m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < (N1 * N1 + NT - 1) / NT; ++i) {
+        const int e = tid + i * NT;
+        if (e < N1 * N1) m1 = fmaxf(m1, fabsf(P1[e]));
+    }
+#pragma unroll
+    for (int i = 0; i < (N2 * N2 + NT - 1) / NT; ++i) {
+        const int e = tid + i * NT;
+        if (e < N2 * N2) m2 = fmaxf(m2, fabsf(P2[e]));
+    }
+    m1 = wave_max(m1);
+    m2 = wave_max(m2);
+    if (lane == 0) {
+        red[wave] = m1;
+        red[C::NW + wave] = m2;
+    }
+    __syncthreads();
+    m1 = 0.0f;
+    m2 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) {
+        m1 = fmaxf(m1, red[w]);
+        m2 = fmaxf(m2, red[C::NW + w]);
+    }
+    const int e1 = m1 > 0.0f ? -ilog2f(m1) : 0;   // max|P1 * 2^e1| in [1, 2)
+    const int e2 = m2 > 0.0f ? -ilog2f(m2) : 0;
+
+    // ---- P1 fragments (stage-2 A operand) into LDS ---------------------------
+    // fragment (ob, s), lane (gg, ii), element e holds P1[rho][16*ob + ii],
+    // rho = 32s + 4gg + e (e < 4) or 32s + 16 + 4gg + (e - 4) (e >= 4): the
+    // rows of T that the stage-1 accumulators of lane group gg hold.
+#pragma unroll
+    for (int i = 0; i < (C::P1F + NT - 1) / NT; ++i) {
+        const int idx = tid + i * NT;
+        if (idx >= C::P1F) break;
+        const int e = idx & 7;
+        const int ln = (idx >> 3) & 63;
+        const int slot = idx >> 9;
+        const int sk = slot % C::KS2;
+        const int ob = slot / C::KS2;
+        const int gg = ln >> 4, ii = ln & 15;
+        const int rho = 32 * sk + (e < 4 ? 4 * gg + e : 16 + 4 * gg + (e - 4));
+        const float v = rho < N1 ? ldexpf(P1[rho * N1 + 16 * ob + ii], e1) : 0.0f;
+        const _Float16 h = static_cast<_Float16>(v);
+        p1hi[idx] = h;
+        p1lo[idx] = static_cast<_Float16>(v - static_cast<float>(h));
+    }
+
+    // ---- P2 fragments (stage-1 B operand) of this wave's 16 columns ---------
+    const int tslot = wave / C::CB;
+    const int cb = wave % C::CB;
+    v8h p2hi[C::KS1], p2lo[C::KS1];
+#pragma unroll
+    for (int ks = 0; ks < C::KS1; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int kk = 32 * ks + 8 * g + e;
+            const float v = kk < N2 ? ldexpf(P2[kk * N2 + 16 * cb + li], e2) : 0.0f;
+            const _Float16 h = static_cast<_Float16>(v);
+            p2hi[ks][e] = h;
+            p2lo[ks][e] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+    }
+    // ---- X̄ tiles: HBM -> registers (next tile) -> LDS (double buffer) --------
+    uint4 xr[C::XLD];
+    auto load_tile = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < C::XLD; ++i) {
+            const int c = tid + i * NT;
+            const int t = c / C::XCH;
+            if (c < C::TPI * C::XCH && b + t < M)
+                xr[i] = reinterpret_cast<const uint4*>(X + static_cast<size_t>(b) * K)[c];
+            else
+                xr[i] = make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto stage_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < C::XLD; ++i) {
+            const int c = tid + i * NT;
+            if (c < C::TPI * C::XCH) {
+                const int t = c / C::XCH;
+                const int cc = c - t * C::XCH;
+                const int row = cc / (N2 / 8);
+                const int col = cc - row * (N2 / 8);
+                *reinterpret_cast<uint4*>(&xs[buf][t * C::XSLOT + row * C::XROW + col * 16]) = xr[i];
+            }
+        }
+    };
+    const int stride = gridDim.x * C::TPI;
+    int base = blockIdx.x * C::TPI;
+    if (base < M) load_tile(base);
+    stage_tile(0);
+    // the token loop reuses red[] and reads xs[0] after this barrier
+    __syncthreads();
+
+    for (int it = 0; base < M; base += stride, ++it) {
+        const int buf = it & 1;
+        if (base + stride < M) load_tile(base + stride);   // in flight during compute
+        const int m = base + tslot;
+        const bool valid = m < M;
+        v4f Z[C::RB];
+        float wmax = 0.0f;
+        if (valid) {
+            const uint8_t* xt = &xs[buf][tslot * C::XSLOT];
+            // stage 1: T[:, cb] = X̄ · P2'[:, cb]
+            v4f T[C::RB];
+#pragma unroll
+            for (int rb = 0; rb < C::RB; ++rb) {
+                v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < C::KS1; ++ks) {
+                    v8h a;
+                    if (32 * ks + 8 * g < N2)
+                        a = *reinterpret_cast<const v8h*>(xt + (16 * rb + li) * C::XROW +
+                                                          (32 * ks + 8 * g) * 2);
+                    else
+                        a = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p2hi[ks], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p2lo[ks], acc, 0, 0, 0);
+                }
+                T[rb] = acc;
+            }
+            // per-wave power-of-two prescale of T into the fp16 range
+            float tm = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tm = fmaxf(tm, fabsf(T[rb][r]));
+            tm = wave_max(tm);
+            const int et = tm > 0.0f ? 14 - ilog2f(tm) : 0;
+            // stage-2 B operand: accumulator rows 4g+r of blocks 2s and 2s+1
+            v8h bh[C::KS2], bl[C::KS2];
+#pragma unroll
+            for (int sk = 0; sk < C::KS2; ++sk) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int rb = 2 * sk + (e >> 2);
+                    const float v = rb < C::RB ? ldexpf(T[rb < C::RB ? rb : 0][e & 3], et) : 0.0f;
+                    const _Float16 h = static_cast<_Float16>(v);
+                    bh[sk][e] = h;
+                    bl[sk][e] = static_cast<_Float16>(v - static_cast<float>(h));
+                }
+            }
+            // stage 2: Z[:, cb] = P1'^T · T'[:, cb]
+            const int unscale = -(e1 + e2 + et);
+#pragma unroll
+            for (int ob = 0; ob < C::RB; ++ob) {
+                v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int sk = 0; sk < C::KS2; ++sk) {
+                    const int off = ((ob * C::KS2 + sk) * 64 + lane) * 8;
+                    const v8h ah = *reinterpret_cast<const v8h*>(p1hi + off);
+                    const v8h al = *reinterpret_cast<const v8h*>(p1lo + off);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh[sk], z, 0, 0, 0);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[sk], z, 0, 0, 0);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh[sk], z, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    z[r] = ldexpf(z[r], unscale);
+                    wmax = fmaxf(wmax, fabsf(z[r]));
+                }
+                Z[ob] = z;
+            }
+        }
+        // ---- per-token absmax and scale ---------------------------------------
+        wmax = wave_max(wmax);
+        if (lane == 0) red[wave] = wmax;
+        __syncthreads();
+        float amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < C::CB; ++w) amax = fmaxf(amax, red[tslot * C::CB + w]);
+        const float s = alpha * amax / 7.0f;
+        if (tid < C::TPI) {
+            float a2 = 0.0f;
+            for (int w = 0; w < C::CB; ++w) a2 = fmaxf(a2, red[tid * C::CB + w]);
+            tok_s[tid] = alpha * a2 / 7.0f;
+        }
+        if (valid) {
+            if (Zout != nullptr) {
+                float* zo = Zout + static_cast<size_t>(m) * K;
+#pragma unroll
+                for (int ob = 0; ob < C::RB; ++ob)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        zo[(16 * ob + 4 * g + r) * N2 + 16 * cb + li] = Z[ob][r];
+            } else {
+                const bool zero = !(s > 0.0f);
+                const float inv = zero ? 0.0f : 1.0f / s;
+                uint8_t* qb = qbuf + tslot * (K / 2);
+#pragma unroll
+                for (int ob = 0; ob < C::RB; ++ob)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t nib = quant_nibble(Z[ob][r], inv, zero);
+                        const uint32_t odd = lane_xor1(nib);
+                        if ((li & 1) == 0) {
+                            const int k = (16 * ob + 4 * g + r) * N2 + 16 * cb + li;
+                            qb[k >> 1] = static_cast<uint8_t>(nib | (odd << 4));
+                        }
+                    }
+            }
+        }
+        __syncthreads();
+        // ---- coalesced store of the packed rows and the scales ----------------
+        if (Zout == nullptr) {
+            constexpr int CH = K / 32;     // 16-byte chunks per token row
+            for (int c = tid; c < C::TPI * CH; c += NT) {
+                const int t = c / CH;
+                const int mm = base + t;
+                if (mm < M)
+                    reinterpret_cast<uint4*>(Xq + static_cast<size_t>(mm) * (K / 2))[c - t * CH] =
+                        reinterpret_cast<const uint4*>(qbuf)[c];
+            }
+            if (tid < C::TPI && base + tid < M) s_x[base + tid] = tok_s[tid];
+        }
+        // the buffer written here was last read one iteration ago, before two
+        // barriers; the barrier below publishes it for the next iteration
+        if (base + stride < M) stage_tile(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+template <int N1, int N2>
+hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* P2, float alpha,
+                        uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+    using C = FusedCfg<N1, N2>;
+    // persistent grid: as many workgroups as fit on the device at once, so the
+    // per-workgroup fragment setup is paid once per resident workgroup
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_fused<N1, N2>, C::NT, 0) !=
+                hipSuccess || n < 1)
+            n = 1;
+        per_cu = n;
+    }
+    const int units = (M + C::TPI - 1) / C::TPI;
+    const int cap = per_cu * device_cu_count();
+    const int grid = units < cap ? units : cap;
+    k_tq_fused<N1, N2><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, alpha, Xq, s_x, Z);
+    return hipGetLastError();
+}
+
+using FusedFn = hipError_t (*)(const uint16_t*, int, const float*, const float*, float, uint8_t*,
+                               float*, float*, hipStream_t);
+
+// (n1, n2) pairs with a fused instantiation
+FusedFn fused_for(int n1, int n2) {
+#define W4A4_FUSED(a, b) \
+    if (n1 == a && n2 == b) return &launch_fused<a, b>;
+    W4A4_FUSED(16, 16)
+    W4A4_FUSED(32, 32)
+    W4A4_FUSED(16, 64)
+    W4A4_FUSED(32, 64)
+    W4A4_FUSED(64, 64)
+    W4A4_FUSED(32, 128)
+    W4A4_FUSED(64, 128)
+    W4A4_FUSED(96, 128)
+    W4A4_FUSED(112, 128)
+    W4A4_FUSED(128, 128)
+    W4A4_FUSED(128, 64)
+#undef W4A4_FUSED
+    return nullptr;
 }
 
 }  // namespace
 
-TqPath tq_select_path(int M, int n1, int n2) {
+TqPath tq_select_path(int M, int n1, int n2, bool has_c) {
     (void)M;
-    (void)n1;
-    (void)n2;
+    if (!has_c && fused_for(n1, n2) != nullptr) return TqPath::Fused;
     return TqPath::Split;
 }
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-size_t tq_workspace_bytes(int M, int n1, int n2) {
+size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c) {
     const size_t K = static_cast<size_t>(n1) * n2;
-    if (tq_select_path(M, n1, n2) == TqPath::Split)
+    if (tq_select_path(M, n1, n2, has_c) == TqPath::Split)
         return 2 * align256(sizeof(float) * K * M) + align256(sizeof(uint32_t) * M);
     return 0;
 }
@@ -118,6 +464,9 @@ hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
                      hipStream_t stream) {
     (void)ws_bytes;
     if (M == 0) return hipSuccess;
+    if (tq_select_path(M, n1, n2, c != nullptr) == TqPath::Fused)
+        return fused_for(n1, n2)(X, M, P1, P2, alpha, quantize ? Xq : nullptr, s_x,
+                                 quantize ? nullptr : Z, stream);
     const int K = n1 * n2;
     char* p = static_cast<char*>(ws);
     float* T = reinterpret_cast<float*>(p);
