@@ -296,3 +296,26 @@ def test_linear_with_channel_scale_and_clip():
     c = WL.make_channel_scale(wl.K, seed=4)
     inp["Wt"] = O.merge_weights(inp["W"], inp["P1"], inp["P2"], c)
     _layer_parity(inp, c=c, alpha=0.8)
+
+
+NUM_TILE_CONFIGS = 35
+
+
+@pytest.mark.parametrize("tile", range(NUM_TILE_CONFIGS))
+@pytest.mark.parametrize("M,N,K,g,asym", [(300, 520, 1024, 1024, False), (300, 520, 1024, 128, True),
+                                          (513, 392, 512, 512, True)])
+def test_gemm_every_tile_config(tile, M, N, K, g, asym, monkeypatch):
+    """Every tile configuration the dispatcher can pick (forced through the
+    W4A4_GEMM_TILE override; configs without a per-group variant fall back to
+    the default one) against the oracle, with ragged M and N."""
+    log(f"gemm tile {tile}: M={M} N={N} K={K} g={g} asym={asym}")
+    monkeypatch.setenv("W4A4_GEMM_TILE", str(tile))
+    qx, wc, z = _codes(M, N, K, g, asym, seed=tile + 100)
+    rng = np.random.default_rng(tile)
+    sx = (rng.uniform(0.5, 3, M) * 0.05).astype(np.float32)
+    sw = (rng.uniform(0.5, 2, (N, K // g)) * 0.003).astype(np.float16)
+    D_or = O.int_gemm(qx, wc, z, g)
+    desc = W().WeightDesc(N, K, g, int(asym))
+    Y = W().gemm(to_dev(O.pack_nibbles(qx)), to_dev(sx), desc, to_dev(O.pack_nibbles(wc)),
+                 to_dev(sw), to_dev(z) if asym else None).cpu().numpy()
+    assert_y_close(Y, O.epilogue(D_or, sx, sw), O.epilogue(np.abs(D_or), sx, sw))
