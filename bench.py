@@ -44,7 +44,23 @@ def parse():
     ap.add_argument("--workload", default="qkv8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy of a known number of bytes, for calibrating the HBM
+    traffic counters: it must read and write exactly `mib` MiB per launch."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
 def gemm_bytes(wl, M):
@@ -105,6 +121,9 @@ def main():
               "between GPUs, so N > 1 is not run here (each GPU would run the same kernel "
               "on its share of tokens).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     import workloads as WL
