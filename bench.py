@@ -208,7 +208,7 @@ def main():
         achieved = ops / (gemm_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
-    roof["kernel"] = "k_gemm_w4a4"
+    roof["kernel"] = L.gemm_kernel_name(M, desc)
     roof["kernel_us"] = round(gemm_us, 2)
     roof["traffic"] = traffic_from_profiles("gemm", wl.name)
 

@@ -179,6 +179,12 @@ int w4a4_gemm(const uint8_t* Xq, const float* s_x, int32_t M, const w4a4_weight_
 int w4a4_gemm_i32(const uint8_t* Xq, int32_t M, const w4a4_weight_desc* desc,
                   const uint8_t* Wq, const uint16_t* z_w, int32_t* D, void* stream);
 
+/* Name of the kernel configuration w4a4_gemm launches for M tokens and this
+ * weight layout on the current device (for traces and reports), or NULL if
+ * desc is invalid (message in w4a4_last_error).  Static storage; launches
+ * nothing. */
+const char* w4a4_gemm_kernel_name(int32_t M, const w4a4_weight_desc* desc);
+
 /* ------------------------------------------------------------------------ */
 /* Whole layer                                                               */
 /* ------------------------------------------------------------------------ */

@@ -134,3 +134,14 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(W, "_lib", None)
     with pytest.raises(ImportError):
         W.lib()
+
+
+def test_gemm_kernel_name_query():
+    """The configuration name is a host-side query: decode kernels for at most
+    64 tokens, the prefill kernels above; invalid descriptors give NULL."""
+    assert W.gemm_kernel_name(1, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 1")
+    assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 4")
+    assert W.gemm_kernel_name(2048, W.WeightDesc(6144, 4096, 4096, 0)).startswith("k_gemm_dl<")
+    assert W.gemm_kernel_name(2048, W.WeightDesc(28672, 4096, 128, 1)).startswith("k_gemm")
+    with pytest.raises(W.W4A4Error):
+        W.gemm_kernel_name(16, W.WeightDesc(256, 200, 200, 0))

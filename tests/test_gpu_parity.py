@@ -298,7 +298,8 @@ def test_linear_with_channel_scale_and_clip():
     _layer_parity(inp, c=c, alpha=0.8)
 
 
-NUM_TILE_CONFIGS = 35
+NUM_TILE_CONFIGS = 12
+NUM_DECODE_VARIANTS = 4
 
 
 @pytest.mark.parametrize("tile", range(NUM_TILE_CONFIGS))
@@ -316,6 +317,34 @@ def test_gemm_every_tile_config(tile, M, N, K, g, asym, monkeypatch):
     sw = (rng.uniform(0.5, 2, (N, K // g)) * 0.003).astype(np.float16)
     D_or = O.int_gemm(qx, wc, z, g)
     desc = W().WeightDesc(N, K, g, int(asym))
+    Y = W().gemm(to_dev(O.pack_nibbles(qx)), to_dev(sx), desc, to_dev(O.pack_nibbles(wc)),
+                 to_dev(sw), to_dev(z) if asym else None).cpu().numpy()
+    assert_y_close(Y, O.epilogue(D_or, sx, sw), O.epilogue(np.abs(D_or), sx, sw))
+
+
+@pytest.mark.parametrize("variant", range(NUM_DECODE_VARIANTS))
+@pytest.mark.parametrize("M,N,K,g,asym", [
+    (1, 520, 2944, 128, True),        # K tiles not a multiple of the waves
+    (13, 392, 1024, 1024, False),     # fewer K tiles than waves
+    (17, 264, 2560, 256, True),       # wave ranges that split a weight group
+    (33, 200, 2048, 2048, True),      # asymmetric per-channel
+    (64, 520, 1536, 128, False),      # symmetric per-group
+    (50, 136, 4096, 512, True),
+    (16, 264, 16384, 128, True),      # activations too large to stage in LDS
+    (8, 72, 28672, 128, True),        # the 70B down projection's K, staged
+])
+def test_gemm_decode_variants(variant, M, N, K, g, asym, monkeypatch):
+    """Every decode configuration (M <= 64: one, two or four 16-row fragments,
+    forced through W4A4_GEMM_DECODE) against the oracle, ragged N."""
+    log(f"gemm decode variant {variant}: M={M} N={N} K={K} g={g} asym={asym}")
+    monkeypatch.setenv("W4A4_GEMM_DECODE", str(variant))
+    desc = W().WeightDesc(N, K, g, int(asym))
+    assert W().gemm_kernel_name(M, desc).startswith("k_gemm_dec<")
+    qx, wc, z = _codes(M, N, K, g, asym, seed=variant + 7 * M)
+    rng = np.random.default_rng(variant + M)
+    sx = (rng.uniform(0.5, 3, M) * 0.05).astype(np.float32)
+    sw = (rng.uniform(0.5, 2, (N, K // g)) * 0.003).astype(np.float16)
+    D_or = O.int_gemm(qx, wc, z, g)
     Y = W().gemm(to_dev(O.pack_nibbles(qx)), to_dev(sx), desc, to_dev(O.pack_nibbles(wc)),
                  to_dev(sw), to_dev(z) if asym else None).cpu().numpy()
     assert_y_close(Y, O.epilogue(D_or, sx, sw), O.epilogue(np.abs(D_or), sx, sw))

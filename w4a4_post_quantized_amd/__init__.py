@@ -16,7 +16,7 @@ from typing import Optional
 __all__ = [
     "W4A4Error", "WeightDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "merge_weights", "pack_weights", "transform_quant", "transform", "gemm",
-    "gemm_i32", "linear", "merge_workspace_bytes", "transform_quant_workspace_bytes",
+    "gemm_i32", "gemm_kernel_name", "linear", "merge_workspace_bytes", "transform_quant_workspace_bytes",
     "gemm_workspace_bytes", "linear_workspace_bytes", "version",
 ]
 
@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = [
     "w4a4_version", "w4a4_status_str", "w4a4_last_error",
     "w4a4_merge_workspace_bytes", "w4a4_merge_weights", "w4a4_pack_weights",
     "w4a4_transform_quant_workspace_bytes", "w4a4_transform_quant", "w4a4_transform",
-    "w4a4_gemm_workspace_bytes", "w4a4_gemm", "w4a4_gemm_i32",
+    "w4a4_gemm_workspace_bytes", "w4a4_gemm", "w4a4_gemm_i32", "w4a4_gemm_kernel_name",
     "w4a4_linear_workspace_bytes", "w4a4_linear",
 ]
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_workspace_bytes": (sz, [i32, dp]),
             "w4a4_gemm": (ctypes.c_int, [vp, vp, i32, dp, vp, vp, vp, vp, vp, sz, vp]),
             "w4a4_gemm_i32": (ctypes.c_int, [vp, i32, dp, vp, vp, vp, vp]),
+            "w4a4_gemm_kernel_name": (ctypes.c_char_p, [i32, dp]),
             "w4a4_linear_workspace_bytes": (sz, [i32, i32, i32, i32, dp]),
             "w4a4_linear": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, dp, vp, vp, vp, vp, vp, sz, vp]),
         }
@@ -253,6 +254,14 @@ def gemm_i32(Xq, desc: WeightDesc, Wq, z_w=None, stream=None):
     _check(lib().w4a4_gemm_i32(_p(Xq), M, ctypes.byref(desc), _p(Wq), _p(z_w), _p(D),
                                _stream(stream)), "w4a4_gemm_i32")
     return D
+
+
+def gemm_kernel_name(M: int, desc: WeightDesc) -> str:
+    """Name of the kernel configuration w4a4_gemm uses for M tokens."""
+    name = lib().w4a4_gemm_kernel_name(M, ctypes.byref(desc))
+    if name is None:
+        _check(-1, "w4a4_gemm_kernel_name")
+    return name.decode()
 
 
 def linear(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, c=None, alpha_a: float = 1.0,

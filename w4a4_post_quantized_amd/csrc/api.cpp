@@ -267,6 +267,18 @@ int w4a4_gemm_i32(const uint8_t* Xq, int32_t M, const w4a4_weight_desc* desc,
                        "w4a4_gemm_i32");
 }
 
+const char* w4a4_gemm_kernel_name(int32_t M, const w4a4_weight_desc* desc) {
+    if (check_desc(desc, true) != W4A4_OK) return nullptr;
+    if (M < 0) {
+        fail(W4A4_ERR_INVALID_ARG, "M = %d is negative", M);
+        return nullptr;
+    }
+    ok();
+    w4a4::GemmArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, M, desc->N,
+                     desc->K, desc->group_size, desc->asymmetric != 0};
+    return w4a4::gemm_kernel_name(a, false);
+}
+
 // ---------------------------------------------------------------------------
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 

@@ -53,6 +53,15 @@ constexpr int ROWB = BK;         // int8 bytes per LDS row
 // kModeI32: exact int32 D per group.
 enum Mode { kModeChan = 0, kModeGroup = 1, kModeI32 = 2 };
 
+// calls f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // signed nibbles -> 16*q bytes; even codes in `ev`, odd codes in `od`
@@ -297,250 +306,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
 
 
 // ===========================================================================
-// Pipelined kernel (BM = 256, 4 or 8 waves): global loads run two K tiles
-// ahead into two register staging sets; while the MFMAs of tile t run, the
-// staged tile t+1 is unpacked into the other LDS buffer; both k-steps'
-// fragments of tile t are read before its MFMAs; one barrier per tile.  The
-// fp16 output tile is staged through LDS and written as full 16-byte row
-// segments.
-// ===========================================================================
-template <int BN, int WAVES_N, bool ASYM, int MODE>
-__global__ __launch_bounds__(2 * WAVES_N * 64) void k_gemm_pipe(
-    const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
-    const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
-    const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int M, int N, int K,
-    int group_size) {
-    constexpr int BM = 256;
-    constexpr int WAVES_M = 2;
-    constexpr int NT = WAVES_M * WAVES_N * 64;
-    constexpr int WM = BM / WAVES_M;
-    constexpr int WN = BN / WAVES_N;
-    constexpr int FM = WM / 16;
-    constexpr int FN = WN / 16;
-    constexpr int ALD = (BM * 4 + NT - 1) / NT;
-    constexpr int BLD = (BN * 4 + NT - 1) / NT;
-    constexpr int TILE_BYTES = (BM + BN) * ROWB;
-    static_assert(2 * TILE_BYTES >= BM * BN * 2, "output staging must fit the tile buffers");
-    static_assert(MODE != kModeI32, "fp16 output modes only");
-
-    __shared__ __align__(16) uint8_t smem[2 * TILE_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm0 = (wave / WAVES_N) * WM;
-    const int wn0 = (wave % WAVES_N) * WN;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
-    const int KB = K / 2;
-    const int KT = K / BK;
-    const int G = K / group_size;
-    const int TPG = group_size / BK;
-
-    uint4 ra[2][ALD], rb[2][BLD];
-    uint32_t zb[2][ASYM ? BLD : 1];
-
-    auto load_tile = [&](int kt, auto SET) {
-        constexpr int S = decltype(SET)::value;
-#pragma unroll
-        for (int i = 0; i < ALD; ++i) {
-            const int q = tid + i * NT;
-            const int row = q >> 2, pc = q & 3;
-            const int gm = m0 + row;
-            if (q < BM * 4 && gm < M)
-                ra[S][i] = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(gm) * KB + kt * 64 + pc * 16);
-            else
-                ra[S][i] = make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < BLD; ++i) {
-            const int q = tid + i * NT;
-            const int row = q >> 2, pc = q & 3;
-            const int gn = n0 + row;
-            if (q < BN * 4 && gn < N) {
-                rb[S][i] = *reinterpret_cast<const uint4*>(Wq + static_cast<size_t>(gn) * KB + kt * 64 + pc * 16);
-                if constexpr (ASYM) {
-                    const int g = (kt * BK) / group_size;
-                    const uint32_t z = static_cast<uint32_t>(h2f(z_w[static_cast<size_t>(gn) * G + g]));
-                    zb[S][i] = (0x80u - z) * 0x01010101u;
-                }
-            } else {
-                rb[S][i] = make_uint4(0, 0, 0, 0);
-                if constexpr (ASYM) zb[S][i] = 0x80808080u;
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf, auto SET) {
-        constexpr int S = decltype(SET)::value;
-        uint8_t* As = smem + buf * TILE_BYTES;
-        uint8_t* Bs = As + BM * ROWB;
-#pragma unroll
-        for (int i = 0; i < ALD; ++i) {
-            const int q = tid + i * NT;
-            if (q >= BM * 4) break;
-            const int row = q >> 2, pc = q & 3;
-            uint4 ev, od;
-            unpack_signed16(ra[S][i], ev, od);
-            *reinterpret_cast<uint4*>(As + row * ROWB + swz(row, 2 * pc) * 16) = ev;
-            *reinterpret_cast<uint4*>(As + row * ROWB + swz(row, 2 * pc + 1) * 16) = od;
-        }
-#pragma unroll
-        for (int i = 0; i < BLD; ++i) {
-            const int q = tid + i * NT;
-            if (q >= BN * 4) break;
-            const int row = q >> 2, pc = q & 3;
-            uint4 ev, od;
-            if constexpr (ASYM)
-                unpack_asym(rb[S][i], zb[S][i], ev, od);
-            else
-                unpack_signed16(rb[S][i], ev, od);
-            *reinterpret_cast<uint4*>(Bs + row * ROWB + swz(row, 2 * pc) * 16) = ev;
-            *reinterpret_cast<uint4*>(Bs + row * ROWB + swz(row, 2 * pc + 1) * 16) = od;
-        }
-    };
-
-    v4i acc[FM][FN];
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b) acc[a][b] = v4i{0, 0, 0, 0};
-    float facc[(MODE == kModeGroup) ? FM : 1][(MODE == kModeGroup) ? FN : 1][4];
-    if constexpr (MODE == kModeGroup) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
-    }
-
-    const int frow = lane & 15;
-    const int fks = lane >> 4;
-    const int orow = 4 * (lane >> 4);
-    const int ocol = lane & 15;
-
-    auto body = [&](int kt, auto SET) {
-        constexpr int S = decltype(SET)::value;        // == kt & 1
-        const uint8_t* As = smem + S * TILE_BYTES;
-        const uint8_t* Bs = As + BM * ROWB;
-        auto read_frags = [&](int step, v4i* af, v4i* bf) {
-#pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                const int row = wm0 + a * 16 + frow;
-                af[a] = *reinterpret_cast<const v4i*>(As + row * ROWB + swz(row, 4 * step + fks) * 16);
-            }
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int row = wn0 + b * 16 + frow;
-                bf[b] = *reinterpret_cast<const v4i*>(Bs + row * ROWB + swz(row, 4 * step + fks) * 16);
-            }
-        };
-        auto mfmas = [&](const v4i* af, const v4i* bf) {
-#pragma unroll
-            for (int a = 0; a < FM; ++a)
-#pragma unroll
-                for (int b = 0; b < FN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
-        };
-        v4i af[FM], bf[FN];
-        read_frags(0, af, bf);
-        // tile kt+2 -> staging set S (its previous content, tile kt, is in LDS)
-        if (kt + 2 < KT) load_tile(kt + 2, std::integral_constant<int, S>{});
-        // staged tile kt+1 -> the other LDS buffer (read last in iteration kt-1)
-        if (kt + 1 < KT) store_tile(S ^ 1, std::integral_constant<int, S ^ 1>{});
-        mfmas(af, bf);
-        read_frags(1, af, bf);
-        mfmas(af, bf);
-        if constexpr (MODE == kModeGroup) {
-            if (((kt + 1) % TPG) == 0) {
-                const int g = kt / TPG;
-#pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const int gn = n0 + wn0 + b * 16 + ocol;
-                    const float sw = (gn < N) ? h2f(s_w[static_cast<size_t>(gn) * G + g]) : 0.0f;
-#pragma unroll
-                    for (int a = 0; a < FM; ++a)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            facc[a][b][r] = fmaf(static_cast<float>(acc[a][b][r]), sw, facc[a][b][r]);
-                            acc[a][b][r] = 0;
-                        }
-                }
-            }
-        }
-        __syncthreads();
-    };
-
-    load_tile(0, std::integral_constant<int, 0>{});
-    if (KT > 1) load_tile(1, std::integral_constant<int, 1>{});
-    store_tile(0, std::integral_constant<int, 0>{});
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-        body(kt, std::integral_constant<int, 0>{});
-        body(kt + 1, std::integral_constant<int, 1>{});
-    }
-    if (kt < KT) body(kt, std::integral_constant<int, 0>{});
-
-    // ---- epilogue: fp16 tile staged in LDS, written as 16-byte row pieces ----
-    constexpr float kUnshift = ASYM ? (1.0f / 16.0f) : (1.0f / 256.0f);
-    uint16_t* Ys = reinterpret_cast<uint16_t*>(smem);       // [BM][BN] fp16
-#pragma unroll
-    for (int b = 0; b < FN; ++b) {
-        const int cl = wn0 + b * 16 + ocol;
-        const int gn = n0 + cl;
-        float sw1 = 0.0f;
-        if constexpr (MODE == kModeChan) sw1 = (gn < N) ? h2f(s_w[gn]) : 0.0f;
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rl = wm0 + a * 16 + orow + r;
-                const int gm = m0 + rl;
-                const float sx = (gm < M) ? s_x[gm] : 0.0f;
-                float v;
-                if constexpr (MODE == kModeChan)
-                    v = static_cast<float>(acc[a][b][r]) * sw1;
-                else
-                    v = facc[a][b][r];
-                Ys[rl * BN + cl] = f2h(v * sx * kUnshift);
-            }
-    }
-    __syncthreads();
-    constexpr int CPR = BN / 8;            // 16-byte pieces per row
-    for (int c = tid; c < BM * CPR; c += NT) {
-        const int rl = c / CPR;
-        const int cc = c - rl * CPR;
-        const int gm = m0 + rl;
-        const int gn = n0 + cc * 8;
-        if (gm >= M) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(Ys + rl * BN + cc * 8);
-        uint16_t* dst = Y + static_cast<size_t>(gm) * N + gn;
-        if (gn + 8 <= N && (N & 7) == 0) {
-            *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-            const uint16_t* pv = reinterpret_cast<const uint16_t*>(&v);
-            for (int j = 0; j < 8 && gn + j < N; ++j) dst[j] = pv[j];
-        }
-    }
-}
-
-template <int BN, int WAVES_N, int MODE>
-hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream) {
-    dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, 256));
-    dim3 block(2 * WAVES_N * 64);
-    if (a.asym)
-        k_gemm_pipe<BN, WAVES_N, true, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
-    else
-        k_gemm_pipe<BN, WAVES_N, false, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
-    return hipGetLastError();
-}
-
-
-// ===========================================================================
 // 32x32x32 kernel: same data flow as k_gemm_w4a4 (packed tiles -> registers
 // -> unpacked int8 in double-buffered LDS, one barrier per 128-code K tile),
 // on v_mfma_i32_32x32x32_i8, which sustains ~96% of the int8 peak on gfx950
@@ -551,24 +316,7 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t stream) {
 // ===========================================================================
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-// Interleaving pattern for the scheduler, one step per MFMA: the MFMA, then
-// an even share of the remaining LDS reads, VALU instructions and LDS writes.
-template <int NMF, int NRD, int NVALU, int NWR, int I = 0>
-__device__ __forceinline__ void il_sched() {
-    if constexpr (I < NMF) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-        constexpr int rd = (I + 1) * NRD / NMF - I * NRD / NMF;
-        if constexpr (rd > 0) __builtin_amdgcn_sched_group_barrier(0x100, rd, 0);   // DS read
-        constexpr int va = (I + 1) * NVALU / NMF - I * NVALU / NMF;
-        if constexpr (va > 0) __builtin_amdgcn_sched_group_barrier(0x002, va, 0);   // VALU
-        constexpr int wr = (I + 1) * NWR / NMF - I * NWR / NMF;
-        if constexpr (wr > 0) __builtin_amdgcn_sched_group_barrier(0x200, wr, 0);   // DS write
-        il_sched<NMF, NRD, NVALU, NWR, I + 1>();
-    }
-}
-
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, bool ASYM, int MODE, bool IL = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, bool ASYM, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm32(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
@@ -736,21 +484,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm32(
         }
         // the last iteration stores a clamped duplicate that nobody reads
         store_tile(buf ^ 1, std::integral_constant<int, SN>{});
-        if constexpr (IL) {
-            // Instruction interleaving for the scheduler: the fragment reads of
-            // k-step 0 and the global loads first, then every MFMA followed by
-            // a share of the remaining LDS reads, the unpack VALU work and the
-            // LDS writes of the next tile, so the MFMA pipe stays fed while
-            // the wave does its other work.
-            constexpr int NMF = 4 * FM * FN;              // MFMAs per tile
-            constexpr int NRD = 4 * (FM + FN);            // fragment reads per tile
-            constexpr int NWR = 2 * (ALD + BLD);          // LDS writes per tile
-            constexpr int NVALU = 10 * (ALD + BLD);       // unpack + address VALU (approx.)
-            constexpr int NVM = ALD + BLD + (ASYM ? BLD : 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);   // DS read
-            __builtin_amdgcn_sched_group_barrier(0x020, NVM, 0);       // VMEM read
-            il_sched<NMF, NRD - FM - FN, NVALU, NWR>();
-        }
         __syncthreads();
     };
 
@@ -796,15 +529,15 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm32(
     }
 }
 
-template <int BM, int BN, int WM_, int WN_, int PD, int MODE, bool IL = false>
+template <int BM, int BN, int WM_, int WN_, int PD, int MODE>
 hipError_t launch32(const GemmArgs& a, hipStream_t stream) {
     dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM));
     dim3 block(WM_ * WN_ * 64);
     if (a.asym)
-        k_gemm32<BM, BN, WM_, WN_, PD, true, MODE, IL><<<grid, block, 0, stream>>>(
+        k_gemm32<BM, BN, WM_, WN_, PD, true, MODE><<<grid, block, 0, stream>>>(
             a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
     else
-        k_gemm32<BM, BN, WM_, WN_, PD, false, MODE, IL><<<grid, block, 0, stream>>>(
+        k_gemm32<BM, BN, WM_, WN_, PD, false, MODE><<<grid, block, 0, stream>>>(
             a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
     return hipGetLastError();
 }
@@ -855,7 +588,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int M, int N, int K,
     int group_size) {
     constexpr int NW = WAVES_M * WAVES_N;
-    constexpr int NT = NW * 64;
     constexpr int WM = BM / WAVES_M;
     constexpr int WN = BN / WAVES_N;
     constexpr int FM = WM / 32;
@@ -1085,6 +817,294 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ===========================================================================
+// Decode kernel (M <= 64 tokens): the weight stream is the whole cost, so the
+// packed weights go from HBM straight into registers, with no LDS staging.
+// A workgroup owns 16*FN output columns; its NW waves split the K tiles
+// evenly and each streams its range with loads D-1 tiles ahead (the tile
+// index is clamped, so every step issues the same loads).  A lane loads 16
+// packed bytes of one row per fragment, the row segment of its lane group
+// (lane >> 4), and unpacks them into the even-code and odd-code operands of
+// two 16x16x64 MFMA k-steps; A and B use the same order.  Activation rows
+// past M are clamped and their sums dropped.
+//
+// The workgroup first copies its rows' scales and zero points (one 32-bit
+// word per row and group: fp16 scale | zero point << 16) into LDS, and, when
+// they fit (ALDS, one row fragment), the M activation rows; the K loop then
+// reads them with LDS loads instead of one small global load per tile.  The
+// waves' partial sums (exact int32 per channel, fp32 per group) are added in
+// LDS in wave order and written by the whole workgroup.
+// ===========================================================================
+constexpr int kDecLdsMax = 160 * 1024;      // LDS of one CU
+constexpr int kDecAldsMax = 152 * 1024;     // budget for staged activations + scales
+
+template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS>
+__global__ __launch_bounds__(NW * 64) void k_gemm_dec(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
+    const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
+    const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int M, int N, int K,
+    int group_size) {
+    static_assert(MODE == kModeChan || MODE == kModeGroup, "fp16 output modes only");
+    static_assert(D >= 2 && D <= 8, "prefetch depth");
+    static_assert(!ALDS || FM == 1, "staged activations: one row fragment");
+    constexpr int BN = 16 * FN;
+    constexpr int NT = NW * 64;
+    constexpr int SLOTS = FM * FN * 4;          // accumulator values per lane
+    constexpr bool SZ = (MODE == kModeGroup) || ASYM;
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    const int lane = threadIdx.x & 63;
+    // wave-uniform values live in scalar registers: tile ranges, group
+    // indices and the tile part of every address
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int frow = lane & 15;
+    const int fks = lane >> 4;
+    const int n0 = blockIdx.x * BN;
+    const int KB = K / 2;
+    const int KT = K / BK;
+    const int TPG = group_size / BK;
+    const int G = K / group_size;
+    const int t0 = (KT * wave) / NW;
+    const int t1 = (KT * (wave + 1)) / NW;
+    const int GP = G + 1;          // scale-table row: an odd number of words
+    const int AP = KB + 16;        // staged activation row, padded one chunk
+    uint32_t* sz = reinterpret_cast<uint32_t*>(lds);
+    uint8_t* al = lds + (SZ ? BN * GP * 4 : 0);
+
+    // ---- stage the scale table and the activations ------------------------
+    if constexpr (SZ) {
+        for (int r = wave; r < BN; r += NW) {
+            const size_t nrow = static_cast<size_t>(min(n0 + r, N - 1)) * G;
+            for (int gb = 0; gb < G; gb += 256) {
+                uint32_t v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int g = min(gb + lane + 64 * j, G - 1);
+                    v[j] = (MODE == kModeGroup) ? s_w[nrow + g] : 0u;
+                    if constexpr (ASYM) v[j] |= static_cast<uint32_t>(h2f(z_w[nrow + g])) << 16;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (gb + lane + 64 * j < G) sz[r * GP + gb + lane + 64 * j] = v[j];
+            }
+        }
+    }
+    if constexpr (ALDS) {
+        const int CH = KB / 16;
+        for (int c = threadIdx.x; c < CH; c += NT)
+            for (int r0 = 0; r0 < M; r0 += 4) {
+                uint4 v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(min(r0 + j, M - 1)) * KB + c * 16);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (r0 + j < M) *reinterpret_cast<uint4*>(al + (r0 + j) * AP + c * 16) = v[j];
+            }
+    }
+    if constexpr (SZ || ALDS) __syncthreads();
+
+    // per-lane byte offsets (32-bit) from the wave-uniform bases
+    uint32_t aoff[FM], boff[FN], zoff[FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+        const int r = min(a * 16 + frow, M - 1);
+        aoff[a] = static_cast<uint32_t>(r) * (ALDS ? AP : KB) + fks * 16;
+    }
+#pragma unroll
+    for (int b = 0; b < FN; ++b) {
+        const int r = min(n0 + b * 16 + frow, N - 1) - n0;
+        boff[b] = static_cast<uint32_t>(r) * KB + fks * 16;
+        zoff[b] = static_cast<uint32_t>(b * 16 + frow) * GP;
+    }
+    const uint8_t* wbase = Wq + static_cast<size_t>(n0) * KB;
+
+    v4i acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) acc[a][b] = v4i{0, 0, 0, 0};
+    constexpr int GF = (MODE == kModeGroup) ? 1 : 0;
+    float facc[GF ? FM : 1][GF ? FN : 1][4];
+#pragma unroll
+    for (int a = 0; a < (GF ? FM : 1); ++a)
+#pragma unroll
+        for (int b = 0; b < (GF ? FN : 1); ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
+
+    uint4 abuf[ALDS ? 1 : D][FM], bbuf[D][FN];
+    // issue position: tile it, clamped to the last tile of the range
+    int it = t0;
+    auto issue = [&](auto S) {
+        constexpr int SL = decltype(S)::value;
+        if constexpr (!ALDS) {
+            const uint8_t* xa = Xq + static_cast<size_t>(it) * 64;
+#pragma unroll
+            for (int a = 0; a < FM; ++a) abuf[SL][a] = *reinterpret_cast<const uint4*>(xa + aoff[a]);
+        }
+        const uint8_t* wb = wbase + static_cast<size_t>(it) * 64;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) bbuf[SL][b] = *reinterpret_cast<const uint4*>(wb + boff[b]);
+        if (it + 1 < t1) ++it;
+    };
+    // compute position: group cg of tile t and its place cr inside the group
+    int cg = t0 / TPG, cr = t0 - (t0 / TPG) * TPG;
+    auto compute = [&](int t, auto S) {
+        constexpr int SL = decltype(S)::value;
+        v4i aev[FM], aod[FM], bev[FN], bod[FN];
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+            uint4 w;
+            if constexpr (ALDS)
+                w = *reinterpret_cast<const uint4*>(al + aoff[a] + t * 64);
+            else
+                w = abuf[SL][a];
+            uint4 ev, od;
+            unpack_signed16(w, ev, od);
+            aev[a] = v4i{static_cast<int>(ev.x), static_cast<int>(ev.y), static_cast<int>(ev.z), static_cast<int>(ev.w)};
+            aod[a] = v4i{static_cast<int>(od.x), static_cast<int>(od.y), static_cast<int>(od.z), static_cast<int>(od.w)};
+        }
+        uint32_t szv[FN];
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            if constexpr (SZ) szv[b] = sz[zoff[b] + cg];
+            uint4 ev, od;
+            if constexpr (ASYM) {
+                const uint32_t z = szv[b] >> 16;
+                unpack_asym(bbuf[SL][b], 0x80808080u - z * 0x01010101u, ev, od);
+            } else {
+                unpack_signed16(bbuf[SL][b], ev, od);
+            }
+            bev[b] = v4i{static_cast<int>(ev.x), static_cast<int>(ev.y), static_cast<int>(ev.z), static_cast<int>(ev.w)};
+            bod[b] = v4i{static_cast<int>(od.x), static_cast<int>(od.y), static_cast<int>(od.z), static_cast<int>(od.w)};
+        }
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aev[a], bev[b], acc[a][b], 0, 0, 0);
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod[a], bod[b], acc[a][b], 0, 0, 0);
+        const bool group_end = (++cr == TPG);
+        if constexpr (MODE == kModeGroup) {
+            // end of a weight group, or of this wave's range inside one
+            if (group_end || t + 1 == t1) {
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const float sw = h2f(static_cast<uint16_t>(szv[b] & 0xFFFFu));
+#pragma unroll
+                    for (int a = 0; a < FM; ++a)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            facc[a][b][r] = fmaf(static_cast<float>(acc[a][b][r]), sw, facc[a][b][r]);
+                            acc[a][b][r] = 0;
+                        }
+                }
+            }
+        }
+        if (group_end) {
+            cr = 0;
+            ++cg;
+        }
+    };
+
+    if (t0 < t1) {
+        static_for<0, D - 1>([&](auto U) { issue(U); });
+        for (int t = t0; t < t1; t += D) {
+            static_for<0, D>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                issue(std::integral_constant<int, (u + D - 1) % D>{});
+                if (t + u < t1) compute(t + u, std::integral_constant<int, u>{});
+            });
+        }
+    }
+
+    // ---- add the waves' partial sums in LDS, in wave order -------------------
+    if constexpr (SZ || ALDS) __syncthreads();      // the staged data is dead
+    float* red = reinterpret_cast<float*>(lds);     // [NW][SLOTS][64]
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = (a * FN + b) * 4 + r;
+                red[(wave * SLOTS + i) * 64 + lane] = (MODE == kModeGroup) ? facc[GF ? a : 0][GF ? b : 0][r]
+                                                                           : __int_as_float(acc[a][b][r]);
+            }
+    __syncthreads();
+    constexpr float kUnshift = ASYM ? (1.0f / 16.0f) : (1.0f / 256.0f);
+    for (int sl = threadIdx.x; sl < SLOTS * 64; sl += NT) {
+        const int i = sl >> 6;
+        const int l = sl & 63;
+        const int a = i / (FN * 4);
+        const int b = (i >> 2) % FN;
+        const int r = i & 3;
+        const int gm = a * 16 + 4 * (l >> 4) + r;
+        const int gn = n0 + b * 16 + (l & 15);
+        if (gm >= M || gn >= N) continue;
+        float v;
+        if constexpr (MODE == kModeGroup) {
+            v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += red[(w * SLOTS + i) * 64 + l];
+        } else {
+            int sum = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sum += __float_as_int(red[(w * SLOTS + i) * 64 + l]);
+            v = static_cast<float>(sum) * h2f(s_w[gn]);
+        }
+        Y[static_cast<size_t>(gm) * N + gn] = f2h(v * s_x[gm] * kUnshift);
+    }
+}
+
+template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS>
+hipError_t launch_dec_k(const GemmArgs& a, size_t lds, hipStream_t stream) {
+    auto* kern = &k_gemm_dec<FM, FN, NW, D, ASYM, MODE, ALDS>;
+    if (lds > 64 * 1024) {
+        // more than the default dynamic LDS limit: raise it once per device
+        static bool raised[64] = {};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= 64 || !raised[dev]) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
+            if (e != hipSuccess) return e;
+            if (dev >= 0 && dev < 64) raised[dev] = true;
+        }
+    }
+    kern<<<dim3(ceil_div(a.N, 16 * FN)), dim3(NW * 64), lds, stream>>>(
+        a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
+    return hipGetLastError();
+}
+
+template <int FM, int FN, int NW, int D, bool ASYM, int MODE>
+hipError_t launch_dec_a(const GemmArgs& a, hipStream_t stream) {
+    constexpr int BN = 16 * FN;
+    const int G = a.K / a.group_size;
+    const bool sz = (MODE == kModeGroup) || ASYM;
+    const size_t szb = sz ? static_cast<size_t>(BN) * (G + 1) * 4 : 0;
+    const size_t alb = static_cast<size_t>(a.M) * (a.K / 2 + 16);
+    const size_t red = static_cast<size_t>(NW) * FM * FN * 4 * 64 * 4;
+    if constexpr (FM == 1) {
+        if (szb + alb <= static_cast<size_t>(kDecAldsMax))
+            return launch_dec_k<FM, FN, NW, D, ASYM, MODE, true>(a, szb + alb > red ? szb + alb : red,
+                                                                 stream);
+    }
+    return launch_dec_k<FM, FN, NW, D, ASYM, MODE, false>(a, szb > red ? szb : red, stream);
+}
+
+template <int FM, int FN, int NW, int D, int MODE>
+hipError_t launch_dec(const GemmArgs& a, hipStream_t stream) {
+    return a.asym ? launch_dec_a<FM, FN, NW, D, true, MODE>(a, stream)
+                  : launch_dec_a<FM, FN, NW, D, false, MODE>(a, stream);
+}
+
 template <int BM, int BN, int WM_, int WN_, int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t stream) {
     dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM));
@@ -1100,73 +1120,115 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t stream) {
 
 using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
 
-// Tile configurations (BM x BN, waves along M x N) for the fp16-output
-// modes; index 0 is the default of each mode.
-struct TileCfg {
-    int bm, bn;
+// A kernel configuration: launchers for the per-channel and per-group fp16
+// modes (nullptr where the per-group fp32 accumulators would not fit the
+// register file) and a name for traces.
+struct KernelCfg {
+    const char* name;
     LaunchFn chan, group;
 };
 
-#define W4A4_TILE(BM, BN, WM_, WN_)                                                     \
-    TileCfg {                                                                          \
-        BM, BN, &launch_mode<BM, BN, WM_, WN_, kModeChan>,                              \
-            &launch_mode<BM, BN, WM_, WN_, kModeGroup>                                  \
-    }
-// tiles whose per-group fp32 accumulators do not fit the register file
-#define W4A4_TILE_CHAN(BM, BN, WM_, WN_) \
-    TileCfg { BM, BN, &launch_mode<BM, BN, WM_, WN_, kModeChan>, nullptr }
+#define W4A4_CFG(NAME, L) KernelCfg{NAME, &L<kModeChan>, &L<kModeGroup>}
+#define W4A4_CFG_CHAN(NAME, L) KernelCfg{NAME, &L<kModeChan>, nullptr}
 
-const TileCfg kTiles[] = {
-    W4A4_TILE_CHAN(256, 256, 2, 4),
-    W4A4_TILE_CHAN(256, 256, 2, 2),
-    W4A4_TILE_CHAN(256, 192, 2, 4),
-    W4A4_TILE(256, 128, 2, 4),
-    W4A4_TILE(256, 128, 4, 2),
-    W4A4_TILE(128, 256, 2, 4),
-    W4A4_TILE(128, 128, 2, 2),
-    W4A4_TILE(128, 128, 2, 4),
-    TileCfg{256, 192, &launch_pipe<192, 2, kModeChan>, nullptr},
-    TileCfg{256, 192, &launch_pipe<192, 4, kModeChan>, nullptr},
-    TileCfg{256, 128, &launch_pipe<128, 2, kModeChan>, nullptr},
-    TileCfg{256, 128, &launch_pipe<128, 4, kModeChan>, &launch_pipe<128, 4, kModeGroup>},
-    // 32x32x32 kernels, prefetch depth 1..3
-    TileCfg{256, 256, &launch32<256, 256, 2, 4, 1, kModeChan>, nullptr},
-    TileCfg{256, 256, &launch32<256, 256, 2, 4, 2, kModeChan>, nullptr},
-    TileCfg{256, 256, &launch32<256, 256, 2, 4, 3, kModeChan>, nullptr},
-    TileCfg{256, 192, &launch32<256, 192, 2, 2, 1, kModeChan>, nullptr},
-    TileCfg{256, 192, &launch32<256, 192, 2, 2, 2, kModeChan>, nullptr},
-    TileCfg{256, 192, &launch32<256, 192, 2, 2, 3, kModeChan>, nullptr},
-    TileCfg{256, 128, &launch32<256, 128, 4, 2, 1, kModeChan>, &launch32<256, 128, 4, 2, 1, kModeGroup>},
-    TileCfg{256, 128, &launch32<256, 128, 4, 2, 2, kModeChan>, &launch32<256, 128, 4, 2, 2, kModeGroup>},
-    TileCfg{256, 128, &launch32<256, 128, 4, 2, 3, kModeChan>, &launch32<256, 128, 4, 2, 3, kModeGroup>},
-    TileCfg{128, 128, &launch32<128, 128, 2, 2, 2, kModeChan>, &launch32<128, 128, 2, 2, 2, kModeGroup>},
-    TileCfg{128, 128, &launch32<128, 128, 2, 2, 3, kModeChan>, &launch32<128, 128, 2, 2, 3, kModeGroup>},
-    // explicitly interleaved schedules
-    TileCfg{256, 256, &launch32<256, 256, 2, 4, 3, kModeChan, true>, nullptr},
-    TileCfg{256, 192, &launch32<256, 192, 2, 2, 3, kModeChan, true>, nullptr},
-    TileCfg{256, 256, &launch32<256, 256, 2, 2, 2, kModeChan, true>, nullptr},
-    TileCfg{256, 128, &launch32<256, 128, 4, 2, 2, kModeChan, true>, &launch32<256, 128, 4, 2, 2, kModeGroup, true>},
-    TileCfg{128, 128, &launch32<128, 128, 2, 2, 3, kModeChan, true>, &launch32<128, 128, 2, 2, 3, kModeGroup, true>},
-    // direct-to-LDS kernels (index 28..)
-    TileCfg{256, 256, &launch_dl<256, 256, 2, 4, 3, kModeChan>, nullptr},
-    TileCfg{256, 256, &launch_dl<256, 256, 2, 4, 4, kModeChan>, nullptr},
-    TileCfg{256, 256, &launch_dl<256, 256, 2, 2, 4, kModeChan>, nullptr},
-    TileCfg{256, 192, &launch_dl<256, 192, 2, 2, 4, kModeChan>, nullptr},
-    TileCfg{256, 128, &launch_dl<256, 128, 4, 2, 4, kModeChan>, &launch_dl<256, 128, 4, 2, 4, kModeGroup>},
-    TileCfg{256, 128, &launch_dl<256, 128, 2, 2, 4, kModeChan>, &launch_dl<256, 128, 2, 2, 4, kModeGroup>},
-    TileCfg{128, 128, &launch_dl<128, 128, 2, 2, 4, kModeChan>, &launch_dl<128, 128, 2, 2, 4, kModeGroup>},
+template <int MODE> hipError_t dl256x256_2x4_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 2, 4, 4, MODE>(a, s); }
+template <int MODE> hipError_t dl256x256_2x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 2, 4, 3, MODE>(a, s); }
+template <int MODE> hipError_t dl256x256_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 2, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t dl256x192_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 192, 2, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t dl256x128_4x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 128, 4, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t dl256x128_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 128, 2, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t dl128x128_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t r16_256x256_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 256, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t r16_256x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 128, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t r16_128x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<128, 128, 2, 4, MODE>(a, s); }
+template <int MODE> hipError_t r32_256x256_2x4_p2(const GemmArgs& a, hipStream_t s) { return launch32<256, 256, 2, 4, 2, MODE>(a, s); }
+template <int MODE> hipError_t r32_256x128_4x2_p2(const GemmArgs& a, hipStream_t s) { return launch32<256, 128, 4, 2, 2, MODE>(a, s); }
+
+// Prefill configurations (M > 64).  dl: direct-to-LDS 32x32x32 kernel;
+// r16 / r32: register-staged unpack-to-LDS kernels on 16x16x64 / 32x32x32.
+const KernelCfg kTiles[] = {
+    W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 2x4, 4 stages>", dl256x256_2x4_s4),
+    W4A4_CFG("k_gemm_dl<128x128, waves 2x2, 4 stages>", dl128x128_2x2_s4),
+    W4A4_CFG("k_gemm_w4a4<128x128, waves 2x4>", r16_128x128_2x4),
+    W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 2x4, 3 stages>", dl256x256_2x4_s3),
+    W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 2x2, 4 stages>", dl256x256_2x2_s4),
+    W4A4_CFG_CHAN("k_gemm_dl<256x192, waves 2x2, 4 stages>", dl256x192_2x2_s4),
+    W4A4_CFG("k_gemm_dl<256x128, waves 4x2, 4 stages>", dl256x128_4x2_s4),
+    W4A4_CFG("k_gemm_dl<256x128, waves 2x2, 4 stages>", dl256x128_2x2_s4),
+    W4A4_CFG_CHAN("k_gemm_w4a4<256x256, waves 2x4>", r16_256x256_2x4),
+    W4A4_CFG("k_gemm_w4a4<256x128, waves 2x4>", r16_256x128_2x4),
+    W4A4_CFG_CHAN("k_gemm32<256x256, waves 2x4, prefetch 2>", r32_256x256_2x4_p2),
+    W4A4_CFG("k_gemm32<256x128, waves 4x2, prefetch 2>", r32_256x128_4x2_p2),
 };
-#undef W4A4_TILE
-#undef W4A4_TILE_CHAN
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-// Developer override for tile sweeps and tests: W4A4_GEMM_TILE=<index into
-// kTiles> (read at every call; out-of-range or unset means automatic).
-int tile_override() {
-    const char* e = getenv("W4A4_GEMM_TILE");
+// Decode configurations (M <= 64), per row-fragment count FM = 1, 2, 4:
+// 16*FN columns per workgroup, NW waves splitting K, prefetch depth D.
+template <int FM, int FN, int NW, int D>
+struct Dec {
+    template <int MODE>
+    static hipError_t run(const GemmArgs& a, hipStream_t s) { return launch_dec<FM, FN, NW, D, MODE>(a, s); }
+};
+#define W4A4_DEC(FM, FN, NW, D) \
+    KernelCfg{"k_gemm_dec<FM " #FM ", FN " #FN ", waves " #NW ", depth " #D ">", \
+              &Dec<FM, FN, NW, D>::run<kModeChan>, &Dec<FM, FN, NW, D>::run<kModeGroup>}
+constexpr int kNumDec = 4;
+const KernelCfg kDec[3][kNumDec] = {
+    {W4A4_DEC(1, 1, 16, 4), W4A4_DEC(1, 2, 16, 4), W4A4_DEC(1, 1, 8, 6), W4A4_DEC(1, 2, 8, 6)},
+    {W4A4_DEC(2, 1, 16, 4), W4A4_DEC(2, 2, 8, 4), W4A4_DEC(2, 1, 8, 4), W4A4_DEC(2, 2, 8, 3)},
+    {W4A4_DEC(4, 1, 8, 3), W4A4_DEC(4, 2, 8, 3), W4A4_DEC(4, 1, 8, 2), W4A4_DEC(4, 2, 8, 2)},
+};
+#undef W4A4_DEC
+#undef W4A4_CFG
+#undef W4A4_CFG_CHAN
+
+const KernelCfg kI32{"k_gemm_w4a4<64x64, waves 2x2, int32 out>", nullptr, nullptr};
+
+// Developer overrides for sweeps and tests (read at every call; unset or out
+// of range means automatic): W4A4_GEMM_TILE indexes the prefill table,
+// W4A4_GEMM_DECODE the decode variants.
+int env_index(const char* name, int n) {
+    const char* e = getenv(name);
     if (e == nullptr || *e == '\0') return -1;
     const int v = atoi(e);
-    return (v >= 0 && v < kNumTiles) ? v : -1;
+    return (v >= 0 && v < n) ? v : -1;
+}
+
+const KernelCfg& choose(const GemmArgs& a) {
+    const bool grouped = (a.K / a.group_size) > 1;
+    const int cus = device_cu_count();
+    if (a.M <= 64) {
+        const int fi = a.M <= 16 ? 0 : (a.M <= 32 ? 1 : 2);
+        int v = env_index("W4A4_GEMM_DECODE", kNumDec);
+        if (v < 0) {
+            // measured on MI355X: one 16-column fragment per workgroup while
+            // two workgroups fit a CU, two once the staged activations fill
+            // the LDS (or for two and four row fragments) and the grid still
+            // covers every CU
+            bool wide = ceil_div(a.N, 32) >= cus;
+            if (fi == 0) {
+                const size_t staged = static_cast<size_t>(a.M) * (a.K / 2 + 16);
+                wide = wide && staged > 64 * 1024;
+            }
+            v = wide ? 1 : 0;
+        }
+        return kDec[fi][v];
+    }
+    int t = env_index("W4A4_GEMM_TILE", kNumTiles);
+    if (t < 0 || (grouped && kTiles[t].group == nullptr)) {
+        // measured on MI355X: direct-to-LDS 256x256 tiles when the grid
+        // covers the CUs several times over, direct-to-LDS 128x128 tiles for
+        // about one wave of 256x256 tiles, 16x16x64 128x128 (8 waves) for the
+        // per-group mode
+        const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
+        if (grouped)
+            t = 2;
+        else if (tiles256 >= 2L * cus)
+            t = 0;
+        else
+            t = 1;
+    }
+    return kTiles[t];
 }
 
 }  // namespace
@@ -1181,6 +1243,11 @@ size_t gemm_workspace_bytes(int M, int N, int K, int group_size) {
     return 0;
 }
 
+const char* gemm_kernel_name(const GemmArgs& a, bool i32_out) {
+    if (i32_out) return kI32.name;
+    return choose(a).name;
+}
+
 hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
     (void)ws;
@@ -1188,26 +1255,8 @@ hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_byte
     if (a.M == 0) return hipSuccess;
     if (i32_out) return launch_mode<64, 64, 2, 2, kModeI32>(a, stream);
     const bool grouped = (a.K / a.group_size) > 1;
-    if (a.M <= 64) {
-        if (grouped) return launch_mode<64, 64, 2, 2, kModeGroup>(a, stream);
-        return launch_mode<64, 64, 2, 2, kModeChan>(a, stream);
-    }
-    int t = tile_override();
-    if (t < 0 || (grouped && kTiles[t].group == nullptr)) {
-        // measured on MI355X: direct-to-LDS 256x256 tiles when the grid
-        // covers the CUs several times over, direct-to-LDS 128x128 tiles for
-        // about one wave of 256x256 tiles, 16x16x64 128x128 (8 waves) for the
-        // per-group mode
-        const int cus = device_cu_count();
-        const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
-        if (grouped)
-            t = 7;
-        else if (tiles256 >= 2L * cus)
-            t = 29;     // direct-to-LDS 256x256, 8 waves, 4 stages
-        else
-            t = 34;     // direct-to-LDS 128x128, 4 waves, 4 stages
-    }
-    return grouped ? kTiles[t].group(a, stream) : kTiles[t].chan(a, stream);
+    const KernelCfg& k = choose(a);
+    return grouped ? k.group(a, stream) : k.chan(a, stream);
 }
 
 }  // namespace w4a4

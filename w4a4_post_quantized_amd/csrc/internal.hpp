@@ -35,6 +35,8 @@ struct GemmArgs {
 };
 
 size_t gemm_workspace_bytes(int M, int N, int K, int group_size);
+// name of the configuration gemm_launch would use (launches nothing)
+const char* gemm_kernel_name(const GemmArgs& a, bool i32_out);
 hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
