@@ -57,7 +57,8 @@ def test_transform_permutation_is_exact():
     assert_codes_match(O.unpack_nibbles(Xq, True), r["q"], r["t"])
 
 
-FACTORS = [(16, 16), (32, 32), (64, 64), (64, 128), (112, 128), (224, 128), (8, 2), (128, 256)]
+FACTORS = [(16, 16), (32, 32), (64, 64), (64, 128), (112, 128), (224, 128), (8, 2), (128, 256),
+           (160, 128), (256, 128)]
 
 
 @pytest.mark.parametrize("n1,n2", FACTORS)
@@ -75,7 +76,8 @@ def test_transform_accuracy(n1, n2):
 
 
 @pytest.mark.parametrize("n1,n2,M", [(16, 16, 16), (64, 64, 130), (112, 128, 9), (224, 128, 3),
-                                     (64, 128, 65), (128, 256, 2)])
+                                     (64, 128, 65), (128, 256, 2), (224, 128, 1), (224, 128, 37),
+                                     (192, 128, 5)])
 def test_transform_quant_parity(n1, n2, M):
     log(f"transform_quant ({n1},{n2}) M={M}")
     wl = custom_workload(M=M, n1=n1, n2=n2, N=16, outliers=(7, 100), pivot=100.0, seed=M)

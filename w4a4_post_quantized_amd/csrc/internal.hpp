@@ -10,7 +10,7 @@
 namespace w4a4 {
 
 // ---- activation path (transform_quant.hip) --------------------------------
-enum class TqPath { Fused, Split };
+enum class TqPath { Fused, Cols, Split };
 
 TqPath tq_select_path(int M, int n1, int n2, bool has_c);
 size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c);

@@ -42,6 +42,8 @@ namespace {
 
 constexpr int kSplitThreads = 256;
 
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
 __global__ __launch_bounds__(256) void k_tq_stage1(const uint16_t* __restrict__ X, int K,
                                                    int n2, const float* __restrict__ P2,
                                                    const float* __restrict__ c,
@@ -97,13 +99,22 @@ __global__ __launch_bounds__(256) void k_tq_stage2(const float* __restrict__ T, 
 }
 
 __global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, int K, float alpha,
-                                                  const uint32_t* __restrict__ amax,
+                                                  const uint32_t* __restrict__ amax, int nparts,
                                                   uint8_t* __restrict__ Xq,
                                                   float* __restrict__ s_x) {
     const int m = blockIdx.x;
     const int idx = blockIdx.y * blockDim.x + threadIdx.x;
-    const float a = __uint_as_float(amax[m]);
-    const float s = alpha * a / 7.0f;
+    // the token's absmax: the largest of its partial maxima (bit patterns of
+    // non-negative floats order like the floats), reduced by the workgroup
+    __shared__ float red[4];
+    float ab = 0.0f;
+    for (int q = threadIdx.x; q < nparts; q += 256)
+        ab = fmaxf(ab, __uint_as_float(amax[static_cast<size_t>(m) * nparts + q]));
+    ab = wave_max(ab);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ab;
+    __syncthreads();
+    ab = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = alpha * ab / 7.0f;
     if (idx == 0) s_x[m] = s;
     const int e0 = idx * 8;
     if (e0 >= K) return;
@@ -441,21 +452,307 @@ FusedFn fused_for(int n1, int n2) {
     return nullptr;
 }
 
+// ===========================================================================
+// Column-block MFMA path: factors whose P1 fragments do not fit one LDS (n1
+// above 128), and few tokens.  The unit of work is one token m and one
+// 16-column block cb of Z, computed by one wave with the arithmetic of the
+// fused path (stage 1 on X̄ fp16 and split P2, stage 2 on split T and split
+// P1, power-of-two prescales).  The 16-row blocks of Z (stage-2 outputs) are
+// split into `parts` ranges, one per grid row.  A workgroup of 8 waves is one
+// token and one range: it stages the token's X̄ (rows padded by 16 bytes) and
+// the P1 fragments of its range in LDS, with every load issued before the
+// first wait, and its waves are the token's 8 column blocks; each redoes
+// stage 1 for its block (parts > 1 spreads a handful of tokens over many
+// CUs).  Z goes to the workspace in fp32 with one absmax per (unit,
+// part); k_tq_quant then takes each token's largest partial maximum.
+// ===========================================================================
+constexpr int kColsWaves = 8;
+constexpr int kColsLdsMax = 159 * 1024;       // dynamic LDS of one workgroup
+
+template <int N1, int N2>
+struct ColsCfg {
+    static_assert(N1 % 16 == 0 && N2 % 32 == 0, "factors: n1 multiple of 16, n2 of 32");
+    static constexpr int K = N1 * N2;
+    static constexpr int RB = N1 / 16;           // 16-row blocks of T and Z
+    static constexpr int CB = N2 / 16;           // 16-column blocks (units per token)
+    static constexpr int KS1 = N2 / 32;          // stage-1 MFMA k-steps
+    static constexpr int KS2 = (N1 + 31) / 32;   // stage-2 MFMA k-steps
+    static constexpr int FRAG = 64 * 8;          // fp16 elements of one fragment
+    static constexpr int FRAG_BYTES = 2 * FRAG * 2;   // hi + lo
+    static constexpr int XROW = N2 * 2 + 16;         // staged X̄ row, bytes
+    static constexpr int XBYTES = N1 * XROW;
+    // row blocks of P1 fragments that fit beside the staged token
+    static constexpr int MAX_RBP = (kColsLdsMax - XBYTES) / (KS2 * FRAG_BYTES);
+    static_assert(CB == kColsWaves, "one wave per 16-column block of a token");
+    static_assert(MAX_RBP >= 1, "staged token too large");
+};
+
+// row blocks per part and number of parts for M tokens (every part non-empty)
+template <int N1, int N2>
+void cols_parts(int M, int* rbp, int* parts) {
+    using C = ColsCfg<N1, N2>;
+    const int max_rbp = C::MAX_RBP;
+    // about 8 waves per CU over 256 CUs
+    const long units = static_cast<long>(M) * C::CB;
+    long want = (2048 + units - 1) / units;
+    if (want < 1) want = 1;
+    if (want > C::RB) want = C::RB;
+    int r = static_cast<int>((C::RB + want - 1) / want);
+    if (r > max_rbp) r = max_rbp;
+    *rbp = r;
+    *parts = (C::RB + r - 1) / r;
+}
+
+template <int N1, int N2>
+__global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __restrict__ X, int M,
+                                                             const float* __restrict__ P1,
+                                                             const float* __restrict__ P2, int rbp,
+                                                             int parts, float* __restrict__ Zf,
+                                                             uint32_t* __restrict__ amax) {
+    using C = ColsCfg<N1, N2>;
+    constexpr int K = C::K;
+    constexpr int NT = kColsWaves * 64;
+    extern __shared__ __align__(16) _Float16 cl[];
+    __shared__ float red[kColsWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+    const int li = lane & 15;
+    const int part = blockIdx.y;
+    const int ob0 = part * rbp;
+    const int nob = min(C::RB - ob0, rbp);
+    const int nf = nob * C::KS2;
+    _Float16* p1hi = cl;
+    _Float16* p1lo = cl + nf * C::FRAG;
+    uint8_t* xs = reinterpret_cast<uint8_t*>(cl + 2 * nf * C::FRAG);
+    const int m = blockIdx.x;                        // this workgroup's token
+
+    // ---- the token's X̄ -> LDS (loads issued together with P1's) -------------
+    constexpr int XCH = C::K / 8;                    // 16-byte chunks of one token
+    constexpr int XLD = (XCH + NT - 1) / NT;
+    uint4 xr[XLD];
+#pragma unroll
+    for (int i = 0; i < XLD; ++i)
+        xr[i] = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * C::K)[min(tid + i * NT, XCH - 1)];
+
+    // ---- P1 fragments of row blocks ob0 .. ob0+nob-1 into LDS ----------------
+    // fragment (ob, sk), lane (gg, ii), element e holds P1[rho][16*ob + ii],
+    // rho = 32 sk + 4 gg + e (e < 4) or 32 sk + 16 + 4 gg + (e - 4): the rows
+    // of T that the stage-1 accumulators of lane group gg hold.  Thread tid
+    // owns element tid of every fragment; all its loads are issued before
+    // the power-of-two prescale (the part's max |P1|) is known.
+    constexpr int MAXNF = (C::MAX_RBP < C::RB ? C::MAX_RBP : C::RB) * C::KS2;
+    static_assert(C::FRAG == NT, "one fragment element per thread");
+    float pv[MAXNF];
+    float m1 = 0.0f;
+    {
+        const int e = tid & 7;
+        const int gg = (tid >> 3) >> 4, ii = (tid >> 3) & 15;
+#pragma unroll
+        for (int f = 0; f < MAXNF; ++f) {
+            const int fc = min(f, nf - 1);
+            const int sk = fc % C::KS2;
+            const int ob = ob0 + fc / C::KS2;
+            const int rho = 32 * sk + (e < 4 ? 4 * gg + e : 16 + 4 * gg + (e - 4));
+            pv[f] = P1[min(rho, N1 - 1) * N1 + 16 * ob + ii];
+            if (rho >= N1) pv[f] = 0.0f;
+            m1 = fmaxf(m1, fabsf(pv[f]));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < XLD; ++i) {
+        const int c = tid + i * NT;
+        if (c < XCH) {
+            const int row = c / (N2 / 8);
+            const int col = c - row * (N2 / 8);
+            *reinterpret_cast<uint4*>(xs + row * C::XROW + col * 16) = xr[i];
+        }
+    }
+    m1 = wave_max(m1);
+    if (lane == 0) red[wave] = m1;
+    __syncthreads();
+    m1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kColsWaves; ++w) m1 = fmaxf(m1, red[w]);
+    const int e1 = m1 > 0.0f ? -ilog2f(m1) : 0;
+#pragma unroll
+    for (int f = 0; f < MAXNF; ++f) {
+        if (f < nf) {
+            const float v = ldexpf(pv[f], e1);
+            const _Float16 h = static_cast<_Float16>(v);
+            p1hi[f * C::FRAG + tid] = h;
+            p1lo[f * C::FRAG + tid] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+    }
+    __syncthreads();
+
+    const int cb = wave;                             // this wave's column block
+
+    // ---- P2 fragments of this unit's 16 columns, prescaled per wave ----------
+    float p2v[C::KS1][8];
+    float m2 = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS1; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p2v[ks][e] = P2[(32 * ks + 8 * g + e) * N2 + 16 * cb + li];
+            m2 = fmaxf(m2, fabsf(p2v[ks][e]));
+        }
+    m2 = wave_max(m2);
+    const int e2 = m2 > 0.0f ? -ilog2f(m2) : 0;
+    v8h p2hi[C::KS1], p2lo[C::KS1];
+#pragma unroll
+    for (int ks = 0; ks < C::KS1; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = ldexpf(p2v[ks][e], e2);
+            const _Float16 h = static_cast<_Float16>(v);
+            p2hi[ks][e] = h;
+            p2lo[ks][e] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+
+    // ---- stage 1: T[:, cb] = X̄ · P2'[:, cb] ----------------------------------
+    v4f T[C::RB];
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS1; ++ks) {
+            const v8h a = *reinterpret_cast<const v8h*>(xs + (16 * rb + li) * C::XROW + (32 * ks + 8 * g) * 2);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p2hi[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p2lo[ks], acc, 0, 0, 0);
+        }
+        T[rb] = acc;
+    }
+    float tm = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tm = fmaxf(tm, fabsf(T[rb][r]));
+    tm = wave_max(tm);
+    const int et = tm > 0.0f ? 14 - ilog2f(tm) : 0;
+    // stage-2 B operand: accumulator rows 4g+r of blocks 2s and 2s+1
+    v8h bh[C::KS2], bl[C::KS2];
+#pragma unroll
+    for (int sk = 0; sk < C::KS2; ++sk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int rb = 2 * sk + (e >> 2);
+            const float v = rb < C::RB ? ldexpf(T[rb < C::RB ? rb : 0][e & 3], et) : 0.0f;
+            const _Float16 h = static_cast<_Float16>(v);
+            bh[sk][e] = h;
+            bl[sk][e] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+
+    // ---- stage 2 for this part's row blocks ----------------------------------
+    const int unscale = -(e1 + e2 + et);
+    float wmax = 0.0f;
+    float* zo = Zf + static_cast<size_t>(m) * K + 16 * cb + li;
+    for (int j = 0; j < nob; ++j) {
+        v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sk = 0; sk < C::KS2; ++sk) {
+            const int off = ((j * C::KS2 + sk) * 64 + lane) * 8;
+            const v8h ah = *reinterpret_cast<const v8h*>(p1hi + off);
+            const v8h al = *reinterpret_cast<const v8h*>(p1lo + off);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh[sk], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[sk], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh[sk], z, 0, 0, 0);
+        }
+        const int row0 = 16 * (ob0 + j) + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = ldexpf(z[r], unscale);
+            wmax = fmaxf(wmax, fabsf(v));
+            zo[(row0 + r) * N2] = v;
+        }
+    }
+    wmax = wave_max(wmax);
+    if (lane == 0) amax[(static_cast<size_t>(m) * C::CB + cb) * parts + part] = __float_as_uint(wmax);
+}
+
+template <int N1, int N2>
+size_t cols_ws_bytes(int M) {
+    int rbp, parts;
+    cols_parts<N1, N2>(M, &rbp, &parts);
+    return align256(sizeof(float) * static_cast<size_t>(M) * N1 * N2) +
+           align256(sizeof(uint32_t) * static_cast<size_t>(M) * ColsCfg<N1, N2>::CB * parts);
+}
+
+template <int N1, int N2>
+hipError_t launch_cols(const uint16_t* X, int M, const float* P1, const float* P2, float alpha,
+                       uint8_t* Xq, float* s_x, float* Z, void* ws, hipStream_t stream) {
+    using C = ColsCfg<N1, N2>;
+    int rbp, parts;
+    cols_parts<N1, N2>(M, &rbp, &parts);
+    char* p = static_cast<char*>(ws);
+    float* Zw = Z != nullptr ? Z : reinterpret_cast<float*>(p);
+    p += align256(sizeof(float) * static_cast<size_t>(M) * C::K);
+    uint32_t* amax = reinterpret_cast<uint32_t*>(p);
+    const size_t lds = static_cast<size_t>(rbp) * C::KS2 * C::FRAG_BYTES + C::XBYTES;
+    if (lds > 64 * 1024) {
+        // more than the default dynamic LDS limit: raise it once per device
+        static bool raised[64] = {};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= 64 || !raised[dev]) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tq_cols<N1, N2>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kColsLdsMax);
+            if (e != hipSuccess) return e;
+            if (dev >= 0 && dev < 64) raised[dev] = true;
+        }
+    }
+    const dim3 grid(M, parts);
+    k_tq_cols<N1, N2><<<grid, kColsWaves * 64, lds, stream>>>(X, M, P1, P2, rbp, parts, Zw, amax);
+    if (Z == nullptr)
+        k_tq_quant<<<dim3(M, ceil_div(C::K / 8, 256)), dim3(256), 0, stream>>>(
+            Zw, C::K, alpha, amax, C::CB * parts, Xq, s_x);
+    return hipGetLastError();
+}
+
+struct ColsFns {
+    hipError_t (*launch)(const uint16_t*, int, const float*, const float*, float, uint8_t*, float*,
+                         float*, void*, hipStream_t);
+    size_t (*ws_bytes)(int);
+};
+
+// (n1, n2) pairs with a column-block instantiation
+const ColsFns* cols_for(int n1, int n2) {
+#define W4A4_COLS(a, b)                                                   \
+    if (n1 == a && n2 == b) {                                             \
+        static const ColsFns f{&launch_cols<a, b>, &cols_ws_bytes<a, b>}; \
+        return &f;                                                        \
+    }
+    W4A4_COLS(160, 128)
+    W4A4_COLS(192, 128)
+    W4A4_COLS(224, 128)
+    W4A4_COLS(256, 128)
+#undef W4A4_COLS
+    return nullptr;
+}
+
 }  // namespace
 
 TqPath tq_select_path(int M, int n1, int n2, bool has_c) {
     (void)M;
     if (!has_c && fused_for(n1, n2) != nullptr) return TqPath::Fused;
+    if (!has_c && cols_for(n1, n2) != nullptr) return TqPath::Cols;
     return TqPath::Split;
 }
 
-static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
-
 size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c) {
     const size_t K = static_cast<size_t>(n1) * n2;
-    if (tq_select_path(M, n1, n2, has_c) == TqPath::Split)
-        return 2 * align256(sizeof(float) * K * M) + align256(sizeof(uint32_t) * M);
-    return 0;
+    switch (tq_select_path(M, n1, n2, has_c)) {
+        case TqPath::Fused:
+            return 0;
+        case TqPath::Cols:
+            return cols_for(n1, n2)->ws_bytes(M);
+        default:
+            return 2 * align256(sizeof(float) * K * M) + align256(sizeof(uint32_t) * M);
+    }
 }
 
 hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
@@ -464,9 +761,13 @@ hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
                      hipStream_t stream) {
     (void)ws_bytes;
     if (M == 0) return hipSuccess;
-    if (tq_select_path(M, n1, n2, c != nullptr) == TqPath::Fused)
+    const TqPath path = tq_select_path(M, n1, n2, c != nullptr);
+    if (path == TqPath::Fused)
         return fused_for(n1, n2)(X, M, P1, P2, alpha, quantize ? Xq : nullptr, s_x,
                                  quantize ? nullptr : Z, stream);
+    if (path == TqPath::Cols)
+        return cols_for(n1, n2)->launch(X, M, P1, P2, alpha, Xq, s_x, quantize ? nullptr : Z, ws,
+                                        stream);
     const int K = n1 * n2;
     char* p = static_cast<char*>(ws);
     float* T = reinterpret_cast<float*>(p);
@@ -481,7 +782,7 @@ hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
     k_tq_stage2<<<dim3(M, ceil_div(K, kSplitThreads)), dim3(kSplitThreads), 0, stream>>>(
         T, K, n1, n2, P1, Zout, amax);
     if (quantize) {
-        k_tq_quant<<<dim3(M, ceil_div(K / 8, 256)), dim3(256), 0, stream>>>(Zw, K, alpha, amax,
+        k_tq_quant<<<dim3(M, ceil_div(K / 8, 256)), dim3(256), 0, stream>>>(Zw, K, alpha, amax, 1,
                                                                            Xq, s_x);
     }
     return hipGetLastError();
