@@ -104,6 +104,12 @@ __global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, i
                                                   float* __restrict__ s_x) {
     const int m = blockIdx.x;
     const int idx = blockIdx.y * blockDim.x + threadIdx.x;
+    const int e0 = idx * 8;
+    // this thread's 8 values (loaded before the scale is known)
+    float z[8];
+    const float* zp = Z + static_cast<size_t>(m) * K + min(e0, K - 8);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) z[t] = zp[t];
     // the token's absmax: the largest of its partial maxima (bit patterns of
     // non-negative floats order like the floats), reduced by the workgroup
     __shared__ float red[4];
@@ -116,11 +122,9 @@ __global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, i
     ab = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float s = alpha * ab / 7.0f;
     if (idx == 0) s_x[m] = s;
-    const int e0 = idx * 8;
     if (e0 >= K) return;
     const bool zero = !(s > 0.0f);
     const float inv = zero ? 0.0f : 1.0f / s;
-    const float* z = Z + static_cast<size_t>(m) * K + e0;
     uint32_t word = 0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) word |= quant_nibble(z[t], inv, zero) << (4 * t);
@@ -471,7 +475,8 @@ constexpr int kColsLdsMax = 159 * 1024;       // dynamic LDS of one workgroup
 
 template <int N1, int N2>
 struct ColsCfg {
-    static_assert(N1 % 16 == 0 && N2 % 32 == 0, "factors: n1 multiple of 16, n2 of 32");
+    // n1 a multiple of 32: every fragment row rho is a row of P1
+    static_assert(N1 % 32 == 0 && N2 % 32 == 0, "factors: multiples of 32");
     static constexpr int K = N1 * N2;
     static constexpr int RB = N1 / 16;           // 16-row blocks of T and Z
     static constexpr int CB = N2 / 16;           // 16-column blocks (units per token)
@@ -529,7 +534,14 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
     uint8_t* xs = reinterpret_cast<uint8_t*>(cl + 2 * nf * C::FRAG);
     const int m = blockIdx.x;                        // this workgroup's token
 
-    // ---- the token's X̄ -> LDS (loads issued together with P1's) -------------
+    // ---- this wave's P2 columns and the token's X̄ (to LDS): their loads are
+    //      issued together with P1's, before the first wait -------------------
+    const int cb = wave;                             // this wave's column block
+    float p2v[C::KS1][8];
+#pragma unroll
+    for (int ks = 0; ks < C::KS1; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p2v[ks][e] = P2[(32 * ks + 8 * g + e) * N2 + 16 * cb + li];
     constexpr int XCH = C::K / 8;                    // 16-byte chunks of one token
     constexpr int XLD = (XCH + NT - 1) / NT;
     uint4 xr[XLD];
@@ -540,25 +552,23 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
     // ---- P1 fragments of row blocks ob0 .. ob0+nob-1 into LDS ----------------
     // fragment (ob, sk), lane (gg, ii), element e holds P1[rho][16*ob + ii],
     // rho = 32 sk + 4 gg + e (e < 4) or 32 sk + 16 + 4 gg + (e - 4): the rows
-    // of T that the stage-1 accumulators of lane group gg hold.  Thread tid
-    // owns element tid of every fragment; all its loads are issued before
-    // the power-of-two prescale (the part's max |P1|) is known.
-    constexpr int MAXNF = (C::MAX_RBP < C::RB ? C::MAX_RBP : C::RB) * C::KS2;
-    static_assert(C::FRAG == NT, "one fragment element per thread");
-    float pv[MAXNF];
+    // of T that the stage-1 accumulators of lane group gg hold.  The part's
+    // columns are read as 16-byte row pieces (rows rho, 4 columns each, all
+    // loads issued before the first wait), its max |P1| gives the power-of-
+    // two prescale, and each piece is scattered to 4 fragment lanes.
+    constexpr int MAXI = (N1 * 4 * C::MAX_RBP + NT - 1) / NT;
+    const int pieces = N1 * 4 * nob;                 // 16-byte pieces of the part
+    float4 pv[MAXI];
     float m1 = 0.0f;
-    {
-        const int e = tid & 7;
-        const int gg = (tid >> 3) >> 4, ii = (tid >> 3) & 15;
 #pragma unroll
-        for (int f = 0; f < MAXNF; ++f) {
-            const int fc = min(f, nf - 1);
-            const int sk = fc % C::KS2;
-            const int ob = ob0 + fc / C::KS2;
-            const int rho = 32 * sk + (e < 4 ? 4 * gg + e : 16 + 4 * gg + (e - 4));
-            pv[f] = P1[min(rho, N1 - 1) * N1 + 16 * ob + ii];
-            if (rho >= N1) pv[f] = 0.0f;
-            m1 = fmaxf(m1, fabsf(pv[f]));
+    for (int i = 0; i < MAXI; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < pieces) {
+            const int rho = idx / (4 * nob);
+            const int c4 = idx - rho * (4 * nob);
+            pv[i] = *reinterpret_cast<const float4*>(P1 + static_cast<size_t>(rho) * N1 + 16 * ob0 + 4 * c4);
+            m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(pv[i].x), fabsf(pv[i].y)),
+                                 fmaxf(fabsf(pv[i].z), fabsf(pv[i].w))));
         }
     }
 #pragma unroll
@@ -578,28 +588,36 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
     for (int w = 0; w < kColsWaves; ++w) m1 = fmaxf(m1, red[w]);
     const int e1 = m1 > 0.0f ? -ilog2f(m1) : 0;
 #pragma unroll
-    for (int f = 0; f < MAXNF; ++f) {
-        if (f < nf) {
-            const float v = ldexpf(pv[f], e1);
-            const _Float16 h = static_cast<_Float16>(v);
-            p1hi[f * C::FRAG + tid] = h;
-            p1lo[f * C::FRAG + tid] = static_cast<_Float16>(v - static_cast<float>(h));
+    for (int i = 0; i < MAXI; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < pieces) {
+            const int rho = idx / (4 * nob);
+            const int c4 = idx - rho * (4 * nob);
+            const int sk = rho >> 5;
+            const int rr = rho & 31;
+            const int gg = (rr & 15) >> 2;
+            const int e = (rr & 3) + ((rr >> 4) << 2);
+            const float vv[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = 4 * c4 + q;             // column inside the part
+                const int f = (col >> 4) * C::KS2 + sk;
+                const int off = (f * 64 + gg * 16 + (col & 15)) * 8 + e;
+                const float v = ldexpf(vv[q], e1);
+                const _Float16 h = static_cast<_Float16>(v);
+                p1hi[off] = h;
+                p1lo[off] = static_cast<_Float16>(v - static_cast<float>(h));
+            }
         }
     }
     __syncthreads();
 
-    const int cb = wave;                             // this wave's column block
-
-    // ---- P2 fragments of this unit's 16 columns, prescaled per wave ----------
-    float p2v[C::KS1][8];
+    // ---- P2 fragments of this wave's 16 columns, prescaled per wave ----------
     float m2 = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < C::KS1; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p2v[ks][e] = P2[(32 * ks + 8 * g + e) * N2 + 16 * cb + li];
-            m2 = fmaxf(m2, fabsf(p2v[ks][e]));
-        }
+        for (int e = 0; e < 8; ++e) m2 = fmaxf(m2, fabsf(p2v[ks][e]));
     m2 = wave_max(m2);
     const int e2 = m2 > 0.0f ? -ilog2f(m2) : 0;
     v8h p2hi[C::KS1], p2lo[C::KS1];
