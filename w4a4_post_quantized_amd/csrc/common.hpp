@@ -133,6 +133,15 @@ __device__ __forceinline__ uint32_t quant_nibble(float z, float inv_s, bool zero
     return static_cast<uint32_t>(q) & 0xFu;
 }
 
+// The same code as quant_nibble for finite z: the product is clamped to
+// [-8, 7] (v_med3) and rounded half to even by adding 1.5 * 2^23, whose
+// float lands the integer in the low mantissa bits (two's complement in the
+// low nibble).  A zero scale passes inv_s = 0 and gives code 0.
+__device__ __forceinline__ uint32_t quant_nibble_magic(float z, float inv_s) {
+    const float t = __builtin_amdgcn_fmed3f(z * inv_s, -8.0f, 7.0f);
+    return __float_as_uint(t + 12582912.0f) & 0xFu;
+}
+
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Compute units of the current device (cached per device ordinal).

@@ -434,18 +434,315 @@ hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* 
     return hipGetLastError();
 }
 
+// ===========================================================================
+// Wave-per-token MFMA path (n1, n2 <= 64): one wave transforms, quantizes
+// and packs a whole token with no workgroup barrier.  The workgroup stages
+// the split P2 (stage-1 B operand) and P1 (stage-2 B operand) fragments in
+// LDS once; each wave then walks its own tokens:
+//   stage 1  T = X̄ · P2 as in the fused path, X̄ fragments loaded straight
+//            from HBM one token ahead;
+//   stage 2  computed transposed, Zᵀ = Tᵀ · P1: the split T accumulators are
+//            the A operand in their own k order and the P1 fragments of the
+//            fused path become the B operand, so each lane ends up holding
+//            four consecutive channels of a row of Z;
+//   quant    wave absmax (DPP), 4 codes -> 16 bits per lane and tile,
+//            assembled in the wave's LDS slice and written as 16-byte rows.
+// ===========================================================================
+template <int N1, int N2>
+struct WaveCfg {
+    static_assert(N1 % 16 == 0 && N2 % 16 == 0 && N1 <= 64 && N2 <= 64, "small factors");
+    static constexpr int K = N1 * N2;
+    static constexpr int RB = N1 / 16;           // 16-row blocks of Z (rows i)
+    static constexpr int CB = N2 / 16;           // 16-column blocks of Z (columns j)
+    static constexpr int KS1 = (N2 + 31) / 32;   // stage-1 k-steps
+    static constexpr int KS2 = (N1 + 31) / 32;   // stage-2 k-steps
+    static constexpr int NW = 8;                 // waves per workgroup
+    static constexpr int NT = NW * 64;
+    static constexpr int FRAG = 64 * 8;          // fp16 per fragment
+    static constexpr int P2F = KS1 * CB * FRAG;  // fp16 per P2 fragment set
+    static constexpr int P1F = KS2 * RB * FRAG;  // fp16 per P1 fragment set
+    static constexpr int QB = K / 2;             // packed bytes per token
+    static_assert(QB % 16 == 0, "whole 16-byte chunks per token");
+};
+
+template <int N1, int N2>
+__global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_t* __restrict__ X, int M,
+                                                                const float* __restrict__ P1,
+                                                                const float* __restrict__ P2, float alpha,
+                                                                uint8_t* __restrict__ Xq,
+                                                                float* __restrict__ s_x,
+                                                                float* __restrict__ Zout) {
+    using C = WaveCfg<N1, N2>;
+    constexpr int K = C::K;
+    constexpr int NT = C::NT;
+    __shared__ __align__(16) _Float16 p2hi[C::P2F];
+    __shared__ __align__(16) _Float16 p2lo[C::P2F];
+    __shared__ __align__(16) _Float16 p1hi[C::P1F];
+    __shared__ __align__(16) _Float16 p1lo[C::P1F];
+    __shared__ __align__(16) uint8_t qbuf[C::NW][C::QB];
+    __shared__ float red[2 * C::NW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+    const int li = lane & 15;
+
+    // ---- this wave's tokens ------------------------------------------------------
+    auto load_x = [&](int m, v8h (&xa)[C::RB][C::KS1]) {
+        const uint16_t* xt = X + static_cast<size_t>(min(m, M - 1)) * K;
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < C::KS1; ++ks) {
+                if (32 * ks + 8 * g < N2)
+                    xa[rb][ks] = *reinterpret_cast<const v8h*>(xt + (16 * rb + li) * N2 + 32 * ks + 8 * g);
+                else
+                    xa[rb][ks] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+    };
+    const int stride = gridDim.x * C::NW;
+    int m = blockIdx.x * C::NW + wave;
+    v8h xa[C::RB][C::KS1], xn[C::RB][C::KS1];
+    load_x(m, xa);                  // first token in flight during the setup
+
+    // ---- fragments into LDS ----------------------------------------------------
+    // P2 fragment (ks, cb), lane (gg, ii), element e: P2[32 ks + 8 gg + e][16 cb + ii].
+    // P1 fragment (sk, ob), lane (gg, ii), element e: P1[rho][16 ob + ii] with
+    // rho = 32 sk + 4 gg + e (e < 4) or 32 sk + 16 + 4 gg + (e - 4): the rows
+    // of T held by accumulator lane group gg.  Every factor element appears
+    // once (padding elements are zero), so the fragment values also give the
+    // power-of-two prescales; all loads are issued before the first wait.
+    constexpr int L2N = (C::P2F + NT - 1) / NT;
+    constexpr int L1N = (C::P1F + NT - 1) / NT;
+    float v2[L2N], v1[L1N];
+    float m1 = 0.0f, m2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < L2N; ++i) {
+        const int idx = tid + i * NT;
+        const int e = idx & 7;
+        const int ln = (idx >> 3) & 63;
+        const int slot = idx >> 9;
+        const int cb = slot % C::CB;
+        const int ks = slot / C::CB;
+        const int kk = 32 * ks + 8 * (ln >> 4) + e;
+        const bool in = idx < C::P2F && kk < N2;
+        v2[i] = P2[in ? kk * N2 + 16 * cb + (ln & 15) : 0];
+        if (!in) v2[i] = 0.0f;
+        m2 = fmaxf(m2, fabsf(v2[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < L1N; ++i) {
+        const int idx = tid + i * NT;
+        const int e = idx & 7;
+        const int ln = (idx >> 3) & 63;
+        const int slot = idx >> 9;
+        const int ob = slot % C::RB;
+        const int sk = slot / C::RB;
+        const int gg = ln >> 4;
+        const int rho = 32 * sk + (e < 4 ? 4 * gg + e : 16 + 4 * gg + (e - 4));
+        const bool in = idx < C::P1F && rho < N1;
+        v1[i] = P1[in ? rho * N1 + 16 * ob + (ln & 15) : 0];
+        if (!in) v1[i] = 0.0f;
+        m1 = fmaxf(m1, fabsf(v1[i]));
+    }
+    m1 = wave_max(m1);
+    m2 = wave_max(m2);
+    if (lane == 0) {
+        red[wave] = m1;
+        red[C::NW + wave] = m2;
+    }
+    __syncthreads();
+    m1 = 0.0f;
+    m2 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < C::NW; ++w) {
+        m1 = fmaxf(m1, red[w]);
+        m2 = fmaxf(m2, red[C::NW + w]);
+    }
+    const int e1 = m1 > 0.0f ? -ilog2f(m1) : 0;
+    const int e2 = m2 > 0.0f ? -ilog2f(m2) : 0;
+#pragma unroll
+    for (int i = 0; i < L2N; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < C::P2F) {
+            const float v = ldexpf(v2[i], e2);
+            const _Float16 h = static_cast<_Float16>(v);
+            p2hi[idx] = h;
+            p2lo[idx] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < L1N; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < C::P1F) {
+            const float v = ldexpf(v1[i], e1);
+            const _Float16 h = static_cast<_Float16>(v);
+            p1hi[idx] = h;
+            p1lo[idx] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+    }
+    __syncthreads();
+
+    uint8_t* qb = qbuf[wave];
+    for (; m < M; m += stride) {
+        // an offset the compiler cannot see through: the fragment reads stay
+        // LDS reads in the loop instead of 128 loop-invariant registers, which
+        // lets two waves share a SIMD
+        int fo = 0;
+        asm volatile("" : "+s"(fo));
+        // next token in flight (clamped, unconditional: a branch here would
+        // make the compiler wait for these loads before stage 1)
+        load_x(m + stride, xn);
+
+        // stage 1: T = X̄ · P2'
+        v4f T[C::RB][C::CB];
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+#pragma unroll
+            for (int rb = 0; rb < C::RB; ++rb) T[rb][cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < C::KS1; ++ks) {
+                const int off = ((ks * C::CB + cb) * 64 + lane) * 8 + fo;
+                const v8h bh = *reinterpret_cast<const v8h*>(p2hi + off);
+                const v8h bl = *reinterpret_cast<const v8h*>(p2lo + off);
+#pragma unroll
+                for (int rb = 0; rb < C::RB; ++rb) {
+                    T[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rb][ks], bh, T[rb][cb], 0, 0, 0);
+                    T[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rb][ks], bl, T[rb][cb], 0, 0, 0);
+                }
+            }
+        }
+        // power-of-two prescale of T into the fp16 range, then Tᵀ fragments:
+        // A operand of k-step sk for column block cb = accumulator rows 4g+r
+        // of row blocks 2 sk and 2 sk + 1
+        float tm = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tm = fmaxf(tm, fabsf(T[rb][cb][r]));
+        tm = wave_max(tm);
+        const int et = tm > 0.0f ? 14 - ilog2f(tm) : 0;
+        v8h ah[C::KS2][C::CB], al[C::KS2][C::CB];
+#pragma unroll
+        for (int sk = 0; sk < C::KS2; ++sk)
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int rb = 2 * sk + (e >> 2);
+                    const float v = rb < C::RB ? ldexpf(T[rb < C::RB ? rb : 0][cb][e & 3], et) : 0.0f;
+                    const _Float16 h = static_cast<_Float16>(v);
+                    ah[sk][cb][e] = h;
+                    al[sk][cb][e] = static_cast<_Float16>(v - static_cast<float>(h));
+                }
+        // stage 2: Zᵀ = T'ᵀ · P1'  (tile (cb, ob): rows j, columns i)
+        v4f Z[C::RB][C::CB];
+#pragma unroll
+        for (int ob = 0; ob < C::RB; ++ob) {
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) Z[ob][cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int sk = 0; sk < C::KS2; ++sk) {
+                const int off = ((sk * C::RB + ob) * 64 + lane) * 8 + fo;
+                const v8h bh = *reinterpret_cast<const v8h*>(p1hi + off);
+                const v8h bl = *reinterpret_cast<const v8h*>(p1lo + off);
+#pragma unroll
+                for (int cb = 0; cb < C::CB; ++cb) {
+                    Z[ob][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[sk][cb], bh, Z[ob][cb], 0, 0, 0);
+                    Z[ob][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[sk][cb], bl, Z[ob][cb], 0, 0, 0);
+                    Z[ob][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[sk][cb], bh, Z[ob][cb], 0, 0, 0);
+                }
+            }
+        }
+        // lane (g, li) of tile (ob, cb) holds 2^-unscale * Z[16 ob + li][16 cb + 4 g + r];
+        // the power of two is folded into the scale and the quantizer's
+        // multiplier (exact, so the codes are those of the unscaled values)
+        const int unscale = -(e1 + e2 + et);
+        float zmax = 0.0f;
+#pragma unroll
+        for (int ob = 0; ob < C::RB; ++ob)
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, fabsf(Z[ob][cb][r]));
+        if (Zout != nullptr) {
+#pragma unroll
+            for (int ob = 0; ob < C::RB; ++ob)
+#pragma unroll
+                for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Z[ob][cb][r] = ldexpf(Z[ob][cb][r], unscale);
+            float* zo = Zout + static_cast<size_t>(m) * K;
+#pragma unroll
+            for (int ob = 0; ob < C::RB; ++ob)
+#pragma unroll
+                for (int cb = 0; cb < C::CB; ++cb)
+                    *reinterpret_cast<v4f*>(zo + (16 * ob + li) * N2 + 16 * cb + 4 * g) = Z[ob][cb];
+        } else {
+            const float s = alpha * ldexpf(wave_max(zmax), unscale) / 7.0f;
+            const float inv = s > 0.0f ? ldexpf(1.0f / s, unscale) : 0.0f;
+#pragma unroll
+            for (int ob = 0; ob < C::RB; ++ob)
+#pragma unroll
+                for (int cb = 0; cb < C::CB; ++cb) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w |= quant_nibble_magic(Z[ob][cb][r], inv) << (4 * r);
+                    *reinterpret_cast<uint16_t*>(qb + ((16 * ob + li) * N2 + 16 * cb + 4 * g) / 2) =
+                        static_cast<uint16_t>(w);
+                }
+            // the wave's LDS slice is read back by the same wave: LDS operations
+            // of one wave complete in order
+            uint4* dst = reinterpret_cast<uint4*>(Xq + static_cast<size_t>(m) * (K / 2));
+#pragma unroll
+            for (int c = lane; c < C::QB / 16; c += 64) dst[c] = reinterpret_cast<const uint4*>(qb)[c];
+            if (lane == 0) s_x[m] = s;
+        }
+#pragma unroll
+        for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < C::KS1; ++ks) xa[rb][ks] = xn[rb][ks];
+    }
+}
+
+template <int N1, int N2>
+hipError_t launch_wave(const uint16_t* X, int M, const float* P1, const float* P2, float alpha,
+                       uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+    using C = WaveCfg<N1, N2>;
+    // persistent grid: as many workgroups as fit on the device at once, so
+    // the fragment setup is paid once per resident workgroup
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_wave<N1, N2>, C::NT, 0) !=
+                hipSuccess || n < 1)
+            n = 1;
+        per_cu = n;
+    }
+    const int units = (M + C::NW - 1) / C::NW;
+    const int cap = per_cu * device_cu_count();
+    const int grid = units < cap ? units : cap;
+    k_tq_wave<N1, N2><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, alpha, Xq, s_x, Z);
+    return hipGetLastError();
+}
+
 using FusedFn = hipError_t (*)(const uint16_t*, int, const float*, const float*, float, uint8_t*,
                                float*, float*, hipStream_t);
 
-// (n1, n2) pairs with a fused instantiation
+// (n1, n2) pairs with a fused (or wave-per-token) instantiation
 FusedFn fused_for(int n1, int n2) {
 #define W4A4_FUSED(a, b) \
     if (n1 == a && n2 == b) return &launch_fused<a, b>;
-    W4A4_FUSED(16, 16)
-    W4A4_FUSED(32, 32)
-    W4A4_FUSED(16, 64)
-    W4A4_FUSED(32, 64)
-    W4A4_FUSED(64, 64)
+#define W4A4_WAVE(a, b) \
+    if (n1 == a && n2 == b) return &launch_wave<a, b>;
+    W4A4_WAVE(16, 16)
+    W4A4_WAVE(32, 32)
+    W4A4_WAVE(16, 64)
+    W4A4_WAVE(32, 64)
+    W4A4_WAVE(64, 64)
     W4A4_FUSED(32, 128)
     W4A4_FUSED(64, 128)
     W4A4_FUSED(96, 128)
@@ -453,6 +750,7 @@ FusedFn fused_for(int n1, int n2) {
     W4A4_FUSED(128, 128)
     W4A4_FUSED(128, 64)
 #undef W4A4_FUSED
+#undef W4A4_WAVE
     return nullptr;
 }
 
