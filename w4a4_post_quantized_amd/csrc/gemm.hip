@@ -91,7 +91,7 @@ __device__ __forceinline__ void unpack_asym(const uint4& w, uint32_t bias, uint4
     od.w = usub((w.w >> 4) & 0x0F0F0F0Fu, bias);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool ASYM, int MODE>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool ASYM, int MODE, bool G1 = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
@@ -199,6 +199,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
                 for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
     }
 
+    // a zero accumulator operand the compiler cannot fold into an inline
+    // constant (an MFMA with an inline-zero accumulator gave wrong sums)
+    v4i zc;
+    {
+        int z0;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+        zc = v4i{z0, z0, z0, z0};
+    }
     const int frow = lane & 15;      // fragment row supplied by this lane
     const int fks = lane >> 4;       // k-slice supplied by this lane
     const int orow = 4 * (lane >> 4);  // first output row held by this lane
@@ -231,14 +239,30 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
                 bf[s][b] = *reinterpret_cast<const v4i*>(Bs + row * ROWB + swz(row, ch) * 16);
             }
         }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
+        if constexpr (G1) {
+            // one K tile per weight group: the group's sums start from a zero
+            // register operand, so the accumulators need no clearing
 #pragma unroll
             for (int a = 0; a < FM; ++a)
 #pragma unroll
                 for (int b = 0; b < FN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[s][a], bf[s][b], acc[a][b],
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[0][a], bf[0][b], zc, 0, 0, 0);
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[1][a], bf[1][b], acc[a][b],
                                                                      0, 0, 0);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[s][a], bf[s][b],
+                                                                         acc[a][b], 0, 0, 0);
+        }
 
         // ---- end of a weight group: fold (or emit) the exact int32 sums ----
         const bool group_end = ((kt + 1) % TPG) == 0;
@@ -268,7 +292,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             facc[a][b][r] = fmaf(static_cast<float>(acc[a][b][r]), sw, facc[a][b][r]);
-                            acc[a][b][r] = 0;
+                            if constexpr (!G1) acc[a][b][r] = 0;
                         }
                 }
             }
@@ -1109,6 +1133,17 @@ template <int BM, int BN, int WM_, int WN_, int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t stream) {
     dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM));
     dim3 block(WM_ * WN_ * 64);
+    if constexpr (MODE == kModeGroup) {
+        if (a.group_size == BK) {
+            if (a.asym)
+                k_gemm_w4a4<BM, BN, WM_, WN_, true, MODE, true><<<grid, block, 0, stream>>>(
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.D, a.M, a.N, a.K, a.group_size);
+            else
+                k_gemm_w4a4<BM, BN, WM_, WN_, false, MODE, true><<<grid, block, 0, stream>>>(
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.D, a.M, a.N, a.K, a.group_size);
+            return hipGetLastError();
+        }
+    }
     if (a.asym)
         k_gemm_w4a4<BM, BN, WM_, WN_, true, MODE><<<grid, block, 0, stream>>>(
             a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.D, a.M, a.N, a.K, a.group_size);
