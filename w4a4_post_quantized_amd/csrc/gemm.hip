@@ -44,6 +44,7 @@ namespace w4a4 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 128;          // codes per K tile
 constexpr int ROWB = BK;         // int8 bytes per LDS row
@@ -330,244 +331,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
 
 
 // ===========================================================================
-// 32x32x32 kernel: same data flow as k_gemm_w4a4 (packed tiles -> registers
-// -> unpacked int8 in double-buffered LDS, one barrier per 128-code K tile),
-// on v_mfma_i32_32x32x32_i8, which sustains ~96% of the int8 peak on gfx950
-// where the 16x16x64 form measures ~78%.  Lane l supplies 16 bytes of row
-// (l & 31) from k-slice (l >> 5); a K tile is 4 MFMA k-steps, k-step s using
-// the even- and odd-code chunks of packed chunk s.  Accumulator register r of
-// lane l holds row 8*(r >> 2) + 4*(l >> 5) + (r & 3), column l & 31.
-// ===========================================================================
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, bool ASYM, int MODE>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm32(
-    const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
-    const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
-    const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int M, int N, int K,
-    int group_size) {
-    constexpr int NT = WAVES_M * WAVES_N * 64;
-    constexpr int WM = BM / WAVES_M;
-    constexpr int WN = BN / WAVES_N;
-    constexpr int FM = WM / 32;
-    constexpr int FN = WN / 32;
-    static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
-    static_assert(PD >= 1 && PD <= 4, "prefetch depth");
-    constexpr int ALD = (BM * 4 + NT - 1) / NT;
-    constexpr int BLD = (BN * 4 + NT - 1) / NT;
-    constexpr int TILE_BYTES = (BM + BN) * ROWB;
-    static_assert(MODE != kModeI32, "fp16 output modes only");
-
-    __shared__ __align__(16) uint8_t smem[2 * TILE_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm0 = (wave / WAVES_N) * WM;
-    const int wn0 = (wave % WAVES_N) * WN;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
-    const int KB = K / 2;
-    const int KT = K / BK;
-    const int G = K / group_size;
-    const int TPG = group_size / BK;
-
-    // PD register staging sets: the packed tile kt+PD is loaded while tile kt
-    // is multiplied, so each load has about PD-1 iterations to arrive.  Loads
-    // are branch-free (rows and tiles are clamped to valid ones; a clamped row
-    // only feeds outputs that are never stored), which lets the compiler wait
-    // for exactly the tile it unpacks instead of draining all loads.
-    static_assert((BM * 4) % NT == 0 && (BN * 4) % NT == 0, "whole 16-byte chunks per thread");
-    uint4 ra[PD][ALD], rb[PD][BLD];
-    uint32_t zb[PD][ASYM ? BLD : 1];
-    const uint8_t* arow[ALD];
-    const uint8_t* brow[BLD];
-    int bgn[BLD];
-#pragma unroll
-    for (int i = 0; i < ALD; ++i) {
-        const int q = tid + i * NT;
-        const int gm = min(m0 + (q >> 2), M - 1);
-        arow[i] = Xq + static_cast<size_t>(gm) * KB + (q & 3) * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < BLD; ++i) {
-        const int q = tid + i * NT;
-        bgn[i] = min(n0 + (q >> 2), N - 1);
-        brow[i] = Wq + static_cast<size_t>(bgn[i]) * KB + (q & 3) * 16;
-    }
-
-    auto load_tile = [&](int kt, auto SET) {
-        constexpr int S = decltype(SET)::value;
-        const int kc = min(kt, KT - 1);
-#pragma unroll
-        for (int i = 0; i < ALD; ++i) ra[S][i] = *reinterpret_cast<const uint4*>(arow[i] + kc * 64);
-#pragma unroll
-        for (int i = 0; i < BLD; ++i) {
-            rb[S][i] = *reinterpret_cast<const uint4*>(brow[i] + kc * 64);
-            if constexpr (ASYM) {
-                const int g = (kc * BK) / group_size;
-                const uint32_t z = static_cast<uint32_t>(h2f(z_w[static_cast<size_t>(bgn[i]) * G + g]));
-                zb[S][i] = (0x80u - z) * 0x01010101u;
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf, auto SET) {
-        constexpr int S = decltype(SET)::value;
-        uint8_t* As = smem + buf * TILE_BYTES;
-        uint8_t* Bs = As + BM * ROWB;
-#pragma unroll
-        for (int i = 0; i < ALD; ++i) {
-            const int q = tid + i * NT;
-            const int row = q >> 2, pc = q & 3;
-            uint4 ev, od;
-            unpack_signed16(ra[S][i], ev, od);
-            *reinterpret_cast<uint4*>(As + row * ROWB + swz(row, 2 * pc) * 16) = ev;
-            *reinterpret_cast<uint4*>(As + row * ROWB + swz(row, 2 * pc + 1) * 16) = od;
-        }
-#pragma unroll
-        for (int i = 0; i < BLD; ++i) {
-            const int q = tid + i * NT;
-            const int row = q >> 2, pc = q & 3;
-            uint4 ev, od;
-            if constexpr (ASYM)
-                unpack_asym(rb[S][i], zb[S][i], ev, od);
-            else
-                unpack_signed16(rb[S][i], ev, od);
-            *reinterpret_cast<uint4*>(Bs + row * ROWB + swz(row, 2 * pc) * 16) = ev;
-            *reinterpret_cast<uint4*>(Bs + row * ROWB + swz(row, 2 * pc + 1) * 16) = od;
-        }
-    };
-
-    v16i acc[FM][FN];
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
-    float facc[(MODE == kModeGroup) ? FM : 1][(MODE == kModeGroup) ? FN : 1][16];
-    if constexpr (MODE == kModeGroup) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) facc[a][b][r] = 0.0f;
-    }
-
-    const int frow = lane & 31;
-    const int fks = lane >> 5;
-    const int ocol = lane & 31;
-    const int orow = 4 * (lane >> 5);
-
-    // one K tile: tile kt is in LDS buffer kt & 1 and came from set kt % PD
-    auto body = [&](int kt, auto SET) {
-        constexpr int S = decltype(SET)::value;
-        constexpr int SN = (S + 1) % PD;       // set holding tile kt + 1
-        const int buf = kt & 1;
-        load_tile(kt + PD, std::integral_constant<int, S>{});
-        const uint8_t* As = smem + buf * TILE_BYTES;
-        const uint8_t* Bs = As + BM * ROWB;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int ch = 2 * st + fks;
-            v4i af[FM], bf[FN];
-#pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                const int row = wm0 + a * 32 + frow;
-                af[a] = *reinterpret_cast<const v4i*>(As + row * ROWB + swz(row, ch) * 16);
-            }
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int row = wn0 + b * 32 + frow;
-                bf[b] = *reinterpret_cast<const v4i*>(Bs + row * ROWB + swz(row, ch) * 16);
-            }
-#pragma unroll
-            for (int a = 0; a < FM; ++a)
-#pragma unroll
-                for (int b = 0; b < FN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
-        }
-        if constexpr (MODE == kModeGroup) {
-            if (((kt + 1) % TPG) == 0) {
-                const int g = kt / TPG;
-#pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const int gn = n0 + wn0 + b * 32 + ocol;
-                    const float sw = (gn < N) ? h2f(s_w[static_cast<size_t>(gn) * G + g]) : 0.0f;
-#pragma unroll
-                    for (int a = 0; a < FM; ++a)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            facc[a][b][r] = fmaf(static_cast<float>(acc[a][b][r]), sw, facc[a][b][r]);
-                            acc[a][b][r] = 0;
-                        }
-                }
-            }
-        }
-        // the last iteration stores a clamped duplicate that nobody reads
-        store_tile(buf ^ 1, std::integral_constant<int, SN>{});
-        __syncthreads();
-    };
-
-    // prologue: tiles 0 .. PD-1 in flight, tile 0 unpacked into buffer 0
-    load_tile(0, std::integral_constant<int, 0>{});
-    if constexpr (PD > 1) load_tile(1, std::integral_constant<int, 1 % PD>{});
-    if constexpr (PD > 2) load_tile(2, std::integral_constant<int, 2 % PD>{});
-    if constexpr (PD > 3) load_tile(3, std::integral_constant<int, 3 % PD>{});
-    store_tile(0, std::integral_constant<int, 0>{});
-    __syncthreads();
-
-    int kt = 0;
-    for (; kt + PD <= KT; kt += PD) {
-        body(kt, std::integral_constant<int, 0>{});
-        if constexpr (PD > 1) body(kt + 1, std::integral_constant<int, 1 % PD>{});
-        if constexpr (PD > 2) body(kt + 2, std::integral_constant<int, 2 % PD>{});
-        if constexpr (PD > 3) body(kt + 3, std::integral_constant<int, 3 % PD>{});
-    }
-    if (kt < KT) body(kt, std::integral_constant<int, 0>{});
-    if constexpr (PD > 2) if (kt + 1 < KT) body(kt + 1, std::integral_constant<int, 1 % PD>{});
-    if constexpr (PD > 3) if (kt + 2 < KT) body(kt + 2, std::integral_constant<int, 2 % PD>{});
-
-    constexpr float kUnshift = ASYM ? (1.0f / 16.0f) : (1.0f / 256.0f);
-#pragma unroll
-    for (int b = 0; b < FN; ++b) {
-        const int gn = n0 + wn0 + b * 32 + ocol;
-        if (gn >= N) continue;
-        float sw1 = 1.0f;
-        if constexpr (MODE == kModeChan) sw1 = h2f(s_w[gn]);
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int gm = m0 + wm0 + a * 32 + 8 * (r >> 2) + orow + (r & 3);
-                if (gm >= M) continue;
-                float v;
-                if constexpr (MODE == kModeChan)
-                    v = static_cast<float>(acc[a][b][r]) * sw1;
-                else
-                    v = facc[a][b][r];
-                Y[static_cast<size_t>(gm) * N + gn] = f2h(v * s_x[gm] * kUnshift);
-            }
-    }
-}
-
-template <int BM, int BN, int WM_, int WN_, int PD, int MODE>
-hipError_t launch32(const GemmArgs& a, hipStream_t stream) {
-    dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM));
-    dim3 block(WM_ * WN_ * 64);
-    if (a.asym)
-        k_gemm32<BM, BN, WM_, WN_, PD, true, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
-    else
-        k_gemm32<BM, BN, WM_, WN_, PD, false, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
-    return hipGetLastError();
-}
-
-
-// ===========================================================================
 // Direct-to-LDS kernel.  Packed tiles go from HBM straight into a ring of
 // STAGES LDS buffers with global_load_lds_dwordx4 (no VGPR staging, no VALU,
 // no ds_write), STAGES-1 tiles in flight.  A packed row of a K tile is 64
@@ -622,7 +385,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     constexpr int CHUNKS = (BM + BN) * 4;             // 16-byte chunks per tile
     static_assert(CHUNKS % (64 * NW) == 0 && (BM * 4) % 64 == 0, "whole wave loads");
     constexpr int LPW = CHUNKS / (64 * NW);           // load instructions per wave per tile
-    static_assert(STAGES >= 3 && STAGES <= 4 && (STAGES - 2) * LPW < 64, "stages / vmcnt range");
+    static_assert(STAGES >= 3 && STAGES <= 8 && (STAGES - 2) * LPW < 64, "stages / vmcnt range");
     static_assert(MODE != kModeI32, "fp16 output modes only");
 
     // one LDS array per stage: distinct objects let the compiler see that
@@ -631,12 +394,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     __shared__ __align__(16) uint8_t st1[STAGE_BYTES];
     __shared__ __align__(16) uint8_t st2[STAGES > 2 ? STAGE_BYTES : 16];
     __shared__ __align__(16) uint8_t st3[STAGES > 3 ? STAGE_BYTES : 16];
+    __shared__ __align__(16) uint8_t st4[STAGES > 4 ? STAGE_BYTES : 16];
+    __shared__ __align__(16) uint8_t st5[STAGES > 5 ? STAGE_BYTES : 16];
+    __shared__ __align__(16) uint8_t st6[STAGES > 6 ? STAGE_BYTES : 16];
+    __shared__ __align__(16) uint8_t st7[STAGES > 7 ? STAGE_BYTES : 16];
     auto stage_ptr = [&](auto S) -> uint8_t* {
         constexpr int I = decltype(S)::value;
         if constexpr (I == 0) return st0;
         else if constexpr (I == 1) return st1;
         else if constexpr (I == 2) return st2;
-        else return st3;
+        else if constexpr (I == 3) return st3;
+        else if constexpr (I == 4) return st4;
+        else if constexpr (I == 5) return st5;
+        else if constexpr (I == 6) return st6;
+        else return st7;
     };
 
     const int tid = threadIdx.x;
@@ -788,22 +559,16 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     };
 
     // prologue: tiles 0 .. STAGES-2 in flight; wait for tile 0
-    issue(0, std::integral_constant<int, 0>{});
-    issue(1, std::integral_constant<int, 1 % STAGES>{});
-    if constexpr (STAGES > 3) issue(2, std::integral_constant<int, 2>{});
+    static_for<0, STAGES - 1>([&](auto I) { issue(decltype(I)::value, I); });
     wait_vmcnt<(STAGES - 2) * LPW>();
     lds_barrier();
 
     int kt = 0;
-    for (; kt + STAGES <= KT; kt += STAGES) {
-        body(kt, std::integral_constant<int, 0>{});
-        body(kt + 1, std::integral_constant<int, 1>{});
-        if constexpr (STAGES > 2) body(kt + 2, std::integral_constant<int, 2 % STAGES>{});
-        if constexpr (STAGES > 3) body(kt + 3, std::integral_constant<int, 3 % STAGES>{});
-    }
-    if (kt < KT) body(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < KT) body(kt + 1, std::integral_constant<int, 1 % STAGES>{});
-    if constexpr (STAGES > 3) if (kt + 2 < KT) body(kt + 2, std::integral_constant<int, 2 % STAGES>{});
+    for (; kt + STAGES <= KT; kt += STAGES)
+        static_for<0, STAGES>([&](auto I) { body(kt + decltype(I)::value, I); });
+    static_for<0, STAGES - 1>([&](auto I) {
+        if (kt + decltype(I)::value < KT) body(kt + decltype(I)::value, I);
+    });
 
     constexpr float kUnshift = ASYM ? (1.0f / 16.0f) : (1.0f / 256.0f);
 #pragma unroll
@@ -1168,34 +933,24 @@ struct KernelCfg {
 
 template <int MODE> hipError_t dl256x256_2x4_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 2, 4, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl256x256_2x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 2, 4, 3, MODE>(a, s); }
-template <int MODE> hipError_t dl256x256_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 2, 2, 4, MODE>(a, s); }
-template <int MODE> hipError_t dl256x192_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 192, 2, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl256x128_4x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 128, 4, 2, 4, MODE>(a, s); }
-template <int MODE> hipError_t dl256x128_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 128, 2, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl128x128_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl128x128_2x2_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 3, MODE>(a, s); }
-template <int MODE> hipError_t r16_256x256_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 256, 2, 4, MODE>(a, s); }
+
+
 template <int MODE> hipError_t r16_256x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 128, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t r16_128x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<128, 128, 2, 4, MODE>(a, s); }
-template <int MODE> hipError_t r32_256x256_2x4_p2(const GemmArgs& a, hipStream_t s) { return launch32<256, 256, 2, 4, 2, MODE>(a, s); }
-template <int MODE> hipError_t r32_256x128_4x2_p2(const GemmArgs& a, hipStream_t s) { return launch32<256, 128, 4, 2, 2, MODE>(a, s); }
 
 // Prefill configurations (M > 64).  dl: direct-to-LDS 32x32x32 kernel;
-// r16 / r32: register-staged unpack-to-LDS kernels on 16x16x64 / 32x32x32.
+// r16: register-staged unpack-to-LDS kernel on 16x16x64.
 const KernelCfg kTiles[] = {
     W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 2x4, 4 stages>", dl256x256_2x4_s4),
     W4A4_CFG("k_gemm_dl<128x128, waves 2x2, 4 stages>", dl128x128_2x2_s4),
     W4A4_CFG("k_gemm_w4a4<128x128, waves 2x4>", r16_128x128_2x4),
     W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 2x4, 3 stages>", dl256x256_2x4_s3),
-    W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 2x2, 4 stages>", dl256x256_2x2_s4),
-    W4A4_CFG_CHAN("k_gemm_dl<256x192, waves 2x2, 4 stages>", dl256x192_2x2_s4),
     W4A4_CFG("k_gemm_dl<256x128, waves 4x2, 4 stages>", dl256x128_4x2_s4),
-    W4A4_CFG("k_gemm_dl<256x128, waves 2x2, 4 stages>", dl256x128_2x2_s4),
-    W4A4_CFG_CHAN("k_gemm_w4a4<256x256, waves 2x4>", r16_256x256_2x4),
-    W4A4_CFG("k_gemm_w4a4<256x128, waves 2x4>", r16_256x128_2x4),
-    W4A4_CFG_CHAN("k_gemm32<256x256, waves 2x4, prefetch 2>", r32_256x256_2x4_p2),
-    W4A4_CFG("k_gemm32<256x128, waves 4x2, prefetch 2>", r32_256x128_4x2_p2),
     W4A4_CFG("k_gemm_dl<128x128, waves 2x2, 3 stages>", dl128x128_2x2_s3),
+    W4A4_CFG("k_gemm_w4a4<256x128, waves 2x4>", r16_256x128_2x4),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
