@@ -627,7 +627,7 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
 constexpr int kDecLdsMax = 160 * 1024;      // LDS of one CU
 constexpr int kDecAldsMax = 152 * 1024;     // budget for staged activations + scales
 
-template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS>
+template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS, bool G1>
 __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
@@ -636,6 +636,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
     static_assert(MODE == kModeChan || MODE == kModeGroup, "fp16 output modes only");
     static_assert(D >= 2 && D <= 8, "prefetch depth");
     static_assert(!ALDS || FM == 1, "staged activations: one row fragment");
+    static_assert(!G1 || MODE == kModeGroup, "one-tile groups: per-group mode");
     constexpr int BN = 16 * FN;
     constexpr int NT = NW * 64;
     constexpr int SLOTS = FM * FN * 4;          // accumulator values per lane
@@ -723,6 +724,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
             for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
 
     uint4 abuf[ALDS ? 1 : D][FM], bbuf[D][FN];
+    // a zero accumulator operand the compiler cannot fold into an inline
+    // constant (an MFMA with an inline-zero accumulator gave wrong sums)
+    v4i zc;
+    {
+        int z0;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+        zc = v4i{z0, z0, z0, z0};
+    }
     // issue position: tile it, clamped to the last tile of the range
     int it = t0;
     auto issue = [&](auto S) {
@@ -757,7 +766,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
         uint32_t szv[FN];
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
-            if constexpr (SZ) szv[b] = sz[zoff[b] + cg];
+            if constexpr (SZ) szv[b] = sz[zoff[b] + (G1 ? t : cg)];
             uint4 ev, od;
             if constexpr (ASYM) {
                 const uint32_t z = szv[b] >> 16;
@@ -767,6 +776,23 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
             }
             bev[b] = v4i{static_cast<int>(ev.x), static_cast<int>(ev.y), static_cast<int>(ev.z), static_cast<int>(ev.w)};
             bod[b] = v4i{static_cast<int>(od.x), static_cast<int>(od.y), static_cast<int>(od.z), static_cast<int>(od.w)};
+        }
+        if constexpr (G1) {
+            // one tile per weight group: the group's sums start from a zero
+            // register operand and are folded into fp32 at once
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const float sw = h2f(static_cast<uint16_t>(szv[b] & 0xFFFFu));
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aev[a], bev[b], zc, 0, 0, 0);
+                    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod[a], bod[b], p, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        facc[a][b][r] = fmaf(static_cast<float>(p[r]), sw, facc[a][b][r]);
+                }
+            }
+            return;
         }
 #pragma unroll
         for (int a = 0; a < FM; ++a)
@@ -851,9 +877,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
     }
 }
 
-template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS>
-hipError_t launch_dec_k(const GemmArgs& a, size_t lds, hipStream_t stream) {
-    auto* kern = &k_gemm_dec<FM, FN, NW, D, ASYM, MODE, ALDS>;
+template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS, bool G1>
+hipError_t launch_dec_g(const GemmArgs& a, size_t lds, hipStream_t stream) {
+    auto* kern = &k_gemm_dec<FM, FN, NW, D, ASYM, MODE, ALDS, G1>;
     if (lds > 64 * 1024) {
         // more than the default dynamic LDS limit: raise it once per device
         static bool raised[64] = {};
@@ -870,6 +896,14 @@ hipError_t launch_dec_k(const GemmArgs& a, size_t lds, hipStream_t stream) {
     kern<<<dim3(ceil_div(a.N, 16 * FN)), dim3(NW * 64), lds, stream>>>(
         a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
     return hipGetLastError();
+}
+
+template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS>
+hipError_t launch_dec_k(const GemmArgs& a, size_t lds, hipStream_t stream) {
+    if constexpr (MODE == kModeGroup) {
+        if (a.group_size == BK) return launch_dec_g<FM, FN, NW, D, ASYM, MODE, ALDS, true>(a, lds, stream);
+    }
+    return launch_dec_g<FM, FN, NW, D, ASYM, MODE, ALDS, false>(a, lds, stream);
 }
 
 template <int FM, int FN, int NW, int D, bool ASYM, int MODE>
