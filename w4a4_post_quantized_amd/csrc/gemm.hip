@@ -970,6 +970,7 @@ template <int MODE> hipError_t dl256x256_2x4_s3(const GemmArgs& a, hipStream_t s
 template <int MODE> hipError_t dl256x128_4x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 128, 4, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl128x128_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl128x128_2x2_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 3, MODE>(a, s); }
+template <int MODE> hipError_t dl128x256_2x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 256, 2, 4, 3, MODE>(a, s); }
 
 
 template <int MODE> hipError_t r16_256x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 128, 2, 4, MODE>(a, s); }
@@ -985,6 +986,7 @@ const KernelCfg kTiles[] = {
     W4A4_CFG("k_gemm_dl<256x128, waves 4x2, 4 stages>", dl256x128_4x2_s4),
     W4A4_CFG("k_gemm_dl<128x128, waves 2x2, 3 stages>", dl128x128_2x2_s3),
     W4A4_CFG("k_gemm_w4a4<256x128, waves 2x4>", r16_256x128_2x4),
+    W4A4_CFG_CHAN("k_gemm_dl<128x256, waves 2x4, 3 stages>", dl128x256_2x4_s3),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
