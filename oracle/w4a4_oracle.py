@@ -26,6 +26,10 @@ Every step is plain numpy in float64, written from the pages:
   so the activation scale can be applied after the integer product.
 * PT2-LLM: Post-Training Ternarization for Large Language Models, "关键设计"
   item 1: a joint column permutation leaves X W^T unchanged.
+* Static activation quantization (steps fixed offline, no runtime absmax):
+  FPTQuant page, "核心贡献" item on static INT4 quantization (one step per
+  tensor); MergeQuant page, "核心思路" and "关键设计" item 2 (per-channel
+  steps migrated into the weights of the linear layer, "QSM").
 
 Readings where the pages are silent or garbled (each restated in the design doc):
 round half to even; symmetric activations s = α·max|z|/7 with codes clamped to
@@ -43,6 +47,7 @@ __all__ = [
     "transform_quant", "pack_nibbles", "unpack_nibbles", "merge_weights",
     "fp16_rne", "quantize_weights", "int_gemm", "int_gemm_loop",
     "epilogue", "linear", "dequant_act", "dequant_weights",
+    "quantize_act_static", "transform_quant_static", "migrate_steps", "linear_static",
 ]
 
 QMIN, QMAX = -8, 7          # signed 4-bit code range (b = 4)
@@ -325,6 +330,71 @@ def linear(X, P1, P2, wq, c=None, alpha_a: float = 1.0, rows=None, cols=None):
     if rows is not None:
         Xs = Xs[rows]
     act = transform_quant(Xs, P1, P2, c, alpha_a)
+    codes, s, z = wq["codes"], wq["s"], wq["z"]
+    if cols is not None:
+        codes, s, z = codes[cols], s[cols], z[cols]
+    D = int_gemm(act["q"], codes, z, wq["group_size"])
+    Y64 = epilogue(D, act["s_x"], s)
+    return dict(Y64=Y64, act=act, D=D)
+
+
+# ----------------------------------------------------------------------------
+# Static activation quantization (steps fixed offline)
+# ----------------------------------------------------------------------------
+def quantize_act_static(Z, steps, per_channel: bool):
+    """Static INT4 activation codes with precomputed positive steps.
+
+    FPTQuant page, "核心贡献" (static INT4): one step for the whole tensor,
+    fixed offline, so no per-token absmax is taken at run time; the per-token
+    scale is that step.  MergeQuant page, "核心思路" / "关键设计" item 2: one
+    step per channel, migrated into the weights (see migrate_steps), so the
+    activation side carries no runtime scale at all (s_x = 1).
+    Codes clamp(round_half_even(Z / step), -8, 7).  Returns (q, t, s_x).
+    """
+    Z = np.asarray(Z, dtype=np.float64)
+    st = np.asarray(steps, dtype=np.float64).reshape(-1)
+    if per_channel:
+        if st.shape[0] != Z.shape[1]:
+            raise ValueError("one step per channel expected")
+        t = Z / st[None, :]
+        s_x = np.ones(Z.shape[0])
+    else:
+        if st.shape[0] != 1:
+            raise ValueError("one step per tensor expected")
+        t = Z / st[0]
+        s_x = np.full(Z.shape[0], st[0])
+    q = np.clip(np.rint(t), QMIN, QMAX).astype(np.int8)
+    return q, t, s_x
+
+
+def transform_quant_static(X, P1, P2, steps, per_channel: bool, c=None):
+    """Transform, then static quantization and packing.  Returns dict(Z, s_x, q, t, packed)."""
+    Z = kron_transform(X, P1, P2, c)
+    q, t, s_x = quantize_act_static(Z, steps, per_channel)
+    return dict(Z=Z, s_x=s_x, q=q, t=t, packed=pack_nibbles(q))
+
+
+def migrate_steps(Wt, steps, out_dtype=np.float32):
+    """Weight side of the step migration: W̃'[n, k] = W̃[n, k] · step_k.
+
+    MergeQuant page, "关键设计" item 2: the per-channel activation steps are
+    folded into the linear layer's weights, Σ_k (step_k q_k) W̃[n, k] =
+    Σ_k q_k W̃'[n, k].  The float64 product of two float32 values is exact,
+    so one rounding to float32 gives the correctly rounded product.
+    """
+    W64 = np.asarray(Wt, dtype=np.float64)
+    st = np.asarray(steps, dtype=np.float64).reshape(1, -1)
+    return (W64 * st).astype(out_dtype)
+
+
+def linear_static(X, P1, P2, wq, steps, per_channel: bool, c=None, rows=None, cols=None):
+    """Whole layer with static activation steps.  With per-channel steps ``wq``
+    quantizes the migrated weights migrate_steps(W̃, steps).  Returns
+    dict(Y64, act, D)."""
+    Xs = np.asarray(X)
+    if rows is not None:
+        Xs = Xs[rows]
+    act = transform_quant_static(Xs, P1, P2, steps, per_channel, c)
     codes, s, z = wq["codes"], wq["s"], wq["z"]
     if cols is not None:
         codes, s, z = codes[cols], s[cols], z[cols]

@@ -402,3 +402,153 @@ def test_linear_rows_cols_subset_consistent():
     rows, cols = np.array([0, 3, 15]), np.array([1, 100, 255])
     sub = O.linear(inp["X"], inp["P1"], inp["P2"], wq, rows=rows, cols=cols)
     assert np.array_equal(sub["Y64"], full["Y64"][np.ix_(rows, cols)])
+
+
+# ---------------------------------------------------------------------------
+# static activation quantization (steps fixed offline) and step migration
+# ---------------------------------------------------------------------------
+def test_golden_act_static_tensor():
+    g = GOLD["act_static_tensor"]
+    q, _, s_x = O.quantize_act_static(np.array([g["Z"]]), [g["step"]], per_channel=False)
+    assert q[0].tolist() == g["q"] and s_x[0] == g["s_x"]
+
+
+def test_golden_act_static_channel():
+    g = GOLD["act_static_channel"]
+    q, _, s_x = O.quantize_act_static(np.array([g["Z"]]), g["steps"], per_channel=True)
+    assert q[0].tolist() == g["q"] and s_x[0] == g["s_x"]
+
+
+def test_golden_qsm_migration():
+    g = GOLD["qsm_migration"]
+    Wm = O.migrate_steps(np.array([g["W"]], dtype=np.float32), g["steps"])
+    assert Wm[0].tolist() == g["W_migrated"]
+    q = np.array(g["q"])
+    # integer codes against the migrated row, as a Python-integer/rational sum
+    y = sum(Fraction(int(a)) * Fraction(float(b)) for a, b in zip(q, Wm[0]))
+    assert y == Fraction(g["y"])
+
+
+def test_static_tensor_step_equal_to_dynamic_scale_matches_dynamic():
+    """A per-tensor step equal to the token's own dynamic scale reproduces the
+    dynamic codes: static quantization differs only in where the step comes from."""
+    rng = np.random.default_rng(40)
+    Z = rng.standard_normal((7, 96)) * rng.uniform(0.1, 30, (7, 1))
+    for alpha in (1.0, 0.8):
+        s = O.act_scale(Z, alpha)
+        qd, _ = O.quantize_act(Z, s)
+        for m in range(Z.shape[0]):
+            qs, _, sx = O.quantize_act_static(Z[m:m + 1], [s[m]], per_channel=False)
+            assert np.array_equal(qs[0], qd[m]) and sx[0] == s[m]
+
+
+def _static_nearest_bruteforce(Z, steps):
+    """Nearest point of the clipped grid {step·q : q in [-8, 7]}, ties to the
+    even code, found by scanning all 16 codes with exact rationals."""
+    out = np.zeros(Z.shape, dtype=np.int64)
+    for idx, z in np.ndenumerate(Z):
+        st = Fraction(float(steps[idx[1]]))
+        zf = Fraction(float(z))
+        best = min(range(-8, 8), key=lambda c: (abs(zf - st * c), c % 2))
+        out[idx] = best
+    return out
+
+
+def _mut_static_divide_by_alpha_scale(Z, steps, per_channel):
+    # plausible slip: re-deriving the scale from the data instead of the fixed step
+    q, _ = O.quantize_act(Z, O.act_scale(Z, 1.0))
+    return q, None, np.ones(Z.shape[0])
+
+
+def _mut_static_channel_steps_transposed(Z, steps, per_channel):
+    st = np.asarray(steps)[::-1]
+    return O.quantize_act_static(Z, st, per_channel)
+
+
+@pytest.mark.parametrize("mut", [None, _mut_static_divide_by_alpha_scale,
+                                 _mut_static_channel_steps_transposed])
+def test_static_channel_codes_bruteforce(mut):
+    rng = np.random.default_rng(41)
+    Z = rng.standard_normal((5, 12)) * 6
+    Z[0, :4] = [0.5, 1.5, -2.5, 3.5]           # ties on a unit step
+    steps = np.concatenate([[1.0, 1.0, 1.0, 1.0], rng.uniform(0.2, 3.0, 8)])
+    want = _static_nearest_bruteforce(Z, steps)
+    fn = O.quantize_act_static if mut is None else mut
+    q = fn(Z, steps, True)[0]
+    assert np.array_equal(q, want) == (mut is None)
+
+
+def test_static_rtn_bound():
+    """Inside the clip range the static code is within half a step of z."""
+    rng = np.random.default_rng(42)
+    Z = rng.standard_normal((9, 64))
+    steps = rng.uniform(0.3, 1.0, 64)
+    q, t, _ = O.quantize_act_static(Z, steps, True)
+    inside = np.abs(t) <= 7
+    err = np.abs(Z - q * steps[None, :])
+    assert np.all(err[inside] <= steps[None, :].repeat(9, 0)[inside] / 2 + 1e-15)
+    assert np.all(q[~inside] == np.where(t[~inside] > 0, 7, -8))
+
+
+def test_qsm_layer_equals_step_dequantized_matmul():
+    """With per-channel steps migrated into the weights and weight codes that
+    are exact (power-of-two channel scales), the static layer equals
+    (q·step) W^T exactly and stays within sum_k |W[n,k]|·step_k/2 of Z W^T."""
+    rng = np.random.default_rng(43)
+    n1, n2, N = 4, 8, 6
+    K = n1 * n2
+    steps = 2.0 ** rng.integers(-3, 2, K)
+    ints = rng.integers(-7, 8, (N, K))
+    ints[:, 0] = 7                               # each row reaches |code| 7
+    cn = 2.0 ** rng.integers(-6, -2, N)
+    W = (cn[:, None] * ints / steps[None, :]).astype(np.float32)   # exact in fp32
+    Wm = O.migrate_steps(W, steps)
+    assert np.array_equal(Wm.astype(np.float64), cn[:, None] * ints)
+    wq = O.quantize_weights(Wm, K, False)
+    assert np.array_equal(wq["codes"], ints)
+    P1, P2 = np.eye(n1), np.eye(n2)
+    X = (rng.uniform(-7.0, 7.0, (5, K)) * steps[None, :]).astype(np.float16)
+    X[0, :3] = [100, -100, 0]                    # clipped entries in row 0
+    out = O.linear_static(X, P1, P2, wq, steps, per_channel=True)
+    deq = out["act"]["q"] * steps[None, :]
+    assert np.array_equal(out["Y64"], deq @ W.astype(np.float64).T)
+    Zx = X.astype(np.float64)
+    bound = (np.abs(W.astype(np.float64)) @ steps) / 2
+    t = Zx / steps[None, :]
+    rows_inside = np.all((t <= 7.5) & (t >= -8.5), axis=1)
+    err = np.abs(out["Y64"] - Zx @ W.astype(np.float64).T)
+    assert rows_inside.sum() == 4 and not rows_inside[0]
+    assert np.all(err[rows_inside] <= bound[None, :] + 1e-12)
+
+
+def _mut_migrate_divides(Wt, steps, out_dtype=np.float32):
+    return (np.asarray(Wt, np.float64) / np.asarray(steps).reshape(1, -1)).astype(out_dtype)
+
+
+def test_qsm_pin_catches_dividing_migration():
+    g = GOLD["qsm_migration"]
+    Wm = _mut_migrate_divides(np.array([g["W"]], dtype=np.float32), g["steps"])
+    assert Wm[0].tolist() != g["W_migrated"]
+
+
+def test_static_tensor_layer_transform_and_epilogue():
+    """Per-tensor static layer: s_x is the step on every token, and the layer
+    equals the dequantize-then-multiply simulation (step·q)(s_w·codes)^T."""
+    rng = np.random.default_rng(44)
+    X = rng.standard_normal((6, 64)).astype(np.float16)
+    P1 = WL.random_invertible(rng, 8)
+    P2 = WL.random_invertible(rng, 8)
+    W = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
+    wq = O.quantize_weights(O.merge_weights(W, P1, P2), 64, False)
+    step = 0.37
+    out = O.linear_static(X, P1, P2, wq, [step], per_channel=False)
+    assert np.all(out["act"]["s_x"] == step)
+    sim = O.dequant_act(out["act"]["q"], out["act"]["s_x"]) @ O.dequant_weights(wq).T
+    assert np.allclose(out["Y64"], sim, rtol=1e-12, atol=1e-12 * np.abs(sim).max())
+
+
+def test_static_rejects_wrong_step_count():
+    with pytest.raises(ValueError):
+        O.quantize_act_static(np.zeros((2, 4)), [1.0, 2.0], per_channel=True)
+    with pytest.raises(ValueError):
+        O.quantize_act_static(np.zeros((2, 4)), [1.0, 2.0], per_channel=False)
