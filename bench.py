@@ -2,6 +2,7 @@
 """Benchmark of the W4A4 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qkv8b]
+                    [--act-quant dynamic|tensor|channel]
 
 A step is one pass of the whole hot path over one batch: w4a4_linear =
 fused activation transform + per-token INT4 quantization + packing, then the
@@ -9,6 +10,11 @@ INT4 x INT4 GEMM with int32 accumulation and the fp16 dequant epilogue.
 Inputs are seeded synthetic LLaMA-shaped tensors (workloads/), resident in
 HBM before the timed region; weights are merged (P^-1 folded in), quantized
 and packed on the GPU beforehand, as a deployment would do offline.
+
+With --act-quant tensor|channel the activation steps are static (fixed
+offline from a seeded calibration batch, FPTQuant / MergeQuant): one step
+for the tensor, or one per channel migrated into the weights before packing;
+the step runs w4a4_linear_static instead.
 
 Prints ONE JSON line.  `value` is TOPS of the whole layer (2*M*N*K integer
 ops per step / step time).  `roofline` reports the dominant kernel (the GEMM)
@@ -44,6 +50,9 @@ def parse():
     ap.add_argument("--workload", default="qkv8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--act-quant", choices=["dynamic", "tensor", "channel"], default="dynamic",
+                    help="activation quantizer: per-token dynamic scales, or static steps "
+                         "(one per tensor, or one per channel migrated into the weights)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -85,7 +94,17 @@ def traffic_from_profiles(kernel_tag, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, budget_s):
+CAL_TOKENS = 256                 # calibration batch for static steps
+CAL_SEED_OFFSET = 7919
+
+
+def calibration_batch(wl, inp):
+    import workloads as WL
+    return WL.make_calibration_activations(wl, CAL_TOKENS, inp["outlier_channels"],
+                                           seed=wl.seed + CAL_SEED_OFFSET)
+
+
+def cpu_baseline(wl, inp, budget_s, act_quant="dynamic"):
     """The CPU oracle on the same workload: whole passes until `budget_s`."""
     import oracle as O
     try:
@@ -93,15 +112,26 @@ def cpu_baseline(wl, inp, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    # weights are prepared offline on both sides (not timed)
+    # weights (and static steps) are prepared offline on both sides (not timed)
     Wt = O.merge_weights(inp["W"], inp["P1"], inp["P2"], inp["c"])
+    static = act_quant != "dynamic"
+    pc = act_quant == "channel"
+    if static:
+        Zc = O.kron_transform(calibration_batch(wl, inp), inp["P1"], inp["P2"], inp["c"])
+        steps = O.calibrate_steps(Zc, pc).astype(np.float64)
+        del Zc
+        if pc:
+            Wt = O.migrate_steps(Wt, steps)
     wq = O.quantize_weights(Wt, wl.group_size, wl.asymmetric)
     del Wt
     times = []
     t_end = time.perf_counter() + budget_s
     while True:
         t0 = time.perf_counter()
-        O.linear(inp["X"], inp["P1"], inp["P2"], wq, c=inp["c"])
+        if static:
+            O.linear_static(inp["X"], inp["P1"], inp["P2"], wq, steps, pc, c=inp["c"])
+        else:
+            O.linear(inp["X"], inp["P1"], inp["P2"], wq, c=inp["c"])
         times.append(time.perf_counter() - t0)
         if time.perf_counter() >= t_end:
             break
@@ -148,6 +178,17 @@ def main():
     Wraw = torch.from_numpy(inp["W"]).to(dev)
     Wt = L.merge_weights(Wraw, P1, P2)
     del Wraw
+    static = args.act_quant != "dynamic"
+    pc = args.act_quant == "channel"
+    steps = None
+    if static:
+        # offline calibration: range of the transformed calibration batch / 7
+        Zc = L.transform(torch.from_numpy(calibration_batch(wl, inp)).to(dev), P1, P2)
+        amax = Zc.abs().amax(dim=0) if pc else Zc.abs().amax().reshape(1)
+        steps = torch.where(amax > 0, amax / 7.0, torch.ones_like(amax)).contiguous()
+        del Zc, amax
+        if pc:
+            Wt = L.migrate_steps(Wt, steps)
     packs = []
     for i in range(copies):
         packs.append(L.pack_weights(Wt if i == 0 else Wt * (1.0 + 1e-3 * i), wl.group_size,
@@ -165,7 +206,16 @@ def main():
 
     def step(i):
         _, Wq, sw, zw = packs[i % copies]
-        L.linear(X, P1, P2, desc, Wq, sw, zw, out=Y, ws=ws)
+        if static:
+            L.linear_static(X, P1, P2, steps, pc, desc, Wq, sw, zw, out=Y, ws=ws)
+        else:
+            L.linear(X, P1, P2, desc, Wq, sw, zw, out=Y, ws=ws)
+
+    def act(i):
+        if static:
+            L.transform_quant_static(X, P1, P2, steps, pc, out=(Xq, sx), ws=tq_ws)
+        else:
+            L.transform_quant(X, P1, P2, out=(Xq, sx), ws=tq_ws)
 
     for i in range(args.warmup):
         step(i)
@@ -181,12 +231,12 @@ def main():
     # which the binding uses); the GEMM reads the activations the transform
     # left in Xq / sx and rotates the weight copies like the timed steps
     for i in range(args.warmup):
-        L.transform_quant(X, P1, P2, out=(Xq, sx), ws=tq_ws)
+        act(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
-        L.transform_quant(X, P1, P2, out=(Xq, sx), ws=tq_ws)
+        act(i)
     e1.record()
     torch.cuda.synchronize()
     tq_us = e0.elapsed_time(e1) * 1e3 / args.steps
@@ -226,7 +276,8 @@ def main():
         "data": "synthetic (seeded; LLaMA-shaped, outlier channels and pivot token)",
         "config": {"workload": wl.description, "name": wl.name, "M": M, "K": K, "N": N,
                    "n1": wl.n1, "n2": wl.n2, "group_size": wl.group_size,
-                   "asymmetric_weights": wl.asymmetric, "weight_copies_rotated": copies},
+                   "asymmetric_weights": wl.asymmetric, "weight_copies_rotated": copies,
+                   "act_quant": args.act_quant},
         "us_per_layer": round(t_step * 1e6, 2),
         "transform_quant_us": round(tq_us, 2),
         "gemm_us": round(gemm_us, 2),
@@ -234,7 +285,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.act_quant)
     print(json.dumps(out), flush=True)
 
 

@@ -120,6 +120,20 @@ int w4a4_merge_weights(const float* W, int32_t N, int32_t K, int32_t n1, int32_t
 int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha_w,
                       uint8_t* Wq, uint16_t* s_w, uint16_t* z_w, void* stream);
 
+/* Step migration for static per-channel activation steps (offline).
+ * MergeQuant page ("MergeQuant: Accurate 4-bit Static Quantization of Large
+ * Language Models by Channel-wise Calibration"), sections 核心思路 and
+ * 关键设计 item 2: the per-channel quantization steps of the layer's input
+ * are folded into its weights, so that
+ *   Σ_k (step_k · q_k) · W̃[n, k] = Σ_k q_k · Wm[n, k],  Wm[n, k] = W̃[n, k] · step_k.
+ *   Wt [N, K] fp32 merged weights, steps [K] fp32 (positive), Wm [N, K] fp32
+ *   output: each element is the correctly rounded fp32 product.  Wm may be
+ *   Wt (in place).  K must be a multiple of 4.  Quantize Wm with
+ *   w4a4_pack_weights and run the layer with w4a4_linear_static(...,
+ *   per_channel = 1). */
+int w4a4_migrate_steps(const float* Wt, int32_t N, int32_t K, const float* steps, float* Wm,
+                       void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Online activation path                                                    */
 /* ------------------------------------------------------------------------ */
@@ -146,6 +160,26 @@ size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2, i
 int w4a4_transform_quant(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                          const float* P1, const float* P2, const float* c, float alpha_a,
                          uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes, void* stream);
+
+/* Static-step form of w4a4_transform_quant: the activation steps are fixed
+ * offline and read from `steps`, so no per-token absmax is taken.
+ *   per_channel = 0: FPTQuant page, section 核心贡献 (static INT4
+ *     quantization): one step for the tensor, steps[0];
+ *     q = clamp(round_half_even(Z_m / steps[0]), -8, 7), s_x[m] = steps[0].
+ *   per_channel = 1: MergeQuant page, sections 核心思路 and 关键设计 items
+ *     1-2 (per-channel static steps migrated into the weights): steps[K];
+ *     q[k] = clamp(round_half_even(Z_m[k] / steps[k]), -8, 7), s_x[m] = 1
+ *     (the steps live in the weights, see w4a4_migrate_steps).
+ * Z_m, X, P1, P2, c, Xq, s_x and ws as for w4a4_transform_quant (same
+ * workspace size).  steps: device fp32, 16-byte aligned, positive and finite
+ * (the values stay on the device and are not checked).  The division by a
+ * per-channel step uses the hardware reciprocal (within one ulp), so a code
+ * may differ from the exact quotient's only where Z/step lies within a few
+ * 1e-6 of a rounding tie. */
+int w4a4_transform_quant_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                                const float* P1, const float* P2, const float* c,
+                                const float* steps, int32_t per_channel, uint8_t* Xq,
+                                float* s_x, void* ws, size_t ws_bytes, void* stream);
 
 /* Debug / parity form of the transform: writes Z [M, K] fp32 (the value that
  * w4a4_transform_quant quantizes, same kernels, same arithmetic). */
@@ -200,6 +234,18 @@ int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                 const float* P1, const float* P2, const float* c, float alpha_a,
                 const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
                 const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
+
+/* w4a4_linear with static activation steps (w4a4_transform_quant_static
+ * followed by w4a4_gemm; same workspace as w4a4_linear).  With
+ * per_channel = 1 the weights must carry the migrated steps
+ * (w4a4_migrate_steps before w4a4_pack_weights): the epilogue then scales by
+ * s_w alone, as the MergeQuant page's step migration (关键设计 item 2) has no
+ * activation dequantization after the product. */
+int w4a4_linear_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                       const float* P1, const float* P2, const float* c, const float* steps,
+                       int32_t per_channel, const w4a4_weight_desc* desc, const uint8_t* Wq,
+                       const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y, void* ws,
+                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,7 @@ __all__ = [
     "fp16_rne", "quantize_weights", "int_gemm", "int_gemm_loop",
     "epilogue", "linear", "dequant_act", "dequant_weights",
     "quantize_act_static", "transform_quant_static", "migrate_steps", "linear_static",
+    "calibrate_steps",
 ]
 
 QMIN, QMAX = -8, 7          # signed 4-bit code range (b = 4)
@@ -341,6 +342,29 @@ def linear(X, P1, P2, wq, c=None, alpha_a: float = 1.0, rows=None, cols=None):
 # ----------------------------------------------------------------------------
 # Static activation quantization (steps fixed offline)
 # ----------------------------------------------------------------------------
+def calibrate_steps(Zc, per_channel: bool, ratio: float = 1.0):
+    """Offline steps from a calibration batch of transformed activations Zc.
+
+    The pages fix the steps offline (FPTQuant page, "核心贡献"; MergeQuant
+    page, "技术框架" items 1 and 4: per-channel calibration with a clipping
+    range) without giving the estimator; the plain reading taken here is the
+    calibration range divided by the largest positive code:
+    ratio · max|Zc| / 7 for the tensor, ratio · max_m |Zc[m, k]| / 7 per
+    channel.  A channel that is zero over the whole batch gets step 1 (any
+    positive step maps its zeros to code 0).  Returned as float32, the
+    precision the steps are stored in.
+    """
+    Zc = np.abs(np.asarray(Zc, dtype=np.float64))
+    if per_channel:
+        st = ratio * Zc.max(axis=0) / 7.0
+        st[st == 0] = 1.0
+    else:
+        st = np.array([ratio * Zc.max() / 7.0])
+        if st[0] == 0:
+            st[0] = 1.0
+    return st.astype(np.float32)
+
+
 def quantize_act_static(Z, steps, per_channel: bool):
     """Static INT4 activation codes with precomputed positive steps.
 

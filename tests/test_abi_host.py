@@ -145,3 +145,37 @@ def test_gemm_kernel_name_query():
     assert W.gemm_kernel_name(2048, W.WeightDesc(28672, 4096, 128, 1)).startswith("k_gemm")
     with pytest.raises(W.W4A4Error):
         W.gemm_kernel_name(16, W.WeightDesc(256, 200, 200, 0))
+
+
+def test_static_entry_points_validation():
+    L = W.lib()
+
+    def tq(X=FAKE, M=4, n1=16, n2=16, st=FAKE, pc=0, Xq=FAKE, sx=FAKE, c=None):
+        return L.w4a4_transform_quant_static(X, M, n1, n2, FAKE, FAKE, c, st, pc, Xq, sx, FAKE,
+                                             1 << 30, None)
+
+    assert tq(st=None) == -1 and "steps" in last()
+    assert tq(pc=2) == -1 and "per_channel" in last()
+    assert tq(st=MISALIGNED) == -3
+    assert tq(X=None) == -1
+    assert tq(n1=3, n2=5) == -2
+    assert tq(M=0, X=None) == 0                       # empty: nothing to do
+
+    assert L.w4a4_migrate_steps(FAKE, 8, 256, None, FAKE, None) == -1
+    assert L.w4a4_migrate_steps(FAKE, 8, 258, FAKE, FAKE, None) == -2   # K % 4
+    assert L.w4a4_migrate_steps(FAKE, -1, 256, FAKE, FAKE, None) == -1
+    assert L.w4a4_migrate_steps(MISALIGNED, 8, 256, FAKE, FAKE, None) == -3
+    assert L.w4a4_migrate_steps(None, 0, 256, FAKE, FAKE, None) == 0     # empty
+
+    d = desc(N=256, K=256, g=256)
+    nb = L.w4a4_linear_workspace_bytes(16, 16, 16, 0, d)
+
+    def lin(st=FAKE, pc=1, n1=16, wsb=nb):
+        return L.w4a4_linear_static(FAKE, 16, n1, 16, FAKE, FAKE, None, st, pc, d, FAKE, FAKE,
+                                    None, FAKE, FAKE, wsb, None)
+
+    assert lin(st=None) == -1
+    assert lin(pc=-1) == -1
+    assert lin(n1=8) == -1                            # desc K != n1*n2
+    assert lin(wsb=nb - 1) == -4
+    assert lin(st=MISALIGNED) == -3

@@ -552,3 +552,28 @@ def test_static_rejects_wrong_step_count():
         O.quantize_act_static(np.zeros((2, 4)), [1.0, 2.0], per_channel=True)
     with pytest.raises(ValueError):
         O.quantize_act_static(np.zeros((2, 4)), [1.0, 2.0], per_channel=False)
+
+
+def test_calibrate_steps_hand_case():
+    """Zc = [[1, -14, 0], [-7, 3.5, 0]]: range 14 -> step 2 for the tensor;
+    per channel 7/7 = 1, 14/7 = 2 and 1 for the all-zero channel."""
+    Zc = np.array([[1.0, -14.0, 0.0], [-7.0, 3.5, 0.0]])
+    assert O.calibrate_steps(Zc, False).tolist() == [2.0]
+    assert O.calibrate_steps(Zc, True).tolist() == [1.0, 2.0, 1.0]
+    assert O.calibrate_steps(Zc, False, ratio=0.5).tolist() == [1.0]
+
+
+def test_calibrated_steps_cover_their_own_batch():
+    """Steps calibrated (ratio 1) on a batch quantize that batch without
+    clipping: every |t| <= 7, so no code reaches -8, and every channel's (or
+    the tensor's) largest magnitude maps to code +-7."""
+    rng = np.random.default_rng(45)
+    Z = rng.standard_normal((20, 48)) * rng.uniform(0.1, 10, 48)[None, :]
+    for pc in (False, True):
+        st = O.calibrate_steps(Z, pc)
+        q, t, _ = O.quantize_act_static(Z, st.astype(np.float64), pc)
+        assert np.all(np.abs(t) <= 7 * (1 + 1e-6)) and not (q == -8).any()
+        if pc:
+            assert np.all(np.abs(q).max(axis=0) == 7)
+        else:
+            assert np.abs(q).max() == 7

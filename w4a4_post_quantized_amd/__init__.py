@@ -18,6 +18,7 @@ __all__ = [
     "merge_weights", "pack_weights", "transform_quant", "transform", "gemm",
     "gemm_i32", "gemm_kernel_name", "linear", "merge_workspace_bytes", "transform_quant_workspace_bytes",
     "gemm_workspace_bytes", "linear_workspace_bytes", "version",
+    "migrate_steps", "transform_quant_static", "linear_static",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so")
@@ -26,9 +27,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so"
 EXPORTED_SYMBOLS = [
     "w4a4_version", "w4a4_status_str", "w4a4_last_error",
     "w4a4_merge_workspace_bytes", "w4a4_merge_weights", "w4a4_pack_weights",
-    "w4a4_transform_quant_workspace_bytes", "w4a4_transform_quant", "w4a4_transform",
+    "w4a4_migrate_steps",
+    "w4a4_transform_quant_workspace_bytes", "w4a4_transform_quant", "w4a4_transform_quant_static",
+    "w4a4_transform",
     "w4a4_gemm_workspace_bytes", "w4a4_gemm", "w4a4_gemm_i32", "w4a4_gemm_kernel_name",
-    "w4a4_linear_workspace_bytes", "w4a4_linear",
+    "w4a4_linear_workspace_bytes", "w4a4_linear", "w4a4_linear_static",
 ]
 
 
@@ -80,6 +83,11 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm_kernel_name": (ctypes.c_char_p, [i32, dp]),
             "w4a4_linear_workspace_bytes": (sz, [i32, i32, i32, i32, dp]),
             "w4a4_linear": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, dp, vp, vp, vp, vp, vp, sz, vp]),
+            "w4a4_migrate_steps": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
+            "w4a4_transform_quant_static": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
+                                                           vp, sz, vp]),
+            "w4a4_linear_static": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, i32, dp, vp, vp, vp,
+                                                  vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -220,6 +228,46 @@ def transform_quant(X, P1, P2, c=None, alpha_a: float = 1.0, out=None, ws=None, 
     return Xq, s_x
 
 
+def transform_quant_static(X, P1, P2, steps, per_channel: bool, c=None, out=None, ws=None,
+                           stream=None):
+    """Transform + INT4 quantization with offline steps (steps [1] per tensor,
+    [K] per channel): returns (Xq [M,K/2], s_x [M])."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    _need(X, torch.float16, (M, K), "X")
+    _need(P1, torch.float32, (n1, n1), "P1")
+    _need(P2, torch.float32, (n2, n2), "P2")
+    _need(steps, torch.float32, (K if per_channel else 1,), "steps")
+    if c is not None:
+        _need(c, torch.float32, (K,), "c")
+    if out is None:
+        Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+        s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
+    else:
+        Xq, s_x = out
+    nb = transform_quant_workspace_bytes(M, n1, n2, c is not None)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_transform_quant_static(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), _p(steps),
+                                             int(bool(per_channel)), _p(Xq), _p(s_x), _p(ws),
+                                             nb if ws is None else ws.numel(), _stream(stream)),
+           "w4a4_transform_quant_static")
+    return Xq, s_x
+
+
+def migrate_steps(Wt, steps, out=None, stream=None):
+    """Wm [N, K] fp32 = Wt · diag(steps): per-channel activation steps folded
+    into the weights (pass out=Wt for in place)."""
+    torch = _torch()
+    N, K = Wt.shape
+    _need(Wt, torch.float32, (N, K), "Wt")
+    _need(steps, torch.float32, (K,), "steps")
+    Wm = out if out is not None else torch.empty_like(Wt)
+    _check(lib().w4a4_migrate_steps(_p(Wt), N, K, _p(steps), _p(Wm), _stream(stream)),
+           "w4a4_migrate_steps")
+    return Wm
+
+
 def transform(X, P1, P2, c=None, stream=None):
     """Debug form: the fp32 transformed activations Z [M, K]."""
     torch = _torch()
@@ -276,4 +324,21 @@ def linear(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, c=None, alpha_a: floa
     _check(lib().w4a4_linear(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
                              ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y), _p(ws),
                              nb if ws is None else ws.numel(), _stream(stream)), "w4a4_linear")
+    return Y
+
+
+def linear_static(X, P1, P2, steps, per_channel: bool, desc: WeightDesc, Wq, s_w, z_w=None,
+                  c=None, out=None, ws=None, stream=None):
+    """Whole W4A4 layer with static activation steps: Y [M, N] fp16."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    _need(steps, torch.float32, (K if per_channel else 1,), "steps")
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=X.device)
+    nb = linear_workspace_bytes(M, n1, n2, desc, c is not None)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_linear_static(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), _p(steps),
+                                    int(bool(per_channel)), ctypes.byref(desc), _p(Wq), _p(s_w),
+                                    _p(z_w), _p(Y), _p(ws), nb if ws is None else ws.numel(),
+                                    _stream(stream)), "w4a4_linear_static")
     return Y

@@ -152,6 +152,24 @@ int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha
     return hip_status(e, "w4a4_pack_weights");
 }
 
+int w4a4_migrate_steps(const float* Wt, int32_t N, int32_t K, const float* steps, float* Wm,
+                       void* stream) {
+    REQUIRE(N >= 0, W4A4_ERR_INVALID_ARG, "N = %d is negative", N);
+    REQUIRE(K >= 1 && K <= W4A4_MAX_K, W4A4_ERR_INVALID_ARG, "K = %d outside [1, %d]", K,
+            W4A4_MAX_K);
+    REQUIRE(K % 4 == 0, W4A4_ERR_UNSUPPORTED, "K = %d is not a multiple of 4", K);
+    if (N == 0) return ok();
+    REQUIRE_PTR(Wt);
+    REQUIRE_PTR(steps);
+    REQUIRE_PTR(Wm);
+    REQUIRE_ALIGNED(Wt);
+    REQUIRE_ALIGNED(steps);
+    REQUIRE_ALIGNED(Wm);
+    hipError_t e = w4a4::migrate_steps_launch(Wt, N, K, steps, Wm,
+                                              static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_migrate_steps");
+}
+
 // ---------------------------------------------------------------------------
 size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t has_c) {
     if (M < 0 || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR || n2 > W4A4_MAX_FACTOR) return 0;
@@ -159,13 +177,15 @@ size_t w4a4_transform_quant_workspace_bytes(int32_t M, int32_t n1, int32_t n2, i
 }
 
 static int tq_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
-                     const float* P2, const float* c, float alpha_a, bool quantize,
+                     const float* P2, const float* c, w4a4::ActQuant aq, bool quantize,
                      uint8_t* Xq, float* s_x, float* Z, void* ws, size_t ws_bytes,
                      void* stream, const char* name) {
     if (int s = check_factors(M, n1, n2)) return s;
-    REQUIRE(alpha_a > 0.0f && alpha_a <= 1.0f, W4A4_ERR_INVALID_ARG,
-            "alpha_a = %g must lie in (0, 1]", static_cast<double>(alpha_a));
+    if (aq.steps == nullptr)
+        REQUIRE(aq.alpha > 0.0f && aq.alpha <= 1.0f, W4A4_ERR_INVALID_ARG,
+                "alpha_a = %g must lie in (0, 1]", static_cast<double>(aq.alpha));
     if (M == 0) return ok();
+    if (aq.steps != nullptr) REQUIRE_ALIGNED(aq.steps);
     REQUIRE_PTR(X);
     REQUIRE_PTR(P1);
     REQUIRE_PTR(P2);
@@ -188,7 +208,7 @@ static int tq_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const
                 "workspace %zu < %zu bytes", ws ? ws_bytes : 0, need);
         REQUIRE_ALIGNED(ws);
     }
-    hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, alpha_a, quantize, Xq, s_x, Z, ws,
+    hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, aq, quantize, Xq, s_x, Z, ws,
                                    ws_bytes, static_cast<hipStream_t>(stream));
     return hip_status(e, name);
 }
@@ -196,15 +216,26 @@ static int tq_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const
 int w4a4_transform_quant(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                          const float* P1, const float* P2, const float* c, float alpha_a,
                          uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes, void* stream) {
-    return tq_common(X, M, n1, n2, P1, P2, c, alpha_a, true, Xq, s_x, nullptr, ws, ws_bytes,
-                     stream, "w4a4_transform_quant");
+    return tq_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{alpha_a, nullptr, false}, true, Xq,
+                     s_x, nullptr, ws, ws_bytes, stream, "w4a4_transform_quant");
+}
+
+int w4a4_transform_quant_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                                const float* P1, const float* P2, const float* c,
+                                const float* steps, int32_t per_channel, uint8_t* Xq,
+                                float* s_x, void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE_PTR(steps);
+    REQUIRE(per_channel == 0 || per_channel == 1, W4A4_ERR_INVALID_ARG,
+            "per_channel = %d must be 0 or 1", per_channel);
+    return tq_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{1.0f, steps, per_channel != 0}, true,
+                     Xq, s_x, nullptr, ws, ws_bytes, stream, "w4a4_transform_quant_static");
 }
 
 int w4a4_transform(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
                    const float* P2, const float* c, float* Z, void* ws, size_t ws_bytes,
                    void* stream) {
-    return tq_common(X, M, n1, n2, P1, P2, c, 1.0f, false, nullptr, nullptr, Z, ws, ws_bytes,
-                     stream, "w4a4_transform");
+    return tq_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{1.0f, nullptr, false}, false,
+                     nullptr, nullptr, Z, ws, ws_bytes, stream, "w4a4_transform");
 }
 
 // ---------------------------------------------------------------------------
@@ -293,16 +324,18 @@ size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t ha
     return align256(K / 2 * M) + align256(sizeof(float) * M) + (tq > gm ? tq : gm);
 }
 
-int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
-                const float* P2, const float* c, float alpha_a, const w4a4_weight_desc* desc,
-                const uint8_t* Wq, const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y,
-                void* ws, size_t ws_bytes, void* stream) {
+static int linear_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                         const float* P2, const float* c, w4a4::ActQuant aq,
+                         const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                         const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes,
+                         void* stream, const char* name) {
     if (int s = check_desc(desc, true)) return s;
     if (int s = check_factors(M, n1, n2)) return s;
     REQUIRE(desc->K == n1 * n2, W4A4_ERR_INVALID_ARG, "desc->K = %d != n1*n2 = %d", desc->K,
             n1 * n2);
-    REQUIRE(alpha_a > 0.0f && alpha_a <= 1.0f, W4A4_ERR_INVALID_ARG,
-            "alpha_a = %g must lie in (0, 1]", static_cast<double>(alpha_a));
+    if (aq.steps == nullptr)
+        REQUIRE(aq.alpha > 0.0f && aq.alpha <= 1.0f, W4A4_ERR_INVALID_ARG,
+                "alpha_a = %g must lie in (0, 1]", static_cast<double>(aq.alpha));
     if (M == 0) return ok();
     REQUIRE_PTR(X);
     REQUIRE_PTR(P1);
@@ -316,6 +349,7 @@ int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const floa
     REQUIRE_ALIGNED(P1);
     REQUIRE_ALIGNED(P2);
     if (c) REQUIRE_ALIGNED(c);
+    if (aq.steps) REQUIRE_ALIGNED(aq.steps);
     REQUIRE_ALIGNED(Wq);
     REQUIRE_ALIGNED(s_w);
     if (desc->asymmetric) REQUIRE_ALIGNED(z_w);
@@ -334,13 +368,33 @@ int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const floa
     const size_t sub_bytes = ws_bytes - static_cast<size_t>(p - static_cast<char*>(ws));
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, alpha_a, true, Xq, s_x, nullptr,
-                                   sub, sub_bytes, st);
-    if (e != hipSuccess) return hip_status(e, "w4a4_linear (transform_quant)");
+    hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, aq, true, Xq, s_x, nullptr, sub,
+                                   sub_bytes, st);
+    if (e != hipSuccess) return hip_status(e, name);
     w4a4::GemmArgs a{Xq, s_x, Wq, s_w, z_w, Y, nullptr, M, desc->N, desc->K, desc->group_size,
                      desc->asymmetric != 0};
     e = w4a4::gemm_launch(a, false, sub, sub_bytes, st);
-    return hip_status(e, "w4a4_linear (gemm)");
+    return hip_status(e, name);
+}
+
+int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                const float* P2, const float* c, float alpha_a, const w4a4_weight_desc* desc,
+                const uint8_t* Wq, const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y,
+                void* ws, size_t ws_bytes, void* stream) {
+    return linear_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{alpha_a, nullptr, false}, desc,
+                         Wq, s_w, z_w, Y, ws, ws_bytes, stream, "w4a4_linear");
+}
+
+int w4a4_linear_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                       const float* P2, const float* c, const float* steps, int32_t per_channel,
+                       const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                       const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes,
+                       void* stream) {
+    REQUIRE_PTR(steps);
+    REQUIRE(per_channel == 0 || per_channel == 1, W4A4_ERR_INVALID_ARG,
+            "per_channel = %d must be 0 or 1", per_channel);
+    return linear_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{1.0f, steps, per_channel != 0},
+                         desc, Wq, s_w, z_w, Y, ws, ws_bytes, stream, "w4a4_linear_static");
 }
 
 }  // extern "C"

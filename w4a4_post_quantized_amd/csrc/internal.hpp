@@ -12,12 +12,22 @@ namespace w4a4 {
 // ---- activation path (transform_quant.hip) --------------------------------
 enum class TqPath { Fused, Cols, Split };
 
+// Activation quantizer of one call.  Dynamic (steps == nullptr): per-token
+// scale alpha * max|z| / 7.  Static: steps fixed offline, either one step for
+// the whole tensor (the token scale is that step) or one step per channel
+// (codes round z_k / step_k; the token scale written is 1).
+struct ActQuant {
+    float alpha;
+    const float* steps;
+    bool per_channel;
+};
+
 TqPath tq_select_path(int M, int n1, int n2, bool has_c);
 size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c);
 
 // quantize=true: Xq/s_x outputs; quantize=false: Z (fp32 [M,K]) output.
 hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
-                     const float* P2, const float* c, float alpha, bool quantize,
+                     const float* P2, const float* c, ActQuant aq, bool quantize,
                      uint8_t* Xq, float* s_x, float* Z, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
@@ -46,6 +56,9 @@ size_t merge_workspace_bytes(int n1, int n2, int K);
 hipError_t merge_launch(const float* W, int N, int K, int n1, int n2, const float* P1,
                         const float* P2, const float* c, float* Wt, void* ws,
                         hipStream_t stream, bool* singular);
+// Wm[n, k] = Wt[n, k] * steps[k] (fp32, one rounding); Wm may equal Wt
+hipError_t migrate_steps_launch(const float* Wt, int N, int K, const float* steps, float* Wm,
+                                hipStream_t stream);
 hipError_t pack_weights_launch(const float* Wt, int N, int K, int group_size, bool asym,
                                float alpha_w, uint8_t* Wq, uint16_t* s_w, uint16_t* z_w,
                                hipStream_t stream);

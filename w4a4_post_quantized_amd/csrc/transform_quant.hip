@@ -40,6 +40,9 @@ namespace w4a4 {
 
 namespace {
 
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 constexpr int kSplitThreads = 256;
 
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -98,45 +101,68 @@ __global__ __launch_bounds__(256) void k_tq_stage2(const float* __restrict__ T, 
     }
 }
 
-__global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, int K, float alpha,
+__global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, int K, ActQuant aq,
                                                   const uint32_t* __restrict__ amax, int nparts,
                                                   uint8_t* __restrict__ Xq,
                                                   float* __restrict__ s_x) {
     const int m = blockIdx.x;
     const int idx = blockIdx.y * blockDim.x + threadIdx.x;
     const int e0 = idx * 8;
+    const int ec = min(e0, K - 8);
     // this thread's 8 values (loaded before the scale is known)
     float z[8];
-    const float* zp = Z + static_cast<size_t>(m) * K + min(e0, K - 8);
+    const float* zp = Z + static_cast<size_t>(m) * K + ec;
 #pragma unroll
     for (int t = 0; t < 8; ++t) z[t] = zp[t];
-    // the token's absmax: the largest of its partial maxima (bit patterns of
-    // non-negative floats order like the floats), reduced by the workgroup
-    __shared__ float red[4];
-    float ab = 0.0f;
-    for (int q = threadIdx.x; q < nparts; q += 256)
-        ab = fmaxf(ab, __uint_as_float(amax[static_cast<size_t>(m) * nparts + q]));
-    ab = wave_max(ab);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ab;
-    __syncthreads();
-    ab = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = alpha * ab / 7.0f;
+    float s;
+    if (aq.steps == nullptr) {
+        // the token's absmax: the largest of its partial maxima (bit patterns
+        // of non-negative floats order like the floats), reduced by the
+        // workgroup
+        __shared__ float red[4];
+        float ab = 0.0f;
+        for (int q = threadIdx.x; q < nparts; q += 256)
+            ab = fmaxf(ab, __uint_as_float(amax[static_cast<size_t>(m) * nparts + q]));
+        ab = wave_max(ab);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ab;
+        __syncthreads();
+        ab = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        s = aq.alpha * ab / 7.0f;
+    } else {
+        s = aq.per_channel ? 1.0f : aq.steps[0];
+    }
     if (idx == 0) s_x[m] = s;
     if (e0 >= K) return;
-    const bool zero = !(s > 0.0f);
-    const float inv = zero ? 0.0f : 1.0f / s;
     uint32_t word = 0;
+    if (aq.steps != nullptr && aq.per_channel) {
+        const v4f st0 = *reinterpret_cast<const v4f*>(aq.steps + ec);
+        const v4f st1 = *reinterpret_cast<const v4f*>(aq.steps + ec + 4);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) word |= quant_nibble(z[t], inv, zero) << (4 * t);
+        for (int t = 0; t < 4; ++t) {
+            word |= quant_nibble_magic(z[t], __builtin_amdgcn_rcpf(st0[t])) << (4 * t);
+            word |= quant_nibble_magic(z[t + 4], __builtin_amdgcn_rcpf(st1[t])) << (4 * (t + 4));
+        }
+    } else {
+        const bool zero = !(s > 0.0f);
+        const float inv = zero ? 0.0f : 1.0f / s;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) word |= quant_nibble(z[t], inv, zero) << (4 * t);
+    }
     reinterpret_cast<uint32_t*>(Xq + static_cast<size_t>(m) * (K / 2))[idx] = word;
 }
 
 
+// Static per-channel steps through a buffer resource: the per-lane part of
+// a channel's byte offset sits in one VGPR and the part fixed at compile
+// time in the scalar offset, so a batch of step loads needs no 64-bit
+// address registers (reads past K return 0 and are never used).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t steps_rsrc(const float* steps, int K) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(steps), 0, K * 4, 0x00020000);
+}
+
 // ===========================================================================
 // Fused MFMA path
 // ===========================================================================
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 // floor(log2(x)) for a positive normal float
 __device__ __forceinline__ int ilog2f(float x) {
@@ -164,10 +190,12 @@ struct FusedCfg {
     static constexpr int XLD = (TPI * XCH + NT - 1) / NT;  // chunks per thread per tile
 };
 
-template <int N1, int N2>
+// PC: static per-channel steps (a separate instantiation, so that the
+// per-token paths carry none of its registers)
+template <int N1, int N2, bool PC>
 __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint16_t* __restrict__ X, int M,
                                                   const float* __restrict__ P1,
-                                                  const float* __restrict__ P2, float alpha,
+                                                  const float* __restrict__ P2, ActQuant aq,
                                                   uint8_t* __restrict__ Xq,
                                                   float* __restrict__ s_x,
                                                   float* __restrict__ Zout) {
@@ -362,11 +390,14 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
         float amax = 0.0f;
 #pragma unroll
         for (int w = 0; w < C::CB; ++w) amax = fmaxf(amax, red[tslot * C::CB + w]);
-        const float s = alpha * amax / 7.0f;
+        // static steps: the token scale is the tensor's step (or 1 with
+        // per-channel steps); the reduction above is then unused
+        const float s_static = PC ? 1.0f : (aq.steps ? aq.steps[0] : 0.0f);
+        const float s = aq.steps ? s_static : aq.alpha * amax / 7.0f;
         if (tid < C::TPI) {
             float a2 = 0.0f;
             for (int w = 0; w < C::CB; ++w) a2 = fmaxf(a2, red[tid * C::CB + w]);
-            tok_s[tid] = alpha * a2 / 7.0f;
+            tok_s[tid] = aq.steps ? s_static : aq.alpha * a2 / 7.0f;
         }
         if (valid) {
             if (Zout != nullptr) {
@@ -380,17 +411,32 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
                 const bool zero = !(s > 0.0f);
                 const float inv = zero ? 0.0f : 1.0f / s;
                 uint8_t* qb = qbuf + tslot * (K / 2);
+                const __amdgpu_buffer_rsrc_t srs = steps_rsrc(aq.steps, K);
+                const int svoff = ((4 * g) * N2 + 16 * cb + li) * 4;
 #pragma unroll
-                for (int ob = 0; ob < C::RB; ++ob)
+                for (int ob = 0; ob < C::RB; ++ob) {
+                    float rst[4];
+                    if (PC) {
+                        // this row block's four steps only: no batch of all
+                        // the token's step loads competing for registers
+                        asm volatile("" ::: "memory");
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            rst[r] = __builtin_amdgcn_rcpf(__builtin_bit_cast(
+                                float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           srs, svoff, (16 * ob + r) * N2 * 4, 0)));
+                    }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const uint32_t nib = quant_nibble(Z[ob][r], inv, zero);
+                        const uint32_t nib = PC ? quant_nibble_magic(Z[ob][r], rst[r])
+                                                : quant_nibble(Z[ob][r], inv, zero);
                         const uint32_t odd = lane_xor1(nib);
                         if ((li & 1) == 0) {
                             const int k = (16 * ob + 4 * g + r) * N2 + 16 * cb + li;
                             qb[k >> 1] = static_cast<uint8_t>(nib | (odd << 4));
                         }
                     }
+                }
             }
         }
         __syncthreads();
@@ -413,16 +459,16 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
     }
 }
 
-template <int N1, int N2>
-hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* P2, float alpha,
-                        uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+template <int N1, int N2, bool PC>
+hipError_t launch_fused_k(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
+                          uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
     using C = FusedCfg<N1, N2>;
     // persistent grid: as many workgroups as fit on the device at once, so the
     // per-workgroup fragment setup is paid once per resident workgroup
     static int per_cu = 0;
     if (per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_fused<N1, N2>, C::NT, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_fused<N1, N2, PC>, C::NT, 0) !=
                 hipSuccess || n < 1)
             n = 1;
         per_cu = n;
@@ -430,8 +476,16 @@ hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* 
     const int units = (M + C::TPI - 1) / C::TPI;
     const int cap = per_cu * device_cu_count();
     const int grid = units < cap ? units : cap;
-    k_tq_fused<N1, N2><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, alpha, Xq, s_x, Z);
+    k_tq_fused<N1, N2, PC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, aq, Xq, s_x, Z);
     return hipGetLastError();
+}
+
+template <int N1, int N2>
+hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
+                        uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+    if (aq.steps != nullptr && aq.per_channel && Xq != nullptr)
+        return launch_fused_k<N1, N2, true>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
+    return launch_fused_k<N1, N2, false>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
 }
 
 // ===========================================================================
@@ -465,10 +519,10 @@ struct WaveCfg {
     static_assert(QB % 16 == 0, "whole 16-byte chunks per token");
 };
 
-template <int N1, int N2>
+template <int N1, int N2, bool PC>
 __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_t* __restrict__ X, int M,
                                                                 const float* __restrict__ P1,
-                                                                const float* __restrict__ P2, float alpha,
+                                                                const float* __restrict__ P2, ActQuant aq,
                                                                 uint8_t* __restrict__ Xq,
                                                                 float* __restrict__ s_x,
                                                                 float* __restrict__ Zout) {
@@ -481,6 +535,10 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
     __shared__ __align__(16) _Float16 p1lo[C::P1F];
     __shared__ __align__(16) uint8_t qbuf[C::NW][C::QB];
     __shared__ float red[2 * C::NW];
+    // static per-channel steps: their reciprocals, rows of n2 padded by 4 so
+    // the 16 rows one quarter-wave reads fall in distinct banks
+    constexpr int SROW = N2 + 4;
+    __shared__ __align__(16) float rstep[PC ? N1 * SROW : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -546,6 +604,13 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
         if (!in) v1[i] = 0.0f;
         m1 = fmaxf(m1, fabsf(v1[i]));
     }
+    // static per-channel steps, loaded with the fragments (clamped, so the
+    // load count is fixed)
+    constexpr int SLN = PC ? (K / 4 + NT - 1) / NT : 0;
+    v4f stv[SLN > 0 ? SLN : 1];
+#pragma unroll
+    for (int i = 0; i < SLN; ++i)
+        stv[i] = reinterpret_cast<const v4f*>(aq.steps)[min(tid + i * NT, K / 4 - 1)];
     m1 = wave_max(m1);
     m2 = wave_max(m2);
     if (lane == 0) {
@@ -580,6 +645,16 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
             const _Float16 h = static_cast<_Float16>(v);
             p1hi[idx] = h;
             p1lo[idx] = static_cast<_Float16>(v - static_cast<float>(h));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SLN; ++i) {
+        const int c4 = tid + i * NT;
+        if (c4 < K / 4) {
+            const int r = (4 * c4) / N2, j = (4 * c4) % N2;
+            *reinterpret_cast<v4f*>(rstep + r * SROW + j) =
+                v4f{__builtin_amdgcn_rcpf(stv[i][0]), __builtin_amdgcn_rcpf(stv[i][1]),
+                    __builtin_amdgcn_rcpf(stv[i][2]), __builtin_amdgcn_rcpf(stv[i][3])};
         }
     }
     __syncthreads();
@@ -682,18 +757,41 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
                 for (int cb = 0; cb < C::CB; ++cb)
                     *reinterpret_cast<v4f*>(zo + (16 * ob + li) * N2 + 16 * cb + 4 * g) = Z[ob][cb];
         } else {
-            const float s = alpha * ldexpf(wave_max(zmax), unscale) / 7.0f;
+            float s;
+            if (PC)
+                s = 1.0f;
+            else if (aq.steps == nullptr)
+                s = aq.alpha * ldexpf(wave_max(zmax), unscale) / 7.0f;
+            else
+                s = aq.steps[0];
             const float inv = s > 0.0f ? ldexpf(1.0f / s, unscale) : 0.0f;
+            if (PC) {
+                // one step per channel: the lane's four consecutive channels
 #pragma unroll
-            for (int ob = 0; ob < C::RB; ++ob)
+                for (int ob = 0; ob < C::RB; ++ob)
 #pragma unroll
-                for (int cb = 0; cb < C::CB; ++cb) {
-                    uint32_t w = 0;
+                    for (int cb = 0; cb < C::CB; ++cb) {
+                        const int k0 = (16 * ob + li) * N2 + 16 * cb + 4 * g;
+                        const v4f rs = *reinterpret_cast<const v4f*>(
+                            rstep + (16 * ob + li) * SROW + 16 * cb + 4 * g + fo);
+                        uint32_t w = 0;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) w |= quant_nibble_magic(Z[ob][cb][r], inv) << (4 * r);
-                    *reinterpret_cast<uint16_t*>(qb + ((16 * ob + li) * N2 + 16 * cb + 4 * g) / 2) =
-                        static_cast<uint16_t>(w);
-                }
+                        for (int r = 0; r < 4; ++r)
+                            w |= quant_nibble_magic(ldexpf(Z[ob][cb][r], unscale), rs[r]) << (4 * r);
+                        *reinterpret_cast<uint16_t*>(qb + k0 / 2) = static_cast<uint16_t>(w);
+                    }
+            } else {
+#pragma unroll
+                for (int ob = 0; ob < C::RB; ++ob)
+#pragma unroll
+                    for (int cb = 0; cb < C::CB; ++cb) {
+                        uint32_t w = 0;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) w |= quant_nibble_magic(Z[ob][cb][r], inv) << (4 * r);
+                        *reinterpret_cast<uint16_t*>(qb + ((16 * ob + li) * N2 + 16 * cb + 4 * g) / 2) =
+                            static_cast<uint16_t>(w);
+                    }
+            }
             // the wave's LDS slice is read back by the same wave: LDS operations
             // of one wave complete in order
             uint4* dst = reinterpret_cast<uint4*>(Xq + static_cast<size_t>(m) * (K / 2));
@@ -708,16 +806,16 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
     }
 }
 
-template <int N1, int N2>
-hipError_t launch_wave(const uint16_t* X, int M, const float* P1, const float* P2, float alpha,
-                       uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+template <int N1, int N2, bool PC>
+hipError_t launch_wave_k(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
+                         uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
     using C = WaveCfg<N1, N2>;
     // persistent grid: as many workgroups as fit on the device at once, so
     // the fragment setup is paid once per resident workgroup
     static int per_cu = 0;
     if (per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_wave<N1, N2>, C::NT, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_wave<N1, N2, PC>, C::NT, 0) !=
                 hipSuccess || n < 1)
             n = 1;
         per_cu = n;
@@ -725,11 +823,19 @@ hipError_t launch_wave(const uint16_t* X, int M, const float* P1, const float* P
     const int units = (M + C::NW - 1) / C::NW;
     const int cap = per_cu * device_cu_count();
     const int grid = units < cap ? units : cap;
-    k_tq_wave<N1, N2><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, alpha, Xq, s_x, Z);
+    k_tq_wave<N1, N2, PC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, aq, Xq, s_x, Z);
     return hipGetLastError();
 }
 
-using FusedFn = hipError_t (*)(const uint16_t*, int, const float*, const float*, float, uint8_t*,
+template <int N1, int N2>
+hipError_t launch_wave(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
+                       uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+    if (aq.steps != nullptr && aq.per_channel && Xq != nullptr)
+        return launch_wave_k<N1, N2, true>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
+    return launch_wave_k<N1, N2, false>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
+}
+
+using FusedFn = hipError_t (*)(const uint16_t*, int, const float*, const float*, ActQuant, uint8_t*,
                                float*, float*, hipStream_t);
 
 // (n1, n2) pairs with a fused (or wave-per-token) instantiation
@@ -998,7 +1104,7 @@ size_t cols_ws_bytes(int M) {
 }
 
 template <int N1, int N2>
-hipError_t launch_cols(const uint16_t* X, int M, const float* P1, const float* P2, float alpha,
+hipError_t launch_cols(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
                        uint8_t* Xq, float* s_x, float* Z, void* ws, hipStream_t stream) {
     using C = ColsCfg<N1, N2>;
     int rbp, parts;
@@ -1025,12 +1131,12 @@ hipError_t launch_cols(const uint16_t* X, int M, const float* P1, const float* P
     k_tq_cols<N1, N2><<<grid, kColsWaves * 64, lds, stream>>>(X, M, P1, P2, rbp, parts, Zw, amax);
     if (Z == nullptr)
         k_tq_quant<<<dim3(M, ceil_div(C::K / 8, 256)), dim3(256), 0, stream>>>(
-            Zw, C::K, alpha, amax, C::CB * parts, Xq, s_x);
+            Zw, C::K, aq, amax, C::CB * parts, Xq, s_x);
     return hipGetLastError();
 }
 
 struct ColsFns {
-    hipError_t (*launch)(const uint16_t*, int, const float*, const float*, float, uint8_t*, float*,
+    hipError_t (*launch)(const uint16_t*, int, const float*, const float*, ActQuant, uint8_t*, float*,
                          float*, void*, hipStream_t);
     size_t (*ws_bytes)(int);
 };
@@ -1072,17 +1178,17 @@ size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c) {
 }
 
 hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
-                     const float* P2, const float* c, float alpha, bool quantize,
+                     const float* P2, const float* c, ActQuant aq, bool quantize,
                      uint8_t* Xq, float* s_x, float* Z, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
     (void)ws_bytes;
     if (M == 0) return hipSuccess;
     const TqPath path = tq_select_path(M, n1, n2, c != nullptr);
     if (path == TqPath::Fused)
-        return fused_for(n1, n2)(X, M, P1, P2, alpha, quantize ? Xq : nullptr, s_x,
+        return fused_for(n1, n2)(X, M, P1, P2, aq, quantize ? Xq : nullptr, s_x,
                                  quantize ? nullptr : Z, stream);
     if (path == TqPath::Cols)
-        return cols_for(n1, n2)->launch(X, M, P1, P2, alpha, Xq, s_x, quantize ? nullptr : Z, ws,
+        return cols_for(n1, n2)->launch(X, M, P1, P2, aq, Xq, s_x, quantize ? nullptr : Z, ws,
                                         stream);
     const int K = n1 * n2;
     char* p = static_cast<char*>(ws);
@@ -1098,7 +1204,7 @@ hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
     k_tq_stage2<<<dim3(M, ceil_div(K, kSplitThreads)), dim3(kSplitThreads), 0, stream>>>(
         T, K, n1, n2, P1, Zout, amax);
     if (quantize) {
-        k_tq_quant<<<dim3(M, ceil_div(K / 8, 256)), dim3(256), 0, stream>>>(Zw, K, alpha, amax, 1,
+        k_tq_quant<<<dim3(M, ceil_div(K / 8, 256)), dim3(256), 0, stream>>>(Zw, K, aq, amax, 1,
                                                                            Xq, s_x);
     }
     return hipGetLastError();

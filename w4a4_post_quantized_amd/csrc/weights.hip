@@ -6,6 +6,8 @@
 // diag(c) undone on the weights, clipping threshold α_w.
 // FRM-PTQ page, section 初步介绍: Q(W) = clamp(round(W/s) + z, 0, 2^b - 1),
 // and the page's group-wise (multi-granularity) weight quantization.
+// MergeQuant page, 关键设计 item 2: per-channel static activation steps are
+// folded into the weights of the linear layer (step migration).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -212,6 +214,27 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ Wt, int 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Step migration: Wm[n, k] = Wt[n, k] * steps[k].  One fp32 multiply is the
+// correctly rounded product, so the result is exactly fp32(Wt * step).
+// Grid-stride over 4-element chunks (K % 4 == 0); in place is allowed.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_migrate(const float* Wt, int K, size_t chunks,
+                                                 const float* __restrict__ steps, float* Wm) {
+    const int kc = K / 4;
+    for (size_t c = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+         c += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const int k4 = static_cast<int>(c % kc);
+        float4 w = reinterpret_cast<const float4*>(Wt)[c];
+        const float4 st = reinterpret_cast<const float4*>(steps)[k4];
+        w.x *= st.x;
+        w.y *= st.y;
+        w.z *= st.z;
+        w.w *= st.w;
+        reinterpret_cast<float4*>(Wm)[c] = w;
+    }
+}
+
 constexpr int kMergeBlocks = 256;
 
 }  // namespace
@@ -254,6 +277,16 @@ hipError_t merge_launch(const float* W, int N, int K, int n1, int n2, const floa
     const int blocks = N < kMergeBlocks ? N : kMergeBlocks;
     if (blocks > 0) k_merge<<<blocks, 256, 0, stream>>>(W, N, n1, n2, P1inv, P2invT, c, U, Wt);
     (void)K;
+    return hipGetLastError();
+}
+
+hipError_t migrate_steps_launch(const float* Wt, int N, int K, const float* steps, float* Wm,
+                                hipStream_t stream) {
+    const size_t chunks = static_cast<size_t>(N) * (K / 4);
+    if (chunks == 0) return hipSuccess;
+    const size_t want = (chunks + 255) / 256;
+    const int blocks = static_cast<int>(want < 8192 ? want : 8192);
+    k_migrate<<<blocks, 256, 0, stream>>>(Wt, K, chunks, steps, Wm);
     return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "make_activations", "make_factors",
-           "make_inputs", "random_invertible"]
+           "make_inputs", "random_invertible", "make_calibration_activations"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -164,3 +164,13 @@ def make_channel_scale(K: int, seed: int = 1) -> np.ndarray:
     """A positive per-channel vector c (fp32) for tests of the diag(c) option."""
     rng = np.random.default_rng(seed)
     return rng.uniform(0.25, 4.0, size=K).astype(np.float32)
+
+
+def make_calibration_activations(wl: Workload, M: int, outlier_channels, seed: int) -> np.ndarray:
+    """A calibration batch for static activation steps: ``M`` tokens drawn
+    like the workload's activations (same kind, the given outlier channels,
+    no pivot token) from ``numpy.random.default_rng(seed)``; fp16 [M, K]."""
+    cal = dataclasses.replace(wl, outlier_channels=tuple(int(c) for c in outlier_channels),
+                              outlier_frac=0.0, pivot_token_scale=0.0, seed=seed)
+    X, _ = make_activations(cal, np.random.default_rng(seed), M)
+    return X
