@@ -2,7 +2,7 @@
 """Benchmark of the W4A4 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qkv8b]
-                    [--act-quant dynamic|tensor|channel]
+                    [--act-quant dynamic|tensor|channel] [--path two|single]
 
 A step is one pass of the whole hot path over one batch: w4a4_linear =
 fused activation transform + per-token INT4 quantization + packing, then the
@@ -15,6 +15,10 @@ With --act-quant tensor|channel the activation steps are static (fixed
 offline from a seeded calibration batch, FPTQuant / MergeQuant): one step
 for the tensor, or one per channel migrated into the weights before packing;
 the step runs w4a4_linear_static instead.
+
+With --path single (decode, M <= 16) the step is one w4a4_linear_decode
+launch (transform, quantization and GEMM in one kernel) and the roofline
+kernel is that kernel, priced at the layer's algorithmic bytes.
 
 Prints ONE JSON line.  `value` is TOPS of the whole layer (2*M*N*K integer
 ops per step / step time).  `roofline` reports the dominant kernel (the GEMM)
@@ -50,6 +54,10 @@ def parse():
     ap.add_argument("--workload", default="qkv8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--path", choices=["two", "single"], default="two",
+                    help="'two' = w4a4_linear (transform kernel, then GEMM kernel; the faster "
+                         "path measured on MI355X); 'single' = w4a4_linear_decode (one launch, "
+                         "M <= 16 tokens)")
     ap.add_argument("--act-quant", choices=["dynamic", "tensor", "channel"], default="dynamic",
                     help="activation quantizer: per-token dynamic scales, or static steps "
                          "(one per tensor, or one per channel migrated into the weights)")
@@ -80,14 +88,21 @@ def gemm_bytes(wl, M):
     return b
 
 
-def traffic_from_profiles(kernel_tag, workload):
+def layer_bytes(wl, M):
+    """Algorithmic HBM bytes of the whole layer in one kernel: the GEMM's
+    operands and output plus the fp16 activations and the fp32 factors (the
+    packed activations stay in the workspace, written and read once)."""
+    return gemm_bytes(wl, M) + 2 * M * wl.K + 4 * (wl.n1 * wl.n1 + wl.n2 * wl.n2)
+
+
+def traffic_from_profiles(kernel_tag, workload, source="gemm.hip"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "w4a4_post_quantized_amd", "csrc", rec.get("source", "gemm.hip"))
+    src = os.path.join(ROOT, "w4a4_post_quantized_amd", "csrc", rec.get("source", source))
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if sha != rec.get("source_sha256"):
         return None
@@ -204,9 +219,31 @@ def main():
                         dtype=torch.uint8, device=dev)
     g_ws = torch.empty(max(1, L.gemm_workspace_bytes(M, desc)), dtype=torch.uint8, device=dev)
 
+    # single-kernel decode (one launch per layer), on request
+    single = False
+    sync = dws = None
+    if args.path == "single" and M <= 16:
+        sync = L.decode_sync_buffer(dev)
+        dws = torch.empty(max(1, L.linear_decode_workspace_bytes(M, wl.n1, wl.n2)),
+                          dtype=torch.uint8, device=dev)
+        _, Wq, sw, zw = packs[0]
+        L.linear_decode(X, P1, P2, desc, Wq, sw, zw, sync=sync, steps=steps, per_channel=pc,
+                        out=Y, ws=dws)
+        torch.cuda.synchronize()
+        single = True
+    elif args.path == "single":
+        raise SystemExit("--path single needs M <= 16")
+
+    def decode_call(i):
+        _, Wq, sw, zw = packs[i % copies]
+        L.linear_decode(X, P1, P2, desc, Wq, sw, zw, sync=sync, steps=steps, per_channel=pc,
+                        out=Y, ws=dws)
+
     def step(i):
         _, Wq, sw, zw = packs[i % copies]
-        if static:
+        if single:
+            decode_call(i)
+        elif static:
             L.linear_static(X, P1, P2, steps, pc, desc, Wq, sw, zw, out=Y, ws=ws)
         else:
             L.linear(X, P1, P2, desc, Wq, sw, zw, out=Y, ws=ws)
@@ -252,20 +289,46 @@ def main():
     torch.cuda.synchronize()
     gemm_us = e0.elapsed_time(e1) * 1e3 / args.steps
 
+    single_us = None
+    if single:
+        for i in range(args.warmup):
+            decode_call(i)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            decode_call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        single_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        if int(sync[L.DECODE_SYNC_ERROR_WORD].item()) != 0:
+            raise SystemExit("the single-kernel decode timed out waiting for its activations")
+
     ops = 2.0 * M * N * K
     value = ops / t_step / 1e12
-    if decode:
+    if single:
+        # the one kernel of the layer: weights, scales, activations in and out
+        gb = layer_bytes(wl, M)
+        achieved = gb / (single_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        roof["kernel"] = f"k_linear_dec<n1 {wl.n1}, 8 waves, depth 12>"
+        roof["kernel_us"] = round(single_us, 2)
+        roof["traffic"] = traffic_from_profiles("linear_dec", wl.name, "linear_decode.hip")
+    elif decode:
         gb = gemm_bytes(wl, M)
         achieved = gb / (gemm_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        roof["kernel"] = L.gemm_kernel_name(M, desc)
+        roof["kernel_us"] = round(gemm_us, 2)
+        roof["traffic"] = traffic_from_profiles("gemm", wl.name)
     else:
         achieved = ops / (gemm_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4)}
-    roof["kernel"] = L.gemm_kernel_name(M, desc)
-    roof["kernel_us"] = round(gemm_us, 2)
-    roof["traffic"] = traffic_from_profiles("gemm", wl.name)
+        roof["kernel"] = L.gemm_kernel_name(M, desc)
+        roof["kernel_us"] = round(gemm_us, 2)
+        roof["traffic"] = traffic_from_profiles("gemm", wl.name)
     roof["timing"] = "HIP events around back-to-back launches of the kernel, launch stream"
 
     out = {
@@ -279,8 +342,10 @@ def main():
                    "asymmetric_weights": wl.asymmetric, "weight_copies_rotated": copies,
                    "act_quant": args.act_quant},
         "us_per_layer": round(t_step * 1e6, 2),
+        "path": "single-kernel decode (w4a4_linear_decode)" if single else "two launches (w4a4_linear)",
         "transform_quant_us": round(tq_us, 2),
         "gemm_us": round(gemm_us, 2),
+        "single_kernel_us": None if single_us is None else round(single_us, 2),
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -247,6 +247,46 @@ int w4a4_linear_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                        const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Single-kernel decode layer                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of the sync buffer w4a4_linear_decode needs. */
+#define W4A4_DECODE_SYNC_BYTES 1024
+/* 32-bit word of the sync buffer that is non-zero once a call has timed out
+ * waiting for its activations (that call's Y is then invalid). */
+#define W4A4_DECODE_SYNC_ERROR_WORD 128
+
+/* Bytes of workspace w4a4_linear_decode needs (0 for M outside [1, 16]). */
+size_t w4a4_linear_decode_workspace_bytes(int32_t M, int32_t n1, int32_t n2);
+
+/* The whole layer for a few tokens in ONE kernel launch: the same result as
+ * w4a4_linear (steps == NULL) or w4a4_linear_static (steps != NULL), with
+ * the weight stream starting while the activations are transformed.
+ * FlatQuant page, section 高效 Kernel 设计 (transform and quantization fused
+ * with the layer); MergeQuant page, section 问题定义 (the per-token quantize
+ * and dequantize steps are a large share of autoregressive decoding).
+ *   Arguments as for w4a4_linear / w4a4_linear_static (no diag(c)); steps
+ *   NULL selects per-token dynamic scales with alpha_a, otherwise
+ *   per_channel selects the static form (alpha_a is then ignored).
+ *   sync: device buffer of W4A4_DECODE_SYNC_BYTES, zero-filled by the caller
+ *   once before its first use; every call leaves it valid for the next (its
+ *   counters carry a tag unique to each call).  Calls that share a sync
+ *   buffer or a workspace must not run concurrently.
+ *   ws: device workspace of w4a4_linear_decode_workspace_bytes(M, n1, n2)
+ *   bytes.
+ * Supported: 1 <= M <= 16, n2 = 128, n1 in {64, 224}, the activation rows
+ * and the scale table of 16 weight rows within one CU's LDS, and no more
+ * transform workgroups (M * n1 / 16) than the device holds at once;
+ * otherwise W4A4_ERR_UNSUPPORTED and nothing runs (use w4a4_linear).  A
+ * wait inside the kernel is bounded (20 ms); if it runs out, word
+ * W4A4_DECODE_SYNC_ERROR_WORD of sync becomes non-zero. */
+int w4a4_linear_decode(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                       const float* P1, const float* P2, float alpha_a, const float* steps,
+                       int32_t per_channel, const w4a4_weight_desc* desc, const uint8_t* Wq,
+                       const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y, void* ws,
+                       size_t ws_bytes, uint32_t* sync, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

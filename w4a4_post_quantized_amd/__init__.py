@@ -19,6 +19,8 @@ __all__ = [
     "gemm_i32", "gemm_kernel_name", "linear", "merge_workspace_bytes", "transform_quant_workspace_bytes",
     "gemm_workspace_bytes", "linear_workspace_bytes", "version",
     "migrate_steps", "transform_quant_static", "linear_static",
+    "linear_decode", "linear_decode_workspace_bytes", "decode_sync_buffer",
+    "DECODE_SYNC_BYTES", "DECODE_SYNC_ERROR_WORD",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so")
@@ -32,7 +34,11 @@ EXPORTED_SYMBOLS = [
     "w4a4_transform",
     "w4a4_gemm_workspace_bytes", "w4a4_gemm", "w4a4_gemm_i32", "w4a4_gemm_kernel_name",
     "w4a4_linear_workspace_bytes", "w4a4_linear", "w4a4_linear_static",
+    "w4a4_linear_decode_workspace_bytes", "w4a4_linear_decode",
 ]
+
+DECODE_SYNC_BYTES = 1024          # W4A4_DECODE_SYNC_BYTES
+DECODE_SYNC_ERROR_WORD = 128      # W4A4_DECODE_SYNC_ERROR_WORD
 
 
 class W4A4Error(RuntimeError):
@@ -88,6 +94,9 @@ def lib() -> ctypes.CDLL:
                                                            vp, sz, vp]),
             "w4a4_linear_static": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, i32, dp, vp, vp, vp,
                                                   vp, vp, sz, vp]),
+            "w4a4_linear_decode_workspace_bytes": (sz, [i32, i32, i32]),
+            "w4a4_linear_decode": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, f32, vp, i32, dp, vp, vp,
+                                                  vp, vp, vp, sz, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -341,4 +350,35 @@ def linear_static(X, P1, P2, steps, per_channel: bool, desc: WeightDesc, Wq, s_w
                                     int(bool(per_channel)), ctypes.byref(desc), _p(Wq), _p(s_w),
                                     _p(z_w), _p(Y), _p(ws), nb if ws is None else ws.numel(),
                                     _stream(stream)), "w4a4_linear_static")
+    return Y
+
+
+def linear_decode_workspace_bytes(M: int, n1: int, n2: int) -> int:
+    return lib().w4a4_linear_decode_workspace_bytes(M, n1, n2)
+
+
+def decode_sync_buffer(device):
+    """A zero-filled sync buffer for linear_decode (reuse it across calls)."""
+    torch = _torch()
+    return torch.zeros(DECODE_SYNC_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def linear_decode(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, sync=None, alpha_a: float = 1.0,
+                  steps=None, per_channel: bool = False, out=None, ws=None, stream=None):
+    """The whole layer for M <= 16 tokens in one kernel launch: Y [M, N] fp16."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    _need(X, torch.float16, (M, K), "X")
+    if steps is not None:
+        _need(steps, torch.float32, (K if per_channel else 1,), "steps")
+    if sync is None:
+        raise ValueError("linear_decode needs a sync buffer (decode_sync_buffer)")
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=X.device)
+    nb = linear_decode_workspace_bytes(M, n1, n2)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_linear_decode(_p(X), M, n1, n2, _p(P1), _p(P2), float(alpha_a), _p(steps),
+                                    int(bool(per_channel)), ctypes.byref(desc), _p(Wq), _p(s_w),
+                                    _p(z_w), _p(Y), _p(ws), nb if ws is None else ws.numel(),
+                                    _p(sync), _stream(stream)), "w4a4_linear_decode")
     return Y

@@ -31,7 +31,7 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 
-SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "weights.hip"]
+SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "weights.hip", "linear_decode.hip"]
 
 
 def _compile(src: str, extra=()):

@@ -397,4 +397,66 @@ int w4a4_linear_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, con
                          desc, Wq, s_w, z_w, Y, ws, ws_bytes, stream, "w4a4_linear_static");
 }
 
+// ---------------------------------------------------------------------------
+size_t w4a4_linear_decode_workspace_bytes(int32_t M, int32_t n1, int32_t n2) {
+    if (M < 1 || M > 16 || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR || n2 > W4A4_MAX_FACTOR)
+        return 0;
+    return w4a4::linear_decode_workspace_bytes(M, n1, n2);
+}
+
+int w4a4_linear_decode(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                       const float* P2, float alpha_a, const float* steps, int32_t per_channel,
+                       const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                       const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes,
+                       uint32_t* sync, void* stream) {
+    if (int s = check_desc(desc, true)) return s;
+    if (int s = check_factors(M, n1, n2)) return s;
+    REQUIRE(desc->K == n1 * n2, W4A4_ERR_INVALID_ARG, "desc->K = %d != n1*n2 = %d", desc->K,
+            n1 * n2);
+    REQUIRE(per_channel == 0 || per_channel == 1, W4A4_ERR_INVALID_ARG,
+            "per_channel = %d must be 0 or 1", per_channel);
+    if (steps == nullptr)
+        REQUIRE(alpha_a > 0.0f && alpha_a <= 1.0f, W4A4_ERR_INVALID_ARG,
+                "alpha_a = %g must lie in (0, 1]", static_cast<double>(alpha_a));
+    if (M == 0) return ok();
+    REQUIRE(M <= 16, W4A4_ERR_UNSUPPORTED, "M = %d: the single-kernel decode takes at most 16 tokens", M);
+    REQUIRE_PTR(X);
+    REQUIRE_PTR(P1);
+    REQUIRE_PTR(P2);
+    REQUIRE_PTR(Wq);
+    REQUIRE_PTR(s_w);
+    REQUIRE_PTR(Y);
+    REQUIRE_PTR(ws);
+    REQUIRE_PTR(sync);
+    if (desc->asymmetric) REQUIRE_PTR(z_w);
+    REQUIRE_ALIGNED(X);
+    REQUIRE_ALIGNED(P1);
+    REQUIRE_ALIGNED(P2);
+    if (steps) REQUIRE_ALIGNED(steps);
+    REQUIRE_ALIGNED(Wq);
+    REQUIRE_ALIGNED(s_w);
+    if (desc->asymmetric) REQUIRE_ALIGNED(z_w);
+    REQUIRE_ALIGNED(Y);
+    REQUIRE_ALIGNED(ws);
+    REQUIRE_ALIGNED(sync);
+    int cap = 0;
+    const int chk = w4a4::linear_decode_check(M, n1, n2, desc->N, desc->K, desc->group_size,
+                                              desc->asymmetric != 0, &cap);
+    REQUIRE(chk != 1, W4A4_ERR_UNSUPPORTED,
+            "factors (%d, %d) have no single-kernel decode (n2 = 128, n1 in {64, 224})", n1, n2);
+    REQUIRE(chk != 2, W4A4_ERR_UNSUPPORTED, "M = %d tokens of K = %d do not fit the LDS", M,
+            desc->K);
+    REQUIRE(chk != 3, W4A4_ERR_UNSUPPORTED,
+            "the %d transform workgroups exceed the device's resident capacity (%d)",
+            M * (n1 / 16), cap);
+    const size_t need = w4a4::linear_decode_workspace_bytes(M, n1, n2);
+    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    w4a4::GemmArgs g{nullptr, nullptr, Wq, s_w, z_w, Y, nullptr, M, desc->N, desc->K,
+                     desc->group_size, desc->asymmetric != 0};
+    hipError_t e = w4a4::linear_decode_launch(
+        X, M, n1, n2, P1, P2, w4a4::ActQuant{alpha_a, steps, per_channel != 0}, g, ws, sync,
+        static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_linear_decode");
+}
+
 }  // extern "C"

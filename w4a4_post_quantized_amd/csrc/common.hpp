@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "w4a4.h"
 
 namespace w4a4 {
@@ -140,6 +142,50 @@ __device__ __forceinline__ uint32_t quant_nibble(float z, float inv_s, bool zero
 __device__ __forceinline__ uint32_t quant_nibble_magic(float z, float inv_s) {
     const float t = __builtin_amdgcn_fmed3f(z * inv_s, -8.0f, 7.0f);
     return __float_as_uint(t + 12582912.0f) & 0xFu;
+}
+
+// floor(log2(x)) for a positive normal float
+__device__ __forceinline__ int ilog2f(float x) {
+    return static_cast<int>((__float_as_uint(x) >> 23) & 0xFFu) - 127;
+}
+
+// ---------------------------------------------------------------------------
+// Packed 4-bit codes -> int8 MFMA operands
+// ---------------------------------------------------------------------------
+// signed nibbles -> 16*q bytes; even codes in `ev`, odd codes in `od`
+__device__ __forceinline__ void unpack_signed16(const uint4& w, uint4& ev, uint4& od) {
+    ev.x = (w.x << 4) & 0xF0F0F0F0u;
+    ev.y = (w.y << 4) & 0xF0F0F0F0u;
+    ev.z = (w.z << 4) & 0xF0F0F0F0u;
+    ev.w = (w.w << 4) & 0xF0F0F0F0u;
+    od.x = w.x & 0xF0F0F0F0u;
+    od.y = w.y & 0xF0F0F0F0u;
+    od.z = w.z & 0xF0F0F0F0u;
+    od.w = w.w & 0xF0F0F0F0u;
+}
+
+// unsigned nibbles u, zero point z -> bytes (u - z) as int8
+__device__ __forceinline__ uint32_t usub(uint32_t u4, uint32_t bias) {
+    return (u4 + bias) ^ 0x80808080u;
+}
+__device__ __forceinline__ void unpack_asym(const uint4& w, uint32_t bias, uint4& ev, uint4& od) {
+    ev.x = usub(w.x & 0x0F0F0F0Fu, bias);
+    ev.y = usub(w.y & 0x0F0F0F0Fu, bias);
+    ev.z = usub(w.z & 0x0F0F0F0Fu, bias);
+    ev.w = usub(w.w & 0x0F0F0F0Fu, bias);
+    od.x = usub((w.x >> 4) & 0x0F0F0F0Fu, bias);
+    od.y = usub((w.y >> 4) & 0x0F0F0F0Fu, bias);
+    od.z = usub((w.z >> 4) & 0x0F0F0F0Fu, bias);
+    od.w = usub((w.w >> 4) & 0x0F0F0F0Fu, bias);
+}
+
+// calls f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }

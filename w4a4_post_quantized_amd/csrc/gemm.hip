@@ -54,43 +54,7 @@ constexpr int ROWB = BK;         // int8 bytes per LDS row
 // kModeI32: exact int32 D per group.
 enum Mode { kModeChan = 0, kModeGroup = 1, kModeI32 = 2 };
 
-// calls f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
-// signed nibbles -> 16*q bytes; even codes in `ev`, odd codes in `od`
-__device__ __forceinline__ void unpack_signed16(const uint4& w, uint4& ev, uint4& od) {
-    ev.x = (w.x << 4) & 0xF0F0F0F0u;
-    ev.y = (w.y << 4) & 0xF0F0F0F0u;
-    ev.z = (w.z << 4) & 0xF0F0F0F0u;
-    ev.w = (w.w << 4) & 0xF0F0F0F0u;
-    od.x = w.x & 0xF0F0F0F0u;
-    od.y = w.y & 0xF0F0F0F0u;
-    od.z = w.z & 0xF0F0F0F0u;
-    od.w = w.w & 0xF0F0F0F0u;
-}
-
-// unsigned nibbles u, zero point z -> bytes (u - z) as int8
-__device__ __forceinline__ uint32_t usub(uint32_t u4, uint32_t bias) {
-    return (u4 + bias) ^ 0x80808080u;
-}
-__device__ __forceinline__ void unpack_asym(const uint4& w, uint32_t bias, uint4& ev, uint4& od) {
-    ev.x = usub(w.x & 0x0F0F0F0Fu, bias);
-    ev.y = usub(w.y & 0x0F0F0F0Fu, bias);
-    ev.z = usub(w.z & 0x0F0F0F0Fu, bias);
-    ev.w = usub(w.w & 0x0F0F0F0Fu, bias);
-    od.x = usub((w.x >> 4) & 0x0F0F0F0Fu, bias);
-    od.y = usub((w.y >> 4) & 0x0F0F0F0Fu, bias);
-    od.z = usub((w.z >> 4) & 0x0F0F0F0Fu, bias);
-    od.w = usub((w.w >> 4) & 0x0F0F0F0Fu, bias);
-}
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool ASYM, int MODE, bool G1 = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(

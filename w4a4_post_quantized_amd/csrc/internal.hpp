@@ -50,6 +50,16 @@ const char* gemm_kernel_name(const GemmArgs& a, bool i32_out);
 hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+// ---- single-kernel decode layer (linear_decode.hip) --------------------------
+size_t linear_decode_workspace_bytes(int M, int n1, int n2);
+// 0: supported; 1: shape not covered; 2: too much LDS; 3: the producers
+// exceed the device's resident capacity
+int linear_decode_check(int M, int n1, int n2, int N, int K, int group_size, bool asym,
+                        int* cap);
+hipError_t linear_decode_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
+                                const float* P2, ActQuant aq, const GemmArgs& g, void* ws,
+                                uint32_t* sync, hipStream_t stream);
+
 // ---- offline weight preparation (weights.hip) ------------------------------
 size_t merge_workspace_bytes(int n1, int n2, int K);
 // returns hipSuccess and sets *singular when a factor has no usable pivot

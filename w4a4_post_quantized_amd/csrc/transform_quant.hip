@@ -164,11 +164,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t steps_rsrc(const float* steps,
 // Fused MFMA path
 // ===========================================================================
 
-// floor(log2(x)) for a positive normal float
-__device__ __forceinline__ int ilog2f(float x) {
-    return static_cast<int>((__float_as_uint(x) >> 23) & 0xFFu) - 127;
-}
-
 template <int N1, int N2>
 struct FusedCfg {
     static_assert(N1 % 16 == 0 && N2 % 16 == 0, "factors must be multiples of 16");
