@@ -179,3 +179,28 @@ def test_static_entry_points_validation():
     assert lin(n1=8) == -1                            # desc K != n1*n2
     assert lin(wsb=nb - 1) == -4
     assert lin(st=MISALIGNED) == -3
+
+
+def test_linear_decode_validation():
+    L = W.lib()
+    d = desc(N=256, K=28672, g=128, asym=1)
+    nb = L.w4a4_linear_decode_workspace_bytes(1, 224, 128)
+    assert nb >= 28672 // 2 + 4
+    assert L.w4a4_linear_decode_workspace_bytes(0, 224, 128) == 0
+    assert L.w4a4_linear_decode_workspace_bytes(17, 224, 128) == 0
+
+    def call(M=1, n1=224, sync=FAKE, pc=0, zw=FAKE, d=d, alpha=1.0):
+        return L.w4a4_linear_decode(FAKE, M, n1, 128, FAKE, FAKE, alpha, None, pc, d, FAKE, FAKE,
+                                    zw, FAKE, FAKE, nb, sync, None)
+
+    assert call(sync=None) == -1 and "sync" in last()
+    assert call(pc=3) == -1
+    assert call(alpha=0.0) == -1
+    assert call(n1=112) == -1                          # desc K != n1*n2
+    assert call(zw=None) == -1                         # asymmetric weights need z_w
+    assert call(M=17) == -2 and "16 tokens" in last()
+    assert call(sync=MISALIGNED) == -3
+    assert call(M=0) == 0                              # empty: nothing to do
+    hdr = open(os.path.join(ROOT, "include", "w4a4.h")).read()
+    assert f"#define W4A4_DECODE_SYNC_BYTES {W.DECODE_SYNC_BYTES}" in hdr
+    assert f"#define W4A4_DECODE_SYNC_ERROR_WORD {W.DECODE_SYNC_ERROR_WORD}" in hdr
