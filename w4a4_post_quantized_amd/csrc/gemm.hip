@@ -935,6 +935,7 @@ template <int MODE> hipError_t dl256x128_4x2_s4(const GemmArgs& a, hipStream_t s
 template <int MODE> hipError_t dl128x128_2x2_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl128x128_2x2_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 3, MODE>(a, s); }
 template <int MODE> hipError_t dl128x256_2x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 256, 2, 4, 3, MODE>(a, s); }
+template <int MODE> hipError_t dl256x256_4x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 4, 4, 3, MODE>(a, s); }
 
 
 template <int MODE> hipError_t r16_256x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 128, 2, 4, MODE>(a, s); }
@@ -951,6 +952,7 @@ const KernelCfg kTiles[] = {
     W4A4_CFG("k_gemm_dl<128x128, waves 2x2, 3 stages>", dl128x128_2x2_s3),
     W4A4_CFG("k_gemm_w4a4<256x128, waves 2x4>", r16_256x128_2x4),
     W4A4_CFG_CHAN("k_gemm_dl<128x256, waves 2x4, 3 stages>", dl128x256_2x4_s3),
+    W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 4x4, 3 stages>", dl256x256_4x4_s3),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -1008,15 +1010,18 @@ const KernelCfg& choose(const GemmArgs& a) {
     }
     int t = env_index("W4A4_GEMM_TILE", kNumTiles);
     if (t < 0 || (grouped && kTiles[t].group == nullptr)) {
-        // measured on MI355X: direct-to-LDS 256x256 tiles when the grid
-        // covers the CUs several times over, direct-to-LDS 128x128 tiles for
-        // about one wave of 256x256 tiles, 16x16x64 128x128 (8 waves) for the
-        // per-group mode
+        // measured on MI355X: direct-to-LDS 256x256 tiles (8 waves) when the
+        // grid covers the CUs several times over, 256x256 tiles with 16 waves
+        // for about one wave of tiles (2048x6144: 57 against 60 us for
+        // 128x128 tiles), direct-to-LDS 128x128 tiles below that, 16x16x64
+        // 128x128 (8 waves) for the per-group mode
         const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
         if (grouped)
             t = 2;
         else if (tiles256 >= 2L * cus)
             t = 0;
+        else if (2L * tiles256 >= cus)
+            t = 8;
         else
             t = 1;
     }
