@@ -139,23 +139,58 @@ def cpu_baseline(wl, inp, budget_s, act_quant="dynamic"):
             Wt = O.migrate_steps(Wt, steps)
     wq = O.quantize_weights(Wt, wl.group_size, wl.asymmetric)
     del Wt
-    times = []
+    # one pass = the oracle's steps in order: transform + quantize + pack
+    # (O1-O4), then the exact integer GEMM and the epilogue (O6-O7)
+    t_act, t_gemm = [], []
     t_end = time.perf_counter() + budget_s
     while True:
         t0 = time.perf_counter()
         if static:
-            O.linear_static(inp["X"], inp["P1"], inp["P2"], wq, steps, pc, c=inp["c"])
+            act = O.transform_quant_static(inp["X"], inp["P1"], inp["P2"], steps, pc, c=inp["c"])
         else:
-            O.linear(inp["X"], inp["P1"], inp["P2"], wq, c=inp["c"])
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() >= t_end:
+            act = O.transform_quant(inp["X"], inp["P1"], inp["P2"], inp["c"])
+        t1 = time.perf_counter()
+        D = O.int_gemm(act["q"], wq["codes"], wq["z"], wq["group_size"])
+        O.epilogue(D, act["s_x"], wq["s"])
+        t2 = time.perf_counter()
+        t_act.append(t1 - t0)
+        t_gemm.append(t2 - t1)
+        del act, D
+        if t2 >= t_end:
             break
-    t = float(np.median(times))
+    ta, tg = float(np.median(t_act)), float(np.median(t_gemm))
+    t = ta + tg
     ops = 2.0 * wl.M * wl.N * wl.K
     return {"value": ops / t / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"whole {wl.name} layer ({wl.M}x{wl.K}->{wl.N}), {len(times)} passes, "
+            "cpu": cpu_model(),
+            "sample": f"whole {wl.name} layer ({wl.M}x{wl.K}->{wl.N}), {len(t_act)} passes, "
                       f"median {t * 1e3:.1f} ms/pass, weights prepared untimed",
-            "us_per_layer": t * 1e6}
+            "us_per_layer": t * 1e6, "transform_quant_us": ta * 1e6, "gemm_epilogue_us": tg * 1e6}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def event_stats(launch, n):
+    """Per-launch durations (HIP events around each launch on the launch
+    stream): median, p10 and p90 in microseconds."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"median": round(float(np.median(d)), 2), "p10": round(float(np.percentile(d, 10)), 2),
+            "p90": round(float(np.percentile(d, 90)), 2), "launches": n}
 
 
 def main():
@@ -303,8 +338,21 @@ def main():
         if int(sync[L.DECODE_SYNC_ERROR_WORD].item()) != 0:
             raise SystemExit("the single-kernel decode timed out waiting for its activations")
 
+    def gemm_call(i):
+        _, Wq, sw, zw = packs[i % copies]
+        L.gemm(Xq, sx, desc, Wq, sw, zw, out=Y, ws=g_ws)
+
+    dist = event_stats(decode_call if single else gemm_call, max(20, args.steps))
+
     ops = 2.0 * M * N * K
     value = ops / t_step / 1e12
+    tq_bytes = 2 * M * K + M * K // 2 + 4 * M + 4 * (wl.n1 * wl.n1 + wl.n2 * wl.n2)
+    tq_flops = 2.0 * M * K * (wl.n1 + wl.n2)
+    transform = {"us": round(tq_us, 2), "bytes": tq_bytes, "flops": tq_flops,
+                 "achieved_GBps": round(tq_bytes / (tq_us * 1e-6) / 1e9, 1),
+                 "achieved_GFLOPps": round(tq_flops / (tq_us * 1e-6) / 1e9, 1),
+                 "t_at_hbm_us": round(tq_bytes / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
+                 "t_at_fp32_vector_us": round(tq_flops / 157.3e12 * 1e6, 2)}
     if single:
         # the one kernel of the layer: weights, scales, activations in and out
         gb = layer_bytes(wl, M)
@@ -329,7 +377,9 @@ def main():
         roof["kernel"] = L.gemm_kernel_name(M, desc)
         roof["kernel_us"] = round(gemm_us, 2)
         roof["traffic"] = traffic_from_profiles("gemm", wl.name)
-    roof["timing"] = "HIP events around back-to-back launches of the kernel, launch stream"
+    roof["timing"] = ("mean over HIP events around back-to-back launches on the launch stream; "
+                      "per_launch_us from events around each launch")
+    roof["per_launch_us"] = dist
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
@@ -344,6 +394,7 @@ def main():
         "us_per_layer": round(t_step * 1e6, 2),
         "path": "single-kernel decode (w4a4_linear_decode)" if single else "two launches (w4a4_linear)",
         "transform_quant_us": round(tq_us, 2),
+        "transform_quant": transform,
         "gemm_us": round(gemm_us, 2),
         "single_kernel_us": None if single_us is None else round(single_us, 2),
         "roofline": roof,
