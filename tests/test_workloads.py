@@ -48,3 +48,21 @@ def test_activation_shapes_medium(name):
 def test_all_workloads_consistent():
     for wl in WL.WORKLOADS.values():
         assert wl.n1 * wl.n2 == wl.K and wl.K % wl.group_size == 0
+
+
+def test_kv_workloads_deterministic_and_shaped():
+    from workloads import kv as WKV
+    wl = WKV.get_kv("kv_tiny")
+    a = WKV.make_kv_static(wl)
+    b = WKV.make_kv_static(wl)
+    for key in ("lengths", "outliers", "P_h", "P_v", "q"):
+        np.testing.assert_array_equal(a[key], b[key])
+    assert a["lengths"][0] == wl.max_seq
+    assert ((a["lengths"] >= wl.min_len) & (a["lengths"] <= wl.max_seq)).all()
+    assert a["q"].shape == (wl.batch, wl.heads_q, wl.head_dim) and a["q"].dtype == np.float16
+    k, v = WKV.make_history(wl, 1, 17, a["outliers"])
+    k2, _ = WKV.make_history(wl, 1, 17, a["outliers"])
+    np.testing.assert_array_equal(k, k2)
+    assert k.shape == (17, wl.heads_kv, wl.head_dim) and v.dtype == np.float16
+    for w in WKV.KV_WORKLOADS.values():
+        assert w.max_seq % 32 == 0 and w.heads_q % w.heads_kv == 0
