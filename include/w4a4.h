@@ -287,6 +287,95 @@ int w4a4_linear_decode(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                        const uint16_t* s_w, const uint16_t* z_w, uint16_t* Y, void* ws,
                        size_t ws_bytes, uint32_t* sync, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* INT4 KV cache with per-head transforms, and decode attention over it      */
+/* ------------------------------------------------------------------------ */
+/* FlatQuant page, section Transformer 集成: the key cache and the value cache
+ * each carry a transform applied per head, P_h and P_v (full d x d matrices,
+ * not Kronecker-factored).  The caches hold Q(k·P_h) and Q(v·P_v); the query
+ * takes P_h^-T so that (q·P_h^-T)·(k·P_h)^T = q·k^T (section 核心思想: the
+ * inverse goes on the other operand), and P_v^-1 belongs to the output
+ * projection's weights, so the attention output is in the P_v basis.
+ * FPTQuant page, sections 核心贡献 and 实验结果: the KV cache in INT4
+ * (W4A4KV4).  Quantizer: the activations' symmetric one per head vector of
+ * each token, s = alpha * max|z| / 7 (fp32), codes clamp(rne(z / s), -8, 7).
+ *
+ * Cache layout of one layer (head size d = 128, the only size supported):
+ *   k_cache  uint8  [batch][heads_kv][max_seq][64]: the key codes of a token
+ *            and head, two per byte, low nibble = even channel;
+ *   v_cache  uint32 [batch][heads_kv][max_seq / 8][128]: nibble j (bits
+ *            4j..4j+3) of word [blk][ch] is the value code of token 8*blk + j,
+ *            channel ch;
+ *   k_scale, v_scale  float [batch][heads_kv][max_seq]: the scales.
+ * Codes are two's-complement nibbles.  max_seq must be a positive multiple
+ * of 32.  P matrices are float [d][d] row-major (shared by the heads) or
+ * [heads_kv][d][d] (per_head = 1). */
+#define W4A4_KV_HEAD_DIM 128
+
+/* Bytes of the three cache buffers of one layer (any pointer may be NULL).
+ * Returns W4A4_OK or W4A4_ERR_INVALID_ARG / W4A4_ERR_UNSUPPORTED. */
+int w4a4_kv_cache_bytes(int32_t batch, int32_t heads_kv, int32_t head_dim, int32_t max_seq,
+                        size_t* k_bytes, size_t* v_bytes, size_t* scale_bytes);
+
+/* Bytes of workspace w4a4_kv_query_factor needs for count matrices. */
+size_t w4a4_kv_query_factor_workspace_bytes(int32_t head_dim, int32_t count);
+
+/* Offline: P_h_inv_t[i] = (P_h[i])^-T for count matrices of d x d (float,
+ * computed in float64 by Gauss-Jordan elimination with partial pivoting and
+ * rounded once).  Synchronizes the stream.  A singular matrix returns
+ * W4A4_ERR_INVALID_ARG (the output is then undefined). */
+int w4a4_kv_query_factor(const float* P_h, int32_t head_dim, int32_t count, float* P_h_inv_t,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Transform, quantize and write new tokens into the caches.
+ *   k, v: fp16 [tokens][heads_kv][d], post-RoPE keys and values.
+ *   Segment i (0 <= i < segments) is tokens cu_tokens[i] .. cu_tokens[i+1]-1
+ *   of k and v; they go to sequence seg_seq[i] at positions seg_start[i],
+ *   seg_start[i]+1, ...  seg_seq, seg_start: int32 [segments] and cu_tokens:
+ *   int32 [segments + 1], DEVICE arrays, cu_tokens non-decreasing.
+ *   A segment whose sequence is outside [0, batch), whose start is outside
+ *   [0, max_seq) or whose token range is outside [0, tokens] is skipped;
+ *   positions past max_seq are dropped.  Every (sequence, position) may
+ *   appear at most once per call.
+ *   P_h, P_v, per_head: the per-head transforms; alpha_k, alpha_v in (0, 1]
+ *   the clipping ratios.  Positions not written keep their contents (value
+ *   words shared with other positions are merged).
+ * Decode (one token per sequence) and prefill (long segments) use the same
+ * call.  Host-checked: d = 128, heads_kv >= 1, batch >= 0, tokens >= 0,
+ * segments >= 0, max_seq a positive multiple of 32, alignment. */
+int w4a4_kv_append(const uint16_t* k, const uint16_t* v, int32_t tokens, const int32_t* seg_seq,
+                   const int32_t* seg_start, const int32_t* cu_tokens, int32_t segments,
+                   int32_t heads_kv, int32_t head_dim, const float* P_h, const float* P_v,
+                   int32_t per_head, float alpha_k, float alpha_v, uint8_t* k_cache,
+                   float* k_scale, uint32_t* v_cache, float* v_scale, int32_t batch,
+                   int32_t max_seq, void* stream);
+
+/* Bytes of workspace w4a4_attn_decode needs (0 for invalid shapes). */
+size_t w4a4_attn_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                        int32_t head_dim, int32_t max_seq);
+
+/* Decode attention over the INT4 caches, one query token per sequence:
+ *   out[b][h] = softmax(sm_scale * q~[b][h] · K^[b][h/G][:L]^T) · V^[b][h/G][:L]
+ * with q~ = q · P_h^-T, K^ and V^ the dequantized cache contents
+ * (scale * code), L = lengths[b] clamped to [0, max_seq] and G =
+ * heads_q / heads_kv.  An empty context (L = 0) gives zeros.  The output
+ * stays in the P_v basis.
+ *   q: fp16 [batch][heads_q][d], post-RoPE queries.
+ *   P_h_inv_t: float [d][d] or [heads_kv][d][d] (per_head = 1), from
+ *   w4a4_kv_query_factor.
+ *   lengths: int32 [batch], DEVICE array.
+ *   out: fp16 [batch][heads_q][d].
+ *   ws: w4a4_attn_decode_workspace_bytes(...) bytes.
+ * Host-checked: d = 128, heads_q a multiple of heads_kv with G <= 16,
+ * batch >= 0, max_seq a positive multiple of 32, sm_scale finite and > 0,
+ * alignment.  Three kernel launches (query transform, chunked partial
+ * attention, merge). */
+int w4a4_attn_decode(const uint16_t* q, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                     int32_t head_dim, const float* P_h_inv_t, int32_t per_head,
+                     const uint8_t* k_cache, const float* k_scale, const uint32_t* v_cache,
+                     const float* v_scale, const int32_t* lengths, int32_t max_seq,
+                     float sm_scale, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

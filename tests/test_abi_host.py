@@ -204,3 +204,74 @@ def test_linear_decode_validation():
     hdr = open(os.path.join(ROOT, "include", "w4a4.h")).read()
     assert f"#define W4A4_DECODE_SYNC_BYTES {W.DECODE_SYNC_BYTES}" in hdr
     assert f"#define W4A4_DECODE_SYNC_ERROR_WORD {W.DECODE_SYNC_ERROR_WORD}" in hdr
+
+
+def test_kv_cache_bytes_and_workspaces():
+    L = W.lib()
+    assert W.kv_cache_bytes(2, 8, 64) == (2 * 8 * 64 * 64, 2 * 8 * 64 * 64, 2 * 8 * 64 * 4)
+    k = ctypes.c_size_t()
+    assert L.w4a4_kv_cache_bytes(2, 8, 64, 48, ctypes.byref(k), None, None) == -2   # max_seq % 32
+    assert L.w4a4_kv_cache_bytes(2, 8, 96, 64, ctypes.byref(k), None, None) == -2   # head size
+    assert L.w4a4_kv_cache_bytes(-1, 8, 128, 64, None, None, None) == -1
+    assert L.w4a4_kv_cache_bytes(2, 0, 128, 64, None, None, None) == -1
+    assert L.w4a4_kv_query_factor_workspace_bytes(128, 1) >= 2 * 128 * 128 * 8
+    assert L.w4a4_kv_query_factor_workspace_bytes(64, 1) == 0
+    assert L.w4a4_attn_decode_workspace_bytes(4, 32, 8, 128, 1024) >= 4 * 32 * 128 * 4
+    assert L.w4a4_attn_decode_workspace_bytes(4, 30, 8, 128, 1024) == 0    # heads_q % heads_kv
+    assert L.w4a4_attn_decode_workspace_bytes(4, 136, 8, 128, 1024) == 0   # G = 17
+    hdr = open(os.path.join(ROOT, "include", "w4a4.h")).read()
+    assert f"#define W4A4_KV_HEAD_DIM {W.KV_HEAD_DIM}" in hdr
+
+
+def test_kv_append_validation():
+    L = W.lib()
+
+    def call(T=4, S=2, H=8, d=128, ph=0, ak=1.0, av=1.0, B=2, ms=64, k=FAKE, kc=FAKE, vs=FAKE):
+        return L.w4a4_kv_append(k, FAKE, T, FAKE, FAKE, FAKE, S, H, d, FAKE, FAKE, ph, ak, av,
+                                kc, FAKE, FAKE, vs, B, ms, None)
+
+    assert call(d=64) == -2 and "head_dim" in last()
+    assert call(ms=40) == -2
+    assert call(H=0) == -1
+    assert call(T=-1) == -1
+    assert call(S=-1) == -1
+    assert call(ph=2) == -1
+    assert call(ak=0.0) == -1 and "alpha" in last()
+    assert call(av=1.5) == -1
+    assert call(k=None) == -1 and "k is NULL" in last()
+    assert call(kc=MISALIGNED) == -3
+    assert call(vs=None) == -1
+    assert call(T=0) == 0 and call(S=0) == 0 and call(B=0) == 0    # nothing to write
+
+
+def test_attn_decode_validation():
+    L = W.lib()
+    nb = L.w4a4_attn_decode_workspace_bytes(2, 8, 2, 128, 64)
+
+    def call(B=2, Hq=8, Hkv=2, d=128, ph=0, ms=64, sm=0.08, ws=FAKE, wsb=nb, out=FAKE, ln=FAKE):
+        return L.w4a4_attn_decode(FAKE, B, Hq, Hkv, d, FAKE, ph, FAKE, FAKE, FAKE, FAKE, ln, ms, sm,
+                                  out, ws, wsb, None)
+
+    assert call(Hq=9) == -1 and "multiple" in last()
+    assert call(Hq=34) == -2                                   # G = 17
+    assert call(d=256) == -2
+    assert call(ms=0) == -2
+    assert call(sm=0.0) == -1 and "sm_scale" in last()
+    assert call(sm=float("inf")) == -1
+    assert call(sm=float("nan")) == -1
+    assert call(ph=5) == -1
+    assert call(ln=None) == -1 and "lengths" in last()
+    assert call(out=MISALIGNED) == -3
+    assert call(wsb=nb - 1) == -4
+    assert call(ws=None) == -1
+    assert call(B=0) == 0
+
+
+def test_kv_query_factor_validation():
+    L = W.lib()
+    nb = L.w4a4_kv_query_factor_workspace_bytes(128, 2)
+    assert L.w4a4_kv_query_factor(FAKE, 128, 2, FAKE, FAKE, nb - 1, None) == -4
+    assert L.w4a4_kv_query_factor(FAKE, 64, 2, FAKE, FAKE, nb, None) == -2
+    assert L.w4a4_kv_query_factor(FAKE, 128, 0, FAKE, FAKE, nb, None) == -1
+    assert L.w4a4_kv_query_factor(None, 128, 2, FAKE, FAKE, nb, None) == -1
+    assert L.w4a4_kv_query_factor(MISALIGNED, 128, 2, FAKE, FAKE, nb, None) == -3

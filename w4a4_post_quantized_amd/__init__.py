@@ -21,6 +21,8 @@ __all__ = [
     "migrate_steps", "transform_quant_static", "linear_static",
     "linear_decode", "linear_decode_workspace_bytes", "decode_sync_buffer",
     "DECODE_SYNC_BYTES", "DECODE_SYNC_ERROR_WORD",
+    "KV_HEAD_DIM", "KvCache", "kv_cache_bytes", "kv_query_factor", "kv_append",
+    "attn_decode_workspace_bytes", "attn_decode",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so")
@@ -35,10 +37,13 @@ EXPORTED_SYMBOLS = [
     "w4a4_gemm_workspace_bytes", "w4a4_gemm", "w4a4_gemm_i32", "w4a4_gemm_kernel_name",
     "w4a4_linear_workspace_bytes", "w4a4_linear", "w4a4_linear_static",
     "w4a4_linear_decode_workspace_bytes", "w4a4_linear_decode",
+    "w4a4_kv_cache_bytes", "w4a4_kv_query_factor_workspace_bytes", "w4a4_kv_query_factor",
+    "w4a4_kv_append", "w4a4_attn_decode_workspace_bytes", "w4a4_attn_decode",
 ]
 
 DECODE_SYNC_BYTES = 1024          # W4A4_DECODE_SYNC_BYTES
 DECODE_SYNC_ERROR_WORD = 128      # W4A4_DECODE_SYNC_ERROR_WORD
+KV_HEAD_DIM = 128                 # W4A4_KV_HEAD_DIM
 
 
 class W4A4Error(RuntimeError):
@@ -73,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         dp = ctypes.POINTER(WeightDesc)
+        szp = ctypes.POINTER(ctypes.c_size_t)
         sig = {
             "w4a4_version": (ctypes.c_int, []),
             "w4a4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -97,6 +103,14 @@ def lib() -> ctypes.CDLL:
             "w4a4_linear_decode_workspace_bytes": (sz, [i32, i32, i32]),
             "w4a4_linear_decode": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, f32, vp, i32, dp, vp, vp,
                                                   vp, vp, vp, sz, vp, vp]),
+            "w4a4_kv_cache_bytes": (ctypes.c_int, [i32, i32, i32, i32, szp, szp, szp]),
+            "w4a4_kv_query_factor_workspace_bytes": (sz, [i32, i32]),
+            "w4a4_kv_query_factor": (ctypes.c_int, [vp, i32, i32, vp, vp, sz, vp]),
+            "w4a4_kv_append": (ctypes.c_int, [vp, vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, i32,
+                                              f32, f32, vp, vp, vp, vp, i32, i32, vp]),
+            "w4a4_attn_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+            "w4a4_attn_decode": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                                i32, f32, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -382,3 +396,96 @@ def linear_decode(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, sync=None, alp
                                     _p(z_w), _p(Y), _p(ws), nb if ws is None else ws.numel(),
                                     _p(sync), _stream(stream)), "w4a4_linear_decode")
     return Y
+
+
+# ---------------------------------------------------------------------------
+# INT4 KV cache with per-head transforms, decode attention
+# ---------------------------------------------------------------------------
+def kv_cache_bytes(batch: int, heads_kv: int, max_seq: int, head_dim: int = KV_HEAD_DIM):
+    """(key bytes, value bytes, scale bytes) of one layer's cache buffers."""
+    k, v, sc = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().w4a4_kv_cache_bytes(batch, heads_kv, head_dim, max_seq, ctypes.byref(k),
+                                     ctypes.byref(v), ctypes.byref(sc)), "w4a4_kv_cache_bytes")
+    return k.value, v.value, sc.value
+
+
+class KvCache:
+    """One layer's INT4 KV cache buffers in the layout of include/w4a4.h:
+    k_cache uint8 [B, H, S, 64], v_cache int32 [B, H, S/8, 128] (the bits of
+    the uint32 words), k_scale / v_scale float32 [B, H, S]."""
+
+    def __init__(self, batch: int, heads_kv: int, max_seq: int, device, zero: bool = True):
+        torch = _torch()
+        kv_cache_bytes(batch, heads_kv, max_seq)          # validates the shape
+        make = torch.zeros if zero else torch.empty
+        self.batch, self.heads_kv, self.max_seq = batch, heads_kv, max_seq
+        d = KV_HEAD_DIM
+        self.k_cache = make((batch, heads_kv, max_seq, d // 2), dtype=torch.uint8, device=device)
+        self.v_cache = make((batch, heads_kv, max_seq // 8, d), dtype=torch.int32, device=device)
+        self.k_scale = make((batch, heads_kv, max_seq), dtype=torch.float32, device=device)
+        self.v_scale = make((batch, heads_kv, max_seq), dtype=torch.float32, device=device)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.k_cache, self.v_cache, self.k_scale, self.v_scale))
+
+
+def kv_query_factor(P_h, out=None, stream=None):
+    """P_h^-T (float32) of a [d, d] or [H, d, d] stack of per-head key transforms."""
+    torch = _torch()
+    d = P_h.shape[-1]
+    count = 1 if P_h.dim() == 2 else P_h.shape[0]
+    _need(P_h, torch.float32, tuple(P_h.shape), "P_h")
+    out = out if out is not None else torch.empty_like(P_h)
+    nb = lib().w4a4_kv_query_factor_workspace_bytes(d, count)
+    ws = _ws(nb, P_h.device)
+    _check(lib().w4a4_kv_query_factor(_p(P_h), d, count, _p(out), _p(ws), nb, _stream(stream)),
+           "w4a4_kv_query_factor")
+    return out
+
+
+def kv_append(k, v, seg_seq, seg_start, cu_tokens, P_h, P_v, cache: KvCache,
+              alpha_k: float = 1.0, alpha_v: float = 1.0, stream=None):
+    """Transform, quantize and write tokens into ``cache`` (see w4a4_kv_append).
+    k, v: fp16 [T, H, 128]; seg_seq, seg_start: int32 [S]; cu_tokens: int32 [S+1]."""
+    torch = _torch()
+    T, H, d = k.shape
+    _need(k, torch.float16, (T, H, d), "k")
+    _need(v, torch.float16, (T, H, d), "v")
+    S = seg_seq.shape[0]
+    _need(seg_seq, torch.int32, (S,), "seg_seq")
+    _need(seg_start, torch.int32, (S,), "seg_start")
+    _need(cu_tokens, torch.int32, (S + 1,), "cu_tokens")
+    per_head = P_h.dim() == 3
+    _need(P_h, torch.float32, tuple(P_h.shape), "P_h")
+    _need(P_v, torch.float32, tuple(P_h.shape), "P_v")
+    _check(lib().w4a4_kv_append(_p(k), _p(v), T, _p(seg_seq), _p(seg_start), _p(cu_tokens), S, H, d,
+                                _p(P_h), _p(P_v), int(per_head), float(alpha_k), float(alpha_v),
+                                _p(cache.k_cache), _p(cache.k_scale), _p(cache.v_cache),
+                                _p(cache.v_scale), cache.batch, cache.max_seq, _stream(stream)),
+           "w4a4_kv_append")
+
+
+def attn_decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_seq: int) -> int:
+    return lib().w4a4_attn_decode_workspace_bytes(batch, heads_q, heads_kv, KV_HEAD_DIM, max_seq)
+
+
+def attn_decode(q, P_h_inv_t, cache: KvCache, lengths, sm_scale: float, out=None, ws=None,
+                stream=None):
+    """Decode attention over the INT4 cache: out [B, H_q, 128] fp16 in the P_v basis."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _need(q, torch.float16, (B, Hq, d), "q")
+    _need(lengths, torch.int32, (B,), "lengths")
+    per_head = P_h_inv_t.dim() == 3
+    _need(P_h_inv_t, torch.float32, tuple(P_h_inv_t.shape), "P_h_inv_t")
+    out = out if out is not None else torch.empty((B, Hq, d), dtype=torch.float16, device=q.device)
+    nb = attn_decode_workspace_bytes(B, Hq, cache.heads_kv, cache.max_seq)
+    ws = _ws(nb, q.device, ws)
+    _check(lib().w4a4_attn_decode(_p(q), B, Hq, cache.heads_kv, d, _p(P_h_inv_t), int(per_head),
+                                  _p(cache.k_cache), _p(cache.k_scale), _p(cache.v_cache),
+                                  _p(cache.v_scale), _p(lengths), cache.max_seq, float(sm_scale),
+                                  _p(out), _p(ws), nb if ws is None else ws.numel(),
+                                  _stream(stream)), "w4a4_attn_decode")
+    return out

@@ -31,7 +31,8 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 
-SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "weights.hip", "linear_decode.hip"]
+SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "weights.hip", "linear_decode.hip",
+           "kv_cache.hip", "attention.hip"]
 
 
 def _compile(src: str, extra=()):

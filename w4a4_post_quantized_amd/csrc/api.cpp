@@ -459,4 +459,182 @@ int w4a4_linear_decode(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, con
     return hip_status(e, "w4a4_linear_decode");
 }
 
+// ---------------------------------------------------------------------------
+// INT4 KV cache and decode attention
+// ---------------------------------------------------------------------------
+namespace {
+
+int check_kv_shape(int32_t batch, int32_t heads_kv, int32_t head_dim, int32_t max_seq) {
+    REQUIRE(batch >= 0, W4A4_ERR_INVALID_ARG, "batch = %d is negative", batch);
+    REQUIRE(heads_kv >= 1, W4A4_ERR_INVALID_ARG, "heads_kv = %d must be >= 1", heads_kv);
+    REQUIRE(head_dim == W4A4_KV_HEAD_DIM, W4A4_ERR_UNSUPPORTED,
+            "head_dim = %d: only %d is supported", head_dim, W4A4_KV_HEAD_DIM);
+    REQUIRE(max_seq >= 32 && max_seq % 32 == 0, W4A4_ERR_UNSUPPORTED,
+            "max_seq = %d must be a positive multiple of 32", max_seq);
+    REQUIRE(static_cast<int64_t>(batch) * heads_kv * max_seq <= (int64_t{1} << 40),
+            W4A4_ERR_UNSUPPORTED, "cache of %d x %d x %d positions is too large", batch,
+            heads_kv, max_seq);
+    return W4A4_OK;
+}
+
+size_t a256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+int w4a4_kv_cache_bytes(int32_t batch, int32_t heads_kv, int32_t head_dim, int32_t max_seq,
+                        size_t* k_bytes, size_t* v_bytes, size_t* scale_bytes) {
+    if (int s = check_kv_shape(batch, heads_kv, head_dim, max_seq)) return s;
+    const size_t pos = static_cast<size_t>(batch) * heads_kv * max_seq;
+    if (k_bytes) *k_bytes = pos * (head_dim / 2);
+    if (v_bytes) *v_bytes = pos * (head_dim / 2);
+    if (scale_bytes) *scale_bytes = pos * sizeof(float);
+    return ok();
+}
+
+size_t w4a4_kv_query_factor_workspace_bytes(int32_t head_dim, int32_t count) {
+    if (head_dim != W4A4_KV_HEAD_DIM || count < 1 || count > 4096) return 0;
+    return w4a4::invert_t_workspace_bytes(head_dim, count);
+}
+
+int w4a4_kv_query_factor(const float* P_h, int32_t head_dim, int32_t count, float* P_h_inv_t,
+                         void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE(head_dim == W4A4_KV_HEAD_DIM, W4A4_ERR_UNSUPPORTED,
+            "head_dim = %d: only %d is supported", head_dim, W4A4_KV_HEAD_DIM);
+    REQUIRE(count >= 1 && count <= 4096, W4A4_ERR_INVALID_ARG,
+            "count = %d must lie in [1, 4096]", count);
+    REQUIRE_PTR(P_h);
+    REQUIRE_PTR(P_h_inv_t);
+    REQUIRE_PTR(ws);
+    REQUIRE_ALIGNED(P_h);
+    REQUIRE_ALIGNED(P_h_inv_t);
+    REQUIRE_ALIGNED(ws);
+    const size_t need = w4a4::invert_t_workspace_bytes(head_dim, count);
+    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    bool singular = false;
+    hipError_t e = w4a4::invert_t_launch(P_h, head_dim, count, P_h_inv_t, ws,
+                                         static_cast<hipStream_t>(stream), &singular);
+    if (e != hipSuccess) return hip_status(e, "w4a4_kv_query_factor");
+    REQUIRE(!singular, W4A4_ERR_INVALID_ARG, "a P_h matrix is singular");
+    return ok();
+}
+
+int w4a4_kv_append(const uint16_t* k, const uint16_t* v, int32_t tokens, const int32_t* seg_seq,
+                   const int32_t* seg_start, const int32_t* cu_tokens, int32_t segments,
+                   int32_t heads_kv, int32_t head_dim, const float* P_h, const float* P_v,
+                   int32_t per_head, float alpha_k, float alpha_v, uint8_t* k_cache,
+                   float* k_scale, uint32_t* v_cache, float* v_scale, int32_t batch,
+                   int32_t max_seq, void* stream) {
+    if (int s = check_kv_shape(batch, heads_kv, head_dim, max_seq)) return s;
+    REQUIRE(tokens >= 0, W4A4_ERR_INVALID_ARG, "tokens = %d is negative", tokens);
+    REQUIRE(segments >= 0, W4A4_ERR_INVALID_ARG, "segments = %d is negative", segments);
+    REQUIRE(per_head == 0 || per_head == 1, W4A4_ERR_INVALID_ARG,
+            "per_head = %d must be 0 or 1", per_head);
+    REQUIRE(alpha_k > 0.0f && alpha_k <= 1.0f && alpha_v > 0.0f && alpha_v <= 1.0f,
+            W4A4_ERR_INVALID_ARG, "alpha_k = %g, alpha_v = %g must lie in (0, 1]",
+            static_cast<double>(alpha_k), static_cast<double>(alpha_v));
+    REQUIRE(static_cast<int64_t>(tokens) * heads_kv * head_dim < (int64_t{1} << 40),
+            W4A4_ERR_UNSUPPORTED, "tokens = %d is too large", tokens);
+    REQUIRE(segments <= (1 << 24), W4A4_ERR_UNSUPPORTED, "segments = %d is too large",
+            segments);
+    if (tokens == 0 || segments == 0 || batch == 0) return ok();
+    REQUIRE_PTR(k);
+    REQUIRE_PTR(v);
+    REQUIRE_PTR(seg_seq);
+    REQUIRE_PTR(seg_start);
+    REQUIRE_PTR(cu_tokens);
+    REQUIRE_PTR(P_h);
+    REQUIRE_PTR(P_v);
+    REQUIRE_PTR(k_cache);
+    REQUIRE_PTR(k_scale);
+    REQUIRE_PTR(v_cache);
+    REQUIRE_PTR(v_scale);
+    REQUIRE_ALIGNED(k);
+    REQUIRE_ALIGNED(v);
+    REQUIRE_ALIGNED(P_h);
+    REQUIRE_ALIGNED(P_v);
+    REQUIRE_ALIGNED(k_cache);
+    REQUIRE_ALIGNED(k_scale);
+    REQUIRE_ALIGNED(v_cache);
+    REQUIRE_ALIGNED(v_scale);
+    w4a4::KvAppendArgs a{k, v, seg_seq, seg_start, cu_tokens, P_h, P_v, alpha_k, alpha_v,
+                         k_cache, k_scale, v_cache, v_scale, tokens, segments, heads_kv,
+                         batch, max_seq, w4a4::kv_append_hpw(tokens, segments, heads_kv)};
+    hipError_t e = w4a4::kv_append_launch(a, per_head != 0, static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_kv_append");
+}
+
+namespace {
+
+int check_attn_shape(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t head_dim,
+                     int32_t max_seq) {
+    if (int s = check_kv_shape(batch, heads_kv, head_dim, max_seq)) return s;
+    REQUIRE(heads_q >= 1 && heads_q % heads_kv == 0, W4A4_ERR_INVALID_ARG,
+            "heads_q = %d is not a positive multiple of heads_kv = %d", heads_q, heads_kv);
+    REQUIRE(heads_q / heads_kv <= 16, W4A4_ERR_UNSUPPORTED,
+            "%d query heads per KV head exceed 16", heads_q / heads_kv);
+    return W4A4_OK;
+}
+
+size_t attn_ws_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t max_seq,
+                     int chunk) {
+    return a256(static_cast<size_t>(batch) * heads_q * W4A4_KV_HEAD_DIM * sizeof(float)) +
+           a256(w4a4::attn_partial_bytes(batch, heads_q, heads_kv, max_seq, chunk));
+}
+
+}  // namespace
+
+size_t w4a4_attn_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                        int32_t head_dim, int32_t max_seq) {
+    if (check_attn_shape(batch, heads_q, heads_kv, head_dim, max_seq) != W4A4_OK) return 0;
+    const int chunk = w4a4::attn_chunk(batch, heads_kv, max_seq);
+    return attn_ws_bytes(batch, heads_q, heads_kv, max_seq, chunk);
+}
+
+int w4a4_attn_decode(const uint16_t* q, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                     int32_t head_dim, const float* P_h_inv_t, int32_t per_head,
+                     const uint8_t* k_cache, const float* k_scale, const uint32_t* v_cache,
+                     const float* v_scale, const int32_t* lengths, int32_t max_seq,
+                     float sm_scale, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    if (int s = check_attn_shape(batch, heads_q, heads_kv, head_dim, max_seq)) return s;
+    REQUIRE(per_head == 0 || per_head == 1, W4A4_ERR_INVALID_ARG,
+            "per_head = %d must be 0 or 1", per_head);
+    REQUIRE(sm_scale > 0.0f && sm_scale < 3.0e38f, W4A4_ERR_INVALID_ARG,
+            "sm_scale = %g must be finite and > 0", static_cast<double>(sm_scale));
+    if (batch == 0) return ok();
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(P_h_inv_t);
+    REQUIRE_PTR(k_cache);
+    REQUIRE_PTR(k_scale);
+    REQUIRE_PTR(v_cache);
+    REQUIRE_PTR(v_scale);
+    REQUIRE_PTR(lengths);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(ws);
+    REQUIRE_ALIGNED(q);
+    REQUIRE_ALIGNED(P_h_inv_t);
+    REQUIRE_ALIGNED(k_cache);
+    REQUIRE_ALIGNED(k_scale);
+    REQUIRE_ALIGNED(v_cache);
+    REQUIRE_ALIGNED(v_scale);
+    REQUIRE_ALIGNED(out);
+    REQUIRE_ALIGNED(ws);
+    const int chunk = w4a4::attn_chunk(batch, heads_kv, max_seq);
+    const size_t need = attn_ws_bytes(batch, heads_q, heads_kv, max_seq, chunk);
+    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    float* qt = static_cast<float*>(ws);
+    float* part = reinterpret_cast<float*>(
+        static_cast<char*>(ws) +
+        a256(static_cast<size_t>(batch) * heads_q * W4A4_KV_HEAD_DIM * sizeof(float)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // log2(e): the softmax runs in base 2
+    hipError_t e = w4a4::rows_xform_launch(q, batch, heads_q, heads_kv, P_h_inv_t,
+                                           per_head != 0, sm_scale * 1.4426950408889634f, qt,
+                                           st);
+    if (e != hipSuccess) return hip_status(e, "w4a4_attn_decode");
+    w4a4::AttnArgs a{qt, k_cache, k_scale, v_cache, v_scale, lengths, out, part,
+                     batch, heads_q, heads_kv, max_seq, chunk};
+    e = w4a4::attn_decode_launch(a, st);
+    return hip_status(e, "w4a4_attn_decode");
+}
+
 }  // extern "C"

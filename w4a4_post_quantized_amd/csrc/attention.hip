@@ -1,0 +1,325 @@
+// Decode attention over the INT4 KV cache (one query token per sequence).
+//
+// FlatQuant: Flatness Matters for LLM Quantization, sections 核心思想 and
+// Transformer 集成: the key cache holds Q(k·P_h) per head, so the query takes
+// the inverse transpose, (q·P_h^-T)·(k·P_h)^T = q·k^T; the value cache holds
+// Q(v·P_v) and the attention output stays in the P_v basis (P_v^-1 belongs to
+// the output projection's weights).  Softmax attention with grouped query
+// heads (head h reads KV head h / G) is the textbook definition.
+//
+// Three launches:
+//   1. q~ = q · P_h^-T · (sm_scale · log2 e), fp32 (k_rows_xform, kv_cache.hip);
+//   2. k_attn_partial: one workgroup per (chunk of C positions, KV head,
+//      sequence); four waves stream 32-token tiles of packed keys and values
+//      from HBM into registers and run both products on fp16 MFMA
+//      (v_mfma_f32_16x16x32_f16) with exact operands: codes are integers
+//      (exact in fp16) and q~ and the probabilities are split into fp16
+//      hi + lo parts, so every product is exact and only the fp32
+//      accumulation rounds.  Online softmax in base 2; the waves' states
+//      are merged in LDS and one partial record per workgroup is written;
+//   3. k_attn_combine merges the chunks of each (sequence, KV head).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace w4a4 {
+
+namespace {
+
+constexpr int kHd = 128;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kGMax = 16;             // query heads per KV head (MFMA columns)
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Eight signed nibbles (nibble j = element j) as fp16 in the slot order
+// 0, 4, 1, 5, 2, 6, 3, 7: the offset-binary nibble u = q + 8 is placed in the
+// mantissa of 1024.0 (exact), and 1032 is subtracted (exact).
+__device__ __forceinline__ v8h nib8_h8(uint32_t w) {
+    const uint32_t u = w ^ 0x88888888u;
+    const uint32_t bias = 0x64006400u;
+    const v2h off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+    const v2h a0 = __builtin_bit_cast(v2h, (u & 0x000F000Fu) | bias) - off;
+    const v2h a1 = __builtin_bit_cast(v2h, ((u >> 4) & 0x000F000Fu) | bias) - off;
+    const v2h a2 = __builtin_bit_cast(v2h, ((u >> 8) & 0x000F000Fu) | bias) - off;
+    const v2h a3 = __builtin_bit_cast(v2h, ((u >> 12) & 0x000F000Fu) | bias) - off;
+    const v4h lo = __builtin_shufflevector(a0, a1, 0, 1, 2, 3);
+    const v4h hi = __builtin_shufflevector(a2, a3, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// x = hi + lo with hi = fp16(x) and lo = fp16(x - hi): for |x| < 2 the pair
+// carries x to within 2^-25 absolute.
+__device__ __forceinline__ void split_h(float x, _Float16& hi, _Float16& lo) {
+    hi = static_cast<_Float16>(x);
+    lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+__device__ __forceinline__ float pow2i(int e) { return __builtin_ldexpf(1.0f, e); }
+
+// ---------------------------------------------------------------------------
+// Partial attention of one chunk.  Lane l of a wave: c16 = l % 16, q4 = l / 16.
+//  - score product S^T[token, g] = K[token, :] · q~[g, :]^T: A = key rows,
+//    B = q~ (column g = c16).  A 32-token tile is two 16-row products whose
+//    row r holds token 8*(r/4) + 4*s + r%4 (s = product index), so lane l ends
+//    with tokens 8*q4 .. 8*q4+7 of column g = c16;
+//  - value product O^T[ch, g] += V^T[ch, tokens] · P^T[tokens, g]: A = value
+//    words (row c16 <-> channel 4*c16 + db%4 + 64*(db/4) for block db), B =
+//    the lane's own probabilities; the output column is again g = c16, so the
+//    softmax state (m, l) of column g lives in the lanes that hold its O.
+// Contraction slots follow the nibble order of nib8_h8 on both operands.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
+    __shared__ float so[kWaves][kGMax][kHd];
+    __shared__ float sm[kWaves][kGMax];
+    __shared__ float sl[kWaves][kGMax];
+    __shared__ float svmax[kWaves];
+
+    const int c = blockIdx.x;
+    const int hk = blockIdx.y;
+    const int b = blockIdx.z;
+    const int C = a.chunk;
+    int L = a.lengths[b];
+    L = L < 0 ? 0 : (L > a.max_seq ? a.max_seq : L);
+    const int t_begin = c * C;
+    if (t_begin >= L) return;
+    const int t_end = min(L, t_begin + C);
+    const int G = a.heads_q / a.heads_kv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int c16 = lane & 15;
+    const int q4 = lane >> 4;
+    const size_t bh = static_cast<size_t>(b) * a.heads_kv + hk;
+    const float* ksc = a.k_scale + bh * a.max_seq;
+    const float* vsc = a.v_scale + bh * a.max_seq;
+
+    // chunk-wide power of two that brings the value scales below 2
+    float vm = 0.0f;
+    for (int t = t_begin + tid; t < t_end; t += kThreads) vm = fmaxf(vm, fabsf(vsc[t]));
+    vm = wave_max(vm);
+    if (lane == 0) svmax[w] = vm;
+    __syncthreads();
+    vm = fmaxf(fmaxf(svmax[0], svmax[1]), fmaxf(svmax[2], svmax[3]));
+    const int ev = vm > 0.0f ? ilog2f(vm) : 0;
+    const float fv = pow2i(-ev);
+
+    // q~ of column g = c16 as hi/lo fp16 B operands, scaled by a per-column
+    // power of two into [1, 2)
+    const int g = c16;
+    const bool gval = g < G;
+    const float* qrow = a.qt + (static_cast<size_t>(b) * a.heads_q + hk * G + (gval ? g : 0)) * kHd;
+    float qv[4][8];
+    float qmax = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * q4 + 8 * ks);
+        const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * q4 + 8 * ks + 4);
+        const float e8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        constexpr int nu[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            qv[ks][j] = gval ? e8[nu[j]] : 0.0f;
+            qmax = fmaxf(qmax, fabsf(qv[ks][j]));
+        }
+    }
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+    const int eq = qmax > 0.0f ? ilog2f(qmax) : 0;
+    const float fq = pow2i(-eq);
+    const float uq = pow2i(eq);
+    v8h qh[4], ql[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            _Float16 h, l;
+            split_h(qv[ks][j] * fq, h, l);
+            qh[ks][j] = h;
+            ql[ks][j] = l;
+        }
+
+    float m = -__builtin_inff();
+    float lp = 0.0f;
+    v4f O[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) O[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int tau0 = 8 * (c16 >> 2) + (c16 & 3);      // key row of product s: tau0 + 4 s
+    const uint8_t* kbase = a.k_cache + (bh * a.max_seq) * (kHd / 2) + 16 * q4;
+    const uint32_t* vbase = a.v_cache + bh * (a.max_seq / 8) * kHd + 4 * c16;
+
+    for (int t0 = t_begin + 32 * w; t0 < t_end; t0 += 32 * kWaves) {
+        const uint4 k0 = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0 + tau0) * (kHd / 2));
+        const uint4 k1 = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0 + tau0 + 4) * (kHd / 2));
+        const uint32_t* vb = vbase + static_cast<size_t>(t0 / 8 + q4) * kHd;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(vb);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(vb + 64);
+        const float4 sk0 = *reinterpret_cast<const float4*>(ksc + t0 + 8 * q4);
+        const float4 sk1 = *reinterpret_cast<const float4*>(ksc + t0 + 8 * q4 + 4);
+        const float4 sv0 = *reinterpret_cast<const float4*>(vsc + t0 + 8 * q4);
+        const float4 sv1 = *reinterpret_cast<const float4*>(vsc + t0 + 8 * q4 + 4);
+
+        // scores
+        const uint32_t kw[2][4] = {{k0.x, k0.y, k0.z, k0.w}, {k1.x, k1.y, k1.z, k1.w}};
+        v4f acc[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            acc[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const v8h ka = nib8_h8(kw[s][ks]);
+                acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[ks], acc[s], 0, 0, 0);
+                acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql[ks], acc[s], 0, 0, 0);
+            }
+        }
+        const float skv[2][4] = {{sk0.x, sk0.y, sk0.z, sk0.w}, {sk1.x, sk1.y, sk1.z, sk1.w}};
+        const float svv[2][4] = {{sv0.x, sv0.y, sv0.z, sv0.w}, {sv1.x, sv1.y, sv1.z, sv1.w}};
+        float x[2][4];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = t0 + 8 * q4 + 4 * s + i < t_end;
+                x[s][i] = ok ? acc[s][i] * uq * skv[s][i] : -__builtin_inff();
+                mx = fmaxf(mx, x[s][i]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        if (__any(mn > m)) {
+            const float al = __builtin_amdgcn_exp2f(m - mn);
+            lp *= al;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) O[db] *= al;
+            m = mn;
+        }
+        // probabilities (times the value scale) as hi/lo B operands
+        v8h ph, pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const bool ok = t0 + 8 * q4 + 4 * s + i < t_end;
+                const float p = __builtin_amdgcn_exp2f(x[s][i] - m);
+                lp += p;
+                const float pv = ok ? p * svv[s][i] * fv : 0.0f;
+                _Float16 h, l;
+                split_h(pv, h, l);
+                ph[2 * i + s] = h;
+                pl[2 * i + s] = l;
+            }
+        const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const v8h va = nib8_h8(vw[db]);
+            O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, O[db], 0, 0, 0);
+            O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl, O[db], 0, 0, 0);
+        }
+    }
+
+    // merge the four waves' states in LDS
+    lp += __shfl_xor(lp, 16);
+    lp += __shfl_xor(lp, 32);
+    if (q4 == 0) {
+        sm[w][c16] = m;
+        sl[w][c16] = lp;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            so[w][c16][16 * q4 + 4 * i + (db & 3) + 64 * (db >> 2)] = O[db][i];
+    __syncthreads();
+    const int nch = (a.max_seq + C - 1) / C;
+    float* rec = a.part + ((bh * nch) + c) * static_cast<size_t>(G) * (kHd + 2);
+    const float unv = pow2i(ev);
+    for (int it = tid; it < G * kHd; it += kThreads) {
+        const int gg = it / kHd;
+        const int d = it % kHd;
+        float M = sm[0][gg];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm[ww][gg]);
+        float o = 0.0f, l = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float f = __builtin_amdgcn_exp2f(sm[ww][gg] - M);
+            o += f * so[ww][gg][d];
+            l += f * sl[ww][gg];
+        }
+        rec[2 * G + gg * kHd + d] = o * unv;
+        if (d == 0) {
+            rec[gg] = M;
+            rec[G + gg] = l;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge the chunk records of one (sequence, KV head); fp16 output.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_attn_combine(AttnArgs a) {
+    const int hk = blockIdx.x;
+    const int b = blockIdx.y;
+    const int C = a.chunk;
+    const int G = a.heads_q / a.heads_kv;
+    int L = a.lengths[b];
+    L = L < 0 ? 0 : (L > a.max_seq ? a.max_seq : L);
+    const int nc = (L + C - 1) / C;
+    const int nch = (a.max_seq + C - 1) / C;
+    const size_t bh = static_cast<size_t>(b) * a.heads_kv + hk;
+    const float* rec0 = a.part + bh * nch * static_cast<size_t>(G) * (kHd + 2);
+    const size_t rs = static_cast<size_t>(G) * (kHd + 2);
+    uint16_t* out = a.out + (static_cast<size_t>(b) * a.heads_q + hk * G) * kHd;
+    for (int it = threadIdx.x; it < G * kHd; it += kThreads) {
+        const int gg = it / kHd;
+        const int d = it % kHd;
+        float r = 0.0f;
+        if (nc > 0) {
+            float M = -__builtin_inff();
+            for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, rec0[cc * rs + gg]);
+            float num = 0.0f, den = 0.0f;
+            for (int cc = 0; cc < nc; ++cc) {
+                const float* rc = rec0 + cc * rs;
+                const float f = __builtin_amdgcn_exp2f(rc[gg] - M);
+                num += f * rc[2 * G + gg * kHd + d];
+                den += f * rc[G + gg];
+            }
+            r = num / den;
+        }
+        out[it] = f2h(r);
+    }
+}
+
+}  // namespace
+
+int attn_chunk(int batch, int heads_kv, int max_seq) {
+    // the largest power of two (<= 1024) that still gives about 8 workgroups
+    // per compute unit
+    const int cus = device_cu_count();
+    int C = 1024;
+    while (C > 128 &&
+           static_cast<long>((max_seq + C - 1) / C) * batch * heads_kv < 8L * cus)
+        C /= 2;
+    return C;
+}
+
+size_t attn_partial_bytes(int batch, int heads_q, int heads_kv, int max_seq, int chunk) {
+    const size_t nch = static_cast<size_t>((max_seq + chunk - 1) / chunk);
+    const size_t G = static_cast<size_t>(heads_q / heads_kv);
+    return static_cast<size_t>(batch) * heads_kv * nch * G * (kHd + 2) * sizeof(float);
+}
+
+hipError_t attn_decode_launch(const AttnArgs& a, hipStream_t stream) {
+    if (a.batch == 0) return hipSuccess;
+    const int nch = (a.max_seq + a.chunk - 1) / a.chunk;
+    k_attn_partial<<<dim3(nch, a.heads_kv, a.batch), kThreads, 0, stream>>>(a);
+    k_attn_combine<<<dim3(a.heads_kv, a.batch), kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace w4a4

@@ -60,6 +60,47 @@ hipError_t linear_decode_launch(const uint16_t* X, int M, int n1, int n2, const 
                                 const float* P2, ActQuant aq, const GemmArgs& g, void* ws,
                                 uint32_t* sync, hipStream_t stream);
 
+// ---- INT4 KV cache (kv_cache.hip) -------------------------------------------
+struct KvAppendArgs {
+    const uint16_t* k;          // [tokens][heads][128] fp16
+    const uint16_t* v;
+    const int32_t* seg_seq;     // [segments]
+    const int32_t* seg_start;   // [segments]
+    const int32_t* cu_tokens;   // [segments + 1]
+    const float* P_h;           // [128][128] or [heads][128][128]
+    const float* P_v;
+    float alpha_k, alpha_v;
+    uint8_t* k_cache;
+    float* k_scale;
+    uint32_t* v_cache;
+    float* v_scale;
+    int tokens, segments, heads, batch, max_seq;
+    int hpw;                    // heads per workgroup (kv_append_hpw)
+};
+int kv_append_hpw(int tokens, int segments, int heads);
+hipError_t kv_append_launch(const KvAppendArgs& a, bool per_head, hipStream_t stream);
+// out[b][h][:] = scale * q[b][h][:] · M[h / G] (fp32), G = heads_q / heads_kv
+hipError_t rows_xform_launch(const uint16_t* q, int batch, int heads_q, int heads_kv,
+                             const float* M, bool per_head, float scale, float* out,
+                             hipStream_t stream);
+
+// ---- decode attention over the INT4 KV cache (attention.hip) ---------------
+struct AttnArgs {
+    const float* qt;            // [batch][heads_q][128], scaled by sm_scale * log2(e)
+    const uint8_t* k_cache;
+    const float* k_scale;
+    const uint32_t* v_cache;
+    const float* v_scale;
+    const int32_t* lengths;     // [batch]
+    uint16_t* out;              // [batch][heads_q][128] fp16
+    float* part;                // partial records
+    int batch, heads_q, heads_kv, max_seq, chunk;
+};
+// positions per partial-attention workgroup for this device
+int attn_chunk(int batch, int heads_kv, int max_seq);
+size_t attn_partial_bytes(int batch, int heads_q, int heads_kv, int max_seq, int chunk);
+hipError_t attn_decode_launch(const AttnArgs& a, hipStream_t stream);
+
 // ---- offline weight preparation (weights.hip) ------------------------------
 size_t merge_workspace_bytes(int n1, int n2, int K);
 // returns hipSuccess and sets *singular when a factor has no usable pivot
@@ -69,6 +110,11 @@ hipError_t merge_launch(const float* W, int N, int K, int n1, int n2, const floa
 // Wm[n, k] = Wt[n, k] * steps[k] (fp32, one rounding); Wm may equal Wt
 hipError_t migrate_steps_launch(const float* Wt, int N, int K, const float* steps, float* Wm,
                                 hipStream_t stream);
+// out[i] = P[i]^-T (fp32, computed in fp64) for count n x n matrices; sets
+// *singular when one has no usable pivot
+size_t invert_t_workspace_bytes(int n, int count);
+hipError_t invert_t_launch(const float* P, int n, int count, float* out, void* ws,
+                           hipStream_t stream, bool* singular);
 hipError_t pack_weights_launch(const float* Wt, int N, int K, int group_size, bool asym,
                                float alpha_w, uint8_t* Wq, uint16_t* s_w, uint16_t* z_w,
                                hipStream_t stream);

@@ -100,6 +100,15 @@ __global__ __launch_bounds__(256) void k_extract_inverse(const double* __restric
     out[transpose ? col * n + r : e] = v;
 }
 
+// [I | P^-1] -> (P^-1)^T as fp32 (one rounding from fp64)
+__global__ __launch_bounds__(256) void k_extract_inverse_t32(const double* __restrict__ A, int n,
+                                                             float* __restrict__ out) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n * n) return;
+    const int r = e / n, col = e % n;
+    out[col * n + r] = static_cast<float>(A[r * 2 * n + n + col]);
+}
+
 // ---------------------------------------------------------------------------
 // Merge: Wt[n] = P1inv · (W̄[n] / c) · P2inv^T in float64, rounded to fp32.
 // One persistent workgroup per row slot; U = W̄·P2inv^T lives in a float64
@@ -278,6 +287,36 @@ hipError_t merge_launch(const float* W, int N, int K, int n1, int n2, const floa
     if (blocks > 0) k_merge<<<blocks, 256, 0, stream>>>(W, N, n1, n2, P1inv, P2invT, c, U, Wt);
     (void)K;
     return hipGetLastError();
+}
+
+size_t invert_t_workspace_bytes(int n, int count) {
+    return align256(sizeof(double) * 2 * n * n) + align256(sizeof(double) * count);
+}
+
+hipError_t invert_t_launch(const float* P, int n, int count, float* out, void* ws,
+                           hipStream_t stream, bool* singular) {
+    double* A = static_cast<double*>(ws);
+    double* piv = reinterpret_cast<double*>(static_cast<char*>(ws) +
+                                            align256(sizeof(double) * 2 * n * n));
+    for (int i = 0; i < count; ++i) {
+        k_invert<<<1, 1024, 0, stream>>>(P + static_cast<size_t>(i) * n * n, n, A, piv + i);
+        k_extract_inverse_t32<<<ceil_div(n * n, 256), 256, 0, stream>>>(
+            A, n, out + static_cast<size_t>(i) * n * n);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    double hp[64];
+    *singular = false;
+    for (int i0 = 0; i0 < count; i0 += 64) {
+        const int c = count - i0 < 64 ? count - i0 : 64;
+        e = hipMemcpyAsync(hp, piv + i0, sizeof(double) * c, hipMemcpyDeviceToHost, stream);
+        if (e != hipSuccess) return e;
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return e;
+        for (int i = 0; i < c; ++i)
+            if (!(hp[i] > 1e-300)) *singular = true;
+    }
+    return hipSuccess;
 }
 
 hipError_t migrate_steps_launch(const float* Wt, int N, int K, const float* steps, float* Wm,

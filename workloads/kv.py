@@ -27,7 +27,7 @@ import numpy as np
 from . import random_invertible
 
 __all__ = ["KvWorkload", "KV_WORKLOADS", "get_kv", "make_kv_static", "make_history",
-           "make_new_tokens"]
+           "make_new_tokens", "make_tokens"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -103,3 +103,9 @@ def make_new_tokens(wl: KvWorkload, outliers):
     fp16 [B, H_kv, d] each."""
     rng = np.random.default_rng([wl.seed, 2])
     return _kv_rows(wl, rng, wl.batch, outliers)
+
+
+def make_tokens(wl: KvWorkload, n: int, outliers, seed):
+    """``n`` keys and values drawn like the workload's (for custom test
+    layouts), fp16 [n, H_kv, d] each, from default_rng(seed)."""
+    return _kv_rows(wl, np.random.default_rng(seed), n, outliers)
