@@ -20,6 +20,12 @@ With --path single (decode, M <= 16) the step is one w4a4_linear_decode
 launch (transform, quantization and GEMM in one kernel) and the roofline
 kernel is that kernel, priced at the layer's algorithmic bytes.
 
+With --workload attn8b|attn70b the step is one decode step of attention over
+the INT4 KV cache with per-head transforms: w4a4_kv_append of the batch's new
+tokens, then w4a4_attn_decode over the ragged contexts (up to 8192 cached
+tokens).  Its roofline unit is the w4a4_attn_decode call (query transform,
+chunked partial attention, merge) priced at the cache bytes it must read.
+
 Prints ONE JSON line.  `value` is TOPS of the whole layer (2*M*N*K integer
 ops per step / step time).  `roofline` reports the dominant kernel (the GEMM)
 against the INT8 MFMA peak (prefill) or HBM bandwidth (decode), its duration
@@ -51,7 +57,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qkv8b")
+    ap.add_argument("--workload", default="qkv8b",
+                    help="linear: qkv8b gateup8b down8b gateup70b down70b_m{1,8,64}; "
+                         "attention over the INT4 KV cache: attn8b attn70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--path", choices=["two", "single"], default="two",
@@ -208,6 +216,11 @@ def main():
     import torch
     import workloads as WL
     import w4a4_post_quantized_amd as L
+    from workloads import kv as WKV
+
+    if args.workload in WKV.KV_WORKLOADS:
+        attn_main(args)
+        return
 
     wl = WL.get(args.workload)
     dev = torch.device("cuda:0")
@@ -403,6 +416,188 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.act_quant)
     print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# decode attention over the INT4 KV cache
+# ---------------------------------------------------------------------------
+ATTN_BYTES_PER_TOKEN_HEAD = 64 + 64 + 4 + 4      # key and value codes, two fp32 scales
+
+
+def attn_bytes(wl, lengths):
+    """Algorithmic bytes of one w4a4_attn_decode call: the cached codes and
+    scales of every context token and KV head, the fp16 queries and outputs,
+    and the fp32 query factor."""
+    tok = int(np.sum(lengths))
+    return (tok * wl.heads_kv * ATTN_BYTES_PER_TOKEN_HEAD + 2 * 2 * wl.batch * wl.heads_q * 128
+            + 4 * 128 * 128)
+
+
+def attn_cpu_baseline(wl, st, budget_s):
+    """The oracle's decode attention on whole sequences until `budget_s`,
+    projected to the layer by context tokens."""
+    import math
+    from oracle import kv_oracle as KV
+    from workloads import kv as WKV
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    sm = 1.0 / math.sqrt(128)
+    done_tok, t_used, seqs = 0, 0.0, 0
+    for b in range(wl.batch):
+        L = int(st["lengths"][b])
+        k, v = WKV.make_history(wl, b, L, st["outliers"])
+        oc = KV.KvCache(1, wl.heads_kv, wl.max_seq, 128)
+        KV.kv_append(oc, k, v, [0], [0], [0, L], st["P_h"], st["P_v"])   # untimed
+        t0 = time.perf_counter()
+        KV.attention_decode(st["q"][b:b + 1], oc, np.array([L]), st["P_h"], sm)
+        t_used += time.perf_counter() - t0
+        done_tok += L
+        seqs += 1
+        if t_used >= budget_s:
+            break
+    total_tok = int(np.sum(st["lengths"]))
+    t_layer = t_used / done_tok * total_tok
+    ops = 4.0 * total_tok * wl.heads_q * 128
+    return {"value": ops / t_layer / 1e12, "unit": "TOPS", "cores": int(threads),
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"decode attention of {seqs} of the {wl.batch} sequences ({done_tok} context "
+                      f"tokens, caches built untimed), {t_used:.1f} s, projected to all "
+                      f"{total_tok} tokens",
+            "us_per_layer": t_layer * 1e6}
+
+
+def attn_main(args):
+    import math
+    import torch
+    import w4a4_post_quantized_amd as L
+    from workloads import kv as WKV
+
+    wl = WKV.get_kv(args.workload)
+    st = WKV.make_kv_static(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Hq, Hkv, S = wl.batch, wl.heads_q, wl.heads_kv, wl.max_seq
+    lengths = st["lengths"]                      # contexts including the step's new token
+    cache = L.KvCache(B, Hkv, S, dev)
+    P_h = torch.from_numpy(st["P_h"]).to(dev)
+    P_v = torch.from_numpy(st["P_v"]).to(dev)
+    # the cached history (positions 0 .. L-2), drawn on the GPU with the
+    # workload's distribution: N(0,1), keys with x8 outlier channels per head
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    hist = (lengths - 1).astype(np.int64)
+    T = int(hist.sum())
+    kscale = torch.ones((Hkv, 128), device=dev)
+    for h in range(Hkv):
+        kscale[h, torch.from_numpy(st["outliers"][h]).to(dev)] = wl.outlier_scale
+    k = (torch.randn((T, Hkv, 128), generator=g, device=dev) * kscale).half()
+    v = torch.randn((T, Hkv, 128), generator=g, device=dev).half()
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(hist)]).astype(np.int32)).to(dev)
+    seqs = torch.arange(B, dtype=torch.int32, device=dev)
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+    L.kv_append(k, v, seqs, zeros, cu, P_h, P_v, cache)
+    torch.cuda.synchronize()
+    del k, v
+
+    # prefill append rate: one 2048-token segment of one sequence
+    kp = torch.randn((2048, Hkv, 128), generator=g, device=dev).half()
+    vp = torch.randn((2048, Hkv, 128), generator=g, device=dev).half()
+    cup = torch.tensor([0, 2048], dtype=torch.int32, device=dev)
+    one = torch.tensor([B - 1], dtype=torch.int32, device=dev)
+    zero1 = torch.zeros(1, dtype=torch.int32, device=dev)
+    pre_cache = L.KvCache(1, Hkv, 2048, dev)
+    for _ in range(3):
+        L.kv_append(kp, vp, zero1, zero1, cup, P_h, P_v, pre_cache)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        L.kv_append(kp, vp, zero1, zero1, cup, P_h, P_v, pre_cache)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_us = e0.elapsed_time(e1) * 1e3 / 20
+    prefill_bytes = 2 * 2048 * Hkv * 128 * 2 + 2048 * Hkv * ATTN_BYTES_PER_TOKEN_HEAD
+    del kp, vp, pre_cache, one
+
+    # the decode step: append the new token at position L-1, attend over L
+    kn, vn = WKV.make_new_tokens(wl, st["outliers"])
+    kn = torch.from_numpy(kn).to(dev)
+    vn = torch.from_numpy(vn).to(dev)
+    pos = torch.from_numpy(hist.astype(np.int32)).to(dev)
+    cun = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    q = torch.from_numpy(st["q"]).to(dev)
+    lens = torch.from_numpy(lengths.astype(np.int32)).to(dev)
+    Pinv = L.kv_query_factor(P_h)
+    sm = 1.0 / math.sqrt(128)
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
+    ws = torch.empty(max(1, L.attn_decode_workspace_bytes(B, Hq, Hkv, S)), dtype=torch.uint8,
+                     device=dev)
+
+    def attend(i):
+        L.attn_decode(q, Pinv, cache, lens, sm, out=out, ws=ws)
+
+    def step(i):
+        L.kv_append(kn, vn, seqs, pos, cun, P_h, P_v, cache)
+        attend(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+
+    for i in range(args.warmup):
+        attend(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        attend(i)
+    e1.record()
+    torch.cuda.synchronize()
+    attn_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    e0.record()
+    for i in range(args.steps):
+        L.kv_append(kn, vn, seqs, pos, cun, P_h, P_v, cache)
+    e1.record()
+    torch.cuda.synchronize()
+    append_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    dist = event_stats(attend, max(20, args.steps))
+
+    gb = attn_bytes(wl, lengths)
+    achieved = gb / (attn_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "kernel": "w4a4_attn_decode (k_rows_xform + k_attn_partial + k_attn_combine)",
+            "kernel_us": round(attn_us, 2), "bytes": gb,
+            "bytes_per_unit": f"{ATTN_BYTES_PER_TOKEN_HEAD} B per cached (token, KV head)",
+            "traffic": traffic_from_profiles("attn", wl.name, "attention.hip"),
+            "timing": "mean over HIP events around back-to-back calls on the launch stream; "
+                      "per_launch_us from events around each call",
+            "per_launch_us": dist}
+    ops = 4.0 * float(np.sum(lengths)) * Hq * 128
+    res = {
+        "metric": METRIC, "value": round(ops / t_step / 1e12, 3), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 KV codes, fp16 MFMA with exact hi/lo operands, fp32 accumulation",
+        "data": "synthetic (seeded; N(0,1) queries, keys with x8 outlier channels, values; "
+                "ragged contexts)",
+        "config": {"workload": wl.description, "name": wl.name, "batch": B, "heads_q": Hq,
+                   "heads_kv": Hkv, "head_dim": 128, "max_seq": S,
+                   "context_tokens": int(np.sum(lengths))},
+        "us_per_layer": round(t_step * 1e6, 2),
+        "path": "w4a4_kv_append (decode tokens) + w4a4_attn_decode",
+        "attn_us": round(attn_us, 2), "append_decode_us": round(append_us, 2),
+        "append_prefill_2048": {"us": round(prefill_us, 2), "bytes": prefill_bytes,
+                                "achieved_GBps": round(prefill_bytes / (prefill_us * 1e-6) / 1e9, 1)},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = attn_cpu_baseline(wl, st, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -11,13 +11,20 @@
 //   1. q~ = q · P_h^-T · (sm_scale · log2 e), fp32 (k_rows_xform, kv_cache.hip);
 //   2. k_attn_partial: one workgroup per (chunk of C positions, KV head,
 //      sequence); four waves stream 32-token tiles of packed keys and values
-//      from HBM into registers and run both products on fp16 MFMA
-//      (v_mfma_f32_16x16x32_f16) with exact operands: codes are integers
-//      (exact in fp16) and q~ and the probabilities are split into fp16
-//      hi + lo parts, so every product is exact and only the fp32
-//      accumulation rounds.  Online softmax in base 2; the waves' states
-//      are merged in LDS and one partial record per workgroup is written;
+//      from HBM into registers (the next tile's loads in flight while the
+//      current one is computed) and run both products on MFMA with exact
+//      operands.  Online softmax in base 2; the waves' states are merged in
+//      LDS and one partial record per workgroup is written;
 //   3. k_attn_combine merges the chunks of each (sequence, KV head).
+//
+// Arithmetic of the two products (fp16 MFMA, v_mfma_f32_16x16x32_f16):
+//   codes enter as q or 16 q, exact in fp16 (nib8_h8x16); q~ is scaled by a
+//   power of two per head into [1, 2), and the value weights
+//   p'_t = p_t * s_v[t] by one power of two per chunk into (0, 2); both are
+//   split into fp16 hi + lo, so every product is exact and only the fp32
+//   accumulation rounds.  The running maximum of the online softmax is
+//   raised only when a tile exceeds it by more than 2^10 (weights up to 2^10
+//   stay exact in the split), so O is rarely rescaled.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -30,35 +37,29 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kGMax = 16;             // query heads per KV head (MFMA columns)
 
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-// Eight signed nibbles (nibble j = element j) as fp16 in the slot order
-// 0, 4, 1, 5, 2, 6, 3, 7: the offset-binary nibble u = q + 8 is placed in the
-// mantissa of 1024.0 (exact), and 1032 is subtracted (exact).
-__device__ __forceinline__ v8h nib8_h8(uint32_t w) {
-    const uint32_t u = w ^ 0x88888888u;
-    const uint32_t bias = 0x64006400u;
-    const v2h off = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-    const v2h a0 = __builtin_bit_cast(v2h, (u & 0x000F000Fu) | bias) - off;
-    const v2h a1 = __builtin_bit_cast(v2h, ((u >> 4) & 0x000F000Fu) | bias) - off;
-    const v2h a2 = __builtin_bit_cast(v2h, ((u >> 8) & 0x000F000Fu) | bias) - off;
-    const v2h a3 = __builtin_bit_cast(v2h, ((u >> 12) & 0x000F000Fu) | bias) - off;
-    const v4h lo = __builtin_shufflevector(a0, a1, 0, 1, 2, 3);
-    const v4h hi = __builtin_shufflevector(a2, a3, 0, 1, 2, 3);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+// Eight signed nibbles (nibble j = element j) as fp16 MFMA operand slots in
+// the order 0, 4, 1, 5, 2, 6, 3, 7.  Each nibble stays where it is inside
+// its 16-bit half: flipping its top bit gives the offset-binary u = q + 8,
+// and OR-ing the exponent of 1024 gives 1024 + u (bits 0-3) or 1024 + 16 u
+// (bits 4-7), both exact; subtracting 1032 or 1152 leaves q or 16 q.  So
+// slots 2, 3, 6, 7 carry 16 q, and the other operand puts a factor 16 on
+// slots 0, 1, 4, 5 instead (kSlotScale): every product is 16 q b.
+__device__ __forceinline__ v8h nib8_h8x16(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    const v4u r = {(w & 0x000F000Fu) ^ 0x64086408u, (w & 0x00F000F0u) ^ 0x64806480u,
+                   (w8 & 0x000F000Fu) ^ 0x64086408u, (w8 & 0x00F000F0u) ^ 0x64806480u};
+    const _Float16 a = static_cast<_Float16>(1032.0f);
+    const _Float16 b = static_cast<_Float16>(1152.0f);
+    return __builtin_bit_cast(v8h, r) - v8h{a, a, b, b, a, a, b, b};
 }
-
-// x = hi + lo with hi = fp16(x) and lo = fp16(x - hi): for |x| < 2 the pair
-// carries x to within 2^-25 absolute.
-__device__ __forceinline__ void split_h(float x, _Float16& hi, _Float16& lo) {
-    hi = static_cast<_Float16>(x);
-    lo = static_cast<_Float16>(x - static_cast<float>(hi));
-}
+constexpr float kSlotScale[8] = {16.0f, 16.0f, 1.0f, 1.0f, 16.0f, 16.0f, 1.0f, 1.0f};
 
 __device__ __forceinline__ float pow2i(int e) { return __builtin_ldexpf(1.0f, e); }
+
 
 // ---------------------------------------------------------------------------
 // Partial attention of one chunk.  Lane l of a wave: c16 = l % 16, q4 = l / 16.
@@ -66,13 +67,15 @@ __device__ __forceinline__ float pow2i(int e) { return __builtin_ldexpf(1.0f, e)
 //    B = q~ (column g = c16).  A 32-token tile is two 16-row products whose
 //    row r holds token 8*(r/4) + 4*s + r%4 (s = product index), so lane l ends
 //    with tokens 8*q4 .. 8*q4+7 of column g = c16;
-//  - value product O^T[ch, g] += V^T[ch, tokens] · P^T[tokens, g]: A = value
+//  - value product O^T[ch, g] += V^T[ch, tokens] · P'^T[tokens, g]: A = value
 //    words (row c16 <-> channel 4*c16 + db%4 + 64*(db/4) for block db), B =
-//    the lane's own probabilities; the output column is again g = c16, so the
-//    softmax state (m, l) of column g lives in the lanes that hold its O.
-// Contraction slots follow the nibble order of nib8_h8 on both operands.
+//    the lane's own weights; the output column is again g = c16, so the
+//    softmax state of column g lives in the lanes that hold its O.
+// Contraction slots follow the nibble order 0, 4, 1, 5, 2, 6, 3, 7 on both
+// operands.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void
+k_attn_partial(AttnArgs a) {
     __shared__ float so[kWaves][kGMax][kHd];
     __shared__ float sm[kWaves][kGMax];
     __shared__ float sl[kWaves][kGMax];
@@ -94,30 +97,49 @@ __global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
     const int c16 = lane & 15;
     const int q4 = lane >> 4;
     const size_t bh = static_cast<size_t>(b) * a.heads_kv + hk;
-    const float* ksc = a.k_scale + bh * a.max_seq;
-    const float* vsc = a.v_scale + bh * a.max_seq;
+    const float* ksc = a.k_scale + bh * a.max_seq + 8 * q4;
+    const float* vsc = a.v_scale + bh * a.max_seq + 8 * q4;
+    const int tau0 = 8 * (c16 >> 2) + (c16 & 3);      // key row of product s: tau0 + 4 s
+    const uint8_t* kbase = a.k_cache + (bh * a.max_seq + tau0) * (kHd / 2) + 16 * q4;
+    const uint32_t* vbase = a.v_cache + (bh * (a.max_seq / 8) + q4) * kHd + 4 * c16;
 
-    // chunk-wide power of two that brings the value scales below 2
+    // Tile data is loaded one operand at a time: each operand's registers
+    // take the next tile's load as soon as the current tile has consumed them,
+    // so the loads of tile n+1 overlap the rest of tile n without a second
+    // register set.
+    auto kptr = [&](int t) { return kbase + static_cast<size_t>(t) * (kHd / 2); };
+    auto vptr = [&](int t) { return vbase + static_cast<size_t>(t / 8) * kHd; };
+
+    int t0 = t_begin + 32 * w;
+    const int tf = t0 < t_end ? t0 : t_begin;  // first tile, in flight during the setup
+    uint4 k0 = *reinterpret_cast<const uint4*>(kptr(tf));
+    uint4 k1 = *reinterpret_cast<const uint4*>(kptr(tf) + 4 * (kHd / 2));
+    float4 sk0 = *reinterpret_cast<const float4*>(ksc + tf);
+    float4 sk1 = *reinterpret_cast<const float4*>(ksc + tf + 4);
+    float4 sv0 = *reinterpret_cast<const float4*>(vsc + tf);
+    float4 sv1 = *reinterpret_cast<const float4*>(vsc + tf + 4);
+    uint4 v0 = *reinterpret_cast<const uint4*>(vptr(tf));
+    uint4 v1 = *reinterpret_cast<const uint4*>(vptr(tf) + 64);
+
+    // chunk-wide power of two that brings the value scales into (0, 2)
     float vm = 0.0f;
-    for (int t = t_begin + tid; t < t_end; t += kThreads) vm = fmaxf(vm, fabsf(vsc[t]));
-    vm = wave_max(vm);
-    if (lane == 0) svmax[w] = vm;
-    __syncthreads();
-    vm = fmaxf(fmaxf(svmax[0], svmax[1]), fmaxf(svmax[2], svmax[3]));
-    const int ev = vm > 0.0f ? ilog2f(vm) : 0;
-    const float fv = pow2i(-ev);
+    {
+        const float* vs0 = a.v_scale + bh * a.max_seq;
+        for (int t = t_begin + tid; t < t_end; t += kThreads) vm = fmaxf(vm, fabsf(vs0[t]));
+    }
 
-    // q~ of column g = c16 as hi/lo fp16 B operands, scaled by a per-column
+    // q~ of column g = c16 as fp16 hi/lo B operands, scaled by a per-column
     // power of two into [1, 2)
     const int g = c16;
     const bool gval = g < G;
-    const float* qrow = a.qt + (static_cast<size_t>(b) * a.heads_q + hk * G + (gval ? g : 0)) * kHd;
+    const float* qrow =
+        a.qt + (static_cast<size_t>(b) * a.heads_q + hk * G + (gval ? g : 0)) * kHd + 32 * q4;
     float qv[4][8];
     float qmax = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * q4 + 8 * ks);
-        const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * q4 + 8 * ks + 4);
+        const float4 x0 = *reinterpret_cast<const float4*>(qrow + 8 * ks);
+        const float4 x1 = *reinterpret_cast<const float4*>(qrow + 8 * ks + 4);
         const float e8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         constexpr int nu[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
@@ -128,40 +150,37 @@ __global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
     }
     qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
     qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+    vm = wave_max(vm);
+    if (lane == 0) svmax[w] = vm;
     const int eq = qmax > 0.0f ? ilog2f(qmax) : 0;
     const float fq = pow2i(-eq);
-    const float uq = pow2i(eq);
+    const float uq = pow2i(eq - 4);         // the slot factor 16 comes off here
     v8h qh[4], ql[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            _Float16 h, l;
-            split_h(qv[ks][j] * fq, h, l);
-            qh[ks][j] = h;
-            ql[ks][j] = l;
+            const F16Pair hl = split_f16(qv[ks][j] * (fq * kSlotScale[j]));
+            qh[ks][j] = hl.hi;
+            ql[ks][j] = hl.lo;
         }
 
+    __syncthreads();
+    vm = fmaxf(fmaxf(svmax[0], svmax[1]), fmaxf(svmax[2], svmax[3]));
+    const int ev = vm > 0.0f ? ilog2f(vm) : 0;
+    const float fv = pow2i(-ev);
+    const float fv16 = pow2i(4 - ev);       // with the slot factor 16 (even i)
+
     float m = -__builtin_inff();
-    float lp = 0.0f;
+    float lp = 0.0f;      // sum of p over the lane's tokens (rescaled with m)
     v4f O[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) O[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int tau0 = 8 * (c16 >> 2) + (c16 & 3);      // key row of product s: tau0 + 4 s
-    const uint8_t* kbase = a.k_cache + (bh * a.max_seq) * (kHd / 2) + 16 * q4;
-    const uint32_t* vbase = a.v_cache + bh * (a.max_seq / 8) * kHd + 4 * c16;
-
-    for (int t0 = t_begin + 32 * w; t0 < t_end; t0 += 32 * kWaves) {
-        const uint4 k0 = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0 + tau0) * (kHd / 2));
-        const uint4 k1 = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0 + tau0 + 4) * (kHd / 2));
-        const uint32_t* vb = vbase + static_cast<size_t>(t0 / 8 + q4) * kHd;
-        const uint4 v0 = *reinterpret_cast<const uint4*>(vb);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(vb + 64);
-        const float4 sk0 = *reinterpret_cast<const float4*>(ksc + t0 + 8 * q4);
-        const float4 sk1 = *reinterpret_cast<const float4*>(ksc + t0 + 8 * q4 + 4);
-        const float4 sv0 = *reinterpret_cast<const float4*>(vsc + t0 + 8 * q4);
-        const float4 sv1 = *reinterpret_cast<const float4*>(vsc + t0 + 8 * q4 + 4);
+    // one 32-token tile; MASK: the tile crosses t_end (only the last one can)
+    auto tile = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int tn = t0 + 32 * kWaves < t_end ? t0 + 32 * kWaves : t0;   // next (or again)
 
         // scores
         const uint32_t kw[2][4] = {{k0.x, k0.y, k0.z, k0.w}, {k1.x, k1.y, k1.z, k1.w}};
@@ -171,60 +190,73 @@ __global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
             acc[s] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const v8h ka = nib8_h8(kw[s][ks]);
+                const v8h ka = nib8_h8x16(kw[s][ks]);
                 acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[ks], acc[s], 0, 0, 0);
                 acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql[ks], acc[s], 0, 0, 0);
             }
         }
+        k0 = *reinterpret_cast<const uint4*>(kptr(tn));
+        k1 = *reinterpret_cast<const uint4*>(kptr(tn) + 4 * (kHd / 2));
         const float skv[2][4] = {{sk0.x, sk0.y, sk0.z, sk0.w}, {sk1.x, sk1.y, sk1.z, sk1.w}};
-        const float svv[2][4] = {{sv0.x, sv0.y, sv0.z, sv0.w}, {sv1.x, sv1.y, sv1.z, sv1.w}};
+        const int nval = t_end - t0 - 8 * q4;          // lane's tokens below t_end
         float x[2][4];
         float mx = -__builtin_inff();
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = t0 + 8 * q4 + 4 * s + i < t_end;
-                x[s][i] = ok ? acc[s][i] * uq * skv[s][i] : -__builtin_inff();
+                x[s][i] = acc[s][i] * (uq * skv[s][i]);
+                if (MASK && !(4 * s + i < nval)) x[s][i] = -__builtin_inff();
                 mx = fmaxf(mx, x[s][i]);
             }
+        sk0 = *reinterpret_cast<const float4*>(ksc + tn);
+        sk1 = *reinterpret_cast<const float4*>(ksc + tn + 4);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx);
-        if (__any(mn > m)) {
+        if (__any(mx > m + 10.0f)) {
+            const float mn = fmaxf(m, mx);
             const float al = __builtin_amdgcn_exp2f(m - mn);
             lp *= al;
 #pragma unroll
             for (int db = 0; db < 8; ++db) O[db] *= al;
             m = mn;
         }
-        // probabilities (times the value scale) as hi/lo B operands
+        // weights p' = p * s_v * 2^-ev (times the slot factor) as fp16 hi/lo
+        const float svv[2][4] = {{sv0.x, sv0.y, sv0.z, sv0.w}, {sv1.x, sv1.y, sv1.z, sv1.w}};
         v8h ph, pl;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const bool ok = t0 + 8 * q4 + 4 * s + i < t_end;
                 const float p = __builtin_amdgcn_exp2f(x[s][i] - m);
                 lp += p;
-                const float pv = ok ? p * svv[s][i] * fv : 0.0f;
-                _Float16 h, l;
-                split_h(pv, h, l);
-                ph[2 * i + s] = h;
-                pl[2 * i + s] = l;
+                float pv = p * (svv[s][i] * (i & 1 ? fv : fv16));
+                // past t_end the scale may be anything: the weight is zero
+                if (MASK && !(4 * s + i < nval)) pv = 0.0f;
+                const F16Pair hl = split_f16(pv);
+                ph[2 * i + s] = hl.hi;
+                pl[2 * i + s] = hl.lo;
             }
+        sv0 = *reinterpret_cast<const float4*>(vsc + tn);
+        sv1 = *reinterpret_cast<const float4*>(vsc + tn + 4);
         const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            const v8h va = nib8_h8(vw[db]);
+            const v8h va = nib8_h8x16(vw[db]);
             O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, O[db], 0, 0, 0);
             O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl, O[db], 0, 0, 0);
         }
-    }
+        v0 = *reinterpret_cast<const uint4*>(vptr(tn));
+        v1 = *reinterpret_cast<const uint4*>(vptr(tn) + 64);
+    };
+    for (; t0 + 32 <= t_end; t0 += 32 * kWaves) tile(std::false_type{});
+    if (t0 < t_end) tile(std::true_type{});
 
-    // merge the four waves' states in LDS
+    // column totals over the four lane groups; the chunk's value scale
+    // exponent goes back in here (a power of two, exact)
     lp += __shfl_xor(lp, 16);
     lp += __shfl_xor(lp, 32);
+    const float unv = pow2i(ev - 4);
     if (q4 == 0) {
         sm[w][c16] = m;
         sl[w][c16] = lp;
@@ -233,11 +265,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
     for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            so[w][c16][16 * q4 + 4 * i + (db & 3) + 64 * (db >> 2)] = O[db][i];
+            so[w][c16][16 * q4 + 4 * i + (db & 3) + 64 * (db >> 2)] = O[db][i] * unv;
     __syncthreads();
+    // merge the four waves
     const int nch = (a.max_seq + C - 1) / C;
     float* rec = a.part + ((bh * nch) + c) * static_cast<size_t>(G) * (kHd + 2);
-    const float unv = pow2i(ev);
     for (int it = tid; it < G * kHd; it += kThreads) {
         const int gg = it / kHd;
         const int d = it % kHd;
@@ -251,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
             o += f * so[ww][gg][d];
             l += f * sl[ww][gg];
         }
-        rec[2 * G + gg * kHd + d] = o * unv;
+        rec[2 * G + gg * kHd + d] = o;
         if (d == 0) {
             rec[gg] = M;
             rec[G + gg] = l;
@@ -260,9 +292,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_partial(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge the chunk records of one (sequence, KV head); fp16 output.
+// Merge the chunk records of one (sequence, KV head); fp16 output.  The
+// chunk weights exp2(m_c - M) / sum_c l_c exp2(m_c - M) are formed once per
+// head in LDS, then every output element is one weighted sum whose loads are
+// independent.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_attn_combine(AttnArgs a) {
+    __shared__ float wgt[kGMax][64];
     const int hk = blockIdx.x;
     const int b = blockIdx.y;
     const int C = a.chunk;
@@ -272,26 +308,48 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(AttnArgs a) {
     const int nc = (L + C - 1) / C;
     const int nch = (a.max_seq + C - 1) / C;
     const size_t bh = static_cast<size_t>(b) * a.heads_kv + hk;
-    const float* rec0 = a.part + bh * nch * static_cast<size_t>(G) * (kHd + 2);
     const size_t rs = static_cast<size_t>(G) * (kHd + 2);
+    const float* rec0 = a.part + bh * nch * rs;
     uint16_t* out = a.out + (static_cast<size_t>(b) * a.heads_q + hk * G) * kHd;
-    for (int it = threadIdx.x; it < G * kHd; it += kThreads) {
+    const int tid = threadIdx.x;
+    if (nc <= 64) {
+        // weights: one wave per head, one lane per chunk
+        const int lane = tid & 63;
+        for (int gg = tid >> 6; gg < G; gg += kWaves) {
+            const float mc = lane < nc ? rec0[lane * rs + gg] : -__builtin_inff();
+            const float lc = lane < nc ? rec0[lane * rs + G + gg] : 0.0f;
+            const float M = wave_max(mc);
+            const float f = lane < nc ? __builtin_amdgcn_exp2f(mc - M) : 0.0f;
+            float den = f * lc;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+            wgt[gg][lane] = den > 0.0f ? f / den : 0.0f;
+        }
+        __syncthreads();
+        for (int it = tid; it < G * kHd; it += kThreads) {
+            const int gg = it / kHd;
+            const int d = it % kHd;
+            float r = 0.0f;
+#pragma unroll 8
+            for (int cc = 0; cc < nc; ++cc) r += wgt[gg][cc] * rec0[cc * rs + 2 * G + gg * kHd + d];
+            out[it] = f2h(r);
+        }
+        return;
+    }
+    // long contexts (more than 64 chunks): two passes per element
+    for (int it = tid; it < G * kHd; it += kThreads) {
         const int gg = it / kHd;
         const int d = it % kHd;
-        float r = 0.0f;
-        if (nc > 0) {
-            float M = -__builtin_inff();
-            for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, rec0[cc * rs + gg]);
-            float num = 0.0f, den = 0.0f;
-            for (int cc = 0; cc < nc; ++cc) {
-                const float* rc = rec0 + cc * rs;
-                const float f = __builtin_amdgcn_exp2f(rc[gg] - M);
-                num += f * rc[2 * G + gg * kHd + d];
-                den += f * rc[G + gg];
-            }
-            r = num / den;
+        float M = -__builtin_inff();
+        for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, rec0[cc * rs + gg]);
+        float num = 0.0f, den = 0.0f;
+        for (int cc = 0; cc < nc; ++cc) {
+            const float* rc = rec0 + cc * rs;
+            const float f = __builtin_amdgcn_exp2f(rc[gg] - M);
+            num += f * rc[2 * G + gg * kHd + d];
+            den += f * rc[G + gg];
         }
-        out[it] = f2h(r);
+        out[it] = f2h(nc > 0 ? num / den : 0.0f);
     }
 }
 

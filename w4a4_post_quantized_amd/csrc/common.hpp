@@ -144,6 +144,21 @@ __device__ __forceinline__ uint32_t quant_nibble_magic(float z, float inv_s) {
     return __float_as_uint(t + 12582912.0f) & 0xFu;
 }
 
+// x = hi + lo in fp16 for MFMA operands.  hi is x with its float mantissa
+// cut to fp16's 11 significant bits, so the conversion of hi to fp16 is exact
+// (for |x| in fp16's normal range) whatever instruction and rounding the
+// compiler picks for it; the packed and the scalar fp16 conversions have
+// been seen to round a value very close to a rounding tie differently, and a
+// hi converted twice must be the same number in both places.  lo = x - hi is
+// exact in fp32 (at most 13 bits) and rounds once: |x - hi - lo| <= 2^-22 |x|.
+struct F16Pair {
+    _Float16 hi, lo;
+};
+__device__ __forceinline__ F16Pair split_f16(float x) {
+    const float h = __uint_as_float(__float_as_uint(x) & 0xFFFFE000u);
+    return {static_cast<_Float16>(h), static_cast<_Float16>(x - h)};
+}
+
 // floor(log2(x)) for a positive normal float
 __device__ __forceinline__ int ilog2f(float x) {
     return static_cast<int>((__float_as_uint(x) >> 23) & 0xFFu) - 127;

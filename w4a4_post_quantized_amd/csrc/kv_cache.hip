@@ -87,11 +87,57 @@ __device__ bool find_unit(const KvAppendArgs& a, int u, int* seg, int* tile) {
 }
 
 // ---------------------------------------------------------------------------
+// Z[r][:] = xs[r][:] · Pm for r < rows (rows <= 32), in place, fp32.  Thread:
+// column e = tid % 128 and half dh = tid / 128 of the contraction.  The
+// thread's 64 matrix entries are loaded at once (all in flight) and reused by
+// every row; the two halves are added through LDS.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rows_times(float (*xs)[kHd], int rows,
+                                           const float* __restrict__ Pm) {
+    const int tid = threadIdx.x;
+    const int e = tid & (kHd - 1);
+    const int dh = tid >> 7;
+    float p[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) p[i] = Pm[(64 * dh + i) * kHd + e];
+    float acc[kTile];
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+        acc[r] = 0.0f;
+        if (r < rows) {
+            const float4* xr = reinterpret_cast<const float4*>(&xs[r][64 * dh]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float4 x = xr[j];
+                acc[r] = fmaf(x.x, p[4 * j], acc[r]);
+                acc[r] = fmaf(x.y, p[4 * j + 1], acc[r]);
+                acc[r] = fmaf(x.z, p[4 * j + 2], acc[r]);
+                acc[r] = fmaf(x.w, p[4 * j + 3], acc[r]);
+            }
+        }
+    }
+    __syncthreads();
+    if (dh == 1) {
+#pragma unroll
+        for (int r = 0; r < kTile; ++r)
+            if (r < rows) xs[r][e] = acc[r];
+    }
+    __syncthreads();
+    if (dh == 0) {
+#pragma unroll
+        for (int r = 0; r < kTile; ++r)
+            if (r < rows) xs[r][e] += acc[r];
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // One workgroup: one 32-position tile of one segment, heads
 // [blockIdx.y * hpw, +hpw), keys (blockIdx.z == 0) or values (== 1).
 // Rows (position, head) are processed in batches of at most 32, each batch
 // holding whole heads so that a value word's 8 tokens are written together.
-// The transform runs in fp32 (fp16 inputs are exact in fp32).
+// The transform runs in fp32 (fp16 inputs are exact in fp32).  The LDS
+// holds the batch's inputs, then its Z, then its codes.
 // ---------------------------------------------------------------------------
 template <bool PER_HEAD>
 __global__ __launch_bounds__(kThreads) void k_kv_append(KvAppendArgs a) {
@@ -113,7 +159,9 @@ __global__ __launch_bounds__(kThreads) void k_kv_append(KvAppendArgs a) {
     const int h0 = blockIdx.y * a.hpw;
     const int nh = min(a.hpw, a.heads - h0);
     if (nh <= 0) return;
-    const int hpb = max(1, min(nh, kTile / npos));  // heads per batch
+    // heads per batch: with per-head matrices one head, so that the rows of a
+    // batch share their matrix
+    const int hpb = PER_HEAD ? 1 : max(1, min(nh, kTile / npos));
     const int H = a.heads;
 
     for (int hb = 0; hb < nh; hb += hpb) {
@@ -135,37 +183,8 @@ __global__ __launch_bounds__(kThreads) void k_kv_append(KvAppendArgs a) {
             }
         }
         __syncthreads();
-        // Z[r][e] = sum_d X[r][d] * P[d][e]; thread: column e, rows rb + 2k
-        const int e = tid & (kHd - 1);
-        const int rb = tid >> 7;
-        float acc[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-        if (!PER_HEAD) {
-            for (int d = 0; d < kHd; ++d) {
-                const float pv = P[d * kHd + e];
-#pragma unroll
-                for (int k = 0; k < 16; ++k)
-                    if (rb + 2 * k < rows) acc[k] = fmaf(xs[rb + 2 * k][d], pv, acc[k]);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int r = rb + 2 * k;
-                if (r < rows) {
-                    const float* Pr =
-                        P + static_cast<size_t>(h0 + hb + r / npos) * kHd * kHd + e;
-                    float t = 0.0f;
-                    for (int d = 0; d < kHd; ++d) t = fmaf(xs[r][d], Pr[d * kHd], t);
-                    acc[k] = t;
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            if (rb + 2 * k < rows) xs[rb + 2 * k][e] = acc[k];
-        __syncthreads();
+        // Z = X · P of the batch's head (every row of a batch shares it)
+        rows_times(xs, rows, P + (PER_HEAD ? static_cast<size_t>(h0 + hb) * kHd * kHd : 0));
         // quantize: one wave per row, two channels per lane
         const int lane = tid & 63;
         const int wv = tid >> 6;
@@ -232,37 +251,25 @@ __global__ __launch_bounds__(kThreads) void k_kv_append(KvAppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Rows y[r] = scale * x[r] · M for G rows sharing one matrix (query heads of
-// one KV head): fp32 out.  One workgroup per (sequence, KV head).
+// y[h] = scale * q[h] · M for the query heads [blockIdx.x * rw, +rw) of
+// sequence blockIdx.y, fp32 out.  rw = G with per-head matrices (the heads of
+// one KV head), else up to 8 heads sharing the one matrix.
 // ---------------------------------------------------------------------------
 template <bool PER_HEAD>
 __global__ __launch_bounds__(kThreads) void k_rows_xform(const uint16_t* __restrict__ q,
-                                                         int heads_q, int G,
+                                                         int heads_q, int G, int rw,
                                                          const float* __restrict__ M,
                                                          float scale, float* __restrict__ out) {
-    __shared__ float qs[16][kHd];
-    const int hk = blockIdx.x;
+    __shared__ float xs[kTile][kHd];
+    const int h0 = blockIdx.x * rw;
+    const int rows = min(rw, heads_q - h0);
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
-    const size_t row0 = static_cast<size_t>(b) * heads_q + static_cast<size_t>(hk) * G;
-    for (int c = tid; c < G * kHd; c += kThreads)
-        qs[c / kHd][c % kHd] = h2f(q[row0 * kHd + c]);
+    const size_t row0 = static_cast<size_t>(b) * heads_q + h0;
+    for (int c = tid; c < rows * kHd; c += kThreads) xs[c / kHd][c % kHd] = h2f(q[row0 * kHd + c]);
     __syncthreads();
-    const float* Mh = M + (PER_HEAD ? static_cast<size_t>(hk) * kHd * kHd : 0);
-    const int e = tid & (kHd - 1);
-    const int rb = tid >> 7;
-    float acc[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-    for (int d = 0; d < kHd; ++d) {
-        const float mv = Mh[d * kHd + e];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (rb + 2 * k < G) acc[k] = fmaf(qs[rb + 2 * k][d], mv, acc[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        if (rb + 2 * k < G) out[(row0 + rb + 2 * k) * kHd + e] = acc[k] * scale;
+    rows_times(xs, rows, M + (PER_HEAD ? static_cast<size_t>(h0 / G) * kHd * kHd : 0));
+    for (int c = tid; c < rows * kHd; c += kThreads) out[row0 * kHd + c] = xs[c / kHd][c % kHd] * scale;
 }
 
 }  // namespace
@@ -288,12 +295,15 @@ hipError_t rows_xform_launch(const uint16_t* q, int batch, int heads_q, int head
                              const float* M, bool per_head, float scale, float* out,
                              hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    dim3 grid(heads_kv, batch);
     const int G = heads_q / heads_kv;
+    // 8 heads per workgroup (one KV head's G with per-head matrices): enough
+    // workgroups to cover the chip for decode batches
+    const int rw = per_head ? G : min(heads_q, 8);
+    dim3 grid(ceil_div(heads_q, rw), batch);
     if (per_head)
-        k_rows_xform<true><<<grid, kThreads, 0, stream>>>(q, heads_q, G, M, scale, out);
+        k_rows_xform<true><<<grid, kThreads, 0, stream>>>(q, heads_q, G, rw, M, scale, out);
     else
-        k_rows_xform<false><<<grid, kThreads, 0, stream>>>(q, heads_q, G, M, scale, out);
+        k_rows_xform<false><<<grid, kThreads, 0, stream>>>(q, heads_q, G, rw, M, scale, out);
     return hipGetLastError();
 }
 

@@ -215,9 +215,11 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
                     const int col = 4 * c4 + q;
                     const int off = (sk * 64 + gg * 16 + col) * 8 + e;
                     const float v = ldexpf(vv[q], e1);
-                    const _Float16 h = static_cast<_Float16>(v);
-                    p1hi[off] = h;
-                    p1lo[off] = static_cast<_Float16>(v - static_cast<float>(h));
+                    {
+                        const F16Pair hl = split_f16(v);
+                        p1hi[off] = hl.hi;
+                        p1lo[off] = hl.lo;
+                    }
                 }
             }
         }
@@ -237,9 +239,11 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float v = ldexpf(p2v[ks][e], e2);
-                const _Float16 h = static_cast<_Float16>(v);
-                p2hi[ks][e] = h;
-                p2lo[ks][e] = static_cast<_Float16>(v - static_cast<float>(h));
+                {
+                    const F16Pair hl = split_f16(v);
+                    p2hi[ks][e] = hl.hi;
+                    p2lo[ks][e] = hl.lo;
+                }
             }
 
         // stage 1: T[:, cb] = X̄ · P2'[:, cb]
@@ -270,9 +274,11 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
             for (int e = 0; e < 8; ++e) {
                 const int rb = 2 * sk + (e >> 2);
                 const float v = ldexpf(T[rb][e & 3], et);
-                const _Float16 h = static_cast<_Float16>(v);
-                bh[sk][e] = h;
-                bl[sk][e] = static_cast<_Float16>(v - static_cast<float>(h));
+                {
+                    const F16Pair hl = split_f16(v);
+                    bh[sk][e] = hl.hi;
+                    bl[sk][e] = hl.lo;
+                }
             }
         // stage 2: rows 16 part .. 16 part + 15 of Z, columns of block cb
         v4f z = {0.0f, 0.0f, 0.0f, 0.0f};

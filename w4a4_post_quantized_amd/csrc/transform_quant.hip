@@ -255,9 +255,11 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
         const int gg = ln >> 4, ii = ln & 15;
         const int rho = 32 * sk + (e < 4 ? 4 * gg + e : 16 + 4 * gg + (e - 4));
         const float v = rho < N1 ? ldexpf(P1[rho * N1 + 16 * ob + ii], e1) : 0.0f;
-        const _Float16 h = static_cast<_Float16>(v);
-        p1hi[idx] = h;
-        p1lo[idx] = static_cast<_Float16>(v - static_cast<float>(h));
+        {
+            const F16Pair hl = split_f16(v);
+            p1hi[idx] = hl.hi;
+            p1lo[idx] = hl.lo;
+        }
     }
 
     // ---- P2 fragments (stage-1 B operand) of this wave's 16 columns ---------
@@ -270,9 +272,11 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
         for (int e = 0; e < 8; ++e) {
             const int kk = 32 * ks + 8 * g + e;
             const float v = kk < N2 ? ldexpf(P2[kk * N2 + 16 * cb + li], e2) : 0.0f;
-            const _Float16 h = static_cast<_Float16>(v);
-            p2hi[ks][e] = h;
-            p2lo[ks][e] = static_cast<_Float16>(v - static_cast<float>(h));
+            {
+                const F16Pair hl = split_f16(v);
+                p2hi[ks][e] = hl.hi;
+                p2lo[ks][e] = hl.lo;
+            }
         }
     }
     // ---- X̄ tiles: HBM -> registers (next tile) -> LDS (double buffer) --------
@@ -351,9 +355,11 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
                 for (int e = 0; e < 8; ++e) {
                     const int rb = 2 * sk + (e >> 2);
                     const float v = rb < C::RB ? ldexpf(T[rb < C::RB ? rb : 0][e & 3], et) : 0.0f;
-                    const _Float16 h = static_cast<_Float16>(v);
-                    bh[sk][e] = h;
-                    bl[sk][e] = static_cast<_Float16>(v - static_cast<float>(h));
+                    {
+                        const F16Pair hl = split_f16(v);
+                        bh[sk][e] = hl.hi;
+                        bl[sk][e] = hl.lo;
+                    }
                 }
             }
             // stage 2: Z[:, cb] = P1'^T · T'[:, cb]
@@ -627,9 +633,11 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
         const int idx = tid + i * NT;
         if (idx < C::P2F) {
             const float v = ldexpf(v2[i], e2);
-            const _Float16 h = static_cast<_Float16>(v);
-            p2hi[idx] = h;
-            p2lo[idx] = static_cast<_Float16>(v - static_cast<float>(h));
+            {
+                const F16Pair hl = split_f16(v);
+                p2hi[idx] = hl.hi;
+                p2lo[idx] = hl.lo;
+            }
         }
     }
 #pragma unroll
@@ -637,9 +645,11 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
         const int idx = tid + i * NT;
         if (idx < C::P1F) {
             const float v = ldexpf(v1[i], e1);
-            const _Float16 h = static_cast<_Float16>(v);
-            p1hi[idx] = h;
-            p1lo[idx] = static_cast<_Float16>(v - static_cast<float>(h));
+            {
+                const F16Pair hl = split_f16(v);
+                p1hi[idx] = hl.hi;
+                p1lo[idx] = hl.lo;
+            }
         }
     }
 #pragma unroll
@@ -704,9 +714,11 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
                 for (int e = 0; e < 8; ++e) {
                     const int rb = 2 * sk + (e >> 2);
                     const float v = rb < C::RB ? ldexpf(T[rb < C::RB ? rb : 0][cb][e & 3], et) : 0.0f;
-                    const _Float16 h = static_cast<_Float16>(v);
-                    ah[sk][cb][e] = h;
-                    al[sk][cb][e] = static_cast<_Float16>(v - static_cast<float>(h));
+                    {
+                        const F16Pair hl = split_f16(v);
+                        ah[sk][cb][e] = hl.hi;
+                        al[sk][cb][e] = hl.lo;
+                    }
                 }
         // stage 2: Zᵀ = T'ᵀ · P1'  (tile (cb, ob): rows j, columns i)
         v4f Z[C::RB][C::CB];
@@ -1003,9 +1015,11 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
                 const int f = (col >> 4) * C::KS2 + sk;
                 const int off = (f * 64 + gg * 16 + (col & 15)) * 8 + e;
                 const float v = ldexpf(vv[q], e1);
-                const _Float16 h = static_cast<_Float16>(v);
-                p1hi[off] = h;
-                p1lo[off] = static_cast<_Float16>(v - static_cast<float>(h));
+                {
+                    const F16Pair hl = split_f16(v);
+                    p1hi[off] = hl.hi;
+                    p1lo[off] = hl.lo;
+                }
             }
         }
     }
@@ -1025,9 +1039,11 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float v = ldexpf(p2v[ks][e], e2);
-            const _Float16 h = static_cast<_Float16>(v);
-            p2hi[ks][e] = h;
-            p2lo[ks][e] = static_cast<_Float16>(v - static_cast<float>(h));
+            {
+                const F16Pair hl = split_f16(v);
+                p2hi[ks][e] = hl.hi;
+                p2lo[ks][e] = hl.lo;
+            }
         }
 
     // ---- stage 1: T[:, cb] = X̄ · P2'[:, cb] ----------------------------------
@@ -1058,9 +1074,11 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
         for (int e = 0; e < 8; ++e) {
             const int rb = 2 * sk + (e >> 2);
             const float v = rb < C::RB ? ldexpf(T[rb < C::RB ? rb : 0][e & 3], et) : 0.0f;
-            const _Float16 h = static_cast<_Float16>(v);
-            bh[sk][e] = h;
-            bl[sk][e] = static_cast<_Float16>(v - static_cast<float>(h));
+            {
+                const F16Pair hl = split_f16(v);
+                bh[sk][e] = hl.hi;
+                bl[sk][e] = hl.lo;
+            }
         }
 
     // ---- stage 2 for this part's row blocks ----------------------------------
