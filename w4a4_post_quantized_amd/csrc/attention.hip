@@ -74,9 +74,11 @@ __device__ __forceinline__ float pow2i(int e) { return __builtin_ldexpf(1.0f, e)
 // Contraction slots follow the nibble order 0, 4, 1, 5, 2, 6, 3, 7 on both
 // operands.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 k_attn_partial(AttnArgs a) {
-    __shared__ float so[kWaves][kGMax][kHd];
+    // dynamic LDS: the q~ operands during the tile loop, then the waves' O
+    // rows g < G for the merge (attn_partial_lds bytes)
+    extern __shared__ __align__(16) uint8_t dyn[];
     __shared__ float sm[kWaves][kGMax];
     __shared__ float sl[kWaves][kGMax];
     __shared__ float svmax[kWaves];
@@ -155,15 +157,23 @@ k_attn_partial(AttnArgs a) {
     const int eq = qmax > 0.0f ? ilog2f(qmax) : 0;
     const float fq = pow2i(-eq);
     const float uq = pow2i(eq - 4);         // the slot factor 16 comes off here
-    v8h qh[4], ql[4];
+    // the B operands live in LDS (one copy per workgroup, read per tile), not
+    // in 32 registers per lane: that keeps the kernel at four waves per SIMD
+    v8h (*sq)[4][64] = reinterpret_cast<v8h (*)[4][64]>(dyn);
+    if (w == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) {
+            v8h hv, lv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const F16Pair hl = split_f16(qv[ks][j] * (fq * kSlotScale[j]));
-            qh[ks][j] = hl.hi;
-            ql[ks][j] = hl.lo;
+            for (int j = 0; j < 8; ++j) {
+                const F16Pair hl = split_f16(qv[ks][j] * (fq * kSlotScale[j]));
+                hv[j] = hl.hi;
+                lv[j] = hl.lo;
+            }
+            sq[0][ks][lane] = hv;
+            sq[1][ks][lane] = lv;
         }
+    }
 
     __syncthreads();
     vm = fmaxf(fmaxf(svmax[0], svmax[1]), fmaxf(svmax[2], svmax[3]));
@@ -182,7 +192,14 @@ k_attn_partial(AttnArgs a) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int tn = t0 + 32 * kWaves < t_end ? t0 + 32 * kWaves : t0;   // next (or again)
 
-        // scores
+        // scores; the compiler barrier keeps the q~ operand reads inside the loop
+        __asm__ volatile("" ::: "memory");
+        v8h qh[4], ql[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            qh[ks] = sq[0][ks][lane];
+            ql[ks] = sq[1][ks][lane];
+        }
         const uint32_t kw[2][4] = {{k0.x, k0.y, k0.z, k0.w}, {k1.x, k1.y, k1.z, k1.w}};
         v4f acc[2];
 #pragma unroll
@@ -261,11 +278,16 @@ k_attn_partial(AttnArgs a) {
         sm[w][c16] = m;
         sl[w][c16] = lp;
     }
+    __syncthreads();                         // every wave is done with sq
+    float* so = reinterpret_cast<float*>(dyn);     // [kWaves][G][kHd]
+    if (c16 < G) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            so[w][c16][16 * q4 + 4 * i + (db & 3) + 64 * (db >> 2)] = O[db][i] * unv;
+            for (int i = 0; i < 4; ++i)
+                so[(w * G + c16) * kHd + 16 * q4 + 4 * i + (db & 3) + 64 * (db >> 2)] =
+                    O[db][i] * unv;
+    }
     __syncthreads();
     // merge the four waves
     const int nch = (a.max_seq + C - 1) / C;
@@ -280,7 +302,7 @@ k_attn_partial(AttnArgs a) {
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
             const float f = __builtin_amdgcn_exp2f(sm[ww][gg] - M);
-            o += f * so[ww][gg][d];
+            o += f * so[(ww * G + gg) * kHd + d];
             l += f * sl[ww][gg];
         }
         rec[2 * G + gg * kHd + d] = o;
@@ -292,13 +314,14 @@ k_attn_partial(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge the chunk records of one (sequence, KV head); fp16 output.  The
-// chunk weights exp2(m_c - M) / sum_c l_c exp2(m_c - M) are formed once per
-// head in LDS, then every output element is one weighted sum whose loads are
-// independent.
+// Merge the chunk records of one (sequence, KV head); fp16 output.  A thread
+// owns output elements (g, d); for up to 16 chunks it issues all its loads
+// (m_c, l_c and O_c[g][d] of every chunk) at once, so the merge costs one
+// memory round trip.
 // ---------------------------------------------------------------------------
+constexpr int kCombineFast = 16;
+
 __global__ __launch_bounds__(kThreads) void k_attn_combine(AttnArgs a) {
-    __shared__ float wgt[kGMax][64];
     const int hk = blockIdx.x;
     const int b = blockIdx.y;
     const int C = a.chunk;
@@ -311,49 +334,55 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(AttnArgs a) {
     const size_t rs = static_cast<size_t>(G) * (kHd + 2);
     const float* rec0 = a.part + bh * nch * rs;
     uint16_t* out = a.out + (static_cast<size_t>(b) * a.heads_q + hk * G) * kHd;
-    const int tid = threadIdx.x;
-    if (nc <= 64) {
-        // weights: one wave per head, one lane per chunk
-        const int lane = tid & 63;
-        for (int gg = tid >> 6; gg < G; gg += kWaves) {
-            const float mc = lane < nc ? rec0[lane * rs + gg] : -__builtin_inff();
-            const float lc = lane < nc ? rec0[lane * rs + G + gg] : 0.0f;
-            const float M = wave_max(mc);
-            const float f = lane < nc ? __builtin_amdgcn_exp2f(mc - M) : 0.0f;
-            float den = f * lc;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
-            wgt[gg][lane] = den > 0.0f ? f / den : 0.0f;
-        }
-        __syncthreads();
-        for (int it = tid; it < G * kHd; it += kThreads) {
-            const int gg = it / kHd;
-            const int d = it % kHd;
-            float r = 0.0f;
-#pragma unroll 8
-            for (int cc = 0; cc < nc; ++cc) r += wgt[gg][cc] * rec0[cc * rs + 2 * G + gg * kHd + d];
-            out[it] = f2h(r);
-        }
-        return;
-    }
-    // long contexts (more than 64 chunks): two passes per element
-    for (int it = tid; it < G * kHd; it += kThreads) {
+    for (int it = threadIdx.x; it < G * kHd; it += kThreads) {
         const int gg = it / kHd;
         const int d = it % kHd;
-        float M = -__builtin_inff();
-        for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, rec0[cc * rs + gg]);
-        float num = 0.0f, den = 0.0f;
-        for (int cc = 0; cc < nc; ++cc) {
-            const float* rc = rec0 + cc * rs;
-            const float f = __builtin_amdgcn_exp2f(rc[gg] - M);
-            num += f * rc[2 * G + gg * kHd + d];
-            den += f * rc[G + gg];
+        float r = 0.0f;
+        if (nc > 0 && nc <= kCombineFast) {
+            float mc[kCombineFast], lc[kCombineFast], oc[kCombineFast];
+#pragma unroll
+            for (int cc = 0; cc < kCombineFast; ++cc) {
+                const float* rc = rec0 + (cc < nc ? cc : 0) * rs;
+                mc[cc] = rc[gg];
+                lc[cc] = rc[G + gg];
+                oc[cc] = rc[2 * G + gg * kHd + d];
+            }
+            float M = -__builtin_inff();
+#pragma unroll
+            for (int cc = 0; cc < kCombineFast; ++cc)
+                if (cc < nc) M = fmaxf(M, mc[cc]);
+            float num = 0.0f, den = 0.0f;
+#pragma unroll
+            for (int cc = 0; cc < kCombineFast; ++cc)
+                if (cc < nc) {
+                    const float f = __builtin_amdgcn_exp2f(mc[cc] - M);
+                    num += f * oc[cc];
+                    den += f * lc[cc];
+                }
+            r = num / den;
+        } else if (nc > 0) {
+            float M = -__builtin_inff();
+            for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, rec0[cc * rs + gg]);
+            float num = 0.0f, den = 0.0f;
+            for (int cc = 0; cc < nc; ++cc) {
+                const float* rc = rec0 + cc * rs;
+                const float f = __builtin_amdgcn_exp2f(rc[gg] - M);
+                num += f * rc[2 * G + gg * kHd + d];
+                den += f * rc[G + gg];
+            }
+            r = num / den;
         }
-        out[it] = f2h(nc > 0 ? num / den : 0.0f);
+        out[it] = f2h(r);
     }
 }
 
 }  // namespace
+
+size_t attn_partial_lds(int G) {
+    const size_t q = 2 * 4 * 64 * sizeof(v8h);
+    const size_t o = static_cast<size_t>(kWaves) * G * kHd * sizeof(float);
+    return q > o ? q : o;
+}
 
 int attn_chunk(int batch, int heads_kv, int max_seq) {
     // the largest power of two (<= 1024) that still gives about 8 workgroups
@@ -375,7 +404,8 @@ size_t attn_partial_bytes(int batch, int heads_q, int heads_kv, int max_seq, int
 hipError_t attn_decode_launch(const AttnArgs& a, hipStream_t stream) {
     if (a.batch == 0) return hipSuccess;
     const int nch = (a.max_seq + a.chunk - 1) / a.chunk;
-    k_attn_partial<<<dim3(nch, a.heads_kv, a.batch), kThreads, 0, stream>>>(a);
+    const size_t lds = attn_partial_lds(a.heads_q / a.heads_kv);
+    k_attn_partial<<<dim3(nch, a.heads_kv, a.batch), kThreads, lds, stream>>>(a);
     k_attn_combine<<<dim3(a.heads_kv, a.batch), kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }

@@ -89,17 +89,21 @@ __device__ bool find_unit(const KvAppendArgs& a, int u, int* seg, int* tile) {
 // ---------------------------------------------------------------------------
 // Z[r][:] = xs[r][:] · Pm for r < rows (rows <= 32), in place, fp32.  Thread:
 // column e = tid % 128 and half dh = tid / 128 of the contraction.  The
-// thread's 64 matrix entries are loaded at once (all in flight) and reused by
-// every row; the two halves are added through LDS.
+// thread's 64 matrix entries (pcol_load, issued before the rows are loaded so
+// that the two loads overlap) stay in registers and serve every row; the two
+// halves are added through LDS.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rows_times(float (*xs)[kHd], int rows,
-                                           const float* __restrict__ Pm) {
+__device__ __forceinline__ void pcol_load(const float* __restrict__ Pm, float (&p)[64]) {
+    const int e = threadIdx.x & (kHd - 1);
+    const int dh = threadIdx.x >> 7;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) p[i] = Pm[(64 * dh + i) * kHd + e];
+}
+
+__device__ __forceinline__ void rows_times(float (*xs)[kHd], int rows, const float (&p)[64]) {
     const int tid = threadIdx.x;
     const int e = tid & (kHd - 1);
     const int dh = tid >> 7;
-    float p[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) p[i] = Pm[(64 * dh + i) * kHd + e];
     float acc[kTile];
 #pragma unroll
     for (int r = 0; r < kTile; ++r) {
@@ -164,8 +168,11 @@ __global__ __launch_bounds__(kThreads) void k_kv_append(KvAppendArgs a) {
     const int hpb = PER_HEAD ? 1 : max(1, min(nh, kTile / npos));
     const int H = a.heads;
 
+    float p[64];
+    if (!PER_HEAD) pcol_load(P, p);
     for (int hb = 0; hb < nh; hb += hpb) {
         const int bh = min(hpb, nh - hb);
+        if (PER_HEAD) pcol_load(P + static_cast<size_t>(h0 + hb) * kHd * kHd, p);
         const int rows = bh * npos;                 // row r: head hb + r / npos, position lo + r % npos
         // load the rows (16 halves per thread-iteration)
         for (int c = tid; c < rows * (kHd / 8); c += kThreads) {
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void k_kv_append(KvAppendArgs a) {
         }
         __syncthreads();
         // Z = X · P of the batch's head (every row of a batch shares it)
-        rows_times(xs, rows, P + (PER_HEAD ? static_cast<size_t>(h0 + hb) * kHd * kHd : 0));
+        rows_times(xs, rows, p);
         // quantize: one wave per row, two channels per lane
         const int lane = tid & 63;
         const int wv = tid >> 6;
@@ -266,9 +273,11 @@ __global__ __launch_bounds__(kThreads) void k_rows_xform(const uint16_t* __restr
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const size_t row0 = static_cast<size_t>(b) * heads_q + h0;
+    float p[64];
+    pcol_load(M + (PER_HEAD ? static_cast<size_t>(h0 / G) * kHd * kHd : 0), p);
     for (int c = tid; c < rows * kHd; c += kThreads) xs[c / kHd][c % kHd] = h2f(q[row0 * kHd + c]);
     __syncthreads();
-    rows_times(xs, rows, M + (PER_HEAD ? static_cast<size_t>(h0 / G) * kHd * kHd : 0));
+    rows_times(xs, rows, p);
     for (int c = tid; c < rows * kHd; c += kThreads) out[row0 * kHd + c] = xs[c / kHd][c % kHd] * scale;
 }
 
