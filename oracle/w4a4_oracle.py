@@ -31,7 +31,11 @@ Every step is plain numpy in float64, written from the pages:
   tensor); MergeQuant page, "核心思路" and "关键设计" item 2 (per-channel
   steps migrated into the weights of the linear layer, "QSM").
 
-Readings where the pages are silent or garbled (each restated in the design doc):
+W3A3 (FRM-PTQ page, introduction and its contributions: weights and
+activations at 3 bits) is the same layer with b = 3; the codes are stored one
+per nibble like the 4-bit ones.
+
+Readings where the pages are silent or garbled:
 round half to even; symmetric activations s = α·max|z|/7 with codes clamped to
 [-8, 7]; asymmetric weights with zero-inclusive range, s = (hi-lo)/15 and
 z = clamp(round(-lo/s), 0, 15); weight scales stored in fp16 (direct RNE from
@@ -48,11 +52,21 @@ __all__ = [
     "fp16_rne", "quantize_weights", "int_gemm", "int_gemm_loop",
     "epilogue", "linear", "dequant_act", "dequant_weights",
     "quantize_act_static", "transform_quant_static", "migrate_steps", "linear_static",
-    "calibrate_steps",
+    "calibrate_steps", "code_range",
 ]
 
 QMIN, QMAX = -8, 7          # signed 4-bit code range (b = 4)
 UMAX = 15                   # unsigned 4-bit code range, 2^b - 1
+
+
+def code_range(bits: int):
+    """(qmin, qmax, umax) of b-bit codes: signed [-2^(b-1), 2^(b-1) - 1],
+    unsigned [0, 2^b - 1] (FRM-PTQ page, "初步介绍": the unsigned range of the
+    uniform quantizer is 0 .. 2^b - 1; its introduction evaluates b = 4 and
+    b = 3, W4A4 and W3A3)."""
+    if bits not in (3, 4):
+        raise ValueError("bits must be 3 or 4")
+    return -(1 << (bits - 1)), (1 << (bits - 1)) - 1, (1 << bits) - 1
 
 
 # ----------------------------------------------------------------------------
@@ -94,19 +108,21 @@ def kron_transform(X, P1, P2, c=None):
     return Z.reshape(M, K)
 
 
-def act_scale(Z, alpha_a: float = 1.0):
-    """Per-token symmetric scale s_x[m] = α_a · max_k |Z[m,k]| / 7 (float64).
+def act_scale(Z, alpha_a: float = 1.0, bits: int = 4):
+    """Per-token symmetric scale s_x[m] = α_a · max_k |Z[m,k]| / qmax (float64),
+    qmax = 2^(bits-1) - 1 (7 for INT4, 3 for INT3).
 
     FRM-PTQ page, "初步介绍" (uniform quantizer, here with z = 0 and the
     signed range of b = 4 bits); FlatQuant page, "额外可学习组件" (α_a clips
     the range).
     """
     a = np.max(np.abs(Z), axis=1) if Z.shape[1] else np.zeros(Z.shape[0])
-    return np.float64(alpha_a) * a / 7.0
+    return np.float64(alpha_a) * a / code_range(bits)[1]
 
 
-def quantize_act(Z, s):
-    """q = clamp(round_half_even(Z / s), -8, 7); s == 0 gives q = 0.
+def quantize_act(Z, s, bits: int = 4):
+    """q = clamp(round_half_even(Z / s), qmin, qmax) ([-8, 7] for INT4, [-4, 3]
+    for INT3); s == 0 gives q = 0.
 
     Returns (q int8 [M,K], t float64 [M,K]) where t = Z/s is kept so parity
     checks can find values within a small window of a rounding tie.
@@ -116,19 +132,20 @@ def quantize_act(Z, s):
     safe = np.where(s > 0, s, 1.0)
     t = np.asarray(Z, dtype=np.float64) / safe[:, None]
     t = np.where((s > 0)[:, None], t, 0.0)
-    q = np.clip(np.rint(t), QMIN, QMAX).astype(np.int8)   # np.rint: half to even
+    qmin, qmax, _ = code_range(bits)
+    q = np.clip(np.rint(t), qmin, qmax).astype(np.int8)   # np.rint: half to even
     return q, t
 
 
-def transform_quant(X, P1, P2, c=None, alpha_a: float = 1.0):
+def transform_quant(X, P1, P2, c=None, alpha_a: float = 1.0, bits: int = 4):
     """Online activation path: transform, per-token scale, quantize, pack.
 
     FlatQuant page "高效 Kernel 设计": transform and quantization of one
     token tile in one step.  Returns dict(Z, s_x, q, t, packed).
     """
     Z = kron_transform(X, P1, P2, c)
-    s_x = act_scale(Z, alpha_a)
-    q, t = quantize_act(Z, s_x)
+    s_x = act_scale(Z, alpha_a, bits)
+    q, t = quantize_act(Z, s_x, bits)
     return dict(Z=Z, s_x=s_x, q=q, t=t, packed=pack_nibbles(q))
 
 
@@ -199,17 +216,19 @@ def fp16_rne(x):
     return np.asarray(x, dtype=np.float64).astype(np.float16)
 
 
-def quantize_weights(Wt, group_size: int, asymmetric: bool, alpha_w: float = 1.0):
+def quantize_weights(Wt, group_size: int, asymmetric: bool, alpha_w: float = 1.0,
+                     bits: int = 4):
     """Round-to-nearest INT4 weights, per output channel or per group.
 
     FRM-PTQ page, "初步介绍": Q(W) = clamp(round(W/s) + z, 0, 2^b - 1); the
     introduction's multi-granularity group quantization gives group_size.
     FlatQuant page, "额外可学习组件": α_w clips the range.
 
-    Symmetric: s = fp16(α·max|v| / 7), q = clamp(round(v/s), -8, 7), z = 0.
-    Asymmetric: lo = α·min(min v, 0), hi = α·max(max v, 0),
-    s = fp16((hi - lo)/15), z = clamp(round(-lo/s), 0, 15),
-    u = clamp(round(v/s) + z, 0, 15).  Codes use the stored fp16 scale.
+    Symmetric: s = fp16(α·max|v| / qmax), q = clamp(round(v/s), qmin, qmax),
+    z = 0.  Asymmetric: lo = α·min(min v, 0), hi = α·max(max v, 0),
+    s = fp16((hi - lo)/umax), z = clamp(round(-lo/s), 0, umax),
+    u = clamp(round(v/s) + z, 0, umax).  (qmin, qmax, umax) = (-8, 7, 15) for
+    b = 4 and (-4, 3, 7) for b = 3.  Codes use the stored fp16 scale.
     A stored scale of 0 gives codes 0 and z = 0.
 
     Returns dict(codes int8 [N,K] (signed q, or unsigned u), s fp16 [N,G],
@@ -222,29 +241,30 @@ def quantize_weights(Wt, group_size: int, asymmetric: bool, alpha_w: float = 1.0
     G = K // group_size
     Vg = V.reshape(N, G, group_size)
     a = np.float64(alpha_w)
+    qmin, qmax, umax = code_range(bits)
     if not asymmetric:
-        s16 = fp16_rne(a * np.max(np.abs(Vg), axis=2) / 7.0)
+        s16 = fp16_rne(a * np.max(np.abs(Vg), axis=2) / qmax)
         s = s16.astype(np.float64)
         safe = np.where(s > 0, s, 1.0)
-        q = np.clip(np.rint(Vg / safe[:, :, None]), QMIN, QMAX)
+        q = np.clip(np.rint(Vg / safe[:, :, None]), qmin, qmax)
         q = np.where((s > 0)[:, :, None], q, 0)
         z16 = np.zeros((N, G), dtype=np.float16)
     else:
         lo = a * np.minimum(np.min(Vg, axis=2), 0.0)
         hi = a * np.maximum(np.max(Vg, axis=2), 0.0)
-        s16 = fp16_rne((hi - lo) / 15.0)
+        s16 = fp16_rne((hi - lo) / umax)
         s = s16.astype(np.float64)
         safe = np.where(s > 0, s, 1.0)
-        # z is an integer in [0, 15]; adding +0.0 turns the -0.0 that
+        # z is an integer in [0, umax]; adding +0.0 turns the -0.0 that
         # rint(-0/s) gives for an all-positive group into the integer 0
-        z = np.clip(np.rint(-lo / safe), 0, UMAX) + 0.0
+        z = np.clip(np.rint(-lo / safe), 0, umax) + 0.0
         z = np.where(s > 0, z, 0.0)
-        q = np.clip(np.rint(Vg / safe[:, :, None]) + z[:, :, None], 0, UMAX)
+        q = np.clip(np.rint(Vg / safe[:, :, None]) + z[:, :, None], 0, umax)
         q = np.where((s > 0)[:, :, None], q, 0)
         z16 = z.astype(np.float16)
     codes = q.reshape(N, K).astype(np.int8)
     return dict(codes=codes, s=s16, z=z16, packed=pack_nibbles(codes),
-                group_size=group_size, asymmetric=asymmetric)
+                group_size=group_size, asymmetric=asymmetric, bits=bits)
 
 
 # ----------------------------------------------------------------------------
@@ -320,7 +340,7 @@ def dequant_weights(wq):
     return (c * np.asarray(wq["s"], dtype=np.float64)[:, :, None]).reshape(N, K)
 
 
-def linear(X, P1, P2, wq, c=None, alpha_a: float = 1.0, rows=None, cols=None):
+def linear(X, P1, P2, wq, c=None, alpha_a: float = 1.0, rows=None, cols=None, bits: int = 4):
     """Whole layer: Y64 = epilogue(int_gemm(Q(transform(X)), Q(W̃))).
 
     ``wq`` is the quantize_weights() result of the merged weights.  ``rows`` /
@@ -330,7 +350,7 @@ def linear(X, P1, P2, wq, c=None, alpha_a: float = 1.0, rows=None, cols=None):
     Xs = np.asarray(X)
     if rows is not None:
         Xs = Xs[rows]
-    act = transform_quant(Xs, P1, P2, c, alpha_a)
+    act = transform_quant(Xs, P1, P2, c, alpha_a, bits)
     codes, s, z = wq["codes"], wq["s"], wq["z"]
     if cols is not None:
         codes, s, z = codes[cols], s[cols], z[cols]

@@ -577,3 +577,67 @@ def test_calibrated_steps_cover_their_own_batch():
             assert np.all(np.abs(q).max(axis=0) == 7)
         else:
             assert np.abs(q).max() == 7
+
+
+# ---------------------------------------------------------------------------
+# 3-bit codes (W3A3, FRM-PTQ page)
+# ---------------------------------------------------------------------------
+def test_golden_act_quant_3bit():
+    g = GOLD["act_quant_3bit"]
+    Z = np.array([g["Z"]])
+    s = O.act_scale(Z, 1.0, bits=3)
+    assert s[0] == g["s_alpha1"]
+    assert O.quantize_act(Z, s, bits=3)[0][0].tolist() == g["q_alpha1"]
+    s = O.act_scale(Z, 0.5, bits=3)
+    assert s[0] == g["s_alpha05"]
+    assert O.quantize_act(Z, s, bits=3)[0][0].tolist() == g["q_alpha05"]
+    # mutant: the 4-bit scale on 3-bit codes
+    q_bad, _ = O.quantize_act(Z, O.act_scale(Z, 1.0, bits=4), bits=3)
+    assert q_bad[0].tolist() != g["q_alpha1"]
+
+
+def test_golden_weight_3bit():
+    g = GOLD["weight_3bit"]
+    wq = O.quantize_weights(np.array([g["sym_v"]], dtype=np.float32), 4, False, bits=3)
+    assert float(wq["s"][0, 0]) == g["sym_s"] and wq["codes"][0].tolist() == g["sym_q"]
+    wq = O.quantize_weights(np.array([g["asym_v"]], dtype=np.float32), 4, True, bits=3)
+    assert float(wq["s"][0, 0]) == g["asym_s"] and float(wq["z"][0, 0]) == g["asym_z"]
+    assert wq["codes"][0].tolist() == g["asym_u"]
+
+
+def test_3bit_codes_nearest_bruteforce():
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((3, 32)) * rng.uniform(0.1, 10, (3, 1))
+    r = O.transform_quant(X, np.eye(4), np.eye(8), bits=3)
+    for m in range(3):
+        s = Fraction(float(np.abs(X[m]).max())) / 3
+        for k in range(32):
+            assert r["q"][m, k] == nearest_code_bruteforce(Fraction(float(X[m, k])) / s, -4, 3)
+    W = (rng.standard_normal((2, 64)) * 0.02).astype(np.float32)
+    for asym in (False, True):
+        wq = O.quantize_weights(W, 32, asym, bits=3)
+        for n in range(2):
+            for k in range(64):
+                gidx = k // 32
+                s = Fraction(float(wq["s"][n, gidx]))
+                z = int(float(wq["z"][n, gidx]))
+                t = Fraction(float(W[n, k])) / s + z
+                lo, hi = (0, 7) if asym else (-4, 3)
+                assert wq["codes"][n, k] == nearest_code_bruteforce(t, lo, hi)
+
+
+def test_3bit_rtn_bounds():
+    rng = np.random.default_rng(32)
+    X = rng.standard_normal((8, 256)).astype(np.float16)
+    P1 = WL.random_invertible(rng, 16)
+    P2 = WL.random_invertible(rng, 16)
+    r = O.transform_quant(X, P1, P2, bits=3)
+    assert r["q"].min() >= -4 and r["q"].max() <= 3
+    err = np.abs(r["Z"] - r["q"] * r["s_x"][:, None])
+    assert np.all(err <= r["s_x"][:, None] / 2 * (1 + 1e-12))
+    W = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    wq = O.quantize_weights(W, 128, True, bits=3)
+    assert wq["codes"].min() >= 0 and wq["codes"].max() <= 7
+    deq = O.dequant_weights(wq)
+    bound = np.repeat(wq["s"].astype(np.float64), 128, axis=1) / 2
+    assert np.all(np.abs(deq - W) <= bound * (1 + 2 ** -9) + 1e-12)
