@@ -248,6 +248,30 @@ int w4a4_linear_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                        size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* 3-bit codes (W3A3)                                                        */
+/* ------------------------------------------------------------------------ */
+/* FRM-PTQ page, introduction and contributions (weights and activations at
+ * 3 bits, W3A3) with the quantizer of its section 初步介绍 at b = 3: the same
+ * layer with codes in [-4, 3] (activations and symmetric weights, scale
+ * alpha * max / 3) or [0, 7] (asymmetric weights, scale (hi - lo) / 7).  The
+ * codes are stored one per nibble exactly like the 4-bit ones, so
+ * w4a4_gemm and every buffer layout are unchanged.  bits must be 3 or 4
+ * (4 is the same as the plain entry points); anything else returns
+ * W4A4_ERR_UNSUPPORTED. */
+int w4a4_pack_weights_bits(const w4a4_weight_desc* desc, const float* Wt, float alpha_w,
+                           int32_t bits, uint8_t* Wq, uint16_t* s_w, uint16_t* z_w,
+                           void* stream);
+int w4a4_transform_quant_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                              const float* P1, const float* P2, const float* c, float alpha_a,
+                              int32_t bits, uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes,
+                              void* stream);
+/* Workspace: w4a4_linear_workspace_bytes. */
+int w4a4_linear_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                     const float* P2, const float* c, float alpha_a, int32_t bits,
+                     const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                     const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Single-kernel decode layer                                                */
 /* ------------------------------------------------------------------------ */
 

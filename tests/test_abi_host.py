@@ -275,3 +275,18 @@ def test_kv_query_factor_validation():
     assert L.w4a4_kv_query_factor(FAKE, 128, 0, FAKE, FAKE, nb, None) == -1
     assert L.w4a4_kv_query_factor(None, 128, 2, FAKE, FAKE, nb, None) == -1
     assert L.w4a4_kv_query_factor(MISALIGNED, 128, 2, FAKE, FAKE, nb, None) == -3
+
+
+def test_bits_entry_points_validation():
+    L = W.lib()
+    d = desc(N=256, K=256, g=128, asym=1)
+    assert L.w4a4_pack_weights_bits(d, FAKE, 1.0, 5, FAKE, FAKE, FAKE, None) == -2
+    assert "bits" in last()
+    assert L.w4a4_pack_weights_bits(d, FAKE, 1.0, 2, FAKE, FAKE, FAKE, None) == -2
+    assert L.w4a4_pack_weights_bits(d, FAKE, 1.0, 3, FAKE, FAKE, None, None) == -1   # z_w
+    assert L.w4a4_transform_quant_bits(FAKE, 4, 16, 16, FAKE, FAKE, None, 1.0, 8, FAKE, FAKE,
+                                       FAKE, 1 << 20, None) == -2
+    assert L.w4a4_transform_quant_bits(FAKE, 0, 16, 16, FAKE, FAKE, None, 1.0, 3, FAKE, FAKE,
+                                       FAKE, 1 << 20, None) == 0
+    assert L.w4a4_linear_bits(FAKE, 4, 16, 16, FAKE, FAKE, None, 1.0, 1, d, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, 1 << 20, None) == -2

@@ -23,6 +23,7 @@ __all__ = [
     "DECODE_SYNC_BYTES", "DECODE_SYNC_ERROR_WORD",
     "KV_HEAD_DIM", "KvCache", "kv_cache_bytes", "kv_query_factor", "kv_append",
     "attn_decode_workspace_bytes", "attn_decode",
+    "pack_weights_bits", "transform_quant_bits", "linear_bits",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so")
@@ -39,6 +40,7 @@ EXPORTED_SYMBOLS = [
     "w4a4_linear_decode_workspace_bytes", "w4a4_linear_decode",
     "w4a4_kv_cache_bytes", "w4a4_kv_query_factor_workspace_bytes", "w4a4_kv_query_factor",
     "w4a4_kv_append", "w4a4_attn_decode_workspace_bytes", "w4a4_attn_decode",
+    "w4a4_pack_weights_bits", "w4a4_transform_quant_bits", "w4a4_linear_bits",
 ]
 
 DECODE_SYNC_BYTES = 1024          # W4A4_DECODE_SYNC_BYTES
@@ -103,6 +105,11 @@ def lib() -> ctypes.CDLL:
             "w4a4_linear_decode_workspace_bytes": (sz, [i32, i32, i32]),
             "w4a4_linear_decode": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, f32, vp, i32, dp, vp, vp,
                                                   vp, vp, vp, sz, vp, vp]),
+            "w4a4_pack_weights_bits": (ctypes.c_int, [dp, vp, f32, i32, vp, vp, vp, vp]),
+            "w4a4_transform_quant_bits": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, i32,
+                                                         vp, vp, vp, sz, vp]),
+            "w4a4_linear_bits": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, i32, dp, vp,
+                                                vp, vp, vp, vp, sz, vp]),
             "w4a4_kv_cache_bytes": (ctypes.c_int, [i32, i32, i32, i32, szp, szp, szp]),
             "w4a4_kv_query_factor_workspace_bytes": (sz, [i32, i32]),
             "w4a4_kv_query_factor": (ctypes.c_int, [vp, i32, i32, vp, vp, sz, vp]),
@@ -489,3 +496,64 @@ def attn_decode(q, P_h_inv_t, cache: KvCache, lengths, sm_scale: float, out=None
                                   _p(out), _p(ws), nb if ws is None else ws.numel(),
                                   _stream(stream)), "w4a4_attn_decode")
     return out
+
+
+# ---------------------------------------------------------------------------
+# 3-bit codes (W3A3): the same layer with codes in [-4, 3] / [0, 7]
+# ---------------------------------------------------------------------------
+def pack_weights_bits(Wt, group_size: int, asymmetric: bool, bits: int, alpha_w: float = 1.0,
+                      stream=None):
+    """pack_weights with b-bit codes (b = 3 or 4), one code per nibble."""
+    torch = _torch()
+    N, K = Wt.shape
+    _need(Wt, torch.float32, (N, K), "Wt")
+    desc = _desc(N, K, group_size, asymmetric)
+    G = K // group_size if group_size > 0 else 0
+    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=Wt.device)
+    s_w = torch.empty((N, max(G, 1)), dtype=torch.float16, device=Wt.device)
+    z_w = torch.empty((N, max(G, 1)), dtype=torch.float16, device=Wt.device) if asymmetric else None
+    _check(lib().w4a4_pack_weights_bits(ctypes.byref(desc), _p(Wt), float(alpha_w), int(bits),
+                                        _p(Wq), _p(s_w), _p(z_w), _stream(stream)),
+           "w4a4_pack_weights_bits")
+    return desc, Wq, s_w, z_w
+
+
+def transform_quant_bits(X, P1, P2, bits: int, c=None, alpha_a: float = 1.0, out=None, ws=None,
+                         stream=None):
+    """transform_quant with b-bit activation codes: returns (Xq [M,K/2], s_x [M])."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    _need(X, torch.float16, (M, K), "X")
+    _need(P1, torch.float32, (n1, n1), "P1")
+    _need(P2, torch.float32, (n2, n2), "P2")
+    if c is not None:
+        _need(c, torch.float32, (K,), "c")
+    if out is None:
+        Xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+        s_x = torch.empty((M,), dtype=torch.float32, device=X.device)
+    else:
+        Xq, s_x = out
+    nb = transform_quant_workspace_bytes(M, n1, n2, c is not None)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_transform_quant_bits(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c),
+                                           float(alpha_a), int(bits), _p(Xq), _p(s_x), _p(ws),
+                                           nb if ws is None else ws.numel(), _stream(stream)),
+           "w4a4_transform_quant_bits")
+    return Xq, s_x
+
+
+def linear_bits(X, P1, P2, bits: int, desc: WeightDesc, Wq, s_w, z_w=None, c=None,
+                alpha_a: float = 1.0, out=None, ws=None, stream=None):
+    """The whole layer with b-bit codes (weights packed by pack_weights_bits)."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=X.device)
+    nb = linear_workspace_bytes(M, n1, n2, desc, c is not None)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_linear_bits(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
+                                  int(bits), ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y),
+                                  _p(ws), nb if ws is None else ws.numel(), _stream(stream)),
+           "w4a4_linear_bits")
+    return Y

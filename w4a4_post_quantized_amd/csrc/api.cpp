@@ -133,9 +133,11 @@ int w4a4_merge_weights(const float* W, int32_t N, int32_t K, int32_t n1, int32_t
     return ok();
 }
 
-int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha_w,
-                      uint8_t* Wq, uint16_t* s_w, uint16_t* z_w, void* stream) {
+int w4a4_pack_weights_bits(const w4a4_weight_desc* desc, const float* Wt, float alpha_w,
+                           int32_t bits, uint8_t* Wq, uint16_t* s_w, uint16_t* z_w,
+                           void* stream) {
     if (int s = check_desc(desc, false)) return s;
+    REQUIRE(bits == 3 || bits == 4, W4A4_ERR_UNSUPPORTED, "bits = %d: only 3 and 4", bits);
     REQUIRE(alpha_w > 0.0f && alpha_w <= 1.0f, W4A4_ERR_INVALID_ARG,
             "alpha_w = %g must lie in (0, 1]", static_cast<double>(alpha_w));
     REQUIRE_PTR(Wt);
@@ -147,9 +149,14 @@ int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha
     REQUIRE_ALIGNED(s_w);
     if (desc->asymmetric) REQUIRE_ALIGNED(z_w);
     hipError_t e = w4a4::pack_weights_launch(Wt, desc->N, desc->K, desc->group_size,
-                                             desc->asymmetric != 0, alpha_w, Wq, s_w, z_w,
-                                             static_cast<hipStream_t>(stream));
+                                             desc->asymmetric != 0, alpha_w, bits, Wq, s_w,
+                                             z_w, static_cast<hipStream_t>(stream));
     return hip_status(e, "w4a4_pack_weights");
+}
+
+int w4a4_pack_weights(const w4a4_weight_desc* desc, const float* Wt, float alpha_w,
+                      uint8_t* Wq, uint16_t* s_w, uint16_t* z_w, void* stream) {
+    return w4a4_pack_weights_bits(desc, Wt, alpha_w, 4, Wq, s_w, z_w, stream);
 }
 
 int w4a4_migrate_steps(const float* Wt, int32_t N, int32_t K, const float* steps, float* Wm,
@@ -218,6 +225,18 @@ int w4a4_transform_quant(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                          uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes, void* stream) {
     return tq_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{alpha_a, nullptr, false}, true, Xq,
                      s_x, nullptr, ws, ws_bytes, stream, "w4a4_transform_quant");
+}
+
+static float qmax_of(int32_t bits) { return static_cast<float>((1 << (bits - 1)) - 1); }
+
+int w4a4_transform_quant_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
+                              const float* P1, const float* P2, const float* c, float alpha_a,
+                              int32_t bits, uint8_t* Xq, float* s_x, void* ws, size_t ws_bytes,
+                              void* stream) {
+    REQUIRE(bits == 3 || bits == 4, W4A4_ERR_UNSUPPORTED, "bits = %d: only 3 and 4", bits);
+    return tq_common(X, M, n1, n2, P1, P2, c,
+                     w4a4::ActQuant{alpha_a, nullptr, false, qmax_of(bits)}, true, Xq, s_x,
+                     nullptr, ws, ws_bytes, stream, "w4a4_transform_quant_bits");
 }
 
 int w4a4_transform_quant_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
@@ -383,6 +402,16 @@ int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const floa
                 void* ws, size_t ws_bytes, void* stream) {
     return linear_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{alpha_a, nullptr, false}, desc,
                          Wq, s_w, z_w, Y, ws, ws_bytes, stream, "w4a4_linear");
+}
+
+int w4a4_linear_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                     const float* P2, const float* c, float alpha_a, int32_t bits,
+                     const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                     const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE(bits == 3 || bits == 4, W4A4_ERR_UNSUPPORTED, "bits = %d: only 3 and 4", bits);
+    return linear_common(X, M, n1, n2, P1, P2, c,
+                         w4a4::ActQuant{alpha_a, nullptr, false, qmax_of(bits)}, desc, Wq, s_w,
+                         z_w, Y, ws, ws_bytes, stream, "w4a4_linear_bits");
 }
 
 int w4a4_linear_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,

@@ -127,20 +127,22 @@ __device__ __forceinline__ float wave_min(float v) {
 }
 
 // t = z * inv_s (inv_s = 1/s of the token), round half to even, clamp to the
-// signed 4-bit range, as a nibble; zero scale gives code 0
-__device__ __forceinline__ uint32_t quant_nibble(float z, float inv_s, bool zero) {
+// signed range [-qmax - 1, qmax] (qmax = 7 for 4-bit codes, 3 for 3-bit), as a
+// nibble; zero scale gives code 0
+__device__ __forceinline__ uint32_t quant_nibble(float z, float inv_s, bool zero,
+                                                 float qmax = 7.0f) {
     float r = __builtin_rintf(z * inv_s);
-    r = fminf(fmaxf(r, -8.0f), 7.0f);
+    r = fminf(fmaxf(r, -qmax - 1.0f), qmax);
     int q = zero ? 0 : static_cast<int>(r);
     return static_cast<uint32_t>(q) & 0xFu;
 }
 
 // The same code as quant_nibble for finite z: the product is clamped to
-// [-8, 7] (v_med3) and rounded half to even by adding 1.5 * 2^23, whose
+// [-qmax - 1, qmax] (v_med3) and rounded half to even by adding 1.5 * 2^23, whose
 // float lands the integer in the low mantissa bits (two's complement in the
 // low nibble).  A zero scale passes inv_s = 0 and gives code 0.
-__device__ __forceinline__ uint32_t quant_nibble_magic(float z, float inv_s) {
-    const float t = __builtin_amdgcn_fmed3f(z * inv_s, -8.0f, 7.0f);
+__device__ __forceinline__ uint32_t quant_nibble_magic(float z, float inv_s, float qmax = 7.0f) {
+    const float t = __builtin_amdgcn_fmed3f(z * inv_s, -qmax - 1.0f, qmax);
     return __float_as_uint(t + 12582912.0f) & 0xFu;
 }
 

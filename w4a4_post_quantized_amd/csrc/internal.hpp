@@ -16,10 +16,13 @@ enum class TqPath { Fused, Cols, Split };
 // scale alpha * max|z| / 7.  Static: steps fixed offline, either one step for
 // the whole tensor (the token scale is that step) or one step per channel
 // (codes round z_k / step_k; the token scale written is 1).
+// qmax: largest code, 2^(b-1) - 1 (7 for 4-bit codes, 3 for 3-bit); codes are
+// clamped to [-qmax - 1, qmax] and the dynamic scale is alpha * max|z| / qmax.
 struct ActQuant {
     float alpha;
     const float* steps;
     bool per_channel;
+    float qmax = 7.0f;
 };
 
 TqPath tq_select_path(int M, int n1, int n2, bool has_c);
@@ -115,8 +118,9 @@ hipError_t migrate_steps_launch(const float* Wt, int N, int K, const float* step
 size_t invert_t_workspace_bytes(int n, int count);
 hipError_t invert_t_launch(const float* P, int n, int count, float* out, void* ws,
                            hipStream_t stream, bool* singular);
+// bits: 4 or 3 (codes [-8, 7] / [0, 15], or [-4, 3] / [0, 7])
 hipError_t pack_weights_launch(const float* Wt, int N, int K, int group_size, bool asym,
-                               float alpha_w, uint8_t* Wq, uint16_t* s_w, uint16_t* z_w,
-                               hipStream_t stream);
+                               float alpha_w, int bits, uint8_t* Wq, uint16_t* s_w,
+                               uint16_t* z_w, hipStream_t stream);
 
 }  // namespace w4a4

@@ -328,7 +328,7 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
                     }
                 }
                 const uint64_t tm64 = __hip_atomic_load(&tokmax[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                red8[0] = p.aq.alpha * __uint_as_float(static_cast<uint32_t>(tm64)) / 7.0f;
+                red8[0] = p.aq.alpha * __uint_as_float(static_cast<uint32_t>(tm64)) / p.aq.qmax;
             }
             __syncthreads();
             s = red8[0];
@@ -341,8 +341,9 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int k = (row0 + r) * N2 + 16 * cb + li;
-            const uint32_t nib = pc ? quant_nibble_magic(v[r], __builtin_amdgcn_rcpf(p.aq.steps[k]))
-                                    : quant_nibble(v[r], inv, zero);
+            const uint32_t nib = pc ? quant_nibble_magic(v[r], __builtin_amdgcn_rcpf(p.aq.steps[k]),
+                                                         p.aq.qmax)
+                                    : quant_nibble(v[r], inv, zero, p.aq.qmax);
             const uint32_t odd = lane_xor1(nib);
             if ((li & 1) == 0) qs[((4 * g + r) * N2 + 16 * cb + li) >> 1] = static_cast<uint8_t>(nib | (odd << 4));
         }

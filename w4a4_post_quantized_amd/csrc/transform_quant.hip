@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, i
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ab;
         __syncthreads();
         ab = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        s = aq.alpha * ab / 7.0f;
+        s = aq.alpha * ab / aq.qmax;
     } else {
         s = aq.per_channel ? 1.0f : aq.steps[0];
     }
@@ -139,14 +139,14 @@ __global__ __launch_bounds__(256) void k_tq_quant(const float* __restrict__ Z, i
         const v4f st1 = *reinterpret_cast<const v4f*>(aq.steps + ec + 4);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            word |= quant_nibble_magic(z[t], __builtin_amdgcn_rcpf(st0[t])) << (4 * t);
-            word |= quant_nibble_magic(z[t + 4], __builtin_amdgcn_rcpf(st1[t])) << (4 * (t + 4));
+            word |= quant_nibble_magic(z[t], __builtin_amdgcn_rcpf(st0[t]), aq.qmax) << (4 * t);
+            word |= quant_nibble_magic(z[t + 4], __builtin_amdgcn_rcpf(st1[t]), aq.qmax) << (4 * (t + 4));
         }
     } else {
         const bool zero = !(s > 0.0f);
         const float inv = zero ? 0.0f : 1.0f / s;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) word |= quant_nibble(z[t], inv, zero) << (4 * t);
+        for (int t = 0; t < 8; ++t) word |= quant_nibble(z[t], inv, zero, aq.qmax) << (4 * t);
     }
     reinterpret_cast<uint32_t*>(Xq + static_cast<size_t>(m) * (K / 2))[idx] = word;
 }
@@ -394,11 +394,11 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
         // static steps: the token scale is the tensor's step (or 1 with
         // per-channel steps); the reduction above is then unused
         const float s_static = PC ? 1.0f : (aq.steps ? aq.steps[0] : 0.0f);
-        const float s = aq.steps ? s_static : aq.alpha * amax / 7.0f;
+        const float s = aq.steps ? s_static : aq.alpha * amax / aq.qmax;
         if (tid < C::TPI) {
             float a2 = 0.0f;
             for (int w = 0; w < C::CB; ++w) a2 = fmaxf(a2, red[tid * C::CB + w]);
-            tok_s[tid] = aq.steps ? s_static : aq.alpha * a2 / 7.0f;
+            tok_s[tid] = aq.steps ? s_static : aq.alpha * a2 / aq.qmax;
         }
         if (valid) {
             if (Zout != nullptr) {
@@ -429,8 +429,8 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const uint32_t nib = PC ? quant_nibble_magic(Z[ob][r], rst[r])
-                                                : quant_nibble(Z[ob][r], inv, zero);
+                        const uint32_t nib = PC ? quant_nibble_magic(Z[ob][r], rst[r], aq.qmax)
+                                                : quant_nibble(Z[ob][r], inv, zero, aq.qmax);
                         const uint32_t odd = lane_xor1(nib);
                         if ((li & 1) == 0) {
                             const int k = (16 * ob + 4 * g + r) * N2 + 16 * cb + li;
@@ -768,7 +768,7 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
             if (PC)
                 s = 1.0f;
             else if (aq.steps == nullptr)
-                s = aq.alpha * ldexpf(wave_max(zmax), unscale) / 7.0f;
+                s = aq.alpha * ldexpf(wave_max(zmax), unscale) / aq.qmax;
             else
                 s = aq.steps[0];
             const float inv = s > 0.0f ? ldexpf(1.0f / s, unscale) : 0.0f;
@@ -784,7 +784,7 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
                         uint32_t w = 0;
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            w |= quant_nibble_magic(ldexpf(Z[ob][cb][r], unscale), rs[r]) << (4 * r);
+                            w |= quant_nibble_magic(ldexpf(Z[ob][cb][r], unscale), rs[r], aq.qmax) << (4 * r);
                         *reinterpret_cast<uint16_t*>(qb + k0 / 2) = static_cast<uint16_t>(w);
                     }
             } else {
@@ -794,7 +794,7 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
                     for (int cb = 0; cb < C::CB; ++cb) {
                         uint32_t w = 0;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) w |= quant_nibble_magic(Z[ob][cb][r], inv) << (4 * r);
+                        for (int r = 0; r < 4; ++r) w |= quant_nibble_magic(Z[ob][cb][r], inv, aq.qmax) << (4 * r);
                         *reinterpret_cast<uint16_t*>(qb + ((16 * ob + li) * N2 + 16 * cb + 4 * g) / 2) =
                             static_cast<uint16_t>(w);
                     }

@@ -151,12 +151,13 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ W, int 
 // ---------------------------------------------------------------------------
 // Pack: one workgroup per (row, group).  Range reduction in fp32 (exact for
 // min / max), scale arithmetic in float64, direct float64 -> fp16 rounding,
-// codes from the stored fp16 scale with float64 division.
+// codes from the stored fp16 scale with float64 division.  qmax = 2^(b-1) - 1
+// and umax = 2^b - 1 for b-bit codes (b = 4 or 3), one code per nibble.
 // ---------------------------------------------------------------------------
 template <bool ASYM>
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ Wt, int K,
-                                              int group_size, float alpha,
-                                              uint8_t* __restrict__ Wq,
+                                              int group_size, float alpha, double qmax,
+                                              double umax, uint8_t* __restrict__ Wq,
                                               uint16_t* __restrict__ s_w,
                                               uint16_t* __restrict__ z_w) {
     __shared__ float rmin[4], rmax[4];
@@ -188,13 +189,13 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ Wt, int 
         double z = 0.0;
         if (!ASYM) {
             const double amax = fmax(fabs(static_cast<double>(mn)), fabs(static_cast<double>(mx)));
-            sbits = f64_to_f16_rne(a * amax / 7.0);
+            sbits = f64_to_f16_rne(a * amax / qmax);
         } else {
             const double dlo = a * fmin(static_cast<double>(mn), 0.0);
             const double dhi = a * fmax(static_cast<double>(mx), 0.0);
-            sbits = f64_to_f16_rne((dhi - dlo) / 15.0);
+            sbits = f64_to_f16_rne((dhi - dlo) / umax);
             const double s = f16_bits_to_f64(sbits);
-            if (s > 0.0) z = fmin(fmax(__builtin_rint(-dlo / s), 0.0), 15.0);
+            if (s > 0.0) z = fmin(fmax(__builtin_rint(-dlo / s), 0.0), umax);
         }
         const double s = f16_bits_to_f64(sbits);
         s_w[static_cast<size_t>(row) * G + g] = sbits;
@@ -214,9 +215,9 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ Wt, int 
             const double t = static_cast<double>(v[2 * p + h]) / (zero ? 1.0 : s);
             int q;
             if (ASYM)
-                q = zero ? 0 : static_cast<int>(fmin(fmax(__builtin_rint(t) + z, 0.0), 15.0));
+                q = zero ? 0 : static_cast<int>(fmin(fmax(__builtin_rint(t) + z, 0.0), umax));
             else
-                q = zero ? 0 : static_cast<int>(fmin(fmax(__builtin_rint(t), -8.0), 7.0));
+                q = zero ? 0 : static_cast<int>(fmin(fmax(__builtin_rint(t), -qmax - 1.0), qmax));
             byte |= (static_cast<uint32_t>(q) & 0xFu) << (4 * h);
         }
         out[p] = static_cast<uint8_t>(byte);
@@ -330,15 +331,17 @@ hipError_t migrate_steps_launch(const float* Wt, int N, int K, const float* step
 }
 
 hipError_t pack_weights_launch(const float* Wt, int N, int K, int group_size, bool asym,
-                               float alpha_w, uint8_t* Wq, uint16_t* s_w, uint16_t* z_w,
-                               hipStream_t stream) {
+                               float alpha_w, int bits, uint8_t* Wq, uint16_t* s_w,
+                               uint16_t* z_w, hipStream_t stream) {
+    const double qmax = static_cast<double>((1 << (bits - 1)) - 1);
+    const double umax = static_cast<double>((1 << bits) - 1);
     const int G = K / group_size;
     dim3 grid(N, G);
     const int threads = group_size >= 256 ? 256 : ((group_size + 63) / 64) * 64;
     if (asym)
-        k_pack<true><<<grid, threads, 0, stream>>>(Wt, K, group_size, alpha_w, Wq, s_w, z_w);
+        k_pack<true><<<grid, threads, 0, stream>>>(Wt, K, group_size, alpha_w, qmax, umax, Wq, s_w, z_w);
     else
-        k_pack<false><<<grid, threads, 0, stream>>>(Wt, K, group_size, alpha_w, Wq, s_w, z_w);
+        k_pack<false><<<grid, threads, 0, stream>>>(Wt, K, group_size, alpha_w, qmax, umax, Wq, s_w, z_w);
     return hipGetLastError();
 }
 
