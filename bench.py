@@ -16,6 +16,9 @@ offline from a seeded calibration batch, FPTQuant / MergeQuant): one step
 for the tensor, or one per channel migrated into the weights before packing;
 the step runs w4a4_linear_static instead.
 
+With --bits 3 the layer runs with 3-bit codes (W3A3, FRM-PTQ page) through
+w4a4_linear_bits; the codes stay one per nibble, so the bytes are the same.
+
 With --path single (decode, M <= 16) the step is one w4a4_linear_decode
 launch (transform, quantization and GEMM in one kernel) and the roofline
 kernel is that kernel, priced at the layer's algorithmic bytes.
@@ -66,6 +69,8 @@ def parse():
                     help="'two' = w4a4_linear (transform kernel, then GEMM kernel; the faster "
                          "path measured on MI355X); 'single' = w4a4_linear_decode (one launch, "
                          "M <= 16 tokens)")
+    ap.add_argument("--bits", type=int, choices=[3, 4], default=4,
+                    help="code width of weights and activations (3: W3A3, FRM-PTQ)")
     ap.add_argument("--act-quant", choices=["dynamic", "tensor", "channel"], default="dynamic",
                     help="activation quantizer: per-token dynamic scales, or static steps "
                          "(one per tensor, or one per channel migrated into the weights)")
@@ -127,7 +132,7 @@ def calibration_batch(wl, inp):
                                            seed=wl.seed + CAL_SEED_OFFSET)
 
 
-def cpu_baseline(wl, inp, budget_s, act_quant="dynamic"):
+def cpu_baseline(wl, inp, budget_s, act_quant="dynamic", bits=4):
     """The CPU oracle on the same workload: whole passes until `budget_s`."""
     import oracle as O
     try:
@@ -145,7 +150,7 @@ def cpu_baseline(wl, inp, budget_s, act_quant="dynamic"):
         del Zc
         if pc:
             Wt = O.migrate_steps(Wt, steps)
-    wq = O.quantize_weights(Wt, wl.group_size, wl.asymmetric)
+    wq = O.quantize_weights(Wt, wl.group_size, wl.asymmetric, bits=bits)
     del Wt
     # one pass = the oracle's steps in order: transform + quantize + pack
     # (O1-O4), then the exact integer GEMM and the epilogue (O6-O7)
@@ -156,7 +161,7 @@ def cpu_baseline(wl, inp, budget_s, act_quant="dynamic"):
         if static:
             act = O.transform_quant_static(inp["X"], inp["P1"], inp["P2"], steps, pc, c=inp["c"])
         else:
-            act = O.transform_quant(inp["X"], inp["P1"], inp["P2"], inp["c"])
+            act = O.transform_quant(inp["X"], inp["P1"], inp["P2"], inp["c"], bits=bits)
         t1 = time.perf_counter()
         D = O.int_gemm(act["q"], wq["codes"], wq["z"], wq["group_size"])
         O.epilogue(D, act["s_x"], wq["s"])
@@ -212,6 +217,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.bits != 4 and (args.act_quant != "dynamic" or args.path != "two"):
+        raise SystemExit("--bits 3 runs the dynamic two-launch layer only")
 
     import torch
     import workloads as WL
@@ -254,8 +261,8 @@ def main():
             Wt = L.migrate_steps(Wt, steps)
     packs = []
     for i in range(copies):
-        packs.append(L.pack_weights(Wt if i == 0 else Wt * (1.0 + 1e-3 * i), wl.group_size,
-                                    wl.asymmetric))
+        packs.append(L.pack_weights_bits(Wt if i == 0 else Wt * (1.0 + 1e-3 * i), wl.group_size,
+                                         wl.asymmetric, args.bits))
     del Wt
     desc = packs[0][0]
     Y = torch.empty((M, N), dtype=torch.float16, device=dev)
@@ -294,13 +301,13 @@ def main():
         elif static:
             L.linear_static(X, P1, P2, steps, pc, desc, Wq, sw, zw, out=Y, ws=ws)
         else:
-            L.linear(X, P1, P2, desc, Wq, sw, zw, out=Y, ws=ws)
+            L.linear_bits(X, P1, P2, args.bits, desc, Wq, sw, zw, out=Y, ws=ws)
 
     def act(i):
         if static:
             L.transform_quant_static(X, P1, P2, steps, pc, out=(Xq, sx), ws=tq_ws)
         else:
-            L.transform_quant(X, P1, P2, out=(Xq, sx), ws=tq_ws)
+            L.transform_quant_bits(X, P1, P2, args.bits, out=(Xq, sx), ws=tq_ws)
 
     for i in range(args.warmup):
         step(i)
@@ -403,7 +410,7 @@ def main():
         "config": {"workload": wl.description, "name": wl.name, "M": M, "K": K, "N": N,
                    "n1": wl.n1, "n2": wl.n2, "group_size": wl.group_size,
                    "asymmetric_weights": wl.asymmetric, "weight_copies_rotated": copies,
-                   "act_quant": args.act_quant},
+                   "act_quant": args.act_quant, "bits": args.bits},
         "us_per_layer": round(t_step * 1e6, 2),
         "path": "single-kernel decode (w4a4_linear_decode)" if single else "two launches (w4a4_linear)",
         "transform_quant_us": round(tq_us, 2),
@@ -414,7 +421,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.act_quant)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, args.act_quant, args.bits)
     print(json.dumps(out), flush=True)
 
 

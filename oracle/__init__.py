@@ -6,7 +6,9 @@ imports it and shares no code with it.  See w4a4_oracle.py for the steps and
 the passages of the pages each one follows.
 
 kv_oracle.py is the INT4 KV cache with per-head transforms and the decode
-attention over it (pinned by tests/test_kv_oracle_pins.py).
+attention over it (pinned by tests/test_kv_oracle_pins.py); ternary_oracle.py
+is the ternary-weight layer of PT2-LLM with its ITF fitting (pinned by
+tests/test_ternary_oracle_pins.py).
 
 Parity pins: every function here is pinned by tests/test_oracle_pins.py
 against brute force, closed forms, hand-computed values (tests/golden/) or
@@ -17,3 +19,4 @@ is "parity unpinned" (and out of scope).
 """
 from .w4a4_oracle import *  # noqa: F401,F403
 from . import kv_oracle  # noqa: F401
+from . import ternary_oracle  # noqa: F401
