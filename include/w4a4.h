@@ -272,6 +272,43 @@ int w4a4_linear_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const
                      const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Ternary weights (W1.58A16)                                                */
+/* ------------------------------------------------------------------------ */
+/* PT2-LLM page, section 关键设计 item 2: each row of a block of 128 columns is
+ * alpha * T + mu with T in {-1, 0, 1} (ATQ), fitted by ITF, which alternates
+ * the closed-form least-squares (alpha, mu) for fixed T with the nearest grid
+ * point T for fixed (alpha, mu), mu starting at the block row's mean and
+ * alpha at its mean absolute deviation.  The layer is weight-only:
+ * Y = X · Ŵ^T with fp16 activations X (no activation transform).
+ *
+ * Layouts:
+ *   Tq  uint8 [N][K/4]: two-bit codes c = t + 1 in little-endian 32-bit words
+ *       of 16 codes, code 16w + 2s at bits 2s and code 16w + 2s + 1 at bits
+ *       16 + 2s of word w (s = 0 .. 7);
+ *   am  uint32 [N][K/128]: the block's alpha as fp16 bits in the low half and
+ *       mu in the high half (both one rounding from float64). */
+#define W4A4_TERNARY_BLOCK 128
+#define W4A4_TERNARY_MAX_M 64
+
+/* Offline: ternarize merged or raw fp32 weights Wt [N][K] with `iters` ITF
+ * iterations (10 in the pages' setting), float64 arithmetic; the final codes
+ * are the nearest points of the stored (fp16) grid.  K must be a multiple of
+ * 128. */
+int w4a4_pack_ternary(const float* Wt, int32_t N, int32_t K, int32_t iters, uint8_t* Tq,
+                      uint32_t* am, void* stream);
+
+/* Bytes of workspace w4a4_ternary_gemm needs (0 for invalid shapes). */
+size_t w4a4_ternary_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/* Y [M][N] fp16 = X [M][K] fp16 · Ŵ^T for decode-sized batches,
+ * 0 <= M <= W4A4_TERNARY_MAX_M (larger M returns W4A4_ERR_UNSUPPORTED).  The
+ * fp16 MFMA products are exact (codes enter as the fp16 values c * 2^-14) and
+ * the sums run in fp32.  Up to three launches (block row sums of X, the
+ * product with a split of K over workgroups, the merge of the splits). */
+int w4a4_ternary_gemm(const uint16_t* X, int32_t M, int32_t N, int32_t K, const uint8_t* Tq,
+                      const uint32_t* am, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Single-kernel decode layer                                                */
 /* ------------------------------------------------------------------------ */
 

@@ -32,8 +32,12 @@ Readings where the page is silent (restated with the design notes):
   reordering is a column permutation, which leaves X W^T unchanged (pinned for
   the 4-bit layer).
 
-Storage: two bits per code, t + 1 in {0, 1, 2}; byte j of a row holds codes
-4j .. 4j+3, code 4j+i in bits 2i, 2i+1.
+Storage (this library's layout contract): two bits per code, c = t + 1 in
+{0, 1, 2}; a row is a sequence of little-endian 32-bit words of 16 codes, and
+in word w code 16 w + 2 s sits at bits 2 s and code 16 w + 2 s + 1 at bits
+16 + 2 s (s = 0 .. 7): the even codes in the low half, the odd codes in the
+high half.  The per-block parameters are stored as one 32-bit word, alpha's
+fp16 bits in the low half and mu's in the high half.
 """
 from __future__ import annotations
 
@@ -41,7 +45,7 @@ import numpy as np
 
 from .w4a4_oracle import fp16_rne
 
-__all__ = ["TERN_BLOCK", "itf_ternarize", "pack_ternary", "unpack_ternary",
+__all__ = ["TERN_BLOCK", "itf_ternarize", "pack_ternary", "unpack_ternary", "pack_params",
            "dequant_ternary", "ternary_linear", "itf_objective"]
 
 TERN_BLOCK = 128
@@ -105,22 +109,36 @@ def itf_objective(Wt, T, alpha, mu, block: int = TERN_BLOCK):
 
 
 def pack_ternary(T):
-    """codes [..., K] in {-1, 0, 1} -> bytes [..., K/4]: code 4j+i at bits 2i of byte j."""
+    """codes [..., K] in {-1, 0, 1} (K a multiple of 16) -> bytes [..., K/4]:
+    per 16 codes one little-endian word, code 2s at bits 2s, code 2s+1 at
+    bits 16 + 2s."""
     c = np.asarray(T).astype(np.int64) + 1
-    if c.shape[-1] % 4:
-        raise ValueError("K must be a multiple of 4")
-    out = np.zeros(c.shape[:-1] + (c.shape[-1] // 4,), dtype=np.int64)
-    for i in range(4):
-        out |= c[..., i::4] << (2 * i)
-    return out.astype(np.uint8)
+    K = c.shape[-1]
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    cw = c.reshape(c.shape[:-1] + (K // 16, 16))
+    word = np.zeros(cw.shape[:-1], dtype=np.int64)
+    for s_ in range(8):
+        word |= cw[..., 2 * s_] << (2 * s_)
+        word |= cw[..., 2 * s_ + 1] << (16 + 2 * s_)
+    return word.astype("<u4").view(np.uint8).reshape(c.shape[:-1] + (K // 4,))
 
 
 def unpack_ternary(b):
-    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
-    out = np.empty(b.shape[:-1] + (4 * b.shape[-1],), dtype=np.int64)
-    for i in range(4):
-        out[..., i::4] = ((b >> (2 * i)) & 3) - 1
-    return out.astype(np.int8)
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint8))
+    word = b.view("<u4").astype(np.int64)
+    out = np.empty(word.shape + (16,), dtype=np.int64)
+    for s_ in range(8):
+        out[..., 2 * s_] = ((word >> (2 * s_)) & 3) - 1
+        out[..., 2 * s_ + 1] = ((word >> (16 + 2 * s_)) & 3) - 1
+    return out.reshape(word.shape[:-1] + (word.shape[-1] * 16,)).astype(np.int8)
+
+
+def pack_params(alpha, mu):
+    """fp16 alpha, mu [N, G] -> uint32 [N, G]: alpha's bits low, mu's bits high."""
+    a = np.asarray(alpha, dtype=np.float16).view(np.uint16).astype(np.uint32)
+    u = np.asarray(mu, dtype=np.float16).view(np.uint16).astype(np.uint32)
+    return a | (u << 16)
 
 
 def dequant_ternary(tq):

@@ -290,3 +290,24 @@ def test_bits_entry_points_validation():
                                        FAKE, 1 << 20, None) == 0
     assert L.w4a4_linear_bits(FAKE, 4, 16, 16, FAKE, FAKE, None, 1.0, 1, d, FAKE, FAKE, FAKE,
                               FAKE, FAKE, 1 << 20, None) == -2
+
+
+def test_ternary_entry_points_validation():
+    L = W.lib()
+    # K not a multiple of the block, M above the decode limit, bad iteration count
+    assert L.w4a4_pack_ternary(FAKE, 8, 200, 10, FAKE, FAKE, None) == -2
+    assert L.w4a4_pack_ternary(FAKE, 8, 256, -1, FAKE, FAKE, None) == -1
+    assert L.w4a4_pack_ternary(FAKE, 0, 256, 10, FAKE, FAKE, None) == -1
+    assert L.w4a4_pack_ternary(FAKE, 8, 256, 10, None, FAKE, None) == -1
+    assert L.w4a4_pack_ternary(MISALIGNED, 8, 256, 10, FAKE, FAKE, None) == -3
+    assert L.w4a4_ternary_gemm(FAKE, 65, 64, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -2
+    assert "decode" in last()
+    assert L.w4a4_ternary_gemm(FAKE, 4, 64, 256, FAKE, FAKE, FAKE, FAKE, 4, None) == -4
+    assert L.w4a4_ternary_gemm(FAKE, 4, 64, 256, FAKE, MISALIGNED, FAKE, FAKE, 1 << 20, None) == -3
+    assert L.w4a4_ternary_gemm(FAKE, 0, 64, 256, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
+    # workspace: the block row sums (rows padded to 64) and, with a K split, the partials
+    assert W.ternary_gemm_workspace_bytes(65, 64, 256) == 0
+    assert W.ternary_gemm_workspace_bytes(0, 64, 256) == 0
+    nb = W.ternary_gemm_workspace_bytes(1, 64, 8192)
+    assert nb >= 64 * 64 * 4
+    assert nb % 4 == 0

@@ -1,0 +1,154 @@
+"""GPU parity of the ternary-weight layer (W1.58A16; PT2-LLM page, section
+关键设计 item 2: ATQ fitted by ITF), through the C ABI entry points
+w4a4_pack_ternary and w4a4_ternary_gemm.
+
+Checks:
+* pack: codes and the (alpha, mu) words bit-exact against the oracle (both
+  sides run ITF in float64 and round alpha and mu to fp16 once), including
+  all-zero and constant block rows, and a full-size weight matrix on sampled
+  rows;
+* product: Y (fp16) against the oracle's float64 layer on the oracle's own
+  packed weights, per element within half an fp16 ulp of the result plus
+  4e-6 times the magnitude of the summed terms, over decode batches that span
+  the row tiles (M = 1 .. 64, ragged), ragged N, K splits, and the full
+  LLaMA-3-70B decode shapes on sampled output columns.
+"""
+import numpy as np
+import pytest
+
+from oracle import ternary_oracle as TO
+from workloads import ternary as WT
+from gpu_common import log, rel_l2, to_dev, torch_dev, ulp16
+
+pytestmark = pytest.mark.gpu
+
+REL_TERM = 4e-6
+
+
+def W():
+    import w4a4_post_quantized_amd as lib
+    return lib
+
+
+def oracle_pack(Wt, iters=10):
+    r = TO.itf_ternarize(Wt, iters=iters)
+    return r, TO.pack_ternary(r["T"]), TO.pack_params(r["alpha"], r["mu"])
+
+
+def gpu_pack(Wt_np, iters=10):
+    Tq, am = W().pack_ternary(to_dev(Wt_np), iters=iters)
+    return Tq, am
+
+
+def assert_pack_equal(Tq, am, tq_or, am_or, what="pack"):
+    tq = Tq.cpu().numpy()
+    a = am.cpu().numpy().view(np.uint32)
+    bad_t = np.argwhere(tq != tq_or)
+    bad_a = np.argwhere(a != am_or)
+    assert bad_a.size == 0, f"{what}: {len(bad_a)} parameter words differ, first {bad_a[:3].tolist()}"
+    assert bad_t.size == 0, f"{what}: {len(bad_t)} code bytes differ, first {bad_t[:3].tolist()}"
+
+
+def magnitude(X, r, cols=None):
+    """Sum over blocks of (3|alpha| + |mu|) * sum |x| over the block: a bound on
+    the magnitude of every term the kernel adds (alpha 2^24 acc, (mu - alpha) S)."""
+    X = np.abs(np.asarray(X, np.float64))
+    a = np.abs(r["alpha"].astype(np.float64))
+    u = np.abs(r["mu"].astype(np.float64))
+    if cols is not None:
+        a, u = a[cols], u[cols]
+    G = a.shape[1]
+    Xs = X.reshape(X.shape[0], G, -1).sum(axis=2)          # [M, G]
+    return Xs @ (3 * a + u).T
+
+
+def assert_tern_close(Yg, Y64, A, what):
+    Yg = np.asarray(Yg, np.float64)
+    err = np.abs(Yg - Y64)
+    tol = 0.5 * ulp16(Y64) * (1 + 1e-9) + REL_TERM * A
+    bad = err > tol
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound, first {i}: "
+                             f"gpu {Yg[i]} oracle {Y64[i]} tol {tol[i]}")
+    return rel_l2(Yg, Y64)
+
+
+@pytest.mark.parametrize("N,K", [(7, 128), (64, 512), (301, 1024), (1000, 4096)])
+def test_pack_bit_exact(N, K):
+    log(f"pack_ternary N={N} K={K}")
+    wl = WT.TernWorkload("t", M=1, K=K, N=N, x_kind="normal", seed=N + K)
+    Wt = WT.make_tern_weights(wl)
+    Wt[0] = 0.0                                  # zero row
+    if N > 2:
+        Wt[2, :128] = 0.25                       # constant block row (exact mean)
+        Wt[2, 5] = -0.25                         # ... but one entry: T fits it with alpha
+    _, tq_or, am_or = oracle_pack(Wt)
+    Tq, am = gpu_pack(Wt)
+    assert_pack_equal(Tq, am, tq_or, am_or, f"pack N={N} K={K}")
+
+
+@pytest.mark.parametrize("iters", [0, 1, 3])
+def test_pack_iteration_counts(iters):
+    log(f"pack_ternary iters={iters}")
+    wl = WT.TernWorkload("t", M=1, K=768, N=96, x_kind="normal", seed=11 + iters)
+    Wt = WT.make_tern_weights(wl)
+    _, tq_or, am_or = oracle_pack(Wt, iters)
+    Tq, am = gpu_pack(Wt, iters)
+    assert_pack_equal(Tq, am, tq_or, am_or, f"pack iters={iters}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (5, 100, 512), (16, 64, 4096), (17, 130, 1024),
+                                   (33, 257, 2048), (64, 192, 1280), (64, 1000, 8192),
+                                   (2, 3000, 384), (40, 77, 640)])
+def test_gemm_parity(M, N, K):
+    log(f"ternary_gemm M={M} N={N} K={K}")
+    wl = WT.TernWorkload("t", M=M, K=K, N=N, x_kind="silu_product" if M % 2 else "normal",
+                         seed=M * 7 + N)
+    inp = WT.make_tern_inputs(wl)
+    r, tq_or, am_or = oracle_pack(inp["Wt"])
+    Y64 = TO.ternary_linear(inp["X"], r)
+    Y = W().ternary_gemm(to_dev(inp["X"]), to_dev(tq_or), to_dev(am_or.view(np.int32)))
+    rel = assert_tern_close(Y.cpu().numpy(), Y64, magnitude(inp["X"], r), f"M={M} N={N} K={K}")
+    log(f"  rel L2 {rel:.2e}")
+
+
+def test_gemm_zero_rows_and_m0():
+    torch, dev = torch_dev()
+    wl = WT.TernWorkload("t", M=9, K=256, N=64, x_kind="normal", seed=3)
+    inp = WT.make_tern_inputs(wl)
+    X = inp["X"].copy()
+    X[4] = 0
+    r, tq_or, am_or = oracle_pack(inp["Wt"])
+    Y = W().ternary_gemm(to_dev(X), to_dev(tq_or), to_dev(am_or.view(np.int32))).cpu().numpy()
+    assert np.all(Y[4] == 0)
+    assert_tern_close(Y, TO.ternary_linear(X, r), magnitude(X, r), "zero row")
+    Y0 = W().ternary_gemm(torch.empty((0, 256), dtype=torch.float16, device=dev), to_dev(tq_or),
+                          to_dev(am_or.view(np.int32)))
+    assert tuple(Y0.shape) == (0, 64)
+
+
+@pytest.mark.parametrize("name", ["tern_down70b_m8", "tern_gateup70b_m64", "tern_down70b_m1"])
+def test_full_size_sampled(name):
+    """The full decode shape in the launch configuration the benchmark times:
+    the GPU packs the whole matrix; sampled weight rows are packed by the
+    oracle and must match bit for bit; the matching output columns are
+    compared with the oracle's layer on those rows."""
+    log(f"full size {name}")
+    torch, dev = torch_dev()
+    wl = WT.get_tern(name)
+    inp = WT.make_tern_inputs(wl)
+    Tq, am = gpu_pack(inp["Wt"])
+    Y = W().ternary_gemm(to_dev(inp["X"]), Tq, am).cpu().numpy()
+    rng = np.random.default_rng(5)
+    cols = np.unique(np.concatenate([[0, 1, wl.N - 1], rng.choice(wl.N, 21, replace=False)]))
+    Ws = WT.make_tern_weights(wl, rows=cols)
+    np.testing.assert_array_equal(Ws, inp["Wt"][cols])
+    r, tq_or, am_or = oracle_pack(Ws)
+    idx = torch.from_numpy(cols).to(dev)
+    assert_pack_equal(Tq[idx], am[idx], tq_or, am_or, f"{name} sampled rows")
+    Y64 = TO.ternary_linear(inp["X"], r)
+    rel = assert_tern_close(Y[:, cols], Y64, magnitude(inp["X"], r), name)
+    log(f"  rel L2 {rel:.2e}")
+    del Tq, am
+    torch.cuda.empty_cache()

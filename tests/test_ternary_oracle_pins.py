@@ -30,7 +30,7 @@ def test_golden_itf_hand_case():
     assert float(r["alpha"][0, 0]) == g["alpha_fp16"]
     assert float(r["mu"][0, 0]) == g["mu_fp16"]
     assert r["T"][0].tolist() == g["T"]
-    assert TO.pack_ternary(r["T"])[0].tolist() == g["packed"]
+    assert TO.pack_ternary(np.array([g["packed_row16"]]))[0].tolist() == g["packed"]
 
 
 def test_alpha_mu_are_least_squares_fit():
@@ -124,10 +124,15 @@ def test_pack_round_trip_and_bits():
     T = rng.integers(-1, 2, size=(3, 64)).astype(np.int8)
     b = TO.pack_ternary(T)
     np.testing.assert_array_equal(TO.unpack_ternary(b), T)
+    # word 1 of row 2, written out bit by bit
     want = 0
-    for i in range(4):
-        want |= (int(T[2, 20 + i]) + 1) << (2 * i)
-    assert int(b[2, 5]) == want
+    for s_ in range(8):
+        want |= (int(T[2, 16 + 2 * s_]) + 1) << (2 * s_)
+        want |= (int(T[2, 16 + 2 * s_ + 1]) + 1) << (16 + 2 * s_)
+    got = int.from_bytes(bytes(b[2, 4:8].tolist()), "little")
+    assert got == want
+    p = TO.pack_params(np.array([[1.5]], np.float16), np.array([[-0.25]], np.float16))
+    assert int(p[0, 0]) == 0x3E00 | (0xB400 << 16)
 
 
 def test_layer_block_sum_equals_dense_matmul():

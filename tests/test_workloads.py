@@ -66,3 +66,21 @@ def test_kv_workloads_deterministic_and_shaped():
     assert k.shape == (17, wl.heads_kv, wl.head_dim) and v.dtype == np.float16
     for w in WKV.KV_WORKLOADS.values():
         assert w.max_seq % 32 == 0 and w.heads_q % w.heads_kv == 0
+
+
+def test_ternary_workloads_deterministic_and_row_sampling():
+    from workloads import ternary as WT
+    wl = WT.TernWorkload("t", M=3, K=256, N=2100, x_kind="silu_product", seed=4)
+    a = WT.make_tern_inputs(wl)
+    b = WT.make_tern_inputs(wl)
+    assert a["X"].dtype == np.float16 and a["X"].shape == (3, 256)
+    assert a["Wt"].dtype == np.float32 and a["Wt"].shape == (2100, 256)
+    np.testing.assert_array_equal(a["X"], b["X"])
+    np.testing.assert_array_equal(a["Wt"], b["Wt"])
+    rows = [0, 1023, 1024, 2099, 5]
+    np.testing.assert_array_equal(WT.make_tern_weights(wl, rows=rows), a["Wt"][rows])
+    # blocks carry their own offsets: block means spread well beyond sampling noise
+    means = a["Wt"].reshape(2100, 2, 128).mean(axis=2) / np.abs(a["Wt"]).mean()
+    assert means.std() > 0.15
+    for name, w in WT.TERN_WORKLOADS.items():
+        assert w.K % 128 == 0 and w.M <= 64, name

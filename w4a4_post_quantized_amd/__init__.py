@@ -24,6 +24,8 @@ __all__ = [
     "KV_HEAD_DIM", "KvCache", "kv_cache_bytes", "kv_query_factor", "kv_append",
     "attn_decode_workspace_bytes", "attn_decode",
     "pack_weights_bits", "transform_quant_bits", "linear_bits",
+    "TERNARY_BLOCK", "TERNARY_MAX_M", "pack_ternary", "ternary_gemm_workspace_bytes",
+    "ternary_gemm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so")
@@ -41,11 +43,14 @@ EXPORTED_SYMBOLS = [
     "w4a4_kv_cache_bytes", "w4a4_kv_query_factor_workspace_bytes", "w4a4_kv_query_factor",
     "w4a4_kv_append", "w4a4_attn_decode_workspace_bytes", "w4a4_attn_decode",
     "w4a4_pack_weights_bits", "w4a4_transform_quant_bits", "w4a4_linear_bits",
+    "w4a4_pack_ternary", "w4a4_ternary_gemm_workspace_bytes", "w4a4_ternary_gemm",
 ]
 
 DECODE_SYNC_BYTES = 1024          # W4A4_DECODE_SYNC_BYTES
 DECODE_SYNC_ERROR_WORD = 128      # W4A4_DECODE_SYNC_ERROR_WORD
 KV_HEAD_DIM = 128                 # W4A4_KV_HEAD_DIM
+TERNARY_BLOCK = 128               # W4A4_TERNARY_BLOCK
+TERNARY_MAX_M = 64                # W4A4_TERNARY_MAX_M
 
 
 class W4A4Error(RuntimeError):
@@ -110,6 +115,9 @@ def lib() -> ctypes.CDLL:
                                                          vp, vp, vp, sz, vp]),
             "w4a4_linear_bits": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, i32, dp, vp,
                                                 vp, vp, vp, vp, sz, vp]),
+            "w4a4_pack_ternary": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
+            "w4a4_ternary_gemm_workspace_bytes": (sz, [i32, i32, i32]),
+            "w4a4_ternary_gemm": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
             "w4a4_kv_cache_bytes": (ctypes.c_int, [i32, i32, i32, i32, szp, szp, szp]),
             "w4a4_kv_query_factor_workspace_bytes": (sz, [i32, i32]),
             "w4a4_kv_query_factor": (ctypes.c_int, [vp, i32, i32, vp, vp, sz, vp]),
@@ -556,4 +564,41 @@ def linear_bits(X, P1, P2, bits: int, desc: WeightDesc, Wq, s_w, z_w=None, c=Non
                                   int(bits), ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y),
                                   _p(ws), nb if ws is None else ws.numel(), _stream(stream)),
            "w4a4_linear_bits")
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# Ternary weights (W1.58A16)
+# ---------------------------------------------------------------------------
+def pack_ternary(Wt, iters: int = 10, stream=None):
+    """Ternarize fp32 weights [N, K]: returns (Tq uint8 [N, K/4], am int32 [N, K/128]
+    holding the bits of the uint32 parameter words)."""
+    torch = _torch()
+    N, K = Wt.shape
+    _need(Wt, torch.float32, (N, K), "Wt")
+    Tq = torch.empty((N, K // 4), dtype=torch.uint8, device=Wt.device)
+    am = torch.empty((N, max(K // TERNARY_BLOCK, 1)), dtype=torch.int32, device=Wt.device)
+    _check(lib().w4a4_pack_ternary(_p(Wt), N, K, int(iters), _p(Tq), _p(am), _stream(stream)),
+           "w4a4_pack_ternary")
+    return Tq, am
+
+
+def ternary_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().w4a4_ternary_gemm_workspace_bytes(M, N, K)
+
+
+def ternary_gemm(X, Tq, am, out=None, ws=None, stream=None):
+    """Y [M, N] fp16 = X [M, K] fp16 times the ternary weights (M <= TERNARY_MAX_M)."""
+    torch = _torch()
+    M, K = X.shape
+    N = Tq.shape[0]
+    _need(X, torch.float16, (M, K), "X")
+    _need(Tq, torch.uint8, (N, K // 4), "Tq")
+    _need(am, torch.int32, (N, K // TERNARY_BLOCK), "am")
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
+    nb = ternary_gemm_workspace_bytes(M, N, K)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_ternary_gemm(_p(X), M, N, K, _p(Tq), _p(am), _p(Y), _p(ws),
+                                   nb if ws is None else ws.numel(), _stream(stream)),
+           "w4a4_ternary_gemm")
     return Y

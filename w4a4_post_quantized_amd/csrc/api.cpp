@@ -666,4 +666,61 @@ int w4a4_attn_decode(const uint16_t* q, int32_t batch, int32_t heads_q, int32_t 
     return hip_status(e, "w4a4_attn_decode");
 }
 
+// ---------------------------------------------------------------------------
+// Ternary weights (W1.58A16)
+// ---------------------------------------------------------------------------
+namespace {
+int check_tern(int32_t M, int32_t N, int32_t K) {
+    REQUIRE(M >= 0, W4A4_ERR_INVALID_ARG, "M = %d is negative", M);
+    REQUIRE(N >= 1, W4A4_ERR_INVALID_ARG, "N = %d must be >= 1", N);
+    REQUIRE(K >= W4A4_TERNARY_BLOCK && K % W4A4_TERNARY_BLOCK == 0 && K <= W4A4_MAX_K,
+            W4A4_ERR_UNSUPPORTED, "K = %d must be a multiple of %d in [%d, %d]", K,
+            W4A4_TERNARY_BLOCK, W4A4_TERNARY_BLOCK, W4A4_MAX_K);
+    REQUIRE(M <= W4A4_TERNARY_MAX_M, W4A4_ERR_UNSUPPORTED,
+            "M = %d: the ternary product is built for decode batches of at most %d tokens", M,
+            W4A4_TERNARY_MAX_M);
+    return W4A4_OK;
+}
+}  // namespace
+
+int w4a4_pack_ternary(const float* Wt, int32_t N, int32_t K, int32_t iters, uint8_t* Tq,
+                      uint32_t* am, void* stream) {
+    if (int s = check_tern(0, N, K)) return s;
+    REQUIRE(iters >= 0 && iters <= 1000, W4A4_ERR_INVALID_ARG, "iters = %d outside [0, 1000]",
+            iters);
+    REQUIRE_PTR(Wt);
+    REQUIRE_PTR(Tq);
+    REQUIRE_PTR(am);
+    REQUIRE_ALIGNED(Wt);
+    REQUIRE_ALIGNED(Tq);
+    REQUIRE_ALIGNED(am);
+    hipError_t e = w4a4::tern_pack_launch(Wt, N, K, iters, Tq, am, static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_pack_ternary");
+}
+
+size_t w4a4_ternary_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+    if (check_tern(M, N, K) != W4A4_OK) return 0;
+    return w4a4::tern_workspace_bytes(M, N, K);
+}
+
+int w4a4_ternary_gemm(const uint16_t* X, int32_t M, int32_t N, int32_t K, const uint8_t* Tq,
+                      const uint32_t* am, uint16_t* Y, void* ws, size_t ws_bytes, void* stream) {
+    if (int s = check_tern(M, N, K)) return s;
+    if (M == 0) return ok();
+    REQUIRE_PTR(X);
+    REQUIRE_PTR(Tq);
+    REQUIRE_PTR(am);
+    REQUIRE_PTR(Y);
+    REQUIRE_PTR(ws);
+    REQUIRE_ALIGNED(X);
+    REQUIRE_ALIGNED(Tq);
+    REQUIRE_ALIGNED(am);
+    REQUIRE_ALIGNED(Y);
+    REQUIRE_ALIGNED(ws);
+    const size_t need = w4a4::tern_workspace_bytes(M, N, K);
+    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    hipError_t e = w4a4::tern_gemm_launch(X, M, N, K, Tq, am, Y, ws, static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_ternary_gemm");
+}
+
 }  // extern "C"

@@ -104,6 +104,29 @@ int attn_chunk(int batch, int heads_kv, int max_seq);
 size_t attn_partial_bytes(int batch, int heads_q, int heads_kv, int max_seq, int chunk);
 hipError_t attn_decode_launch(const AttnArgs& a, hipStream_t stream);
 
+// ---- ternary weights, W1.58A16 (ternary.hip) --------------------------------
+struct TernArgs {
+    const uint16_t* X;      // fp16 [M][K]
+    const uint8_t* Tq;      // [N][K/4], 16 codes per 32-bit word
+    const uint32_t* am;     // [N][K/128]: alpha fp16 bits low, mu high
+    const float* S;         // [K/128][Mpad] block row sums of X
+    uint16_t* Y;            // fp16 [M][N] (no K-split)
+    float* part;            // [splits][M][N] (K-split) or nullptr
+    int M, N, K, Mpad, gps; // gps: blocks of K per split
+};
+struct TernPlan {
+    int ms;       // 16-row subtiles per wave (1, 2 or 4)
+    int Mpad;     // M rounded up to 64
+    int gps;      // blocks of 128 per K-split
+    int splits;   // K-splits
+};
+TernPlan tern_plan(int M, int N, int K, int cus);
+size_t tern_workspace_bytes(int M, int N, int K);   // for this device
+hipError_t tern_pack_launch(const float* Wt, int N, int K, int iters, uint8_t* Tq, uint32_t* am,
+                            hipStream_t stream);
+hipError_t tern_gemm_launch(const uint16_t* X, int M, int N, int K, const uint8_t* Tq,
+                            const uint32_t* am, uint16_t* Y, void* ws, hipStream_t stream);
+
 // ---- offline weight preparation (weights.hip) ------------------------------
 size_t merge_workspace_bytes(int n1, int n2, int K);
 // returns hipSuccess and sets *singular when a factor has no usable pivot
