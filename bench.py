@@ -29,6 +29,13 @@ tokens, then w4a4_attn_decode over the ragged contexts (up to 8192 cached
 tokens).  Its roofline unit is the w4a4_attn_decode call (query transform,
 chunked partial attention, merge) priced at the cache bytes it must read.
 
+With --workload tern_down70b_m{1,8,64}|tern_gateup70b_m{1,8,64} the step is
+one w4a4_ternary_gemm call: the ternary-weight (W1.58A16, PT2-LLM page) decode
+product Y = X · (alpha T + mu)^T with fp16 activations, weights ternarized on
+the GPU beforehand (ITF, 2-bit codes and one (alpha, mu) word per row and
+block of 128).  Its roofline unit is that call, priced at the packed weight
+bytes plus the activations and outputs.
+
 Prints ONE JSON line.  `value` is TOPS of the whole layer (2*M*N*K integer
 ops per step / step time).  `roofline` reports the dominant kernel (the GEMM)
 against the INT8 MFMA peak (prefill) or HBM bandwidth (decode), its duration
@@ -62,7 +69,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qkv8b",
                     help="linear: qkv8b gateup8b down8b gateup70b down70b_m{1,8,64}; "
-                         "attention over the INT4 KV cache: attn8b attn70b")
+                         "attention over the INT4 KV cache: attn8b attn70b; ternary-weight "
+                         "decode: tern_down70b_m{1,8,64} tern_gateup70b_m{1,8,64}")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--path", choices=["two", "single"], default="two",
@@ -227,6 +235,10 @@ def main():
 
     if args.workload in WKV.KV_WORKLOADS:
         attn_main(args)
+        return
+    from workloads import ternary as WT
+    if args.workload in WT.TERN_WORKLOADS:
+        tern_main(args)
         return
 
     wl = WL.get(args.workload)
@@ -604,6 +616,123 @@ def attn_main(args):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = attn_cpu_baseline(wl, st, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# ternary-weight decode product
+# ---------------------------------------------------------------------------
+TERN_BYTES_PER_WEIGHT = 0.25 + 4.0 / 128       # 2-bit code + one 32-bit word per 128
+
+
+def tern_bytes(wl):
+    """Algorithmic bytes of one w4a4_ternary_gemm call: the packed codes and
+    block parameters, the fp16 activations and the fp16 outputs."""
+    G = wl.K // 128
+    return wl.N * wl.K // 4 + 4 * wl.N * G + 2 * wl.M * wl.K + 2 * wl.M * wl.N
+
+
+def tern_cpu_baseline(wl, X, budget_s):
+    """The oracle's ternary layer on chunks of output columns until `budget_s`
+    of layer time (each chunk ternarized by the oracle first, untimed; the
+    ternarization is offline work), projected to all N columns."""
+    from oracle import ternary_oracle as TO
+    from workloads import ternary as WT
+    threads = os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
+    chunk = 256
+    done, t_used, wall0 = 0, 0.0, time.perf_counter()
+    for r0 in range(0, wl.N, chunk):
+        rows = np.arange(r0, min(wl.N, r0 + chunk))
+        r = TO.itf_ternarize(WT.make_tern_weights(wl, rows=rows))        # untimed
+        t0 = time.perf_counter()
+        TO.ternary_linear(X, r)
+        t_used += time.perf_counter() - t0
+        done += rows.size
+        if t_used >= budget_s or time.perf_counter() - wall0 >= 3 * budget_s:
+            break
+    t_layer = t_used / done * wl.N
+    ops = 2.0 * wl.M * wl.N * wl.K
+    return {"value": ops / t_layer / 1e12, "unit": "TOPS", "cores": int(threads),
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"the float64 layer on {done} of the {wl.N} output columns (weights "
+                      f"ternarized by the oracle untimed), {t_used:.2f} s, projected to all "
+                      f"columns",
+            "us_per_layer": t_layer * 1e6}
+
+
+def tern_main(args):
+    import torch
+    import w4a4_post_quantized_amd as L
+    from workloads import ternary as WT
+
+    wl = WT.get_tern(args.workload)
+    inp = WT.make_tern_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    X = torch.from_numpy(inp["X"]).to(dev)
+    Wt = torch.from_numpy(inp["Wt"]).to(dev)
+    del inp["Wt"]
+    Tq, am = L.pack_ternary(Wt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    del Wt
+    wbytes = Tq.numel() + 4 * am.numel()
+    copies = max(3, -(-MALL_BYTES // wbytes) + 1)
+    packs = [(Tq, am)] + [(Tq.clone(), am.clone()) for _ in range(copies - 1)]
+    Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    ws = torch.empty(max(1, L.ternary_gemm_workspace_bytes(wl.M, wl.N, wl.K)), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        t, a = packs[i % copies]
+        L.ternary_gemm(X, t, a, out=Y, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    call_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    dist = event_stats(step, max(20, args.steps))
+
+    gb = tern_bytes(wl)
+    achieved = gb / (call_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "kernel": "w4a4_ternary_gemm (k_tern_rowsum + k_tern_gemm + k_tern_reduce)",
+            "kernel_us": round(call_us, 2), "bytes": gb,
+            "bytes_per_unit": f"{TERN_BYTES_PER_WEIGHT} B per weight (2-bit code, 32-bit "
+                              "(alpha, mu) word per 128) plus fp16 X and Y",
+            "traffic": traffic_from_profiles("tern", wl.name, "ternary.hip"),
+            "timing": "mean over HIP events around back-to-back calls on the launch stream, "
+                      f"{copies} weight copies rotated past the 256 MiB Infinity Cache; "
+                      "per_launch_us from events around each call",
+            "per_launch_us": dist}
+    ops = 2.0 * wl.M * wl.N * wl.K
+    res = {
+        "metric": METRIC, "value": round(ops / t_step / 1e12, 3), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "ternary weights (2-bit codes), fp16 activations, fp16 MFMA, fp32 accumulation",
+        "data": "synthetic (seeded; weights with per-row scales, per-block offsets and x8 "
+                "outliers; decode activations)",
+        "config": {"workload": wl.description, "name": wl.name, "M": wl.M, "K": wl.K,
+                   "N": wl.N, "block": 128, "weight_copies_rotated": copies},
+        "us_per_layer": round(t_step * 1e6, 2),
+        "path": "w4a4_ternary_gemm",
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = tern_cpu_baseline(wl, inp["X"], args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -283,10 +283,13 @@ int w4a4_linear_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const
  *
  * Layouts:
  *   Tq  uint8 [N][K/4]: two-bit codes c = t + 1 in little-endian 32-bit words
- *       of 16 codes, code 16w + 2s at bits 2s and code 16w + 2s + 1 at bits
- *       16 + 2s of word w (s = 0 .. 7);
- *   am  uint32 [N][K/128]: the block's alpha as fp16 bits in the low half and
- *       mu in the high half (both one rounding from float64). */
+ *       of 16 codes (code 2s of a word at bits 2s, code 2s + 1 at bits
+ *       16 + 2s).  The 32 codes 128 g + 32 q .. + 31 of block g and lane group
+ *       q = 0..3 form an 8-byte piece; in a row, the pieces of a pair of blocks
+ *       (2p, 2p + 1) sit at bytes 64 p + 16 q + 8 (g - 2p), and an unpaired
+ *       last block (odd K/128) has piece q at bytes 64 p + 8 q;
+ *   am  uint32 [K/128][N] (block-major): the block's alpha as fp16 bits in the
+ *       low half and mu in the high half (both one rounding from float64). */
 #define W4A4_TERNARY_BLOCK 128
 #define W4A4_TERNARY_MAX_M 64
 
@@ -297,14 +300,16 @@ int w4a4_linear_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const
 int w4a4_pack_ternary(const float* Wt, int32_t N, int32_t K, int32_t iters, uint8_t* Tq,
                       uint32_t* am, void* stream);
 
-/* Bytes of workspace w4a4_ternary_gemm needs (0 for invalid shapes). */
+/* Bytes of workspace w4a4_ternary_gemm needs: 0 when the shape's output
+ * tiles fill the GPU by themselves (ws may then be NULL), else the fp32
+ * partial sums of a K split across workgroups; 0 for invalid shapes too. */
 size_t w4a4_ternary_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* Y [M][N] fp16 = X [M][K] fp16 · Ŵ^T for decode-sized batches,
  * 0 <= M <= W4A4_TERNARY_MAX_M (larger M returns W4A4_ERR_UNSUPPORTED).  The
  * fp16 MFMA products are exact (codes enter as the fp16 values c * 2^-14) and
- * the sums run in fp32.  Up to three launches (block row sums of X, the
- * product with a split of K over workgroups, the merge of the splits). */
+ * the sums run in fp32.  One launch; two when the workspace is non-empty (the
+ * product with K split across workgroups, then the merge of the splits). */
 int w4a4_ternary_gemm(const uint16_t* X, int32_t M, int32_t N, int32_t K, const uint8_t* Tq,
                       const uint32_t* am, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
 

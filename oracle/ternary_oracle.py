@@ -32,12 +32,17 @@ Readings where the page is silent (restated with the design notes):
   reordering is a column permutation, which leaves X W^T unchanged (pinned for
   the 4-bit layer).
 
-Storage (this library's layout contract): two bits per code, c = t + 1 in
-{0, 1, 2}; a row is a sequence of little-endian 32-bit words of 16 codes, and
-in word w code 16 w + 2 s sits at bits 2 s and code 16 w + 2 s + 1 at bits
-16 + 2 s (s = 0 .. 7): the even codes in the low half, the odd codes in the
-high half.  The per-block parameters are stored as one 32-bit word, alpha's
-fp16 bits in the low half and mu's in the high half.
+Storage (this library's layout contract, not the page's): two bits per code,
+c = t + 1 in {0, 1, 2}, sixteen codes per little-endian 32-bit word, code
+16 w + 2 s at bits 2 s of word w and code 16 w + 2 s + 1 at bits 16 + 2 s
+(s = 0 .. 7): the even codes in the low half, the odd codes in the high half.
+The 32 codes 128 g + 32 q .. 128 g + 32 q + 31 of block g and lane group
+q = 0..3 form an 8-byte piece (two words).  Within a row, the pieces of a pair
+of blocks (2 p, 2 p + 1) sit at bytes 64 p + 16 q + 8 (g - 2 p): ordered by
+lane group, then block; an unpaired last block (odd K / 128) has piece q at
+64 p + 8 q.  The per-block parameters are one 32-bit word per (block, row),
+block-major [K / 128][N], alpha's fp16 bits in the low half and mu's in the
+high half.
 """
 from __future__ import annotations
 
@@ -45,8 +50,8 @@ import numpy as np
 
 from .w4a4_oracle import fp16_rne
 
-__all__ = ["TERN_BLOCK", "itf_ternarize", "pack_ternary", "unpack_ternary", "pack_params",
-           "dequant_ternary", "ternary_linear", "itf_objective"]
+__all__ = ["TERN_BLOCK", "itf_ternarize", "pack_words", "piece_offsets", "pack_ternary",
+           "unpack_ternary", "pack_params", "dequant_ternary", "ternary_linear", "itf_objective"]
 
 TERN_BLOCK = 128
 
@@ -108,9 +113,9 @@ def itf_objective(Wt, T, alpha, mu, block: int = TERN_BLOCK):
     return (d * d).sum(axis=2)
 
 
-def pack_ternary(T):
-    """codes [..., K] in {-1, 0, 1} (K a multiple of 16) -> bytes [..., K/4]:
-    per 16 codes one little-endian word, code 2s at bits 2s, code 2s+1 at
+def pack_words(T):
+    """codes [..., K] in {-1, 0, 1} (K a multiple of 16) -> little-endian
+    32-bit words [..., K/16], code 2s of a word's 16 at bits 2s, code 2s+1 at
     bits 16 + 2s."""
     c = np.asarray(T).astype(np.int64) + 1
     K = c.shape[-1]
@@ -121,24 +126,61 @@ def pack_ternary(T):
     for s_ in range(8):
         word |= cw[..., 2 * s_] << (2 * s_)
         word |= cw[..., 2 * s_ + 1] << (16 + 2 * s_)
-    return word.astype("<u4").view(np.uint8).reshape(c.shape[:-1] + (K // 4,))
+    return word.astype(np.uint32)
 
 
-def unpack_ternary(b):
+def piece_offsets(G):
+    """[G, 4]: the position, in 8-byte pieces from the row start, of the piece
+    of block g and lane group q."""
+    off = np.empty((G, 4), dtype=np.int64)
+    for g in range(G):
+        p, j = divmod(g, 2)
+        for q in range(4):
+            off[g, q] = 8 * p + 2 * q + j if 2 * p + 1 < G else 8 * p + q
+    return off
+
+
+def pack_ternary(T, block: int = TERN_BLOCK):
+    """codes [..., K] in {-1, 0, 1} (K a multiple of 128) -> bytes [..., K/4]
+    in the pair-ordered piece layout."""
+    T = np.asarray(T)
+    K = T.shape[-1]
+    if K % block:
+        raise ValueError("K must be a multiple of the block size")
+    G = K // block
+    words = pack_words(T).reshape(T.shape[:-1] + (G, 4, 2))      # [..., g, q, word]
+    out = np.zeros(T.shape[:-1] + (4 * G, 2), dtype=np.uint32)
+    off = piece_offsets(G)
+    for g in range(G):
+        for q in range(4):
+            out[..., off[g, q], :] = words[..., g, q, :]
+    return out.astype("<u4").view(np.uint8).reshape(T.shape[:-1] + (K // 4,))
+
+
+def unpack_ternary(b, block: int = TERN_BLOCK):
     b = np.ascontiguousarray(np.asarray(b, dtype=np.uint8))
-    word = b.view("<u4").astype(np.int64)
-    out = np.empty(word.shape + (16,), dtype=np.int64)
+    K = b.shape[-1] * 4
+    G = K // block
+    pieces = b.view("<u4").astype(np.int64).reshape(b.shape[:-1] + (4 * G, 2))
+    off = piece_offsets(G)
+    words = np.empty(b.shape[:-1] + (G, 4, 2), dtype=np.int64)
+    for g in range(G):
+        for q in range(4):
+            words[..., g, q, :] = pieces[..., off[g, q], :]
+    words = words.reshape(b.shape[:-1] + (K // 16,))
+    out = np.empty(words.shape + (16,), dtype=np.int64)
     for s_ in range(8):
-        out[..., 2 * s_] = ((word >> (2 * s_)) & 3) - 1
-        out[..., 2 * s_ + 1] = ((word >> (16 + 2 * s_)) & 3) - 1
-    return out.reshape(word.shape[:-1] + (word.shape[-1] * 16,)).astype(np.int8)
+        out[..., 2 * s_] = ((words >> (2 * s_)) & 3) - 1
+        out[..., 2 * s_ + 1] = ((words >> (16 + 2 * s_)) & 3) - 1
+    return out.reshape(b.shape[:-1] + (K,)).astype(np.int8)
 
 
 def pack_params(alpha, mu):
-    """fp16 alpha, mu [N, G] -> uint32 [N, G]: alpha's bits low, mu's bits high."""
+    """fp16 alpha, mu [N, G] -> uint32 [G, N] (block-major): alpha's bits low,
+    mu's bits high."""
     a = np.asarray(alpha, dtype=np.float16).view(np.uint16).astype(np.uint32)
     u = np.asarray(mu, dtype=np.float16).view(np.uint16).astype(np.uint32)
-    return a | (u << 16)
+    return np.ascontiguousarray((a | (u << 16)).T)
 
 
 def dequant_ternary(tq):

@@ -302,12 +302,12 @@ def test_ternary_entry_points_validation():
     assert L.w4a4_pack_ternary(MISALIGNED, 8, 256, 10, FAKE, FAKE, None) == -3
     assert L.w4a4_ternary_gemm(FAKE, 65, 64, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -2
     assert "decode" in last()
-    assert L.w4a4_ternary_gemm(FAKE, 4, 64, 256, FAKE, FAKE, FAKE, FAKE, 4, None) == -4
     assert L.w4a4_ternary_gemm(FAKE, 4, 64, 256, FAKE, MISALIGNED, FAKE, FAKE, 1 << 20, None) == -3
     assert L.w4a4_ternary_gemm(FAKE, 0, 64, 256, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
-    # workspace: the block row sums (rows padded to 64) and, with a K split, the partials
+    # workspace: none when the tiles fill the GPU, else fp32 partials of a K split
     assert W.ternary_gemm_workspace_bytes(65, 64, 256) == 0
     assert W.ternary_gemm_workspace_bytes(0, 64, 256) == 0
+    assert W.ternary_gemm_workspace_bytes(8, 8192, 28672) == 0
     nb = W.ternary_gemm_workspace_bytes(1, 64, 8192)
-    assert nb >= 64 * 64 * 4
-    assert nb % 4 == 0
+    assert nb > 0 and nb % (1 * 64 * 4) == 0
+    assert L.w4a4_ternary_gemm(FAKE, 4, 64, 8192, FAKE, FAKE, FAKE, None, 0, None) == -4

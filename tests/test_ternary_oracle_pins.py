@@ -30,7 +30,8 @@ def test_golden_itf_hand_case():
     assert float(r["alpha"][0, 0]) == g["alpha_fp16"]
     assert float(r["mu"][0, 0]) == g["mu_fp16"]
     assert r["T"][0].tolist() == g["T"]
-    assert TO.pack_ternary(np.array([g["packed_row16"]]))[0].tolist() == g["packed"]
+    words = TO.pack_words(np.array([g["packed_row16"]]))[0]
+    assert list(words.astype("<u4").view(np.uint8)) == g["packed"]
 
 
 def test_alpha_mu_are_least_squares_fit():
@@ -121,18 +122,34 @@ def test_dequant_bound_inside_the_grid():
 
 def test_pack_round_trip_and_bits():
     rng = np.random.default_rng(6)
-    T = rng.integers(-1, 2, size=(3, 64)).astype(np.int8)
+    T = rng.integers(-1, 2, size=(3, 384)).astype(np.int8)       # 3 blocks: a pair and one more
     b = TO.pack_ternary(T)
+    assert b.shape == (3, 96)
     np.testing.assert_array_equal(TO.unpack_ternary(b), T)
-    # word 1 of row 2, written out bit by bit
-    want = 0
-    for s_ in range(8):
-        want |= (int(T[2, 16 + 2 * s_]) + 1) << (2 * s_)
-        want |= (int(T[2, 16 + 2 * s_ + 1]) + 1) << (16 + 2 * s_)
-    got = int.from_bytes(bytes(b[2, 4:8].tolist()), "little")
-    assert got == want
-    p = TO.pack_params(np.array([[1.5]], np.float16), np.array([[-0.25]], np.float16))
-    assert int(p[0, 0]) == 0x3E00 | (0xB400 << 16)
+
+    def word(r, first):        # 16 codes from `first`, written out bit by bit
+        v = 0
+        for s_ in range(8):
+            v |= (int(T[r, first + 2 * s_]) + 1) << (2 * s_)
+            v |= (int(T[r, first + 2 * s_ + 1]) + 1) << (16 + 2 * s_)
+        return v
+
+    def at(r, byte):
+        return int.from_bytes(bytes(b[r, byte:byte + 4].tolist()), "little")
+
+    # block 1 (second of pair 0), lane group 2: codes 128 + 64 .. 128 + 95 at
+    # bytes 16*2 + 8 = 40 .. 47
+    assert at(2, 40) == word(2, 192) and at(2, 44) == word(2, 208)
+    # block 0, lane group 3: bytes 48 .. 55 hold codes 96 .. 127
+    assert at(1, 48) == word(1, 96) and at(1, 52) == word(1, 112)
+    # unpaired block 2, lane group 3: bytes 64 + 24 = 88 .. 95 hold codes 352 .. 383
+    assert at(0, 88) == word(0, 352) and at(0, 92) == word(0, 368)
+    # every piece lands once
+    off = TO.piece_offsets(5)
+    assert sorted(off.ravel().tolist()) == list(range(20))
+    p = TO.pack_params(np.array([[1.5, 2.0]], np.float16), np.array([[-0.25, 0.0]], np.float16))
+    assert p.shape == (2, 1)
+    assert int(p[0, 0]) == 0x3E00 | (0xB400 << 16) and int(p[1, 0]) == 0x4000
 
 
 def test_layer_block_sum_equals_dense_matmul():

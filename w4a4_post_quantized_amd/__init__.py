@@ -571,13 +571,13 @@ def linear_bits(X, P1, P2, bits: int, desc: WeightDesc, Wq, s_w, z_w=None, c=Non
 # Ternary weights (W1.58A16)
 # ---------------------------------------------------------------------------
 def pack_ternary(Wt, iters: int = 10, stream=None):
-    """Ternarize fp32 weights [N, K]: returns (Tq uint8 [N, K/4], am int32 [N, K/128]
+    """Ternarize fp32 weights [N, K]: returns (Tq uint8 [N, K/4], am int32 [K/128, N]
     holding the bits of the uint32 parameter words)."""
     torch = _torch()
     N, K = Wt.shape
     _need(Wt, torch.float32, (N, K), "Wt")
     Tq = torch.empty((N, K // 4), dtype=torch.uint8, device=Wt.device)
-    am = torch.empty((N, max(K // TERNARY_BLOCK, 1)), dtype=torch.int32, device=Wt.device)
+    am = torch.empty((max(K // TERNARY_BLOCK, 1), N), dtype=torch.int32, device=Wt.device)
     _check(lib().w4a4_pack_ternary(_p(Wt), N, K, int(iters), _p(Tq), _p(am), _stream(stream)),
            "w4a4_pack_ternary")
     return Tq, am
@@ -594,7 +594,7 @@ def ternary_gemm(X, Tq, am, out=None, ws=None, stream=None):
     N = Tq.shape[0]
     _need(X, torch.float16, (M, K), "X")
     _need(Tq, torch.uint8, (N, K // 4), "Tq")
-    _need(am, torch.int32, (N, K // TERNARY_BLOCK), "am")
+    _need(am, torch.int32, (K // TERNARY_BLOCK, N), "am")
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
     nb = ternary_gemm_workspace_bytes(M, N, K)
     ws = _ws(nb, X.device, ws)

@@ -711,14 +711,16 @@ int w4a4_ternary_gemm(const uint16_t* X, int32_t M, int32_t N, int32_t K, const 
     REQUIRE_PTR(Tq);
     REQUIRE_PTR(am);
     REQUIRE_PTR(Y);
-    REQUIRE_PTR(ws);
     REQUIRE_ALIGNED(X);
     REQUIRE_ALIGNED(Tq);
     REQUIRE_ALIGNED(am);
     REQUIRE_ALIGNED(Y);
-    REQUIRE_ALIGNED(ws);
     const size_t need = w4a4::tern_workspace_bytes(M, N, K);
-    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (need > 0) {
+        REQUIRE(ws != nullptr && ws_bytes >= need, W4A4_ERR_WORKSPACE,
+                "workspace %zu < %zu bytes", ws == nullptr ? size_t{0} : ws_bytes, need);
+        REQUIRE_ALIGNED(ws);
+    }
     hipError_t e = w4a4::tern_gemm_launch(X, M, N, K, Tq, am, Y, ws, static_cast<hipStream_t>(stream));
     return hip_status(e, "w4a4_ternary_gemm");
 }

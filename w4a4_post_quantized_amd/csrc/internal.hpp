@@ -107,17 +107,16 @@ hipError_t attn_decode_launch(const AttnArgs& a, hipStream_t stream);
 // ---- ternary weights, W1.58A16 (ternary.hip) --------------------------------
 struct TernArgs {
     const uint16_t* X;      // fp16 [M][K]
-    const uint8_t* Tq;      // [N][K/4], 16 codes per 32-bit word
-    const uint32_t* am;     // [N][K/128]: alpha fp16 bits low, mu high
-    const float* S;         // [K/128][Mpad] block row sums of X
+    const uint8_t* Tq;      // [N][K/4], 16 codes per 32-bit word, pieces in pair order
+    const uint32_t* am;     // [K/128][N]: alpha fp16 bits low, mu high
     uint16_t* Y;            // fp16 [M][N] (no K-split)
     float* part;            // [splits][M][N] (K-split) or nullptr
-    int M, N, K, Mpad, gps; // gps: blocks of K per split
+    int M, N, K, pps;       // pps: block pairs of K per split
 };
 struct TernPlan {
-    int ms;       // 16-row subtiles per wave (1, 2 or 4)
-    int Mpad;     // M rounded up to 64
-    int gps;      // blocks of 128 per K-split
+    int ms;       // 16-row subtiles per wave (1 or 2)
+    int ns;       // 16-column subtiles per wave
+    int pps;      // pairs of blocks of 128 per K-split
     int splits;   // K-splits
 };
 TernPlan tern_plan(int M, int N, int K, int cus);

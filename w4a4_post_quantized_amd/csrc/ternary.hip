@@ -8,12 +8,17 @@
 // size 128 of its training strategy.
 //
 // Storage: T as two-bit codes c = t + 1 in words of 16 codes (code 2s at bits
-// 2s, code 2s + 1 at bits 16 + 2s), a row of K codes in K/4 bytes; the block
-// parameters as one word per (row, block), alpha's fp16 bits low, mu's high.
+// 2s, code 2s + 1 at bits 16 + 2s), a row of K codes in K/4 bytes.  The 32
+// codes that one MFMA lane group q (q = 0..3) takes from block g, codes
+// 128 g + 32 q .. + 31, form an 8-byte piece; a pair of blocks (2p, 2p + 1)
+// stores its 8 pieces at bytes 64 p + 16 q + 8 (g - 2p) of the row, so one
+// lane reads both blocks' codes with one 16-byte load and 4 lanes read 64
+// contiguous bytes; an unpaired last block stores piece q at 64 p + 8 q.  The
+// block parameters are one word per (block, row), block-major [K/128][N],
+// alpha's fp16 bits low, mu's high.
 //
 // Kernels:
 //   k_tern_pack    offline ITF in float64, one workgroup per (row, block);
-//   k_tern_rowsum  S[g][m] = sum of X[m] over block g (fp32);
 //   k_tern_gemm    the product for decode-sized M on fp16 MFMA: a code c
 //                  is moved into the exponent field of an fp16 half, which
 //                  makes it the normal number c * 2^-14 (0, 2^-14, 2^-13;
@@ -22,7 +27,8 @@
 //                  block adds alpha 2^14 acc + (mu - alpha) S to the output.
 //                  (Codes as fp16 subnormals c * 2^-24 cost the same but
 //                  measured up to 76 fp16 ulps off on the MFMA sum.)
-//   k_tern_reduce  sums the K-split partials into fp16.
+//   k_tern_reduce  sums the partials of a K split across workgroups (only
+//                  for shapes whose tiles cannot fill the GPU) into fp16.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -89,29 +95,16 @@ __global__ __launch_bounds__(kTB) void k_tern_pack(const float* __restrict__ Wt,
     __syncthreads();
     atomicOr(&words[t >> 4], c << (16 * (t & 1) + 2 * ((t & 15) >> 1)));
     __syncthreads();
-    if (t < kTB / 16)
-        reinterpret_cast<uint32_t*>(Tq + static_cast<size_t>(row) * (K / 4) + g * (kTB / 4))[t] =
-            words[t];
-    if (t == 0) am[static_cast<size_t>(row) * G + g] = static_cast<uint32_t>(a16) | (static_cast<uint32_t>(u16) << 16);
-}
-
-// ---------------------------------------------------------------------------
-// S[g][m] = sum_k in block g of X[m][k] (fp32, rows padded to Mpad), one wave
-// per (m, g)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_tern_rowsum(const uint16_t* __restrict__ X, int M,
-                                                          int K, int Mpad, float* __restrict__ S) {
-    const int G = K / kTB;
-    const int wid = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (wid >= M * G) return;
-    const int m = wid / G;
-    const int g = wid % G;
-    const int lane = threadIdx.x & 63;
-    const uint32_t two = *reinterpret_cast<const uint32_t*>(X + static_cast<size_t>(m) * K + g * kTB + 2 * lane);
-    float v = h2f(static_cast<uint16_t>(two & 0xFFFFu)) + h2f(static_cast<uint16_t>(two >> 16));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) S[static_cast<size_t>(g) * Mpad + m] = v;
+    if (t < kTB / 16) {
+        // word t belongs to lane group q = t / 2 (codes 32q .. 32q + 31)
+        const int q = t >> 1;
+        const int pr = g >> 1;
+        const int off = 2 * pr + 1 < G ? 64 * pr + 16 * q + 8 * (g & 1) : 64 * pr + 8 * q;
+        reinterpret_cast<uint32_t*>(Tq + static_cast<size_t>(row) * (K / 4) + off)[t & 1] = words[t];
+    }
+    if (t == 0)
+        am[static_cast<size_t>(g) * gridDim.x + row] =
+            static_cast<uint32_t>(a16) | (static_cast<uint32_t>(u16) << 16);
 }
 
 // Eight codes of one MFMA step as fp16 values c * 2^-14, in k order: register v
@@ -132,88 +125,189 @@ __device__ __forceinline__ v8h tern8(uint32_t word) {
 }
 
 // ---------------------------------------------------------------------------
-// Product for small M.  Workgroup: 4 waves side by side along N, each 16
-// output columns and MS x 16 rows; grid.z splits the blocks of K.  Lane l:
-// c16 = l % 16 (A row / B column), q4 = l / 16.  MFMA step ks of block g uses
-// k = 128 g + 32 q4 + 8 ks + j in slot j on both operands: the lane's A
-// operand is 16 contiguous bytes of X, its B operand the codes it loaded.
+// Product for small M.  A workgroup of kWaves waves owns NS x 16 output
+// columns and MS x 16 rows; its waves split the block pairs of K between them
+// (wave w takes pairs ps + w, ps + w + kWaves, ...) and add their sums in LDS
+// at the end; grid.z splits K further across workgroups only when the tiles
+// alone cannot fill the GPU.  Lane l: c16 = l % 16 (A row / B column), q4 =
+// l / 16.  MFMA step ks of block g uses k = 128 g + 32 q4 + 8 ks + j in slot
+// j on both operands: the lane's A operand is 16 contiguous bytes of X, its B
+// operand codes from the 16 bytes it loaded for the pair.  One more MFMA per
+// step against a B of ones gives the block row sum S of X in the output
+// layout.  A stage is one pair: codes, block parameters and the A operand,
+// all issued together (vector loads complete in issue order, so a load issued
+// after a stage would make its use wait for the whole stage); NBUF stages
+// rotate, NBUF - 1 of them loading while one is used.  The NS subtiles share
+// the A operand and S.
 // ---------------------------------------------------------------------------
-template <int MS>
-__global__ __launch_bounds__(kThreads) void k_tern_gemm(TernArgs a) {
+constexpr int kWaves = 8;
+
+template <int MS, int NS>
+constexpr int tern_red_floats() { return kWaves * NS * MS * 4 * 64; }
+
+template <int MS, int NS>
+struct TernStage {
+    uint4 c[NS];            // .x .y: block 2p, .z .w: block 2p + 1
+    uint32_t p[2][NS];      // (alpha, mu) words
+    v8h x[2][MS][4];        // A operands
+};
+
+template <int MS, int NS, int NBUF>
+__global__ __launch_bounds__(kWaves * 64) void k_tern_gemm(TernArgs a) {
+    __shared__ float red[tern_red_floats<MS, NS>()];
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int c16 = lane & 15;
     const int q4 = lane >> 4;
     const int G = a.K / kTB;
-    const int n = blockIdx.x * 64 + 16 * w + c16;        // this lane's output column
-    const int nc = n < a.N ? n : a.N - 1;
+    const int P = G / 2;                                   // full pairs
+    const int ps = blockIdx.z * a.pps;
+    const int pe = min(P, ps + a.pps);
+    const bool last_split = blockIdx.z == gridDim.z - 1;
     const int m0 = blockIdx.y * 16 * MS;
-    const int gs = blockIdx.z * a.gps;
-    const int ge = min(G, gs + a.gps);
-    const uint8_t* trow = a.Tq + static_cast<size_t>(nc) * (a.K / 4) + 8 * q4;
-    const uint32_t* amr = a.am + static_cast<size_t>(nc) * G;
 
-    v4f facc[MS];
+    const uint8_t* rowp[NS];
+    int ncol[NS];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) facc[ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // rows of this lane's A operand (zero past M, no load)
+    for (int s = 0; s < NS; ++s) {
+        const int n = blockIdx.x * (16 * NS) + 16 * s + c16;
+        ncol[s] = n < a.N ? n : a.N - 1;
+        rowp[s] = a.Tq + static_cast<size_t>(ncol[s]) * (a.K / 4);
+    }
+    // rows of this lane's A operand: output row r of an MFMA depends on A row
+    // r alone, so rows past M read row M - 1 (in bounds) and their outputs are
+    // dropped at the store
     const uint16_t* xrow[MS];
-    bool xok[MS];
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
-        const int m = m0 + 16 * ms + c16;
-        xok[ms] = m < a.M;
-        xrow[ms] = a.X + static_cast<size_t>(xok[ms] ? m : 0) * a.K + 32 * q4;
+        const int m = min(m0 + 16 * ms + c16, a.M - 1);
+        xrow[ms] = a.X + static_cast<size_t>(m) * a.K + 32 * q4;
     }
 
-    uint2 cw = gs < ge ? *reinterpret_cast<const uint2*>(trow + static_cast<size_t>(gs) * (kTB / 4))
-                       : make_uint2(0, 0);
-    for (int g = gs; g < ge; ++g) {
-        const uint2 cur = cw;
-        if (g + 1 < ge) cw = *reinterpret_cast<const uint2*>(trow + static_cast<size_t>(g + 1) * (kTB / 4));
-        const uint32_t p = amr[g];
-        v4f acc[MS];
+    v4f facc[NS][MS];
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms) acc[ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const uint32_t wd = ks < 2 ? cur.x : cur.y;
-            const v8h b = (ks & 1) ? tern8<1>(wd) : tern8<0>(wd);
+        for (int ms = 0; ms < MS; ++ms) facc[s][ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    using Stage = TernStage<MS, NS>;
+    auto load_x = [&](Stage& st, int j, int g) {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                st.x[j][ms][ks] = *reinterpret_cast<const v8h*>(xrow[ms] + g * kTB + 8 * ks);
+    };
+    auto load_pair = [&](Stage& st, int pr) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            st.c[s] = *reinterpret_cast<const uint4*>(rowp[s] + 64 * pr + 16 * q4);
+            st.p[0][s] = a.am[static_cast<size_t>(2 * pr) * a.N + ncol[s]];
+            st.p[1][s] = a.am[static_cast<size_t>(2 * pr + 1) * a.N + ncol[s]];
+        }
+        load_x(st, 0, 2 * pr);
+        load_x(st, 1, 2 * pr + 1);
+    };
+    const v8h ones = __builtin_bit_cast(v8h, v4u{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+    auto compute = [&](const Stage& st, int nblk) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (j >= nblk) break;
+            // block row sums of X, rows m0 + 16 ms + 4 q4 + i (every column alike)
+            v4f sv[MS];
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) {
-                v8h xa = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-                if (xok[ms]) xa = *reinterpret_cast<const v8h*>(xrow[ms] + g * kTB + 8 * ks);
-                acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, b, acc[ms], 0, 0, 0);
+                sv[ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    sv[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.x[j][ms][ks], ones, sv[ms], 0, 0, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                v4f acc[MS];
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) acc[ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const uint32_t wd = j == 0 ? (ks < 2 ? st.c[s].x : st.c[s].y)
+                                               : (ks < 2 ? st.c[s].z : st.c[s].w);
+                    const v8h bk = (ks & 1) ? tern8<1>(wd) : tern8<0>(wd);
+#pragma unroll
+                    for (int ms = 0; ms < MS; ++ms)
+                        acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.x[j][ms][ks], bk, acc[ms], 0, 0, 0);
+                }
+                // block epilogue: alpha 2^14 acc + (mu - alpha) S
+                const float al = h2f(static_cast<uint16_t>(st.p[j][s] & 0xFFFFu));
+                const float mu = h2f(static_cast<uint16_t>(st.p[j][s] >> 16));
+                const float a14 = al * 16384.0f;
+                const float bm = mu - al;
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        facc[s][ms][i] = __builtin_fmaf(a14, acc[ms][i], __builtin_fmaf(bm, sv[ms][i], facc[s][ms][i]));
             }
         }
-        // block epilogue: alpha 2^14 acc + (mu - alpha) S, rows m0 + 16 ms + 4 q4 + i
-        const float al = h2f(static_cast<uint16_t>(p & 0xFFFFu));
-        const float mu = h2f(static_cast<uint16_t>(p >> 16));
-        const float a14 = al * 16384.0f;
-        const float bm = mu - al;
-        const float* Sg = a.S + static_cast<size_t>(g) * a.Mpad + m0 + 4 * q4;
+    };
+
+    // this wave's pairs: ps + w + kWaves * i, i < np; loads past the end
+    // repeat the wave's last pair (in bounds, never used) so that the
+    // rotation issues its loads unconditionally
+    const int p1 = ps + w;
+    const int np = p1 < pe ? (pe - p1 + kWaves - 1) / kWaves : 0;
+    auto pair_of = [&](int i) { return p1 + kWaves * min(i, np - 1); };
+    if (np > 0) {
+        Stage buf[NBUF];
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms) {
-            const float4 s = *reinterpret_cast<const float4*>(Sg + 16 * ms);
-            facc[ms][0] += a14 * acc[ms][0] + bm * s.x;
-            facc[ms][1] += a14 * acc[ms][1] + bm * s.y;
-            facc[ms][2] += a14 * acc[ms][2] + bm * s.z;
-            facc[ms][3] += a14 * acc[ms][3] + bm * s.w;
+        for (int b = 0; b < NBUF - 1; ++b) load_pair(buf[b], pair_of(b));
+        for (int i0 = 0; i0 < np; i0 += NBUF) {
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) {
+                if (i0 + b >= np) break;
+                load_pair(buf[(b + NBUF - 1) % NBUF], pair_of(i0 + b + NBUF - 1));
+                compute(buf[b], 2);
+            }
         }
     }
-    if (n >= a.N) return;
+    // an unpaired last block (odd K/128), in the last split, by the last wave
+    if ((G & 1) && last_split && w == kWaves - 1) {
+        Stage st;
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + 16 * ms + 4 * q4 + i;
-            if (m >= a.M) continue;
-            if (a.part)
-                a.part[(static_cast<size_t>(blockIdx.z) * a.M + m) * a.N + n] = facc[ms][i];
-            else
-                a.Y[static_cast<size_t>(m) * a.N + n] = f2h(facc[ms][i]);
+        for (int s = 0; s < NS; ++s) {
+            const uint2 u = *reinterpret_cast<const uint2*>(rowp[s] + 64 * P + 8 * q4);
+            st.c[s] = make_uint4(u.x, u.y, 0, 0);
+            st.p[0][s] = a.am[static_cast<size_t>(2 * P) * a.N + ncol[s]];
         }
+        load_x(st, 0, 2 * P);
+        compute(st, 1);
+    }
+
+    // sum the waves' partial results in LDS: red[w][r][lane], r = (s, ms, i)
+    constexpr int R = NS * MS * 4;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[(w * R + (s * MS + ms) * 4 + i) * 64 + lane] = facc[s][ms][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * 64; e += kWaves * 64) {
+        float v = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) v += red[ww * R * 64 + e];
+        const int r = e / 64;
+        const int l = e % 64;
+        const int s = r / (MS * 4);
+        const int ms = (r / 4) % MS;
+        const int i = r % 4;
+        const int n = blockIdx.x * (16 * NS) + 16 * s + (l & 15);
+        const int m = m0 + 16 * ms + 4 * (l >> 4) + i;
+        if (n >= a.N || m >= a.M) continue;
+        if (a.part)
+            a.part[(static_cast<size_t>(blockIdx.z) * a.M + m) * a.N + n] = v;
+        else
+            a.Y[static_cast<size_t>(m) * a.N + n] = f2h(v);
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void k_tern_reduce(const float* __restrict__ part, int splits,
@@ -236,46 +330,39 @@ hipError_t tern_pack_launch(const float* Wt, int N, int K, int iters, uint8_t* T
 
 TernPlan tern_plan(int M, int N, int K, int cus) {
     TernPlan p{};
-    const int G = K / kTB;
-    p.ms = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    p.Mpad = ((M + 63) / 64) * 64;
-    const long tiles = static_cast<long>(ceil_div(N, 64)) * ceil_div(M, 16 * p.ms);
-    // enough workgroups for about four per compute unit
-    int splits = tiles > 0 ? static_cast<int>((4L * cus + tiles - 1) / tiles) : 1;
+    const int P = (K / kTB) / 2;
+    p.ms = M <= 16 ? 1 : 2;
+    p.ns = 2;
+    const long tiles = static_cast<long>(ceil_div(N, 16 * p.ns)) * ceil_div(M, 16 * p.ms);
+    // at least one workgroup of kWaves waves per compute unit; split K across
+    // workgroups only when the tiles fall short of that, keeping at least
+    // two pairs per wave
+    int splits = tiles > 0 ? static_cast<int>((static_cast<long>(cus) + tiles - 1) / tiles) : 1;
+    const int cap = P / (2 * kWaves);
+    if (splits > cap) splits = cap;
     if (splits < 1) splits = 1;
-    if (splits > G) splits = G;
-    p.gps = ceil_div(G, splits);
-    p.splits = ceil_div(G, p.gps);
+    p.pps = ceil_div(P, splits);
+    p.splits = P > 0 ? ceil_div(P, p.pps) : 1;
     return p;
 }
 
 size_t tern_workspace_bytes(int M, int N, int K) {
     const TernPlan p = tern_plan(M, N, K, device_cu_count());
-    const size_t s = static_cast<size_t>(K / kTB) * p.Mpad * sizeof(float);
-    const size_t part = p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
-    return ((s + 255) & ~static_cast<size_t>(255)) + part;
+    return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
 }
 
 hipError_t tern_gemm_launch(const uint16_t* X, int M, int N, int K, const uint8_t* Tq,
                             const uint32_t* am, uint16_t* Y, void* ws, hipStream_t stream) {
     if (M == 0) return hipSuccess;
     const TernPlan p = tern_plan(M, N, K, device_cu_count());
-    const int G = K / kTB;
-    float* S = static_cast<float*>(ws);
-    const size_t sb = static_cast<size_t>(G) * p.Mpad * sizeof(float);
-    float* part = p.splits > 1
-                      ? reinterpret_cast<float*>(static_cast<char*>(ws) + ((sb + 255) & ~static_cast<size_t>(255)))
-                      : nullptr;
-    const int waves = M * G;
-    k_tern_rowsum<<<ceil_div(waves, kThreads / 64), kThreads, 0, stream>>>(X, M, K, p.Mpad, S);
-    TernArgs a{X, Tq, am, S, Y, part, M, N, K, p.Mpad, p.gps};
-    dim3 grid(ceil_div(N, 64), ceil_div(M, 16 * p.ms), p.splits);
+    float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+    TernArgs a{X, Tq, am, Y, part, M, N, K, p.pps};
+    dim3 grid(ceil_div(N, 16 * p.ns), ceil_div(M, 16 * p.ms), p.splits);
+    constexpr int threads = kWaves * 64;
     if (p.ms == 1)
-        k_tern_gemm<1><<<grid, kThreads, 0, stream>>>(a);
-    else if (p.ms == 2)
-        k_tern_gemm<2><<<grid, kThreads, 0, stream>>>(a);
+        k_tern_gemm<1, 2, 3><<<grid, threads, 0, stream>>>(a);
     else
-        k_tern_gemm<4><<<grid, kThreads, 0, stream>>>(a);
+        k_tern_gemm<2, 2, 2><<<grid, threads, 0, stream>>>(a);
     if (part) {
         const size_t count = static_cast<size_t>(M) * N;
         k_tern_reduce<<<static_cast<unsigned>((count + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
