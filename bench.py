@@ -685,7 +685,7 @@ def tern_main(args):
 
     def step(i):
         t, a = packs[i % copies]
-        L.ternary_gemm(X, t, a, out=Y, ws=ws)
+        L.ternary_gemm(X, t, a, wl.N, out=Y, ws=ws)
 
     for i in range(args.warmup):
         step(i)

@@ -281,17 +281,26 @@ int w4a4_linear_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const
  * alpha at its mean absolute deviation.  The layer is weight-only:
  * Y = X · Ŵ^T with fp16 activations X (no activation transform).
  *
- * Layouts:
- *   Tq  uint8 [N][K/4]: two-bit codes c = t + 1 in little-endian 32-bit words
- *       of 16 codes (code 2s of a word at bits 2s, code 2s + 1 at bits
- *       16 + 2s).  The 32 codes 128 g + 32 q .. + 31 of block g and lane group
- *       q = 0..3 form an 8-byte piece; in a row, the pieces of a pair of blocks
- *       (2p, 2p + 1) sit at bytes 64 p + 16 q + 8 (g - 2p), and an unpaired
- *       last block (odd K/128) has piece q at bytes 64 p + 8 q;
- *   am  uint32 [K/128][N] (block-major): the block's alpha as fp16 bits in the
+ * Layouts (rows tiled by 16: Nt = N rounded up to a multiple of 16, padding
+ * rows all zero; w4a4_ternary_weight_bytes gives the sizes):
+ *   Tq  uint8 [Nt * K/4]: two-bit codes c = t + 1 in little-endian 32-bit
+ *       words of 16 codes (code 2s of a word at bits 2s, code 2s + 1 at bits
+ *       16 + 2s).  The 32 codes 128 g + 32 s + 8 q + j (s = 0..3, j = 0..7, in
+ *       that order) of block g form lane group q's 8-byte piece (q = 0..3).
+ *       Tile t = n / 16 starts at byte 4 K t; in it the pair of blocks
+ *       (2p, 2p + 1) fills the 1024 bytes from 1024 p, the 16 bytes at
+ *       1024 p + 16 (16 q + r) holding row r = n % 16's pieces of block 2p and
+ *       then 2p + 1; an unpaired last block (odd K/128) has row r's piece q at
+ *       1024 p + 8 (16 q + r);
+ *   am  uint32 [Nt * K/128]: the word of (row n, block g) at
+ *       ((n / 16) K/128 + g) 16 + n % 16, the block's alpha as fp16 bits in the
  *       low half and mu in the high half (both one rounding from float64). */
 #define W4A4_TERNARY_BLOCK 128
 #define W4A4_TERNARY_MAX_M 64
+
+/* Bytes of Tq and of am for N rows of K weights (N >= 1, K a multiple of
+ * 128); returns W4A4_OK or W4A4_ERR_INVALID_ARG / W4A4_ERR_UNSUPPORTED. */
+int w4a4_ternary_weight_bytes(int32_t N, int32_t K, size_t* tq_bytes, size_t* am_bytes);
 
 /* Offline: ternarize merged or raw fp32 weights Wt [N][K] with `iters` ITF
  * iterations (10 in the pages' setting), float64 arithmetic; the final codes

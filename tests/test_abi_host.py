@@ -304,10 +304,15 @@ def test_ternary_entry_points_validation():
     assert "decode" in last()
     assert L.w4a4_ternary_gemm(FAKE, 4, 64, 256, FAKE, MISALIGNED, FAKE, FAKE, 1 << 20, None) == -3
     assert L.w4a4_ternary_gemm(FAKE, 0, 64, 256, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
+    tq, am = W.ternary_weight_bytes(20, 384)
+    assert (tq, am) == (32 * 96, 32 * 3 * 4)
+    nb = ctypes.c_size_t(0)
+    assert L.w4a4_ternary_weight_bytes(20, 300, ctypes.byref(nb), ctypes.byref(nb)) == -2
+    assert L.w4a4_ternary_weight_bytes(20, 384, None, ctypes.byref(nb)) == -1
     # workspace: none when the tiles fill the GPU, else fp32 partials of a K split
     assert W.ternary_gemm_workspace_bytes(65, 64, 256) == 0
     assert W.ternary_gemm_workspace_bytes(0, 64, 256) == 0
-    assert W.ternary_gemm_workspace_bytes(8, 8192, 28672) == 0
-    nb = W.ternary_gemm_workspace_bytes(1, 64, 8192)
+    assert W.ternary_gemm_workspace_bytes(1, 8192, 28672) == 0
+    nb = W.ternary_gemm_workspace_bytes(1, 64, 65536)
     assert nb > 0 and nb % (1 * 64 * 4) == 0
-    assert L.w4a4_ternary_gemm(FAKE, 4, 64, 8192, FAKE, FAKE, FAKE, None, 0, None) == -4
+    assert L.w4a4_ternary_gemm(FAKE, 1, 64, 65536, FAKE, FAKE, FAKE, None, 0, None) == -4

@@ -40,9 +40,7 @@ def gpu_pack(Wt_np, iters=10):
     return Tq, am
 
 
-def assert_pack_equal(Tq, am, tq_or, am_or, what="pack"):
-    tq = Tq.cpu().numpy()
-    a = am.cpu().numpy().view(np.uint32)
+def assert_pack_equal(tq, a, tq_or, am_or, what="pack"):
     bad_t = np.argwhere(tq != tq_or)
     bad_a = np.argwhere(a != am_or)
     assert bad_a.size == 0, f"{what}: {len(bad_a)} parameter words differ, first {bad_a[:3].tolist()}"
@@ -85,7 +83,8 @@ def test_pack_bit_exact(N, K):
         Wt[2, 5] = -0.25                         # ... but one entry: T fits it with alpha
     _, tq_or, am_or = oracle_pack(Wt)
     Tq, am = gpu_pack(Wt)
-    assert_pack_equal(Tq, am, tq_or, am_or, f"pack N={N} K={K}")
+    assert_pack_equal(Tq.cpu().numpy(), am.cpu().numpy().view(np.uint32), tq_or, am_or,
+                      f"pack N={N} K={K}")
 
 
 @pytest.mark.parametrize("iters", [0, 1, 3])
@@ -95,12 +94,15 @@ def test_pack_iteration_counts(iters):
     Wt = WT.make_tern_weights(wl)
     _, tq_or, am_or = oracle_pack(Wt, iters)
     Tq, am = gpu_pack(Wt, iters)
-    assert_pack_equal(Tq, am, tq_or, am_or, f"pack iters={iters}")
+    assert_pack_equal(Tq.cpu().numpy(), am.cpu().numpy().view(np.uint32), tq_or, am_or,
+                      f"pack iters={iters}")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (5, 100, 512), (16, 64, 4096), (17, 130, 1024),
                                    (33, 257, 2048), (64, 192, 1280), (64, 1000, 8192),
-                                   (2, 3000, 384), (40, 77, 640), (8, 4096, 896), (3, 50, 128)])
+                                   (2, 3000, 384), (40, 77, 640), (8, 4096, 896), (3, 50, 128),
+                                   (4, 300, 1280), (2, 96, 16384), (20, 64, 8192), (12, 200, 8192),
+                                   (9, 64, 12288), (1, 32, 65536), (12, 48, 32768)])
 def test_gemm_parity(M, N, K):
     log(f"ternary_gemm M={M} N={N} K={K}")
     wl = WT.TernWorkload("t", M=M, K=K, N=N, x_kind="silu_product" if M % 2 else "normal",
@@ -108,7 +110,7 @@ def test_gemm_parity(M, N, K):
     inp = WT.make_tern_inputs(wl)
     r, tq_or, am_or = oracle_pack(inp["Wt"])
     Y64 = TO.ternary_linear(inp["X"], r)
-    Y = W().ternary_gemm(to_dev(inp["X"]), to_dev(tq_or), to_dev(am_or.view(np.int32)))
+    Y = W().ternary_gemm(to_dev(inp["X"]), to_dev(tq_or), to_dev(am_or.view(np.int32)), N)
     rel = assert_tern_close(Y.cpu().numpy(), Y64, magnitude(inp["X"], r), f"M={M} N={N} K={K}")
     log(f"  rel L2 {rel:.2e}")
 
@@ -120,11 +122,11 @@ def test_gemm_zero_rows_and_m0():
     X = inp["X"].copy()
     X[4] = 0
     r, tq_or, am_or = oracle_pack(inp["Wt"])
-    Y = W().ternary_gemm(to_dev(X), to_dev(tq_or), to_dev(am_or.view(np.int32))).cpu().numpy()
+    Y = W().ternary_gemm(to_dev(X), to_dev(tq_or), to_dev(am_or.view(np.int32)), 64).cpu().numpy()
     assert np.all(Y[4] == 0)
     assert_tern_close(Y, TO.ternary_linear(X, r), magnitude(X, r), "zero row")
     Y0 = W().ternary_gemm(torch.empty((0, 256), dtype=torch.float16, device=dev), to_dev(tq_or),
-                          to_dev(am_or.view(np.int32)))
+                          to_dev(am_or.view(np.int32)), 64)
     assert tuple(Y0.shape) == (0, 64)
 
 
@@ -139,14 +141,25 @@ def test_full_size_sampled(name):
     wl = WT.get_tern(name)
     inp = WT.make_tern_inputs(wl)
     Tq, am = gpu_pack(inp["Wt"])
-    Y = W().ternary_gemm(to_dev(inp["X"]), Tq, am).cpu().numpy()
+    Y = W().ternary_gemm(to_dev(inp["X"]), Tq, am, wl.N).cpu().numpy()
     rng = np.random.default_rng(5)
     cols = np.unique(np.concatenate([[0, 1, wl.N - 1], rng.choice(wl.N, 21, replace=False)]))
     Ws = WT.make_tern_weights(wl, rows=cols)
     np.testing.assert_array_equal(Ws, inp["Wt"][cols])
-    r, tq_or, am_or = oracle_pack(Ws)
-    idx = torch.from_numpy(cols).to(dev)
-    assert_pack_equal(Tq[idx], am[:, idx], tq_or, am_or, f"{name} sampled rows")
+    r, _, _ = oracle_pack(Ws)
+    # the sampled rows' pieces and parameter words, gathered from both layouts
+    G = wl.K // 128
+    tq32 = Tq.cpu().numpy().view("<u4")
+    am32 = am.cpu().numpy().view(np.uint32)
+    w_full = TO.tile_offsets(wl.N, G)[cols] // 4                  # [rows, G, 4]
+    want_words = TO.piece_words(r["T"], 128)                           # [rows, G, 4, 2]
+    got_words = np.stack([tq32[w_full], tq32[w_full + 1]], axis=-1)
+    a16 = r["alpha"].view(np.uint16).astype(np.uint32)
+    u16 = r["mu"].view(np.uint16).astype(np.uint32)
+    want_am = a16 | (u16 << 16)                                    # [rows, G]
+    t, rr = np.divmod(cols, 16)
+    got_am = am32[((t[:, None] * G) + np.arange(G)[None, :]) * 16 + rr[:, None]]
+    assert_pack_equal(got_words, got_am, want_words, want_am, f"{name} sampled rows")
     Y64 = TO.ternary_linear(inp["X"], r)
     rel = assert_tern_close(Y[:, cols], Y64, magnitude(inp["X"], r), name)
     log(f"  rel L2 {rel:.2e}")

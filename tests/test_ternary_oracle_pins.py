@@ -122,34 +122,47 @@ def test_dequant_bound_inside_the_grid():
 
 def test_pack_round_trip_and_bits():
     rng = np.random.default_rng(6)
-    T = rng.integers(-1, 2, size=(3, 384)).astype(np.int8)       # 3 blocks: a pair and one more
+    N, K = 20, 384                              # two tiles (the second ragged); a pair and one block
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
     b = TO.pack_ternary(T)
-    assert b.shape == (3, 96)
-    np.testing.assert_array_equal(TO.unpack_ternary(b), T)
+    assert b.shape == (32 * K // 4,)
+    np.testing.assert_array_equal(TO.unpack_ternary(b, N, K), T)
 
-    def word(r, first):        # 16 codes from `first`, written out bit by bit
+    def word(n, idx):          # the word of the 16 codes `idx` of row n, written out bit by bit
         v = 0
-        for s_ in range(8):
-            v |= (int(T[r, first + 2 * s_]) + 1) << (2 * s_)
-            v |= (int(T[r, first + 2 * s_ + 1]) + 1) << (16 + 2 * s_)
+        for i, k in enumerate(idx):
+            v |= (int(T[n, k]) + 1) << (2 * (i // 2) + 16 * (i % 2))
         return v
 
-    def at(r, byte):
-        return int.from_bytes(bytes(b[r, byte:byte + 4].tolist()), "little")
+    def piece(g, q):           # code indices of the piece of block g, lane group q
+        return [128 * g + 32 * s_ + 8 * q + j for s_ in range(4) for j in range(8)]
 
-    # block 1 (second of pair 0), lane group 2: codes 128 + 64 .. 128 + 95 at
-    # bytes 16*2 + 8 = 40 .. 47
-    assert at(2, 40) == word(2, 192) and at(2, 44) == word(2, 208)
-    # block 0, lane group 3: bytes 48 .. 55 hold codes 96 .. 127
-    assert at(1, 48) == word(1, 96) and at(1, 52) == word(1, 112)
-    # unpaired block 2, lane group 3: bytes 64 + 24 = 88 .. 95 hold codes 352 .. 383
-    assert at(0, 88) == word(0, 352) and at(0, 92) == word(0, 368)
-    # every piece lands once
+    def at(byte):
+        return int.from_bytes(bytes(b[byte:byte + 4].tolist()), "little")
+
+    pc = piece(1, 2)
+    assert pc[:3] == [144, 145, 146] and pc[8] == 176
+    # row 17 = tile 1 (from byte 4K = 1536), r = 1; block 1 (second of pair 0),
+    # lane group 2: (16*2 + 1) * 16 + 8 = 536
+    o = 1536 + 536
+    assert at(o) == word(17, pc[:16]) and at(o + 4) == word(17, pc[16:])
+    # row 3, block 0, lane group 3: (48 + 3) * 16 = 816
+    assert at(816) == word(3, piece(0, 3)[:16]) and at(820) == word(3, piece(0, 3)[16:])
+    # row 3, unpaired block 2, lane group 3: 1024 + (48 + 3) * 8 = 1432
+    assert at(1432) == word(3, piece(2, 3)[:16]) and at(1436) == word(3, piece(2, 3)[16:])
+    # padded row 25 (tile 1, r = 9) is zero bytes
+    assert not b[1536 + 9 * 16:1536 + 9 * 16 + 8].any()
+    # every 8-byte slot of a tile holds exactly one piece
     off = TO.piece_offsets(5)
-    assert sorted(off.ravel().tolist()) == list(range(20))
-    p = TO.pack_params(np.array([[1.5, 2.0]], np.float16), np.array([[-0.25, 0.0]], np.float16))
-    assert p.shape == (2, 1)
-    assert int(p[0, 0]) == 0x3E00 | (0xB400 << 16) and int(p[1, 0]) == 0x4000
+    assert sorted((off.ravel() // 8).tolist()) == list(range(5 * 4 * 16))
+    # parameters: word (t * G + g) * 16 + r, zero past N
+    a = np.zeros((17, 2), np.float16)
+    u = np.zeros((17, 2), np.float16)
+    a[16, 1], u[16, 1] = 1.5, -0.25
+    p = TO.pack_params(a, u)
+    assert p.shape == (64,)
+    assert int(p[(1 * 2 + 1) * 16 + 0]) == 0x3E00 | (0xB400 << 16)
+    assert np.count_nonzero(p) == 1
 
 
 def test_layer_block_sum_equals_dense_matmul():

@@ -24,7 +24,8 @@ __all__ = [
     "KV_HEAD_DIM", "KvCache", "kv_cache_bytes", "kv_query_factor", "kv_append",
     "attn_decode_workspace_bytes", "attn_decode",
     "pack_weights_bits", "transform_quant_bits", "linear_bits",
-    "TERNARY_BLOCK", "TERNARY_MAX_M", "pack_ternary", "ternary_gemm_workspace_bytes",
+    "TERNARY_BLOCK", "TERNARY_MAX_M", "ternary_weight_bytes", "pack_ternary",
+    "ternary_gemm_workspace_bytes",
     "ternary_gemm",
 ]
 
@@ -43,7 +44,8 @@ EXPORTED_SYMBOLS = [
     "w4a4_kv_cache_bytes", "w4a4_kv_query_factor_workspace_bytes", "w4a4_kv_query_factor",
     "w4a4_kv_append", "w4a4_attn_decode_workspace_bytes", "w4a4_attn_decode",
     "w4a4_pack_weights_bits", "w4a4_transform_quant_bits", "w4a4_linear_bits",
-    "w4a4_pack_ternary", "w4a4_ternary_gemm_workspace_bytes", "w4a4_ternary_gemm",
+    "w4a4_ternary_weight_bytes", "w4a4_pack_ternary", "w4a4_ternary_gemm_workspace_bytes",
+    "w4a4_ternary_gemm",
 ]
 
 DECODE_SYNC_BYTES = 1024          # W4A4_DECODE_SYNC_BYTES
@@ -115,6 +117,7 @@ def lib() -> ctypes.CDLL:
                                                          vp, vp, vp, sz, vp]),
             "w4a4_linear_bits": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, i32, dp, vp,
                                                 vp, vp, vp, vp, sz, vp]),
+            "w4a4_ternary_weight_bytes": (ctypes.c_int, [i32, i32, szp, szp]),
             "w4a4_pack_ternary": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
             "w4a4_ternary_gemm_workspace_bytes": (sz, [i32, i32, i32]),
             "w4a4_ternary_gemm": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
@@ -570,14 +573,23 @@ def linear_bits(X, P1, P2, bits: int, desc: WeightDesc, Wq, s_w, z_w=None, c=Non
 # ---------------------------------------------------------------------------
 # Ternary weights (W1.58A16)
 # ---------------------------------------------------------------------------
+def ternary_weight_bytes(N: int, K: int):
+    """(bytes of Tq, bytes of am) for N rows of K weights (rows tiled by 16)."""
+    tq, am = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().w4a4_ternary_weight_bytes(N, K, ctypes.byref(tq), ctypes.byref(am)),
+           "w4a4_ternary_weight_bytes")
+    return tq.value, am.value
+
+
 def pack_ternary(Wt, iters: int = 10, stream=None):
-    """Ternarize fp32 weights [N, K]: returns (Tq uint8 [N, K/4], am int32 [K/128, N]
-    holding the bits of the uint32 parameter words)."""
+    """Ternarize fp32 weights [N, K]: returns (Tq uint8 [bytes], am int32 [words])
+    in the tiled layout (am holds the bits of the uint32 parameter words)."""
     torch = _torch()
     N, K = Wt.shape
     _need(Wt, torch.float32, (N, K), "Wt")
-    Tq = torch.empty((N, K // 4), dtype=torch.uint8, device=Wt.device)
-    am = torch.empty((max(K // TERNARY_BLOCK, 1), N), dtype=torch.int32, device=Wt.device)
+    tqb, amb = ternary_weight_bytes(N, K)
+    Tq = torch.empty((tqb,), dtype=torch.uint8, device=Wt.device)
+    am = torch.empty((amb // 4,), dtype=torch.int32, device=Wt.device)
     _check(lib().w4a4_pack_ternary(_p(Wt), N, K, int(iters), _p(Tq), _p(am), _stream(stream)),
            "w4a4_pack_ternary")
     return Tq, am
@@ -587,14 +599,15 @@ def ternary_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return lib().w4a4_ternary_gemm_workspace_bytes(M, N, K)
 
 
-def ternary_gemm(X, Tq, am, out=None, ws=None, stream=None):
-    """Y [M, N] fp16 = X [M, K] fp16 times the ternary weights (M <= TERNARY_MAX_M)."""
+def ternary_gemm(X, Tq, am, N: int, out=None, ws=None, stream=None):
+    """Y [M, N] fp16 = X [M, K] fp16 times the ternary weights of N rows
+    (M <= TERNARY_MAX_M)."""
     torch = _torch()
     M, K = X.shape
-    N = Tq.shape[0]
     _need(X, torch.float16, (M, K), "X")
-    _need(Tq, torch.uint8, (N, K // 4), "Tq")
-    _need(am, torch.int32, (K // TERNARY_BLOCK, N), "am")
+    tqb, amb = ternary_weight_bytes(N, K)
+    _need(Tq, torch.uint8, (tqb,), "Tq")
+    _need(am, torch.int32, (amb // 4,), "am")
     Y = out if out is not None else torch.empty((M, N), dtype=torch.float16, device=X.device)
     nb = ternary_gemm_workspace_bytes(M, N, K)
     ws = _ws(nb, X.device, ws)

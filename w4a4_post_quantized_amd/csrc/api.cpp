@@ -683,6 +683,16 @@ int check_tern(int32_t M, int32_t N, int32_t K) {
 }
 }  // namespace
 
+int w4a4_ternary_weight_bytes(int32_t N, int32_t K, size_t* tq_bytes, size_t* am_bytes) {
+    if (int s = check_tern(0, N, K)) return s;
+    REQUIRE_PTR(tq_bytes);
+    REQUIRE_PTR(am_bytes);
+    const size_t rows = static_cast<size_t>(w4a4::tern_rows(N));
+    *tq_bytes = rows * static_cast<size_t>(K) / 4;
+    *am_bytes = rows * static_cast<size_t>(K / W4A4_TERNARY_BLOCK) * sizeof(uint32_t);
+    return ok();
+}
+
 int w4a4_pack_ternary(const float* Wt, int32_t N, int32_t K, int32_t iters, uint8_t* Tq,
                       uint32_t* am, void* stream) {
     if (int s = check_tern(0, N, K)) return s;

@@ -107,19 +107,27 @@ hipError_t attn_decode_launch(const AttnArgs& a, hipStream_t stream);
 // ---- ternary weights, W1.58A16 (ternary.hip) --------------------------------
 struct TernArgs {
     const uint16_t* X;      // fp16 [M][K]
-    const uint8_t* Tq;      // [N][K/4], 16 codes per 32-bit word, pieces in pair order
-    const uint32_t* am;     // [K/128][N]: alpha fp16 bits low, mu high
+    const uint8_t* Tq;      // codes, 16-row tiles (see ternary.hip)
+    const uint32_t* am;     // [N/16][K/128][16]: alpha fp16 bits low, mu high
     uint16_t* Y;            // fp16 [M][N] (no K-split)
     float* part;            // [splits][M][N] (K-split) or nullptr
-    int M, N, K, pps;       // pps: block pairs of K per split
+    int M, N, K, gps;       // gps: groups of blocks of K per split
+    int xls;                // LDS row stride of X (halfs) when X is held in LDS
 };
 struct TernPlan {
     int ms;       // 16-row subtiles per wave (1 or 2)
     int ns;       // 16-column subtiles per wave
-    int pps;      // pairs of blocks of 128 per K-split
+    int qb;       // blocks of 128 per load stage (a group)
+    bool xl;      // X (or its K slice) held in LDS
+    bool nsp;     // waves split the columns instead of K
+    int waves;    // waves per workgroup
+    int xls;      // LDS row stride of X (halfs)
+    size_t lds;   // dynamic LDS bytes
+    int gps;      // groups per K-split
     int splits;   // K-splits
 };
 TernPlan tern_plan(int M, int N, int K, int cus);
+inline int tern_rows(int N) { return (N + 15) / 16 * 16; }   // rows in storage
 size_t tern_workspace_bytes(int M, int N, int K);   // for this device
 hipError_t tern_pack_launch(const float* Wt, int N, int K, int iters, uint8_t* Tq, uint32_t* am,
                             hipStream_t stream);

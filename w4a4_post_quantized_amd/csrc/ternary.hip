@@ -8,14 +8,16 @@
 // size 128 of its training strategy.
 //
 // Storage: T as two-bit codes c = t + 1 in words of 16 codes (code 2s at bits
-// 2s, code 2s + 1 at bits 16 + 2s), a row of K codes in K/4 bytes.  The 32
-// codes that one MFMA lane group q (q = 0..3) takes from block g, codes
-// 128 g + 32 q .. + 31, form an 8-byte piece; a pair of blocks (2p, 2p + 1)
-// stores its 8 pieces at bytes 64 p + 16 q + 8 (g - 2p) of the row, so one
-// lane reads both blocks' codes with one 16-byte load and 4 lanes read 64
-// contiguous bytes; an unpaired last block stores piece q at 64 p + 8 q.  The
-// block parameters are one word per (block, row), block-major [K/128][N],
-// alpha's fp16 bits low, mu's high.
+// 2s, code 2s + 1 at bits 16 + 2s).  The 32 codes that MFMA lane group q
+// (q = 0..3) takes from block g, codes 128 g + 32 s + 8 q + j (step s = 0..3,
+// j = 0..7) in the order (s, j), form an 8-byte piece.  Rows are tiled by 16
+// (N rounded up; padding rows are zero): tile t holds 16 K / 4 bytes from
+// byte 4 K t, and in it the pair of blocks (2p, 2p + 1) the 1024 bytes from
+// 1024 p, lane l = 16 q + r holding row r's pieces of both blocks at 16 l; so
+// one 16-byte load per lane of a wave reads a whole pair for 16 rows, 1024
+// contiguous bytes.  An unpaired last block (odd K/128) holds row r's piece q
+// at 1024 p + 8 (16 q + r).  The block parameters are one word per (row,
+// block) at (t K/128 + g) 16 + r, alpha's fp16 bits low, mu's high.
 //
 // Kernels:
 //   k_tern_pack    offline ITF in float64, one workgroup per (row, block);
@@ -60,15 +62,31 @@ __device__ __forceinline__ double nearest_t(double z) {
     return fmin(fmax(__builtin_rint(z), -1.0), 1.0);
 }
 
-__global__ __launch_bounds__(kTB) void k_tern_pack(const float* __restrict__ Wt, int K, int iters,
+__global__ __launch_bounds__(kTB) void k_tern_pack(const float* __restrict__ Wt, int N, int K, int iters,
                                                    uint8_t* __restrict__ Tq,
                                                    uint32_t* __restrict__ am) {
     __shared__ double red[2];
     __shared__ uint32_t words[kTB / 16];
-    const int row = blockIdx.x;
+    const int row = blockIdx.x;                 // 0 .. rows rounded up to 16
     const int g = blockIdx.y;
     const int G = K / kTB;
     const int t = threadIdx.x;
+    const int tile = row >> 4;
+    const int r = row & 15;
+    uint32_t* const tq32 = reinterpret_cast<uint32_t*>(Tq + static_cast<size_t>(tile) * 4 * K);
+    const int pr = g >> 1;
+    // word w (0, 1) of lane group q's piece of this row and block
+    auto word_at = [&](int q, int wd) -> uint32_t* {
+        const int off = 2 * pr + 1 < G ? 1024 * pr + (16 * q + r) * 16 + 8 * (g & 1)
+                                       : 1024 * pr + (16 * q + r) * 8;
+        return tq32 + (off >> 2) + wd;
+    };
+    uint32_t* const amw = am + (static_cast<size_t>(tile) * G + g) * 16 + r;
+    if (row >= N) {                             // padding rows: zero codes and parameters
+        if (t < kTB / 16) *word_at(t >> 1, t & 1) = 0u;
+        if (t == 0) *amw = 0u;
+        return;
+    }
     const double w = static_cast<double>(Wt[static_cast<size_t>(row) * K + g * kTB + t]);
     const double m = static_cast<double>(kTB);
     const double sW = block_sum128(w, red);
@@ -93,18 +111,15 @@ __global__ __launch_bounds__(kTB) void k_tern_pack(const float* __restrict__ Wt,
     const uint32_t c = static_cast<uint32_t>(static_cast<int>(T) + 1);
     if (t < kTB / 16) words[t] = 0;
     __syncthreads();
-    atomicOr(&words[t >> 4], c << (16 * (t & 1) + 2 * ((t & 15) >> 1)));
-    __syncthreads();
-    if (t < kTB / 16) {
-        // word t belongs to lane group q = t / 2 (codes 32q .. 32q + 31)
-        const int q = t >> 1;
-        const int pr = g >> 1;
-        const int off = 2 * pr + 1 < G ? 64 * pr + 16 * q + 8 * (g & 1) : 64 * pr + 8 * q;
-        reinterpret_cast<uint32_t*>(Tq + static_cast<size_t>(row) * (K / 4) + off)[t & 1] = words[t];
+    {
+        // code t = 32 s + 8 q + j of the block goes to word 2 q + s / 2 of the
+        // block, position i = 8 (s % 2) + j of that word's 16
+        const int sq = t >> 5, q = (t >> 3) & 3, i = 8 * (sq & 1) + (t & 7);
+        atomicOr(&words[2 * q + (sq >> 1)], c << (16 * (i & 1) + 2 * (i >> 1)));
     }
-    if (t == 0)
-        am[static_cast<size_t>(g) * gridDim.x + row] =
-            static_cast<uint32_t>(a16) | (static_cast<uint32_t>(u16) << 16);
+    __syncthreads();
+    if (t < kTB / 16) *word_at(t >> 1, t & 1) = words[t];   // words 2q, 2q + 1: lane group q
+    if (t == 0) *amw = static_cast<uint32_t>(a16) | (static_cast<uint32_t>(u16) << 16);
 }
 
 // Eight codes of one MFMA step as fp16 values c * 2^-14, in k order: register v
@@ -125,54 +140,77 @@ __device__ __forceinline__ v8h tern8(uint32_t word) {
 }
 
 // ---------------------------------------------------------------------------
-// Product for small M.  A workgroup of kWaves waves owns NS x 16 output
-// columns and MS x 16 rows; its waves split the block pairs of K between them
-// (wave w takes pairs ps + w, ps + w + kWaves, ...) and add their sums in LDS
-// at the end; grid.z splits K further across workgroups only when the tiles
-// alone cannot fill the GPU.  Lane l: c16 = l % 16 (A row / B column), q4 =
-// l / 16.  MFMA step ks of block g uses k = 128 g + 32 q4 + 8 ks + j in slot
-// j on both operands: the lane's A operand is 16 contiguous bytes of X, its B
-// operand codes from the 16 bytes it loaded for the pair.  One more MFMA per
-// step against a B of ones gives the block row sum S of X in the output
-// layout.  A stage is one pair: codes, block parameters and the A operand,
-// all issued together (vector loads complete in issue order, so a load issued
-// after a stage would make its use wait for the whole stage); NBUF stages
-// rotate, NBUF - 1 of them loading while one is used.  The NS subtiles share
-// the A operand and S.
+// Product for small M.  A workgroup of W waves owns NS x 16 output columns
+// and MS x 16 rows; its waves split K between them in groups of QB blocks
+// (wave w takes groups gs + w, gs + w + W, ...) and add their sums
+// in LDS at the end; grid.z splits K further across workgroups only when the
+// tiles alone cannot fill the GPU.  Lane l: c16 = l % 16 (A row / B column),
+// q4 = l / 16.  MFMA step ks of block g uses k = 128 g + 32 ks + 8 q4 + j in
+// slot j on both operands, so the 4 lane groups read 64 contiguous bytes of a
+// row of X per step; the B operand is the lane's piece of codes.  One more
+// MFMA per step against a B of ones gives the block row sum S of X in the
+// output layout.  A stage is one group: codes (16 bytes per pair of blocks
+// and lane, the pairs of a group in one 128-byte line when QB = 4), block
+// parameters and the A operand, all issued together (vector loads complete
+// in issue order, so a load issued after a stage would make its use wait for
+// the whole stage); NBUF stages rotate, NBUF - 1 of them loading while one is
+// used.  The NS subtiles share the A operand and S.
 // ---------------------------------------------------------------------------
-constexpr int kWaves = 8;
+// LDS row stride of X (halfs) when X is held in LDS: K plus 16 bytes, so that
+// rows start 4 banks apart
+__host__ __device__ constexpr int tern_xl_stride(int K) { return K + 8; }
+constexpr size_t kXlMax = 136 * 1024;        // X in LDS up to this size
+constexpr int kLdsMax = 160 * 1024;          // LDS of one CU
+size_t tern_xl_bytes(int M, int K) { return static_cast<size_t>(M) * tern_xl_stride(K) * 2; }
 
-template <int MS, int NS>
-constexpr int tern_red_floats() { return kWaves * NS * MS * 4 * 64; }
+template <int MS, int NS, int W, bool NSP>
+constexpr int tern_red_floats() { return NSP ? 1 : W * NS * MS * 4 * 64; }
 
-template <int MS, int NS>
+template <int MS, int NS, int QB, bool XL>
 struct TernStage {
-    uint4 c[NS];            // .x .y: block 2p, .z .w: block 2p + 1
-    uint32_t p[2][NS];      // (alpha, mu) words
-    v8h x[2][MS][4];        // A operands
+    uint4 c[QB / 2][NS];    // pair h: .x .y block 2h, .z .w block 2h + 1
+    uint32_t p[NS];         // (alpha, mu) word of block q4 (lane group), column c16
+    v8h x[QB][MS][4];       // A operands
+};
+template <int MS, int NS, int QB>
+struct TernStage<MS, NS, QB, true> {   // A operands read from LDS
+    uint4 c[QB / 2][NS];
+    uint32_t p[NS];
 };
 
-template <int MS, int NS, int NBUF>
-__global__ __launch_bounds__(kWaves * 64) void k_tern_gemm(TernArgs a) {
-    __shared__ float red[tern_red_floats<MS, NS>()];
+
+template <int MS, int NS, int QB, int NBUF, bool XL, int W, bool NSP>
+__global__ __launch_bounds__(W * 64) void k_tern_gemm(TernArgs a) {
+    static_assert(!NSP || XL, "column-split workgroups hold X in LDS");
+    constexpr int kWaves = W;
+    __shared__ float red[tern_red_floats<MS, NS, W, NSP>()];
+    extern __shared__ __align__(16) _Float16 xl[];      // X [M][slice of K] when XL
+    using Stage = TernStage<MS, NS, QB, XL>;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int c16 = lane & 15;
     const int q4 = lane >> 4;
     const int G = a.K / kTB;
-    const int P = G / 2;                                   // full pairs
-    const int ps = blockIdx.z * a.pps;
-    const int pe = min(P, ps + a.pps);
+    const int NG = G / QB;                                 // full groups
+    const int gs = blockIdx.z * a.gps;
+    const int ge = min(NG, gs + a.gps);
     const bool last_split = blockIdx.z == gridDim.z - 1;
     const int m0 = blockIdx.y * 16 * MS;
+    // the blocks of K this workgroup reads: its groups, and in the last split
+    // the blocks past the last full group
+    const int kb0 = QB * gs;
+    const int kb1 = last_split ? G : QB * ge;
 
-    const uint8_t* rowp[NS];
-    int ncol[NS];
+    // 16-row tiles of the weights (clamped: tiles past the last hold no
+    // output column); this lane's 16 bytes of a pair at 16 * lane
+    const int ntiles = (a.N + 15) / 16;
+    const uint8_t* tilep[NS];
+    const uint32_t* amt[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const int n = blockIdx.x * (16 * NS) + 16 * s + c16;
-        ncol[s] = n < a.N ? n : a.N - 1;
-        rowp[s] = a.Tq + static_cast<size_t>(ncol[s]) * (a.K / 4);
+        const int tile = min((NSP ? blockIdx.x * kWaves + w : blockIdx.x) * NS + s, ntiles - 1);
+        tilep[s] = a.Tq + static_cast<size_t>(tile) * 4 * a.K;
+        amt[s] = a.am + static_cast<size_t>(tile) * G * 16 + c16;
     }
     // rows of this lane's A operand: output row r of an MFMA depends on A row
     // r alone, so rows past M read row M - 1 (in bounds) and their outputs are
@@ -181,7 +219,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_tern_gemm(TernArgs a) {
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
         const int m = min(m0 + 16 * ms + c16, a.M - 1);
-        xrow[ms] = a.X + static_cast<size_t>(m) * a.K + 32 * q4;
+        xrow[ms] = a.X + static_cast<size_t>(m) * a.K + 8 * q4;
     }
 
     v4f facc[NS][MS];
@@ -190,29 +228,55 @@ __global__ __launch_bounds__(kWaves * 64) void k_tern_gemm(TernArgs a) {
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) facc[s][ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    using Stage = TernStage<MS, NS>;
     auto load_x = [&](Stage& st, int j, int g) {
+        if constexpr (!XL) {
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms)
+            for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                st.x[j][ms][ks] = *reinterpret_cast<const v8h*>(xrow[ms] + g * kTB + 8 * ks);
-    };
-    auto load_pair = [&](Stage& st, int pr) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            st.c[s] = *reinterpret_cast<const uint4*>(rowp[s] + 64 * pr + 16 * q4);
-            st.p[0][s] = a.am[static_cast<size_t>(2 * pr) * a.N + ncol[s]];
-            st.p[1][s] = a.am[static_cast<size_t>(2 * pr + 1) * a.N + ncol[s]];
+                for (int ks = 0; ks < 4; ++ks)
+                    st.x[j][ms][ks] = *reinterpret_cast<const v8h*>(xrow[ms] + g * kTB + 32 * ks);
         }
-        load_x(st, 0, 2 * pr);
-        load_x(st, 1, 2 * pr + 1);
+    };
+    // XL (MS = 1, one row tile): this lane's row of X in LDS, blocks kb0 .. kb1
+    const _Float16* xlrow = xl + static_cast<size_t>(min(c16, a.M - 1)) * a.xls + 8 * q4;
+    auto a_op = [&](const Stage& st, int j, int ms, int ks, int g) -> v8h {
+        if constexpr (XL)
+            return *reinterpret_cast<const v8h*>(xlrow + (g - kb0) * kTB + 32 * ks);
+        else
+            return st.x[j][ms][ks];
+    };
+    // parameters of blocks g0 .. g0 + nb - 1: lane group q4 loads block
+    // g0 + q4 (clamped), 64 contiguous words per wave
+    auto load_p = [&](Stage& st, int g0, int nb) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st.p[s] = amt[s][static_cast<size_t>(g0 + min(q4, nb - 1)) * 16];
+    };
+    // blocks g0 .. g0 + 2 * npair - 1 (g0 even) into the stage
+    auto load_pairs = [&](Stage& st, int g0, int npair) {
+#pragma unroll
+        for (int h = 0; h < QB / 2; ++h) {
+            if (h >= npair) break;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                st.c[h][s] = *reinterpret_cast<const uint4*>(tilep[s] + 1024 * (g0 / 2 + h) + 16 * lane);
+        }
+        load_p(st, g0, 2 * npair);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+            if (j >= 2 * npair) break;
+            load_x(st, j, g0 + j);
+        }
     };
     const v8h ones = __builtin_bit_cast(v8h, v4u{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
-    auto compute = [&](const Stage& st, int nblk) {
+    auto compute = [&](const Stage& st, int g0, int nblk) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < QB; ++j) {
             if (j >= nblk) break;
+            v8h xa[MS][4];
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) xa[ms][ks] = a_op(st, j, ms, ks, g0 + j);
             // block row sums of X, rows m0 + 16 ms + 4 q4 + i (every column alike)
             v4f sv[MS];
 #pragma unroll
@@ -220,25 +284,27 @@ __global__ __launch_bounds__(kWaves * 64) void k_tern_gemm(TernArgs a) {
                 sv[ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    sv[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.x[j][ms][ks], ones, sv[ms], 0, 0, 0);
+                    sv[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[ms][ks], ones, sv[ms], 0, 0, 0);
             }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
+                const uint4& cp = st.c[j / 2][s];
                 v4f acc[MS];
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) acc[ms] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const uint32_t wd = j == 0 ? (ks < 2 ? st.c[s].x : st.c[s].y)
-                                               : (ks < 2 ? st.c[s].z : st.c[s].w);
+                    const uint32_t wd = (j & 1) == 0 ? (ks < 2 ? cp.x : cp.y) : (ks < 2 ? cp.z : cp.w);
                     const v8h bk = (ks & 1) ? tern8<1>(wd) : tern8<0>(wd);
 #pragma unroll
                     for (int ms = 0; ms < MS; ++ms)
-                        acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.x[j][ms][ks], bk, acc[ms], 0, 0, 0);
+                        acc[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[ms][ks], bk, acc[ms], 0, 0, 0);
                 }
-                // block epilogue: alpha 2^14 acc + (mu - alpha) S
-                const float al = h2f(static_cast<uint16_t>(st.p[j][s] & 0xFFFFu));
-                const float mu = h2f(static_cast<uint16_t>(st.p[j][s] >> 16));
+                // block epilogue: alpha 2^14 acc + (mu - alpha) S, with this
+                // column's parameters from lane group j
+                const uint32_t pj = static_cast<uint32_t>(__shfl(static_cast<int>(st.p[s]), c16 + 16 * j));
+                const float al = h2f(static_cast<uint16_t>(pj & 0xFFFFu));
+                const float mu = h2f(static_cast<uint16_t>(pj >> 16));
                 const float a14 = al * 16384.0f;
                 const float bm = mu - al;
 #pragma unroll
@@ -250,38 +316,86 @@ __global__ __launch_bounds__(kWaves * 64) void k_tern_gemm(TernArgs a) {
         }
     };
 
-    // this wave's pairs: ps + w + kWaves * i, i < np; loads past the end
-    // repeat the wave's last pair (in bounds, never used) so that the
-    // rotation issues its loads unconditionally
-    const int p1 = ps + w;
-    const int np = p1 < pe ? (pe - p1 + kWaves - 1) / kWaves : 0;
-    auto pair_of = [&](int i) { return p1 + kWaves * min(i, np - 1); };
-    if (np > 0) {
-        Stage buf[NBUF];
+    // this wave's groups: all of gs .. ge - 1 when the waves split the
+    // columns (NSP), else gs + w + kWaves * i; loads past the end repeat the
+    // wave's last group (in bounds, never used) so that the rotation issues
+    // its loads unconditionally
+    const int g1 = NSP ? gs : gs + w;
+    const int gstep = NSP ? 1 : kWaves;
+    const int ng = g1 < ge ? (ge - g1 + gstep - 1) / gstep : 0;
+    auto group_of = [&](int i) { return g1 + gstep * min(i, ng - 1); };
+    Stage buf[NBUF];
+    if (ng > 0) {
 #pragma unroll
-        for (int b = 0; b < NBUF - 1; ++b) load_pair(buf[b], pair_of(b));
-        for (int i0 = 0; i0 < np; i0 += NBUF) {
+        for (int b = 0; b < NBUF - 1; ++b) load_pairs(buf[b], QB * group_of(b), QB / 2);
+    }
+    if constexpr (XL) {
+        // X [M][blocks kb0 .. kb1] into LDS by the whole workgroup, after the
+        // first code loads
+        const int w8 = (kb1 - kb0) * (kTB / 8);
+        const int chunks = a.M * w8;
+        for (int c = threadIdx.x; c < chunks; c += kWaves * 64) {
+            const int m = c / w8;
+            const int k8 = c - m * w8;
+            *reinterpret_cast<v4u*>(xl + static_cast<size_t>(m) * a.xls + 8 * k8) =
+                *reinterpret_cast<const v4u*>(a.X + static_cast<size_t>(m) * a.K + kb0 * kTB + 8 * k8);
+        }
+        __syncthreads();
+    }
+    if (ng > 0) {
+        for (int i0 = 0; i0 < ng; i0 += NBUF) {
 #pragma unroll
             for (int b = 0; b < NBUF; ++b) {
-                if (i0 + b >= np) break;
-                load_pair(buf[(b + NBUF - 1) % NBUF], pair_of(i0 + b + NBUF - 1));
-                compute(buf[b], 2);
+                if (i0 + b >= ng) break;
+                load_pairs(buf[(b + NBUF - 1) % NBUF], QB * group_of(i0 + b + NBUF - 1), QB / 2);
+                compute(buf[b], QB * group_of(i0 + b), QB);
             }
         }
     }
-    // an unpaired last block (odd K/128), in the last split, by the last wave
-    if ((G & 1) && last_split && w == kWaves - 1) {
+    // the blocks past the last full group (G % QB of them), in the last
+    // split, by every wave (NSP: each for its own columns) or the last wave:
+    // whole pairs, then an unpaired last block
+    const int rem = G - QB * NG;
+    if (rem > 0 && last_split && (NSP || w == kWaves - 1)) {
         Stage st;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const uint2 u = *reinterpret_cast<const uint2*>(rowp[s] + 64 * P + 8 * q4);
-            st.c[s] = make_uint4(u.x, u.y, 0, 0);
-            st.p[0][s] = a.am[static_cast<size_t>(2 * P) * a.N + ncol[s]];
+        const int g0 = QB * NG;
+        const int npair = rem / 2;
+        if (npair > 0) {
+            load_pairs(st, g0, npair);
+            compute(st, g0, 2 * npair);
         }
-        load_x(st, 0, 2 * P);
-        compute(st, 1);
+        if (rem & 1) {
+            const int g = G - 1;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const uint2 u = *reinterpret_cast<const uint2*>(tilep[s] + 1024 * (g / 2) + 8 * lane);
+                st.c[0][s] = make_uint4(u.x, u.y, 0, 0);
+            }
+            load_p(st, g, 1);
+            load_x(st, 0, g);
+            compute(st, g, 1);
+        }
     }
 
+    if constexpr (NSP) {
+        // each wave owns its columns: write its sums
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int n = ((blockIdx.x * kWaves + w) * NS + s) * 16 + c16;
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + 16 * ms + 4 * q4 + i;
+                    if (n >= a.N || m >= a.M) continue;
+                    if (a.part)
+                        a.part[(static_cast<size_t>(blockIdx.z) * a.M + m) * a.N + n] = facc[s][ms][i];
+                    else
+                        a.Y[static_cast<size_t>(m) * a.N + n] = f2h(facc[s][ms][i]);
+                }
+        }
+        return;
+    }
     // sum the waves' partial results in LDS: red[w][r][lane], r = (s, ms, i)
     constexpr int R = NS * MS * 4;
 #pragma unroll
@@ -324,25 +438,49 @@ __global__ __launch_bounds__(kThreads) void k_tern_reduce(const float* __restric
 hipError_t tern_pack_launch(const float* Wt, int N, int K, int iters, uint8_t* Tq, uint32_t* am,
                             hipStream_t stream) {
     if (N == 0) return hipSuccess;
-    k_tern_pack<<<dim3(N, K / kTB), kTB, 0, stream>>>(Wt, K, iters, Tq, am);
+    k_tern_pack<<<dim3(tern_rows(N), K / kTB), kTB, 0, stream>>>(Wt, N, K, iters, Tq, am);
     return hipGetLastError();
 }
 
+// kernel variants: MS, NS, QB, NBUF, XL, W, NSP
+struct TernVariant { int ms, ns, qb, nbuf; bool xl; int waves; bool nsp; };
+// one token: waves split K, X (K halfs) in LDS
+constexpr TernVariant kTernM1{1, 2, 4, 4, true, 8, false};
+// 2..16 tokens: waves split the columns (8 x 32 per workgroup, so that few
+// workgroups read X), workgroups split K, X's slice in LDS
+constexpr TernVariant kTernM16{1, 2, 4, 4, true, 8, true};
+// 17..64 tokens: tiles of 32 rows, waves split K, X from global memory
+constexpr TernVariant kTernM64{2, 2, 2, 2, false, 8, false};
+
 TernPlan tern_plan(int M, int N, int K, int cus) {
     TernPlan p{};
-    const int P = (K / kTB) / 2;
-    p.ms = M <= 16 ? 1 : 2;
-    p.ns = 2;
-    const long tiles = static_cast<long>(ceil_div(N, 16 * p.ns)) * ceil_div(M, 16 * p.ms);
-    // at least one workgroup of kWaves waves per compute unit; split K across
-    // workgroups only when the tiles fall short of that, keeping at least
-    // two pairs per wave
+    const TernVariant v = M > 16 ? kTernM64 : (M > 1 || tern_xl_bytes(M, K) > kXlMax ? kTernM16 : kTernM1);
+    p.ms = v.ms;
+    p.ns = v.ns;
+    p.qb = v.qb;
+    p.xl = v.xl;
+    p.nsp = v.nsp;
+    p.waves = v.waves;
+    const int G = K / kTB;
+    const int NG = G / p.qb;
+    const int cols = 16 * p.ns * (p.nsp ? p.waves : 1);
+    const long tiles = static_cast<long>(ceil_div(N, cols)) * ceil_div(M, 16 * p.ms);
+    // at least one workgroup per compute unit; split K across workgroups only
+    // when the tiles fall short of that (or, for NSP, when X's slice must be
+    // narrower to fit in LDS), keeping at least two groups per wave
     int splits = tiles > 0 ? static_cast<int>((static_cast<long>(cus) + tiles - 1) / tiles) : 1;
-    const int cap = P / (2 * kWaves);
-    if (splits > cap) splits = cap;
-    if (splits < 1) splits = 1;
-    p.pps = ceil_div(P, splits);
-    p.splits = P > 0 ? ceil_div(P, p.pps) : 1;
+    const int cap = max(1, p.nsp ? NG / 2 : NG / (2 * p.waves));
+    splits = max(1, min(splits, cap));
+    const int rem = G - NG * p.qb;
+    auto xls_of = [&](int gps) { return (p.nsp ? min(G, gps * p.qb + rem) : G) * kTB + 8; };
+    auto gps_of = [&](int sp) { return NG > 0 ? ceil_div(NG, sp) : 0; };
+    // NSP: X's slice (a split's groups plus the tail blocks) must fit in LDS
+    while (p.nsp && splits < cap && static_cast<size_t>(M) * xls_of(gps_of(splits)) * 2 > kXlMax)
+        ++splits;
+    p.gps = gps_of(splits);
+    p.splits = NG > 0 ? ceil_div(NG, p.gps) : 1;
+    p.xls = xls_of(p.gps);
+    p.lds = p.xl ? static_cast<size_t>(M) * p.xls * 2 : 0;
     return p;
 }
 
@@ -351,18 +489,51 @@ size_t tern_workspace_bytes(int M, int N, int K) {
     return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
 }
 
+namespace {
+template <int MS, int NS, int QB, int NBUF, bool XL, int W, bool NSP>
+hipError_t tern_launch(const TernArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+    auto* kern = &k_tern_gemm<MS, NS, QB, NBUF, XL, W, NSP>;
+    if (lds > 64 * 1024) {
+        // more than the default dynamic LDS limit: raise it once per device
+        static bool raised[64] = {};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= 64 || !raised[dev]) {
+            // the CU's LDS less the kernel's static reduction buffer
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kLdsMax - static_cast<int>(sizeof(float)) * tern_red_floats<MS, NS, W, NSP>());
+            if (e != hipSuccess) return e;
+            if (dev >= 0 && dev < 64) raised[dev] = true;
+        }
+    }
+    kern<<<grid, W * 64, lds, stream>>>(a);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t tern_gemm_launch(const uint16_t* X, int M, int N, int K, const uint8_t* Tq,
                             const uint32_t* am, uint16_t* Y, void* ws, hipStream_t stream) {
     if (M == 0) return hipSuccess;
     const TernPlan p = tern_plan(M, N, K, device_cu_count());
+    if (p.lds + sizeof(float) * tern_red_floats<1, 2, 8, false>() > static_cast<size_t>(kLdsMax))
+        return hipErrorInvalidValue;            // cannot happen for M <= 64, K <= 65536
     float* part = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
-    TernArgs a{X, Tq, am, Y, part, M, N, K, p.pps};
-    dim3 grid(ceil_div(N, 16 * p.ns), ceil_div(M, 16 * p.ms), p.splits);
-    constexpr int threads = kWaves * 64;
-    if (p.ms == 1)
-        k_tern_gemm<1, 2, 3><<<grid, threads, 0, stream>>>(a);
+    TernArgs a{X, Tq, am, Y, part, M, N, K, p.gps, p.xls};
+    const int cols = 16 * p.ns * (p.nsp ? p.waves : 1);
+    dim3 grid(ceil_div(N, cols), ceil_div(M, 16 * p.ms), p.splits);
+    hipError_t e;
+#define W4A4_TERN_LAUNCH(v)                                                                 \
+    tern_launch<v.ms, v.ns, v.qb, v.nbuf, v.xl, v.waves, v.nsp>(a, grid, p.lds, stream)
+    if (p.nsp)
+        e = W4A4_TERN_LAUNCH(kTernM16);
+    else if (p.ms == 1)
+        e = W4A4_TERN_LAUNCH(kTernM1);
     else
-        k_tern_gemm<2, 2, 2><<<grid, threads, 0, stream>>>(a);
+        e = W4A4_TERN_LAUNCH(kTernM64);
+#undef W4A4_TERN_LAUNCH
+    if (e != hipSuccess) return e;
     if (part) {
         const size_t count = static_cast<size_t>(M) * N;
         k_tern_reduce<<<static_cast<unsigned>((count + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
