@@ -424,13 +424,45 @@ __global__ __launch_bounds__(W * 64) void k_tern_gemm(TernArgs a) {
     }
 }
 
+// Y = fp16 of the sum over splits of part[z] (fp32 [splits][count]); each
+// thread four consecutive outputs, the splits' loads issued four at a time
 __global__ __launch_bounds__(kThreads) void k_tern_reduce(const float* __restrict__ part, int splits,
                                                           size_t count, uint16_t* __restrict__ Y) {
-    const size_t e = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (e >= count) return;
-    float s = 0.0f;
-    for (int z = 0; z < splits; ++z) s += part[static_cast<size_t>(z) * count + e];
-    Y[e] = f2h(s);
+    const size_t e0 = (static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
+    if (e0 >= count) return;
+    if (e0 + 4 <= count && (count & 3) == 0) {
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        int z = 0;
+        for (; z + 4 <= splits; z += 4) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = *reinterpret_cast<const float4*>(part + static_cast<size_t>(z + u) * count + e0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc.x += v[u].x;
+                acc.y += v[u].y;
+                acc.z += v[u].z;
+                acc.w += v[u].w;
+            }
+        }
+        for (; z < splits; ++z) {
+            const float4 v = *reinterpret_cast<const float4*>(part + static_cast<size_t>(z) * count + e0);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        const uint32_t lo = static_cast<uint32_t>(f2h(acc.x)) | (static_cast<uint32_t>(f2h(acc.y)) << 16);
+        const uint32_t hi = static_cast<uint32_t>(f2h(acc.z)) | (static_cast<uint32_t>(f2h(acc.w)) << 16);
+        *reinterpret_cast<uint2*>(Y + e0) = make_uint2(lo, hi);
+        return;
+    }
+    for (size_t e = e0; e < e0 + 4 && e < count; ++e) {
+        float acc = 0.0f;
+        for (int z = 0; z < splits; ++z) acc += part[static_cast<size_t>(z) * count + e];
+        Y[e] = f2h(acc);
+    }
 }
 
 }  // namespace
@@ -445,7 +477,7 @@ hipError_t tern_pack_launch(const float* Wt, int N, int K, int iters, uint8_t* T
 // kernel variants: MS, NS, QB, NBUF, XL, W, NSP
 struct TernVariant { int ms, ns, qb, nbuf; bool xl; int waves; bool nsp; };
 // one token: waves split K, X (K halfs) in LDS
-constexpr TernVariant kTernM1{1, 2, 4, 4, true, 8, false};
+constexpr TernVariant kTernM1{1, 1, 4, 4, true, 8, false};
 // 2..16 tokens: waves split the columns (8 x 32 per workgroup, so that few
 // workgroups read X), workgroups split K, X's slice in LDS
 constexpr TernVariant kTernM16{1, 2, 4, 4, true, 8, true};
@@ -536,8 +568,8 @@ hipError_t tern_gemm_launch(const uint16_t* X, int M, int N, int K, const uint8_
     if (e != hipSuccess) return e;
     if (part) {
         const size_t count = static_cast<size_t>(M) * N;
-        k_tern_reduce<<<static_cast<unsigned>((count + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
-            part, p.splits, count, Y);
+        k_tern_reduce<<<static_cast<unsigned>((count + 4 * kThreads - 1) / (4 * kThreads)), kThreads, 0,
+                        stream>>>(part, p.splits, count, Y);
     }
     return hipGetLastError();
 }
