@@ -59,6 +59,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 linear TOPS + µs/layer; % of INT8 MFMA peak (prefill) / HBM BW (decode)"
 PEAK_INT8_TOPS = 5000.0          # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, GB/s
+PEAK_FP6_TOPS = 10100.0          # MI355X dense fp6 MFMA, TOP/s
 MALL_BYTES = 256 << 20           # Infinity Cache: rotate weight copies past it
 
 
@@ -79,6 +80,9 @@ def parse():
                          "M <= 16 tokens)")
     ap.add_argument("--bits", type=int, choices=[3, 4], default=4,
                     help="code width of weights and activations (3: W3A3, FRM-PTQ)")
+    ap.add_argument("--gemm", choices=["int8", "f6"], default="int8",
+                    help="matrix pipe of the INT4 x INT4 product: int8 MFMA on unpacked nibbles, or "
+                         "fp6 MFMA on codes held exactly as E2M3 (w4a4_linear_f6)")
     ap.add_argument("--act-quant", choices=["dynamic", "tensor", "channel"], default="dynamic",
                     help="activation quantizer: per-token dynamic scales, or static steps "
                          "(one per tensor, or one per channel migrated into the weights)")
@@ -227,6 +231,8 @@ def main():
         return
     if args.bits != 4 and (args.act_quant != "dynamic" or args.path != "two"):
         raise SystemExit("--bits 3 runs the dynamic two-launch layer only")
+    if args.gemm == "f6" and (args.bits != 4 or args.act_quant != "dynamic" or args.path != "two"):
+        raise SystemExit("--gemm f6 runs the dynamic two-launch 4-bit layer only")
 
     import torch
     import workloads as WL
@@ -285,6 +291,15 @@ def main():
     tq_ws = torch.empty(max(1, L.transform_quant_workspace_bytes(M, wl.n1, wl.n2, False)),
                         dtype=torch.uint8, device=dev)
     g_ws = torch.empty(max(1, L.gemm_workspace_bytes(M, desc)), dtype=torch.uint8, device=dev)
+    f6 = args.gemm == "f6"
+    if f6:
+        # offline: the packed weights to the fp6 layout (exact), one per copy
+        w6 = [L.pack_weights_f6(desc, Wq, zw) for (_, Wq, _, zw) in packs]
+        ws = torch.empty(max(1, L.linear_f6_workspace_bytes(M, wl.n1, wl.n2, desc)),
+                         dtype=torch.uint8, device=dev)
+        g_ws = torch.empty(max(1, L.gemm_f6_workspace_bytes(M, desc)), dtype=torch.uint8,
+                           device=dev)
+        torch.cuda.synchronize()
 
     # single-kernel decode (one launch per layer), on request
     single = False
@@ -312,8 +327,17 @@ def main():
             decode_call(i)
         elif static:
             L.linear_static(X, P1, P2, steps, pc, desc, Wq, sw, zw, out=Y, ws=ws)
+        elif f6:
+            L.linear_f6(X, P1, P2, desc, w6[i % copies], sw, out=Y, ws=ws)
         else:
             L.linear_bits(X, P1, P2, args.bits, desc, Wq, sw, zw, out=Y, ws=ws)
+
+    def gemm_call(i):
+        _, Wq, sw, zw = packs[i % copies]
+        if f6:
+            L.gemm_f6(Xq, sx, desc, w6[i % copies], sw, out=Y, ws=g_ws)
+        else:
+            L.gemm(Xq, sx, desc, Wq, sw, zw, out=Y, ws=g_ws)
 
     def act(i):
         if static:
@@ -345,13 +369,11 @@ def main():
     torch.cuda.synchronize()
     tq_us = e0.elapsed_time(e1) * 1e3 / args.steps
     for i in range(args.warmup):
-        _, Wq, sw, zw = packs[i % copies]
-        L.gemm(Xq, sx, desc, Wq, sw, zw, out=Y, ws=g_ws)
+        gemm_call(i)
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
-        _, Wq, sw, zw = packs[i % copies]
-        L.gemm(Xq, sx, desc, Wq, sw, zw, out=Y, ws=g_ws)
+        gemm_call(i)
     e1.record()
     torch.cuda.synchronize()
     gemm_us = e0.elapsed_time(e1) * 1e3 / args.steps
@@ -369,10 +391,6 @@ def main():
         single_us = e0.elapsed_time(e1) * 1e3 / args.steps
         if int(sync[L.DECODE_SYNC_ERROR_WORD].item()) != 0:
             raise SystemExit("the single-kernel decode timed out waiting for its activations")
-
-    def gemm_call(i):
-        _, Wq, sw, zw = packs[i % copies]
-        L.gemm(Xq, sx, desc, Wq, sw, zw, out=Y, ws=g_ws)
 
     dist = event_stats(decode_call if single else gemm_call, max(20, args.steps))
 
@@ -402,6 +420,14 @@ def main():
         roof["kernel"] = L.gemm_kernel_name(M, desc)
         roof["kernel_us"] = round(gemm_us, 2)
         roof["traffic"] = traffic_from_profiles("gemm", wl.name)
+    elif f6:
+        # the w4a4_gemm_f6 call: activations to the fp6 layout, then the product
+        achieved = ops / (gemm_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP6_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_FP6_TOPS, 4)}
+        roof["kernel"] = "w4a4_gemm_f6 = k_f6_convert + " + L.gemm_f6_kernel_name(M, desc)
+        roof["kernel_us"] = round(gemm_us, 2)
+        roof["traffic"] = traffic_from_profiles("gemm_f6", wl.name, "gemm_f6.hip")
     else:
         achieved = ops / (gemm_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
@@ -417,14 +443,17 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8 MFMA/int32 acc (int4 codes), fp32 transform",
+        "dtype": ("fp6 E2M3 MFMA on the exact int4 codes (v/2), fp32 acc, fp32 transform" if f6
+                  else "int8 MFMA/int32 acc (int4 codes), fp32 transform"),
         "data": "synthetic (seeded; LLaMA-shaped, outlier channels and pivot token)",
         "config": {"workload": wl.description, "name": wl.name, "M": M, "K": K, "N": N,
                    "n1": wl.n1, "n2": wl.n2, "group_size": wl.group_size,
                    "asymmetric_weights": wl.asymmetric, "weight_copies_rotated": copies,
-                   "act_quant": args.act_quant, "bits": args.bits},
+                   "act_quant": args.act_quant, "bits": args.bits, "gemm": args.gemm},
         "us_per_layer": round(t_step * 1e6, 2),
-        "path": "single-kernel decode (w4a4_linear_decode)" if single else "two launches (w4a4_linear)",
+        "path": ("single-kernel decode (w4a4_linear_decode)" if single else
+                 "transform + fp6 conversion + product (w4a4_linear_f6)" if f6 else
+                 "two launches (w4a4_linear)"),
         "transform_quant_us": round(tq_us, 2),
         "transform_quant": transform,
         "gemm_us": round(gemm_us, 2),

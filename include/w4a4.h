@@ -323,6 +323,49 @@ int w4a4_ternary_gemm(const uint16_t* X, int32_t M, int32_t N, int32_t K, const 
                       const uint32_t* am, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* INT4 x INT4 GEMM on the fp6 matrix pipe (prefill)                         */
+/* ------------------------------------------------------------------------ */
+/* The same layer products as w4a4_gemm (FlatQuant page, section 核心思想;
+ * FRM-PTQ page, section 初步介绍; FPTQuant page, section 3. 伪动态残差缩放):
+ * D[m,n,g] = sum over the group of q_x (u - z) and
+ * Y = fp16(s_x[m] sum_g s_w[n,g] D[m,n,g]).  Every code v the product takes
+ * (q in [-8, 7], u - z in [-15, 15]) is held as v / 2, which an fp6 E2M3
+ * number represents exactly, and the sums are exact in fp32, so D is
+ * computed exactly on the fp6 matrix pipe (twice the int8 rate).  The
+ * operands are kept in an fp6 fragment layout: rows padded to a multiple of
+ * 32 (padding zero), 0.75 bytes per code. */
+
+/* Bytes of the fp6 weights for desc (0 for an invalid desc). */
+size_t w4a4_weights_f6_bytes(const w4a4_weight_desc* desc);
+
+/* Offline: packed weights (w4a4_pack_weights' Wq and, if asymmetric, z_w) to
+ * the fp6 layout W6 (w4a4_weights_f6_bytes bytes), exactly. */
+int w4a4_pack_weights_f6(const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* z_w,
+                         uint8_t* W6, void* stream);
+
+/* Workspace of w4a4_gemm_f6: the activations in the fp6 layout. */
+size_t w4a4_gemm_f6_workspace_bytes(int32_t M, const w4a4_weight_desc* desc);
+
+/* Y [M][N] fp16 from packed activations Xq [M][K/2] (w4a4_transform_quant's
+ * output), s_x, the fp6 weights W6 and s_w; two launches (activations to the
+ * fp6 layout in ws, then the product). */
+int w4a4_gemm_f6(const uint8_t* Xq, const float* s_x, int32_t M, const w4a4_weight_desc* desc,
+                 const uint8_t* W6, const uint16_t* s_w, uint16_t* Y, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Name of the kernel configuration w4a4_gemm_f6 would run (host query). */
+const char* w4a4_gemm_f6_kernel_name(int32_t M, const w4a4_weight_desc* desc);
+
+/* The whole dynamic layer (as w4a4_linear) with the product on the fp6 pipe;
+ * weights from w4a4_pack_weights_f6. */
+size_t w4a4_linear_f6_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t has_c,
+                                      const w4a4_weight_desc* desc);
+int w4a4_linear_f6(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                   const float* P2, const float* c, float alpha_a, const w4a4_weight_desc* desc,
+                   const uint8_t* W6, const uint16_t* s_w, uint16_t* Y, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Single-kernel decode layer                                                */
 /* ------------------------------------------------------------------------ */
 

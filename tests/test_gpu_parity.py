@@ -300,7 +300,7 @@ def test_linear_with_channel_scale_and_clip():
     _layer_parity(inp, c=c, alpha=0.8)
 
 
-NUM_TILE_CONFIGS = 9
+NUM_TILE_CONFIGS = 12
 NUM_DECODE_VARIANTS = 4
 
 

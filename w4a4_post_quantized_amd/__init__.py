@@ -27,6 +27,8 @@ __all__ = [
     "TERNARY_BLOCK", "TERNARY_MAX_M", "ternary_weight_bytes", "pack_ternary",
     "ternary_gemm_workspace_bytes",
     "ternary_gemm",
+    "weights_f6_bytes", "pack_weights_f6", "gemm_f6_workspace_bytes", "gemm_f6",
+    "gemm_f6_kernel_name", "linear_f6_workspace_bytes", "linear_f6",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so")
@@ -46,6 +48,9 @@ EXPORTED_SYMBOLS = [
     "w4a4_pack_weights_bits", "w4a4_transform_quant_bits", "w4a4_linear_bits",
     "w4a4_ternary_weight_bytes", "w4a4_pack_ternary", "w4a4_ternary_gemm_workspace_bytes",
     "w4a4_ternary_gemm",
+    "w4a4_weights_f6_bytes", "w4a4_pack_weights_f6", "w4a4_gemm_f6_workspace_bytes",
+    "w4a4_gemm_f6", "w4a4_gemm_f6_kernel_name", "w4a4_linear_f6_workspace_bytes",
+    "w4a4_linear_f6",
 ]
 
 DECODE_SYNC_BYTES = 1024          # W4A4_DECODE_SYNC_BYTES
@@ -102,6 +107,14 @@ def lib() -> ctypes.CDLL:
             "w4a4_gemm": (ctypes.c_int, [vp, vp, i32, dp, vp, vp, vp, vp, vp, sz, vp]),
             "w4a4_gemm_i32": (ctypes.c_int, [vp, i32, dp, vp, vp, vp, vp]),
             "w4a4_gemm_kernel_name": (ctypes.c_char_p, [i32, dp]),
+            "w4a4_weights_f6_bytes": (sz, [dp]),
+            "w4a4_pack_weights_f6": (ctypes.c_int, [dp, vp, vp, vp, vp]),
+            "w4a4_gemm_f6_workspace_bytes": (sz, [i32, dp]),
+            "w4a4_gemm_f6": (ctypes.c_int, [vp, vp, i32, dp, vp, vp, vp, vp, sz, vp]),
+            "w4a4_gemm_f6_kernel_name": (ctypes.c_char_p, [i32, dp]),
+            "w4a4_linear_f6_workspace_bytes": (sz, [i32, i32, i32, i32, dp]),
+            "w4a4_linear_f6": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, ctypes.c_float, dp,
+                                              vp, vp, vp, vp, sz, vp]),
             "w4a4_linear_workspace_bytes": (sz, [i32, i32, i32, i32, dp]),
             "w4a4_linear": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, dp, vp, vp, vp, vp, vp, sz, vp]),
             "w4a4_migrate_steps": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
@@ -614,4 +627,64 @@ def ternary_gemm(X, Tq, am, N: int, out=None, ws=None, stream=None):
     _check(lib().w4a4_ternary_gemm(_p(X), M, N, K, _p(Tq), _p(am), _p(Y), _p(ws),
                                    nb if ws is None else ws.numel(), _stream(stream)),
            "w4a4_ternary_gemm")
+    return Y
+
+
+# ---------------------------------------------------------------------------
+# INT4 GEMM on the fp6 matrix pipe (prefill)
+# ---------------------------------------------------------------------------
+def weights_f6_bytes(desc: WeightDesc) -> int:
+    return lib().w4a4_weights_f6_bytes(ctypes.byref(desc))
+
+
+def pack_weights_f6(desc: WeightDesc, Wq, z_w=None, stream=None):
+    """Packed INT4 weights (and zero points) -> uint8 [weights_f6_bytes] in the fp6 layout."""
+    torch = _torch()
+    W6 = torch.empty((weights_f6_bytes(desc),), dtype=torch.uint8, device=Wq.device)
+    _check(lib().w4a4_pack_weights_f6(ctypes.byref(desc), _p(Wq), _p(z_w), _p(W6), _stream(stream)),
+           "w4a4_pack_weights_f6")
+    return W6
+
+
+def gemm_f6_workspace_bytes(M: int, desc: WeightDesc) -> int:
+    return lib().w4a4_gemm_f6_workspace_bytes(M, ctypes.byref(desc))
+
+
+def gemm_f6(Xq, s_x, desc: WeightDesc, W6, s_w, out=None, ws=None, stream=None):
+    """Y [M, N] fp16 = dequant(Xq · W^T) with the product on the fp6 pipe."""
+    torch = _torch()
+    M = Xq.shape[0]
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=Xq.device)
+    nb = gemm_f6_workspace_bytes(M, desc)
+    ws = _ws(nb, Xq.device, ws)
+    _check(lib().w4a4_gemm_f6(_p(Xq), _p(s_x), M, ctypes.byref(desc), _p(W6), _p(s_w), _p(Y),
+                              _p(ws), nb if ws is None else ws.numel(), _stream(stream)),
+           "w4a4_gemm_f6")
+    return Y
+
+
+def gemm_f6_kernel_name(M: int, desc: WeightDesc) -> str:
+    name = lib().w4a4_gemm_f6_kernel_name(M, ctypes.byref(desc))
+    if name is None:
+        raise W4A4Error(-1, "w4a4_gemm_f6_kernel_name", lib().w4a4_last_error().decode())
+    return name.decode()
+
+
+def linear_f6_workspace_bytes(M: int, n1: int, n2: int, desc: WeightDesc, has_c: bool = False) -> int:
+    return lib().w4a4_linear_f6_workspace_bytes(M, n1, n2, int(bool(has_c)), ctypes.byref(desc))
+
+
+def linear_f6(X, P1, P2, desc: WeightDesc, W6, s_w, c=None, alpha_a: float = 1.0, out=None,
+              ws=None, stream=None):
+    """Whole W4A4 layer with the product on the fp6 pipe: Y [M, N] fp16."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=X.device)
+    nb = linear_f6_workspace_bytes(M, n1, n2, desc, c is not None)
+    ws = _ws(nb, X.device, ws)
+    _check(lib().w4a4_linear_f6(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
+                                ctypes.byref(desc), _p(W6), _p(s_w), _p(Y), _p(ws),
+                                nb if ws is None else ws.numel(), _stream(stream)),
+           "w4a4_linear_f6")
     return Y

@@ -32,7 +32,7 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "weights.hip", "linear_decode.hip",
-           "kv_cache.hip", "attention.hip", "ternary.hip"]
+           "kv_cache.hip", "attention.hip", "ternary.hip", "gemm_f6.hip"]
 
 
 def _compile(src: str, extra=()):

@@ -427,6 +427,141 @@ int w4a4_linear_static(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, con
 }
 
 // ---------------------------------------------------------------------------
+// INT4 GEMM on the fp6 matrix pipe (prefill)
+// ---------------------------------------------------------------------------
+size_t w4a4_weights_f6_bytes(const w4a4_weight_desc* desc) {
+    if (check_desc(desc, true) != W4A4_OK) return 0;
+    return w4a4::f6_bytes(desc->N, desc->K);
+}
+
+int w4a4_pack_weights_f6(const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* z_w,
+                         uint8_t* W6, void* stream) {
+    if (int s = check_desc(desc, true)) return s;
+    REQUIRE_PTR(Wq);
+    REQUIRE_PTR(W6);
+    REQUIRE_ALIGNED(Wq);
+    REQUIRE_ALIGNED(W6);
+    if (desc->asymmetric) {
+        REQUIRE_PTR(z_w);
+        REQUIRE_ALIGNED(z_w);
+    }
+    hipError_t e = w4a4::f6_convert_launch(Wq, desc->N, desc->K, desc->asymmetric ? z_w : nullptr,
+                                           desc->group_size, W6, static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_pack_weights_f6");
+}
+
+size_t w4a4_gemm_f6_workspace_bytes(int32_t M, const w4a4_weight_desc* desc) {
+    if (M < 0 || check_desc(desc, true) != W4A4_OK) return 0;
+    ok();
+    return align256(w4a4::f6_bytes(M, desc->K));
+}
+
+static int gemm_f6_common(const uint8_t* Xq, const float* s_x, int32_t M,
+                          const w4a4_weight_desc* desc, const uint8_t* W6, const uint16_t* s_w,
+                          uint16_t* Y, void* ws, size_t ws_bytes, hipStream_t st,
+                          const char* name) {
+    w4a4::F6Args a{static_cast<const uint8_t*>(ws), s_x, W6, s_w, Y, M, desc->N, desc->K,
+                   desc->group_size};
+    hipError_t e = w4a4::f6_convert_launch(Xq, M, desc->K, nullptr, desc->group_size,
+                                           static_cast<uint8_t*>(ws), st);
+    if (e == hipSuccess) e = w4a4::gemm_f6_launch(a, st);
+    (void)ws_bytes;
+    return hip_status(e, name);
+}
+
+int w4a4_gemm_f6(const uint8_t* Xq, const float* s_x, int32_t M, const w4a4_weight_desc* desc,
+                 const uint8_t* W6, const uint16_t* s_w, uint16_t* Y, void* ws, size_t ws_bytes,
+                 void* stream) {
+    if (int s = check_desc(desc, true)) return s;
+    REQUIRE(M >= 0, W4A4_ERR_INVALID_ARG, "M = %d is negative", M);
+    if (M == 0) return ok();
+    REQUIRE_PTR(Xq);
+    REQUIRE_PTR(s_x);
+    REQUIRE_PTR(W6);
+    REQUIRE_PTR(s_w);
+    REQUIRE_PTR(Y);
+    REQUIRE_ALIGNED(Xq);
+    REQUIRE_ALIGNED(s_x);
+    REQUIRE_ALIGNED(W6);
+    REQUIRE_ALIGNED(s_w);
+    REQUIRE_ALIGNED(Y);
+    const size_t need = w4a4_gemm_f6_workspace_bytes(M, desc);
+    REQUIRE(ws != nullptr && ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes",
+            ws ? ws_bytes : 0, need);
+    REQUIRE_ALIGNED(ws);
+    return gemm_f6_common(Xq, s_x, M, desc, W6, s_w, Y, ws, ws_bytes,
+                          static_cast<hipStream_t>(stream), "w4a4_gemm_f6");
+}
+
+const char* w4a4_gemm_f6_kernel_name(int32_t M, const w4a4_weight_desc* desc) {
+    if (check_desc(desc, true) != W4A4_OK) return nullptr;
+    if (M < 0) {
+        fail(W4A4_ERR_INVALID_ARG, "M = %d is negative", M);
+        return nullptr;
+    }
+    ok();
+    w4a4::F6Args a{nullptr, nullptr, nullptr, nullptr, nullptr, M, desc->N, desc->K,
+                   desc->group_size};
+    return w4a4::gemm_f6_kernel_name(a);
+}
+
+size_t w4a4_linear_f6_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t has_c,
+                                      const w4a4_weight_desc* desc) {
+    if (M < 0 || desc == nullptr || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR ||
+        n2 > W4A4_MAX_FACTOR || desc->K < 1 || desc->group_size < 1)
+        return 0;
+    const size_t K = static_cast<size_t>(n1) * n2;
+    const size_t tq = w4a4::tq_workspace_bytes(M, n1, n2, has_c != 0);
+    const size_t x6 = align256(w4a4::f6_bytes(M, static_cast<int>(K)));
+    return align256(K / 2 * M) + align256(sizeof(float) * M) + (tq > x6 ? tq : x6);
+}
+
+int w4a4_linear_f6(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                   const float* P2, const float* c, float alpha_a, const w4a4_weight_desc* desc,
+                   const uint8_t* W6, const uint16_t* s_w, uint16_t* Y, void* ws,
+                   size_t ws_bytes, void* stream) {
+    if (int s = check_desc(desc, true)) return s;
+    if (int s = check_factors(M, n1, n2)) return s;
+    REQUIRE(desc->K == n1 * n2, W4A4_ERR_INVALID_ARG, "desc->K = %d != n1*n2 = %d", desc->K,
+            n1 * n2);
+    REQUIRE(alpha_a > 0.0f && alpha_a <= 1.0f, W4A4_ERR_INVALID_ARG,
+            "alpha_a = %g must lie in (0, 1]", static_cast<double>(alpha_a));
+    if (M == 0) return ok();
+    REQUIRE_PTR(X);
+    REQUIRE_PTR(P1);
+    REQUIRE_PTR(P2);
+    REQUIRE_PTR(W6);
+    REQUIRE_PTR(s_w);
+    REQUIRE_PTR(Y);
+    REQUIRE_PTR(ws);
+    REQUIRE_ALIGNED(X);
+    REQUIRE_ALIGNED(P1);
+    REQUIRE_ALIGNED(P2);
+    if (c) REQUIRE_ALIGNED(c);
+    REQUIRE_ALIGNED(W6);
+    REQUIRE_ALIGNED(s_w);
+    REQUIRE_ALIGNED(Y);
+    REQUIRE_ALIGNED(ws);
+    const size_t need = w4a4_linear_f6_workspace_bytes(M, n1, n2, c != nullptr, desc);
+    REQUIRE(ws_bytes >= need, W4A4_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+
+    const size_t K = static_cast<size_t>(n1) * n2;
+    char* p = static_cast<char*>(ws);
+    uint8_t* Xq = reinterpret_cast<uint8_t*>(p);
+    p += align256(K / 2 * M);
+    float* s_x = reinterpret_cast<float*>(p);
+    p += align256(sizeof(float) * M);
+    void* sub = p;
+    const size_t sub_bytes = ws_bytes - static_cast<size_t>(p - static_cast<char*>(ws));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{alpha_a, nullptr, false},
+                                   true, Xq, s_x, nullptr, sub, sub_bytes, st);
+    if (e != hipSuccess) return hip_status(e, "w4a4_linear_f6");
+    // the fp6 activations reuse the transform's sub-workspace once it is done
+    return gemm_f6_common(Xq, s_x, M, desc, W6, s_w, Y, sub, sub_bytes, st, "w4a4_linear_f6");
+}
+
+// ---------------------------------------------------------------------------
 size_t w4a4_linear_decode_workspace_bytes(int32_t M, int32_t n1, int32_t n2) {
     if (M < 1 || M > 16 || n1 < 1 || n2 < 1 || n1 > W4A4_MAX_FACTOR || n2 > W4A4_MAX_FACTOR)
         return 0;

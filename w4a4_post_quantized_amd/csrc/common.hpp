@@ -197,6 +197,44 @@ __device__ __forceinline__ void unpack_asym(const uint4& w, uint32_t bias, uint4
 }
 
 // calls f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+// ---------------------------------------------------------------------------
+// direct-to-LDS copies and their synchronisation
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// 16-byte global -> LDS copy of one lane; the LDS address of lane l is
+// lds_wave_base + 16 * l (the hardware adds the lane offset).
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                     16, 0, 0);
+}
+
+// The same copy issued from inline assembly.  The compiler does not model it
+// as a pending LDS write, so it inserts no wait for all outstanding copies
+// before the next LDS read (which it must do for the builtin, not knowing
+// which LDS bytes the copy writes); the caller orders copies and reads with
+// its own s_waitcnt and barrier.  No output registers; the address registers
+// are read at issue.  lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void dma16_async(const void* src, const uint8_t* lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+            (const __attribute__((address_space(3))) uint8_t*)lds_wave_base)));
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+
+// Workgroup barrier without a memory fence; the compiler-only fences keep
+// LDS accesses from being moved across it.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (B < E) {

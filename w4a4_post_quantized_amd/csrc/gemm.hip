@@ -311,27 +311,6 @@ __device__ __forceinline__ int dl_slot(int row, int c) { return c ^ (((row >> 1)
 
 // s_waitcnt with only a vmcnt condition (gfx9 encoding; expcnt and lgkmcnt
 // left at their no-wait maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// 16-byte global -> LDS copy of one lane; the LDS address of lane l is
-// lds_wave_base + 16 * l (the hardware adds the lane offset).
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
-                                     16, 0, 0);
-}
-
-// Workgroup barrier without a memory fence; the compiler-only fences keep
-// LDS accesses from being moved across it.
-__device__ __forceinline__ void lds_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool ASYM, int MODE>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
@@ -936,6 +915,9 @@ template <int MODE> hipError_t dl128x128_2x2_s4(const GemmArgs& a, hipStream_t s
 template <int MODE> hipError_t dl128x128_2x2_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 128, 2, 2, 3, MODE>(a, s); }
 template <int MODE> hipError_t dl128x256_2x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 256, 2, 4, 3, MODE>(a, s); }
 template <int MODE> hipError_t dl256x256_4x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<256, 256, 4, 4, 3, MODE>(a, s); }
+template <int MODE> hipError_t dl128x384_2x4_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 384, 2, 4, 4, MODE>(a, s); }
+template <int MODE> hipError_t dl128x384_2x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 384, 2, 4, 3, MODE>(a, s); }
+template <int MODE> hipError_t dl128x384_4x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 384, 4, 4, 3, MODE>(a, s); }
 
 
 template <int MODE> hipError_t r16_256x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 128, 2, 4, MODE>(a, s); }
@@ -953,6 +935,9 @@ const KernelCfg kTiles[] = {
     W4A4_CFG("k_gemm_w4a4<256x128, waves 2x4>", r16_256x128_2x4),
     W4A4_CFG_CHAN("k_gemm_dl<128x256, waves 2x4, 3 stages>", dl128x256_2x4_s3),
     W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 4x4, 3 stages>", dl256x256_4x4_s3),
+    W4A4_CFG_CHAN("k_gemm_dl<128x384, waves 2x4, 4 stages>", dl128x384_2x4_s4),
+    W4A4_CFG_CHAN("k_gemm_dl<128x384, waves 2x4, 3 stages>", dl128x384_2x4_s3),
+    W4A4_CFG_CHAN("k_gemm_dl<128x384, waves 4x4, 3 stages>", dl128x384_4x4_s3),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 

@@ -54,6 +54,22 @@ hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_byte
                        hipStream_t stream);
 
 // ---- single-kernel decode layer (linear_decode.hip) --------------------------
+// ---- INT4 GEMM on the fp6 matrix pipe (gemm_f6.hip) ------------------------
+struct F6Args {
+    const uint8_t* X6;      // activation codes / 2, fp6 fragment layout
+    const float* s_x;
+    const uint8_t* W6;      // weight codes (u - z or q) / 2, fp6 fragment layout
+    const uint16_t* s_w;
+    uint16_t* Y;
+    int M, N, K, group_size;
+};
+inline int f6_rows(int R) { return (R + 31) / 32 * 32; }
+size_t f6_bytes(int R, int K);
+hipError_t f6_convert_launch(const uint8_t* src, int R, int K, const uint16_t* z, int group_size,
+                             uint8_t* dst, hipStream_t stream);
+const char* gemm_f6_kernel_name(const F6Args& a);
+hipError_t gemm_f6_launch(const F6Args& a, hipStream_t stream);
+
 size_t linear_decode_workspace_bytes(int M, int n1, int n2);
 // 0: supported; 1: shape not covered; 2: too much LDS; 3: the producers
 // exceed the device's resident capacity
