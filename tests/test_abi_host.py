@@ -316,3 +316,18 @@ def test_ternary_entry_points_validation():
     nb = W.ternary_gemm_workspace_bytes(1, 64, 65536)
     assert nb > 0 and nb % (1 * 64 * 4) == 0
     assert L.w4a4_ternary_gemm(FAKE, 1, 64, 65536, FAKE, FAKE, FAKE, None, 0, None) == -4
+
+
+def test_f6_entry_points_validation():
+    L = W.lib()
+    d = desc(N=100, K=256, g=128, asym=1)
+    assert W.weights_f6_bytes(W.WeightDesc(100, 256, 128, 1)) == 128 * 256 * 3 // 4
+    assert L.w4a4_pack_weights_f6(d, FAKE, None, FAKE, None) == -1        # z_w for asymmetric
+    assert L.w4a4_pack_weights_f6(d, MISALIGNED, FAKE, FAKE, None) == -3
+    assert W.gemm_f6_workspace_bytes(40, W.WeightDesc(100, 256, 128, 1)) >= 64 * 256 * 3 // 4
+    assert L.w4a4_gemm_f6(FAKE, FAKE, 40, d, FAKE, FAKE, FAKE, FAKE, 16, None) == -4
+    assert L.w4a4_gemm_f6(FAKE, FAKE, 0, d, FAKE, FAKE, FAKE, None, 0, None) == 0
+    assert L.w4a4_gemm_f6(FAKE, FAKE, -1, d, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert "k_gemm_f6" in W.gemm_f6_kernel_name(2048, W.WeightDesc(6144, 4096, 4096, 0))
+    assert L.w4a4_linear_f6(FAKE, 4, 16, 16, FAKE, FAKE, None, 1.5, desc(N=64, K=256, g=256),
+                            FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1   # alpha_a
