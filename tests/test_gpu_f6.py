@@ -98,7 +98,8 @@ def _codes(M, N, K, g, asym, seed):
 @pytest.mark.parametrize("tile", range(NUM_F6_TILES))
 @pytest.mark.parametrize("M,N,K,g,asym", [(300, 520, 1024, 1024, False), (300, 520, 1024, 128, True),
                                           (513, 392, 512, 512, True), (70, 96, 128, 128, False),
-                                          (260, 264, 2048, 256, False)])
+                                          (260, 264, 2048, 256, False), (1, 33, 128, 128, True),
+                                          (31, 1, 256, 256, False)])
 def test_gemm_f6_every_tile(tile, M, N, K, g, asym, monkeypatch):
     """Every fp6 tile configuration (forced through W4A4_GEMM_F6_TILE; the
     per-channel-only ones fall back to the default for per-group weights)

@@ -103,7 +103,7 @@ def test_pack_iteration_counts(iters):
                                    (2, 3000, 384), (40, 77, 640), (8, 4096, 896), (3, 50, 128),
                                    (4, 300, 1280), (2, 96, 16384), (20, 64, 8192), (12, 200, 8192),
                                    (9, 64, 12288), (1, 32, 65536), (12, 48, 32768), (3, 50, 8192),
-                                   (7, 33, 4096)])
+                                   (7, 33, 4096), (64, 16, 128), (17, 1, 256), (64, 40, 384)])
 def test_gemm_parity(M, N, K):
     log(f"ternary_gemm M={M} N={N} K={K}")
     wl = WT.TernWorkload("t", M=M, K=K, N=N, x_kind="silu_product" if M % 2 else "normal",
