@@ -20,7 +20,7 @@ from gpu_common import (assert_linear_close, assert_y_close, custom_workload, lo
 
 pytestmark = pytest.mark.gpu
 
-NUM_F6_TILES = 5
+NUM_F6_TILES = 6
 
 
 def W():
@@ -99,7 +99,8 @@ def _codes(M, N, K, g, asym, seed):
 @pytest.mark.parametrize("M,N,K,g,asym", [(300, 520, 1024, 1024, False), (300, 520, 1024, 128, True),
                                           (513, 392, 512, 512, True), (70, 96, 128, 128, False),
                                           (260, 264, 2048, 256, False), (1, 33, 128, 128, True),
-                                          (31, 1, 256, 256, False)])
+                                          (31, 1, 256, 256, False), (130, 200, 5120, 128, True),
+                                          (64, 96, 1536, 128, False), (129, 136, 12288, 128, True)])
 def test_gemm_f6_every_tile(tile, M, N, K, g, asym, monkeypatch):
     """Every fp6 tile configuration (forced through W4A4_GEMM_F6_TILE; the
     per-channel-only ones fall back to the default for per-group weights)
@@ -119,6 +120,35 @@ def test_gemm_f6_every_tile(tile, M, N, K, g, asym, monkeypatch):
     W6 = W().pack_weights_f6(desc, to_dev(O.pack_nibbles(wc)), to_dev(z) if asym else None)
     Y = W().gemm_f6(to_dev(O.pack_nibbles(qx)), to_dev(sx), desc, W6, to_dev(sw)).cpu().numpy()
     assert_y_close(Y, O.epilogue(D_or, sx, sw), O.epilogue(np.abs(D_or), sx, sw))
+
+
+def test_gemm_f6_group_scale_table_offsets():
+    """Groups of 128 codes stage their scales in LDS with 16-byte copies of
+    the scale table: tables at 16-byte aligned offsets inside a larger buffer
+    give the oracle's result, and a table that is not 16-byte aligned is
+    refused by the entry point."""
+    torch, dev = torch_dev()
+    M, N, K, g = 200, 136, 4096, 128
+    qx, wc, z = _codes(M, N, K, g, True, seed=77)
+    rng = np.random.default_rng(78)
+    sx = (rng.uniform(0.5, 3, M) * 0.05).astype(np.float32)
+    sw = (rng.uniform(0.5, 2, (N, K // g)) * 0.003).astype(np.float16)
+    ref = O.epilogue(O.int_gemm(qx, wc, z, g), sx, sw)
+    A = O.epilogue(np.abs(O.int_gemm(qx, wc, z, g)), sx, sw)
+    desc = W().WeightDesc(N, K, g, 1)
+    W6 = W().pack_weights_f6(desc, to_dev(O.pack_nibbles(wc)), to_dev(z))
+    Xq, sx_d = to_dev(O.pack_nibbles(qx)), to_dev(sx)
+    for off in (0, 8, 1):
+        log(f"gemm_f6 scale table at element offset {off}")
+        big = torch.zeros(N * (K // g) + off, dtype=torch.float16, device=dev)
+        big[off:] = to_dev(sw).reshape(-1)
+        sw_d = big[off:].view(N, K // g)
+        if off % 8:
+            with pytest.raises(W().W4A4Error, match="aligned"):
+                W().gemm_f6(Xq, sx_d, desc, W6, sw_d)
+            continue
+        Y = W().gemm_f6(Xq, sx_d, desc, W6, sw_d).cpu().numpy()
+        assert_y_close(Y, ref, A)
 
 
 def _layer_parity_f6(inp, c=None, alpha=1.0):

@@ -229,6 +229,15 @@ __device__ __forceinline__ void dma16_async(const void* src, const uint8_t* lds_
 
 // Workgroup barrier without a memory fence; the compiler-only fences keep
 // LDS accesses from being moved across it.
+// dma16_async with a wave-uniform 64-bit base (scalar registers) and a
+// per-lane 32-bit byte offset
+__device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, const uint8_t* lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint8_t*)lds_wave_base)));
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();

@@ -99,10 +99,21 @@ __global__ __launch_bounds__(256) void k_f6_convert(const uint8_t* __restrict__ 
 // FM x FN MFMAs.  Rows and columns past M, N read the last fragment (in
 // bounds) and are dropped at the store.
 // ---------------------------------------------------------------------------
-enum F6Mode { kF6Chan = 0, kF6Group = 1 };
+//
+// Per-group weights: the sums of each group are folded into an fp32 sum with
+// the group's scale at the group's end (kF6Group).  For groups of one K tile
+// (128 codes) kF6G1 needs no persistent group accumulators: each fragment's
+// first MFMA of a tile takes a zero register operand, and the tile's sums are
+// folded at once (one FMA per element).  Its scales are staged in LDS in
+// chunks of 32 groups by the same direct-to-LDS copies as the operands: a
+// chunk is issued with the first K tile that uses it, and it has landed once
+// that tile's wait has retired all but the newest tile's copies, so kF6G1
+// runs with 3 stages.
+enum F6Mode { kF6Chan = 0, kF6Group = 1, kF6G1 = 2 };
+constexpr int kF6ScaleChunk = 32;   // groups per staged scale chunk (kF6G1)
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_f6(
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) __attribute__((amdgpu_waves_per_eu(MODE == 2 ? 2 : 1))) void k_gemm_f6(
     const uint8_t* __restrict__ X6, const float* __restrict__ s_x, const uint8_t* __restrict__ W6,
     const uint16_t* __restrict__ s_w, uint16_t* __restrict__ Y, int M, int N, int K,
     int group_size) {
@@ -118,11 +129,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_f6(
     static_assert(CHUNKS % (64 * NW) == 0, "whole wave loads");
     constexpr int LPW = CHUNKS / (64 * NW);
     static_assert(STAGES >= 3 && STAGES <= 4 && (STAGES - 2) * LPW < 64, "stages / vmcnt range");
+    constexpr bool G1 = MODE == kF6G1;
+    constexpr int CG = kF6ScaleChunk;
+    constexpr int SWB = BN * CG * 2;                   // bytes of a staged scale chunk
+    constexpr int SWL = SWB / 16 / (64 * NW);          // its copies per wave
+    static_assert(!G1 || (STAGES == 3 && (SWB / 16) % (64 * NW) == 0), "kF6G1: 3 stages, whole wave loads");
 
     __shared__ __align__(16) uint8_t st0[STAGE_BYTES];
     __shared__ __align__(16) uint8_t st1[STAGE_BYTES];
     __shared__ __align__(16) uint8_t st2[STAGE_BYTES];
     __shared__ __align__(16) uint8_t st3[STAGES > 3 ? STAGE_BYTES : 16];
+    // kF6G1: scales of the chunk in use, [column of the tile][32 groups] fp16
+    __shared__ __align__(16) uint8_t swl[G1 ? SWB : 16];
     auto stage_ptr = [&](auto S) __attribute__((always_inline)) -> uint8_t* {
         constexpr int I = decltype(S)::value;
         if constexpr (I == 0) return st0;
@@ -144,40 +162,70 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_f6(
     const int MF = (M + 31) / 32;                      // row fragments of X6
     const int NF = (N + 31) / 32;                      // row fragments of W6
 
-    // source of each of this lane's copies (K tile 0) and its K-tile stride
-    const uint8_t* src[LPW];
-    size_t step[LPW];
+    // this lane's copies: load i of a wave covers 64 consecutive 16-byte
+    // slots of the stage, all in A or all in B (a fragment pair is 192
+    // slots), so its base is wave-uniform (scalar registers) and only the
+    // byte offset inside the K tile's slab is per lane
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t soff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-        const int j = (i * NW + wave) * 64 + lane;    // 16-byte slot in the stage
+        const int j = (i * NW + wave_u) * 64 + lane;  // 16-byte slot in the stage
         const int f = j / (2 * kFrag / 16);            // fragment pair within the stage
         const int o = (j % (2 * kFrag / 16)) * 16;
-        if (f < AF) {
-            src[i] = X6 + static_cast<size_t>(min(m0 / 32 + f, MF - 1)) * (2 * kFrag) + o;
-            step[i] = static_cast<size_t>(MF) * (2 * kFrag);
-        } else {
-            src[i] = W6 + static_cast<size_t>(min(n0 / 32 + f - AF, NF - 1)) * (2 * kFrag) + o;
-            step[i] = static_cast<size_t>(NF) * (2 * kFrag);
-        }
+        const int r = ((i * NW + wave_u) * 64) / (2 * kFrag / 16) < AF ? min(m0 / 32 + f, MF - 1)
+                                                                       : min(n0 / 32 + f - AF, NF - 1);
+        soff[i] = static_cast<uint32_t>(r) * (2 * kFrag) + o;
     }
     auto issue = [&](int kt, auto S) __attribute__((always_inline)) {
-        const int kc = min(kt, KT - 1);
+        const size_t kc = static_cast<size_t>(min(kt, KT - 1));
+        const uint8_t* xb = X6 + kc * MF * (2 * kFrag);
+        const uint8_t* wb = W6 + kc * NF * (2 * kFrag);
         uint8_t* stage = stage_ptr(S);
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) dma16_async(src[i] + kc * step[i], stage + (i * NW + wave) * 1024);
+        for (int i = 0; i < LPW; ++i) {
+            const bool isA = ((i * NW + wave_u) * 64) / (2 * kFrag / 16) < AF;
+            dma16_async_sv(isA ? xb : wb, soff[i], stage + (i * NW + wave) * 1024);
+        }
     };
 
-    v16f acc[FM][FN];
-    float facc[MODE == kF6Group ? FM : 1][MODE == kF6Group ? FN : 1][16];
+    // kF6G1: copies of scale chunk c (groups 32 c .. 32 c + 31 of the tile's
+    // columns; 16 bytes = 8 groups of one column per lane).  Columns past N
+    // read the last column and groups past G the last 8 groups (in bounds,
+    // never used); the host guarantees G % 8 == 0 and 16-byte aligned s_w.
+    auto issue_scales = [&](int c) __attribute__((always_inline)) {
+        const int G = K / group_size;
+#pragma unroll
+        for (int i = 0; i < SWL; ++i) {
+            const int j = (i * NW + wave) * 64 + lane;
+            const int n = min(n0 + (j >> 2), N - 1);
+            int g = c * CG + 8 * (j & 3);
+            g = g < G ? g : G - 8;
+            dma16_async(s_w + static_cast<size_t>(n) * G + g, swl + (i * NW + wave) * 1024);
+        }
+    };
+
+    constexpr bool PF = MODE != kF6Chan;               // fp32 per-group sums
+    v16f acc[G1 ? 1 : FM][G1 ? 1 : FN];
+    float facc[PF ? FM : 1][PF ? FN : 1][16];
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
         for (int b = 0; b < FN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                acc[a][b][r] = 0.0f;
-                if constexpr (MODE == kF6Group) facc[a][b][r] = 0.0f;
+                if constexpr (!G1) acc[a][b][r] = 0.0f;
+                if constexpr (PF) facc[a][b][r] = 0.0f;
             }
+    // a zero accumulator operand the compiler cannot fold into an inline
+    // constant (an MFMA with an inline-zero accumulator gave wrong sums)
+    v16f zc;
+    if constexpr (G1) {
+        float z0;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zc[r] = z0;
+    }
 
     const int col = lane & 31;
     int bcol[FN];
@@ -192,7 +240,52 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_f6(
                    static_cast<int>(d1.y), static_cast<int>(d2.x), static_cast<int>(d2.y), 0, 0};
     };
 
+    // kF6G1 tile: the two 64-code halves of every fragment from a zero
+    // operand, then (after the tile's wait and barrier, when its scale chunk
+    // has landed) one FMA per element with the group's scale
+    auto body_g1 = [&](int kt, auto S) __attribute__((always_inline)) {
+        constexpr int SI = decltype(S)::value;
+        if (kt > 0 && kt % CG == 0) {
+            // every wave has folded the previous chunk's last tile
+            lds_barrier();
+            issue_scales(kt / CG);
+        }
+        issue(kt + STAGES - 1, std::integral_constant<int, (SI + STAGES - 1) % STAGES>{});
+        const uint8_t* stage = stage_ptr(S);
+        v16f t[FM][FN];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            v8i av[FM], bv[FN];
+#pragma unroll
+            for (int a = 0; a < FM; ++a) av[a] = read_op(stage + (wm0 / 32 + a) * (2 * kFrag) + kk * kFrag);
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                bv[b] = read_op(stage + (AF + wn0 / 32 + b) * (2 * kFrag) + kk * kFrag);
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+                for (int b = 0; b < FN; ++b)
+                    t[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        av[a], bv[b], kk == 0 ? zc : t[a][b], kFmtE2M3, kFmtE2M3, 0, kScaleOne, 0, kScaleOne);
+        }
+        wait_vmcnt<(STAGES - 2) * LPW>();
+        lds_barrier();
+        const int gl = kt % CG;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const float sw = h2f(*reinterpret_cast<const uint16_t*>(swl + (wn0 + 32 * b + col) * (2 * CG) + 2 * gl));
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) facc[a][b][r] = fmaf(t[a][b][r], sw, facc[a][b][r]);
+        }
+    };
+
     auto body = [&](int kt, auto S) __attribute__((always_inline)) {
+        if constexpr (G1) {
+            body_g1(kt, S);
+            return;
+        }
         constexpr int SI = decltype(S)::value;
         issue(kt + STAGES - 1, std::integral_constant<int, (SI + STAGES - 1) % STAGES>{});
         const uint8_t* stage = stage_ptr(S);
@@ -233,6 +326,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_f6(
         lds_barrier();
     };
 
+    if constexpr (G1) issue_scales(0);
     static_for<0, STAGES - 1>([&](auto I) { issue(decltype(I)::value, I); });
     wait_vmcnt<(STAGES - 2) * LPW>();
     lds_barrier();
@@ -256,7 +350,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_f6(
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm0 + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (gm >= M) continue;
-                const float v = MODE == kF6Chan ? acc[a][b][r] : facc[a][b][r];
+                float v;
+                if constexpr (PF)
+                    v = facc[a][b][r];
+                else
+                    v = acc[a][b][r];
                 Y[static_cast<size_t>(gm) * N + gn] = f2h(v * sw4 * s_x[gm]);
             }
     }
@@ -275,29 +373,46 @@ using F6Fn = hipError_t (*)(const F6Args&, hipStream_t);
 struct F6Cfg {
     const char* name;
     F6Fn chan, group;       // group: nullptr where the per-group accumulators do not fit
+    F6Fn g1;                // groups of one K tile with staged scales, or nullptr
 };
 
 #define W4A4_F6(NAME, BM, BN, WM_, WN_, ST)                                                      \
-    F6Cfg{NAME, &launch_f6<BM, BN, WM_, WN_, ST, kF6Chan>, &launch_f6<BM, BN, WM_, WN_, ST, kF6Group>}
+    F6Cfg{NAME, &launch_f6<BM, BN, WM_, WN_, ST, kF6Chan>, &launch_f6<BM, BN, WM_, WN_, ST, kF6Group>, \
+          nullptr}
+#define W4A4_F6_G1(NAME, BM, BN, WM_, WN_, ST)                                                   \
+    F6Cfg{NAME, &launch_f6<BM, BN, WM_, WN_, ST, kF6Chan>, &launch_f6<BM, BN, WM_, WN_, ST, kF6Group>, \
+          &launch_f6<BM, BN, WM_, WN_, ST, kF6G1>}
 #define W4A4_F6_CHAN(NAME, BM, BN, WM_, WN_, ST)                                                 \
-    F6Cfg{NAME, &launch_f6<BM, BN, WM_, WN_, ST, kF6Chan>, nullptr}
+    F6Cfg{NAME, &launch_f6<BM, BN, WM_, WN_, ST, kF6Chan>, nullptr, nullptr}
 const F6Cfg kF6Tiles[] = {
     W4A4_F6_CHAN("k_gemm_f6<256x256, waves 2x4, 3 stages>", 256, 256, 2, 4, 3),
     W4A4_F6_CHAN("k_gemm_f6<128x384, waves 4x4, 3 stages>", 128, 384, 4, 4, 3),
     W4A4_F6("k_gemm_f6<256x128, waves 2x2, 3 stages>", 256, 128, 2, 2, 3),
     W4A4_F6("k_gemm_f6<128x128, waves 2x2, 4 stages>", 128, 128, 2, 2, 4),
     W4A4_F6_CHAN("k_gemm_f6<256x256, waves 4x4, 3 stages>", 256, 256, 4, 4, 3),
+    W4A4_F6_G1("k_gemm_f6<128x128, waves 2x2, 3 stages>", 128, 128, 2, 2, 3),
 };
 #undef W4A4_F6
+#undef W4A4_F6_G1
 #undef W4A4_F6_CHAN
 constexpr int kNumF6 = sizeof(kF6Tiles) / sizeof(kF6Tiles[0]);
 
+// groups of one K tile whose scales can be staged by 16-byte copies
+bool f6_g1_ok(const F6Args& a) {
+    const int G = a.K / a.group_size;
+    return G > 1 && a.group_size == kTileK && G % 8 == 0 &&
+           (reinterpret_cast<uintptr_t>(a.s_w) & 15) == 0;
+}
+
 const F6Cfg& choose_f6(const F6Args& a) {
     const bool grouped = a.K / a.group_size > 1;
+    const bool g1 = f6_g1_ok(a);
     const char* e = getenv("W4A4_GEMM_F6_TILE");
     if (e != nullptr && *e != '\0') {
         const int v = atoi(e);
-        if (v >= 0 && v < kNumF6 && (!grouped || kF6Tiles[v].group != nullptr)) return kF6Tiles[v];
+        if (v >= 0 && v < kNumF6 &&
+            (!grouped || kF6Tiles[v].group != nullptr || (g1 && kF6Tiles[v].g1 != nullptr)))
+            return kF6Tiles[v];
     }
     const int cus = device_cu_count();
     const long t256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
@@ -305,7 +420,9 @@ const F6Cfg& choose_f6(const F6Args& a) {
     const long t256x128 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 128);
     // measured on MI355X: 256x256 tiles (8 waves) when the grid covers the
     // CUs twice, 128x384 (16 waves) for about one wave of tiles; per-group
-    // weights need a second accumulator set, which fits the 4-wave tiles only
+    // weights need a second accumulator set, which fits the 4-wave tiles
+    // only, and groups of one K tile take the staged-scale mode
+    if (g1) return kF6Tiles[5];
     if (grouped) return t256x128 >= cus ? kF6Tiles[2] : kF6Tiles[3];
     if (t256 >= 2L * cus) return kF6Tiles[0];
     if (t384 >= cus) return kF6Tiles[1];
@@ -331,7 +448,9 @@ const char* gemm_f6_kernel_name(const F6Args& a) { return choose_f6(a).name; }
 hipError_t gemm_f6_launch(const F6Args& a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
     const F6Cfg& c = choose_f6(a);
-    return (a.K / a.group_size > 1) ? c.group(a, stream) : c.chan(a, stream);
+    if (a.K / a.group_size == 1) return c.chan(a, stream);
+    if (c.g1 != nullptr && f6_g1_ok(a)) return c.g1(a, stream);
+    return c.group(a, stream);
 }
 
 }  // namespace w4a4

@@ -665,15 +665,13 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
     __syncthreads();
 
     uint8_t* qb = qbuf[wave];
-    for (; m < M; m += stride) {
+    // one token: xa holds its X̄ fragments
+    auto token = [&](int m) __attribute__((always_inline)) {
         // an offset the compiler cannot see through: the fragment reads stay
         // LDS reads in the loop instead of 128 loop-invariant registers, which
         // lets two waves share a SIMD
         int fo = 0;
         asm volatile("" : "+s"(fo));
-        // next token in flight (clamped, unconditional: a branch here would
-        // make the compiler wait for these loads before stage 1)
-        load_x(m + stride, xn);
 
         // stage 1: T = X̄ · P2'
         v4f T[C::RB][C::CB];
@@ -806,11 +804,19 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
             for (int c = lane; c < C::QB / 16; c += 64) dst[c] = reinterpret_cast<const uint4*>(qb)[c];
             if (lane == 0) s_x[m] = s;
         }
+    };
+    // every token but the wave's last has the next one in flight (an
+    // unconditional load inside the token loop: a branch there would make the
+    // compiler wait for it before stage 1); the last token loads nothing more
+    for (; m + stride < M; m += stride) {
+        load_x(m + stride, xn);
+        token(m);
 #pragma unroll
         for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
             for (int ks = 0; ks < C::KS1; ++ks) xa[rb][ks] = xn[rb][ks];
     }
+    if (m < M) token(m);
 }
 
 template <int N1, int N2, bool PC>
