@@ -234,7 +234,15 @@ __device__ __forceinline__ void dma16_async(const void* src, const uint8_t* lds_
 __device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, const uint8_t* lds_wave_base) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (const __attribute__((address_space(3))) uint8_t*)lds_wave_base)));
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(m0)
+    // the base is wave-uniform by contract; readfirstlane puts it in scalar
+    // registers where the compiler cannot prove it.  The builtin returns a
+    // signed int: each half goes through uint32_t before widening, so the
+    // low half is zero-extended
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(bs), "s"(m0)
                  : "memory", "m0");
 }
 

@@ -365,26 +365,43 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const int G = K / group_size;
     const int TPG = group_size / BK;
 
-    // this lane's source row (clamped) and chunk for each of its loads
-    const uint8_t* src[LPW];
+    // this lane's source row (clamped) and chunk for each of its loads.
+    // Symmetric weights: load i of a wave covers 64 consecutive slots, all in
+    // A or all in B, so the copies take a wave-uniform base (the tile's first
+    // row, scalar registers) and a 32-bit lane offset, issued from inline
+    // assembly.  Asymmetric weights keep the builtin copies: their zero points
+    // are loaded inside the K loop, and the compiler's waits for those loads
+    // must count the copies.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint8_t* src[ASYM ? LPW : 1];
+    uint32_t soff[ASYM ? 1 : LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-        const int j = (i * NW + wave) * 64 + lane;     // 16-byte slot in the stage
-        const bool isA = j < BM * 4;
+        const int j = (i * NW + wave_u) * 64 + lane;   // 16-byte slot in the stage
+        const bool isA = (i * NW + wave_u) * 64 < BM * 4;
         const int jj = isA ? j : j - BM * 4;
         const int row = jj >> 2;
         const int c = (jj & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
-        if (isA)
-            src[i] = Xq + static_cast<size_t>(min(m0 + row, M - 1)) * KB + c * 16;
+        const int r = isA ? min(m0 + row, M - 1) : min(n0 + row, N - 1);
+        if constexpr (ASYM)
+            src[i] = (isA ? Xq : Wq) + static_cast<size_t>(r) * KB + c * 16;
         else
-            src[i] = Wq + static_cast<size_t>(min(n0 + row, N - 1)) * KB + c * 16;
+            soff[i] = static_cast<uint32_t>(r - (isA ? m0 : n0)) * KB + c * 16;
     }
     auto issue = [&](int kt, auto S) {
         const int kc = min(kt, KT - 1);
         uint8_t* stage = stage_ptr(S);
+        if constexpr (ASYM) {
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-            dma16(src[i] + kc * 64, stage + (i * NW + wave) * 1024);
+            for (int i = 0; i < LPW; ++i) dma16(src[i] + kc * 64, stage + (i * NW + wave) * 1024);
+        } else {
+            const uint8_t* xb = Xq + static_cast<size_t>(m0) * KB + kc * 64;
+            const uint8_t* wb = Wq + static_cast<size_t>(n0) * KB + kc * 64;
+#pragma unroll
+            for (int i = 0; i < LPW; ++i)
+                dma16_async_sv((i * NW + wave_u) * 64 < BM * 4 ? xb : wb, soff[i],
+                               stage + (i * NW + wave) * 1024);
+        }
     };
 
     v16i acc[FM][FN];
