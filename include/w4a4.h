@@ -80,6 +80,27 @@ const char* w4a4_status_str(int status);
 /* Message of the last failing call made by this host thread ("" if none). */
 const char* w4a4_last_error(void);
 
+/* Kernel selection override, for tests and tuning sweeps only (normal use
+ * never needs it).  `which` names a dispatcher:
+ *   W4A4_OVERRIDE_PREFILL_TILE  prefill GEMM configurations (M > 64);
+ *   W4A4_OVERRIDE_DECODE        decode GEMM variants (M <= 64);
+ *   W4A4_OVERRIDE_F6_TILE       configurations of the fp6-pipe product.
+ * index in [0, w4a4_kernel_config_count(which)) forces that configuration for
+ * every later call in this process; -1 restores the automatic choice.  An
+ * index past the table, or a configuration without the call's weight mode,
+ * also leaves the choice automatic.  Process-wide and atomic, but a call
+ * running on another thread may see the old or the new value.  Returns the
+ * previous index (>= -1), or W4A4_ERR_INVALID_ARG for an unknown `which` or
+ * an index below -1. */
+#define W4A4_OVERRIDE_PREFILL_TILE 0
+#define W4A4_OVERRIDE_DECODE 1
+#define W4A4_OVERRIDE_F6_TILE 2
+int w4a4_set_kernel_override(int32_t which, int32_t index);
+
+/* Number of configurations behind `which` (as above), or
+ * W4A4_ERR_INVALID_ARG. */
+int w4a4_kernel_config_count(int32_t which);
+
 /* ------------------------------------------------------------------------ */
 /* Offline weight preparation                                               */
 /* ------------------------------------------------------------------------ */
@@ -308,6 +329,14 @@ int w4a4_ternary_weight_bytes(int32_t N, int32_t K, size_t* tq_bytes, size_t* am
  * 128. */
 int w4a4_pack_ternary(const float* Wt, int32_t N, int32_t K, int32_t iters, uint8_t* Tq,
                       uint32_t* am, void* stream);
+
+/* The inverse of the tiled layout above (a bijection on the N real rows):
+ * T int8 [N][K] gets the codes t in {-1, 0, 1}, row-major; alpha and mu fp16
+ * [N][K/128] get the parameter halves of each block's word.  For reading
+ * packed weights back (tests, inspection); one launch, no workspace.  All
+ * pointers device memory, 16-byte aligned. */
+int w4a4_unpack_ternary(const uint8_t* Tq, const uint32_t* am, int32_t N, int32_t K, int8_t* T,
+                        uint16_t* alpha, uint16_t* mu, void* stream);
 
 /* Bytes of workspace w4a4_ternary_gemm needs: 0 when the shape's output
  * tiles fill the GPU by themselves (ws may then be NULL), else the fp32

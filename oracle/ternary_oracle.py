@@ -32,22 +32,12 @@ Readings where the page is silent (restated with the design notes):
   reordering is a column permutation, which leaves X W^T unchanged (pinned for
   the 4-bit layer).
 
-Storage (this library's layout contract, not the page's): two bits per code,
-c = t + 1 in {0, 1, 2}, sixteen codes per little-endian 32-bit word, code
-16 w + 2 s at bits 2 s of word w and code 16 w + 2 s + 1 at bits 16 + 2 s
-(s = 0 .. 7): the even codes in the low half, the odd codes in the high half.
-The 32 codes that lane group q = 0..3 takes from block g in the product,
-codes 128 g + 32 s + 8 q + j for step s = 0..3 and j = 0..7, in the order
-(s, j), form an 8-byte piece (two words).  Rows are stored in tiles of 16
-(N rounded up to a multiple of 16; rows past N are zero bytes with zero
-parameters), tile t taking 16 * K / 4 bytes from byte 4 K t.  Within a
-tile, the pair of blocks (2 p, 2 p + 1) occupies 1024 bytes from 1024 p:
-the 16 bytes at (16 q + r) * 16 hold row r's pieces of block 2 p (first 8
-bytes) and block 2 p + 1 (last 8), so that one 16-byte load per lane of a
-64-lane wave reads a whole pair for 16 rows; an unpaired last block (odd
-K / 128) has row r's piece q at 1024 p + (16 q + r) * 8.  The per-block
-parameters are one 32-bit word per (row, block), alpha's fp16 bits in the
-low half and mu's in the high half, at word (t * K / 128 + g) * 16 + r.
+Storage is the library's business, not the page's.  The oracle's plain form
+is the codes T themselves, and, for a hand-checked encoding of the 2-bit
+codes, `pack_words`: c = t + 1 in {0, 1, 2}, sixteen consecutive codes of a
+row per little-endian 32-bit word, code 16 w + 2 s at bits 2 s of word w and
+code 16 w + 2 s + 1 at bits 16 + 2 s (s = 0 .. 7).  The library's tiled
+layout is checked through its own unpack entry point against T, alpha, mu.
 """
 from __future__ import annotations
 
@@ -55,9 +45,8 @@ import numpy as np
 
 from .w4a4_oracle import fp16_rne
 
-__all__ = ["TERN_BLOCK", "itf_ternarize", "pack_words", "tiled_rows", "piece_offsets", "piece_words", "tile_offsets",
-           "pack_ternary",
-           "unpack_ternary", "pack_params", "dequant_ternary", "ternary_linear", "itf_objective"]
+__all__ = ["TERN_BLOCK", "itf_ternarize", "pack_words", "dequant_ternary", "ternary_linear",
+           "itf_objective"]
 
 TERN_BLOCK = 128
 
@@ -133,86 +122,6 @@ def pack_words(T):
         word |= cw[..., 2 * s_] << (2 * s_)
         word |= cw[..., 2 * s_ + 1] << (16 + 2 * s_)
     return word.astype(np.uint32)
-
-
-def tiled_rows(N):
-    """Rows in storage: N rounded up to a multiple of 16."""
-    return (N + 15) // 16 * 16
-
-
-def piece_offsets(G):
-    """[G, 4, 16]: the byte offset, from the start of a 16-row tile, of the
-    8-byte piece of block g, lane group q, row r."""
-    off = np.empty((G, 4, 16), dtype=np.int64)
-    for g in range(G):
-        p, j = divmod(g, 2)
-        for q in range(4):
-            for r in range(16):
-                if 2 * p + 1 < G:
-                    off[g, q, r] = 1024 * p + (16 * q + r) * 16 + 8 * j
-                else:
-                    off[g, q, r] = 1024 * p + (16 * q + r) * 8
-    return off
-
-
-def piece_words(T, block):
-    """codes [N, K] -> words [N, G, 4, 2] (row, block, lane group, word)."""
-    N, K = T.shape
-    G = K // block
-    # [n, g, s, q, j] -> [n, g, q, s, j]: each lane group's 32 codes in (s, j) order
-    Tq = np.moveaxis(T.reshape(N, G, 4, 4, 8), 3, 2).reshape(N, G, 4, 32)
-    return pack_words(Tq).reshape(N, G, 4, 2)
-
-
-def tile_offsets(N, G):
-    """[N, G, 4]: byte offset of every (row, block, lane group) piece."""
-    n = np.arange(N)
-    t, r = np.divmod(n, 16)
-    off = piece_offsets(G)                       # [G, 4, 16]
-    return (4 * 128 * G) * t[:, None, None] + np.moveaxis(off[:, :, r], 2, 0)
-
-
-def pack_ternary(T, block: int = TERN_BLOCK):
-    """codes [N, K] in {-1, 0, 1} (K a multiple of 128) -> bytes
-    [tiled_rows(N) * K / 4] in the tiled layout."""
-    T = np.asarray(T)
-    N, K = T.shape
-    if K % block:
-        raise ValueError("K must be a multiple of the block size")
-    G = K // block
-    words = piece_words(T, block)                    # [N, G, 4, 2]
-    out = np.zeros(tiled_rows(N) * K // 16, dtype=np.uint32)
-    w = tile_offsets(N, G) // 4                 # word index of each piece
-    out[w] = words[..., 0]
-    out[w + 1] = words[..., 1]
-    return out.astype("<u4").view(np.uint8)
-
-
-def unpack_ternary(b, N, K, block: int = TERN_BLOCK):
-    """bytes of the tiled layout -> codes [N, K]."""
-    b32 = np.ascontiguousarray(np.asarray(b, dtype=np.uint8)).view("<u4").astype(np.int64)
-    G = K // block
-    w = tile_offsets(N, G) // 4
-    words = np.stack([b32[w], b32[w + 1]], axis=-1)                # [n, g, q, word]
-    out = np.empty(words.shape + (16,), dtype=np.int64)            # [n, g, q, word, i]
-    for s_ in range(8):
-        out[..., 2 * s_] = ((words >> (2 * s_)) & 3) - 1
-        out[..., 2 * s_ + 1] = ((words >> (16 + 2 * s_)) & 3) - 1
-    out = out.reshape(N, G, 4, 4, 8)                                # [n, g, q, s, j]
-    return np.moveaxis(out, 2, 3).reshape(N, K).astype(np.int8)
-
-
-def pack_params(alpha, mu):
-    """fp16 alpha, mu [N, G] -> uint32 words [tiled_rows(N) * G] in the tiled
-    order (t * G + g) * 16 + r: alpha's bits low, mu's bits high; zero for
-    rows past N."""
-    a = np.asarray(alpha, dtype=np.float16).view(np.uint16).astype(np.uint32)
-    u = np.asarray(mu, dtype=np.float16).view(np.uint16).astype(np.uint32)
-    N, G = a.shape
-    NP = tiled_rows(N)
-    w = np.zeros((NP, G), dtype=np.uint32)
-    w[:N] = a | (u << 16)
-    return np.ascontiguousarray(w.reshape(NP // 16, 16, G).transpose(0, 2, 1)).reshape(-1)
 
 
 def dequant_ternary(tq):

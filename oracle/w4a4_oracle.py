@@ -50,7 +50,7 @@ __all__ = [
     "kron_factors", "kron_transform", "act_scale", "quantize_act",
     "transform_quant", "pack_nibbles", "unpack_nibbles", "merge_weights",
     "fp16_rne", "quantize_weights", "int_gemm", "int_gemm_loop",
-    "epilogue", "linear", "dequant_act", "dequant_weights",
+    "epilogue", "epilogue_by_group", "linear", "dequant_act", "dequant_weights",
     "quantize_act_static", "transform_quant_static", "migrate_steps", "linear_static",
     "calibrate_steps", "code_range",
 ]
@@ -326,6 +326,43 @@ def epilogue(D, s_x, s_w):
     sw = np.asarray(s_w, dtype=np.float64)
     acc = np.einsum("mng,ng->mn", D, sw)
     return np.asarray(s_x, dtype=np.float64)[:, None] * acc
+
+
+def epilogue_by_group(qx, wq, s_x, cols=None, chunk: int = 1024):
+    """(Y64, A) for whole-size outputs without holding D[M, N, G].
+
+    Y64[m,n] = s_x[m] · Σ_g s_w[n,g] · D[m,n,g] -- the quantity of
+    epilogue(int_gemm(...)) -- and A[m,n] = s_x[m] · Σ_g s_w[n,g] · |D[m,n,g]|,
+    the magnitude of the summed terms.  D[:, :, g] is the integer product of
+    group g (FlatQuant page, "核心思想"), each entry an integer of magnitude
+    <= group·8·15, formed exactly by a float64 product of integer-valued
+    arrays; the groups are then added in order, `chunk` output channels at a
+    time (the summation order is free: the per-token scale commutes with the
+    bias-free product, FPTQuant page "3. 伪动态残差缩放").  ``cols`` selects
+    output channels of ``wq``.
+    """
+    qx = np.asarray(qx)
+    M, K = qx.shape
+    g = wq["group_size"]
+    G = K // g
+    idx = np.arange(wq["codes"].shape[0]) if cols is None else np.asarray(cols)
+    x = qx.astype(np.float64).reshape(M, G, g)
+    sx = np.asarray(s_x, dtype=np.float64)[:, None]
+    Y = np.empty((M, len(idx)))
+    A = np.empty((M, len(idx)))
+    for c0 in range(0, len(idx), chunk):
+        cc = idx[c0:c0 + chunk]
+        w = _centered(wq["codes"][cc], wq["z"][cc], g).astype(np.float64)   # [n, G, g]
+        sw = np.asarray(wq["s"][cc], dtype=np.float64)                      # [n, G]
+        y = np.zeros((M, len(cc)))
+        a = np.zeros((M, len(cc)))
+        for j in range(G):
+            Dg = x[:, j, :] @ w[:, j, :].T
+            y += Dg * sw[:, j]
+            a += np.abs(Dg) * sw[:, j]
+        Y[:, c0:c0 + len(cc)] = sx * y
+        A[:, c0:c0 + len(cc)] = sx * a
+    return Y, A
 
 
 def dequant_act(q, s_x):

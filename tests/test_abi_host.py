@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert W.version() == 0x000100
+    assert W.version() == 0x000200
     L = W.lib()
     assert L.w4a4_status_str(0) == b"W4A4_OK"
     assert L.w4a4_status_str(-3) == b"W4A4_ERR_ALIGNMENT"
@@ -145,6 +145,32 @@ def test_gemm_kernel_name_query():
     assert W.gemm_kernel_name(2048, W.WeightDesc(28672, 4096, 128, 1)).startswith("k_gemm")
     with pytest.raises(W.W4A4Error):
         W.gemm_kernel_name(16, W.WeightDesc(256, 200, 200, 0))
+
+
+def test_kernel_override_is_a_host_setting():
+    """The selection override changes which configuration a query reports,
+    restores the automatic choice with -1, and rejects unknown kinds."""
+    d = W.WeightDesc(28672, 4096, 128, 1)
+    auto = W.gemm_kernel_name(2048, d)
+    n = W.kernel_config_count(W.OVERRIDE_PREFILL_TILE)
+    names = set()
+    for t in range(n):
+        assert W.set_kernel_override(W.OVERRIDE_PREFILL_TILE, t) == (t - 1 if t else -1)
+        names.add(W.gemm_kernel_name(2048, W.WeightDesc(6144, 4096, 4096, 0)))
+    assert len(names) == n                      # every per-channel config is distinct
+    assert W.set_kernel_override(W.OVERRIDE_PREFILL_TILE, -1) == n - 1
+    assert W.gemm_kernel_name(2048, d) == auto
+    assert W.set_kernel_override(W.OVERRIDE_DECODE, 2) == -1
+    v2 = W.gemm_kernel_name(8, d)
+    W.set_kernel_override(W.OVERRIDE_DECODE, 3)
+    assert W.gemm_kernel_name(8, d) != v2
+    W.set_kernel_override(W.OVERRIDE_DECODE, -1)
+    assert W.kernel_config_count(W.OVERRIDE_DECODE) == 4
+    assert W.kernel_config_count(W.OVERRIDE_F6_TILE) >= 1
+    L = W.lib()
+    assert L.w4a4_set_kernel_override(3, 0) == -1 and "kind" in last()
+    assert L.w4a4_set_kernel_override(0, -2) == -1
+    assert L.w4a4_kernel_config_count(-1) == -1
 
 
 def test_static_entry_points_validation():

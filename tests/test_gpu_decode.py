@@ -6,8 +6,9 @@ launch (FlatQuant page, section 高效 Kernel 设计; MergeQuant page, section
 问题定义).  Checks, per case:
   * the packed activation codes the kernel leaves in its workspace equal the
     oracle's up to the 1e-4 tie window, and its token scales match;
-  * the fp16 output meets the whole-layer bound against the oracle (rows with
-    equal codes per element, rows with tie flips per flip);
+  * the fp16 output meets the per-element bound and relative L2 <= 1e-3
+    against the oracle's product and epilogue on the kernel's own codes and
+    token scales;
   * for n1 = 224 in per-channel weight mode the output equals the two-launch
     path's bit for bit (same column-block transform arithmetic, exact int32
     sums); elsewhere the two differ only by fp32 summation order and ties;
@@ -21,7 +22,7 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from gpu_common import assert_codes_match, assert_linear_close, custom_workload, log, rel_l2, \
+from gpu_common import assert_codes_match, assert_layer_close, custom_workload, log, rel_l2, \
     to_dev, torch_dev
 
 pytestmark = pytest.mark.gpu
@@ -77,10 +78,8 @@ def run_case(wl, mode, sync, alpha=1.0, seed_cal=7919):
     q = O.unpack_nibbles(Xq, True)
     n = assert_codes_match(q, ref["act"]["q"], ref["act"]["t"])
     np.testing.assert_allclose(sx.astype(np.float64), ref["act"]["s_x"], rtol=2e-6)
-    flips = (q != ref["act"]["q"]).sum(axis=1)
-    A = O.epilogue(np.abs(ref["D"]), ref["act"]["s_x"], wq["s"])
     Yh = Y.cpu().numpy()
-    assert_linear_close(Yh.astype(np.float64), ref["Y64"], A, flips)
+    assert_layer_close(Yh, q, sx, wq)
     # the two-launch path on the same inputs
     if mode == "dynamic":
         Y2 = L.linear(Xd, P1d, P2d, desc, Wq, sw, zw, alpha_a=alpha).cpu().numpy()

@@ -15,7 +15,8 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from gpu_common import (assert_linear_close, assert_y_close, custom_workload, log, prepared,
+from gpu_common import (assert_codes_match, assert_layer_close, assert_y_close, custom_workload,
+                        kernel_override, log, prepared,
                         rel_l2, sample_rows, to_dev, torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -101,12 +102,11 @@ def _codes(M, N, K, g, asym, seed):
                                           (260, 264, 2048, 256, False), (1, 33, 128, 128, True),
                                           (31, 1, 256, 256, False), (130, 200, 5120, 128, True),
                                           (64, 96, 1536, 128, False), (129, 136, 12288, 128, True)])
-def test_gemm_f6_every_tile(tile, M, N, K, g, asym, monkeypatch):
-    """Every fp6 tile configuration (forced through W4A4_GEMM_F6_TILE; the
+def test_gemm_f6_every_tile(tile, M, N, K, g, asym):
+    """Every fp6 tile configuration (forced through w4a4_set_kernel_override; the
     per-channel-only ones fall back to the default for per-group weights)
     against the oracle's exact integer product, extreme codes included."""
     log(f"gemm_f6 tile {tile}: M={M} N={N} K={K} g={g} asym={asym}")
-    monkeypatch.setenv("W4A4_GEMM_F6_TILE", str(tile))
     qx, wc, z = _codes(M, N, K, g, asym, seed=tile + 200)
     qx[0, :] = -8                                   # the extreme products
     wc[0, :] = 0 if asym else -8
@@ -118,8 +118,13 @@ def test_gemm_f6_every_tile(tile, M, N, K, g, asym, monkeypatch):
     D_or = O.int_gemm(qx, wc, z, g)
     desc = W().WeightDesc(N, K, g, int(asym))
     W6 = W().pack_weights_f6(desc, to_dev(O.pack_nibbles(wc)), to_dev(z) if asym else None)
-    Y = W().gemm_f6(to_dev(O.pack_nibbles(qx)), to_dev(sx), desc, W6, to_dev(sw)).cpu().numpy()
+    with kernel_override(W().OVERRIDE_F6_TILE, tile):
+        Y = W().gemm_f6(to_dev(O.pack_nibbles(qx)), to_dev(sx), desc, W6, to_dev(sw)).cpu().numpy()
     assert_y_close(Y, O.epilogue(D_or, sx, sw), O.epilogue(np.abs(D_or), sx, sw))
+
+
+def test_f6_config_count():
+    assert W().kernel_config_count(W().OVERRIDE_F6_TILE) == NUM_F6_TILES
 
 
 def test_gemm_f6_group_scale_table_offsets():
@@ -161,11 +166,12 @@ def _layer_parity_f6(inp, c=None, alpha=1.0):
     cd = None if c is None else to_dev(c)
     Y = W().linear_f6(to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"]), desc, W6, sw,
                       c=cd, alpha_a=alpha).cpu().numpy()
-    Xq, _ = W().transform_quant(to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"]), cd, alpha)
-    flips = (O.unpack_nibbles(Xq.cpu().numpy(), True) != ref["act"]["q"]).sum(axis=1)
-    A = O.epilogue(np.abs(ref["D"]), ref["act"]["s_x"], wq["s"])
-    assert_linear_close(Y.astype(np.float64), ref["Y64"], A, flips, what="linear_f6")
-    log(f"  linear_f6 relative L2 {rel_l2(Y, ref['Y64']):.2e}")
+    Xq, sx = W().transform_quant(to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"]), cd, alpha)
+    gq = O.unpack_nibbles(Xq.cpu().numpy(), True)
+    assert_codes_match(gq, ref["act"]["q"], ref["act"]["t"])
+    rel = assert_layer_close(Y, gq, sx.cpu().numpy(), wq, what="linear_f6")
+    log(f"  linear_f6 relative L2 {rel:.2e} on the library's codes, "
+        f"{rel_l2(Y, ref['Y64']):.2e} against the oracle's own codes")
 
 
 @pytest.mark.parametrize("wl", [
@@ -203,16 +209,15 @@ def test_full_size_f6(name):
     W6 = W().pack_weights_f6(desc, Wq, zw)
     X_d, P1_d, P2_d = to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"])
     Y = W().linear_f6(X_d, P1_d, P2_d, desc, W6, sw)
-    Xq, _ = W().transform_quant(X_d, P1_d, P2_d)
+    Xq, sx = W().transform_quant(X_d, P1_d, P2_d)
     torch.cuda.synchronize()
     act = O.transform_quant(inp["X"], inp["P1"], inp["P2"])
+    gq_all = O.unpack_nibbles(Xq.cpu().numpy(), True)
+    n = assert_codes_match(gq_all, act["q"], act["t"], what=f"{name} activation codes")
     wq_s = O.quantize_weights(inp["W"][cols], wl.group_size, wl.asymmetric)
-    D_or = O.int_gemm(act["q"][rows], wq_s["codes"], wq_s["z"], wl.group_size)
-    ref = O.epilogue(D_or, act["s_x"][rows], wq_s["s"])
-    A_ref = O.epilogue(np.abs(D_or), act["s_x"][rows], wq_s["s"])
-    gq = O.unpack_nibbles(Xq.index_select(0, torch.as_tensor(rows, device=dev)).cpu().numpy(), True)
-    flips = (gq != act["q"][rows]).sum(axis=1)
     Ys = Y.index_select(0, torch.as_tensor(rows, device=dev)).index_select(
         1, torch.as_tensor(cols, device=dev)).cpu().numpy()
-    nflip, worst = assert_linear_close(Ys, ref, A_ref, flips, what=f"{name} linear_f6")
-    log(f"[{name}] linear_f6 relative L2 on samples {rel_l2(Ys, ref):.2e}; tie-flip rows {nflip}")
+    rel = assert_layer_close(Ys, gq_all[rows], sx.cpu().numpy()[rows], wq_s,
+                             what=f"{name} linear_f6")
+    log(f"[{name}] linear_f6 relative L2 on samples {rel:.2e} on the library's codes "
+        f"({n} tie cells over all tokens)")

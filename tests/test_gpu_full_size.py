@@ -1,24 +1,28 @@
 """Full-size LLaMA-shaped workloads, in the launch configuration the benchmark
-times (w4a4_linear on the whole M x K input), checked on sampled outputs.
+times (w4a4_linear on the whole M x K input).
 
 To keep host time bounded, the raw N(0, 0.02) weight draws serve directly as
 the merged matrix W̃ here (the merge itself is checked at smaller sizes in
 test_gpu_parity.py); every other input is the workload's own.  Per workload:
-  * weight codes / scales / zero points of sampled output channels: bit-exact;
-  * activation codes of sampled tokens: bit-exact up to the tie window;
-  * int32 accumulators of sampled tokens, all channels and groups: bit-exact
-    (sampled channels compared with the oracle);
-  * fp16 GEMM output given the oracle's codes: per-element bound on samples;
-  * whole layer on sampled tokens x channels: tokens whose codes equal the
-    oracle's within the per-element bound, tokens with tie flips within a
-    per-flip relative L2 bound.
+  * weight codes / scales / zero points: bit-exact (every output channel of
+    the 8B shapes, sampled channels of the 70B ones);
+  * activation codes of every token: bit-exact up to the tie window, and
+    every token scale;
+  * int32 accumulators of sampled tokens against the oracle's codes,
+    bit-exact over all groups (every channel of the 8B shapes);
+  * fp16 GEMM output given the oracle's codes on sampled tokens: per-element
+    bound and relative L2;
+  * the whole layer against the oracle's product and epilogue on the
+    library's own codes and token scales: the full [M, N] output of the 8B
+    shapes, sampled tokens x channels of the 70B ones; per-element bound
+    and relative L2 <= 1e-3 over everything compared.
 """
 import numpy as np
 import pytest
 
 import oracle as O
 import workloads as WL
-from gpu_common import (assert_codes_match, assert_linear_close, assert_y_close, log, rel_l2,
+from gpu_common import (assert_codes_match, assert_layer_close, assert_y_close, log, rel_l2,
                         sample_rows, to_dev, torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +37,9 @@ def take(t, rows=None, cols=None):
         t = t.index_select(1, torch.as_tensor(cols, device=t.device))
     return t.cpu().numpy()
 
+
 NAMES = ["qkv8b", "gateup8b", "down8b", "gateup70b", "down70b_m1", "down70b_m8", "down70b_m64"]
+FULL_OUTPUT = {"qkv8b", "gateup8b", "down8b"}
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -41,14 +47,18 @@ def test_full_size(name):
     import w4a4_post_quantized_amd as L
     torch, dev = torch_dev()
     wl = WL.get(name)
+    full = name in FULL_OUTPUT
     log(f"[{name}] generate M={wl.M} K={wl.K} N={wl.N} P=({wl.n1},{wl.n2}) "
-        f"g={wl.group_size} asym={wl.asymmetric}")
+        f"g={wl.group_size} asym={wl.asymmetric} full output={full}")
     inp = WL.make_inputs(name)
     Wt = inp["W"]
     M, K, N = wl.M, wl.K, wl.N
     rows = sample_rows(M)
-    rng = np.random.default_rng(7)
-    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, 512), replace=False)]))
+    if full:
+        cols = np.arange(N)
+    else:
+        rng = np.random.default_rng(7)
+        cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, 512), replace=False)]))
 
     X_d, P1_d, P2_d = to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"])
     Wt_d = to_dev(Wt)
@@ -56,10 +66,11 @@ def test_full_size(name):
     desc, Wq, sw, zw = L.pack_weights(Wt_d, wl.group_size, wl.asymmetric)
     del Wt_d
     wq_s = O.quantize_weights(Wt[cols], wl.group_size, wl.asymmetric)
-    assert np.array_equal(take(Wq, cols), wq_s["packed"])
-    assert np.array_equal(take(sw, cols).view(np.uint16), wq_s["s"].view(np.uint16))
+    assert np.array_equal(take(Wq, None if full else cols), wq_s["packed"])
+    assert np.array_equal(take(sw, None if full else cols).view(np.uint16), wq_s["s"].view(np.uint16))
     if wl.asymmetric:
-        assert np.array_equal(take(zw, cols).view(np.uint16), wq_s["z"].view(np.uint16))
+        assert np.array_equal(take(zw, None if full else cols).view(np.uint16),
+                              wq_s["z"].view(np.uint16))
 
     log(f"[{name}] transform_quant + linear (full size)")
     Xq, sx = L.transform_quant(X_d, P1_d, P2_d)
@@ -68,15 +79,17 @@ def test_full_size(name):
 
     log(f"[{name}] oracle activation path (all tokens)")
     act = O.transform_quant(inp["X"], inp["P1"], inp["P2"])
-    n = assert_codes_match(O.unpack_nibbles(take(Xq, rows), True), act["q"][rows],
-                           act["t"][rows], what=f"{name} activation codes")
-    np.testing.assert_allclose(sx.cpu().numpy(), act["s_x"], rtol=2e-6)
-    log(f"[{name}] sampled tokens: excused tie cells {n}")
+    gq = O.unpack_nibbles(Xq.cpu().numpy(), True)
+    gsx = sx.cpu().numpy()
+    n = assert_codes_match(gq, act["q"], act["t"], what=f"{name} activation codes")
+    np.testing.assert_allclose(gsx, act["s_x"], rtol=2e-6)
+    log(f"[{name}] all {M} tokens: excused tie cells {n}")
 
     # int32 accumulators of the sampled tokens against the oracle's codes
     D = L.gemm_i32(to_dev(act["packed"][rows]), desc, Wq, zw).cpu().numpy()
     D_or = O.int_gemm(act["q"][rows], wq_s["codes"], wq_s["z"], wl.group_size)
     assert np.array_equal(D[:, cols, :], D_or)
+    del D
 
     # fp16 GEMM at full size given the oracle's codes and fp32 scales
     sx32 = act["s_x"].astype(np.float32)
@@ -84,15 +97,17 @@ def test_full_size(name):
     Y64 = O.epilogue(D_or, sx32[rows], wq_s["s"])
     A = O.epilogue(np.abs(D_or), sx32[rows], wq_s["s"])
     assert_y_close(Yg, Y64, A, what=f"{name} gemm")
+    del D_or
 
-    # whole layer end to end: library codes may differ from the oracle's at
-    # rounding ties (level 1 window); rows without such flips are held to the
-    # tight per-element bound, the others to a per-flip bound
-    gq = O.unpack_nibbles(take(Xq, rows), True)
-    flips = (gq != act["q"][rows]).sum(axis=1)
-    ref = O.epilogue(D_or, act["s_x"][rows], wq_s["s"])
-    A_ref = O.epilogue(np.abs(D_or), act["s_x"][rows], wq_s["s"])
-    Ys = take(Y, rows, cols)
-    nflip, worst = assert_linear_close(Ys, ref, A_ref, flips, what=f"{name} linear")
-    log(f"[{name}] linear relative L2 on samples {rel_l2(Ys, ref):.2e}; "
-        f"rows with tie flips {nflip}/{len(rows)} (worst {worst:.2e} per flip)")
+    # whole layer on the library's own codes: every output of the 8B shapes
+    if full:
+        log(f"[{name}] oracle product on the library's codes, all {M}x{N} outputs")
+        Ys = Y.cpu().numpy()
+        rel = assert_layer_close(Ys, gq, gsx, wq_s, what=f"{name} linear")
+        r_or = rel_l2(Ys[rows], O.epilogue_by_group(act["q"][rows], wq_s, act["s_x"][rows])[0])
+    else:
+        Ys = take(Y, rows, cols)
+        rel = assert_layer_close(Ys, gq[rows], gsx[rows], wq_s, what=f"{name} linear")
+        r_or = rel_l2(Ys, O.epilogue_by_group(act["q"][rows], wq_s, act["s_x"][rows])[0])
+    log(f"[{name}] linear relative L2 {rel:.2e} on the library's codes; "
+        f"{r_or:.2e} on sampled tokens against the oracle's own codes")

@@ -16,7 +16,7 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from gpu_common import assert_codes_match, assert_linear_close, custom_workload, log, rel_l2, \
+from gpu_common import assert_codes_match, assert_layer_close, custom_workload, log, rel_l2, \
     to_dev, torch_dev
 
 pytestmark = pytest.mark.gpu
@@ -146,8 +146,9 @@ def test_linear_static_parity(wl, per_channel):
     assert np.array_equal(Wq.cpu().numpy(), wq["packed"])
     Xd, P1d, P2d, std = to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"]), to_dev(st)
     Y = W().linear_static(Xd, P1d, P2d, std, per_channel, desc, Wq, sw, zw).cpu().numpy()
-    Xq, _ = W().transform_quant_static(Xd, P1d, P2d, std, per_channel)
-    flips = (O.unpack_nibbles(Xq.cpu().numpy(), True) != ref["act"]["q"]).sum(axis=1)
-    A = O.epilogue(np.abs(ref["D"]), ref["act"]["s_x"], wq["s"])
-    assert_linear_close(Y.astype(np.float64), ref["Y64"], A, flips)
-    log(f"  relative L2 {rel_l2(Y, ref['Y64']):.2e}, rows with tie flips {int((flips > 0).sum())}")
+    Xq, sx = W().transform_quant_static(Xd, P1d, P2d, std, per_channel)
+    gq = O.unpack_nibbles(Xq.cpu().numpy(), True)
+    n = assert_codes_match(gq, ref["act"]["q"], ref["act"]["t"])
+    rel = assert_layer_close(Y, gq, sx.cpu().numpy(), wq)
+    log(f"  relative L2 {rel:.2e} on the library's codes ({n} tie cells), "
+        f"{rel_l2(Y, ref['Y64']):.2e} against the oracle's own codes")

@@ -1,17 +1,21 @@
 """GPU parity of the ternary-weight layer (W1.58A16; PT2-LLM page, section
 关键设计 item 2: ATQ fitted by ITF), through the C ABI entry points
-w4a4_pack_ternary and w4a4_ternary_gemm.
+w4a4_pack_ternary, w4a4_unpack_ternary and w4a4_ternary_gemm.
 
 Checks:
-* pack: codes and the (alpha, mu) words bit-exact against the oracle (both
-  sides run ITF in float64 and round alpha and mu to fp16 once), including
-  all-zero and constant block rows, and a full-size weight matrix on sampled
-  rows;
-* product: Y (fp16) against the oracle's float64 layer on the oracle's own
-  packed weights, per element within half an fp16 ulp of the result plus
-  4e-6 times the magnitude of the summed terms, over decode batches that span
-  the row tiles (M = 1 .. 64, ragged), ragged N, K splits, and the full
-  LLaMA-3-70B decode shapes on sampled output columns.
+* pack: the library's tiled storage, read back through its own unpack entry
+  point (the documented bijection), gives codes T and fp16 alpha, mu equal
+  to the oracle's bit for bit (both sides run ITF in float64 and round alpha
+  and mu to fp16 once), including all-zero and constant block rows, and a
+  full-size weight matrix on sampled rows;
+* unpack is an inverse: padding rows stay zero and unpacking touches only
+  the N real rows;
+* product: Y (fp16) from the library's own packed weights against the
+  oracle's float64 layer on the oracle's (equal) T, alpha, mu, per element
+  within half an fp16 ulp of the result plus 4e-6 times the magnitude of the
+  summed terms, over decode batches that span the row tiles (M = 1 .. 64,
+  ragged), ragged N, K splits, and the full LLaMA-3-70B decode shapes on
+  sampled output columns.
 """
 import numpy as np
 import pytest
@@ -30,21 +34,26 @@ def W():
     return lib
 
 
-def oracle_pack(Wt, iters=10):
-    r = TO.itf_ternarize(Wt, iters=iters)
-    return r, TO.pack_ternary(r["T"]), TO.pack_params(r["alpha"], r["mu"])
-
-
 def gpu_pack(Wt_np, iters=10):
     Tq, am = W().pack_ternary(to_dev(Wt_np), iters=iters)
     return Tq, am
 
 
-def assert_pack_equal(tq, a, tq_or, am_or, what="pack"):
-    bad_t = np.argwhere(tq != tq_or)
-    bad_a = np.argwhere(a != am_or)
-    assert bad_a.size == 0, f"{what}: {len(bad_a)} parameter words differ, first {bad_a[:3].tolist()}"
-    assert bad_t.size == 0, f"{what}: {len(bad_t)} code bytes differ, first {bad_t[:3].tolist()}"
+def assert_pack_equal(Tq, am, r, N, K, rows=None, what="pack"):
+    """The library's packed weights, unpacked by the library, against the
+    oracle's ternarization `r` (of the rows `rows` of the matrix)."""
+    torch, dev = torch_dev()
+    T, a, u = W().unpack_ternary(Tq, am, N, K)
+    if rows is not None:
+        idx = torch.as_tensor(rows, device=T.device)
+        T, a, u = T.index_select(0, idx), a.index_select(0, idx), u.index_select(0, idx)
+    T, a, u = T.cpu().numpy(), a.cpu().numpy(), u.cpu().numpy()
+    bad_a = np.argwhere(a.view(np.uint16) != r["alpha"].view(np.uint16))
+    bad_u = np.argwhere(u.view(np.uint16) != r["mu"].view(np.uint16))
+    bad_t = np.argwhere(T != r["T"])
+    assert bad_a.size == 0, f"{what}: {len(bad_a)} alpha differ, first {bad_a[:3].tolist()}"
+    assert bad_u.size == 0, f"{what}: {len(bad_u)} mu differ, first {bad_u[:3].tolist()}"
+    assert bad_t.size == 0, f"{what}: {len(bad_t)} codes differ, first {bad_t[:3].tolist()}"
 
 
 def magnitude(X, r, cols=None):
@@ -81,10 +90,18 @@ def test_pack_bit_exact(N, K):
     if N > 2:
         Wt[2, :128] = 0.25                       # constant block row (exact mean)
         Wt[2, 5] = -0.25                         # ... but one entry: T fits it with alpha
-    _, tq_or, am_or = oracle_pack(Wt)
+    r = TO.itf_ternarize(Wt)
     Tq, am = gpu_pack(Wt)
-    assert_pack_equal(Tq.cpu().numpy(), am.cpu().numpy().view(np.uint32), tq_or, am_or,
-                      f"pack N={N} K={K}")
+    assert_pack_equal(Tq, am, r, N, K, what=f"pack N={N} K={K}")
+    # padding rows (N up to a multiple of 16) hold zero bytes and zero words
+    tqb, amb = W().ternary_weight_bytes(N, K)
+    assert Tq.numel() == tqb and am.numel() * 4 == amb
+    if N % 16:
+        Np = (N + 15) // 16 * 16
+        Tp, ap, up = W().unpack_ternary(Tq, am, Np, K)      # the padding rows as well
+        assert (Tp.cpu().numpy()[N:] == -1).all()            # zero bytes: every c = 0
+        assert not ap.cpu().numpy()[N:].view(np.uint16).any()
+        assert not up.cpu().numpy()[N:].view(np.uint16).any()
 
 
 @pytest.mark.parametrize("iters", [0, 1, 3])
@@ -92,10 +109,9 @@ def test_pack_iteration_counts(iters):
     log(f"pack_ternary iters={iters}")
     wl = WT.TernWorkload("t", M=1, K=768, N=96, x_kind="normal", seed=11 + iters)
     Wt = WT.make_tern_weights(wl)
-    _, tq_or, am_or = oracle_pack(Wt, iters)
+    r = TO.itf_ternarize(Wt, iters=iters)
     Tq, am = gpu_pack(Wt, iters)
-    assert_pack_equal(Tq.cpu().numpy(), am.cpu().numpy().view(np.uint32), tq_or, am_or,
-                      f"pack iters={iters}")
+    assert_pack_equal(Tq, am, r, 96, 768, what=f"pack iters={iters}")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (5, 100, 512), (16, 64, 4096), (17, 130, 1024),
@@ -109,9 +125,11 @@ def test_gemm_parity(M, N, K):
     wl = WT.TernWorkload("t", M=M, K=K, N=N, x_kind="silu_product" if M % 2 else "normal",
                          seed=M * 7 + N)
     inp = WT.make_tern_inputs(wl)
-    r, tq_or, am_or = oracle_pack(inp["Wt"])
+    r = TO.itf_ternarize(inp["Wt"])
+    Tq, am = gpu_pack(inp["Wt"])
+    assert_pack_equal(Tq, am, r, N, K, what=f"pack N={N} K={K}")
     Y64 = TO.ternary_linear(inp["X"], r)
-    Y = W().ternary_gemm(to_dev(inp["X"]), to_dev(tq_or), to_dev(am_or.view(np.int32)), N)
+    Y = W().ternary_gemm(to_dev(inp["X"]), Tq, am, N)
     rel = assert_tern_close(Y.cpu().numpy(), Y64, magnitude(inp["X"], r), f"M={M} N={N} K={K}")
     log(f"  rel L2 {rel:.2e}")
 
@@ -122,12 +140,13 @@ def test_gemm_zero_rows_and_m0():
     inp = WT.make_tern_inputs(wl)
     X = inp["X"].copy()
     X[4] = 0
-    r, tq_or, am_or = oracle_pack(inp["Wt"])
-    Y = W().ternary_gemm(to_dev(X), to_dev(tq_or), to_dev(am_or.view(np.int32)), 64).cpu().numpy()
+    r = TO.itf_ternarize(inp["Wt"])
+    Tq, am = gpu_pack(inp["Wt"])
+    assert_pack_equal(Tq, am, r, 64, 256)
+    Y = W().ternary_gemm(to_dev(X), Tq, am, 64).cpu().numpy()
     assert np.all(Y[4] == 0)
     assert_tern_close(Y, TO.ternary_linear(X, r), magnitude(X, r), "zero row")
-    Y0 = W().ternary_gemm(torch.empty((0, 256), dtype=torch.float16, device=dev), to_dev(tq_or),
-                          to_dev(am_or.view(np.int32)), 64)
+    Y0 = W().ternary_gemm(torch.empty((0, 256), dtype=torch.float16, device=dev), Tq, am, 64)
     assert tuple(Y0.shape) == (0, 64)
 
 
@@ -136,7 +155,8 @@ def test_full_size_sampled(name):
     """The full decode shape in the launch configuration the benchmark times:
     the GPU packs the whole matrix; sampled weight rows are packed by the
     oracle and must match bit for bit; the matching output columns are
-    compared with the oracle's layer on those rows."""
+    compared with the oracle's layer on those rows.  The library's codes and
+    parameters come back through its own unpack entry point."""
     log(f"full size {name}")
     torch, dev = torch_dev()
     wl = WT.get_tern(name)
@@ -147,20 +167,8 @@ def test_full_size_sampled(name):
     cols = np.unique(np.concatenate([[0, 1, wl.N - 1], rng.choice(wl.N, 21, replace=False)]))
     Ws = WT.make_tern_weights(wl, rows=cols)
     np.testing.assert_array_equal(Ws, inp["Wt"][cols])
-    r, _, _ = oracle_pack(Ws)
-    # the sampled rows' pieces and parameter words, gathered from both layouts
-    G = wl.K // 128
-    tq32 = Tq.cpu().numpy().view("<u4")
-    am32 = am.cpu().numpy().view(np.uint32)
-    w_full = TO.tile_offsets(wl.N, G)[cols] // 4                  # [rows, G, 4]
-    want_words = TO.piece_words(r["T"], 128)                           # [rows, G, 4, 2]
-    got_words = np.stack([tq32[w_full], tq32[w_full + 1]], axis=-1)
-    a16 = r["alpha"].view(np.uint16).astype(np.uint32)
-    u16 = r["mu"].view(np.uint16).astype(np.uint32)
-    want_am = a16 | (u16 << 16)                                    # [rows, G]
-    t, rr = np.divmod(cols, 16)
-    got_am = am32[((t[:, None] * G) + np.arange(G)[None, :]) * 16 + rr[:, None]]
-    assert_pack_equal(got_words, got_am, want_words, want_am, f"{name} sampled rows")
+    r = TO.itf_ternarize(Ws)
+    assert_pack_equal(Tq, am, r, wl.N, wl.K, rows=cols, what=f"{name} sampled rows")
     Y64 = TO.ternary_linear(inp["X"], r)
     rel = assert_tern_close(Y[:, cols], Y64, magnitude(inp["X"], r), name)
     log(f"  rel L2 {rel:.2e}")

@@ -394,6 +394,35 @@ def test_epilogue_equals_dequantized_matmul(g, asym):
     assert np.linalg.norm(out["Y64"] - ref) < 0.6 * np.linalg.norm(ref)
 
 
+@pytest.mark.parametrize("g,asym", [(8, True), (16, False), (32, True)])
+def test_epilogue_by_group_matches_brute_force(g, asym):
+    """The group-by-group form (chunked over channels, a subset of channels)
+    gives the dequantize-then-multiply product and, for the magnitude of the
+    summed terms, s_x·Σ_g s_w·|D| with D from the pure-Python triple loop."""
+    rng = np.random.default_rng(17 + g)
+    M, N, K = 5, 7, 32
+    qx = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq = O.quantize_weights(W, g, asym)
+    sx = rng.uniform(0.1, 2, M).astype(np.float32)
+    cols = np.array([6, 0, 3, 4])
+    Y, A = O.epilogue_by_group(qx, wq, sx, cols=cols, chunk=3)
+    sim = O.dequant_act(qx, sx) @ O.dequant_weights(wq)[cols].T
+    assert np.allclose(Y, sim, rtol=1e-13, atol=1e-13 * np.abs(sim).max())
+    D = O.int_gemm_loop(qx, wq["codes"][cols], wq["z"][cols], g)
+    absum = np.zeros((M, len(cols)))
+    for m in range(M):
+        for j in range(len(cols)):
+            absum[m, j] = float(sx[m]) * sum(float(wq["s"][cols[j], h]) * abs(int(D[m, j, h]))
+                                              for h in range(K // g))
+    assert np.allclose(A, absum, rtol=1e-13, atol=0)
+    if asym:
+        # mutant: a dropped zero point changes the product
+        wq0 = dict(wq, z=np.zeros_like(wq["z"]))
+        Y0, _ = O.epilogue_by_group(qx, wq0, sx, cols=cols)
+        assert not np.allclose(Y0, sim, rtol=1e-6)
+
+
 def test_linear_rows_cols_subset_consistent():
     inp = WL.make_inputs("tiny")
     Wt = O.merge_weights(inp["W"], inp["P1"], inp["P2"])

@@ -5,7 +5,7 @@ least-squares optimality of the closed-form (alpha, mu) checked against
 numpy's polynomial fit, the nearest-grid property by exhaustive search, the
 monotone decrease of the fitting error over the alternating steps, the
 dequantization bound, the layer's block-sum form against a dense matmul, and
-the storage encoding.  Mutants planted here on the CPU show each pin bites.
+the 2-bit word encoding.  Mutants planted here on the CPU show each pin bites.
 """
 import json
 import os
@@ -120,49 +120,28 @@ def test_dequant_bound_inside_the_grid():
     assert np.all(np.abs(W - deq)[inside] <= a[inside] / 2 * (1 + 1e-12))
 
 
-def test_pack_round_trip_and_bits():
+def test_pack_words_bits():
+    """The row-major 2-bit encoding, each word written out bit by bit: code
+    16 w + 2 s of a row at bits 2 s of word w, code 16 w + 2 s + 1 at bits
+    16 + 2 s, as c = t + 1."""
     rng = np.random.default_rng(6)
-    N, K = 20, 384                              # two tiles (the second ragged); a pair and one block
+    N, K = 3, 64
     T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
-    b = TO.pack_ternary(T)
-    assert b.shape == (32 * K // 4,)
-    np.testing.assert_array_equal(TO.unpack_ternary(b, N, K), T)
-
-    def word(n, idx):          # the word of the 16 codes `idx` of row n, written out bit by bit
-        v = 0
-        for i, k in enumerate(idx):
-            v |= (int(T[n, k]) + 1) << (2 * (i // 2) + 16 * (i % 2))
-        return v
-
-    def piece(g, q):           # code indices of the piece of block g, lane group q
-        return [128 * g + 32 * s_ + 8 * q + j for s_ in range(4) for j in range(8)]
-
-    def at(byte):
-        return int.from_bytes(bytes(b[byte:byte + 4].tolist()), "little")
-
-    pc = piece(1, 2)
-    assert pc[:3] == [144, 145, 146] and pc[8] == 176
-    # row 17 = tile 1 (from byte 4K = 1536), r = 1; block 1 (second of pair 0),
-    # lane group 2: (16*2 + 1) * 16 + 8 = 536
-    o = 1536 + 536
-    assert at(o) == word(17, pc[:16]) and at(o + 4) == word(17, pc[16:])
-    # row 3, block 0, lane group 3: (48 + 3) * 16 = 816
-    assert at(816) == word(3, piece(0, 3)[:16]) and at(820) == word(3, piece(0, 3)[16:])
-    # row 3, unpaired block 2, lane group 3: 1024 + (48 + 3) * 8 = 1432
-    assert at(1432) == word(3, piece(2, 3)[:16]) and at(1436) == word(3, piece(2, 3)[16:])
-    # padded row 25 (tile 1, r = 9) is zero bytes
-    assert not b[1536 + 9 * 16:1536 + 9 * 16 + 8].any()
-    # every 8-byte slot of a tile holds exactly one piece
-    off = TO.piece_offsets(5)
-    assert sorted((off.ravel() // 8).tolist()) == list(range(5 * 4 * 16))
-    # parameters: word (t * G + g) * 16 + r, zero past N
-    a = np.zeros((17, 2), np.float16)
-    u = np.zeros((17, 2), np.float16)
-    a[16, 1], u[16, 1] = 1.5, -0.25
-    p = TO.pack_params(a, u)
-    assert p.shape == (64,)
-    assert int(p[(1 * 2 + 1) * 16 + 0]) == 0x3E00 | (0xB400 << 16)
-    assert np.count_nonzero(p) == 1
+    words = TO.pack_words(T)
+    assert words.shape == (N, K // 16) and words.dtype == np.uint32
+    for n in range(N):
+        for w in range(K // 16):
+            v = 0
+            for i in range(16):
+                v |= (int(T[n, 16 * w + i]) + 1) << (2 * (i // 2) + 16 * (i % 2))
+            assert int(words[n, w]) == v
+    # every code is recoverable from its two bits (the encoding is a bijection)
+    back = np.empty_like(T)
+    for i in range(16):
+        back[:, i::16] = ((words >> (2 * (i // 2) + 16 * (i % 2))) & 3).astype(np.int8) - 1
+    np.testing.assert_array_equal(back, T)
+    with pytest.raises(ValueError):
+        TO.pack_words(T[:, :8])
 
 
 def test_layer_block_sum_equals_dense_matmul():

@@ -15,6 +15,8 @@ from typing import Optional
 
 __all__ = [
     "W4A4Error", "WeightDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "OVERRIDE_PREFILL_TILE", "OVERRIDE_DECODE", "OVERRIDE_F6_TILE", "set_kernel_override",
+    "kernel_config_count",
     "merge_weights", "pack_weights", "transform_quant", "transform", "gemm",
     "gemm_i32", "gemm_kernel_name", "linear", "merge_workspace_bytes", "transform_quant_workspace_bytes",
     "gemm_workspace_bytes", "linear_workspace_bytes", "version",
@@ -24,7 +26,7 @@ __all__ = [
     "KV_HEAD_DIM", "KvCache", "kv_cache_bytes", "kv_query_factor", "kv_append",
     "attn_decode_workspace_bytes", "attn_decode",
     "pack_weights_bits", "transform_quant_bits", "linear_bits",
-    "TERNARY_BLOCK", "TERNARY_MAX_M", "ternary_weight_bytes", "pack_ternary",
+    "TERNARY_BLOCK", "TERNARY_MAX_M", "ternary_weight_bytes", "pack_ternary", "unpack_ternary",
     "ternary_gemm_workspace_bytes",
     "ternary_gemm",
     "weights_f6_bytes", "pack_weights_f6", "gemm_f6_workspace_bytes", "gemm_f6",
@@ -35,7 +37,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a4.so"
 
 # every function include/w4a4.h declares
 EXPORTED_SYMBOLS = [
-    "w4a4_version", "w4a4_status_str", "w4a4_last_error",
+    "w4a4_version", "w4a4_status_str", "w4a4_last_error", "w4a4_set_kernel_override",
+    "w4a4_kernel_config_count",
     "w4a4_merge_workspace_bytes", "w4a4_merge_weights", "w4a4_pack_weights",
     "w4a4_migrate_steps",
     "w4a4_transform_quant_workspace_bytes", "w4a4_transform_quant", "w4a4_transform_quant_static",
@@ -46,7 +49,8 @@ EXPORTED_SYMBOLS = [
     "w4a4_kv_cache_bytes", "w4a4_kv_query_factor_workspace_bytes", "w4a4_kv_query_factor",
     "w4a4_kv_append", "w4a4_attn_decode_workspace_bytes", "w4a4_attn_decode",
     "w4a4_pack_weights_bits", "w4a4_transform_quant_bits", "w4a4_linear_bits",
-    "w4a4_ternary_weight_bytes", "w4a4_pack_ternary", "w4a4_ternary_gemm_workspace_bytes",
+    "w4a4_ternary_weight_bytes", "w4a4_pack_ternary", "w4a4_unpack_ternary",
+    "w4a4_ternary_gemm_workspace_bytes",
     "w4a4_ternary_gemm",
     "w4a4_weights_f6_bytes", "w4a4_pack_weights_f6", "w4a4_gemm_f6_workspace_bytes",
     "w4a4_gemm_f6", "w4a4_gemm_f6_kernel_name", "w4a4_linear_f6_workspace_bytes",
@@ -89,6 +93,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m w4a4_post_quantized_amd.build`")
+        # PyTorch's HIP runtime must be the process's one: loading torch first
+        # makes the library's libamdhip64.so.7 resolve to it (loaded the other
+        # way round, torch would bring a second runtime and the library's
+        # calls would see no device)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         dp = ctypes.POINTER(WeightDesc)
@@ -97,6 +106,8 @@ def lib() -> ctypes.CDLL:
             "w4a4_version": (ctypes.c_int, []),
             "w4a4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "w4a4_last_error": (ctypes.c_char_p, []),
+            "w4a4_set_kernel_override": (ctypes.c_int, [i32, i32]),
+            "w4a4_kernel_config_count": (ctypes.c_int, [i32]),
             "w4a4_merge_workspace_bytes": (sz, [i32, i32, i32]),
             "w4a4_merge_weights": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "w4a4_pack_weights": (ctypes.c_int, [dp, vp, f32, vp, vp, vp, vp]),
@@ -132,6 +143,7 @@ def lib() -> ctypes.CDLL:
                                                 vp, vp, vp, vp, sz, vp]),
             "w4a4_ternary_weight_bytes": (ctypes.c_int, [i32, i32, szp, szp]),
             "w4a4_pack_ternary": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
+            "w4a4_unpack_ternary": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp]),
             "w4a4_ternary_gemm_workspace_bytes": (sz, [i32, i32, i32]),
             "w4a4_ternary_gemm": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
             "w4a4_kv_cache_bytes": (ctypes.c_int, [i32, i32, i32, i32, szp, szp, szp]),
@@ -153,6 +165,27 @@ def lib() -> ctypes.CDLL:
 
 def version() -> int:
     return lib().w4a4_version()
+
+
+OVERRIDE_PREFILL_TILE = 0         # W4A4_OVERRIDE_PREFILL_TILE
+OVERRIDE_DECODE = 1               # W4A4_OVERRIDE_DECODE
+OVERRIDE_F6_TILE = 2              # W4A4_OVERRIDE_F6_TILE
+
+
+def set_kernel_override(which: int, index: int) -> int:
+    """Force a kernel configuration (tests and sweeps); -1 = automatic.
+    Returns the previous index."""
+    r = lib().w4a4_set_kernel_override(which, index)
+    if r < -1:
+        _check(r, "w4a4_set_kernel_override")
+    return r
+
+
+def kernel_config_count(which: int) -> int:
+    r = lib().w4a4_kernel_config_count(which)
+    if r < 0:
+        _check(r, "w4a4_kernel_config_count")
+    return r
 
 
 # ---------------------------------------------------------------------------
@@ -606,6 +639,18 @@ def pack_ternary(Wt, iters: int = 10, stream=None):
     _check(lib().w4a4_pack_ternary(_p(Wt), N, K, int(iters), _p(Tq), _p(am), _stream(stream)),
            "w4a4_pack_ternary")
     return Tq, am
+
+
+def unpack_ternary(Tq, am, N: int, K: int, stream=None):
+    """The tiled layout back to (T int8 [N, K], alpha fp16 [N, K/128],
+    mu fp16 [N, K/128])."""
+    torch = _torch()
+    T = torch.empty((N, K), dtype=torch.int8, device=Tq.device)
+    alpha = torch.empty((N, K // TERNARY_BLOCK), dtype=torch.float16, device=Tq.device)
+    mu = torch.empty_like(alpha)
+    _check(lib().w4a4_unpack_ternary(_p(Tq), _p(am), N, K, _p(T), _p(alpha), _p(mu),
+                                     _stream(stream)), "w4a4_unpack_ternary")
+    return T, alpha, mu
 
 
 def ternary_gemm_workspace_bytes(M: int, N: int, K: int) -> int:

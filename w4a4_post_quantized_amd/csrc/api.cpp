@@ -4,6 +4,7 @@
 // output.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -81,9 +82,33 @@ int check_desc(const w4a4_weight_desc* d, bool for_gemm) {
 
 }  // namespace
 
+namespace w4a4 {
+namespace {
+std::atomic<int> g_kernel_override[kOverrideKinds] = {-1, -1, -1};
+}  // namespace
+int kernel_override(int which) { return g_kernel_override[which].load(std::memory_order_relaxed); }
+}  // namespace w4a4
+
 extern "C" {
 
-int w4a4_version(void) { return (0 << 16) | (1 << 8) | 0; }
+int w4a4_version(void) { return (0 << 16) | (2 << 8) | 0; }
+
+int w4a4_kernel_config_count(int32_t which) {
+    switch (which) {
+        case W4A4_OVERRIDE_PREFILL_TILE: ok(); return w4a4::gemm_num_tile_configs();
+        case W4A4_OVERRIDE_DECODE: ok(); return w4a4::gemm_num_decode_configs();
+        case W4A4_OVERRIDE_F6_TILE: ok(); return w4a4::gemm_f6_num_configs();
+        default: return fail(W4A4_ERR_INVALID_ARG, "unknown override kind %d", which);
+    }
+}
+
+int w4a4_set_kernel_override(int32_t which, int32_t index) {
+    if (which < 0 || which >= w4a4::kOverrideKinds)
+        return fail(W4A4_ERR_INVALID_ARG, "unknown override kind %d", which);
+    if (index < -1) return fail(W4A4_ERR_INVALID_ARG, "override index %d < -1", index);
+    ok();
+    return w4a4::g_kernel_override[which].exchange(index, std::memory_order_relaxed);
+}
 
 const char* w4a4_status_str(int status) {
     switch (status) {
@@ -841,6 +866,23 @@ int w4a4_pack_ternary(const float* Wt, int32_t N, int32_t K, int32_t iters, uint
     REQUIRE_ALIGNED(am);
     hipError_t e = w4a4::tern_pack_launch(Wt, N, K, iters, Tq, am, static_cast<hipStream_t>(stream));
     return hip_status(e, "w4a4_pack_ternary");
+}
+
+int w4a4_unpack_ternary(const uint8_t* Tq, const uint32_t* am, int32_t N, int32_t K, int8_t* T,
+                        uint16_t* alpha, uint16_t* mu, void* stream) {
+    if (int s = check_tern(0, N, K)) return s;
+    REQUIRE_PTR(Tq);
+    REQUIRE_PTR(am);
+    REQUIRE_PTR(T);
+    REQUIRE_PTR(alpha);
+    REQUIRE_PTR(mu);
+    REQUIRE_ALIGNED(Tq);
+    REQUIRE_ALIGNED(am);
+    REQUIRE_ALIGNED(T);
+    REQUIRE_ALIGNED(alpha);
+    REQUIRE_ALIGNED(mu);
+    hipError_t e = w4a4::tern_unpack_launch(Tq, am, N, K, T, alpha, mu, static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_unpack_ternary");
 }
 
 size_t w4a4_ternary_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) {

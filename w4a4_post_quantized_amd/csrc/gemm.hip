@@ -33,7 +33,6 @@
 //  * MFMA: v_mfma_i32_16x16x64_i8.  Lane l supplies 16 bytes of row (l & 15)
 //    from k-slice (l >> 4) for A and for B; the result lane l holds rows
 //    4*(l >> 4) + r, column l & 15.
-#include <cstdlib>
 #include <type_traits>
 
 #include "common.hpp"
@@ -311,7 +310,7 @@ __device__ __forceinline__ int dl_slot(int row, int c) { return c ^ (((row >> 1)
 
 // s_waitcnt with only a vmcnt condition (gfx9 encoding; expcnt and lgkmcnt
 // left at their no-wait maxima)
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool ASYM, int MODE>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool ASYM, int MODE, bool G1 = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
@@ -328,8 +327,13 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     constexpr int CHUNKS = (BM + BN) * 4;             // 16-byte chunks per tile
     static_assert(CHUNKS % (64 * NW) == 0 && (BM * 4) % 64 == 0, "whole wave loads");
     constexpr int LPW = CHUNKS / (64 * NW);           // load instructions per wave per tile
-    static_assert(STAGES >= 3 && STAGES <= 8 && (STAGES - 2) * LPW < 64, "stages / vmcnt range");
+    // vector-memory ops a wave issues per tile besides its copies: the next
+    // tile's scale (and zero point) per B fragment in one-tile-group mode
+    constexpr int NSZ = G1 ? FN * (ASYM ? 2 : 1) : 0;
+    constexpr int WAITN = (STAGES - 2) * LPW + (STAGES - 1) * NSZ;
+    static_assert(STAGES >= 3 && STAGES <= 8 && WAITN < 64, "stages / vmcnt range");
     static_assert(MODE != kModeI32, "fp16 output modes only");
+    static_assert(!G1 || MODE == kModeGroup, "one-tile groups: per-group mode");
 
     // one LDS array per stage: distinct objects let the compiler see that
     // reads of one stage do not depend on the DMA writes into the others
@@ -373,8 +377,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     // are loaded inside the K loop, and the compiler's waits for those loads
     // must count the copies.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const uint8_t* src[ASYM ? LPW : 1];
-    uint32_t soff[ASYM ? 1 : LPW];
+    constexpr bool kBuiltinCopies = ASYM || G1;
+    const uint8_t* src[kBuiltinCopies ? LPW : 1];
+    uint32_t soff[kBuiltinCopies ? 1 : LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int j = (i * NW + wave_u) * 64 + lane;   // 16-byte slot in the stage
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         const int row = jj >> 2;
         const int c = (jj & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
         const int r = isA ? min(m0 + row, M - 1) : min(n0 + row, N - 1);
-        if constexpr (ASYM)
+        if constexpr (kBuiltinCopies)
             src[i] = (isA ? Xq : Wq) + static_cast<size_t>(r) * KB + c * 16;
         else
             soff[i] = static_cast<uint32_t>(r - (isA ? m0 : n0)) * KB + c * 16;
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     auto issue = [&](int kt, auto S) {
         const int kc = min(kt, KT - 1);
         uint8_t* stage = stage_ptr(S);
-        if constexpr (ASYM) {
+        if constexpr (kBuiltinCopies) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i) dma16(src[i] + kc * 64, stage + (i * NW + wave) * 1024);
         } else {
@@ -444,6 +449,34 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
 #pragma unroll
     for (int b = 0; b < FN; ++b) brow_g[b] = min(n0 + wn0 + b * 32 + frow, N - 1);
 
+    // One-tile groups (group size 128): each K tile is one weight group.  The
+    // tile's MFMA chain starts from a zero register operand and its exact
+    // int32 sums are folded at once into the fp32 sums with the group's
+    // scale, so no accumulator is ever cleared.  The lane's B row is its
+    // output column (frow == ocol), so one scale and one zero point per B
+    // fragment serve both the unpack and the fold; they are loaded one tile
+    // ahead.  A zero made opaque to the compiler: an MFMA whose accumulator
+    // operand was an inline-constant zero gave wrong sums.
+    v16i zc16;
+    const uint16_t* swp[G1 ? FN : 1];
+    const uint16_t* zwp[G1 && ASYM ? FN : 1];
+    uint16_t s_nx[G1 ? FN : 1], z_nx[G1 && ASYM ? FN : 1];
+    if constexpr (G1) {
+        int z0;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zc16[r] = z0;
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            swp[b] = s_w + static_cast<size_t>(brow_g[b]) * G;
+            s_nx[b] = swp[b][0];
+            if constexpr (ASYM) {
+                zwp[b] = z_w + static_cast<size_t>(brow_g[b]) * G;
+                z_nx[b] = zwp[b][0];
+            }
+        }
+    }
+
     // one K tile: tile kt is in stage kt % STAGES; the DMA of tile
     // kt+STAGES-1 goes into the stage tile kt-1 used
     auto body = [&](int kt, auto S) {
@@ -451,7 +484,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         issue(kt + STAGES - 1, std::integral_constant<int, (SI + STAGES - 1) % STAGES>{});
         const uint8_t* stage = stage_ptr(S);
         uint32_t zbias[FN];
-        if constexpr (ASYM) {
+        float sw_t[G1 ? FN : 1];
+        if constexpr (G1) {
+            // this tile's scale and zero point, then the next tile's loads
+            const int kn = min(kt + 1, KT - 1);
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                sw_t[b] = h2f(s_nx[b]);
+                if constexpr (ASYM) {
+                    const uint32_t z = static_cast<uint32_t>(h2f(z_nx[b]));
+                    zbias[b] = (0x80u - z) * 0x01010101u;
+                }
+                s_nx[b] = swp[b][kn];
+                if constexpr (ASYM) z_nx[b] = zwp[b][kn];
+            }
+        } else if constexpr (ASYM) {
             const int g = (kt * BK) / group_size;
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
@@ -485,14 +532,23 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
             for (int a = 0; a < FM; ++a)
 #pragma unroll
                 for (int b = 0; b < FN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo[a], blo[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        alo[a], blo[b], (G1 && p == 0) ? zc16 : acc[a][b], 0, 0, 0);
 #pragma unroll
             for (int a = 0; a < FM; ++a)
 #pragma unroll
                 for (int b = 0; b < FN; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[a], bhi[b], acc[a][b], 0, 0, 0);
         }
-        if constexpr (MODE == kModeGroup) {
+        if constexpr (G1) {
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        facc[a][b][r] = fmaf(static_cast<float>(acc[a][b][r]), sw_t[b], facc[a][b][r]);
+        } else if constexpr (MODE == kModeGroup) {
             if (((kt + 1) % TPG) == 0) {
                 const int g = kt / TPG;
 #pragma unroll
@@ -510,11 +566,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
             }
         }
         // tile kt+1 has landed once at most STAGES-2 tiles of this wave's
-        // loads are outstanding; the barrier makes every wave's part visible
-        // and retires the reads of stage kt before it is refilled.  A plain
+        // copies (and the scale loads issued after tile kt+1's copies) are
+        // outstanding; the barrier makes every wave's part visible and
+        // retires the reads of stage kt before it is refilled.  A plain
         // s_barrier: a workgroup fence would also drain the newer DMA loads,
         // and every LDS read of this tile has already fed an MFMA.
-        wait_vmcnt<(STAGES - 2) * LPW>();
+        wait_vmcnt<WAITN>();
         lds_barrier();
     };
 
@@ -557,6 +614,17 @@ template <int BM, int BN, int WM_, int WN_, int ST, int MODE>
 hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
     dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM));
     dim3 block(WM_ * WN_ * 64);
+    if constexpr (MODE == kModeGroup) {
+        if (a.group_size == BK) {
+            if (a.asym)
+                k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE, true><<<grid, block, 0, stream>>>(
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
+            else
+                k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE, true><<<grid, block, 0, stream>>>(
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
+            return hipGetLastError();
+        }
+    }
     if (a.asym)
         k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE><<<grid, block, 0, stream>>>(
             a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
@@ -935,6 +1003,7 @@ template <int MODE> hipError_t dl256x256_4x4_s3(const GemmArgs& a, hipStream_t s
 template <int MODE> hipError_t dl128x384_2x4_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 384, 2, 4, 4, MODE>(a, s); }
 template <int MODE> hipError_t dl128x384_2x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 384, 2, 4, 3, MODE>(a, s); }
 template <int MODE> hipError_t dl128x384_4x4_s3(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 384, 4, 4, 3, MODE>(a, s); }
+template <int MODE> hipError_t dl128x256_2x4_s4(const GemmArgs& a, hipStream_t s) { return launch_dl<128, 256, 2, 4, 4, MODE>(a, s); }
 
 
 template <int MODE> hipError_t r16_256x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 128, 2, 4, MODE>(a, s); }
@@ -955,6 +1024,7 @@ const KernelCfg kTiles[] = {
     W4A4_CFG_CHAN("k_gemm_dl<128x384, waves 2x4, 4 stages>", dl128x384_2x4_s4),
     W4A4_CFG_CHAN("k_gemm_dl<128x384, waves 2x4, 3 stages>", dl128x384_2x4_s3),
     W4A4_CFG_CHAN("k_gemm_dl<128x384, waves 4x4, 3 stages>", dl128x384_4x4_s3),
+    W4A4_CFG("k_gemm_dl<128x256, waves 2x4, 4 stages>", dl128x256_2x4_s4),
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -980,13 +1050,11 @@ const KernelCfg kDec[3][kNumDec] = {
 
 const KernelCfg kI32{"k_gemm_w4a4<64x64, waves 2x2, int32 out>", nullptr, nullptr};
 
-// Developer overrides for sweeps and tests (read at every call; unset or out
-// of range means automatic): W4A4_GEMM_TILE indexes the prefill table,
-// W4A4_GEMM_DECODE the decode variants.
-int env_index(const char* name, int n) {
-    const char* e = getenv(name);
-    if (e == nullptr || *e == '\0') return -1;
-    const int v = atoi(e);
+// Selection override for tests and sweeps (w4a4_set_kernel_override): an
+// index into the prefill table or the decode variants, -1 or out of range =
+// automatic.
+int override_index(int which, int n) {
+    const int v = kernel_override(which);
     return (v >= 0 && v < n) ? v : -1;
 }
 
@@ -995,7 +1063,7 @@ const KernelCfg& choose(const GemmArgs& a) {
     const int cus = device_cu_count();
     if (a.M <= 64) {
         const int fi = a.M <= 16 ? 0 : (a.M <= 32 ? 1 : 2);
-        int v = env_index("W4A4_GEMM_DECODE", kNumDec);
+        int v = override_index(1, kNumDec);
         if (v < 0) {
             // measured on MI355X: one 16-column fragment per workgroup while
             // two workgroups fit a CU, two once the staged activations fill
@@ -1010,7 +1078,7 @@ const KernelCfg& choose(const GemmArgs& a) {
         }
         return kDec[fi][v];
     }
-    int t = env_index("W4A4_GEMM_TILE", kNumTiles);
+    int t = override_index(0, kNumTiles);
     if (t < 0 || (grouped && kTiles[t].group == nullptr)) {
         // measured on MI355X: direct-to-LDS 256x256 tiles (8 waves) when the
         // grid covers the CUs several times over, 256x256 tiles with 16 waves
@@ -1021,7 +1089,10 @@ const KernelCfg& choose(const GemmArgs& a) {
         // 2048x6144 takes 50.6 against 53.3 us with 256x256 tiles)
         const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
         const long tiles384 = static_cast<long>(ceil_div(a.M, 128)) * ceil_div(a.N, 384);
-        if (grouped)
+        const long tiles256x128 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 128);
+        if (grouped && a.group_size == BK)
+            t = tiles256x128 >= cus ? 4 : 1;
+        else if (grouped)
             t = 2;
         else if (tiles256 >= 2L * cus)
             t = 0;
@@ -1038,6 +1109,7 @@ const KernelCfg& choose(const GemmArgs& a) {
 }  // namespace
 
 int gemm_num_tile_configs() { return kNumTiles; }
+int gemm_num_decode_configs() { return kNumDec; }
 
 size_t gemm_workspace_bytes(int M, int N, int K, int group_size) {
     (void)M;

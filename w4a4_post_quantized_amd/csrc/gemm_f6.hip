@@ -25,7 +25,6 @@
 //   at ((kt / 2) Rp / 32 + rt) · 3072 + (kt % 2) · 1536: the two fragments of
 //   a 128-code K tile are adjacent and a K tile of consecutive row fragments
 //   is contiguous.
-#include <cstdlib>
 #include <type_traits>
 
 #include "common.hpp"
@@ -407,9 +406,9 @@ bool f6_g1_ok(const F6Args& a) {
 const F6Cfg& choose_f6(const F6Args& a) {
     const bool grouped = a.K / a.group_size > 1;
     const bool g1 = f6_g1_ok(a);
-    const char* e = getenv("W4A4_GEMM_F6_TILE");
-    if (e != nullptr && *e != '\0') {
-        const int v = atoi(e);
+    // selection override for tests and sweeps (w4a4_set_kernel_override)
+    {
+        const int v = kernel_override(2);
         if (v >= 0 && v < kNumF6 &&
             (!grouped || kF6Tiles[v].group != nullptr || (g1 && kF6Tiles[v].g1 != nullptr)))
             return kF6Tiles[v];
@@ -431,6 +430,8 @@ const F6Cfg& choose_f6(const F6Args& a) {
 }
 
 }  // namespace
+
+int gemm_f6_num_configs() { return kNumF6; }
 
 size_t f6_bytes(int R, int K) { return static_cast<size_t>(f6_rows(R)) * K * 3 / 4; }
 

@@ -9,6 +9,14 @@
 
 namespace w4a4 {
 
+// ---- kernel selection overrides (w4a4_set_kernel_override) -----------------
+// which: 0 prefill GEMM tile, 1 decode GEMM variant, 2 fp6 tile; -1 = automatic
+constexpr int kOverrideKinds = 3;
+int kernel_override(int which);
+int gemm_num_tile_configs();
+int gemm_num_decode_configs();
+int gemm_f6_num_configs();
+
 // ---- activation path (transform_quant.hip) --------------------------------
 enum class TqPath { Fused, Cols, Split };
 
@@ -147,6 +155,8 @@ inline int tern_rows(int N) { return (N + 15) / 16 * 16; }   // rows in storage
 size_t tern_workspace_bytes(int M, int N, int K);   // for this device
 hipError_t tern_pack_launch(const float* Wt, int N, int K, int iters, uint8_t* Tq, uint32_t* am,
                             hipStream_t stream);
+hipError_t tern_unpack_launch(const uint8_t* Tq, const uint32_t* am, int N, int K, int8_t* T,
+                              uint16_t* alpha, uint16_t* mu, hipStream_t stream);
 hipError_t tern_gemm_launch(const uint16_t* X, int M, int N, int K, const uint8_t* Tq,
                             const uint32_t* am, uint16_t* Y, void* ws, hipStream_t stream);
 

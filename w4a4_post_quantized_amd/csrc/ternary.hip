@@ -122,6 +122,36 @@ __global__ __launch_bounds__(kTB) void k_tern_pack(const float* __restrict__ Wt,
     if (t == 0) *amw = static_cast<uint32_t>(a16) | (static_cast<uint32_t>(u16) << 16);
 }
 
+// The inverse of the storage layout k_tern_pack writes: one workgroup of 128
+// threads per (row, block), thread t reading code t of the block from its
+// lane group's piece (the same word and bit position the pack wrote it to),
+// thread 0 the block's parameter word.  Codes go out as int8 in {-1, 0, 1}
+// row-major [N][K], alpha and mu as fp16 bits [N][K/128].
+__global__ __launch_bounds__(kTB) void k_tern_unpack(const uint8_t* __restrict__ Tq,
+                                                     const uint32_t* __restrict__ am, int N, int K,
+                                                     int8_t* __restrict__ T, uint16_t* __restrict__ alpha,
+                                                     uint16_t* __restrict__ mu) {
+    const int row = blockIdx.x;
+    const int g = blockIdx.y;
+    const int G = K / kTB;
+    const int t = threadIdx.x;
+    const int tile = row >> 4;
+    const int r = row & 15;
+    const uint32_t* const tq32 = reinterpret_cast<const uint32_t*>(Tq + static_cast<size_t>(tile) * 4 * K);
+    const int pr = g >> 1;
+    const int sq = t >> 5, q = (t >> 3) & 3, i = 8 * (sq & 1) + (t & 7);
+    const int off = 2 * pr + 1 < G ? 1024 * pr + (16 * q + r) * 16 + 8 * (g & 1)
+                                   : 1024 * pr + (16 * q + r) * 8;
+    const uint32_t word = tq32[(off >> 2) + (sq >> 1)];
+    const int c = static_cast<int>((word >> (16 * (i & 1) + 2 * (i >> 1))) & 3u);
+    T[static_cast<size_t>(row) * K + g * kTB + t] = static_cast<int8_t>(c - 1);
+    if (t == 0) {
+        const uint32_t w = am[(static_cast<size_t>(tile) * G + g) * 16 + r];
+        alpha[static_cast<size_t>(row) * G + g] = static_cast<uint16_t>(w & 0xFFFFu);
+        mu[static_cast<size_t>(row) * G + g] = static_cast<uint16_t>(w >> 16);
+    }
+}
+
 // Eight codes of one MFMA step as fp16 values c * 2^-14, in k order: register v
 // holds codes 8h + 2v (low half) and 8h + 2v + 1 (high half), each moved from
 // its bit position 8h + 2v (+ 16) to the exponent field, bits 10-11 (+ 16).
@@ -471,6 +501,12 @@ hipError_t tern_pack_launch(const float* Wt, int N, int K, int iters, uint8_t* T
                             hipStream_t stream) {
     if (N == 0) return hipSuccess;
     k_tern_pack<<<dim3(tern_rows(N), K / kTB), kTB, 0, stream>>>(Wt, N, K, iters, Tq, am);
+    return hipGetLastError();
+}
+
+hipError_t tern_unpack_launch(const uint8_t* Tq, const uint32_t* am, int N, int K, int8_t* T,
+                              uint16_t* alpha, uint16_t* mu, hipStream_t stream) {
+    k_tern_unpack<<<dim3(N, K / kTB), kTB, 0, stream>>>(Tq, am, N, K, T, alpha, mu);
     return hipGetLastError();
 }
 
