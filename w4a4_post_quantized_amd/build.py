@@ -34,14 +34,10 @@ COMMON_FLAGS = [
 SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "weights.hip", "linear_decode.hip",
            "kv_cache.hip", "attention.hip", "ternary.hip", "gemm_f6.hip"]
 
-# Per-source flags.  gemm.hip: MFMA results in VGPRs (not AGPRs), so the
-# per-group fold reads the int32 sums without a v_accvgpr_read per element.
-SOURCE_FLAGS = {"gemm.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
-
 
 def _compile(src: str, extra=()):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra]
+    cmd = [HIPCC, *COMMON_FLAGS, *extra]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -1083,15 +1083,17 @@ const KernelCfg& choose(const GemmArgs& a) {
         // measured on MI355X: direct-to-LDS 256x256 tiles (8 waves) when the
         // grid covers the CUs several times over, 256x256 tiles with 16 waves
         // for about one wave of tiles (2048x6144: 57 against 60 us for
-        // 128x128 tiles), direct-to-LDS 128x128 tiles below that, 16x16x64
-        // 128x128 (8 waves) for the per-group mode
+        // 128x128 tiles), direct-to-LDS 128x128 tiles below that
         // (128x384 tiles with 16 waves when they give about one tile per CU:
-        // 2048x6144 takes 50.6 against 53.3 us with 256x256 tiles)
+        // 2048x6144 takes 50.6 against 53.3 us with 256x256 tiles).
+        // Groups of 128: the direct-to-LDS 128x128 tile with 3 stages and
+        // one-tile groups (2048x4096 -> 28672: 442 against 467 us for the
+        // 16x16x64 register-staged tile); other group sizes: the 16x16x64
+        // 128x128 tile (8 waves)
         const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
         const long tiles384 = static_cast<long>(ceil_div(a.M, 128)) * ceil_div(a.N, 384);
-        const long tiles256x128 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 128);
         if (grouped && a.group_size == BK)
-            t = tiles256x128 >= cus ? 4 : 1;
+            t = 5;
         else if (grouped)
             t = 2;
         else if (tiles256 >= 2L * cus)
