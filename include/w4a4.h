@@ -256,6 +256,25 @@ int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                 const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
                 const uint16_t* z_w, uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* w4a4_linear for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and results as w4a4_linear, with its workspace (packed activations,
+ * their scales, the transform's intermediates) taken from a scratch array of
+ * W4A4_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one per
+ * device it runs on, until the process ends.  The caller still passes every
+ * input and the output Y.  No call allocates or frees memory; the scratch's
+ * device address is looked up once per device (first call with that device
+ * current).  A call whose workspace would exceed the scratch returns
+ * W4A4_ERR_UNSUPPORTED and launches nothing.  Every call on a device shares
+ * that device's scratch and leaves its contents behind; each call writes all
+ * the scratch it reads, so nothing has to be cleared, but calls that overlap
+ * on one device (several streams or threads) race on it. */
+#define W4A4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int w4a4_linear_noalloc(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                        const float* P2, const float* c, float alpha_a,
+                        const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                        const uint16_t* z_w, uint16_t* Y, void* stream);
+
 /* w4a4_linear with static activation steps (w4a4_transform_quant_static
  * followed by w4a4_gemm; same workspace as w4a4_linear).  With
  * per_channel = 1 the weights must carry the migrated steps

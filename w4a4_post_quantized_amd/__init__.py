@@ -18,7 +18,8 @@ __all__ = [
     "OVERRIDE_PREFILL_TILE", "OVERRIDE_DECODE", "OVERRIDE_F6_TILE", "set_kernel_override",
     "kernel_config_count",
     "merge_weights", "pack_weights", "transform_quant", "transform", "gemm",
-    "gemm_i32", "gemm_kernel_name", "linear", "merge_workspace_bytes", "transform_quant_workspace_bytes",
+    "gemm_i32", "gemm_kernel_name", "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "merge_workspace_bytes", "transform_quant_workspace_bytes",
     "gemm_workspace_bytes", "linear_workspace_bytes", "version",
     "migrate_steps", "transform_quant_static", "linear_static",
     "linear_decode", "linear_decode_workspace_bytes", "decode_sync_buffer",
@@ -44,7 +45,7 @@ EXPORTED_SYMBOLS = [
     "w4a4_transform_quant_workspace_bytes", "w4a4_transform_quant", "w4a4_transform_quant_static",
     "w4a4_transform",
     "w4a4_gemm_workspace_bytes", "w4a4_gemm", "w4a4_gemm_i32", "w4a4_gemm_kernel_name",
-    "w4a4_linear_workspace_bytes", "w4a4_linear", "w4a4_linear_static",
+    "w4a4_linear_workspace_bytes", "w4a4_linear", "w4a4_linear_noalloc", "w4a4_linear_static",
     "w4a4_linear_decode_workspace_bytes", "w4a4_linear_decode",
     "w4a4_kv_cache_bytes", "w4a4_kv_query_factor_workspace_bytes", "w4a4_kv_query_factor",
     "w4a4_kv_append", "w4a4_attn_decode_workspace_bytes", "w4a4_attn_decode",
@@ -128,6 +129,8 @@ def lib() -> ctypes.CDLL:
                                               vp, vp, vp, vp, sz, vp]),
             "w4a4_linear_workspace_bytes": (sz, [i32, i32, i32, i32, dp]),
             "w4a4_linear": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, dp, vp, vp, vp, vp, vp, sz, vp]),
+            "w4a4_linear_noalloc": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, f32, dp, vp, vp,
+                                                   vp, vp, vp]),
             "w4a4_migrate_steps": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
             "w4a4_transform_quant_static": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                                            vp, sz, vp]),
@@ -411,6 +414,24 @@ def linear(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, c=None, alpha_a: floa
     _check(lib().w4a4_linear(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
                              ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y), _p(ws),
                              nb if ws is None else ws.numel(), _stream(stream)), "w4a4_linear")
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # W4A4_NOALLOC_SCRATCH_BYTES
+
+
+def linear_noalloc(X, P1, P2, desc: WeightDesc, Wq, s_w, z_w=None, c=None, alpha_a: float = 1.0,
+                   out=None, stream=None):
+    """w4a4_linear with the library's own device scratch instead of a
+    workspace (the library allocates nothing).  `out` should be given by
+    callers that cannot allocate; otherwise the output is allocated here."""
+    torch = _torch()
+    M, K = X.shape
+    n1, n2 = P1.shape[0], P2.shape[0]
+    Y = out if out is not None else torch.empty((M, desc.N), dtype=torch.float16, device=X.device)
+    _check(lib().w4a4_linear_noalloc(_p(X), M, n1, n2, _p(P1), _p(P2), _p(c), float(alpha_a),
+                                     ctypes.byref(desc), _p(Wq), _p(s_w), _p(z_w), _p(Y),
+                                     _stream(stream)), "w4a4_linear_noalloc")
     return Y
 
 

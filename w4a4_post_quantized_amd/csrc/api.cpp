@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -427,6 +428,65 @@ int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const floa
                 void* ws, size_t ws_bytes, void* stream) {
     return linear_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{alpha_a, nullptr, false}, desc,
                          Wq, s_w, z_w, Y, ws, ws_bytes, stream, "w4a4_linear");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of w4a4_linear_noalloc: a file-scope device array (each device the
+// library runs on holds its own copy until the process ends).  Host code
+// never passes the array's name to a kernel: its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and
+// that address is what the kernels receive.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kNoAllocScratchBytes = W4A4_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "w4a4_linear_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(W4A4_ERR_UNSUPPORTED, "w4a4_linear_noalloc: device ordinal %d >= %d", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "w4a4_linear_noalloc: hipGetSymbolAddress");
+        if (p == nullptr)
+            return fail(W4A4_ERR_HIP, "w4a4_linear_noalloc: no device address for the scratch");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int w4a4_linear_noalloc(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
+                        const float* P2, const float* c, float alpha_a,
+                        const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
+                        const uint16_t* z_w, uint16_t* Y, void* stream) {
+    if (int s = check_desc(desc, true)) return s;
+    if (int s = check_factors(M, n1, n2)) return s;
+    REQUIRE(desc->K == n1 * n2, W4A4_ERR_INVALID_ARG, "desc->K = %d != n1*n2 = %d", desc->K,
+            n1 * n2);
+    const size_t need = w4a4_linear_workspace_bytes(M, n1, n2, c != nullptr, desc);
+    REQUIRE(need <= kNoAllocScratchBytes, W4A4_ERR_UNSUPPORTED,
+            "w4a4_linear_noalloc: M = %d tokens need %zu bytes of scratch, more than its %zu "
+            "(W4A4_NOALLOC_SCRATCH_BYTES); use w4a4_linear with a workspace", M, need,
+            kNoAllocScratchBytes);
+    if (M == 0) return ok();
+    void* ws = nullptr;
+    if (int s = scratch_of_current_device(&ws)) return s;
+    return linear_common(X, M, n1, n2, P1, P2, c, w4a4::ActQuant{alpha_a, nullptr, false}, desc,
+                         Wq, s_w, z_w, Y, ws, kNoAllocScratchBytes, stream, "w4a4_linear_noalloc");
 }
 
 int w4a4_linear_bits(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const float* P1,
