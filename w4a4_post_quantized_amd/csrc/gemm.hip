@@ -308,6 +308,23 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
 // ===========================================================================
 __device__ __forceinline__ int dl_slot(int row, int c) { return c ^ (((row >> 1) ^ (row >> 3)) & 3); }
 
+// XCD-aware tile order.  Workgroups are dispatched round-robin over the 8
+// XCDs (workgroup L to XCD L % 8), each with its own L2.  The 1-D grid index
+// is turned into a tile index t so that XCD x walks the contiguous range of
+// tiles it owns, in the order its workgroups start; t runs down the M tiles
+// of one column of N tiles first, so the workgroups an XCD holds at once share
+// one or two weight panels (each weight panel is read into one L2 once) and
+// reuse the activation panels, which stay in the L2s and the Infinity Cache.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_tile(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int T = tiles_m * tiles_n;
+    const int per = T / kXcds, rem = T % kXcds;
+    const int x = L % kXcds, local = L / kXcds;
+    const int t = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
+    tn = t / tiles_m;
+    tm = t - tn * tiles_m;
+}
+
 // s_waitcnt with only a vmcnt condition (gfx9 encoding; expcnt and lgkmcnt
 // left at their no-wait maxima)
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool ASYM, int MODE, bool G1 = false>
@@ -362,8 +379,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const int wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM;
     const int wn0 = (wave % WAVES_N) * WN;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+    int tm, tn;
+    xcd_tile(blockIdx.x, ceil_div(M, BM), ceil_div(N, BN), tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
     const int KB = K / 2;
     const int KT = K / BK;
     const int G = K / group_size;
@@ -612,7 +631,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
 
 template <int BM, int BN, int WM_, int WN_, int ST, int MODE>
 hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
-    dim3 grid(ceil_div(a.N, BN), ceil_div(a.M, BM));
+    // one workgroup per output tile, in a 1-D grid (tile order: xcd_tile)
+    dim3 grid(ceil_div(a.N, BN) * ceil_div(a.M, BM));
     dim3 block(WM_ * WN_ * 64);
     if constexpr (MODE == kModeGroup) {
         if (a.group_size == BK) {
@@ -1080,10 +1100,11 @@ const KernelCfg& choose(const GemmArgs& a) {
     }
     int t = override_index(0, kNumTiles);
     if (t < 0 || (grouped && kTiles[t].group == nullptr)) {
-        // measured on MI355X: direct-to-LDS 256x256 tiles (8 waves) when the
-        // grid covers the CUs several times over, 256x256 tiles with 16 waves
-        // for about one wave of tiles (2048x6144: 57 against 60 us for
-        // 128x128 tiles), direct-to-LDS 128x128 tiles below that
+        // measured on MI355X: direct-to-LDS 256x256 tiles with 16 waves when
+        // the grid covers the CUs at least half over (4096x8192 -> 57344 with
+        // three weight copies rotated: 1486-1520 against 1545-1549 us for 8
+        // waves; 2048x6144: 57 against 60 us for 128x128 tiles),
+        // direct-to-LDS 128x128 tiles below that
         // (128x384 tiles with 16 waves when they give about one tile per CU:
         // 2048x6144 takes 50.6 against 53.3 us with 256x256 tiles).
         // Groups of 128: the direct-to-LDS 128x128 tile with 3 stages and
@@ -1096,8 +1117,6 @@ const KernelCfg& choose(const GemmArgs& a) {
             t = 5;
         else if (grouped)
             t = 2;
-        else if (tiles256 >= 2L * cus)
-            t = 0;
         else if (tiles384 >= cus && tiles384 < 2L * cus)
             t = 11;
         else if (2L * tiles256 >= cus)
