@@ -84,7 +84,9 @@ const char* w4a4_last_error(void);
  * never needs it).  `which` names a dispatcher:
  *   W4A4_OVERRIDE_PREFILL_TILE  prefill GEMM configurations (M > 64);
  *   W4A4_OVERRIDE_DECODE        decode GEMM variants (M <= 64);
- *   W4A4_OVERRIDE_F6_TILE       configurations of the fp6-pipe product.
+ *   W4A4_OVERRIDE_F6_TILE       configurations of the fp6-pipe product;
+ *   W4A4_OVERRIDE_TILE_GROUP    M tiles per group in the prefill GEMM's
+ *                               order of output tiles (index = the count).
  * index in [0, w4a4_kernel_config_count(which)) forces that configuration for
  * every later call in this process; -1 restores the automatic choice.  An
  * index past the table, or a configuration without the call's weight mode,
@@ -95,6 +97,7 @@ const char* w4a4_last_error(void);
 #define W4A4_OVERRIDE_PREFILL_TILE 0
 #define W4A4_OVERRIDE_DECODE 1
 #define W4A4_OVERRIDE_F6_TILE 2
+#define W4A4_OVERRIDE_TILE_GROUP 3   /* M tiles per group of the prefill tile order */
 int w4a4_set_kernel_override(int32_t which, int32_t index);
 
 /* Number of configurations behind `which` (as above), or

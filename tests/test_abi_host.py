@@ -168,7 +168,9 @@ def test_kernel_override_is_a_host_setting():
     assert W.kernel_config_count(W.OVERRIDE_DECODE) == 4
     assert W.kernel_config_count(W.OVERRIDE_F6_TILE) >= 1
     L = W.lib()
-    assert L.w4a4_set_kernel_override(3, 0) == -1 and "kind" in last()
+    assert L.w4a4_set_kernel_override(4, 0) == -1 and "kind" in last()
+    assert W.set_kernel_override(W.OVERRIDE_TILE_GROUP, 4) == -1
+    assert W.set_kernel_override(W.OVERRIDE_TILE_GROUP, -1) == 4
     assert L.w4a4_set_kernel_override(0, -2) == -1
     assert L.w4a4_kernel_config_count(-1) == -1
 

@@ -15,7 +15,8 @@ from typing import Optional
 
 __all__ = [
     "W4A4Error", "WeightDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
-    "OVERRIDE_PREFILL_TILE", "OVERRIDE_DECODE", "OVERRIDE_F6_TILE", "set_kernel_override",
+    "OVERRIDE_PREFILL_TILE", "OVERRIDE_DECODE", "OVERRIDE_F6_TILE", "OVERRIDE_TILE_GROUP",
+    "set_kernel_override",
     "kernel_config_count",
     "merge_weights", "pack_weights", "transform_quant", "transform", "gemm",
     "gemm_i32", "gemm_kernel_name", "linear", "linear_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -173,6 +174,7 @@ def version() -> int:
 OVERRIDE_PREFILL_TILE = 0         # W4A4_OVERRIDE_PREFILL_TILE
 OVERRIDE_DECODE = 1               # W4A4_OVERRIDE_DECODE
 OVERRIDE_F6_TILE = 2              # W4A4_OVERRIDE_F6_TILE
+OVERRIDE_TILE_GROUP = 3           # W4A4_OVERRIDE_TILE_GROUP
 
 
 def set_kernel_override(which: int, index: int) -> int:

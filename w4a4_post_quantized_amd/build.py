@@ -31,8 +31,8 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 
-SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "weights.hip", "linear_decode.hip",
-           "kv_cache.hip", "attention.hip", "ternary.hip", "gemm_f6.hip"]
+SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "gemm_decode.hip", "weights.hip",
+           "linear_decode.hip", "kv_cache.hip", "attention.hip", "ternary.hip", "gemm_f6.hip"]
 
 
 def _compile(src: str, extra=()):

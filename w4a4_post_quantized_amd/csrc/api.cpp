@@ -85,7 +85,7 @@ int check_desc(const w4a4_weight_desc* d, bool for_gemm) {
 
 namespace w4a4 {
 namespace {
-std::atomic<int> g_kernel_override[kOverrideKinds] = {-1, -1, -1};
+std::atomic<int> g_kernel_override[kOverrideKinds] = {-1, -1, -1, -1};
 }  // namespace
 int kernel_override(int which) { return g_kernel_override[which].load(std::memory_order_relaxed); }
 }  // namespace w4a4
@@ -99,6 +99,7 @@ int w4a4_kernel_config_count(int32_t which) {
         case W4A4_OVERRIDE_PREFILL_TILE: ok(); return w4a4::gemm_num_tile_configs();
         case W4A4_OVERRIDE_DECODE: ok(); return w4a4::gemm_num_decode_configs();
         case W4A4_OVERRIDE_F6_TILE: ok(); return w4a4::gemm_f6_num_configs();
+        case W4A4_OVERRIDE_TILE_GROUP: ok(); return 1 << 16;
         default: return fail(W4A4_ERR_INVALID_ARG, "unknown override kind %d", which);
     }
 }

@@ -311,18 +311,23 @@ __device__ __forceinline__ int dl_slot(int row, int c) { return c ^ (((row >> 1)
 // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8
 // XCDs (workgroup L to XCD L % 8), each with its own L2.  The 1-D grid index
 // is turned into a tile index t so that XCD x walks the contiguous range of
-// tiles it owns, in the order its workgroups start; t runs down the M tiles
-// of one column of N tiles first, so the workgroups an XCD holds at once share
-// one or two weight panels (each weight panel is read into one L2 once) and
-// reuse the activation panels, which stay in the L2s and the Infinity Cache.
+// tiles it owns, in the order its workgroups start.  t runs over groups of
+// gm M tiles: down the gm M tiles of one column of N tiles, then the next
+// column, then the next group of M tiles.  The workgroups an XCD holds at
+// once then share gm activation panels and a few weight panels, whose K
+// slices they read from that XCD's L2 at about the same time.
 constexpr int kXcds = 8;
-__device__ __forceinline__ void xcd_tile(int L, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void xcd_tile(int L, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
     const int T = tiles_m * tiles_n;
     const int per = T / kXcds, rem = T % kXcds;
     const int x = L % kXcds, local = L / kXcds;
     const int t = x < rem ? x * (per + 1) + local : rem * (per + 1) + (x - rem) * per + local;
-    tn = t / tiles_m;
-    tm = t - tn * tiles_m;
+    const int grp = t / (gm * tiles_n);
+    const int m_base = grp * gm;
+    const int gsz = min(gm, tiles_m - m_base);          // the last group may be short
+    const int r = t - grp * gm * tiles_n;
+    tn = r / gsz;
+    tm = m_base + (r - tn * gsz);
 }
 
 // s_waitcnt with only a vmcnt condition (gfx9 encoding; expcnt and lgkmcnt
@@ -332,7 +337,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
     const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int M, int N, int K,
-    int group_size) {
+    int group_size, int tile_group) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M;
     constexpr int WN = BN / WAVES_N;
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const int wm0 = (wave / WAVES_N) * WM;
     const int wn0 = (wave % WAVES_N) * WN;
     int tm, tn;
-    xcd_tile(blockIdx.x, ceil_div(M, BM), ceil_div(N, BN), tm, tn);
+    xcd_tile(blockIdx.x, ceil_div(M, BM), ceil_div(N, BN), tile_group, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int KB = K / 2;
@@ -606,375 +611,100 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         if (kt + decltype(I)::value < KT) body(kt + decltype(I)::value, I);
     });
 
+    // epilogue: row by row, the wave's FN column fragments of a row one after
+    // the other, so the halves of a 128-byte output line are written by
+    // consecutive stores
     constexpr float kUnshift = ASYM ? (1.0f / 16.0f) : (1.0f / 256.0f);
+    float sw1[FN];
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
         const int gn = n0 + wn0 + b * 32 + ocol;
-        if (gn >= N) continue;
-        float sw1 = 1.0f;
-        if constexpr (MODE == kModeChan) sw1 = h2f(s_w[gn]);
+        sw1[b] = (MODE == kModeChan && gn < N) ? h2f(s_w[gn]) : 1.0f;
+    }
 #pragma unroll
-        for (int a = 0; a < FM; ++a)
+    for (int a = 0; a < FM; ++a)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int gm = m0 + wm0 + a * 32 + 8 * (r >> 2) + orow + (r & 3);
-                if (gm >= M) continue;
+        for (int r = 0; r < 16; ++r) {
+            const int gm = m0 + wm0 + a * 32 + 8 * (r >> 2) + orow + (r & 3);
+            if (gm >= M) continue;
+            const float sx = s_x[gm] * kUnshift;
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int gn = n0 + wn0 + b * 32 + ocol;
+                if (gn >= N) continue;
                 float v;
                 if constexpr (MODE == kModeChan)
-                    v = static_cast<float>(acc[a][b][r]) * sw1;
+                    v = static_cast<float>(acc[a][b][r]) * sw1[b];
                 else
                     v = facc[a][b][r];
-                Y[static_cast<size_t>(gm) * N + gn] = f2h(v * s_x[gm] * kUnshift);
+                Y[static_cast<size_t>(gm) * N + gn] = f2h(v * sx);
             }
+        }
+}
+
+// M tiles per group of the tile order (xcd_tile).  An XCD holds W tiles at
+// once (32 CUs x the workgroups one CU holds); a group of gm M tiles then
+// fetches gm activation panels (BM rows) and W / gm weight panels (BN rows)
+// per K slice into the XCD's L2, least for gm = sqrt(W BN / BM); the power of
+// two below it is taken.  Measured on MI355X for 4096x8192 -> 57344 in
+// 256x256 tiles (W = 32, gm = 4) with three weight copies rotated: groups of 4
+// took 1362-1374 us against 1384-1386 (2), 1407 (3), 1382 (6) and 1426-1478
+// us for one group of all 16; for 2048x4096 -> 6144 in 128x384 tiles the
+// formula gives 8 (fetch: 59 MB per launch with groups of 4).  A sweep
+// override may ask for another count.
+constexpr int kCusPerXcd = 32;
+int tile_group_for(int tiles_m, int BM, int BN, int wgs_per_cu) {
+    const int v = kernel_override(3);
+    int g = 1;
+    if (v >= 1) {
+        g = v;
+    } else {
+        const double want = __builtin_sqrt(static_cast<double>(kCusPerXcd) * wgs_per_cu * BN / BM);
+        while (2 * g <= want) g *= 2;
     }
+    return g < tiles_m ? g : tiles_m;
+}
+
+// workgroups of a kernel one CU holds (cached per instantiation)
+template <typename Kern>
+int wgs_per_cu(Kern kern, int threads) {
+    static int n = 0;
+    if (n == 0) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, 0) != hipSuccess || v < 1)
+            v = 1;
+        n = v;
+    }
+    return n;
 }
 
 template <int BM, int BN, int WM_, int WN_, int ST, int MODE>
 hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
     // one workgroup per output tile, in a 1-D grid (tile order: xcd_tile)
     dim3 grid(ceil_div(a.N, BN) * ceil_div(a.M, BM));
+    const int occ = wgs_per_cu(&k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE>, WM_ * WN_ * 64);
+    const int tg = tile_group_for(ceil_div(a.M, BM), BM, BN, occ);
     dim3 block(WM_ * WN_ * 64);
     if constexpr (MODE == kModeGroup) {
         if (a.group_size == BK) {
             if (a.asym)
                 k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE, true><<<grid, block, 0, stream>>>(
-                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
             else
                 k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE, true><<<grid, block, 0, stream>>>(
-                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
             return hipGetLastError();
         }
     }
     if (a.asym)
         k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
+            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
     else
         k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
+            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
     return hipGetLastError();
 }
 
-// ===========================================================================
-// Decode kernel (M <= 64 tokens): the weight stream is the whole cost, so the
-// packed weights go from HBM straight into registers, with no LDS staging.
-// A workgroup owns 16*FN output columns; its NW waves split the K tiles
-// evenly and each streams its range with loads D-1 tiles ahead (the tile
-// index is clamped, so every step issues the same loads).  A lane loads 16
-// packed bytes of one row per fragment, the row segment of its lane group
-// (lane >> 4), and unpacks them into the even-code and odd-code operands of
-// two 16x16x64 MFMA k-steps; A and B use the same order.  Activation rows
-// past M are clamped and their sums dropped.
-//
-// The workgroup first copies its rows' scales and zero points (one 32-bit
-// word per row and group: fp16 scale | zero point << 16) into LDS, and, when
-// they fit (ALDS, one row fragment), the M activation rows; the K loop then
-// reads them with LDS loads instead of one small global load per tile.  The
-// waves' partial sums (exact int32 per channel, fp32 per group) are added in
-// LDS in wave order and written by the whole workgroup.
-// ===========================================================================
-constexpr int kDecLdsMax = 160 * 1024;      // LDS of one CU
-constexpr int kDecAldsMax = 152 * 1024;     // budget for staged activations + scales
-
-template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS, bool G1>
-__global__ __launch_bounds__(NW * 64) void k_gemm_dec(
-    const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
-    const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
-    const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int M, int N, int K,
-    int group_size) {
-    static_assert(MODE == kModeChan || MODE == kModeGroup, "fp16 output modes only");
-    static_assert(D >= 2 && D <= 8, "prefetch depth");
-    static_assert(!ALDS || FM == 1, "staged activations: one row fragment");
-    static_assert(!G1 || MODE == kModeGroup, "one-tile groups: per-group mode");
-    constexpr int BN = 16 * FN;
-    constexpr int NT = NW * 64;
-    constexpr int SLOTS = FM * FN * 4;          // accumulator values per lane
-    constexpr bool SZ = (MODE == kModeGroup) || ASYM;
-    extern __shared__ __align__(16) uint8_t lds[];
-
-    const int lane = threadIdx.x & 63;
-    // wave-uniform values live in scalar registers: tile ranges, group
-    // indices and the tile part of every address
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int frow = lane & 15;
-    const int fks = lane >> 4;
-    const int n0 = blockIdx.x * BN;
-    const int KB = K / 2;
-    const int KT = K / BK;
-    const int TPG = group_size / BK;
-    const int G = K / group_size;
-    const int t0 = (KT * wave) / NW;
-    const int t1 = (KT * (wave + 1)) / NW;
-    const int GP = G + 1;          // scale-table row: an odd number of words
-    const int AP = KB + 16;        // staged activation row, padded one chunk
-    uint32_t* sz = reinterpret_cast<uint32_t*>(lds);
-    uint8_t* al = lds + (SZ ? BN * GP * 4 : 0);
-
-    // ---- stage the scale table and the activations ------------------------
-    if constexpr (SZ) {
-        for (int r = wave; r < BN; r += NW) {
-            const size_t nrow = static_cast<size_t>(min(n0 + r, N - 1)) * G;
-            for (int gb = 0; gb < G; gb += 256) {
-                uint32_t v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int g = min(gb + lane + 64 * j, G - 1);
-                    v[j] = (MODE == kModeGroup) ? s_w[nrow + g] : 0u;
-                    if constexpr (ASYM) v[j] |= static_cast<uint32_t>(h2f(z_w[nrow + g])) << 16;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (gb + lane + 64 * j < G) sz[r * GP + gb + lane + 64 * j] = v[j];
-            }
-        }
-    }
-    if constexpr (ALDS) {
-        const int CH = KB / 16;
-        for (int c = threadIdx.x; c < CH; c += NT)
-            for (int r0 = 0; r0 < M; r0 += 4) {
-                uint4 v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    v[j] = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(min(r0 + j, M - 1)) * KB + c * 16);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (r0 + j < M) *reinterpret_cast<uint4*>(al + (r0 + j) * AP + c * 16) = v[j];
-            }
-    }
-    if constexpr (SZ || ALDS) __syncthreads();
-
-    // per-lane byte offsets (32-bit) from the wave-uniform bases
-    uint32_t aoff[FM], boff[FN], zoff[FN];
-#pragma unroll
-    for (int a = 0; a < FM; ++a) {
-        const int r = min(a * 16 + frow, M - 1);
-        aoff[a] = static_cast<uint32_t>(r) * (ALDS ? AP : KB) + fks * 16;
-    }
-#pragma unroll
-    for (int b = 0; b < FN; ++b) {
-        const int r = min(n0 + b * 16 + frow, N - 1) - n0;
-        boff[b] = static_cast<uint32_t>(r) * KB + fks * 16;
-        zoff[b] = static_cast<uint32_t>(b * 16 + frow) * GP;
-    }
-    const uint8_t* wbase = Wq + static_cast<size_t>(n0) * KB;
-
-    v4i acc[FM][FN];
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b) acc[a][b] = v4i{0, 0, 0, 0};
-    constexpr int GF = (MODE == kModeGroup) ? 1 : 0;
-    float facc[GF ? FM : 1][GF ? FN : 1][4];
-#pragma unroll
-    for (int a = 0; a < (GF ? FM : 1); ++a)
-#pragma unroll
-        for (int b = 0; b < (GF ? FN : 1); ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
-
-    uint4 abuf[ALDS ? 1 : D][FM], bbuf[D][FN];
-    // a zero accumulator operand the compiler cannot fold into an inline
-    // constant (an MFMA with an inline-zero accumulator gave wrong sums)
-    v4i zc;
-    {
-        int z0;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
-        zc = v4i{z0, z0, z0, z0};
-    }
-    // issue position: tile it, clamped to the last tile of the range
-    int it = t0;
-    auto issue = [&](auto S) {
-        constexpr int SL = decltype(S)::value;
-        if constexpr (!ALDS) {
-            const uint8_t* xa = Xq + static_cast<size_t>(it) * 64;
-#pragma unroll
-            for (int a = 0; a < FM; ++a) abuf[SL][a] = *reinterpret_cast<const uint4*>(xa + aoff[a]);
-        }
-        const uint8_t* wb = wbase + static_cast<size_t>(it) * 64;
-#pragma unroll
-        for (int b = 0; b < FN; ++b) bbuf[SL][b] = *reinterpret_cast<const uint4*>(wb + boff[b]);
-        if (it + 1 < t1) ++it;
-    };
-    // compute position: group cg of tile t and its place cr inside the group
-    int cg = t0 / TPG, cr = t0 - (t0 / TPG) * TPG;
-    auto compute = [&](int t, auto S) {
-        constexpr int SL = decltype(S)::value;
-        v4i aev[FM], aod[FM], bev[FN], bod[FN];
-#pragma unroll
-        for (int a = 0; a < FM; ++a) {
-            uint4 w;
-            if constexpr (ALDS)
-                w = *reinterpret_cast<const uint4*>(al + aoff[a] + t * 64);
-            else
-                w = abuf[SL][a];
-            uint4 ev, od;
-            unpack_signed16(w, ev, od);
-            aev[a] = v4i{static_cast<int>(ev.x), static_cast<int>(ev.y), static_cast<int>(ev.z), static_cast<int>(ev.w)};
-            aod[a] = v4i{static_cast<int>(od.x), static_cast<int>(od.y), static_cast<int>(od.z), static_cast<int>(od.w)};
-        }
-        uint32_t szv[FN];
-#pragma unroll
-        for (int b = 0; b < FN; ++b) {
-            if constexpr (SZ) szv[b] = sz[zoff[b] + (G1 ? t : cg)];
-            uint4 ev, od;
-            if constexpr (ASYM) {
-                const uint32_t z = szv[b] >> 16;
-                unpack_asym(bbuf[SL][b], 0x80808080u - z * 0x01010101u, ev, od);
-            } else {
-                unpack_signed16(bbuf[SL][b], ev, od);
-            }
-            bev[b] = v4i{static_cast<int>(ev.x), static_cast<int>(ev.y), static_cast<int>(ev.z), static_cast<int>(ev.w)};
-            bod[b] = v4i{static_cast<int>(od.x), static_cast<int>(od.y), static_cast<int>(od.z), static_cast<int>(od.w)};
-        }
-        if constexpr (G1) {
-            // one tile per weight group: the group's sums start from a zero
-            // register operand and are folded into fp32 at once
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const float sw = h2f(static_cast<uint16_t>(szv[b] & 0xFFFFu));
-#pragma unroll
-                for (int a = 0; a < FM; ++a) {
-                    v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aev[a], bev[b], zc, 0, 0, 0);
-                    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod[a], bod[b], p, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        facc[a][b][r] = fmaf(static_cast<float>(p[r]), sw, facc[a][b][r]);
-                }
-            }
-            return;
-        }
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aev[a], bev[b], acc[a][b], 0, 0, 0);
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod[a], bod[b], acc[a][b], 0, 0, 0);
-        const bool group_end = (++cr == TPG);
-        if constexpr (MODE == kModeGroup) {
-            // end of a weight group, or of this wave's range inside one
-            if (group_end || t + 1 == t1) {
-#pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const float sw = h2f(static_cast<uint16_t>(szv[b] & 0xFFFFu));
-#pragma unroll
-                    for (int a = 0; a < FM; ++a)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            facc[a][b][r] = fmaf(static_cast<float>(acc[a][b][r]), sw, facc[a][b][r]);
-                            acc[a][b][r] = 0;
-                        }
-                }
-            }
-        }
-        if (group_end) {
-            cr = 0;
-            ++cg;
-        }
-    };
-
-    if (t0 < t1) {
-        static_for<0, D - 1>([&](auto U) { issue(U); });
-        for (int t = t0; t < t1; t += D) {
-            static_for<0, D>([&](auto U) {
-                constexpr int u = decltype(U)::value;
-                issue(std::integral_constant<int, (u + D - 1) % D>{});
-                if (t + u < t1) compute(t + u, std::integral_constant<int, u>{});
-            });
-        }
-    }
-
-    // ---- add the waves' partial sums in LDS, in wave order -------------------
-    if constexpr (SZ || ALDS) __syncthreads();      // the staged data is dead
-    float* red = reinterpret_cast<float*>(lds);     // [NW][SLOTS][64]
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = (a * FN + b) * 4 + r;
-                red[(wave * SLOTS + i) * 64 + lane] = (MODE == kModeGroup) ? facc[GF ? a : 0][GF ? b : 0][r]
-                                                                           : __int_as_float(acc[a][b][r]);
-            }
-    __syncthreads();
-    constexpr float kUnshift = ASYM ? (1.0f / 16.0f) : (1.0f / 256.0f);
-    for (int sl = threadIdx.x; sl < SLOTS * 64; sl += NT) {
-        const int i = sl >> 6;
-        const int l = sl & 63;
-        const int a = i / (FN * 4);
-        const int b = (i >> 2) % FN;
-        const int r = i & 3;
-        const int gm = a * 16 + 4 * (l >> 4) + r;
-        const int gn = n0 + b * 16 + (l & 15);
-        if (gm >= M || gn >= N) continue;
-        float v;
-        if constexpr (MODE == kModeGroup) {
-            v = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) v += red[(w * SLOTS + i) * 64 + l];
-        } else {
-            int sum = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) sum += __float_as_int(red[(w * SLOTS + i) * 64 + l]);
-            v = static_cast<float>(sum) * h2f(s_w[gn]);
-        }
-        Y[static_cast<size_t>(gm) * N + gn] = f2h(v * s_x[gm] * kUnshift);
-    }
-}
-
-template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS, bool G1>
-hipError_t launch_dec_g(const GemmArgs& a, size_t lds, hipStream_t stream) {
-    auto* kern = &k_gemm_dec<FM, FN, NW, D, ASYM, MODE, ALDS, G1>;
-    if (lds > 64 * 1024) {
-        // more than the default dynamic LDS limit: raise it once per device
-        static bool raised[64] = {};
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        if (dev < 0 || dev >= 64 || !raised[dev]) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
-            if (e != hipSuccess) return e;
-            if (dev >= 0 && dev < 64) raised[dev] = true;
-        }
-    }
-    kern<<<dim3(ceil_div(a.N, 16 * FN)), dim3(NW * 64), lds, stream>>>(
-        a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size);
-    return hipGetLastError();
-}
-
-template <int FM, int FN, int NW, int D, bool ASYM, int MODE, bool ALDS>
-hipError_t launch_dec_k(const GemmArgs& a, size_t lds, hipStream_t stream) {
-    if constexpr (MODE == kModeGroup) {
-        if (a.group_size == BK) return launch_dec_g<FM, FN, NW, D, ASYM, MODE, ALDS, true>(a, lds, stream);
-    }
-    return launch_dec_g<FM, FN, NW, D, ASYM, MODE, ALDS, false>(a, lds, stream);
-}
-
-template <int FM, int FN, int NW, int D, bool ASYM, int MODE>
-hipError_t launch_dec_a(const GemmArgs& a, hipStream_t stream) {
-    constexpr int BN = 16 * FN;
-    const int G = a.K / a.group_size;
-    const bool sz = (MODE == kModeGroup) || ASYM;
-    const size_t szb = sz ? static_cast<size_t>(BN) * (G + 1) * 4 : 0;
-    const size_t alb = static_cast<size_t>(a.M) * (a.K / 2 + 16);
-    const size_t red = static_cast<size_t>(NW) * FM * FN * 4 * 64 * 4;
-    if constexpr (FM == 1) {
-        if (szb + alb <= static_cast<size_t>(kDecAldsMax))
-            return launch_dec_k<FM, FN, NW, D, ASYM, MODE, true>(a, szb + alb > red ? szb + alb : red,
-                                                                 stream);
-    }
-    return launch_dec_k<FM, FN, NW, D, ASYM, MODE, false>(a, szb > red ? szb : red, stream);
-}
-
-template <int FM, int FN, int NW, int D, int MODE>
-hipError_t launch_dec(const GemmArgs& a, hipStream_t stream) {
-    return a.asym ? launch_dec_a<FM, FN, NW, D, true, MODE>(a, stream)
-                  : launch_dec_a<FM, FN, NW, D, false, MODE>(a, stream);
-}
 
 template <int BM, int BN, int WM_, int WN_, int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t stream) {
@@ -1029,7 +759,8 @@ template <int MODE> hipError_t dl128x256_2x4_s4(const GemmArgs& a, hipStream_t s
 template <int MODE> hipError_t r16_256x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<256, 128, 2, 4, MODE>(a, s); }
 template <int MODE> hipError_t r16_128x128_2x4(const GemmArgs& a, hipStream_t s) { return launch_mode<128, 128, 2, 4, MODE>(a, s); }
 
-// Prefill configurations (M > 64).  dl: direct-to-LDS 32x32x32 kernel;
+// Prefill configurations (M > 64; decode kernels: gemm_decode.hip).
+// dl: direct-to-LDS 32x32x32 kernel;
 // r16: register-staged unpack-to-LDS kernel on 16x16x64.
 const KernelCfg kTiles[] = {
     W4A4_CFG_CHAN("k_gemm_dl<256x256, waves 2x4, 4 stages>", dl256x256_2x4_s4),
@@ -1048,31 +779,13 @@ const KernelCfg kTiles[] = {
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-// Decode configurations (M <= 64), per row-fragment count FM = 1, 2, 4:
-// 16*FN columns per workgroup, NW waves splitting K, prefetch depth D.
-template <int FM, int FN, int NW, int D>
-struct Dec {
-    template <int MODE>
-    static hipError_t run(const GemmArgs& a, hipStream_t s) { return launch_dec<FM, FN, NW, D, MODE>(a, s); }
-};
-#define W4A4_DEC(FM, FN, NW, D) \
-    KernelCfg{"k_gemm_dec<FM " #FM ", FN " #FN ", waves " #NW ", depth " #D ">", \
-              &Dec<FM, FN, NW, D>::run<kModeChan>, &Dec<FM, FN, NW, D>::run<kModeGroup>}
-constexpr int kNumDec = 4;
-const KernelCfg kDec[3][kNumDec] = {
-    {W4A4_DEC(1, 1, 16, 4), W4A4_DEC(1, 2, 16, 4), W4A4_DEC(1, 1, 8, 6), W4A4_DEC(1, 2, 8, 6)},
-    {W4A4_DEC(2, 1, 16, 4), W4A4_DEC(2, 2, 8, 4), W4A4_DEC(2, 1, 8, 4), W4A4_DEC(2, 2, 8, 3)},
-    {W4A4_DEC(4, 1, 8, 3), W4A4_DEC(4, 2, 8, 3), W4A4_DEC(4, 1, 8, 2), W4A4_DEC(4, 2, 8, 2)},
-};
-#undef W4A4_DEC
 #undef W4A4_CFG
 #undef W4A4_CFG_CHAN
 
 const KernelCfg kI32{"k_gemm_w4a4<64x64, waves 2x2, int32 out>", nullptr, nullptr};
 
 // Selection override for tests and sweeps (w4a4_set_kernel_override): an
-// index into the prefill table or the decode variants, -1 or out of range =
-// automatic.
+// index into the prefill table, -1 or out of range = automatic.
 int override_index(int which, int n) {
     const int v = kernel_override(which);
     return (v >= 0 && v < n) ? v : -1;
@@ -1081,23 +794,6 @@ int override_index(int which, int n) {
 const KernelCfg& choose(const GemmArgs& a) {
     const bool grouped = (a.K / a.group_size) > 1;
     const int cus = device_cu_count();
-    if (a.M <= 64) {
-        const int fi = a.M <= 16 ? 0 : (a.M <= 32 ? 1 : 2);
-        int v = override_index(1, kNumDec);
-        if (v < 0) {
-            // measured on MI355X: one 16-column fragment per workgroup while
-            // two workgroups fit a CU, two once the staged activations fill
-            // the LDS (or for two and four row fragments) and the grid still
-            // covers every CU
-            bool wide = ceil_div(a.N, 32) >= cus;
-            if (fi == 0) {
-                const size_t staged = static_cast<size_t>(a.M) * (a.K / 2 + 16);
-                wide = wide && staged > 64 * 1024;
-            }
-            v = wide ? 1 : 0;
-        }
-        return kDec[fi][v];
-    }
     int t = override_index(0, kNumTiles);
     if (t < 0 || (grouped && kTiles[t].group == nullptr)) {
         // measured on MI355X: direct-to-LDS 256x256 tiles with 16 waves when
@@ -1130,7 +826,6 @@ const KernelCfg& choose(const GemmArgs& a) {
 }  // namespace
 
 int gemm_num_tile_configs() { return kNumTiles; }
-int gemm_num_decode_configs() { return kNumDec; }
 
 size_t gemm_workspace_bytes(int M, int N, int K, int group_size) {
     (void)M;
@@ -1142,6 +837,7 @@ size_t gemm_workspace_bytes(int M, int N, int K, int group_size) {
 
 const char* gemm_kernel_name(const GemmArgs& a, bool i32_out) {
     if (i32_out) return kI32.name;
+    if (a.M <= kDecodeMaxM) return gemm_decode_kernel_name(a);
     return choose(a).name;
 }
 
@@ -1151,6 +847,7 @@ hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_byte
     (void)ws_bytes;
     if (a.M == 0) return hipSuccess;
     if (i32_out) return launch_mode<64, 64, 2, 2, kModeI32>(a, stream);
+    if (a.M <= kDecodeMaxM) return gemm_decode_launch(a, stream);
     const bool grouped = (a.K / a.group_size) > 1;
     const KernelCfg& k = choose(a);
     return grouped ? k.group(a, stream) : k.chan(a, stream);

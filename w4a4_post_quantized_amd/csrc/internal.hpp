@@ -10,8 +10,9 @@
 namespace w4a4 {
 
 // ---- kernel selection overrides (w4a4_set_kernel_override) -----------------
-// which: 0 prefill GEMM tile, 1 decode GEMM variant, 2 fp6 tile; -1 = automatic
-constexpr int kOverrideKinds = 3;
+// which: 0 prefill GEMM tile, 1 decode GEMM variant, 2 fp6 tile, 3 M tiles per
+// group of the prefill GEMM's tile order; -1 = automatic
+constexpr int kOverrideKinds = 4;
 int kernel_override(int which);
 int gemm_num_tile_configs();
 int gemm_num_decode_configs();
@@ -60,6 +61,11 @@ size_t gemm_workspace_bytes(int M, int N, int K, int group_size);
 const char* gemm_kernel_name(const GemmArgs& a, bool i32_out);
 hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+// ---- decode GEMM (gemm_decode.hip): batches of at most kDecodeMaxM tokens ----
+constexpr int kDecodeMaxM = 64;
+const char* gemm_decode_kernel_name(const GemmArgs& a);
+hipError_t gemm_decode_launch(const GemmArgs& a, hipStream_t stream);
 
 // ---- single-kernel decode layer (linear_decode.hip) --------------------------
 // ---- INT4 GEMM on the fp6 matrix pipe (gemm_f6.hip) ------------------------
