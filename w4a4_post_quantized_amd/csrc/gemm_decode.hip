@@ -373,16 +373,26 @@ const KernelCfg& choose_dec(const GemmArgs& a) {
     const int o = kernel_override(1);
     int v = (o >= 0 && o < kNumDec) ? o : -1;
     if (v < 0) {
-        // measured on MI355X: one 16-column fragment per workgroup while
-        // two workgroups fit a CU, two once the staged activations fill
-        // the LDS (or for two and four row fragments) and the grid still
-        // covers every CU
+        // measured on MI355X (28672 -> 8192, group 128, weight copies
+        // rotated): two 16-column fragments per workgroup once the staged
+        // activations fill the LDS (or for two and four row fragments) and
+        // the grid still covers every CU (8 tokens: 31.8-32.0 us against
+        // 35.7-37.2 us); one fragment otherwise, with 8 waves and 6 tiles in
+        // flight for one row fragment (1 token: 27.0-27.1 us against
+        // 28.5-30.2 us with 16 waves and 4 tiles) and 16 waves for more; for
+        // four row fragments 2 tiles in flight (64 tokens: 56.7 against
+        // 57.5 us with 3)
         bool wide = ceil_div(a.N, 32) >= cus;
         if (fi == 0) {
             const size_t staged = static_cast<size_t>(a.M) * (a.K / 2 + 16);
             wide = wide && staged > 64 * 1024;
         }
-        v = wide ? 1 : 0;
+        if (fi == 0)
+            v = wide ? 1 : 2;
+        else if (fi == 2)
+            v = wide ? 3 : 0;
+        else
+            v = wide ? 1 : 0;
     }
     return kDec[fi][v];
 }
