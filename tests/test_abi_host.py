@@ -90,12 +90,15 @@ def test_transform_quant_validation():
     assert call(n1=3, n2=5) == -2                     # K % 16
     assert call(a=0.0) == -1 and call(a=1.5) == -1
     assert call(c=MISALIGNED) == -3
-    need = L.w4a4_transform_quant_workspace_bytes(4, 16, 16, 1)
+    # with c, (64, 128) runs the split path and needs a workspace
+    need = L.w4a4_transform_quant_workspace_bytes(4, 64, 128, 1)
     assert need > 0
-    assert call(c=FAKE, wsb=need - 1) == -4
-    assert call(c=FAKE, ws=None) == -4
-    # without c the (16, 16) shape runs fused and needs no workspace
+    assert call(n1=64, n2=128, c=FAKE, wsb=need - 1) == -4
+    assert call(n1=64, n2=128, c=FAKE, ws=None) == -4
+    assert L.w4a4_transform_quant_workspace_bytes(4, 64, 128, 0) == 0
+    # (16, 16) runs the wave kernel, with or without c, and needs no workspace
     assert L.w4a4_transform_quant_workspace_bytes(4, 16, 16, 0) == 0
+    assert L.w4a4_transform_quant_workspace_bytes(4, 16, 16, 1) == 0
     assert call(M=0, X=None) == 0
 
 

@@ -61,14 +61,17 @@ FACTORS = [(16, 16), (32, 32), (64, 64), (64, 128), (112, 128), (224, 128), (8, 
            (160, 128), (256, 128)]
 
 
-@pytest.mark.parametrize("n1,n2", FACTORS)
-def test_transform_accuracy(n1, n2):
+@pytest.mark.parametrize("n1,n2,with_c", [(a, b, False) for a, b in FACTORS] +
+                         [(16, 16, True), (32, 64, True), (64, 64, True), (64, 128, True)])
+def test_transform_accuracy(n1, n2, with_c):
     """fp32 Z against the fp64 oracle, in code units of the token's scale."""
-    log(f"transform accuracy ({n1},{n2})")
+    log(f"transform accuracy ({n1},{n2}) c={with_c}")
     wl = custom_workload(M=19, n1=n1, n2=n2, N=16, outliers=(3, n1 * n2 - 5), pivot=100.0, seed=n1)
     inp = WL.make_inputs(wl, with_weights=False)
-    Zg = W().transform(to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"])).cpu().numpy()
-    Zo = O.kron_transform(inp["X"], inp["P1"], inp["P2"])
+    c = WL.make_channel_scale(wl.K, seed=n1 + n2) if with_c else None
+    Zg = W().transform(to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"]),
+                       None if c is None else to_dev(c)).cpu().numpy()
+    Zo = O.kron_transform(inp["X"], inp["P1"], inp["P2"], c)
     s = O.act_scale(Zo)
     err = np.abs(Zg - Zo) / s[:, None]
     log(f"  max error {err.max():.3e} code units")
@@ -89,11 +92,20 @@ def test_transform_quant_parity(n1, n2, M):
     np.testing.assert_allclose(sx, r["s_x"], rtol=2e-6, atol=0)
 
 
-def test_transform_quant_channel_scale_and_clip():
-    log("transform_quant with diag(c) and alpha_a = 0.6")
-    wl = custom_workload(M=40, n1=32, n2=64, N=16, outliers=(5,), pivot=30.0, seed=5)
+# diag(c) on every activation path: the wave-per-token kernel (n1, n2 <= 64;
+# M = 3000 gives the (64, 64) waves several tokens each, and the scaled c
+# vectors move the kernel's power-of-two prescale of c far from 1), and the
+# split kernels (n2 = 128, n1 > 128)
+@pytest.mark.parametrize("n1,n2,M,cmul", [(16, 16, 37, 1.0), (32, 32, 300, 1.0), (16, 64, 9, 1.0),
+                                          (32, 64, 40, 1.0), (64, 64, 130, 1.0),
+                                          (64, 64, 3000, 1.0), (64, 64, 50, 300.0),
+                                          (32, 32, 20, 1.0 / 512), (64, 128, 33, 1.0),
+                                          (224, 128, 5, 1.0)])
+def test_transform_quant_channel_scale_and_clip(n1, n2, M, cmul):
+    log(f"transform_quant with diag(c) x {cmul} and alpha_a = 0.6, ({n1},{n2}) M={M}")
+    wl = custom_workload(M=M, n1=n1, n2=n2, N=16, outliers=(5,), pivot=30.0, seed=5 + n1 + M)
     inp = WL.make_inputs(wl, with_weights=False)
-    c = WL.make_channel_scale(wl.K, seed=3)
+    c = (WL.make_channel_scale(wl.K, seed=3 + n2) * np.float32(cmul)).astype(np.float32)
     r = O.transform_quant(inp["X"], inp["P1"], inp["P2"], c=c, alpha_a=0.6)
     assert (r["q"] == -8).any() or (r["q"] == 7).any()
     Xq, sx = gpu_act(inp, c=c, alpha=0.6)
@@ -291,9 +303,10 @@ def test_linear_small_shapes(wl):
     _layer_parity(prepared(wl))
 
 
-def test_linear_with_channel_scale_and_clip():
-    log("linear with diag(c), alpha_a 0.8")
-    wl = custom_workload(M=70, n1=16, n2=32, N=136, group_size=256, asym=True, seed=21)
+@pytest.mark.parametrize("n1,n2,M,N", [(16, 32, 70, 136), (64, 64, 200, 264)])
+def test_linear_with_channel_scale_and_clip(n1, n2, M, N):
+    log(f"linear with diag(c), alpha_a 0.8, ({n1},{n2}) M={M} N={N}")
+    wl = custom_workload(M=M, n1=n1, n2=n2, N=N, group_size=256, asym=True, seed=21)
     inp = WL.make_inputs(wl)
     c = WL.make_channel_scale(wl.K, seed=4)
     inp["Wt"] = O.merge_weights(inp["W"], inp["P1"], inp["P2"], c)

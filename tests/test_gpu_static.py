@@ -35,8 +35,9 @@ def static_inputs(wl, per_channel, ratio=0.8, c=None, M_cal=48):
     return inp
 
 
-# every activation path: wave (n1, n2 <= 64), fused (n2 = 128), column-block
-# (n1 > 128), split (other shapes, or diag(c))
+# every activation path: wave (n1, n2 <= 64, with or without diag(c)),
+# fused (n2 = 128), column-block (n1 > 128), split (other shapes, and diag(c)
+# with n2 = 128 or n1 > 128)
 SHAPES = [(16, 16, 37), (64, 64, 130), (32, 64, 9), (64, 128, 65), (112, 128, 9),
           (224, 128, 3), (224, 128, 37), (128, 256, 2), (8, 2, 5)]
 
@@ -62,9 +63,10 @@ def test_transform_quant_static_parity(n1, n2, M, per_channel):
 
 
 @pytest.mark.parametrize("per_channel", [False, True], ids=["tensor", "channel"])
-def test_transform_quant_static_with_channel_scale(per_channel):
-    log(f"transform_quant_static with diag(c), per_channel={per_channel}")
-    wl = custom_workload(M=40, n1=32, n2=64, N=0, outliers=(5,), pivot=30.0, seed=5)
+@pytest.mark.parametrize("n1,n2,M", [(32, 64, 40), (64, 64, 2100), (16, 16, 11), (64, 128, 20)])
+def test_transform_quant_static_with_channel_scale(n1, n2, M, per_channel):
+    log(f"transform_quant_static with diag(c), ({n1},{n2}) M={M} per_channel={per_channel}")
+    wl = custom_workload(M=M, n1=n1, n2=n2, N=0, outliers=(5,), pivot=30.0, seed=5)
     c = WL.make_channel_scale(wl.K, seed=3)
     inp = static_inputs(wl, per_channel, c=c)
     st = inp["steps"]

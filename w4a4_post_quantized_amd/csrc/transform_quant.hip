@@ -481,9 +481,12 @@ hipError_t launch_fused_k(const uint16_t* X, int M, const float* P1, const float
     return hipGetLastError();
 }
 
+// c: unused (the token-batched kernel has no diag(c); fused_for does not
+// offer it for a layer with c)
 template <int N1, int N2>
-hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
-                        uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* P2, const float* c,
+                        ActQuant aq, uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+    (void)c;
     if (aq.steps != nullptr && aq.per_channel && Xq != nullptr)
         return launch_fused_k<N1, N2, true>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
     return launch_fused_k<N1, N2, false>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
@@ -520,10 +523,16 @@ struct WaveCfg {
     static_assert(QB % 16 == 0, "whole 16-byte chunks per token");
 };
 
-template <int N1, int N2, bool PC>
+// HC: the per-channel scale diag(c) multiplies the activations before the
+// transform.  x ⊙ c is no longer an fp16 number, so the stage-1 A operand is
+// split like the factors: c is prescaled by a power of two (|c'| < 1, so
+// |x c'| stays in fp16's range), x·c' is formed in fp32 and split into fp16
+// hi + lo, and stage 1 takes hi·P2hi + hi·P2lo + lo·P2hi.
+template <int N1, int N2, bool PC, bool HC>
 __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_t* __restrict__ X, int M,
                                                                 const float* __restrict__ P1,
-                                                                const float* __restrict__ P2, ActQuant aq,
+                                                                const float* __restrict__ P2,
+                                                                const float* __restrict__ cvec, ActQuant aq,
                                                                 uint8_t* __restrict__ Xq,
                                                                 float* __restrict__ s_x,
                                                                 float* __restrict__ Zout) {
@@ -535,11 +544,13 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
     __shared__ __align__(16) _Float16 p1hi[C::P1F];
     __shared__ __align__(16) _Float16 p1lo[C::P1F];
     __shared__ __align__(16) uint8_t qbuf[C::NW][C::QB];
-    __shared__ float red[2 * C::NW];
+    __shared__ float red[3 * C::NW];
     // static per-channel steps: their reciprocals, rows of n2 padded by 4 so
     // the 16 rows one quarter-wave reads fall in distinct banks
     constexpr int SROW = N2 + 4;
     __shared__ __align__(16) float rstep[PC ? N1 * SROW : 4];
+    // diag(c), prescaled, in the k order of the token
+    __shared__ __align__(16) float cs[HC ? K : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -612,22 +623,42 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
 #pragma unroll
     for (int i = 0; i < SLN; ++i)
         stv[i] = reinterpret_cast<const v4f*>(aq.steps)[min(tid + i * NT, K / 4 - 1)];
+    constexpr int CLN = HC ? (K / 4 + NT - 1) / NT : 0;
+    v4f cv[CLN > 0 ? CLN : 1];
+    float m3 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CLN; ++i) {
+        cv[i] = reinterpret_cast<const v4f*>(cvec)[min(tid + i * NT, K / 4 - 1)];
+        m3 = fmaxf(m3, fmaxf(fmaxf(fabsf(cv[i][0]), fabsf(cv[i][1])), fmaxf(fabsf(cv[i][2]), fabsf(cv[i][3]))));
+    }
     m1 = wave_max(m1);
     m2 = wave_max(m2);
+    if constexpr (HC) m3 = wave_max(m3);
     if (lane == 0) {
         red[wave] = m1;
         red[C::NW + wave] = m2;
+        if constexpr (HC) red[2 * C::NW + wave] = m3;
     }
     __syncthreads();
     m1 = 0.0f;
     m2 = 0.0f;
+    m3 = 0.0f;
 #pragma unroll
     for (int w = 0; w < C::NW; ++w) {
         m1 = fmaxf(m1, red[w]);
         m2 = fmaxf(m2, red[C::NW + w]);
+        if constexpr (HC) m3 = fmaxf(m3, red[2 * C::NW + w]);
     }
     const int e1 = m1 > 0.0f ? -ilog2f(m1) : 0;
     const int e2 = m2 > 0.0f ? -ilog2f(m2) : 0;
+    const int ec = m3 > 0.0f ? -ilog2f(m3) - 1 : 0;   // max|c 2^ec| < 1
+#pragma unroll
+    for (int i = 0; i < CLN; ++i) {
+        const int c4 = tid + i * NT;
+        if (c4 < K / 4)
+            *reinterpret_cast<v4f*>(cs + 4 * c4) =
+                v4f{ldexpf(cv[i][0], ec), ldexpf(cv[i][1], ec), ldexpf(cv[i][2], ec), ldexpf(cv[i][3], ec)};
+    }
 #pragma unroll
     for (int i = 0; i < L2N; ++i) {
         const int idx = tid + i * NT;
@@ -673,6 +704,29 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
         int fo = 0;
         asm volatile("" : "+s"(fo));
 
+        // with diag(c): the A operand x ⊙ c' as fp16 hi + lo (x fp16, c' fp32)
+        v8h xlo[HC ? C::RB : 1][HC ? C::KS1 : 1];
+        if constexpr (HC) {
+#pragma unroll
+            for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < C::KS1; ++ks) {
+                    if (32 * ks + 8 * g >= N2) {
+                        xlo[rb][ks] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+                        continue;
+                    }
+                    const float* cp = cs + (16 * rb + li) * N2 + 32 * ks + 8 * g + fo;
+                    const v4f c0 = *reinterpret_cast<const v4f*>(cp);
+                    const v4f c1 = *reinterpret_cast<const v4f*>(cp + 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float v = static_cast<float>(xa[rb][ks][e]) * (e < 4 ? c0[e] : c1[e - 4]);
+                        const F16Pair hl = split_f16(v);
+                        xa[rb][ks][e] = hl.hi;
+                        xlo[rb][ks][e] = hl.lo;
+                    }
+                }
+        }
         // stage 1: T = X̄ · P2'
         v4f T[C::RB][C::CB];
 #pragma unroll
@@ -686,6 +740,8 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
                 const v8h bl = *reinterpret_cast<const v8h*>(p2lo + off);
 #pragma unroll
                 for (int rb = 0; rb < C::RB; ++rb) {
+                    if constexpr (HC)
+                        T[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xlo[rb][ks], bh, T[rb][cb], 0, 0, 0);
                     T[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rb][ks], bh, T[rb][cb], 0, 0, 0);
                     T[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[rb][ks], bl, T[rb][cb], 0, 0, 0);
                 }
@@ -740,7 +796,7 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
         // lane (g, li) of tile (ob, cb) holds 2^-unscale * Z[16 ob + li][16 cb + 4 g + r];
         // the power of two is folded into the scale and the quantizer's
         // multiplier (exact, so the codes are those of the unscaled values)
-        const int unscale = -(e1 + e2 + et);
+        const int unscale = -(e1 + e2 + et + ec);
         float zmax = 0.0f;
 #pragma unroll
         for (int ob = 0; ob < C::RB; ++ob)
@@ -819,16 +875,16 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
     if (m < M) token(m);
 }
 
-template <int N1, int N2, bool PC>
-hipError_t launch_wave_k(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
-                         uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+template <int N1, int N2, bool PC, bool HC>
+hipError_t launch_wave_k(const uint16_t* X, int M, const float* P1, const float* P2, const float* c,
+                         ActQuant aq, uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
     using C = WaveCfg<N1, N2>;
     // persistent grid: as many workgroups as fit on the device at once, so
     // the fragment setup is paid once per resident workgroup
     static int per_cu = 0;
     if (per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_wave<N1, N2, PC>, C::NT, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_tq_wave<N1, N2, PC, HC>, C::NT, 0) !=
                 hipSuccess || n < 1)
             n = 1;
         per_cu = n;
@@ -836,25 +892,29 @@ hipError_t launch_wave_k(const uint16_t* X, int M, const float* P1, const float*
     const int units = (M + C::NW - 1) / C::NW;
     const int cap = per_cu * device_cu_count();
     const int grid = units < cap ? units : cap;
-    k_tq_wave<N1, N2, PC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, aq, Xq, s_x, Z);
+    k_tq_wave<N1, N2, PC, HC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, c, aq, Xq, s_x, Z);
     return hipGetLastError();
 }
 
 template <int N1, int N2>
-hipError_t launch_wave(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
-                       uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
-    if (aq.steps != nullptr && aq.per_channel && Xq != nullptr)
-        return launch_wave_k<N1, N2, true>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
-    return launch_wave_k<N1, N2, false>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
+hipError_t launch_wave(const uint16_t* X, int M, const float* P1, const float* P2, const float* c,
+                       ActQuant aq, uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+    const bool pc = aq.steps != nullptr && aq.per_channel && Xq != nullptr;
+    if (c != nullptr)
+        return pc ? launch_wave_k<N1, N2, true, true>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream)
+                  : launch_wave_k<N1, N2, false, true>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream);
+    return pc ? launch_wave_k<N1, N2, true, false>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream)
+              : launch_wave_k<N1, N2, false, false>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream);
 }
 
-using FusedFn = hipError_t (*)(const uint16_t*, int, const float*, const float*, ActQuant, uint8_t*,
-                               float*, float*, hipStream_t);
+using FusedFn = hipError_t (*)(const uint16_t*, int, const float*, const float*, const float*,
+                               ActQuant, uint8_t*, float*, float*, hipStream_t);
 
-// (n1, n2) pairs with a fused (or wave-per-token) instantiation
-FusedFn fused_for(int n1, int n2) {
+// (n1, n2) pairs with a fused (or wave-per-token) instantiation; with
+// diag(c) only the wave-per-token kernels apply
+FusedFn fused_for(int n1, int n2, bool has_c) {
 #define W4A4_FUSED(a, b) \
-    if (n1 == a && n2 == b) return &launch_fused<a, b>;
+    if (n1 == a && n2 == b) return has_c ? nullptr : &launch_fused<a, b>;
 #define W4A4_WAVE(a, b) \
     if (n1 == a && n2 == b) return &launch_wave<a, b>;
     W4A4_WAVE(16, 16)
@@ -1179,7 +1239,7 @@ const ColsFns* cols_for(int n1, int n2) {
 
 TqPath tq_select_path(int M, int n1, int n2, bool has_c) {
     (void)M;
-    if (!has_c && fused_for(n1, n2) != nullptr) return TqPath::Fused;
+    if (fused_for(n1, n2, has_c) != nullptr) return TqPath::Fused;
     if (!has_c && cols_for(n1, n2) != nullptr) return TqPath::Cols;
     return TqPath::Split;
 }
@@ -1204,8 +1264,8 @@ hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
     if (M == 0) return hipSuccess;
     const TqPath path = tq_select_path(M, n1, n2, c != nullptr);
     if (path == TqPath::Fused)
-        return fused_for(n1, n2)(X, M, P1, P2, aq, quantize ? Xq : nullptr, s_x,
-                                 quantize ? nullptr : Z, stream);
+        return fused_for(n1, n2, c != nullptr)(X, M, P1, P2, c, aq, quantize ? Xq : nullptr, s_x,
+                                               quantize ? nullptr : Z, stream);
     if (path == TqPath::Cols)
         return cols_for(n1, n2)->launch(X, M, P1, P2, aq, Xq, s_x, quantize ? nullptr : Z, ws,
                                         stream);
