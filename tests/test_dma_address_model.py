@@ -12,8 +12,9 @@ form (tile base + K tile, plus the lane offset), for every prefill tile shape
 with symmetric weights, ragged M and N, every workgroup, wave, lane, copy and
 K tile, and with operand buffers whose low address word is >= 2^31.  It
 checks that the zero-extended assembly reproduces every pointer, and that a
-sign-extended low half (the form that once faulted the GPU) would not.
-Nothing here runs on a GPU.
+sign-extended low half (the form that once faulted the GPU) would not.  A
+second model covers the 4-byte copies of the weight scales and zero points
+that the one-tile-group kernels stage per K tile.  Nothing here runs on a GPU.
 """
 import numpy as np
 import pytest
@@ -100,3 +101,57 @@ def test_assembly_on_edge_bases():
             assert assemble(base, sign_extend_low=True) == base | 0xFFFFFFFF_00000000
         else:
             assert assemble(base, sign_extend_low=True) == base
+
+
+# (BM, BN, WAVES_M, WAVES_N) of the k_gemm_dl configurations that run groups
+# of one K tile (128 codes)
+GROUP_TILES = [(128, 128, 2, 2), (256, 128, 4, 2), (128, 256, 2, 4)]
+SZSLOT = 256
+
+
+@pytest.mark.parametrize("BM,BN,WM,WN", GROUP_TILES)
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("N,K", [(520, 1024), (136, 384), (1, 128), (28672, 4096), (77, 14336)])
+def test_scale_copies_address_every_group_scale(BM, BN, WM, WN, asym, N, K):
+    """One-tile-group scale copies: wave w copies, per tile kt, the aligned
+    4-byte word holding element row * G + kt of the scale (or zero-point)
+    array for the 64 rows of its item into its LDS slot; the reading lane
+    takes the half that the element's parity selects.  Every copied word
+    lies inside the array rounded up to whole words, the offset fits 32 bits,
+    the slots of the waves do not overlap, and every (row, group) a B
+    fragment reads is the element it needs."""
+    NW = WM * WN
+    G = K // 128
+    KT = G
+    kinds = 2 if asym else 1
+    SZI = kinds * BN // 64
+    assert SZI <= NW
+    for n0 in range(0, N, BN):
+        for kt in sorted({0, 1, KT - 1, KT // 2, KT + 1}):
+            kc = min(kt, KT - 1)
+            lds = {}
+            for w in range(NW):
+                it = w % SZI
+                kind = 1 if it >= BN // 64 else 0
+                lane = np.arange(64)
+                row = np.minimum(n0 + (it % (BN // 64)) * 64 + lane, N - 1)
+                e0 = row * G
+                off = 2 * ((e0 + kc) & ~1)
+                assert off.max() < 1 << 32
+                assert off.min() >= 0 and (off + 4).max() <= 2 * (N * G + (N * G) % 2)
+                assert (off % 4 == 0).all()
+                slot = w * SZSLOT + 4 * lane
+                assert slot.max() + 4 <= (w + 1) * SZSLOT
+                for l in range(64):
+                    word_elems = (off[l] // 2, off[l] // 2 + 1)
+                    lds[slot[l]] = (kind, word_elems)
+            # readers: every B row the tile's waves hold
+            for rr in range(BN):
+                rowg = min(n0 + rr, N - 1)
+                want = rowg * G + kc
+                base = (rr >> 6) * SZSLOT + 4 * (rr & 63)
+                for kind in range(kinds):
+                    k_, elems = lds[kind * (BN // 64) * SZSLOT + base]
+                    assert k_ == kind
+                    half = (rowg * G + kc) & 1
+                    assert elems[half] == want

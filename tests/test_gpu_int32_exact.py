@@ -100,6 +100,7 @@ PREFILL_CASES = [
     (300, 520, 1024, 128, False),
     (200, 264, 2048, 256, True),
     (257, 136, 4096, 128, True),
+    (130, 519, 1152, 128, True),      # N x G odd: the last scale word is half used
 ]
 
 

@@ -326,7 +326,8 @@ def test_kernel_config_counts():
 @pytest.mark.parametrize("tile", range(NUM_TILE_CONFIGS))
 @pytest.mark.parametrize("M,N,K,g,asym", [(300, 520, 1024, 1024, False), (300, 520, 1024, 128, True),
                                           (300, 520, 1024, 128, False), (513, 392, 512, 512, True),
-                                          (200, 264, 2048, 256, True)])
+                                          (200, 264, 2048, 256, True),
+                                          (300, 519, 1152, 128, True)])
 def test_gemm_every_tile_config(tile, M, N, K, g, asym):
     """Every tile configuration the dispatcher can pick (forced through
     w4a4_set_kernel_override; configs without a per-group variant fall back

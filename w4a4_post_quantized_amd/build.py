@@ -35,9 +35,17 @@ SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "gemm_decode.hip", "wei
            "linear_decode.hip", "kv_cache.hip", "attention.hip", "ternary.hip", "gemm_f6.hip"]
 
 
+# per-source flags.  gemm.hip: MFMA results in ordinary VGPRs, so the
+# one-tile-group fold reads its int32 sums without accumulator-register moves
+# (64 v_accvgpr_read per K tile and wave in the 128x128 tile)
+SOURCE_FLAGS = {
+    "gemm.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, extra=()):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *extra]
+    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

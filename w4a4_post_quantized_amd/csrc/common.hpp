@@ -246,6 +246,21 @@ __device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, c
                  : "memory", "m0");
 }
 
+// 4-byte copy of one lane from a wave-uniform 64-bit base and a per-lane
+// 32-bit byte offset; the LDS address of lane l is lds_wave_base + 4 * l.
+// Issued like dma16_async_sv: the compiler does not see it, the caller's
+// s_waitcnt counts it.
+__device__ __forceinline__ void dma4_async_sv(const void* base, uint32_t off, const uint8_t* lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint8_t*)lds_wave_base)));
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(bs), "s"(m0)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();

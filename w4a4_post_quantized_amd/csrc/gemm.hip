@@ -345,14 +345,22 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     constexpr int FN = WN / 32;
     static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
     constexpr int PROW = 64;                          // packed bytes per tile row
-    constexpr int STAGE_BYTES = (BM + BN) * PROW;
+    constexpr int OPER_BYTES = (BM + BN) * PROW;
+    // One-tile groups: a stage also holds the tile's weight scales (and zero
+    // points) of its BN rows, copied by the same DMA as the operands: per row
+    // and kind the aligned 4-byte word that holds the 16-bit value, 64 rows
+    // per copy (lane l's word lands at slot + 4 l).  Every wave issues
+    // exactly one such copy per tile into its own 256-byte slot; waves past
+    // the SZI items repeat item wave % SZI.
+    constexpr int SZI = G1 ? (ASYM ? 2 : 1) * BN / 64 : 1;
+    static_assert(!G1 || (BN % 64 == 0 && SZI <= NW), "scale copies: at most one item per wave");
+    constexpr int SZSLOT = 256;
+    constexpr int STAGE_BYTES = OPER_BYTES + (G1 ? NW * SZSLOT : 0);
     constexpr int CHUNKS = (BM + BN) * 4;             // 16-byte chunks per tile
     static_assert(CHUNKS % (64 * NW) == 0 && (BM * 4) % 64 == 0, "whole wave loads");
     constexpr int LPW = CHUNKS / (64 * NW);           // load instructions per wave per tile
-    // vector-memory ops a wave issues per tile besides its copies: the next
-    // tile's scale (and zero point) per B fragment in one-tile-group mode
-    constexpr int NSZ = G1 ? FN * (ASYM ? 2 : 1) : 0;
-    constexpr int WAITN = (STAGES - 2) * LPW + (STAGES - 1) * NSZ;
+    constexpr int NSZ = G1 ? 1 : 0;                   // scale copies per wave per tile
+    constexpr int WAITN = (STAGES - 2) * (LPW + NSZ);
     static_assert(STAGES >= 3 && STAGES <= 8 && WAITN < 64, "stages / vmcnt range");
     static_assert(MODE != kModeI32, "fp16 output modes only");
     static_assert(!G1 || MODE == kModeGroup, "one-tile groups: per-group mode");
@@ -394,14 +402,19 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const int TPG = group_size / BK;
 
     // this lane's source row (clamped) and chunk for each of its loads.
-    // Symmetric weights: load i of a wave covers 64 consecutive slots, all in
-    // A or all in B, so the copies take a wave-uniform base (the tile's first
-    // row, scalar registers) and a 32-bit lane offset, issued from inline
-    // assembly.  Asymmetric weights keep the builtin copies: their zero points
-    // are loaded inside the K loop, and the compiler's waits for those loads
-    // must count the copies.
+    // Load i of a wave covers 64 consecutive slots, all in A or all in B, so
+    // the copies take a wave-uniform base (the tile's first row, scalar
+    // registers) and a 32-bit lane offset, issued from inline assembly: the
+    // compiler does not see them, so it neither drains them before LDS reads
+    // (as it does for the builtin copies, not knowing which bytes they write)
+    // nor counts them; every wait in the K loop is explicit.  The K loop then
+    // must hold no other global load (a compiler-inserted wait for it would
+    // drain the copies): per-channel zero points are read once before the
+    // loop, one-tile-group scales come through the stages.  Groups spanning
+    // several K tiles load their scales in the loop and keep the builtin
+    // copies.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    constexpr bool kBuiltinCopies = ASYM || G1;
+    constexpr bool kBuiltinCopies = MODE == kModeGroup && !G1;
     const uint8_t* src[kBuiltinCopies ? LPW : 1];
     uint32_t soff[kBuiltinCopies ? 1 : LPW];
 #pragma unroll
@@ -417,9 +430,22 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         else
             soff[i] = static_cast<uint32_t>(r - (isA ? m0 : n0)) * KB + c * 16;
     }
+    // this wave's scale copy: kind (scale or zero point) and 64-row block of
+    // its item, and the lane's element index of group 0
+    const uint16_t* sz_base = s_w;
+    uint32_t sz_e0 = 0;
+    if constexpr (G1) {
+        const int it = wave_u % SZI;
+        sz_base = (it >= BN / 64) ? z_w : s_w;
+        sz_e0 = static_cast<uint32_t>(min(n0 + (it % (BN / 64)) * 64 + lane, N - 1)) *
+                static_cast<uint32_t>(G);
+    }
     auto issue = [&](int kt, auto S) {
         const int kc = min(kt, KT - 1);
         uint8_t* stage = stage_ptr(S);
+        if constexpr (G1)
+            dma4_async_sv(sz_base, 2u * ((sz_e0 + static_cast<uint32_t>(kc)) & ~1u),
+                          stage + OPER_BYTES + wave * SZSLOT);
         if constexpr (kBuiltinCopies) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i) dma16(src[i] + kc * 64, stage + (i * NW + wave) * 1024);
@@ -478,26 +504,24 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     // int32 sums are folded at once into the fp32 sums with the group's
     // scale, so no accumulator is ever cleared.  The lane's B row is its
     // output column (frow == ocol), so one scale and one zero point per B
-    // fragment serve both the unpack and the fold; they are loaded one tile
-    // ahead.  A zero made opaque to the compiler: an MFMA whose accumulator
-    // operand was an inline-constant zero gave wrong sums.
+    // fragment serve both the unpack and the fold; they are read from the
+    // tile's stage (the half of the copied word that the element's index
+    // parity selects).  A zero made opaque to the compiler: an MFMA whose
+    // accumulator operand was an inline-constant zero gave wrong sums.
     v16i zc16;
-    const uint16_t* swp[G1 ? FN : 1];
-    const uint16_t* zwp[G1 && ASYM ? FN : 1];
-    uint16_t s_nx[G1 ? FN : 1], z_nx[G1 && ASYM ? FN : 1];
     if constexpr (G1) {
         int z0;
         asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
 #pragma unroll
         for (int r = 0; r < 16; ++r) zc16[r] = z0;
+    }
+    // per-channel zero points: read once, before any copy is in flight
+    uint32_t zb_chan[(ASYM && MODE == kModeChan) ? FN : 1];
+    if constexpr (ASYM && MODE == kModeChan) {
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
-            swp[b] = s_w + static_cast<size_t>(brow_g[b]) * G;
-            s_nx[b] = swp[b][0];
-            if constexpr (ASYM) {
-                zwp[b] = z_w + static_cast<size_t>(brow_g[b]) * G;
-                z_nx[b] = zwp[b][0];
-            }
+            const uint32_t z = static_cast<uint32_t>(h2f(z_w[brow_g[b]]));
+            zb_chan[b] = (0x80u - z) * 0x01010101u;
         }
     }
 
@@ -510,18 +534,25 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         uint32_t zbias[FN];
         float sw_t[G1 ? FN : 1];
         if constexpr (G1) {
-            // this tile's scale and zero point, then the next tile's loads
-            const int kn = min(kt + 1, KT - 1);
+            // this tile's scale and zero point from its stage: item i holds
+            // kind i / (BN / 64), rows 64 (i % (BN / 64)) + lane
+            const uint8_t* szs = stage + OPER_BYTES;
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
-                sw_t[b] = h2f(s_nx[b]);
+                const int rr = wn0 + b * 32 + frow;
+                const int r = (rr >> 6) * SZSLOT + 4 * (rr & 63);
+                const uint32_t sh = 16u * ((static_cast<uint32_t>(brow_g[b]) * static_cast<uint32_t>(G) +
+                                            static_cast<uint32_t>(kt)) & 1u);
+                sw_t[b] = h2f(static_cast<uint16_t>(*reinterpret_cast<const uint32_t*>(szs + r) >> sh));
                 if constexpr (ASYM) {
-                    const uint32_t z = static_cast<uint32_t>(h2f(z_nx[b]));
-                    zbias[b] = (0x80u - z) * 0x01010101u;
+                    const uint16_t zh = static_cast<uint16_t>(
+                        *reinterpret_cast<const uint32_t*>(szs + (BN / 64) * SZSLOT + r) >> sh);
+                    zbias[b] = (0x80u - static_cast<uint32_t>(h2f(zh))) * 0x01010101u;
                 }
-                s_nx[b] = swp[b][kn];
-                if constexpr (ASYM) z_nx[b] = zwp[b][kn];
             }
+        } else if constexpr (ASYM && MODE == kModeChan) {
+#pragma unroll
+            for (int b = 0; b < FN; ++b) zbias[b] = zb_chan[b];
         } else if constexpr (ASYM) {
             const int g = (kt * BK) / group_size;
 #pragma unroll
@@ -601,7 +632,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
 
     // prologue: tiles 0 .. STAGES-2 in flight; wait for tile 0
     static_for<0, STAGES - 1>([&](auto I) { issue(decltype(I)::value, I); });
-    wait_vmcnt<(STAGES - 2) * LPW>();
+    wait_vmcnt<(STAGES - 2) * (LPW + NSZ)>();
     lds_barrier();
 
     int kt = 0;
@@ -687,6 +718,9 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
     dim3 block(WM_ * WN_ * 64);
     if constexpr (MODE == kModeGroup) {
         if (a.group_size == BK) {
+            // the scale copies address N x G 16-bit elements with 32-bit offsets
+            if (static_cast<size_t>(a.N) * static_cast<size_t>(a.K / BK) >= (size_t{1} << 31))
+                return hipErrorInvalidValue;
             if (a.asym)
                 k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE, true><<<grid, block, 0, stream>>>(
                     a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
