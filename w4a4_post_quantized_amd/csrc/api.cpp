@@ -287,7 +287,8 @@ int w4a4_transform(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, const f
 // ---------------------------------------------------------------------------
 size_t w4a4_gemm_workspace_bytes(int32_t M, const w4a4_weight_desc* desc) {
     if (M < 0 || desc == nullptr || desc->K < 1 || desc->group_size < 1) return 0;
-    return w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size);
+    return w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size,
+                                      desc->asymmetric != 0);
 }
 
 static int gemm_common(const uint8_t* Xq, const float* s_x, int32_t M,
@@ -314,7 +315,8 @@ static int gemm_common(const uint8_t* Xq, const float* s_x, int32_t M,
         REQUIRE_ALIGNED(s_w);
         REQUIRE_ALIGNED(Y);
         const size_t need =
-            w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size);
+            w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size,
+                                       desc->asymmetric != 0);
         if (need) {
             REQUIRE(ws != nullptr && ws_bytes >= need, W4A4_ERR_WORKSPACE,
                     "workspace %zu < %zu bytes", ws ? ws_bytes : 0, need);
@@ -366,7 +368,8 @@ size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t ha
         return 0;
     const size_t K = static_cast<size_t>(n1) * n2;
     const size_t tq = w4a4::tq_workspace_bytes(M, n1, n2, has_c != 0);
-    const size_t gm = w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size);
+    const size_t gm = w4a4::gemm_workspace_bytes(M, desc->N, desc->K, desc->group_size,
+                                                 desc->asymmetric != 0);
     return align256(K / 2 * M) + align256(sizeof(float) * M) + (tq > gm ? tq : gm);
 }
 

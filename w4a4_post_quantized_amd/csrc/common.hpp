@@ -196,6 +196,18 @@ __device__ __forceinline__ void unpack_asym(const uint4& w, uint32_t bias, uint4
     od.w = usub((w.w >> 4) & 0x0F0F0F0Fu, bias);
 }
 
+// unsigned nibbles u -> bytes u in [0, 15]
+__device__ __forceinline__ void unpack_unsigned(const uint4& w, uint4& ev, uint4& od) {
+    ev.x = w.x & 0x0F0F0F0Fu;
+    ev.y = w.y & 0x0F0F0F0Fu;
+    ev.z = w.z & 0x0F0F0F0Fu;
+    ev.w = w.w & 0x0F0F0F0Fu;
+    od.x = (w.x >> 4) & 0x0F0F0F0Fu;
+    od.y = (w.y >> 4) & 0x0F0F0F0Fu;
+    od.z = (w.z >> 4) & 0x0F0F0F0Fu;
+    od.w = (w.w >> 4) & 0x0F0F0F0Fu;
+}
+
 // calls f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
 // ---------------------------------------------------------------------------
 // direct-to-LDS copies and their synchronisation

@@ -44,6 +44,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
 
 constexpr int BK = 128;          // codes per K tile
 constexpr int ROWB = BK;         // int8 bytes per LDS row
@@ -332,12 +334,44 @@ __device__ __forceinline__ void xcd_tile(int L, int tiles_m, int tiles_n, int gm
 
 // s_waitcnt with only a vmcnt condition (gfx9 encoding; expcnt and lgkmcnt
 // left at their no-wait maxima)
+// Per-token sums of the signed activation codes over each group of one K
+// tile, times 16 (the K loop's scale of the activation operand), as fp16
+// (|16 S| <= 16384, exact): S16[m, g] for g < K / 128, zero for the padding
+// up to Gp.  One thread per (m, g); the 64 packed bytes of a group are
+// summed as unsigned nibbles minus 16 per negative code.
+__global__ __launch_bounds__(256) void k_act_group_sums(const uint8_t* __restrict__ Xq, int M,
+                                                        int K, int Gp,
+                                                        uint16_t* __restrict__ S16) {
+    const long t = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= static_cast<long>(M) * Gp) return;
+    const int m = static_cast<int>(t / Gp);
+    const int g = static_cast<int>(t % Gp);
+    int sum = 0;
+    if (g < K / BK) {
+        const uint4* p = reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(m) * (K / 2) +
+                                                        static_cast<size_t>(g) * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = p[i];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = w4[j];
+                const uint32_t u = (w & 0x0F0F0F0Fu) + ((w >> 4) & 0x0F0F0F0Fu);
+                sum += static_cast<int>((u * 0x01010101u) >> 24) -
+                       16 * __builtin_popcount(w & 0x88888888u);
+            }
+        }
+    }
+    S16[t] = f2h(static_cast<float>(16 * sum));
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool ASYM, int MODE, bool G1 = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const uint8_t* __restrict__ Xq, const float* __restrict__ s_x,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ s_w,
     const uint16_t* __restrict__ z_w, uint16_t* __restrict__ Y, int M, int N, int K,
-    int group_size, int tile_group) {
+    int group_size, int tile_group, const uint16_t* __restrict__ Sg, int Gp) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M;
     constexpr int WN = BN / WAVES_N;
@@ -346,13 +380,17 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
     constexpr int PROW = 64;                          // packed bytes per tile row
     constexpr int OPER_BYTES = (BM + BN) * PROW;
-    // One-tile groups: a stage also holds the tile's weight scales (and zero
-    // points) of its BN rows, copied by the same DMA as the operands: per row
-    // and kind the aligned 4-byte word that holds the 16-bit value, 64 rows
+    // One-tile groups with asymmetric weights multiply the unsigned codes u in
+    // the K loop and subtract z[n,g] * Σ_{k in g} q_x[m,k] in the epilogue
+    // (Σ q (u - z) = Σ q u - z Σ q), so the loop needs no zero points.
+    constexpr bool ZID = G1 && ASYM;
+    // One-tile groups: a stage also holds the tile's weight scales of its BN
+    // rows, copied by the same DMA as the operands: per row the aligned
+    // 4-byte word that holds the 16-bit value, 64 rows
     // per copy (lane l's word lands at slot + 4 l).  Every wave issues
     // exactly one such copy per tile into its own 256-byte slot; waves past
     // the SZI items repeat item wave % SZI.
-    constexpr int SZI = G1 ? (ASYM ? 2 : 1) * BN / 64 : 1;
+    constexpr int SZI = G1 ? BN / 64 : 1;
     static_assert(!G1 || (BN % 64 == 0 && SZI <= NW), "scale copies: at most one item per wave");
     constexpr int SZSLOT = 256;
     constexpr int STAGE_BYTES = OPER_BYTES + (G1 ? NW * SZSLOT : 0);
@@ -394,8 +432,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     const int wn0 = (wave % WAVES_N) * WN;
     int tm, tn;
     xcd_tile(blockIdx.x, ceil_div(M, BM), ceil_div(N, BN), tile_group, tm, tn);
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    // tile origin: workgroup-uniform, kept in scalar registers so that the
+    // copies' scalar bases need no per-copy readfirstlane
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+    const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
     const int KB = K / 2;
     const int KT = K / BK;
     const int G = K / group_size;
@@ -430,22 +470,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         else
             soff[i] = static_cast<uint32_t>(r - (isA ? m0 : n0)) * KB + c * 16;
     }
-    // this wave's scale copy: kind (scale or zero point) and 64-row block of
-    // its item, and the lane's element index of group 0
-    const uint16_t* sz_base = s_w;
+    // this wave's scale copy: the 64-row block of its item and the lane's
+    // element index of group 0
     uint32_t sz_e0 = 0;
-    if constexpr (G1) {
-        const int it = wave_u % SZI;
-        sz_base = (it >= BN / 64) ? z_w : s_w;
-        sz_e0 = static_cast<uint32_t>(min(n0 + (it % (BN / 64)) * 64 + lane, N - 1)) *
+    if constexpr (G1)
+        sz_e0 = static_cast<uint32_t>(min(n0 + (wave_u % SZI) * 64 + lane, N - 1)) *
                 static_cast<uint32_t>(G);
-    }
     auto issue = [&](int kt, auto S) {
         const int kc = min(kt, KT - 1);
         uint8_t* stage = stage_ptr(S);
         if constexpr (G1)
-            dma4_async_sv(sz_base, 2u * ((sz_e0 + static_cast<uint32_t>(kc)) & ~1u),
-                          stage + OPER_BYTES + wave * SZSLOT);
+            dma4_async_sv(s_w, 2u * ((sz_e0 + static_cast<uint32_t>(kc)) & ~1u),
+                          stage + OPER_BYTES + wave_u * SZSLOT);
         if constexpr (kBuiltinCopies) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i) dma16(src[i] + kc * 64, stage + (i * NW + wave) * 1024);
@@ -455,7 +491,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
 #pragma unroll
             for (int i = 0; i < LPW; ++i)
                 dma16_async_sv((i * NW + wave_u) * 64 < BM * 4 ? xb : wb, soff[i],
-                               stage + (i * NW + wave) * 1024);
+                               stage + (i * NW + wave_u) * 1024);
         }
     };
 
@@ -534,8 +570,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         uint32_t zbias[FN];
         float sw_t[G1 ? FN : 1];
         if constexpr (G1) {
-            // this tile's scale and zero point from its stage: item i holds
-            // kind i / (BN / 64), rows 64 (i % (BN / 64)) + lane
+            // this tile's scales from its stage: item i holds rows
+            // 64 i + lane
             const uint8_t* szs = stage + OPER_BYTES;
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
@@ -544,11 +580,6 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
                 const uint32_t sh = 16u * ((static_cast<uint32_t>(brow_g[b]) * static_cast<uint32_t>(G) +
                                             static_cast<uint32_t>(kt)) & 1u);
                 sw_t[b] = h2f(static_cast<uint16_t>(*reinterpret_cast<const uint32_t*>(szs + r) >> sh));
-                if constexpr (ASYM) {
-                    const uint16_t zh = static_cast<uint16_t>(
-                        *reinterpret_cast<const uint32_t*>(szs + (BN / 64) * SZSLOT + r) >> sh);
-                    zbias[b] = (0x80u - static_cast<uint32_t>(h2f(zh))) * 0x01010101u;
-                }
             }
         } else if constexpr (ASYM && MODE == kModeChan) {
 #pragma unroll
@@ -576,7 +607,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
             for (int b = 0; b < FN; ++b) {
                 const uint4 w = *reinterpret_cast<const uint4*>(stage + boff[p][b]);
                 uint4 ev, od;
-                if constexpr (ASYM)
+                if constexpr (ZID)
+                    unpack_unsigned(w, ev, od);
+                else if constexpr (ASYM)
                     unpack_asym(w, zbias[b], ev, od);
                 else
                     unpack_signed16(w, ev, od);
@@ -641,6 +674,66 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     static_for<0, STAGES - 1>([&](auto I) {
         if (kt + decltype(I)::value < KT) body(kt + decltype(I)::value, I);
     });
+
+    // zero-point correction (asymmetric one-tile groups): the K loop summed
+    // s_w[n,g] * 16 Σ_k q_x u; subtract Σ_g (16 S[m,g]) (s_w z_w)[n,g] with
+    // S[m,g] = Σ_{k in g} q_x[m,k], on the fp16 matrix pipe: 16 S is exact in
+    // fp16, s z (an fp16 scale times a 4-bit integer) has at most 15
+    // significant bits and is split into fp16 hi + lo, so every product is
+    // exact and the accumulation is the fp32 one of the fold.  Lane (row
+    // frow, half fks) supplies groups g0 + 8 fks .. + 7 of A and of B.
+    if constexpr (ZID) {
+        const bool vec = (G & 7) == 0;
+        for (int g0 = 0; g0 < Gp; g0 += 16) {
+            const int gb = g0 + 8 * fks;
+            v8h_t sa[FM];
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                const int row = min(m0 + wm0 + a * 32 + frow, M - 1);
+                sa[a] = *reinterpret_cast<const v8h_t*>(Sg + static_cast<size_t>(row) * Gp + gb);
+            }
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const size_t e0 = static_cast<size_t>(brow_g[b]) * G + gb;
+                uint16_t sv[8], zv[8];
+                if (vec && gb + 8 <= G) {
+                    const uint4 s4 = *reinterpret_cast<const uint4*>(s_w + e0);
+                    const uint4 z4 = *reinterpret_cast<const uint4*>(z_w + e0);
+                    const uint32_t sw4[4] = {s4.x, s4.y, s4.z, s4.w};
+                    const uint32_t zw4[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        sv[e] = static_cast<uint16_t>(sw4[e >> 1] >> (16 * (e & 1)));
+                        zv[e] = static_cast<uint16_t>(zw4[e >> 1] >> (16 * (e & 1)));
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const bool in = gb + e < G;
+                        sv[e] = in ? s_w[e0 + e] : uint16_t{0};
+                        zv[e] = in ? z_w[e0 + e] : uint16_t{0};
+                    }
+                }
+                v8h_t bh, bl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const F16Pair hl = split_f16(-h2f(sv[e]) * h2f(zv[e]));
+                    bh[e] = hl.hi;
+                    bl[e] = hl.lo;
+                }
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    v16f c;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) c[r] = facc[a][b][r];
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[a], bh, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[a], bl, c, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) facc[a][b][r] = c[r];
+                }
+            }
+        }
+    }
 
     // epilogue: row by row, the wave's FN column fragments of a row one after
     // the other, so the halves of a 128-byte output line are written by
@@ -721,21 +814,24 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
             // the scale copies address N x G 16-bit elements with 32-bit offsets
             if (static_cast<size_t>(a.N) * static_cast<size_t>(a.K / BK) >= (size_t{1} << 31))
                 return hipErrorInvalidValue;
+            if (a.asym && (a.S == nullptr || a.Gp < a.K / BK)) return hipErrorInvalidValue;
             if (a.asym)
                 k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE, true><<<grid, block, 0, stream>>>(
-                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg, a.S,
+                    a.Gp);
             else
                 k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE, true><<<grid, block, 0, stream>>>(
-                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
+                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg,
+                    nullptr, 0);
             return hipGetLastError();
         }
     }
     if (a.asym)
         k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
+            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg, nullptr, 0);
     else
         k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg);
+            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg, nullptr, 0);
     return hipGetLastError();
 }
 
@@ -837,14 +933,15 @@ const KernelCfg& choose(const GemmArgs& a) {
         // direct-to-LDS 128x128 tiles below that
         // (128x384 tiles with 16 waves when they give about one tile per CU:
         // 2048x6144 takes 50.6 against 53.3 us with 256x256 tiles).
-        // Groups of 128: the direct-to-LDS 128x128 tile with 3 stages and
-        // one-tile groups (2048x4096 -> 28672: 442 against 467 us for the
-        // 16x16x64 register-staged tile); other group sizes: the 16x16x64
-        // 128x128 tile (8 waves)
+        // Groups of 128 (one-tile groups, direct-to-LDS): 256x128 tiles with
+        // 8 waves and 4 stages (2048x4096 -> 28672: 358-361 us against 374-391
+        // for 128x256 and 383-391 for 128x128 4-wave tiles; 2048x14336 ->
+        // 4096: 167-172 against 177-180 and 197-203 us, one box); other
+        // group sizes: the 16x16x64 128x128 tile (8 waves)
         const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
         const long tiles384 = static_cast<long>(ceil_div(a.M, 128)) * ceil_div(a.N, 384);
         if (grouped && a.group_size == BK)
-            t = 5;
+            t = 4;
         else if (grouped)
             t = 2;
         else if (tiles384 >= cus && tiles384 < 2L * cus)
@@ -861,12 +958,17 @@ const KernelCfg& choose(const GemmArgs& a) {
 
 int gemm_num_tile_configs() { return kNumTiles; }
 
-size_t gemm_workspace_bytes(int M, int N, int K, int group_size) {
-    (void)M;
+// prefill with asymmetric groups of one K tile: the per-token group sums
+static int group_sums_pad(int K) { return (K / BK + 15) / 16 * 16; }
+static bool uses_group_sums(int M, int K, int group_size, bool asym) {
+    return asym && group_size == BK && M > kDecodeMaxM && K / group_size > 1;
+}
+
+size_t gemm_workspace_bytes(int M, int N, int K, int group_size, bool asym) {
     (void)N;
-    (void)K;
-    (void)group_size;
-    return 0;
+    if (!uses_group_sums(M, K, group_size, asym)) return 0;
+    const size_t b = sizeof(uint16_t) * static_cast<size_t>(M) * group_sums_pad(K);
+    return (b + 255) & ~static_cast<size_t>(255);
 }
 
 const char* gemm_kernel_name(const GemmArgs& a, bool i32_out) {
@@ -877,14 +979,26 @@ const char* gemm_kernel_name(const GemmArgs& a, bool i32_out) {
 
 hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (a.M == 0) return hipSuccess;
     if (i32_out) return launch_mode<64, 64, 2, 2, kModeI32>(a, stream);
     if (a.M <= kDecodeMaxM) return gemm_decode_launch(a, stream);
     const bool grouped = (a.K / a.group_size) > 1;
     const KernelCfg& k = choose(a);
-    return grouped ? k.group(a, stream) : k.chan(a, stream);
+    if (!grouped) return k.chan(a, stream);
+    GemmArgs g = a;
+    if (uses_group_sums(a.M, a.K, a.group_size, a.asym)) {
+        const size_t need = gemm_workspace_bytes(a.M, a.N, a.K, a.group_size, a.asym);
+        if (ws == nullptr || ws_bytes < need) return hipErrorInvalidValue;
+        g.Gp = group_sums_pad(a.K);
+        uint16_t* S = static_cast<uint16_t*>(ws);
+        const long total = static_cast<long>(a.M) * g.Gp;
+        k_act_group_sums<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
+            a.Xq, a.M, a.K, g.Gp, S);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g.S = S;
+    }
+    return k.group(g, stream);
 }
 
 }  // namespace w4a4

@@ -54,9 +54,14 @@ struct GemmArgs {
     int32_t* D;      // int32 output (mode i32)
     int M, N, K, group_size;
     bool asym;
+    // per-token group sums 16 * Σ_{k in g} q_x[m,k] (fp16, [M, Gp], zero for
+    // g >= G): set by gemm_launch for the prefill kernels that apply the
+    // zero-point correction in the epilogue
+    const uint16_t* S = nullptr;
+    int Gp = 0;
 };
 
-size_t gemm_workspace_bytes(int M, int N, int K, int group_size);
+size_t gemm_workspace_bytes(int M, int N, int K, int group_size, bool asym);
 // name of the configuration gemm_launch would use (launches nothing)
 const char* gemm_kernel_name(const GemmArgs& a, bool i32_out);
 hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_bytes,
