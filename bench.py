@@ -47,6 +47,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -86,6 +87,10 @@ def parse():
     ap.add_argument("--act-quant", choices=["dynamic", "tensor", "channel"], default="dynamic",
                     help="activation quantizer: per-token dynamic scales, or static steps "
                          "(one per tensor, or one per channel migrated into the weights)")
+    ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="MB",
+                    help="only time a plain device read (a sum) of MB megabytes, rotated over "
+                         "enough buffers to exceed the 256 MB Infinity Cache: the HBM read "
+                         "rate one launch of that size reaches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -103,6 +108,33 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
+def read_ceiling(mb, steps, warmup):
+    """HIP-event timing of a plain read of `mb` MB per launch (the library's
+    w4a4_read_probe), the buffers rotated like the benchmark's weight copies;
+    the launches go to torch's current stream, where the events are."""
+    import torch
+    import w4a4_post_quantized_amd as L
+    n = int(mb * 1e6) // 16 * 4
+    copies = max(3, math.ceil(MALL_BYTES / (4 * n)) + 1)
+    bufs = [torch.full((n,), i + 1, dtype=torch.int32, device="cuda:0") for i in range(copies)]
+    out = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    for i in range(warmup):
+        L.read_probe(bufs[i % copies], out, stream=st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        L.read_probe(bufs[i % copies], out, stream=st)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"read_ceiling_bytes_per_launch": 4 * n, "buffers_rotated": copies,
+                      "us_per_launch": round(us, 2), "GBps": round(4 * n / us / 1e3, 1),
+                      "fraction_of_8TBps": round(4 * n / us / 1e3 / 8000.0, 4),
+                      "steps": steps}), flush=True)
 
 
 def gemm_bytes(wl, M):
@@ -247,6 +279,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.read_ceiling:
+        read_ceiling(args.read_ceiling, args.steps, args.warmup)
         return
     if args.bits != 4 and (args.act_quant != "dynamic" or args.path != "two"):
         raise SystemExit("--bits 3 runs the dynamic two-launch layer only")

@@ -545,6 +545,19 @@ int w4a4_attn_decode(const uint16_t* q, int32_t batch, int32_t heads_q, int32_t 
                      const float* v_scale, const int32_t* lengths, int32_t max_seq,
                      float sm_scale, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement aid                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* A plain streaming read of `bytes` bytes of device memory (16-byte loads
+ * over a persistent grid), for measuring the HBM read rate one launch of
+ * that size reaches: the ceiling against which the bandwidth of the decode
+ * GEMM (an HBM-bound read of the packed weights) is judged.  The XOR of all
+ * 32-bit words of buf is XORed into *out (device word; clear it first to
+ * read the checksum).  buf and out 16-byte aligned, bytes a multiple of 16;
+ * W4A4_ERR_INVALID_ARG / W4A4_ERR_ALIGNMENT otherwise.  One launch. */
+int w4a4_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -362,3 +362,13 @@ def test_f6_entry_points_validation():
     assert "k_gemm_f6" in W.gemm_f6_kernel_name(2048, W.WeightDesc(6144, 4096, 4096, 0))
     assert L.w4a4_linear_f6(FAKE, 4, 16, 16, FAKE, FAKE, None, 1.5, desc(N=64, K=256, g=256),
                             FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1   # alpha_a
+
+
+def test_read_probe_validation():
+    L = W.lib()
+    assert L.w4a4_read_probe(None, 0, None, None) == 0          # nothing to read
+    assert L.w4a4_read_probe(None, 16, FAKE, None) == -1
+    assert L.w4a4_read_probe(FAKE, 16, None, None) == -1
+    assert L.w4a4_read_probe(FAKE, 24, FAKE, None) == -1         # not a multiple of 16
+    assert L.w4a4_read_probe(MISALIGNED, 16, FAKE, None) == -3
+    assert L.w4a4_read_probe(FAKE, 16, MISALIGNED, None) == -3

@@ -14,7 +14,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "W4A4Error", "WeightDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "W4A4Error", "WeightDesc", "lib", "LIB_PATH", "EXPORTED_SYMBOLS", "read_probe",
     "OVERRIDE_PREFILL_TILE", "OVERRIDE_DECODE", "OVERRIDE_F6_TILE", "OVERRIDE_TILE_GROUP",
     "set_kernel_override",
     "kernel_config_count",
@@ -57,6 +57,7 @@ EXPORTED_SYMBOLS = [
     "w4a4_weights_f6_bytes", "w4a4_pack_weights_f6", "w4a4_gemm_f6_workspace_bytes",
     "w4a4_gemm_f6", "w4a4_gemm_f6_kernel_name", "w4a4_linear_f6_workspace_bytes",
     "w4a4_linear_f6",
+    "w4a4_read_probe",
 ]
 
 DECODE_SYNC_BYTES = 1024          # W4A4_DECODE_SYNC_BYTES
@@ -149,6 +150,7 @@ def lib() -> ctypes.CDLL:
             "w4a4_pack_ternary": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
             "w4a4_unpack_ternary": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp]),
             "w4a4_ternary_gemm_workspace_bytes": (sz, [i32, i32, i32]),
+            "w4a4_read_probe": (ctypes.c_int, [vp, sz, vp, vp]),
             "w4a4_ternary_gemm": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
             "w4a4_kv_cache_bytes": (ctypes.c_int, [i32, i32, i32, i32, szp, szp, szp]),
             "w4a4_kv_query_factor_workspace_bytes": (sz, [i32, i32]),
@@ -696,6 +698,18 @@ def ternary_gemm(X, Tq, am, N: int, out=None, ws=None, stream=None):
                                    nb if ws is None else ws.numel(), _stream(stream)),
            "w4a4_ternary_gemm")
     return Y
+
+
+def read_probe(buf, out, stream=None):
+    """Measurement aid: a plain streaming read of the whole of `buf` (a
+    contiguous device tensor of a multiple of 16 bytes); the XOR of its 32-bit
+    words is XORed into `out` (an int32 device tensor of one element)."""
+    torch = _torch()
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous CUDA (HIP) tensor")
+    _need(out, torch.int32, (1,), "out")
+    _check(lib().w4a4_read_probe(_p(buf), buf.numel() * buf.element_size(), _p(out),
+                                 _stream(stream)), "w4a4_read_probe")
 
 
 # ---------------------------------------------------------------------------

@@ -32,7 +32,8 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["api.cpp", "transform_quant.hip", "gemm.hip", "gemm_decode.hip", "weights.hip",
-           "linear_decode.hip", "kv_cache.hip", "attention.hip", "ternary.hip", "gemm_f6.hip"]
+           "linear_decode.hip", "kv_cache.hip", "attention.hip", "ternary.hip", "gemm_f6.hip",
+           "measure.hip"]
 
 
 # per-source flags.  gemm.hip: MFMA results in ordinary VGPRs, so the

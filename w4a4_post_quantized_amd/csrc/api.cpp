@@ -976,4 +976,16 @@ int w4a4_ternary_gemm(const uint16_t* X, int32_t M, int32_t N, int32_t K, const 
     return hip_status(e, "w4a4_ternary_gemm");
 }
 
+// ---------------------------------------------------------------------------
+int w4a4_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+    if (bytes == 0) return ok();
+    REQUIRE_PTR(buf);
+    REQUIRE_PTR(out);
+    REQUIRE(bytes % 16 == 0, W4A4_ERR_INVALID_ARG, "bytes = %zu is not a multiple of 16", bytes);
+    REQUIRE_ALIGNED(buf);
+    REQUIRE_ALIGNED(out);
+    hipError_t e = w4a4::read_probe_launch(buf, bytes, out, static_cast<hipStream_t>(stream));
+    return hip_status(e, "w4a4_read_probe");
+}
+
 }  // extern "C"

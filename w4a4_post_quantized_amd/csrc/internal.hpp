@@ -190,4 +190,7 @@ hipError_t pack_weights_launch(const float* Wt, int N, int K, int group_size, bo
                                float alpha_w, int bits, uint8_t* Wq, uint16_t* s_w,
                                uint16_t* z_w, hipStream_t stream);
 
+// measurement aid (measure.hip): XOR of all 32-bit words of buf into *out
+hipError_t read_probe_launch(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
+
 }  // namespace w4a4
