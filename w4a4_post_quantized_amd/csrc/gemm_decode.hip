@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
         const uint8_t* wb = wbase + static_cast<size_t>(it) * 64;
 #pragma unroll
         for (int b = 0; b < FN; ++b) bbuf[SL][b] = *reinterpret_cast<const uint4*>(wb + boff[b]);
-        if (it + 1 < t1) ++it;
+        it = min(it + 1, t1 - 1);
     };
     // compute position: group cg of tile t and its place cr inside the group
     int cg = t0 / TPG, cr = t0 - (t0 / TPG) * TPG;
@@ -241,15 +241,28 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
         }
     };
 
+    // Main loop over whole groups of D tiles with no branch around a step
+    // (with one, the compiler's waits at the join assumed the fewest loads in
+    // flight and drained the prefetch), then at most D - 1 tiles whose loads
+    // are already in flight.  Tile t uses buffer slot (t - t0) % D.
     if (t0 < t1) {
         static_for<0, D - 1>([&](auto U) { issue(U); });
-        for (int t = t0; t < t1; t += D) {
+        int t = t0;
+        for (; t + D <= t1; t += D) {
             static_for<0, D>([&](auto U) {
                 constexpr int u = decltype(U)::value;
                 issue(std::integral_constant<int, (u + D - 1) % D>{});
-                if (t + u < t1) compute(t + u, std::integral_constant<int, u>{});
+                // keep the step's loads ahead of its arithmetic: left free,
+                // the scheduler sinks them below the MFMAs and the waits for
+                // the current tile then cover them too
+                __builtin_amdgcn_sched_barrier(0);
+                compute(t + u, std::integral_constant<int, u>{});
             });
         }
+        static_for<0, D - 1>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if (t + u < t1) compute(t + u, std::integral_constant<int, u>{});
+        });
     }
 
     // ---- add the waves' partial sums in LDS, in wave order -------------------
@@ -363,7 +376,7 @@ constexpr int kNumDec = 4;
 const KernelCfg kDec[3][kNumDec] = {
     {W4A4_DEC(1, 1, 16, 4), W4A4_DEC(1, 2, 16, 4), W4A4_DEC(1, 1, 8, 6), W4A4_DEC(1, 2, 8, 6)},
     {W4A4_DEC(2, 1, 16, 4), W4A4_DEC(2, 2, 8, 4), W4A4_DEC(2, 1, 8, 4), W4A4_DEC(2, 2, 8, 3)},
-    {W4A4_DEC(4, 1, 8, 3), W4A4_DEC(4, 2, 8, 3), W4A4_DEC(4, 1, 8, 2), W4A4_DEC(4, 2, 8, 2)},
+    {W4A4_DEC(4, 1, 8, 3), W4A4_DEC(4, 2, 8, 4), W4A4_DEC(4, 1, 8, 6), W4A4_DEC(4, 2, 8, 6)},
 };
 #undef W4A4_DEC
 
@@ -376,12 +389,12 @@ const KernelCfg& choose_dec(const GemmArgs& a) {
         // measured on MI355X (28672 -> 8192, group 128, weight copies
         // rotated): two 16-column fragments per workgroup once the staged
         // activations fill the LDS (or for two and four row fragments) and
-        // the grid still covers every CU (8 tokens: 31.8-32.0 us against
-        // 35.7-37.2 us); one fragment otherwise, with 8 waves and 6 tiles in
-        // flight for one row fragment (1 token: 27.0-27.1 us against
-        // 28.5-30.2 us with 16 waves and 4 tiles) and 16 waves for more; for
-        // four row fragments 2 tiles in flight (64 tokens: 56.7 against
-        // 57.5 us with 3)
+        // the grid still covers every CU (8 tokens: 29.3 us against 32.7 us);
+        // one fragment otherwise, with 8 waves and 6 tiles in flight for one
+        // row fragment (1 token: 24.9 us against 26.3 us with 16 waves and 4
+        // tiles) and 16 waves for more; for four row fragments 6 tiles in
+        // flight (64 tokens: 56.6 against 57.3 us with 4 and 83-86 us with
+        // one column fragment)
         bool wide = ceil_div(a.N, 32) >= cus;
         if (fi == 0) {
             const size_t staged = static_cast<size_t>(a.M) * (a.K / 2 + 16);
