@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
     auto issue = [&](auto S) {
         constexpr int SL = decltype(S)::value;
         bbuf[SL] = *reinterpret_cast<const uint4*>(wbase + static_cast<size_t>(it) * 64 + boff);
-        if (it + 1 < t1) ++it;
+        it = min(it + 1, t1 - 1);
     };
     // the first weight tiles are in flight while the activations are made
     if (t0 < t1) static_for<0, D - 1>([&](auto U) { issue(U); });
@@ -517,14 +517,23 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
         }
     };
 
+    // whole groups of D tiles with no branch around a step and the step's
+    // load kept ahead of its arithmetic (as in the decode GEMM), then the
+    // last tiles, whose loads are in flight; tile t uses slot (t - t0) % D
     if (t0 < t1) {
-        for (int t = t0; t < t1; t += D) {
+        int t = t0;
+        for (; t + D <= t1; t += D) {
             static_for<0, D>([&](auto U) {
                 constexpr int u = decltype(U)::value;
                 issue(std::integral_constant<int, (u + D - 1) % D>{});
-                if (t + u < t1) compute(t + u, std::integral_constant<int, u>{});
+                __builtin_amdgcn_sched_barrier(0);
+                compute(t + u, std::integral_constant<int, u>{});
             });
         }
+        static_for<0, D - 1>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if (t + u < t1) compute(t + u, std::integral_constant<int, u>{});
+        });
     }
 
     // ---- add the waves' partial sums in LDS, in wave order ------------------

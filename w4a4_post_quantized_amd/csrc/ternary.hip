@@ -372,15 +372,23 @@ __global__ __launch_bounds__(W * 64) void k_tern_gemm(TernArgs a) {
         }
         __syncthreads();
     }
+    // whole rotations of NBUF groups with no branch around a step (a branch
+    // there let the compiler's waits at the join assume the fewest loads in
+    // flight), a scheduling barrier keeping each step's loads ahead of its
+    // arithmetic; then the last ng % NBUF groups, whose loads are in flight
     if (ng > 0) {
-        for (int i0 = 0; i0 < ng; i0 += NBUF) {
+        int i0 = 0;
+        for (; i0 + NBUF <= ng; i0 += NBUF) {
 #pragma unroll
             for (int b = 0; b < NBUF; ++b) {
-                if (i0 + b >= ng) break;
                 load_pairs(buf[(b + NBUF - 1) % NBUF], QB * group_of(i0 + b + NBUF - 1), QB / 2);
+                __builtin_amdgcn_sched_barrier(0);
                 compute(buf[b], QB * group_of(i0 + b), QB);
             }
         }
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b)
+            if (i0 + b < ng) compute(buf[b], QB * group_of(i0 + b), QB);
     }
     // the blocks past the last full group (G % QB of them), in the last
     // split, by every wave (NSP: each for its own columns) or the last wave:
