@@ -319,6 +319,7 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
         const bool valid = m < M;
         v4f Z[C::RB];
         float wmax = 0.0f;
+        int unscale = 0;
         if (valid) {
             const uint8_t* xt = &xs[buf][tslot * C::XSLOT];
             // stage 1: T[:, cb] = X̄ · P2'[:, cb]
@@ -362,8 +363,12 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
                     }
                 }
             }
-            // stage 2: Z[:, cb] = P1'^T · T'[:, cb]
-            const int unscale = -(e1 + e2 + et);
+            // stage 2, transposed: Zᵀ = T'ᵀ · P1' with the split T as the A
+            // operand in its accumulators' own k order and the P1 fragments
+            // as the B operand (the fragment's rows rho are that order), so
+            // lane (g, li) of tile ob holds 2^-unscale Z[16 ob + li][16 cb +
+            // 4 g + r]: four consecutive channels of one row
+            unscale = -(e1 + e2 + et);
 #pragma unroll
             for (int ob = 0; ob < C::RB; ++ob) {
                 v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -372,20 +377,18 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
                     const int off = ((ob * C::KS2 + sk) * 64 + lane) * 8;
                     const v8h ah = *reinterpret_cast<const v8h*>(p1hi + off);
                     const v8h al = *reinterpret_cast<const v8h*>(p1lo + off);
-                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh[sk], z, 0, 0, 0);
-                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[sk], z, 0, 0, 0);
-                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh[sk], z, 0, 0, 0);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh[sk], al, z, 0, 0, 0);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(bl[sk], ah, z, 0, 0, 0);
+                    z = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh[sk], ah, z, 0, 0, 0);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    z[r] = ldexpf(z[r], unscale);
-                    wmax = fmaxf(wmax, fabsf(z[r]));
-                }
+                for (int r = 0; r < 4; ++r) wmax = fmaxf(wmax, fabsf(z[r]));
                 Z[ob] = z;
             }
         }
         // ---- per-token absmax and scale ---------------------------------------
-        wmax = wave_max(wmax);
+        // (each wave's power of two is applied to its maximum: exact)
+        wmax = ldexpf(wave_max(wmax), unscale);
         if (lane == 0) red[wave] = wmax;
         __syncthreads();
         float amax = 0.0f;
@@ -404,39 +407,41 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
             if (Zout != nullptr) {
                 float* zo = Zout + static_cast<size_t>(m) * K;
 #pragma unroll
-                for (int ob = 0; ob < C::RB; ++ob)
+                for (int ob = 0; ob < C::RB; ++ob) {
+                    v4f zz;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        zo[(16 * ob + 4 * g + r) * N2 + 16 * cb + li] = Z[ob][r];
+                    for (int r = 0; r < 4; ++r) zz[r] = ldexpf(Z[ob][r], unscale);
+                    *reinterpret_cast<v4f*>(zo + (16 * ob + li) * N2 + 16 * cb + 4 * g) = zz;
+                }
             } else {
-                const bool zero = !(s > 0.0f);
-                const float inv = zero ? 0.0f : 1.0f / s;
+                // the wave's power of two goes into the quantizer's multiplier
+                // (exact, so the codes are those of the unscaled values)
+                const float inv = s > 0.0f ? ldexpf(1.0f / s, unscale) : 0.0f;
                 uint8_t* qb = qbuf + tslot * (K / 2);
                 const __amdgpu_buffer_rsrc_t srs = steps_rsrc(aq.steps, K);
-                const int svoff = ((4 * g) * N2 + 16 * cb + li) * 4;
+                const int svoff = (li * N2 + 16 * cb + 4 * g) * 4;
 #pragma unroll
                 for (int ob = 0; ob < C::RB; ++ob) {
-                    float rst[4];
+                    v4f rst;
                     if (PC) {
-                        // this row block's four steps only: no batch of all
-                        // the token's step loads competing for registers
+                        // this row block's four steps only (one 16-byte load):
+                        // no batch of all the token's step loads competing
+                        // for registers
                         asm volatile("" ::: "memory");
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            rst[r] = __builtin_amdgcn_rcpf(__builtin_bit_cast(
-                                float, __builtin_amdgcn_raw_buffer_load_b32(
-                                           srs, svoff, (16 * ob + r) * N2 * 4, 0)));
+                        rst = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           srs, svoff, 16 * ob * N2 * 4, 0));
                     }
+                    uint32_t w = 0;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const uint32_t nib = PC ? quant_nibble_magic(Z[ob][r], rst[r], aq.qmax)
-                                                : quant_nibble(Z[ob][r], inv, zero, aq.qmax);
-                        const uint32_t odd = lane_xor1(nib);
-                        if ((li & 1) == 0) {
-                            const int k = (16 * ob + 4 * g + r) * N2 + 16 * cb + li;
-                            qb[k >> 1] = static_cast<uint8_t>(nib | (odd << 4));
-                        }
+                        const uint32_t nib =
+                            PC ? quant_nibble_magic(ldexpf(Z[ob][r], unscale),
+                                                    __builtin_amdgcn_rcpf(rst[r]), aq.qmax)
+                               : quant_nibble_magic(Z[ob][r], inv, aq.qmax);
+                        w |= nib << (4 * r);
                     }
+                    const int k0 = (16 * ob + li) * N2 + 16 * cb + 4 * g;
+                    *reinterpret_cast<uint16_t*>(qb + (k0 >> 1)) = static_cast<uint16_t>(w);
                 }
             }
         }
