@@ -143,7 +143,10 @@ def test_gemm_kernel_name_query():
     """The configuration name is a host-side query: decode kernels for at most
     64 tokens, the prefill kernels above; invalid descriptors give NULL."""
     assert W.gemm_kernel_name(1, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 1")
-    assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 4")
+    assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec64<")
+    assert W.gemm_kernel_name(32, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 2")
+    # other group sizes keep the register-streamed kernel
+    assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 512, 1)).startswith("k_gemm_dec<FM 4")
     assert W.gemm_kernel_name(2048, W.WeightDesc(6144, 4096, 4096, 0)).startswith("k_gemm_dl<")
     assert W.gemm_kernel_name(2048, W.WeightDesc(28672, 4096, 128, 1)).startswith("k_gemm")
     with pytest.raises(W.W4A4Error):
@@ -168,7 +171,10 @@ def test_kernel_override_is_a_host_setting():
     W.set_kernel_override(W.OVERRIDE_DECODE, 3)
     assert W.gemm_kernel_name(8, d) != v2
     W.set_kernel_override(W.OVERRIDE_DECODE, -1)
-    assert W.kernel_config_count(W.OVERRIDE_DECODE) == 4
+    assert W.kernel_config_count(W.OVERRIDE_DECODE) == 5
+    W.set_kernel_override(W.OVERRIDE_DECODE, 4)           # the split-K kernel, any M
+    assert W.gemm_kernel_name(8, d).startswith("k_gemm_dec64<")
+    W.set_kernel_override(W.OVERRIDE_DECODE, -1)
     assert W.kernel_config_count(W.OVERRIDE_F6_TILE) >= 1
     L = W.lib()
     assert L.w4a4_set_kernel_override(4, 0) == -1 and "kind" in last()

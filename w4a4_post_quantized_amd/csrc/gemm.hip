@@ -965,7 +965,9 @@ static bool uses_group_sums(int M, int K, int group_size, bool asym) {
 }
 
 size_t gemm_workspace_bytes(int M, int N, int K, int group_size, bool asym) {
-    (void)N;
+    // decode: the split-K kernel's partial sums (per channel or groups of 128)
+    if (M <= kDecodeMaxM)
+        return (K / group_size == 1 || group_size == BK) ? gemm_decode_workspace_bytes(M, N) : 0;
     if (!uses_group_sums(M, K, group_size, asym)) return 0;
     const size_t b = sizeof(uint16_t) * static_cast<size_t>(M) * group_sums_pad(K);
     return (b + 255) & ~static_cast<size_t>(255);
@@ -981,7 +983,7 @@ hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_byte
                        hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
     if (i32_out) return launch_mode<64, 64, 2, 2, kModeI32>(a, stream);
-    if (a.M <= kDecodeMaxM) return gemm_decode_launch(a, stream);
+    if (a.M <= kDecodeMaxM) return gemm_decode_launch(a, ws, ws_bytes, stream);
     const bool grouped = (a.K / a.group_size) > 1;
     const KernelCfg& k = choose(a);
     if (!grouped) return k.chan(a, stream);
