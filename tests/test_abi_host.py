@@ -143,7 +143,7 @@ def test_gemm_kernel_name_query():
     """The configuration name is a host-side query: decode kernels for at most
     64 tokens, the prefill kernels above; invalid descriptors give NULL."""
     assert W.gemm_kernel_name(1, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 1")
-    assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec64<")
+    assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec_split<FM 4")
     assert W.gemm_kernel_name(32, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 2")
     # other group sizes keep the register-streamed kernel
     assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 512, 1)).startswith("k_gemm_dec<FM 4")
@@ -151,6 +151,26 @@ def test_gemm_kernel_name_query():
     assert W.gemm_kernel_name(2048, W.WeightDesc(28672, 4096, 128, 1)).startswith("k_gemm")
     with pytest.raises(W.W4A4Error):
         W.gemm_kernel_name(16, W.WeightDesc(256, 200, 200, 0))
+
+
+def test_decode_split_workspace():
+    """The split-K decode kernel's partial sums: S ranges x M x N int32, S the
+    smallest split giving 256 workgroups of 256 columns whose activations
+    and scale tables fit the LDS (28672 -> 8192: 32 column blocks, 8 ranges of
+    28 tiles; 28 tiles of 64 rows take 115.7 KiB and two tables 30 KiB)."""
+    L = W.lib()
+    d = W.WeightDesc(8192, 28672, 128, 1)
+    assert L.w4a4_gemm_workspace_bytes(64, ctypes.byref(d)) == 8 * 64 * 8192 * 4
+    assert L.w4a4_gemm_workspace_bytes(8, ctypes.byref(d)) == 8 * 8 * 8192 * 4
+    # 57344 columns: 224 blocks, two ranges of 32 tiles (K 8192)
+    d = W.WeightDesc(57344, 8192, 128, 1)
+    assert L.w4a4_gemm_workspace_bytes(40, ctypes.byref(d)) == 2 * 40 * 57344 * 4
+    # the LDS bound: 256 column blocks fill the CUs with one range, but 64
+    # staged rows of 64 tiles take 257 KiB: two ranges of 32 tiles
+    d = W.WeightDesc(65536, 8192, 8192, 0)
+    assert L.w4a4_gemm_workspace_bytes(64, ctypes.byref(d)) == 2 * 64 * 65536 * 4
+    # group sizes other than one tile or the whole row take no workspace
+    assert L.w4a4_gemm_workspace_bytes(64, ctypes.byref(W.WeightDesc(8192, 28672, 512, 1))) == 0
 
 
 def test_kernel_override_is_a_host_setting():
@@ -173,7 +193,7 @@ def test_kernel_override_is_a_host_setting():
     W.set_kernel_override(W.OVERRIDE_DECODE, -1)
     assert W.kernel_config_count(W.OVERRIDE_DECODE) == 5
     W.set_kernel_override(W.OVERRIDE_DECODE, 4)           # the split-K kernel, any M
-    assert W.gemm_kernel_name(8, d).startswith("k_gemm_dec64<")
+    assert W.gemm_kernel_name(8, d).startswith("k_gemm_dec_split<FM 1")
     W.set_kernel_override(W.OVERRIDE_DECODE, -1)
     assert W.kernel_config_count(W.OVERRIDE_F6_TILE) >= 1
     L = W.lib()

@@ -966,8 +966,7 @@ static bool uses_group_sums(int M, int K, int group_size, bool asym) {
 
 size_t gemm_workspace_bytes(int M, int N, int K, int group_size, bool asym) {
     // decode: the split-K kernel's partial sums (per channel or groups of 128)
-    if (M <= kDecodeMaxM)
-        return (K / group_size == 1 || group_size == BK) ? gemm_decode_workspace_bytes(M, N) : 0;
+    if (M <= kDecodeMaxM) return gemm_decode_workspace_bytes(M, N, K, group_size, asym);
     if (!uses_group_sums(M, K, group_size, asym)) return 0;
     const size_t b = sizeof(uint16_t) * static_cast<size_t>(M) * group_sums_pad(K);
     return (b + 255) & ~static_cast<size_t>(255);

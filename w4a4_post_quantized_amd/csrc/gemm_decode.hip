@@ -357,267 +357,400 @@ hipError_t launch_dec(const GemmArgs& a, hipStream_t stream) {
 
 
 // ===========================================================================
-// Split-K decode kernel for up to 64 tokens with the copies of the prefill
-// kernels.  A workgroup of 8 waves owns 128 output columns (16 per wave) and
-// one of kD64Split ranges of K tiles; all its waves walk the same K tiles, so
-// the activation tile (64 rows, clamped to M) is copied and unpacked once
-// per workgroup.  Every K tile goes into a ring of LDS stages by
-// global_load_lds copies issued from inline assembly with explicit waits
-// (the compiler sees no vector load in the K loop, so none of its waits can
-// drain the ring): waves 0-3 copy 16 activation rows and 16 weight rows
-// each, waves 4-7 16 weight rows and one 64-row item of weight scales (and
-// zero points) of the tile's group.  Per K tile the waves unpack the staged
-// activation tile once into int8 even-code and odd-code halves (8 bytes of
-// packed codes per lane) for the next tile, then multiply: four 16-row
-// activation fragments against the wave's 16 weight rows on
-// v_mfma_i32_16x16x64_i8, exactly as the register-streamed kernel above.
-// Each workgroup writes its range's sums (int32 per channel, fp32 per group
-// of 128) for its columns; k_dec64_reduce adds the ranges in a fixed order
-// and applies the token scale.
+// Split-K decode kernel (M <= 64 tokens): a workgroup of 8 waves owns 256
+// output columns (32 per wave, two 16-column fragments) and one of S ranges
+// of K tiles.  Before its K loop it copies the range's activation rows
+// (packed, M rows, each padded by one 16-byte chunk) and, for groups of one
+// K tile, the range's weight scales and zero points of its columns into LDS,
+// all by global_load_lds copies issued from inline assembly and retired by
+// one wait.  The packed weights then stream from HBM into registers as in
+// k_gemm_dec (D - 1 tiles of loads in flight per wave), and every wave
+// reads its activation fragments from the staged rows.  The activations are
+// thus read from L2 once per 256 columns, not once per 16 or 32 as in
+// k_gemm_dec, and the weight stream has no LDS stage or barrier in its way.
+// S is the smallest split that gives about one workgroup per CU, with at
+// least 8 K tiles per range (the partial sums stay a small fraction of the
+// weight bytes) and a staged range that fits the LDS.  Each workgroup writes its range's sums (exact
+// int32 per channel, fp32 per one-tile group) for its columns;
+// k_dec_split_reduce adds the ranges in a fixed order and applies the
+// scales.
 // ===========================================================================
-constexpr int kD64Rows = 64;
-constexpr int kD64Cols = 128;
-constexpr int kD64Waves = 8;
-constexpr int kD64Stages = 6;
-constexpr int kD64Split = 4;
-constexpr int kD64A = kD64Rows * 64;          // packed activation tile
-constexpr int kD64B = kD64Cols * 64;          // packed weight tile
-constexpr int kD64SZ = 4 * 256;               // four 64-row items of 4-byte words
-constexpr int kD64Stage = kD64A + kD64B + kD64SZ;
-constexpr int kD64Half = kD64Rows * 4 * 16;   // one unpacked half (even or odd codes)
-constexpr int kD64Lds = kD64Stages * kD64Stage + 2 * 2 * kD64Half;
+constexpr int kSpCols = 256;                 // columns per workgroup
+constexpr int kSpWaves = 8;
+constexpr int kSpDepth = 6;                  // weight tiles in flight per wave, plus one
+constexpr int kSpLds = 160 * 1024;
+constexpr int kSpTargetGroups = 256;         // one workgroup per CU of MI355X
+constexpr int kSpMinTiles = 8;             // K tiles per range at least (bounds the partial sums)
 
-template <bool ASYM, bool G1>
-__global__ __launch_bounds__(kD64Waves * 64) void k_gemm_dec64(
+struct SplitPlan {
+    int FM = 1;            // 16-row activation fragments
+    int S = 1;             // K ranges
+    int kps = 1;           // K tiles per range (the last range may be shorter)
+    int ap = 0;            // bytes per staged activation row: 64 kps + 16
+    int wr = 0;            // 4-byte words per scale-table row (odd)
+    int a_bytes = 0;       // staged activations, a multiple of 1 KiB
+    int t_bytes = 0;       // one scale (or zero-point) table, a multiple of 256 bytes
+    int lds = 0;
+};
+
+int split_fm(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+SplitPlan split_layout(int M, int kps, bool g1, bool asym) {
+    SplitPlan p;
+    p.FM = split_fm(M);
+    p.kps = kps;
+    p.ap = 64 * kps + 16;
+    p.a_bytes = ceil_div(M * p.ap, 1024) * 1024;
+    p.wr = (kps / 2 + 1) | 1;
+    p.t_bytes = g1 ? ceil_div(kSpCols * p.wr * 4, 256) * 256 : 0;
+    p.lds = p.a_bytes + (asym ? 2 : 1) * p.t_bytes;
+    return p;
+}
+
+SplitPlan split_plan(int M, int N, int K, int group_size, bool asym) {
+    const int KT = K / BK;
+    const bool g1 = K / group_size > 1;
+    const int nbx = ceil_div(N, kSpCols);
+    const int s0 = std::max(1, std::min(KT, ceil_div(kSpTargetGroups, nbx)));
+    int kps = std::max(ceil_div(KT, s0), std::min(KT, kSpMinTiles));
+    while (kps > 1 && split_layout(M, kps, g1, asym).lds > kSpLds) --kps;
+    const int S = ceil_div(KT, kps);
+    SplitPlan p = split_layout(M, ceil_div(KT, S), g1, asym);
+    p.S = S;
+    return p;
+}
+
+template <int FM, int D, bool ASYM, bool G1>
+__global__ __launch_bounds__(kSpWaves * 64) void k_gemm_dec_split(
     const uint8_t* __restrict__ Xq, const uint8_t* __restrict__ Wq,
     const uint16_t* __restrict__ s_w, const uint16_t* __restrict__ z_w,
-    int32_t* __restrict__ part, int M, int N, int K, int kps) {
-    constexpr int D = kD64Stages;
-    constexpr int WAITN = (D - 3) * 2;          // copies per wave and tile: 2
+    int32_t* __restrict__ part, int M, int N, int K, int S, int kps, int wr, int a_bytes,
+    int t_bytes) {
+    static_assert(D >= 2 && D <= 8, "prefetch depth");
     extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t* a8 = lds + D * kD64Stage;          // [buffer][even | odd] unpacked activations
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int frow = lane & 15;
     const int fks = lane >> 4;
-    const int n0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kD64Cols);
+    // workgroups are dealt to the 8 XCDs in turn; when they divide evenly,
+    // XCD x takes the x-th eighth of the (column block, range) list, so all
+    // ranges of a column block share one L2: the rows of the scale tables
+    // (one row holds every range's groups) are fetched once, not once per
+    // range.  The activations are then read by every XCD (64 B per row and
+    // tile, a hundredth of the weights).
+    const int bid = static_cast<int>(blockIdx.x);
+    const int total = static_cast<int>(gridDim.x);
+    const int wid = (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
+    const int by = wid % S;
+    const int n0 = (wid / S) * kSpCols;
     const int KB = K / 2;
     const int KT = K / BK;
     const int G = G1 ? KT : 1;
-    const int kt0 = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.y) * kps);
-    const int nt = max(0, min(KT, kt0 + kps) - kt0);
+    const int kt0 = by * kps;
+    const int nt = min(KT, kt0 + kps) - kt0;        // >= 1: S = ceil(KT / kps)
 
-    // ---- this wave's two copies per tile -----------------------------------
-    // first: activation rows 16 w .. (waves 0-3) or weight rows 16 w .. (4-7);
-    // second: weight rows 16 w .. (0-3) or scale item w - 4 (4-7).  Lane l
-    // moves 16 bytes: row 16 w + l / 4, chunk l % 4 (row-major in the stage).
-    const int crow = 16 * (wave & 3) + (lane >> 2);
-    const int cchk = lane & 3;
-    const bool first_a = wave < 4;
-    const uint8_t* base1 = first_a ? Xq : Wq;
-    uint32_t off1;
-    if (first_a)
-        off1 = static_cast<uint32_t>(min(crow, M - 1)) * KB + cchk * 16;
-    else
-        off1 = static_cast<uint32_t>(min(n0 + 16 * wave + (lane >> 2), N - 1) - n0) * KB + cchk * 16;
-    const uint32_t off2b = static_cast<uint32_t>(min(n0 + 16 * wave + (lane >> 2), N - 1) - n0) * KB + cchk * 16;
-    // scale item it = wave - 4: kind it / 2 (scale, zero point), rows 64 (it % 2) + lane
-    const int it = wave & 3;
-    const uint16_t* szb = (ASYM && it >= 2) ? z_w : s_w;
-    const uint32_t sz_e0 = static_cast<uint32_t>(min(n0 + 64 * (it & 1) + lane, N - 1)) *
-                           static_cast<uint32_t>(G);
-    const int dst1 = first_a ? wave * 1024 : kD64A + wave * 1024;
-    const int dst2 = first_a ? kD64A + wave * 1024 : kD64A + kD64B + it * 256;
-    auto issue = [&](int i) {
-        const int kc = kt0 + min(i, nt - 1);            // clamped: every step copies
-        uint8_t* st = lds + (i % D) * kD64Stage;
-        if (first_a) {
-            dma16_async_sv(Xq + static_cast<size_t>(kc) * 64, off1, st + dst1);
-            dma16_async_sv(Wq + static_cast<size_t>(n0) * KB + static_cast<size_t>(kc) * 64, off2b,
-                           st + dst2);
-        } else {
-            dma16_async_sv(base1 + static_cast<size_t>(n0) * KB + static_cast<size_t>(kc) * 64, off1,
-                           st + dst1);
-            const uint32_t g = G1 ? static_cast<uint32_t>(kc) : 0u;
-            dma4_async_sv(szb, 2u * ((sz_e0 + g) & ~1u), st + dst2);
+    // ---- weight loads of the first D - 1 tiles ------------------------------
+    const uint8_t* wbase = Wq + static_cast<size_t>(n0) * KB + static_cast<size_t>(kt0) * 64;
+    uint32_t boff[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+        boff[b] = static_cast<uint32_t>(min(n0 + 32 * wave + 16 * b + frow, N - 1) - n0) * KB + fks * 16;
+    uint4 bbuf[D][2];
+    int it = 0;
+    auto issue = [&](auto SL) {
+        constexpr int sl = decltype(SL)::value;
+        const uint8_t* wb = wbase + static_cast<size_t>(it) * 64;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) bbuf[sl][b] = *reinterpret_cast<const uint4*>(wb + boff[b]);
+        it = min(it + 1, nt - 1);
+    };
+    static_for<0, D - 1>([&](auto U) { issue(U); });
+
+    // ---- stage the range's activations: slot s of 16 bytes holds row
+    // s / (4 kps + 1), chunk s % (4 kps + 1); the last chunk of a row, and
+    // chunks past the range, are padding (copied from a valid address, never
+    // read).  Lane l of copy j fills slot 64 j + l.
+    const int rslots = 4 * kps + 1;
+    const uint8_t* xbase = Xq + static_cast<size_t>(kt0) * 64;
+    for (int j = wave; j * 64 < a_bytes / 16; j += kSpWaves) {
+        const int s = j * 64 + lane;
+        const int r = s / rslots;
+        const int c = s - r * rslots;
+        const uint32_t off = (r < M && c < 4 * nt) ? static_cast<uint32_t>(r) * KB + c * 16 : 0u;
+        dma16_async_sv(xbase, off, lds + j * 1024);
+    }
+    // ---- stage the scale (and zero-point) table of one-tile groups: row r
+    // holds the 4-byte words from the one containing element (n0 + r) G + kt0
+    // on, so tile t of the range is half (p + t) % 2 of word (p + t) / 2,
+    // p the parity of that first element.  Words past the array are clamped.
+    if constexpr (G1) {
+        const uint32_t last_word = (static_cast<uint32_t>(N) * static_cast<uint32_t>(G) - 1u) >> 1;
+        for (int j = wave; j * 64 < t_bytes / 4; j += kSpWaves) {
+            const int s = j * 64 + lane;
+            const int r = s / wr;
+            const int w = s - r * wr;
+            const uint32_t e0 = static_cast<uint32_t>(min(n0 + r, N - 1)) * static_cast<uint32_t>(G) + kt0;
+            const uint32_t word = min((e0 >> 1) + static_cast<uint32_t>(w), last_word);
+            dma4_async_sv(s_w, 4u * word, lds + a_bytes + j * 256);
+            if constexpr (ASYM) dma4_async_sv(z_w, 4u * word, lds + a_bytes + t_bytes + j * 256);
         }
-    };
+    }
 
-    // ---- unpack of one staged activation tile into int8 halves -------------
-    // lane j of the workgroup (512) takes 8 packed bytes: chunk j / 2 (row
-    // chunk / 4, chunk % 4), half j % 2
-    const int uj = wave * 64 + lane;
-    const int uchunk = uj >> 1, uhalf = uj & 1;
-    auto unpack_a = [&](int i, int buf) {
-        const uint8_t* st = lds + (i % D) * kD64Stage;
-        const uint2 w = *reinterpret_cast<const uint2*>(st + uchunk * 16 + uhalf * 8);
-        const uint2 ev = make_uint2((w.x << 4) & 0xF0F0F0F0u, (w.y << 4) & 0xF0F0F0F0u);
-        const uint2 od = make_uint2(w.x & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u);
-        uint8_t* ab = a8 + buf * 2 * kD64Half;
-        *reinterpret_cast<uint2*>(ab + uchunk * 16 + uhalf * 8) = ev;
-        *reinterpret_cast<uint2*>(ab + kD64Half + uchunk * 16 + uhalf * 8) = od;
-    };
+    // per-lane LDS offsets of the activation fragments (rows past M clamped)
+    uint32_t aoff[FM];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+        aoff[a] = static_cast<uint32_t>(min(16 * a + frow, M - 1)) * (64 * kps + 16) + fks * 16;
+    // the lane's two columns: scale-table word base and parity, or the
+    // per-channel zero point
+    uint32_t tb[2], par[2], zb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int r = 32 * wave + 16 * b + frow;
+        const int ncol = min(n0 + r, N - 1);
+        tb[b] = static_cast<uint32_t>(r * wr);
+        par[b] = (static_cast<uint32_t>(ncol) * static_cast<uint32_t>(G) + kt0) & 1u;
+        zb[b] = 0x80808080u;
+        if constexpr (ASYM && !G1) zb[b] = 0x80808080u - static_cast<uint32_t>(h2f(z_w[ncol])) * 0x01010101u;
+    }
+    const uint32_t* stab = reinterpret_cast<const uint32_t*>(lds + a_bytes);
+    const uint32_t* ztab = reinterpret_cast<const uint32_t*>(lds + a_bytes + t_bytes);
 
-    // per-channel zero point of this lane's column (read before any copy)
-    const int ncol = min(n0 + 16 * wave + frow, N - 1);
-    uint32_t zb_chan = 0x80808080u;
-    if constexpr (ASYM && !G1) zb_chan = (0x80u - static_cast<uint32_t>(h2f(z_w[ncol]))) * 0x01010101u;
-
-    v4i acc[4];
+    v4i acc[FM][2];
+    float facc[G1 ? FM : 1][G1 ? 2 : 1][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) acc[a] = v4i{0, 0, 0, 0};
-    float facc[G1 ? 4 : 1][4];
+    for (int a = 0; a < FM; ++a)
 #pragma unroll
-    for (int a = 0; a < (G1 ? 4 : 1); ++a)
+        for (int b = 0; b < 2; ++b) acc[a][b] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) facc[a][r] = 0.0f;
+    for (int a = 0; a < (G1 ? FM : 1); ++a)
+#pragma unroll
+        for (int b = 0; b < (G1 ? 2 : 1); ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) facc[a][b][r] = 0.0f;
+    // a zero accumulator operand the compiler cannot fold into an inline constant
     v4i zc;
     {
         int z0;
         asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
         zc = v4i{z0, z0, z0, z0};
     }
-    const int brow = 16 * wave + frow;                      // the lane's weight row in the tile
-    const uint32_t spar = static_cast<uint32_t>(ncol) * static_cast<uint32_t>(G);
 
-    if (nt > 0) {
-        // prologue: tiles 0 .. D-2 in flight; tile 0 landed and unpacked
-        for (int i = 0; i < D - 1; ++i) issue(i);
-        wait_vmcnt<(D - 2) * 2>();
-        lds_barrier();
-        unpack_a(0, 0);
-        for (int i = 0; i < nt; ++i) {
-            // tile i + 1 has landed once at most D - 3 newer tiles' copies are
-            // outstanding; after the barrier every wave's copies of it are
-            // visible, every read of tile i - 1's stage is done, and the
-            // unpacked tile i (written before the barrier) is visible
-            wait_vmcnt<WAITN>();
-            lds_barrier();
-            issue(i + D - 1);
-            if (i + 1 < nt) unpack_a(i + 1, (i + 1) & 1);
-            const uint8_t* st = lds + (i % D) * kD64Stage;
-            const uint8_t* ab = a8 + (i & 1) * 2 * kD64Half;
-            const uint4 wb = *reinterpret_cast<const uint4*>(st + kD64A + brow * 64 + fks * 16);
-            uint32_t zbias = zb_chan;
-            float sw = 0.0f;
-            if constexpr (G1) {
-                const uint8_t* szs = st + kD64A + kD64B;
-                const uint32_t sh = 16u * ((spar + static_cast<uint32_t>(kt0 + i)) & 1u);
-                const int so = (brow >> 6) * 256 + 4 * (brow & 63);
-                sw = h2f(static_cast<uint16_t>(*reinterpret_cast<const uint32_t*>(szs + so) >> sh));
-                if constexpr (ASYM) {
-                    const uint16_t zh = static_cast<uint16_t>(
-                        *reinterpret_cast<const uint32_t*>(szs + 512 + so) >> sh);
-                    zbias = (0x80u - static_cast<uint32_t>(h2f(zh))) * 0x01010101u;
-                }
-            }
-            uint4 bev, bod;
-            if constexpr (ASYM)
-                unpack_asym(wb, zbias, bev, bod);
-            else
-                unpack_signed16(wb, bev, bod);
-            const v4i be = v4i{static_cast<int>(bev.x), static_cast<int>(bev.y), static_cast<int>(bev.z), static_cast<int>(bev.w)};
-            const v4i bo = v4i{static_cast<int>(bod.x), static_cast<int>(bod.y), static_cast<int>(bod.z), static_cast<int>(bod.w)};
+    // every copy (and weight load) of this wave has landed; after the
+    // barrier every wave's staged data is visible
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    auto compute = [&](int t, auto SL) {
+        constexpr int sl = decltype(SL)::value;
+        v4i aev[FM], aod[FM], bev[2], bod[2];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int ao = ((16 * a + frow) * 4 + fks) * 16;
-                const v4i ae = *reinterpret_cast<const v4i*>(ab + ao);
-                const v4i aod = *reinterpret_cast<const v4i*>(ab + kD64Half + ao);
-                if constexpr (G1) {
-                    v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae, be, zc, 0, 0, 0);
-                    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod, bo, p, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) facc[a][r] = fmaf(static_cast<float>(p[r]), sw, facc[a][r]);
-                } else {
-                    acc[a] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ae, be, acc[a], 0, 0, 0);
-                    acc[a] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod, bo, acc[a], 0, 0, 0);
-                }
-            }
+        for (int a = 0; a < FM; ++a) {
+            const uint4 w = *reinterpret_cast<const uint4*>(lds + aoff[a] + t * 64);
+            uint4 ev, od;
+            unpack_signed16(w, ev, od);
+            aev[a] = v4i{static_cast<int>(ev.x), static_cast<int>(ev.y), static_cast<int>(ev.z), static_cast<int>(ev.w)};
+            aod[a] = v4i{static_cast<int>(od.x), static_cast<int>(od.y), static_cast<int>(od.z), static_cast<int>(od.w)};
         }
-        // retire the clamped copies still in flight before the workgroup ends
-        wait_vmcnt<0>();
-    }
-
-    // ---- this range's sums: lane (g, li) holds rows 16 a + 4 g + r, column li
-    const int gn = n0 + 16 * wave + frow;
-    if (gn < N) {
-        int32_t* pr = part + static_cast<size_t>(blockIdx.y) * M * N;
+        float sw[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < 2; ++b) {
+            uint32_t bias = zb[b];
+            if constexpr (G1) {
+                const uint32_t q = par[b] + static_cast<uint32_t>(t);
+                const uint32_t wi = tb[b] + (q >> 1);
+                const uint32_t sh = 16u * (q & 1u);
+                sw[b] = h2f(static_cast<uint16_t>(stab[wi] >> sh));
+                if constexpr (ASYM)
+                    bias = 0x80808080u - static_cast<uint32_t>(h2f(static_cast<uint16_t>(ztab[wi] >> sh))) * 0x01010101u;
+            }
+            uint4 ev, od;
+            if constexpr (ASYM)
+                unpack_asym(bbuf[sl][b], bias, ev, od);
+            else
+                unpack_signed16(bbuf[sl][b], ev, od);
+            bev[b] = v4i{static_cast<int>(ev.x), static_cast<int>(ev.y), static_cast<int>(ev.z), static_cast<int>(ev.w)};
+            bod[b] = v4i{static_cast<int>(od.x), static_cast<int>(od.y), static_cast<int>(od.z), static_cast<int>(od.w)};
+        }
+        if constexpr (G1) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aev[a], bev[b], zc, 0, 0, 0);
+                    p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod[a], bod[b], p, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) facc[a][b][r] = fmaf(static_cast<float>(p[r]), sw[b], facc[a][b][r]);
+                }
+        } else {
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aev[a], bev[b], acc[a][b], 0, 0, 0);
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aod[a], bod[b], acc[a][b], 0, 0, 0);
+        }
+    };
+
+    // whole rotations of D tiles with no branch around a step, then at most
+    // D - 1 tiles whose loads are in flight (as in k_gemm_dec)
+    int t = 0;
+    for (; t + D <= nt; t += D) {
+        static_for<0, D>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            issue(std::integral_constant<int, (u + D - 1) % D>{});
+            __builtin_amdgcn_sched_barrier(0);
+            compute(t + u, std::integral_constant<int, u>{});
+        });
+    }
+    static_for<0, D - 1>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        if (t + u < nt) compute(t + u, std::integral_constant<int, u>{});
+    });
+
+    // ---- this range's sums: lane (fks, frow) holds rows 16 a + 4 fks + r of
+    // column n0 + 32 wave + 16 b + frow
+    int32_t* pr = part + static_cast<size_t>(by) * M * N;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int gn = n0 + 32 * wave + 16 * b + frow;
+        if (gn >= N) continue;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int gm = 16 * a + 4 * fks + r;
                 if (gm < M)
-                    pr[static_cast<size_t>(gm) * N + gn] =
-                        G1 ? __float_as_int(facc[a][r]) : acc[a][r];
+                    pr[static_cast<size_t>(gm) * N + gn] = G1 ? __float_as_int(facc[a][b][r]) : acc[a][b][r];
             }
     }
 }
 
 // Y = fp16(s_x[m] * unshift * (sum of the ranges' sums, in range order)
-//          [* s_w[n] per channel])
+//          [* s_w[n] per channel]); thread i takes outputs 4 i .. 4 i + 3 of
+// the row-major [M, N] result (16-byte loads when N % 4 == 0)
 template <bool ASYM, bool G1>
-__global__ __launch_bounds__(256) void k_dec64_reduce(const int32_t* __restrict__ part,
-                                                      const float* __restrict__ s_x,
-                                                      const uint16_t* __restrict__ s_w,
-                                                      uint16_t* __restrict__ Y, int M, int N,
-                                                      int splits) {
-    const long e = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= static_cast<long>(M) * N) return;
-    const int m = static_cast<int>(e / N);
-    const int n = static_cast<int>(e - static_cast<long>(m) * N);
+__global__ __launch_bounds__(256) void k_dec_split_reduce(const int32_t* __restrict__ part,
+                                                          const float* __restrict__ s_x,
+                                                          const uint16_t* __restrict__ s_w,
+                                                          uint16_t* __restrict__ Y, int M, int N,
+                                                          int splits) {
+    const size_t MN = static_cast<size_t>(M) * N;
+    const size_t e0 = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (e0 >= MN) return;
     constexpr float kUnshift = ASYM ? (1.0f / 16.0f) : (1.0f / 256.0f);
-    float v;
-    if constexpr (G1) {
-        v = 0.0f;
-        for (int sp = 0; sp < splits; ++sp) v += __int_as_float(part[static_cast<size_t>(sp) * M * N + e]);
-    } else {
-        int sum = 0;
-        for (int sp = 0; sp < splits; ++sp) sum += part[static_cast<size_t>(sp) * M * N + e];
-        v = static_cast<float>(sum) * h2f(s_w[n]);
+    if ((N & 3) == 0) {
+        // four outputs of one row
+        const int m = static_cast<int>(e0 / N);
+        const int n = static_cast<int>(e0 - static_cast<size_t>(m) * N);
+        float v[4];
+        if constexpr (G1) {
+            float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            for (int sp = 0; sp < splits; ++sp) {
+                const int4 w = *reinterpret_cast<const int4*>(part + sp * MN + e0);
+                acc.x += __int_as_float(w.x);
+                acc.y += __int_as_float(w.y);
+                acc.z += __int_as_float(w.z);
+                acc.w += __int_as_float(w.w);
+            }
+            v[0] = acc.x; v[1] = acc.y; v[2] = acc.z; v[3] = acc.w;
+        } else {
+            int4 acc = make_int4(0, 0, 0, 0);
+            for (int sp = 0; sp < splits; ++sp) {
+                const int4 w = *reinterpret_cast<const int4*>(part + sp * MN + e0);
+                acc.x += w.x;
+                acc.y += w.y;
+                acc.z += w.z;
+                acc.w += w.w;
+            }
+            v[0] = static_cast<float>(acc.x) * h2f(s_w[n]);
+            v[1] = static_cast<float>(acc.y) * h2f(s_w[n + 1]);
+            v[2] = static_cast<float>(acc.z) * h2f(s_w[n + 2]);
+            v[3] = static_cast<float>(acc.w) * h2f(s_w[n + 3]);
+        }
+        const float sx = s_x[m] * kUnshift;
+        ushort4 o;
+        o.x = f2h(v[0] * sx);
+        o.y = f2h(v[1] * sx);
+        o.z = f2h(v[2] * sx);
+        o.w = f2h(v[3] * sx);
+        *reinterpret_cast<ushort4*>(Y + e0) = o;
+        return;
     }
-    Y[e] = f2h(v * s_x[m] * kUnshift);
+    for (size_t e = e0; e < e0 + 4 && e < MN; ++e) {
+        const int m = static_cast<int>(e / N);
+        const int n = static_cast<int>(e - static_cast<size_t>(m) * N);
+        float v;
+        if constexpr (G1) {
+            v = 0.0f;
+            for (int sp = 0; sp < splits; ++sp) v += __int_as_float(part[sp * MN + e]);
+        } else {
+            int sum = 0;
+            for (int sp = 0; sp < splits; ++sp) sum += part[sp * MN + e];
+            v = static_cast<float>(sum) * h2f(s_w[n]);
+        }
+        Y[e] = f2h(v * s_x[m] * kUnshift);
+    }
 }
 
-template <bool ASYM, bool G1>
-hipError_t launch_dec64_k(const GemmArgs& a, void* ws, hipStream_t stream) {
-    auto* kern = &k_gemm_dec64<ASYM, G1>;
+template <int FM, bool ASYM, bool G1>
+hipError_t launch_split_k(const GemmArgs& a, const SplitPlan& p, void* ws, hipStream_t stream) {
+    auto* kern = &k_gemm_dec_split<FM, kSpDepth, ASYM, G1>;
     static bool raised[64] = {};
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64 || !raised[dev]) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kD64Lds);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kSpLds);
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) raised[dev] = true;
     }
-    const int KT = a.K / BK;
-    const int kps = ceil_div(KT, kD64Split);
     int32_t* part = static_cast<int32_t*>(ws);
-    kern<<<dim3(ceil_div(a.N, kD64Cols), kD64Split), dim3(kD64Waves * 64), kD64Lds, stream>>>(
-        a.Xq, a.Wq, a.s_w, a.z_w, part, a.M, a.N, a.K, kps);
+    const unsigned groups = static_cast<unsigned>(ceil_div(a.N, kSpCols) * p.S);
+    kern<<<dim3(groups), dim3(kSpWaves * 64), p.lds, stream>>>(a.Xq, a.Wq, a.s_w, a.z_w, part, a.M, a.N,
+                                                                a.K, p.S, p.kps, p.wr, p.a_bytes,
+                                                                p.t_bytes);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long total = static_cast<long>(a.M) * a.N;
-    k_dec64_reduce<ASYM, G1><<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
-        part, a.s_x, a.s_w, a.Y, a.M, a.N, kD64Split);
+    const long quads = (static_cast<long>(a.M) * a.N + 3) / 4;
+    k_dec_split_reduce<ASYM, G1><<<static_cast<unsigned>((quads + 255) / 256), 256, 0, stream>>>(
+        part, a.s_x, a.s_w, a.Y, a.M, a.N, p.S);
     return hipGetLastError();
 }
 
-// per channel or groups of one K tile only
-bool dec64_supports(const GemmArgs& a) {
-    const int G = a.K / a.group_size;
-    return (G == 1 || a.group_size == BK) &&
-           static_cast<size_t>(a.N) * static_cast<size_t>(G) < (size_t{1} << 31);
-}
-
-hipError_t launch_dec64(const GemmArgs& a, void* ws, hipStream_t stream) {
+template <int FM>
+hipError_t launch_split_f(const GemmArgs& a, const SplitPlan& p, void* ws, hipStream_t stream) {
     const bool g1 = (a.K / a.group_size) > 1;
     if (a.asym)
-        return g1 ? launch_dec64_k<true, true>(a, ws, stream) : launch_dec64_k<true, false>(a, ws, stream);
-    return g1 ? launch_dec64_k<false, true>(a, ws, stream) : launch_dec64_k<false, false>(a, ws, stream);
+        return g1 ? launch_split_k<FM, true, true>(a, p, ws, stream)
+                  : launch_split_k<FM, true, false>(a, p, ws, stream);
+    return g1 ? launch_split_k<FM, false, true>(a, p, ws, stream)
+              : launch_split_k<FM, false, false>(a, p, ws, stream);
+}
+
+// per channel, or groups of one K tile; at most 64 tokens
+bool split_supports(const GemmArgs& a) {
+    const int G = a.K / a.group_size;
+    if (a.M < 1 || a.M > 64 || !(G == 1 || a.group_size == BK)) return false;
+    return static_cast<size_t>(a.N) * static_cast<size_t>(G) < (size_t{1} << 31);
+}
+
+size_t split_workspace_bytes(int M, int N, int K, int group_size, bool asym) {
+    const SplitPlan p = split_plan(M, N, K, group_size, asym);
+    const size_t b = sizeof(int32_t) * static_cast<size_t>(p.S) * static_cast<size_t>(M) * static_cast<size_t>(N);
+    return (b + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_split(const GemmArgs& a, void* ws, hipStream_t stream) {
+    const SplitPlan p = split_plan(a.M, a.N, a.K, a.group_size, a.asym);
+    if (p.FM == 1) return launch_split_f<1>(a, p, ws, stream);
+    if (p.FM == 2) return launch_split_f<2>(a, p, ws, stream);
+    return launch_split_f<4>(a, p, ws, stream);
 }
 
 using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
@@ -646,10 +779,10 @@ const KernelCfg kDec[3][kNumDec] = {
 #undef W4A4_DEC
 
 // the split-K kernel (index kNumDec of the override): measured on MI355X for
-// 64 tokens, 28672 -> 8192 in groups of 128 (see the K-loop comment there);
-// taken automatically above 32 tokens where it applies
-bool use_dec64(const GemmArgs& a) {
-    if (!dec64_supports(a)) return false;
+// 64 tokens, 28672 -> 8192 in groups of 128; taken automatically above 32
+// tokens where it applies
+bool use_split(const GemmArgs& a) {
+    if (!split_supports(a)) return false;
     const int o = kernel_override(1);
     if (o >= 0 && o <= kNumDec) return o == kNumDec;
     return a.M > 32;
@@ -689,21 +822,32 @@ const KernelCfg& choose_dec(const GemmArgs& a) {
 
 int gemm_num_decode_configs() { return kNumDec + 1; }
 
-size_t gemm_decode_workspace_bytes(int M, int N) {
-    const size_t b = sizeof(int32_t) * kD64Split * static_cast<size_t>(M) * static_cast<size_t>(N);
-    return (b + 255) & ~static_cast<size_t>(255);
+size_t gemm_decode_workspace_bytes(int M, int N, int K, int group_size, bool asym) {
+    GemmArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.group_size = group_size;
+    a.asym = asym;
+    return split_supports(a) ? split_workspace_bytes(M, N, K, group_size, asym) : 0;
 }
 
 const char* gemm_decode_kernel_name(const GemmArgs& a) {
-    if (use_dec64(a)) return "k_gemm_dec64<64x128, waves 8, 6 stages, K split 4> + k_dec64_reduce";
+    if (use_split(a)) {
+        const int fm = split_fm(a.M);
+        return fm == 1 ? "k_gemm_dec_split<FM 1, 256 columns, waves 8, depth 6> + k_dec_split_reduce"
+             : fm == 2 ? "k_gemm_dec_split<FM 2, 256 columns, waves 8, depth 6> + k_dec_split_reduce"
+                       : "k_gemm_dec_split<FM 4, 256 columns, waves 8, depth 6> + k_dec_split_reduce";
+    }
     return choose_dec(a).name;
 }
 
 hipError_t gemm_decode_launch(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
-    if (use_dec64(a)) {
-        if (ws == nullptr || ws_bytes < gemm_decode_workspace_bytes(a.M, a.N)) return hipErrorInvalidValue;
-        return launch_dec64(a, ws, stream);
+    if (use_split(a)) {
+        if (ws == nullptr || ws_bytes < split_workspace_bytes(a.M, a.N, a.K, a.group_size, a.asym))
+            return hipErrorInvalidValue;
+        return launch_split(a, ws, stream);
     }
     const KernelCfg& k = choose_dec(a);
     return (a.K / a.group_size) > 1 ? k.group(a, stream) : k.chan(a, stream);

@@ -71,8 +71,9 @@ hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_byte
 constexpr int kDecodeMaxM = 64;
 const char* gemm_decode_kernel_name(const GemmArgs& a);
 hipError_t gemm_decode_launch(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
-// workspace of the split-K decode kernel (partial sums of M tokens x N)
-size_t gemm_decode_workspace_bytes(int M, int N);
+// workspace of the split-K decode kernel (partial sums of M tokens x N per
+// K range); 0 for shapes it does not take
+size_t gemm_decode_workspace_bytes(int M, int N, int K, int group_size, bool asym);
 
 // ---- single-kernel decode layer (linear_decode.hip) --------------------------
 // ---- INT4 GEMM on the fp6 matrix pipe (gemm_f6.hip) ------------------------
