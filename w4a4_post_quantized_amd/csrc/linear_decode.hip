@@ -83,7 +83,9 @@ struct LdCfg {
     static constexpr int FRAG = 64 * 8;          // fp16 elements of one fragment
     static constexpr int P1BYTES = KS2 * FRAG * 2 * 2;   // hi + lo fragments of one block
     static constexpr int XROW = N2 * 2 + 16;     // staged X̄ row, padded 16 bytes
-    static constexpr int XBYTES = N1 * XROW;
+    // the staged token, rounded up to whole 64-lane copies of 16 bytes
+    static constexpr int XCOPIES = (N1 * (XROW / 16) + 63) / 64;
+    static constexpr int XBYTES = XCOPIES * 1024;
     static constexpr int QBYTES = 16 * N2 / 2;   // packed codes of one unit
     static constexpr int PROD_LDS = P1BYTES + XBYTES + QBYTES;
     static_assert(CB == kLdWaves, "one wave per 16-column block");
@@ -161,37 +163,43 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
         for (int ks = 0; ks < C::KS1; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) p2v[ks][e] = p.P2[(32 * ks + 8 * g + e) * N2 + 16 * cb + li];
-        constexpr int XCH = K / 8;
-        constexpr int XLD = (XCH + NT - 1) / NT;
-        uint4 xr[XLD];
-#pragma unroll
-        for (int i = 0; i < XLD; ++i)
-            xr[i] = reinterpret_cast<const uint4*>(p.X + static_cast<size_t>(m) * K)[min(tid + i * NT, XCH - 1)];
+        // X̄ goes to LDS by direct copies: 16-byte slot s holds row
+        // s / (N2 / 8 + 1), chunk s % (N2 / 8 + 1); the last chunk of a row,
+        // and slots past the token, are padding (copied from the token's
+        // first chunk, never read)
+        {
+            constexpr int RS = N2 / 8 + 1;
+            const uint16_t* xb = p.X + static_cast<size_t>(m) * K;
+            for (int j = wave; j < C::XCOPIES; j += NW) {
+                const int s = j * 64 + lane;
+                const int r = s / RS;
+                const int c = s - r * RS;
+                const uint32_t off = (r < N1 && c < RS - 1) ? static_cast<uint32_t>(r * N2 * 2 + c * 16) : 0u;
+                dma16_async_sv(xb, off, xs + j * 1024);
+            }
+        }
         constexpr int PIECES = N1 * 4;
         constexpr int MAXI = (PIECES + NT - 1) / NT;
         float4 pv[MAXI];
-        float m1 = 0.0f;
 #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
             const int idx = min(tid + i * NT, PIECES - 1);
             const int rho = idx >> 2;
             const int c4 = idx & 3;
             pv[i] = *reinterpret_cast<const float4*>(p.P1 + static_cast<size_t>(rho) * N1 + 16 * part + 4 * c4);
+        }
+        // all loads in flight before the first use of any
+        __builtin_amdgcn_sched_barrier(0);
+        float m1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i)
             if (tid + i * NT < PIECES)
                 m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(pv[i].x), fabsf(pv[i].y)),
                                      fmaxf(fabsf(pv[i].z), fabsf(pv[i].w))));
-        }
-#pragma unroll
-        for (int i = 0; i < XLD; ++i) {
-            const int c = tid + i * NT;
-            if (c < XCH) {
-                const int row = c / (N2 / 8);
-                const int col = c - row * (N2 / 8);
-                *reinterpret_cast<uint4*>(xs + row * C::XROW + col * 16) = xr[i];
-            }
-        }
         m1 = wave_max(m1);
         if (lane == 0) red8[wave] = m1;
+        // this wave's copies of X̄ have landed; after the barrier every wave's have
+        wait_vmcnt<0>();
         __syncthreads();
         m1 = 0.0f;
 #pragma unroll

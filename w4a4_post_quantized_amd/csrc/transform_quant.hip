@@ -967,7 +967,9 @@ struct ColsCfg {
     static constexpr int FRAG = 64 * 8;          // fp16 elements of one fragment
     static constexpr int FRAG_BYTES = 2 * FRAG * 2;   // hi + lo
     static constexpr int XROW = N2 * 2 + 16;         // staged X̄ row, bytes
-    static constexpr int XBYTES = N1 * XROW;
+    // the staged token, rounded up to whole 64-lane copies of 16 bytes
+    static constexpr int XCOPIES = (N1 * (XROW / 16) + 63) / 64;
+    static constexpr int XBYTES = XCOPIES * 1024;
     // row blocks of P1 fragments that fit beside the staged token
     static constexpr int MAX_RBP = (kColsLdsMax - XBYTES) / (KS2 * FRAG_BYTES);
     static_assert(CB == kColsWaves, "one wave per 16-column block of a token");
@@ -1024,12 +1026,21 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
     for (int ks = 0; ks < C::KS1; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) p2v[ks][e] = P2[(32 * ks + 8 * g + e) * N2 + 16 * cb + li];
-    constexpr int XCH = C::K / 8;                    // 16-byte chunks of one token
-    constexpr int XLD = (XCH + NT - 1) / NT;
-    uint4 xr[XLD];
-#pragma unroll
-    for (int i = 0; i < XLD; ++i)
-        xr[i] = reinterpret_cast<const uint4*>(X + static_cast<size_t>(m) * C::K)[min(tid + i * NT, XCH - 1)];
+    // the token's X̄ goes to LDS by direct copies: 16-byte slot s holds row
+    // s / (N2 / 8 + 1), chunk s % (N2 / 8 + 1); the last chunk of a row, and
+    // slots past the token, are padding (copied from the token's first
+    // chunk, never read)
+    {
+        constexpr int RS = N2 / 8 + 1;
+        const uint16_t* xb = X + static_cast<size_t>(m) * C::K;
+        for (int j = wave; j < C::XCOPIES; j += kColsWaves) {
+            const int s = j * 64 + lane;
+            const int r = s / RS;
+            const int c = s - r * RS;
+            const uint32_t off = (r < N1 && c < RS - 1) ? static_cast<uint32_t>(r * N2 * 2 + c * 16) : 0u;
+            dma16_async_sv(xb, off, xs + j * 1024);
+        }
+    }
 
     // ---- P1 fragments of row blocks ob0 .. ob0+nob-1 into LDS ----------------
     // fragment (ob, sk), lane (gg, ii), element e holds P1[rho][16*ob + ii],
@@ -1038,32 +1049,35 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
     // columns are read as 16-byte row pieces (rows rho, 4 columns each, all
     // loads issued before the first wait), its max |P1| gives the power-of-
     // two prescale, and each piece is scattered to 4 fragment lanes.
+    // Every load of the kernel (P2 columns, X̄, P1 pieces) is issued before
+    // the first use of any: a piece load guarded by its own use, or an X̄
+    // load sunk next to its LDS store, would wait for memory once per load.
+    // A batch of pieces past the part (a uniform test) is skipped; inside a
+    // batch the index is clamped.
     constexpr int MAXI = (N1 * 4 * C::MAX_RBP + NT - 1) / NT;
     const int pieces = N1 * 4 * nob;                 // 16-byte pieces of the part
     float4 pv[MAXI];
-    float m1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < MAXI; ++i) {
-        const int idx = tid + i * NT;
-        if (idx < pieces) {
+        if (i * NT < pieces) {
+            const int idx = min(tid + i * NT, pieces - 1);
             const int rho = idx / (4 * nob);
             const int c4 = idx - rho * (4 * nob);
             pv[i] = *reinterpret_cast<const float4*>(P1 + static_cast<size_t>(rho) * N1 + 16 * ob0 + 4 * c4);
-            m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(pv[i].x), fabsf(pv[i].y)),
-                                 fmaxf(fabsf(pv[i].z), fabsf(pv[i].w))));
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    float m1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < XLD; ++i) {
-        const int c = tid + i * NT;
-        if (c < XCH) {
-            const int row = c / (N2 / 8);
-            const int col = c - row * (N2 / 8);
-            *reinterpret_cast<uint4*>(xs + row * C::XROW + col * 16) = xr[i];
-        }
+    for (int i = 0; i < MAXI; ++i) {
+        if (tid + i * NT < pieces)
+            m1 = fmaxf(m1, fmaxf(fmaxf(fabsf(pv[i].x), fabsf(pv[i].y)),
+                                 fmaxf(fabsf(pv[i].z), fabsf(pv[i].w))));
     }
     m1 = wave_max(m1);
     if (lane == 0) red[wave] = m1;
+    // this wave's copies of X̄ have landed; after the barrier every wave's have
+    wait_vmcnt<0>();
     __syncthreads();
     m1 = 0.0f;
 #pragma unroll
