@@ -51,7 +51,7 @@ def lane_layout(BM, BN, NW, M, N, K, m0, n0):
     isA = ((i * NW + w) * 64 < BM * 4) & np.ones_like(lane, dtype=bool)
     jj = np.where(isA, j, j - BM * 4)
     row = jj >> 2
-    c = (jj & 3) ^ (((row >> 1) ^ (row >> 3)) & 3)
+    c = (jj & 3) ^ ((row >> 2) & 3)
     r = np.where(isA, np.minimum(m0 + row, M - 1), np.minimum(n0 + row, N - 1))
     off = (r - np.where(isA, m0, n0)) * KB + c * 16
     return isA, r, c, off

@@ -300,15 +300,17 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_w4a4(
 // STAGES LDS buffers with global_load_lds_dwordx4 (no VGPR staging, no VALU,
 // no ds_write), STAGES-1 tiles in flight.  A packed row of a K tile is 64
 // bytes (4 chunks of 32 codes); chunk c of row r sits at 16-byte slot
-// c ^ (((r >> 1) ^ (r >> 3)) & 3), which keeps the 16 (or 8) rows one
-// ds_read_b128 touches in distinct banks.  A lane reads one packed chunk and
+// c ^ ((r >> 2) & 3).  With it the fragment reads (lane l: row l % 32,
+// chunk 2p + l / 32) count no LDS bank conflict on gfx950
+// (SQ_LDS_BANK_CONFLICT 0 against 4 cycles per ds_read_b128 with the
+// slot c ^ (((r >> 1) ^ (r >> 3)) & 3) used before).  A lane reads one packed chunk and
 // unpacks it into two 32x32x32 fragments: the even codes (low nibbles) for
 // one k-step and the odd codes (high nibbles) for the next; A and B use the
 // same order, so the products are those of the tile.  Signed codes are kept
 // as 16*q (nibble in the high half of the byte); asymmetric weights become
 // u - z.
 // ===========================================================================
-__device__ __forceinline__ int dl_slot(int row, int c) { return c ^ (((row >> 1) ^ (row >> 3)) & 3); }
+__device__ __forceinline__ int dl_slot(int row, int c) { return c ^ ((row >> 2) & 3); }
 
 // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8
 // XCDs (workgroup L to XCD L % 8), each with its own L2.  The 1-D grid index
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
         const bool isA = (i * NW + wave_u) * 64 < BM * 4;
         const int jj = isA ? j : j - BM * 4;
         const int row = jj >> 2;
-        const int c = (jj & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+        const int c = (jj & 3) ^ ((row >> 2) & 3);
         const int r = isA ? min(m0 + row, M - 1) : min(n0 + row, N - 1);
         if constexpr (kBuiltinCopies)
             src[i] = (isA ? Xq : Wq) + static_cast<size_t>(r) * KB + c * 16;
