@@ -360,7 +360,7 @@ hipError_t launch_dec(const GemmArgs& a, hipStream_t stream) {
 // Split-K decode kernel (M <= 64 tokens): a workgroup of 8 waves owns 256
 // output columns (32 per wave, two 16-column fragments) and one of S ranges
 // of K tiles.  Before its K loop it copies the range's activation rows
-// (packed, M rows, each padded by one 16-byte chunk) and, for groups of one
+// (packed, M rows, each padded to a bank-friendly pitch) and, for groups of one
 // K tile, the range's weight scales and zero points of its columns into LDS,
 // all by global_load_lds copies issued from inline assembly and retired by
 // one wait.  The packed weights then stream from HBM into registers as in
@@ -386,7 +386,7 @@ struct SplitPlan {
     int FM = 1;            // 16-row activation fragments
     int S = 1;             // K ranges
     int kps = 1;           // K tiles per range (the last range may be shorter)
-    int ap = 0;            // bytes per staged activation row: 64 kps + 16
+    int ap = 0;            // bytes per staged activation row (split_row_pitch)
     int wr = 0;            // 4-byte words per scale-table row (odd)
     int a_bytes = 0;       // staged activations, a multiple of 1 KiB
     int t_bytes = 0;       // one scale (or zero-point) table, a multiple of 256 bytes
@@ -395,11 +395,17 @@ struct SplitPlan {
 
 int split_fm(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
+// bytes per staged activation row: the range's 64 kps bytes rounded up to
+// 256 plus 32, so that the 16 rows one fragment read touches (4 chunks of 16
+// bytes each) fall in distinct LDS banks (a pitch of 64 kps + 16 counted 2
+// conflict cycles per ds_read_b128 of the workgroup, one of 32 mod 256 none)
+__host__ __device__ constexpr int split_row_pitch(int kps) { return (64 * kps + 255) / 256 * 256 + 32; }
+
 SplitPlan split_layout(int M, int kps, bool g1, bool asym) {
     SplitPlan p;
     p.FM = split_fm(M);
     p.kps = kps;
-    p.ap = 64 * kps + 16;
+    p.ap = split_row_pitch(kps);
     p.a_bytes = ceil_div(M * p.ap, 1024) * 1024;
     p.wr = (kps / 2 + 1) | 1;
     p.t_bytes = g1 ? ceil_div(kSpCols * p.wr * 4, 256) * 256 : 0;
@@ -467,10 +473,10 @@ __global__ __launch_bounds__(kSpWaves * 64) void k_gemm_dec_split(
     static_for<0, D - 1>([&](auto U) { issue(U); });
 
     // ---- stage the range's activations: slot s of 16 bytes holds row
-    // s / (4 kps + 1), chunk s % (4 kps + 1); the last chunk of a row, and
-    // chunks past the range, are padding (copied from a valid address, never
-    // read).  Lane l of copy j fills slot 64 j + l.
-    const int rslots = 4 * kps + 1;
+    // s / RS, chunk s % RS (RS = split_row_pitch(kps) / 16); chunks past the
+    // range's 4 nt and rows past M are padding (copied from a valid address,
+    // never read).  Lane l of copy j fills slot 64 j + l.
+    const int rslots = split_row_pitch(kps) / 16;
     const uint8_t* xbase = Xq + static_cast<size_t>(kt0) * 64;
     for (int j = wave; j * 64 < a_bytes / 16; j += kSpWaves) {
         const int s = j * 64 + lane;
@@ -500,7 +506,7 @@ __global__ __launch_bounds__(kSpWaves * 64) void k_gemm_dec_split(
     uint32_t aoff[FM];
 #pragma unroll
     for (int a = 0; a < FM; ++a)
-        aoff[a] = static_cast<uint32_t>(min(16 * a + frow, M - 1)) * (64 * kps + 16) + fks * 16;
+        aoff[a] = static_cast<uint32_t>(min(16 * a + frow, M - 1)) * split_row_pitch(kps) + fks * 16;
     // the lane's two columns: scale-table word base and parity, or the
     // per-channel zero point
     uint32_t tb[2], par[2], zb[2];

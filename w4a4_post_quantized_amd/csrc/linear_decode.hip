@@ -82,7 +82,9 @@ struct LdCfg {
     static constexpr int KS2 = N1 / 32;          // stage-2 MFMA k-steps
     static constexpr int FRAG = 64 * 8;          // fp16 elements of one fragment
     static constexpr int P1BYTES = KS2 * FRAG * 2 * 2;   // hi + lo fragments of one block
-    static constexpr int XROW = N2 * 2 + 16;     // staged X̄ row, padded 16 bytes
+    // staged X̄ row: rows of 256 bytes padded by 32 (no LDS bank conflict in
+    // the stage-1 operand reads; 16 bytes gave 4 cycles per read), others 16
+    static constexpr int XROW = N2 * 2 + ((N2 * 2) % 256 == 0 ? 32 : 16);
     // the staged token, rounded up to whole 64-lane copies of 16 bytes
     static constexpr int XCOPIES = (N1 * (XROW / 16) + 63) / 64;
     static constexpr int XBYTES = XCOPIES * 1024;
@@ -163,18 +165,18 @@ __global__ __launch_bounds__(kLdThreads) void k_linear_dec(LdArgs p) {
         for (int ks = 0; ks < C::KS1; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) p2v[ks][e] = p.P2[(32 * ks + 8 * g + e) * N2 + 16 * cb + li];
-        // X̄ goes to LDS by direct copies: 16-byte slot s holds row
-        // s / (N2 / 8 + 1), chunk s % (N2 / 8 + 1); the last chunk of a row,
-        // and slots past the token, are padding (copied from the token's
-        // first chunk, never read)
+        // X̄ goes to LDS by direct copies: 16-byte slot s holds row s / RS,
+        // chunk s % RS (RS = XROW / 16); the chunks past the row's N2 / 8 and
+        // the slots past the token are padding (copied from the token's first
+        // chunk, never read)
         {
-            constexpr int RS = N2 / 8 + 1;
+            constexpr int RS = C::XROW / 16;
             const uint16_t* xb = p.X + static_cast<size_t>(m) * K;
             for (int j = wave; j < C::XCOPIES; j += NW) {
                 const int s = j * 64 + lane;
                 const int r = s / RS;
                 const int c = s - r * RS;
-                const uint32_t off = (r < N1 && c < RS - 1) ? static_cast<uint32_t>(r * N2 * 2 + c * 16) : 0u;
+                const uint32_t off = (r < N1 && c < N2 / 8) ? static_cast<uint32_t>(r * N2 * 2 + c * 16) : 0u;
                 dma16_async_sv(xb, off, xs + j * 1024);
             }
         }

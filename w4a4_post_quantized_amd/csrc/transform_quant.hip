@@ -177,9 +177,11 @@ struct FusedCfg {
     static constexpr int TPI = NW / CB;          // tokens per workgroup iteration
     static_assert(NW % CB == 0 && NW <= 8, "unsupported n2");
     static constexpr int P1F = RB * KS2 * 64 * 8;  // fp16 elements of one P1 fragment set
-    // X̄ staging: token rows padded by 16 bytes so the 16 rows one MFMA
-    // operand read touches fall in distinct LDS banks
-    static constexpr int XROW = N2 * 2 + 16;       // bytes per staged row
+    // X̄ staging: token rows padded so that the 16 rows one MFMA operand
+    // read touches fall in distinct LDS banks.  Rows of 256 bytes take 32
+    // bytes of padding: with 16 the bank-conflict counter showed 4 cycles per
+    // ds_read_b128 of this pattern (16 rows x 4 chunks), with 32 none.
+    static constexpr int XROW = N2 * 2 + ((N2 * 2) % 256 == 0 ? 32 : 16);   // bytes per staged row
     static constexpr int XSLOT = N1 * XROW;        // bytes per staged token
     static constexpr int XCH = K / 8;              // 16-byte chunks per token in HBM
     static constexpr int XLD = (TPI * XCH + NT - 1) / NT;  // chunks per thread per tile
@@ -966,7 +968,9 @@ struct ColsCfg {
     static constexpr int KS2 = (N1 + 31) / 32;   // stage-2 MFMA k-steps
     static constexpr int FRAG = 64 * 8;          // fp16 elements of one fragment
     static constexpr int FRAG_BYTES = 2 * FRAG * 2;   // hi + lo
-    static constexpr int XROW = N2 * 2 + 16;         // staged X̄ row, bytes
+    // staged X̄ row, bytes: padded as in the fused path (32 bytes for rows
+    // of 256 bytes: no bank conflict in the stage-1 operand reads)
+    static constexpr int XROW = N2 * 2 + ((N2 * 2) % 256 == 0 ? 32 : 16);
     // the staged token, rounded up to whole 64-lane copies of 16 bytes
     static constexpr int XCOPIES = (N1 * (XROW / 16) + 63) / 64;
     static constexpr int XBYTES = XCOPIES * 1024;
@@ -1027,17 +1031,17 @@ __global__ __launch_bounds__(kColsWaves * 64) void k_tq_cols(const uint16_t* __r
 #pragma unroll
         for (int e = 0; e < 8; ++e) p2v[ks][e] = P2[(32 * ks + 8 * g + e) * N2 + 16 * cb + li];
     // the token's X̄ goes to LDS by direct copies: 16-byte slot s holds row
-    // s / (N2 / 8 + 1), chunk s % (N2 / 8 + 1); the last chunk of a row, and
-    // slots past the token, are padding (copied from the token's first
-    // chunk, never read)
+    // s / RS, chunk s % RS (RS = XROW / 16); the chunks past the row's N2 / 8
+    // and the slots past the token are padding (copied from the token's
+    // first chunk, never read)
     {
-        constexpr int RS = N2 / 8 + 1;
+        constexpr int RS = C::XROW / 16;
         const uint16_t* xb = X + static_cast<size_t>(m) * C::K;
         for (int j = wave; j < C::XCOPIES; j += kColsWaves) {
             const int s = j * 64 + lane;
             const int r = s / RS;
             const int c = s - r * RS;
-            const uint32_t off = (r < N1 && c < RS - 1) ? static_cast<uint32_t>(r * N2 * 2 + c * 16) : 0u;
+            const uint32_t off = (r < N1 && c < N2 / 8) ? static_cast<uint32_t>(r * N2 * 2 + c * 16) : 0u;
             dma16_async_sv(xb, off, xs + j * 1024);
         }
     }
