@@ -215,7 +215,16 @@ int w4a4_transform(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
 /* INT4 x INT4 GEMM                                                          */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace w4a4_gemm needs for M tokens (0 is possible). */
+/* Bytes of workspace w4a4_gemm needs for M tokens (0 is possible).  The
+ * library owns its contents during a call and leaves nothing in it that a
+ * later call reads:
+ *  - M <= 64 with per-channel weights or groups of 128: the int32 (fp32 for
+ *    groups) partial sums of the split-K decode kernel, S ranges x M x N, S
+ *    chosen from the shape (e.g. 8 for K = 28672, N = 8192);
+ *  - M > 64 with asymmetric groups of 128: the per-token group sums of the
+ *    zero-point correction, M x (K / 128 rounded up to a multiple of 16) fp16
+ *    words;
+ *  - otherwise none. */
 size_t w4a4_gemm_workspace_bytes(int32_t M, const w4a4_weight_desc* desc);
 
 /* Y = dequant(Xq · Wq^T) — FlatQuant page, section 核心思想, the product
