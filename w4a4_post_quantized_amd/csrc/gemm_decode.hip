@@ -71,42 +71,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
     const int t0 = (KT * wave) / NW;
     const int t1 = (KT * (wave + 1)) / NW;
     const int GP = G + 1;          // scale-table row: an odd number of words
-    const int AP = KB + 16;        // staged activation row, padded one chunk
+    // staged activation row: KB rounded up to 256 bytes plus 32, so that the
+    // 16 rows one fragment read touches fall in distinct LDS banks
+    const int AP = (KB + 255) / 256 * 256 + 32;
     uint32_t* sz = reinterpret_cast<uint32_t*>(lds);
     uint8_t* al = lds + (SZ ? BN * GP * 4 : 0);
-
-    // ---- stage the scale table and the activations ------------------------
-    if constexpr (SZ) {
-        for (int r = wave; r < BN; r += NW) {
-            const size_t nrow = static_cast<size_t>(min(n0 + r, N - 1)) * G;
-            for (int gb = 0; gb < G; gb += 256) {
-                uint32_t v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int g = min(gb + lane + 64 * j, G - 1);
-                    v[j] = (MODE == kModeGroup) ? s_w[nrow + g] : 0u;
-                    if constexpr (ASYM) v[j] |= static_cast<uint32_t>(h2f(z_w[nrow + g])) << 16;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (gb + lane + 64 * j < G) sz[r * GP + gb + lane + 64 * j] = v[j];
-            }
-        }
-    }
-    if constexpr (ALDS) {
-        const int CH = KB / 16;
-        for (int c = threadIdx.x; c < CH; c += NT)
-            for (int r0 = 0; r0 < M; r0 += 4) {
-                uint4 v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    v[j] = *reinterpret_cast<const uint4*>(Xq + static_cast<size_t>(min(r0 + j, M - 1)) * KB + c * 16);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (r0 + j < M) *reinterpret_cast<uint4*>(al + (r0 + j) * AP + c * 16) = v[j];
-            }
-    }
-    if constexpr (SZ || ALDS) __syncthreads();
 
     // per-lane byte offsets (32-bit) from the wave-uniform bases
     uint32_t aoff[FM], boff[FN], zoff[FN];
@@ -160,6 +129,55 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
         for (int b = 0; b < FN; ++b) bbuf[SL][b] = *reinterpret_cast<const uint4*>(wb + boff[b]);
         it = min(it + 1, t1 - 1);
     };
+    // the first D - 1 tiles' loads go out before the staging below, which
+    // then overlaps them
+    if (t0 < t1) static_for<0, D - 1>([&](auto U) { issue(U); });
+
+    // ---- stage the activations and the scale table ---------------------------
+    if constexpr (ALDS) {
+        // activation rows by direct-to-LDS copies: 16-byte slot s of the
+        // staged block holds row s / RS, chunk s % RS (RS = AP / 16); chunks
+        // past the row's KB / 16 and rows past M are padding (copied from a
+        // valid address, never read).  Lane l of copy j fills slot 64 j + l.
+        const int RS = AP / 16;
+        const int nslots = M * RS;
+        for (int j = wave; j * 64 < nslots; j += NW) {
+            const int s = j * 64 + lane;
+            const int r = s / RS;
+            const int c = s - r * RS;
+            const uint32_t off = (r < M && c < KB / 16) ? static_cast<uint32_t>(r) * KB + c * 16 : 0u;
+            dma16_async_sv(Xq, off, al + j * 1024);
+        }
+    }
+    if constexpr (SZ) {
+        // the wave's rows wave, wave + NW, ...: every load of a chunk of 256
+        // groups is issued before the first store
+        constexpr int R = (BN + NW - 1) / NW;
+        for (int gb = 0; gb < G; gb += 256) {
+            uint32_t v[R][4];
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int r = min(wave + q * NW, BN - 1);
+                const size_t nrow = static_cast<size_t>(min(n0 + r, N - 1)) * G;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int g = min(gb + lane + 64 * j, G - 1);
+                    v[q][j] = (MODE == kModeGroup) ? s_w[nrow + g] : 0u;
+                    if constexpr (ASYM) v[q][j] |= static_cast<uint32_t>(h2f(z_w[nrow + g])) << 16;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                const int r = wave + q * NW;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (r < BN && gb + lane + 64 * j < G) sz[r * GP + gb + lane + 64 * j] = v[q][j];
+            }
+        }
+    }
+    if constexpr (ALDS) wait_vmcnt<0>();            // this wave's copies have landed
+    if constexpr (SZ || ALDS) __syncthreads();
+
     // compute position: group cg of tile t and its place cr inside the group
     int cg = t0 / TPG, cr = t0 - (t0 / TPG) * TPG;
     auto compute = [&](int t, auto S) {
@@ -246,7 +264,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_dec(
     // flight and drained the prefetch), then at most D - 1 tiles whose loads
     // are already in flight.  Tile t uses buffer slot (t - t0) % D.
     if (t0 < t1) {
-        static_for<0, D - 1>([&](auto U) { issue(U); });
         int t = t0;
         for (; t + D <= t1; t += D) {
             static_for<0, D>([&](auto U) {
@@ -339,7 +356,9 @@ hipError_t launch_dec_a(const GemmArgs& a, hipStream_t stream) {
     const int G = a.K / a.group_size;
     const bool sz = (MODE == kModeGroup) || ASYM;
     const size_t szb = sz ? static_cast<size_t>(BN) * (G + 1) * 4 : 0;
-    const size_t alb = static_cast<size_t>(a.M) * (a.K / 2 + 16);
+    // staged rows at the kernel's pitch, rounded up to whole 1 KiB copies
+    const size_t ap = static_cast<size_t>((a.K / 2 + 255) / 256 * 256 + 32);
+    const size_t alb = (static_cast<size_t>(a.M) * ap + 1023) / 1024 * 1024;
     const size_t red = static_cast<size_t>(NW) * FM * FN * 4 * 64 * 4;
     if constexpr (FM == 1) {
         if (szb + alb <= static_cast<size_t>(kDecAldsMax))
