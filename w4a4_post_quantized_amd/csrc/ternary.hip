@@ -360,16 +360,25 @@ __global__ __launch_bounds__(W * 64) void k_tern_gemm(TernArgs a) {
         for (int b = 0; b < NBUF - 1; ++b) load_pairs(buf[b], QB * group_of(b), QB / 2);
     }
     if constexpr (XL) {
-        // X [M][blocks kb0 .. kb1] into LDS by the whole workgroup, after the
-        // first code loads
+        // X [M][blocks kb0 .. kb1] into LDS after the first code loads, by
+        // direct-to-LDS copies retired by one wait (a loop of load-then-store
+        // waited for memory once per 16-byte chunk and thread): 16-byte slot s
+        // holds row s / RS, chunk s % RS (RS = xls / 8); chunks past the
+        // range and rows past M are padding (copied from a valid address,
+        // never read).  Lane l of copy j fills slot 64 j + l.
         const int w8 = (kb1 - kb0) * (kTB / 8);
-        const int chunks = a.M * w8;
-        for (int c = threadIdx.x; c < chunks; c += kWaves * 64) {
-            const int m = c / w8;
-            const int k8 = c - m * w8;
-            *reinterpret_cast<v4u*>(xl + static_cast<size_t>(m) * a.xls + 8 * k8) =
-                *reinterpret_cast<const v4u*>(a.X + static_cast<size_t>(m) * a.K + kb0 * kTB + 8 * k8);
+        const int RS = a.xls / 8;
+        const int nslots = a.M * RS;
+        const uint16_t* xb = a.X + static_cast<size_t>(kb0) * kTB;
+        uint8_t* xlb = reinterpret_cast<uint8_t*>(xl);
+        for (int j = w; j * 64 < nslots; j += kWaves) {
+            const int s = j * 64 + lane;
+            const int m = s / RS;
+            const int c = s - m * RS;
+            const uint32_t off = (m < a.M && c < w8) ? static_cast<uint32_t>(m) * a.K * 2 + c * 16 : 0u;
+            dma16_async_sv(xb, off, xlb + j * 1024);
         }
+        wait_vmcnt<0>();
         __syncthreads();
     }
     // whole rotations of NBUF groups with no branch around a step (a branch
@@ -556,7 +565,8 @@ TernPlan tern_plan(int M, int N, int K, int cus) {
     p.gps = gps_of(splits);
     p.splits = NG > 0 ? ceil_div(NG, p.gps) : 1;
     p.xls = xls_of(p.gps);
-    p.lds = p.xl ? static_cast<size_t>(M) * p.xls * 2 : 0;
+    // whole 1 KiB copies: the staging's last copy may fill past the rows
+    p.lds = p.xl ? (static_cast<size_t>(M) * p.xls * 2 + 1023) / 1024 * 1024 : 0;
     return p;
 }
 
