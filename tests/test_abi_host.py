@@ -144,7 +144,12 @@ def test_gemm_kernel_name_query():
     64 tokens, the prefill kernels above; invalid descriptors give NULL."""
     assert W.gemm_kernel_name(1, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 1")
     assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec_split<FM 4")
-    assert W.gemm_kernel_name(32, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 2")
+    assert W.gemm_kernel_name(32, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec_split<FM 2")
+    # 8 tokens stage their activations in LDS: the register-streamed kernel;
+    # 16 tokens of 28672 codes do not fit: the split kernel
+    assert W.gemm_kernel_name(8, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec<FM 1")
+    assert W.gemm_kernel_name(16, W.WeightDesc(8192, 28672, 128, 1)).startswith("k_gemm_dec_split<FM 1")
+    assert W.gemm_kernel_name(16, W.WeightDesc(8192, 4096, 128, 1)).startswith("k_gemm_dec<FM 1")
     # other group sizes keep the register-streamed kernel
     assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 512, 1)).startswith("k_gemm_dec<FM 4")
     assert W.gemm_kernel_name(2048, W.WeightDesc(6144, 4096, 4096, 0)).startswith("k_gemm_dl<")

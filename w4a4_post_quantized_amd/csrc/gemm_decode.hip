@@ -803,14 +803,33 @@ const KernelCfg kDec[3][kNumDec] = {
 };
 #undef W4A4_DEC
 
-// the split-K kernel (index kNumDec of the override): measured on MI355X for
-// 64 tokens, 28672 -> 8192 in groups of 128; taken automatically above 32
-// tokens where it applies
+// whether the register-streamed kernel's one-row-fragment configuration, as
+// choose_dec picks it, stages the activations in LDS (launch_dec_a's test)
+bool dec_staged_fits(const GemmArgs& a) {
+    if (a.M > 16) return false;
+    const size_t staged = static_cast<size_t>(a.M) * (a.K / 2 + 16);
+    const bool wide = ceil_div(a.N, 32) >= device_cu_count() && staged > 64 * 1024;
+    const int fn = wide ? 2 : 1;
+    const int G = a.K / a.group_size;
+    const bool sz = G > 1 || a.asym;
+    const size_t szb = sz ? static_cast<size_t>(16 * fn) * (G + 1) * 4 : 0;
+    const size_t ap = static_cast<size_t>((a.K / 2 + 255) / 256 * 256 + 32);
+    const size_t alb = (static_cast<size_t>(a.M) * ap + 1023) / 1024 * 1024;
+    return szb + alb <= static_cast<size_t>(kDecAldsMax);
+}
+
+// the split-K kernel (index kNumDec of the override), taken automatically
+// from 17 tokens on, and from 9 when the register-streamed kernel cannot
+// stage the activations in LDS.  Measured on MI355X (28672 -> 8192, groups
+// of 128): 17 / 24 / 32 tokens 34.0 / 34.4 / 35.0 us against 34.7-37.4 /
+// 37.0-39.4 / 40.7-43.6 us for the register-streamed configurations; 12 and
+// 16 tokens (activations not staged) 32.0 and 32.3 us against 33.0 and
+// 34.3 us; 8 tokens (staged) 34.1 against 27.7-29.5 us.
 bool use_split(const GemmArgs& a) {
     if (!split_supports(a)) return false;
     const int o = kernel_override(1);
     if (o >= 0 && o <= kNumDec) return o == kNumDec;
-    return a.M > 32;
+    return a.M > 16 || (a.M > 8 && !dec_staged_fits(a));
 }
 
 const KernelCfg& choose_dec(const GemmArgs& a) {
