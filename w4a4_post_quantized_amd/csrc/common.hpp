@@ -273,6 +273,35 @@ __device__ __forceinline__ void dma4_async_sv(const void* base, uint32_t off, co
                  : "memory", "m0");
 }
 
+// The same two copies with the wave's LDS destination given as a 32-bit LDS
+// byte address (wave-uniform; the value m0 takes).  Taken from a __shared__
+// array cast to the LDS address space plus scalar offsets, it stays in scalar
+// registers, where a generic LDS pointer is carried in a vector register
+// pair and converted (readfirstlane, null test) at every copy.
+__device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(3))) uint8_t* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, uint32_t lds_m0) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_m0);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(bs), "s"(m0)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4_async_sv(const void* base, uint32_t off, uint32_t lds_m0) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_m0);
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(bs), "s"(m0)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();

@@ -415,6 +415,19 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     __shared__ __align__(16) uint8_t st5[STAGES > 5 ? STAGE_BYTES : 16];
     __shared__ __align__(16) uint8_t st6[STAGES > 6 ? STAGE_BYTES : 16];
     __shared__ __align__(16) uint8_t st7[STAGES > 7 ? STAGE_BYTES : 16];
+    // LDS byte address of a stage (scalar: the copies' m0)
+    auto stage_lds = [&](auto S) -> uint32_t {
+        constexpr int I = decltype(S)::value;
+        typedef const __attribute__((address_space(3))) uint8_t* lp;
+        if constexpr (I == 0) return lds_addr((lp)st0);
+        else if constexpr (I == 1) return lds_addr((lp)st1);
+        else if constexpr (I == 2) return lds_addr((lp)st2);
+        else if constexpr (I == 3) return lds_addr((lp)st3);
+        else if constexpr (I == 4) return lds_addr((lp)st4);
+        else if constexpr (I == 5) return lds_addr((lp)st5);
+        else if constexpr (I == 6) return lds_addr((lp)st6);
+        else return lds_addr((lp)st7);
+    };
     auto stage_ptr = [&](auto S) -> uint8_t* {
         constexpr int I = decltype(S)::value;
         if constexpr (I == 0) return st0;
@@ -481,9 +494,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     auto issue = [&](int kt, auto S) {
         const int kc = min(kt, KT - 1);
         uint8_t* stage = stage_ptr(S);
+        const uint32_t sl = stage_lds(S);
         if constexpr (G1)
             dma4_async_sv(s_w, 2u * ((sz_e0 + static_cast<uint32_t>(kc)) & ~1u),
-                          stage + OPER_BYTES + wave_u * SZSLOT);
+                          sl + static_cast<uint32_t>(OPER_BYTES + wave_u * SZSLOT));
         if constexpr (kBuiltinCopies) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i) dma16(src[i] + kc * 64, stage + (i * NW + wave) * 1024);
@@ -493,7 +507,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
 #pragma unroll
             for (int i = 0; i < LPW; ++i)
                 dma16_async_sv((i * NW + wave_u) * 64 < BM * 4 ? xb : wb, soff[i],
-                               stage + (i * NW + wave_u) * 1024);
+                               sl + static_cast<uint32_t>((i * NW + wave_u) * 1024));
         }
     };
 
@@ -564,8 +578,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void k_gemm_dl(
     }
 
     // one K tile: tile kt is in stage kt % STAGES; the DMA of tile
-    // kt+STAGES-1 goes into the stage tile kt-1 used
-    auto body = [&](int kt, auto S) {
+    // kt+STAGES-1 goes into the stage tile kt-1 used.  Always inlined: a
+    // body emitted out of line (the multi-tile group mode's was) keeps the
+    // accumulators it captures in scratch memory.
+    auto body = [&](int kt, auto S) __attribute__((always_inline)) {
         constexpr int SI = decltype(S)::value;
         issue(kt + STAGES - 1, std::integral_constant<int, (SI + STAGES - 1) % STAGES>{});
         const uint8_t* stage = stage_ptr(S);
