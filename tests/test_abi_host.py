@@ -154,6 +154,11 @@ def test_gemm_kernel_name_query():
     assert W.gemm_kernel_name(64, W.WeightDesc(8192, 28672, 512, 1)).startswith("k_gemm_dec<FM 4")
     assert W.gemm_kernel_name(2048, W.WeightDesc(6144, 4096, 4096, 0)).startswith("k_gemm_dl<")
     assert W.gemm_kernel_name(2048, W.WeightDesc(28672, 4096, 128, 1)).startswith("k_gemm")
+    # groups of 128: 128x128 tiles up to K = 8192, 256x128 tiles above
+    assert W.gemm_kernel_name(2048, W.WeightDesc(28672, 4096, 128, 1)) == \
+        "k_gemm_dl<128x128, waves 2x2, 4 stages>"
+    assert W.gemm_kernel_name(2048, W.WeightDesc(4096, 14336, 128, 1)) == \
+        "k_gemm_dl<256x128, waves 4x2, 4 stages>"
     with pytest.raises(W.W4A4Error):
         W.gemm_kernel_name(16, W.WeightDesc(256, 200, 200, 0))
 

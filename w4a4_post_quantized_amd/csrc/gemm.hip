@@ -807,26 +807,37 @@ int tile_group_for(int tiles_m, int BM, int BN, int wgs_per_cu) {
     return g < tiles_m ? g : tiles_m;
 }
 
-// workgroups of a kernel one CU holds (cached per instantiation)
-template <typename Kern>
-int wgs_per_cu(Kern kern, int threads) {
+// workgroups of kernel Kern one CU holds, cached per kernel: the kernel is a
+// template argument, since every k_gemm_dl instantiation has the same
+// function-pointer type (a cache keyed on that type would keep the first
+// kernel's figure for all of them)
+template <auto Kern>
+int wgs_per_cu(int threads) {
     static int n = 0;
     if (n == 0) {
         int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kern, threads, 0) != hipSuccess || v < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, Kern, threads, 0) != hipSuccess || v < 1)
             v = 1;
         n = v;
     }
     return n;
 }
 
+// one launch of the instantiation Kern; the tile order's group count comes
+// from that kernel's own occupancy
+template <auto Kern, int BM, int BN, int NT>
+hipError_t launch_dl_k(const GemmArgs& a, const uint16_t* S, int Gp, hipStream_t stream) {
+    const dim3 grid(ceil_div(a.N, BN) * ceil_div(a.M, BM));
+    const int tg = tile_group_for(ceil_div(a.M, BM), BM, BN, wgs_per_cu<Kern>(NT));
+    Kern<<<grid, dim3(NT), 0, stream>>>(a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K,
+                                        a.group_size, tg, S, Gp);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WM_, int WN_, int ST, int MODE>
 hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
     // one workgroup per output tile, in a 1-D grid (tile order: xcd_tile)
-    dim3 grid(ceil_div(a.N, BN) * ceil_div(a.M, BM));
-    const int occ = wgs_per_cu(&k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE>, WM_ * WN_ * 64);
-    const int tg = tile_group_for(ceil_div(a.M, BM), BM, BN, occ);
-    dim3 block(WM_ * WN_ * 64);
+    constexpr int NT = WM_ * WN_ * 64;
     if constexpr (MODE == kModeGroup) {
         if (a.group_size == BK) {
             // the scale copies address N x G 16-bit elements with 32-bit offsets
@@ -834,25 +845,18 @@ hipError_t launch_dl(const GemmArgs& a, hipStream_t stream) {
                 return hipErrorInvalidValue;
             if (a.asym && (a.S == nullptr || a.Gp < a.K / BK)) return hipErrorInvalidValue;
             if (a.asym)
-                k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE, true><<<grid, block, 0, stream>>>(
-                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg, a.S,
-                    a.Gp);
-            else
-                k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE, true><<<grid, block, 0, stream>>>(
-                    a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg,
-                    nullptr, 0);
-            return hipGetLastError();
+                return launch_dl_k<&k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE, true>, BM, BN, NT>(
+                    a, a.S, a.Gp, stream);
+            return launch_dl_k<&k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE, true>, BM, BN, NT>(
+                a, nullptr, 0, stream);
         }
     }
     if (a.asym)
-        k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg, nullptr, 0);
-    else
-        k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE><<<grid, block, 0, stream>>>(
-            a.Xq, a.s_x, a.Wq, a.s_w, a.z_w, a.Y, a.M, a.N, a.K, a.group_size, tg, nullptr, 0);
-    return hipGetLastError();
+        return launch_dl_k<&k_gemm_dl<BM, BN, WM_, WN_, ST, true, MODE>, BM, BN, NT>(a, nullptr, 0,
+                                                                                  stream);
+    return launch_dl_k<&k_gemm_dl<BM, BN, WM_, WN_, ST, false, MODE>, BM, BN, NT>(a, nullptr, 0,
+                                                                               stream);
 }
-
 
 template <int BM, int BN, int WM_, int WN_, int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t stream) {
@@ -951,15 +955,17 @@ const KernelCfg& choose(const GemmArgs& a) {
         // direct-to-LDS 128x128 tiles below that
         // (128x384 tiles with 16 waves when they give about one tile per CU:
         // 2048x6144 takes 50.6 against 53.3 us with 256x256 tiles).
-        // Groups of 128 (one-tile groups, direct-to-LDS): 256x128 tiles with
-        // 8 waves and 4 stages (2048x4096 -> 28672: 358-361 us against 374-391
-        // for 128x256 and 383-391 for 128x128 4-wave tiles; 2048x14336 ->
-        // 4096: 167-172 against 177-180 and 197-203 us, one box); other
-        // group sizes: the 16x16x64 128x128 tile (8 waves)
+        // Groups of 128 (one-tile groups, direct-to-LDS): 128x128 tiles with
+        // 4 waves and 4 stages up to K = 8192, 256x128 tiles with 8 waves and
+        // 4 stages above (measured with scalar copy destinations, alternating
+        // runs on one box: 2048x4096 -> 28672 took 333-334 us against 347-352
+        // us with 256x128 tiles; 2048x14336 -> 4096 took 165-170 us with
+        // 256x128 against 175 us with 128x128); other group sizes: the
+        // 16x16x64 128x128 tile (8 waves)
         const long tiles256 = static_cast<long>(ceil_div(a.M, 256)) * ceil_div(a.N, 256);
         const long tiles384 = static_cast<long>(ceil_div(a.M, 128)) * ceil_div(a.N, 384);
         if (grouped && a.group_size == BK)
-            t = 4;
+            t = a.K <= 8192 ? 1 : 4;
         else if (grouped)
             t = 2;
         else if (tiles384 >= cus && tiles384 < 2L * cus)
