@@ -239,69 +239,56 @@ __device__ __forceinline__ void dma16_async(const void* src, const uint8_t* lds_
                  : "memory", "m0");
 }
 
-// Workgroup barrier without a memory fence; the compiler-only fences keep
-// LDS accesses from being moved across it.
-// dma16_async with a wave-uniform 64-bit base (scalar registers) and a
-// per-lane 32-bit byte offset
-__device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, const uint8_t* lds_wave_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (const __attribute__((address_space(3))) uint8_t*)lds_wave_base)));
-    // the base is wave-uniform by contract; readfirstlane puts it in scalar
-    // registers where the compiler cannot prove it.  The builtin returns a
-    // signed int: each half goes through uint32_t before widening, so the
-    // low half is zero-extended
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
-    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(bs), "s"(m0)
-                 : "memory", "m0");
-}
-
-// 4-byte copy of one lane from a wave-uniform 64-bit base and a per-lane
-// 32-bit byte offset; the LDS address of lane l is lds_wave_base + 4 * l.
-// Issued like dma16_async_sv: the compiler does not see it, the caller's
-// s_waitcnt counts it.
-__device__ __forceinline__ void dma4_async_sv(const void* base, uint32_t off, const uint8_t* lds_wave_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (const __attribute__((address_space(3))) uint8_t*)lds_wave_base)));
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
-    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(bs), "s"(m0)
-                 : "memory", "m0");
-}
-
-// The same two copies with the wave's LDS destination given as a 32-bit LDS
-// byte address (wave-uniform; the value m0 takes).  Taken from a __shared__
-// array cast to the LDS address space plus scalar offsets, it stays in scalar
-// registers, where a generic LDS pointer is carried in a vector register
-// pair and converted (readfirstlane, null test) at every copy.
+// Copies from a wave-uniform 64-bit base (scalar registers) and a per-lane
+// 32-bit byte offset, issued like dma16_async: the compiler does not see
+// them, the caller's s_waitcnt counts them.  The wave's LDS destination is a
+// 32-bit LDS byte address (wave-uniform; the value m0 takes).  Taken from a
+// __shared__ array cast to the LDS address space plus scalar offsets, it
+// stays in scalar registers, where a generic LDS pointer is carried in a
+// vector register pair and converted (readfirstlane, null test) at every
+// copy.
 __device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(3))) uint8_t* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-__device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, uint32_t lds_m0) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_m0);
+// the base is wave-uniform by contract; readfirstlane puts it in scalar
+// registers where the compiler cannot prove it.  The builtin returns a signed
+// int: each half goes through uint32_t before widening, so the low half is
+// zero-extended
+__device__ __forceinline__ uint64_t uniform_base(const void* base) {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
-    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// 16 bytes per lane; the LDS address of lane l is lds_m0 + 16 * l
+__device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, uint32_t lds_m0) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_m0);
+    const uint64_t bs = uniform_base(base);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(bs), "s"(m0)
                  : "memory", "m0");
 }
 
+// 4 bytes per lane; the LDS address of lane l is lds_m0 + 4 * l
 __device__ __forceinline__ void dma4_async_sv(const void* base, uint32_t off, uint32_t lds_m0) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_m0);
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
-    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+    const uint64_t bs = uniform_base(base);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(bs), "s"(m0)
                  : "memory", "m0");
 }
 
+// the same with the destination as a generic pointer to the wave's LDS base
+__device__ __forceinline__ void dma16_async_sv(const void* base, uint32_t off, const uint8_t* lds_wave_base) {
+    dma16_async_sv(base, off, lds_addr((const __attribute__((address_space(3))) uint8_t*)lds_wave_base));
+}
+
+__device__ __forceinline__ void dma4_async_sv(const void* base, uint32_t off, const uint8_t* lds_wave_base) {
+    dma4_async_sv(base, off, lds_addr((const __attribute__((address_space(3))) uint8_t*)lds_wave_base));
+}
+
+// Workgroup barrier without a memory fence; the compiler-only fences keep
+// LDS accesses from being moved across it.
 __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
