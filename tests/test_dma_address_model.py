@@ -3,7 +3,7 @@
 
 Those copies are issued as global_load_lds_dwordx4 with a wave-uniform 64-bit
 base in scalar registers and a 32-bit per-lane byte offset
-(dma16_async_sv in common.hpp).  The base is read with readfirstlane, which
+(dma16_async_sv and uniform_base in common.hpp).  The base is read with readfirstlane, which
 returns a signed 32-bit value per half; the 64-bit base must be assembled from
 the two halves each ZERO-extended.  This test models, in exact Python
 integers, (a) the per-lane pointer the compiler-built copies use
