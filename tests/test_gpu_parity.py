@@ -303,6 +303,36 @@ def test_linear_small_shapes(wl):
     _layer_parity(prepared(wl))
 
 
+@pytest.mark.parametrize("n1,n2,M,N,static", [(64, 64, 130, 200, False), (112, 128, 97, 136, False),
+                                               (64, 128, 70, 264, False), (32, 64, 129, 72, False),
+                                               (64, 64, 131, 136, True), (16, 64, 150, 72, False)])
+def test_linear_group_sums_from_transform(n1, n2, M, N, static):
+    """Asymmetric groups of 128 above the decode sizes: the transform kernel
+    of w4a4_linear also writes the per-token group sums of its codes for the
+    GEMM's zero-point correction (no pre-pass).  The layer must equal
+    w4a4_transform_quant followed by w4a4_gemm (which sums the codes in its
+    own pre-pass) bit for bit, and the oracle's layer on those codes."""
+    log(f"linear, group sums from the transform: ({n1},{n2}) M={M} N={N} static={static}")
+    torch, dev = torch_dev()
+    wl = custom_workload(M=M, n1=n1, n2=n2, N=N, group_size=128, asym=True, seed=31 + n1 + M)
+    inp = prepared(wl)
+    X, P1, P2 = to_dev(inp["X"]), to_dev(inp["P1"]), to_dev(inp["P2"])
+    desc, Wq, sw, zw = W().pack_weights(to_dev(inp["Wt"]), 128, True)
+    if static:
+        steps = to_dev(np.array([0.37], np.float32))
+        Y = W().linear_static(X, P1, P2, steps, False, desc, Wq, sw, zw).cpu().numpy()
+        Xq, sx = W().transform_quant_static(X, P1, P2, steps, False)
+    else:
+        Y = W().linear(X, P1, P2, desc, Wq, sw, zw).cpu().numpy()
+        Xq, sx = W().transform_quant(X, P1, P2)
+    Y2 = W().gemm(Xq, sx, desc, Wq, sw, zw).cpu().numpy()
+    assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16))
+    wq = O.quantize_weights(inp["Wt"], 128, True)
+    gq = O.unpack_nibbles(Xq.cpu().numpy(), True)
+    rel = assert_layer_close(Y, gq, sx.cpu().numpy(), wq)
+    log(f"  relative L2 {rel:.2e} on the library's codes")
+
+
 @pytest.mark.parametrize("n1,n2,M,N", [(16, 32, 70, 136), (64, 64, 200, 264)])
 def test_linear_with_channel_scale_and_clip(n1, n2, M, N):
     log(f"linear with diag(c), alpha_a 0.8, ({n1},{n2}) M={M} N={N}")

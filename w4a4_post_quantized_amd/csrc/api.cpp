@@ -417,11 +417,25 @@ static int linear_common(const uint16_t* X, int32_t M, int32_t n1, int32_t n2, c
     const size_t sub_bytes = ws_bytes - static_cast<size_t>(p - static_cast<char*>(ws));
     hipStream_t st = static_cast<hipStream_t>(stream);
 
+    // asymmetric groups of 128: the transform kernel can also write the
+    // per-token group sums the GEMM's zero-point correction takes, at the
+    // start of the GEMM's workspace (the token-batched transforms use no
+    // workspace of their own), which saves the GEMM's pre-pass launch
+    int Gp = 0;
+    const bool want_sums = w4a4::gemm_takes_group_sums(M, desc->K, desc->group_size,
+                                                       desc->asymmetric != 0, &Gp);
+    uint16_t* S16 = want_sums ? static_cast<uint16_t*>(sub) : nullptr;
+    bool sums = false;
     hipError_t e = w4a4::tq_launch(X, M, n1, n2, P1, P2, c, aq, true, Xq, s_x, nullptr, sub,
-                                   sub_bytes, st);
+                                   sub_bytes, st, S16, Gp, &sums);
     if (e != hipSuccess) return hip_status(e, name);
     w4a4::GemmArgs a{Xq, s_x, Wq, s_w, z_w, Y, nullptr, M, desc->N, desc->K, desc->group_size,
                      desc->asymmetric != 0};
+    if (sums) {
+        a.S = S16;
+        a.Gp = Gp;
+        a.sums_ready = true;
+    }
     e = w4a4::gemm_launch(a, false, sub, sub_bytes, st);
     return hip_status(e, name);
 }

@@ -988,6 +988,12 @@ static bool uses_group_sums(int M, int K, int group_size, bool asym) {
     return asym && group_size == BK && M > kDecodeMaxM && K / group_size > 1;
 }
 
+bool gemm_takes_group_sums(int M, int K, int group_size, bool asym, int* Gp) {
+    if (!uses_group_sums(M, K, group_size, asym)) return false;
+    *Gp = group_sums_pad(K);
+    return true;
+}
+
 size_t gemm_workspace_bytes(int M, int N, int K, int group_size, bool asym) {
     // decode: the split-K kernel's partial sums (per channel or groups of 128)
     if (M <= kDecodeMaxM) return gemm_decode_workspace_bytes(M, N, K, group_size, asym);
@@ -1011,7 +1017,9 @@ hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_byte
     const KernelCfg& k = choose(a);
     if (!grouped) return k.chan(a, stream);
     GemmArgs g = a;
-    if (uses_group_sums(a.M, a.K, a.group_size, a.asym)) {
+    if (uses_group_sums(a.M, a.K, a.group_size, a.asym) && a.sums_ready) {
+        if (a.S == nullptr || a.Gp != group_sums_pad(a.K)) return hipErrorInvalidValue;
+    } else if (uses_group_sums(a.M, a.K, a.group_size, a.asym)) {
         const size_t need = gemm_workspace_bytes(a.M, a.N, a.K, a.group_size, a.asym);
         if (ws == nullptr || ws_bytes < need) return hipErrorInvalidValue;
         g.Gp = group_sums_pad(a.K);

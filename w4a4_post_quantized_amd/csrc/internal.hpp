@@ -38,10 +38,15 @@ TqPath tq_select_path(int M, int n1, int n2, bool has_c);
 size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c);
 
 // quantize=true: Xq/s_x outputs; quantize=false: Z (fp32 [M,K]) output.
+// S16 (optional, [M, Gp] fp16): the per-token group sums 16 * Σ_{k in g} q
+// of the codes over groups of 128, zero for g >= K / 128, which the GEMM's
+// zero-point correction takes; written only by the token-batched kernels
+// (*sums_written tells), the other paths leave them to the GEMM's pre-pass.
 hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
                      const float* P2, const float* c, ActQuant aq, bool quantize,
                      uint8_t* Xq, float* s_x, float* Z, void* ws, size_t ws_bytes,
-                     hipStream_t stream);
+                     hipStream_t stream, uint16_t* S16 = nullptr, int Gp = 0,
+                     bool* sums_written = nullptr);
 
 // ---- GEMM (gemm.hip) -------------------------------------------------------
 struct GemmArgs {
@@ -59,9 +64,16 @@ struct GemmArgs {
     // zero-point correction in the epilogue
     const uint16_t* S = nullptr;
     int Gp = 0;
+    // the caller has already written S ([M, Gp] in the workspace, by the
+    // transform kernel): gemm_launch skips its pre-pass
+    bool sums_ready = false;
 };
 
 size_t gemm_workspace_bytes(int M, int N, int K, int group_size, bool asym);
+// whether the prefill GEMM applies the zero-point correction from per-token
+// group sums, and their row pitch Gp (the sums sit at the start of the GEMM
+// workspace)
+bool gemm_takes_group_sums(int M, int K, int group_size, bool asym, int* Gp);
 // name of the configuration gemm_launch would use (launches nothing)
 const char* gemm_kernel_name(const GemmArgs& a, bool i32_out);
 hipError_t gemm_launch(const GemmArgs& a, bool i32_out, void* ws, size_t ws_bytes,

@@ -160,6 +160,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t steps_rsrc(const float* steps,
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(steps), 0, K * 4, 0x00020000);
 }
 
+// Per-token group sums of the codes for the zero-point correction of the
+// GEMM (asymmetric weights, groups of 128 codes): 16 * Σ_{k in g} q[m,k] as
+// fp16 (|16 S| <= 16384, exact), the values the GEMM's own pre-pass would
+// write.  A group is 64 packed bytes, i.e. four consecutive 16-byte chunks of
+// the token's packed row; the four lanes that store them add their chunk
+// sums (the chunk index is the lane index plus a multiple of 64, so a group
+// sits in four consecutive lanes, all active or all inactive).
+__device__ __forceinline__ int nibble_sum(uint32_t w) {
+    // two's complement nibbles: the unsigned nibble sum less 16 per negative code
+    const uint32_t u = (w & 0x0F0F0F0Fu) + ((w >> 4) & 0x0F0F0F0Fu);
+    return static_cast<int>((u * 0x01010101u) >> 24) - 16 * __builtin_popcount(w & 0x88888888u);
+}
+
+__device__ __forceinline__ void store_group_sum(const uint4& v, int chunk, uint16_t* srow) {
+    int sum = nibble_sum(v.x) + nibble_sum(v.y) + nibble_sum(v.z) + nibble_sum(v.w);
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    if ((chunk & 3) == 0) srow[chunk >> 2] = f2h(static_cast<float>(16 * sum));
+}
+
 // ===========================================================================
 // Fused MFMA path
 // ===========================================================================
@@ -195,7 +215,8 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
                                                   const float* __restrict__ P2, ActQuant aq,
                                                   uint8_t* __restrict__ Xq,
                                                   float* __restrict__ s_x,
-                                                  float* __restrict__ Zout) {
+                                                  float* __restrict__ Zout,
+                                                  uint16_t* __restrict__ S16, int Gp) {
     using C = FusedCfg<N1, N2>;
     constexpr int K = C::K;
     __shared__ __align__(16) _Float16 p1hi[C::P1F];
@@ -454,11 +475,18 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
             for (int c = tid; c < C::TPI * CH; c += NT) {
                 const int t = c / CH;
                 const int mm = base + t;
-                if (mm < M)
-                    reinterpret_cast<uint4*>(Xq + static_cast<size_t>(mm) * (K / 2))[c - t * CH] =
-                        reinterpret_cast<const uint4*>(qbuf)[c];
+                if (mm < M) {
+                    const uint4 v = reinterpret_cast<const uint4*>(qbuf)[c];
+                    reinterpret_cast<uint4*>(Xq + static_cast<size_t>(mm) * (K / 2))[c - t * CH] = v;
+                    if (S16 != nullptr) store_group_sum(v, c - t * CH, S16 + static_cast<size_t>(mm) * Gp);
+                }
             }
             if (tid < C::TPI && base + tid < M) s_x[base + tid] = tok_s[tid];
+            // the padding groups of the sums rows: zero
+            if (S16 != nullptr && tid < C::TPI * (Gp - K / 128) && base + tid / (Gp - K / 128) < M) {
+                const int t = tid / (Gp - K / 128);
+                S16[static_cast<size_t>(base + t) * Gp + K / 128 + (tid - t * (Gp - K / 128))] = 0;
+            }
         }
         // the buffer written here was last read one iteration ago, before two
         // barriers; the barrier below publishes it for the next iteration
@@ -469,7 +497,8 @@ __global__ __launch_bounds__((FusedCfg<N1, N2>::NT)) void k_tq_fused(const uint1
 
 template <int N1, int N2, bool PC>
 hipError_t launch_fused_k(const uint16_t* X, int M, const float* P1, const float* P2, ActQuant aq,
-                          uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+                          uint8_t* Xq, float* s_x, float* Z, uint16_t* S16, int Gp,
+                          hipStream_t stream) {
     using C = FusedCfg<N1, N2>;
     // persistent grid: as many workgroups as fit on the device at once, so the
     // per-workgroup fragment setup is paid once per resident workgroup
@@ -484,7 +513,7 @@ hipError_t launch_fused_k(const uint16_t* X, int M, const float* P1, const float
     const int units = (M + C::TPI - 1) / C::TPI;
     const int cap = per_cu * device_cu_count();
     const int grid = units < cap ? units : cap;
-    k_tq_fused<N1, N2, PC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, aq, Xq, s_x, Z);
+    k_tq_fused<N1, N2, PC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, aq, Xq, s_x, Z, S16, Gp);
     return hipGetLastError();
 }
 
@@ -492,11 +521,12 @@ hipError_t launch_fused_k(const uint16_t* X, int M, const float* P1, const float
 // offer it for a layer with c)
 template <int N1, int N2>
 hipError_t launch_fused(const uint16_t* X, int M, const float* P1, const float* P2, const float* c,
-                        ActQuant aq, uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+                        ActQuant aq, uint8_t* Xq, float* s_x, float* Z, uint16_t* S16, int Gp,
+                        hipStream_t stream) {
     (void)c;
     if (aq.steps != nullptr && aq.per_channel && Xq != nullptr)
-        return launch_fused_k<N1, N2, true>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
-    return launch_fused_k<N1, N2, false>(X, M, P1, P2, aq, Xq, s_x, Z, stream);
+        return launch_fused_k<N1, N2, true>(X, M, P1, P2, aq, Xq, s_x, Z, S16, Gp, stream);
+    return launch_fused_k<N1, N2, false>(X, M, P1, P2, aq, Xq, s_x, Z, S16, Gp, stream);
 }
 
 // ===========================================================================
@@ -542,7 +572,8 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
                                                                 const float* __restrict__ cvec, ActQuant aq,
                                                                 uint8_t* __restrict__ Xq,
                                                                 float* __restrict__ s_x,
-                                                                float* __restrict__ Zout) {
+                                                                float* __restrict__ Zout,
+                                                                uint16_t* __restrict__ S16, int Gp) {
     using C = WaveCfg<N1, N2>;
     constexpr int K = C::K;
     constexpr int NT = C::NT;
@@ -864,8 +895,14 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
             // of one wave complete in order
             uint4* dst = reinterpret_cast<uint4*>(Xq + static_cast<size_t>(m) * (K / 2));
 #pragma unroll
-            for (int c = lane; c < C::QB / 16; c += 64) dst[c] = reinterpret_cast<const uint4*>(qb)[c];
+            for (int c = lane; c < C::QB / 16; c += 64) {
+                const uint4 v = reinterpret_cast<const uint4*>(qb)[c];
+                dst[c] = v;
+                if (S16 != nullptr) store_group_sum(v, c, S16 + static_cast<size_t>(m) * Gp);
+            }
             if (lane == 0) s_x[m] = s;
+            // the padding groups of the sums row: zero
+            if (S16 != nullptr && lane < Gp - K / 128) S16[static_cast<size_t>(m) * Gp + K / 128 + lane] = 0;
         }
     };
     // every token but the wave's last has the next one in flight (an
@@ -884,7 +921,8 @@ __global__ __launch_bounds__((WaveCfg<N1, N2>::NT)) void k_tq_wave(const uint16_
 
 template <int N1, int N2, bool PC, bool HC>
 hipError_t launch_wave_k(const uint16_t* X, int M, const float* P1, const float* P2, const float* c,
-                         ActQuant aq, uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+                         ActQuant aq, uint8_t* Xq, float* s_x, float* Z, uint16_t* S16, int Gp,
+                         hipStream_t stream) {
     using C = WaveCfg<N1, N2>;
     // persistent grid: as many workgroups as fit on the device at once, so
     // the fragment setup is paid once per resident workgroup
@@ -899,23 +937,27 @@ hipError_t launch_wave_k(const uint16_t* X, int M, const float* P1, const float*
     const int units = (M + C::NW - 1) / C::NW;
     const int cap = per_cu * device_cu_count();
     const int grid = units < cap ? units : cap;
-    k_tq_wave<N1, N2, PC, HC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, c, aq, Xq, s_x, Z);
+    k_tq_wave<N1, N2, PC, HC><<<grid, C::NT, 0, stream>>>(X, M, P1, P2, c, aq, Xq, s_x, Z, S16, Gp);
     return hipGetLastError();
 }
 
 template <int N1, int N2>
 hipError_t launch_wave(const uint16_t* X, int M, const float* P1, const float* P2, const float* c,
-                       ActQuant aq, uint8_t* Xq, float* s_x, float* Z, hipStream_t stream) {
+                       ActQuant aq, uint8_t* Xq, float* s_x, float* Z, uint16_t* S16, int Gp,
+                       hipStream_t stream) {
     const bool pc = aq.steps != nullptr && aq.per_channel && Xq != nullptr;
     if (c != nullptr)
-        return pc ? launch_wave_k<N1, N2, true, true>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream)
-                  : launch_wave_k<N1, N2, false, true>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream);
-    return pc ? launch_wave_k<N1, N2, true, false>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream)
-              : launch_wave_k<N1, N2, false, false>(X, M, P1, P2, c, aq, Xq, s_x, Z, stream);
+        return pc ? launch_wave_k<N1, N2, true, true>(X, M, P1, P2, c, aq, Xq, s_x, Z, S16, Gp, stream)
+                  : launch_wave_k<N1, N2, false, true>(X, M, P1, P2, c, aq, Xq, s_x, Z, S16, Gp, stream);
+    return pc ? launch_wave_k<N1, N2, true, false>(X, M, P1, P2, c, aq, Xq, s_x, Z, S16, Gp, stream)
+              : launch_wave_k<N1, N2, false, false>(X, M, P1, P2, c, aq, Xq, s_x, Z, S16, Gp, stream);
 }
 
+// S16 / Gp: the per-token group sums of the codes (see store_group_sum),
+// written only when S16 is not null (quantizing calls with K a multiple of
+// 128 and Gp >= K / 128)
 using FusedFn = hipError_t (*)(const uint16_t*, int, const float*, const float*, const float*,
-                               ActQuant, uint8_t*, float*, float*, hipStream_t);
+                               ActQuant, uint8_t*, float*, float*, uint16_t*, int, hipStream_t);
 
 // (n1, n2) pairs with a fused (or wave-per-token) instantiation; with
 // diag(c) only the wave-per-token kernels apply
@@ -1282,13 +1324,21 @@ size_t tq_workspace_bytes(int M, int n1, int n2, bool has_c) {
 hipError_t tq_launch(const uint16_t* X, int M, int n1, int n2, const float* P1,
                      const float* P2, const float* c, ActQuant aq, bool quantize,
                      uint8_t* Xq, float* s_x, float* Z, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+                     hipStream_t stream, uint16_t* S16, int Gp, bool* sums_written) {
     (void)ws_bytes;
+    if (sums_written != nullptr) *sums_written = false;
     if (M == 0) return hipSuccess;
     const TqPath path = tq_select_path(M, n1, n2, c != nullptr);
-    if (path == TqPath::Fused)
-        return fused_for(n1, n2, c != nullptr)(X, M, P1, P2, c, aq, quantize ? Xq : nullptr, s_x,
-                                               quantize ? nullptr : Z, stream);
+    if (path == TqPath::Fused) {
+        const int K = n1 * n2;
+        const bool sums = quantize && S16 != nullptr && K % 128 == 0 && Gp >= K / 128 &&
+                          Gp - K / 128 < 64;
+        const hipError_t e = fused_for(n1, n2, c != nullptr)(
+            X, M, P1, P2, c, aq, quantize ? Xq : nullptr, s_x, quantize ? nullptr : Z,
+            sums ? S16 : nullptr, sums ? Gp : 0, stream);
+        if (e == hipSuccess && sums && sums_written != nullptr) *sums_written = true;
+        return e;
+    }
     if (path == TqPath::Cols)
         return cols_for(n1, n2)->launch(X, M, P1, P2, aq, Xq, s_x, quantize ? nullptr : Z, ws,
                                         stream);
