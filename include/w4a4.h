@@ -262,7 +262,11 @@ size_t w4a4_linear_workspace_bytes(int32_t M, int32_t n1, int32_t n2, int32_t ha
 
 /* w4a4_transform_quant followed by w4a4_gemm on the same stream, with the
  * packed activations and their scales kept in `ws`:
- *   Y [M, N] fp16 = W4A4 linear of X [M, K] fp16 (K = n1*n2 = desc->K). */
+ *   Y [M, N] fp16 = W4A4 linear of X [M, K] fp16 (K = n1*n2 = desc->K).
+ * With asymmetric groups of 128 and M > 64, the token-batched transform
+ * kernels also write the GEMM's per-token group sums into `ws`, so the
+ * GEMM's own pre-pass is not launched; Y is that of the two calls, bit for
+ * bit. */
 int w4a4_linear(const uint16_t* X, int32_t M, int32_t n1, int32_t n2,
                 const float* P1, const float* P2, const float* c, float alpha_a,
                 const w4a4_weight_desc* desc, const uint8_t* Wq, const uint16_t* s_w,
